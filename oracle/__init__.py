@@ -1,0 +1,8 @@
+"""fp64 reference oracle for the PowerSGD compression step (test
+infrastructure: imported only by tests, the smoke entry and the benchmark's
+CPU-baseline leg)."""
+from .powersgd import *  # noqa: F401,F403
+from .powersgd import (KIND_COMPRESSED, KIND_PASSTHRU, KIND_VECTOR, Plan, SetResult, SetState,  # noqa: F401
+                       ZERO_COLUMN_REL, classify, compress_matrix, compress_workers, decompress,
+                       gram_schmidt, init_state, matrix_view, momentum_input, orthonormality_error,
+                       principal_angle_sines, refresh, step_set)

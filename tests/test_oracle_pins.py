@@ -1,0 +1,469 @@
+"""Pins for the fp64 oracle, against what the PowerSGD pages and the
+mathematics fix.  The pages print no worked numerical example, so every pin is
+a closed form, an invariant, a library routine (LAPACK QR / SVD), or brute
+force on tiny inputs.  Several tests plant a mistake in a copy of the oracle
+and check that a pin catches it.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import powersgd as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(autouse=True)
+def _strict_fp():
+    with np.errstate(over="raise", invalid="raise", divide="raise"):
+        yield
+
+
+def rand(g, *shape):
+    return g.standard_normal(shape)
+
+
+def qr_positive(P):
+    """Q factor of LAPACK's QR with signs fixed so that diag(R) > 0."""
+    Qf, R = np.linalg.qr(P)
+    s = np.sign(np.diag(R))
+    s[s == 0] = 1.0
+    return Qf * s
+
+
+# ---------------------------------------------------------------- Gram-Schmidt
+
+@pytest.mark.parametrize("m,r", [(7, 1), (64, 2), (256, 4), (1000, 7), (513, 16), (300, 64)])
+def test_gs_equals_qr_factor(m, r):
+    g = np.random.default_rng(m * 100 + r)
+    P = rand(g, m, r)
+    Ph = oracle.gram_schmidt(P)
+    assert np.abs(Ph - qr_positive(P)).max() <= 1e-12
+
+
+def test_gs_orthonormal_and_triangular_relation():
+    g = np.random.default_rng(11)
+    P = rand(g, 500, 8) @ np.diag(np.logspace(0, -3, 8))  # moderately ill-conditioned
+    Ph = oracle.gram_schmidt(P)
+    assert oracle.orthonormality_error(Ph) <= 1e-12
+    R = Ph.T @ P  # P = Ph R with R upper triangular, positive diagonal
+    assert np.abs(np.tril(R, -1)).max() <= 1e-12 * np.abs(R).max()
+    assert (np.diag(R) > 0).all()
+
+
+def test_gs_zero_and_dependent_columns():
+    g = np.random.default_rng(3)
+    a = rand(g, 50)
+    b = rand(g, 50)
+    P = np.stack([a, np.zeros(50), 2.0 * a, b, a - 3.0 * b], axis=1)
+    Ph = oracle.gram_schmidt(P)
+    assert np.all(Ph[:, 1] == 0) and np.all(Ph[:, 2] == 0) and np.all(Ph[:, 4] == 0)
+    np.testing.assert_allclose(Ph[:, 0], a / np.linalg.norm(a), atol=1e-14)
+    assert abs(Ph[:, 3] @ Ph[:, 0]) <= 1e-14
+    assert abs(np.linalg.norm(Ph[:, 3]) - 1.0) <= 1e-14
+
+
+def test_gs_threshold_is_relative():
+    # A column whose component off the span is 1e-3 of its norm survives;
+    # one at 1e-6 is zeroed (threshold 1e-4, reading R3).
+    g = np.random.default_rng(5)
+    a = rand(g, 40)
+    a /= np.linalg.norm(a)
+    z = rand(g, 40)
+    z -= (a @ z) * a
+    z /= np.linalg.norm(z)
+    keep = oracle.gram_schmidt(np.stack([a, a + 1e-3 * z], 1))
+    drop = oracle.gram_schmidt(np.stack([a, a + 1e-6 * z], 1))
+    np.testing.assert_allclose(keep[:, 1], z, atol=1e-9)
+    assert np.all(drop[:, 1] == 0)
+
+
+# -------------------------------------------------------------- one compression
+
+def test_residual_identity_exact():
+    g = np.random.default_rng(7)
+    M = rand(g, 96, 80)
+    Q = rand(g, 80, 3)
+    res = oracle.compress_matrix(M, Q)
+    scale = np.maximum(np.abs(M), np.abs(res.M_hat))
+    ulp = np.spacing(scale)
+    assert np.all(np.abs(res.M_hat + res.E - M) <= ulp)
+
+
+def test_orthonormal_output():
+    wl = W.SmallMatrixWorkload()
+    res = oracle.compress_matrix(wl.grads[0], wl.Q0)
+    assert oracle.orthonormality_error(res.P_hat) <= 1e-12
+
+
+@pytest.mark.parametrize("m,n,k,r", [(60, 40, 1, 1), (60, 40, 2, 2), (128, 64, 3, 4), (33, 27, 4, 4)])
+def test_exact_recovery_low_rank(m, n, k, r):
+    g = np.random.default_rng(m + n + k + r)
+    M = rand(g, m, k) @ rand(g, n, k).T
+    Q = rand(g, n, r)  # generic Q: rank(B^T Q) = k
+    res = oracle.compress_matrix(M, Q)
+    assert np.linalg.norm(res.E) <= 1e-12 * np.linalg.norm(M)
+    assert np.linalg.norm(res.M_hat - M) <= 1e-12 * np.linalg.norm(M)
+
+
+def test_eckart_young_limit():
+    # Fixed M, error memory reset to zero every round: repeated warm-started
+    # single iterations are subspace iteration on M^T M, so the residual tends
+    # to the best rank-r error sqrt(sum_{k>r} sigma_k^2) (LAPACK SVD).
+    g = np.random.default_rng(1)
+    m, n, r = 256, 128, 2
+    U = W.orthonormal(g, m, n)
+    V = W.orthonormal(g, n, n)
+    s = 1.0 / np.arange(1, n + 1)
+    M = (U * s) @ V.T
+    Q = rand(g, n, r)
+    for _ in range(40):
+        res = oracle.compress_matrix(M, Q)
+        Q = res.Q
+    sv = np.linalg.svd(M, compute_uv=False)
+    best = math.sqrt(float(np.sum(sv[r:] ** 2)))
+    assert abs(np.linalg.norm(res.E) - best) <= 1e-10 * best
+    # and the reconstruction is the truncated SVD itself
+    Uf, sf, Vf = np.linalg.svd(M)
+    trunc = (Uf[:, :r] * sf[:r]) @ Vf[:r]
+    assert np.linalg.norm(res.M_hat - trunc) <= 1e-9 * np.linalg.norm(trunc)
+
+
+def test_eckart_young_rate():
+    # Error of the rank-r subspace decays like (sigma_{r+1}/sigma_r)^(2t).
+    g = np.random.default_rng(2)
+    m, n, r = 120, 80, 3
+    U = W.orthonormal(g, m, n)
+    V = W.orthonormal(g, n, n)
+    s = 0.9 ** np.arange(n)
+    M = (U * s) @ V.T
+    Q = rand(g, n, r)
+    sines = []
+    for _ in range(12):
+        res = oracle.compress_matrix(M, Q)
+        Q = res.Q
+        sines.append(oracle.principal_angle_sines(Q, V[:, :r])[0])
+    ratios = np.array(sines[5:]) / np.array(sines[4:-1])
+    np.testing.assert_allclose(ratios, (s[r] / s[r - 1]) ** 2, rtol=2e-2)
+
+
+def test_zero_matrix():
+    res = oracle.compress_matrix(np.zeros((30, 20)), np.ones((20, 2)))
+    assert not res.P_hat.any() and not res.Q.any() and not res.E.any() and not res.M_hat.any()
+
+
+def test_rank1_power_method():
+    # r = 1 is the power method: q/||q|| -> +-v1 and ||M^T p_hat|| -> sigma_1.
+    g = np.random.default_rng(9)
+    m, n = 90, 70
+    U = W.orthonormal(g, m, n)
+    V = W.orthonormal(g, n, n)
+    s = np.concatenate([[3.0], np.linspace(1.5, 0.1, n - 1)])
+    M = (U * s) @ V.T
+    q = rand(g, n, 1)
+    for _ in range(200):
+        q = oracle.compress_matrix(M, q).Q
+    v = q[:, 0] / np.linalg.norm(q)
+    assert abs(abs(v @ V[:, 0]) - 1.0) <= 1e-12
+    assert abs(np.linalg.norm(q) - 3.0) <= 1e-12
+
+
+def test_triangular_invariance_of_warm_start():
+    # GS(M Q T) = GS(M Q) for upper-triangular T with positive diagonal
+    # (uniqueness of thin QR), so P_hat does not depend on rescaling or
+    # orthonormalising the warm start (reading R2 is immaterial for P_hat).
+    g = np.random.default_rng(4)
+    M = rand(g, 70, 50)
+    Q = rand(g, 50, 4)
+    T = np.triu(rand(g, 4, 4))
+    np.fill_diagonal(T, np.abs(np.diag(T)) + 0.5)
+    a = oracle.compress_matrix(M, Q)
+    b = oracle.compress_matrix(M, Q @ T)
+    assert np.abs(a.P_hat - b.P_hat).max() <= 1e-12
+    assert np.abs(a.Q - b.Q).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- linearity
+
+def test_linearity_of_p_and_q_stages():
+    g = np.random.default_rng(12)
+    M1, M2 = rand(g, 64, 48), rand(g, 64, 48)
+    Q = rand(g, 48, 3)
+    a, b = 0.7, -1.3
+    P = lambda M: oracle.compress_matrix(M, Q).P
+    assert np.abs(P(a * M1 + b * M2) - (a * P(M1) + b * P(M2))).max() <= 1e-13
+    Ph = oracle.gram_schmidt(rand(g, 64, 3))
+    Qs = lambda M: M.T @ Ph
+    assert np.abs(Qs(a * M1 + b * M2) - (a * Qs(M1) + b * Qs(M2))).max() <= 1e-13
+
+
+def test_mean_hook_over_workers_equals_compressing_the_mean():
+    g = np.random.default_rng(13)
+    Ms = [rand(g, 80, 60) for _ in range(4)]
+    Q = rand(g, 60, 2)
+    Ph, Qn, Es = oracle.compress_workers(Ms, Q)
+    ref = oracle.compress_matrix(sum(Ms) / 4, Q)
+    assert np.abs(Ph - ref.P_hat).max() <= 1e-13
+    assert np.abs(Qn - ref.Q).max() <= 1e-13
+    # each worker keeps its own residual against the shared reconstruction
+    for M, E in zip(Ms, Es):
+        assert np.abs(M - E - ref.M_hat).max() <= 1e-13
+
+
+def test_mean_hooks_in_step_set_match_workers():
+    # The hook arguments of compress_matrix carry the aggregation.
+    g = np.random.default_rng(14)
+    Ms = [rand(g, 40, 30) for _ in range(3)]
+    Q = rand(g, 30, 2)
+    Ps = [M @ Q for M in Ms]
+    mean_p = lambda P: sum(Ps) / 3
+    Ph = oracle.gram_schmidt(sum(Ps) / 3)
+    mean_q = lambda Qx: sum(M.T @ Ph for M in Ms) / 3
+    r = oracle.compress_matrix(Ms[0], Q, hook_p=mean_p, hook_q=mean_q)
+    Ph2, Q2, Es = oracle.compress_workers(Ms, Q)
+    assert np.abs(r.P_hat - Ph2).max() <= 1e-13
+    assert np.abs(r.Q - Q2).max() <= 1e-13
+    assert np.abs(r.E - Es[0]).max() <= 1e-13
+
+
+# ----------------------------------------------------------- error feedback
+
+def test_error_feedback_telescopes():
+    # No information is discarded, only delayed: sum_t M_hat_t + E_T = sum_t G_t.
+    wl = W.SmallMatrixWorkload()
+    plan = oracle.Plan([(256, 128)], 2)
+    st = oracle.init_state(plan, [wl.Q0])
+    acc = np.zeros((256, 128))
+    gsum = np.zeros((256, 128))
+    for t in range(wl.steps):
+        res = oracle.step_set(plan, [wl.grads[t]], st)
+        acc += res.M_hat[0]
+        gsum += wl.grads[t].astype(np.float64)
+    err = np.linalg.norm(acc + st.E[0] - gsum) / np.linalg.norm(gsum)
+    assert err <= 1e-12
+
+
+def test_error_feedback_telescopes_with_momentum():
+    g = np.random.default_rng(21)
+    plan = oracle.Plan([(40, 30), (30,)], 2)
+    st = oracle.init_state(plan, [rand(g, 30, 2), None], momentum=True)
+    beta = 0.9
+    acc = np.zeros((40, 30))
+    usum = np.zeros((40, 30))
+    u = np.zeros((40, 30))
+    for t in range(6):
+        G = rand(g, 40, 30)
+        res = oracle.step_set(plan, [G, rand(g, 30)], st, beta=beta)
+        u = beta * u + G
+        usum += u
+        acc += res.M_hat[0]
+    assert np.linalg.norm(acc + st.E[0] - usum) <= 1e-12 * np.linalg.norm(usum)
+
+
+def test_momentum_closed_form():
+    # Constant G: u_t = G (1 - beta^t) / (1 - beta).
+    G = np.arange(12.0).reshape(3, 4)
+    u = np.zeros_like(G)
+    beta = 0.9
+    for t in range(1, 8):
+        u = oracle.momentum_input(u, G, beta)
+        np.testing.assert_allclose(u, G * (1 - beta ** t) / (1 - beta), rtol=1e-14)
+
+
+def test_passthrough_tensors_sent_unchanged():
+    g = np.random.default_rng(22)
+    plan = oracle.Plan([(5,), (2, 2), (64, 32)], 1)
+    assert plan.kinds == [O.KIND_VECTOR, O.KIND_PASSTHRU, O.KIND_COMPRESSED]
+    st = oracle.init_state(plan, [None, None, rand(g, 32, 1)])
+    grads = [rand(g, 5), rand(g, 2, 2), rand(g, 64, 32)]
+    res = oracle.step_set(plan, grads, st)
+    assert np.array_equal(res.M_hat[0], grads[0]) and np.array_equal(res.M_hat[1], grads[1])
+    assert st.E[0] is None and st.E[1] is None
+
+
+# ------------------------------------------------------------- plan / payload
+
+def _golden_payload():
+    rows = {}
+    with open(os.path.join(GOLDEN, "payload_counts.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, r, nm, el, fl, vec = line.split()
+            rows[name] = tuple(int(x) for x in (r, nm, el, fl, vec))
+    return rows
+
+
+@pytest.mark.parametrize("name,tensors", [("resnet18", W.resnet18_cifar_set()),
+                                          ("lstm3", W.lstm3_wikitext_set()),
+                                          ("llama7b", W.llama7b_set())])
+def test_payload_counts(name, tensors):
+    r, nm, el, fl, vec = _golden_payload()[name]
+    plan = oracle.Plan([s for _, s in tensors], r)
+    pm, qn, pt = plan.payload()
+    assert len(plan.compressed) == nm
+    assert plan.dense_elems() == el
+    assert pm + qn == fl
+    assert pt == vec
+    assert el / fl > 100  # "ratios above 100x" at r = 1..4
+
+
+def test_classification_rule():
+    assert oracle.classify((7,), 1) == O.KIND_VECTOR
+    assert oracle.classify((2, 2), 1) == O.KIND_PASSTHRU       # 1*(2+2) = 4 = mn
+    assert oracle.classify((3, 3), 1) == O.KIND_COMPRESSED     # 6 < 9
+    assert oracle.classify((10, 512), 2) == O.KIND_COMPRESSED
+    assert oracle.classify((10, 10), 5) == O.KIND_PASSTHRU     # 100 = 100
+    assert oracle.classify((64, 3, 3, 3), 2) == O.KIND_COMPRESSED
+    assert oracle.matrix_view((64, 3, 3, 3)) == (64, 27)
+    assert oracle.classify((1, 4096), 1) == O.KIND_PASSTHRU    # 4097 >= 4096
+
+
+# ---------------------------------------------------------------- brute force
+
+def _scalar_compress(M, Q):
+    """Scalar-loop PowerSGD step for tiny sizes (no BLAS, no numpy reductions)."""
+    m, n = len(M), len(M[0])
+    r = len(Q[0])
+    P = [[sum(M[i][j] * Q[j][k] for j in range(n)) for k in range(r)] for i in range(m)]
+    Ph = [[0.0] * r for _ in range(m)]
+    for k in range(r):
+        v = [P[i][k] for i in range(m)]
+        nu0 = math.sqrt(sum(x * x for x in v))
+        for j in range(k):
+            d = sum(Ph[i][j] * v[i] for i in range(m))
+            v = [v[i] - d * Ph[i][j] for i in range(m)]
+        nv = math.sqrt(sum(x * x for x in v))
+        if nu0 > 0 and nv > 1e-4 * nu0:
+            for i in range(m):
+                Ph[i][k] = v[i] / nv
+    Qn = [[sum(M[i][j] * Ph[i][k] for i in range(m)) for k in range(r)] for j in range(n)]
+    E = [[M[i][j] - sum(Ph[i][k] * Qn[j][k] for k in range(r)) for j in range(n)] for i in range(m)]
+    return Ph, Qn, E
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_tiny(seed):
+    g = np.random.default_rng(100 + seed)
+    m, n = int(g.integers(2, 7)), int(g.integers(2, 7))
+    r = int(g.integers(1, min(m, n) + 1))
+    M = rand(g, m, n)
+    Q = rand(g, n, r)
+    Ph, Qn, E = _scalar_compress(M.tolist(), Q.tolist())
+    res = oracle.compress_matrix(M, Q)
+    assert np.abs(np.array(Ph) - res.P_hat).max() <= 1e-13
+    assert np.abs(np.array(Qn) - res.Q).max() <= 1e-13
+    assert np.abs(np.array(E) - res.E).max() <= 1e-13
+
+
+# ---------------------------------------------------------------- refresh
+
+def test_refresh_converges_to_svd_subspace():
+    # Well separated leading spectrum: 8 rounds reach the LAPACK subspace.
+    g = np.random.default_rng(31)
+    m, n, r = 300, 200, 4
+    U = W.orthonormal(g, m, n)
+    V = W.orthonormal(g, n, n)
+    s = np.concatenate([[10.0, 8.0, 6.0, 4.0], 0.5 * 0.99 ** np.arange(n - 4)])
+    M = (U * s) @ V.T
+    Q = oracle.refresh(M, rand(g, n, r), 8)
+    _, _, Vt = np.linalg.svd(M)
+    assert oracle.orthonormality_error(Q) <= 1e-12
+    bound = (0.5 / 4.0) ** 16 * 1e3
+    assert oracle.principal_angle_sines(Q, Vt[:r].T)[0] <= bound
+
+
+def test_refresh_fused_form_same_subspace():
+    # GS(M^T (M Q)) spans the same space as GS(M^T GS(M Q)) and, both being
+    # Q factors with positive diagonal of matrices differing by an
+    # upper-triangular factor, they are equal.
+    g = np.random.default_rng(32)
+    M = rand(g, 120, 90)
+    Q = rand(g, 90, 6)
+    two = oracle.gram_schmidt(M.T @ oracle.gram_schmidt(M @ Q))
+    fused = oracle.gram_schmidt(M.T @ (M @ Q))
+    assert np.abs(two - fused).max() <= 1e-12
+    assert np.abs(oracle.refresh(M, Q, 1) - two).max() == 0.0
+
+
+def test_refresh_decaying_spectrum_small_analogue():
+    # sigma_k = exp(-k/20): the first few directions converge in 8 rounds,
+    # the tail of a 32-wide block does not (gap e^{-1/20}).
+    A, V, s = W.decaying_spectrum_matrix(512, 384, seed=5, K=256)
+    A = A.astype(np.float64)
+    Q0 = W.gaussian_q0(384, 32, 5).astype(np.float64)
+    Q = oracle.refresh(A, Q0, 8)
+    _, _, Vt = np.linalg.svd(A)
+    # sin(theta(V_k, span Q)) for the leading k right singular vectors
+    assert oracle.principal_angle_sines(Q, Vt[:1].T)[0] <= 1e-9
+    assert oracle.principal_angle_sines(Q, Vt[:8].T)[0] <= 1e-7
+    assert oracle.principal_angle_sines(Q, Vt[:32].T)[0] > 0.1
+
+
+def test_principal_angles_closed_form():
+    # Two planes in R^3 at a known dihedral angle.
+    th = 0.3
+    A = np.array([[1.0, 0], [0, 1], [0, 0]])
+    B = np.array([[1.0, 0], [0, math.cos(th)], [0, math.sin(th)]])
+    s = oracle.principal_angle_sines(A, B)
+    np.testing.assert_allclose(s, [math.sin(th), 0.0], atol=1e-15)
+
+
+# ------------------------------------------- planted mistakes fail the pins
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    g = np.random.default_rng(41)
+    M = rand(g, 50, 40)
+    Q = rand(g, 40, 3)
+    low = rand(g, 50, 2) @ rand(g, 40, 2).T
+
+    # (a) Gram-Schmidt that forgets one projection term
+    def gs_missing_term(P):
+        P = np.asarray(P, float)
+        out = np.zeros_like(P)
+        for k in range(P.shape[1]):
+            v = P[:, k].copy()
+            for j in range(max(0, k - 1)):
+                v -= (out[:, j] @ v) * out[:, j]
+            out[:, k] = v / np.linalg.norm(v)
+        return out
+
+    assert oracle.orthonormality_error(gs_missing_term(rand(g, 50, 3))) > 1e-3
+
+    # (b) sign flipped normalisation fails the QR pin
+    Pm = rand(g, 30, 3)
+    assert np.abs(-oracle.gram_schmidt(Pm) - qr_positive(Pm)).max() > 0.1
+
+    # (c) Q computed from the raw P instead of P_hat breaks exact recovery
+    P = low @ Q[:, :3]
+    Qbad = low.T @ P
+    Ebad = low - oracle.gram_schmidt(P) @ Qbad.T
+    assert np.linalg.norm(Ebad) > 1e-3 * np.linalg.norm(low)
+
+    # (d) a transposed operand in the left multiply fails on a square case
+    Ms = rand(g, 40, 40)
+    good = oracle.compress_matrix(Ms, Q)
+    Ph = good.P_hat
+    assert np.abs(Ms @ Ph - good.Q).max() > 1e-3
+
+    # (e) forgetting to add E breaks the telescoping pin
+    wl = W.SmallMatrixWorkload()
+    plan = oracle.Plan([(256, 128)], 2)
+    st = oracle.init_state(plan, [wl.Q0])
+    orig = O.compress_matrix
+
+    def no_ef(Mx, Qw, hp=None, hq=None):
+        return orig(Mx - st.E[0], Qw, hp, hq)
+
+    monkeypatch.setattr(O, "compress_matrix", no_ef)
+    acc = np.zeros((256, 128))
+    gsum = np.zeros((256, 128))
+    for t in range(3):
+        res = O.step_set(plan, [wl.grads[t]], st)
+        acc += res.M_hat[0]
+        gsum += wl.grads[t]
+    assert np.linalg.norm(acc + st.E[0] - gsum) > 1e-3 * np.linalg.norm(gsum)
