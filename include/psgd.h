@@ -1,0 +1,241 @@
+/*
+ * psgd.h -- C ABI of the PowerSGD gradient-compression library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library compresses a whole model's gradient set with rank-r PowerSGD:
+ * for every gradient matrix M it adds the error-feedback memory, runs one
+ * warm-started power (subspace) iteration P = M Q, P_hat = GS(P),
+ * Q = M^T P_hat, and replaces the memory with the residual M - P_hat Q^T.
+ * Vectors and small tensors travel uncompressed.
+ *
+ * Sources (cited by page title and section):
+ *   [N152]  anthology-of-the-sota record, note 152 (PowerSGD): "Method",
+ *           "Concepts" ("Linearity of compressor", "Warm-start subspace
+ *           iteration", "Error feedback").
+ *   [GLOSS] inferensys glossary entry "PowerSGD": factorisation, error
+ *           feedback and momentum-compression paragraphs.
+ *   [PSGD+] "From PowerSGD to PowerSGD+: Low-Rank Gradient Compression for
+ *           Distributed Optimization with Convergence Guarantees", Abstract.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - All floating-point data is fp32.  Device pointers are plain HIP device
+ *   addresses, 16-byte aligned; the caller allocates and owns every device
+ *   buffer.  The library allocates no device memory.
+ * - Gradient-shaped buffers (grads, err, mom, mhat/out) are FLAT: one buffer
+ *   per role for the whole model, tensor t occupying `numel(t)` elements from
+ *   its plan offset (psgd_plan_tensor).  A matrix is stored row-major
+ *   (rows x cols); a 4-D conv weight is viewed as (out, in*kh*kw).
+ * - Packed factors: P_hat of compressed tensor t is stored column-major
+ *   (rank columns of `rows` floats) from p_off(t) in the P buffer; Q likewise
+ *   (rank columns of `cols` floats) from q_off(t) in the Q buffer.  The
+ *   pass-through values follow the P_hat region of the P buffer, so the
+ *   aggregation of P carries them.
+ * - Every device-side call is asynchronous on the given stream and performs
+ *   no host synchronisation; device faults surface at the caller's next
+ *   synchronisation.  Calls return a status and never throw; on failure,
+ *   psgd_last_error() gives a thread-local message.
+ * - Thread safety: a plan is immutable after creation and may be shared by
+ *   threads and streams, provided concurrent calls use distinct workspaces.
+ */
+#ifndef PSGD_H_
+#define PSGD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum psgd_status {
+  PSGD_OK = 0,
+  PSGD_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad shape, r < 1, ... */
+  PSGD_ERR_UNSUPPORTED = 2, /* rank above PSGD_MAX_RANK, unknown flag        */
+  PSGD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  PSGD_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed    */
+  PSGD_ERR_HOOK = 5         /* the aggregation hook returned non-zero        */
+} psgd_status_t;
+
+#define PSGD_MAX_RANK 64
+
+/* Tensor kinds ([N152] Method: bias vectors and small tensors are sent
+ * uncompressed). */
+#define PSGD_KIND_VECTOR 0     /* cols <= 1: a vector, passed through          */
+#define PSGD_KIND_PASSTHRU 1   /* matrix with r*(rows+cols) >= rows*cols       */
+#define PSGD_KIND_COMPRESSED 2 /* matrix compressed to rank r                  */
+
+/* Plan flags. */
+#define PSGD_FLAG_MOMENTUM 1u /* compress u <- beta*u + G instead of G ([GLOSS],
+                                 momentum paragraph); needs the `mom` buffer  */
+
+/* Pipeline stages, for psgd_timing_read. */
+#define PSGD_STAGE_EF_P 0      /* EF-add (+momentum) and P = M Q            */
+#define PSGD_STAGE_GS 1        /* Gram-Schmidt of P                          */
+#define PSGD_STAGE_MTP 2       /* partial Q = M^T P_hat over row blocks      */
+#define PSGD_STAGE_QREDUCE 3   /* fixed-order reduction of the partials      */
+#define PSGD_STAGE_RESIDUAL 4  /* E = M - P_hat Q^T (+ M_hat)                */
+#define PSGD_STAGE_PASSTHRU 5  /* pass-through packing / unpacking           */
+#define PSGD_STAGE_REFRESH 6   /* PowerSGD+ subspace refresh                 */
+#define PSGD_NSTAGES 7
+
+typedef struct psgd_plan* psgd_plan_t;
+
+/* Sizes derived from a plan.  Element counts are fp32 elements. */
+typedef struct psgd_plan_info {
+  int32_t ntensors;
+  int32_t ncompressed;
+  int32_t rank;
+  uint32_t flags;
+  size_t flat_elems;     /* elements each flat buffer must hold               */
+  size_t p_elems;        /* P_hat region of the P buffer (with padding)       */
+  size_t passthru_elems; /* pass-through values after the P_hat region        */
+  size_t p_buffer_elems; /* p_elems + passthru_elems: size of the P buffer    */
+  size_t q_elems;        /* Q buffer (with padding)                           */
+  size_t payload_elems;  /* floats sent per step: sum r(m+n) + pass-through   */
+  size_t dense_elems;    /* sum m*n over compressed tensors                   */
+  size_t workspace_bytes;/* device workspace compress/decompress/refresh need */
+} psgd_plan_info_t;
+
+/*
+ * psgd_plan_create -- describe a model's gradient set.  Host only: touches no
+ * device and can run on a machine without a GPU.
+ *
+ *   ntensors   number of tensors (>= 0)
+ *   rows,cols  per tensor, the row-major matrix view: rows = dim0,
+ *              cols = product of the remaining dims (cols <= 1 for vectors,
+ *              then `rows` is the length).  Every size must be >= 1.
+ *   offsets    nullable.  Element offset of each tensor in the flat buffers.
+ *              NULL: the plan packs the tensors in order, each start aligned
+ *              to 64 elements.  Caller offsets must be >= 0 and ranges must
+ *              not overlap; any alignment is accepted (unaligned rows use
+ *              narrower loads).
+ *   rank       r, 1 <= r <= PSGD_MAX_RANK.
+ *   flags      0 or PSGD_FLAG_MOMENTUM.
+ *   beta       momentum coefficient (used only with PSGD_FLAG_MOMENTUM).
+ *   out        receives the plan; release it with psgd_plan_destroy.
+ *
+ * Classification ([N152] Method; the size rule is this library's reading of
+ * "small tensors"): a matrix is compressed iff r*(rows+cols) < rows*cols.
+ */
+psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows, const int64_t* cols,
+                               const int64_t* offsets, int32_t rank, uint32_t flags, float beta,
+                               psgd_plan_t* out);
+
+/* Releases the plan.  Only after every call that used it has completed on the
+ * device (the plan owns the host copy of the tables psgd_workspace_init
+ * uploads, and the timing events). */
+void psgd_plan_destroy(psgd_plan_t plan);
+
+/* Sizes of the plan's buffers; host only. */
+psgd_status_t psgd_plan_get_info(psgd_plan_t plan, psgd_plan_info_t* info);
+
+/* Where tensor `tensor` lives: kind (PSGD_KIND_*), flat element offset,
+ * P offset (P_hat start for compressed tensors; start of its values in the
+ * pass-through region for others) and Q offset (-1 if not compressed).  Host
+ * only.  Any output pointer may be NULL. */
+psgd_status_t psgd_plan_tensor(psgd_plan_t plan, int32_t tensor, int32_t* kind, int64_t* flat_off,
+                               int64_t* p_off, int64_t* q_off);
+
+/*
+ * psgd_workspace_init -- write the plan's device tables (tensor descriptors,
+ * tile lists) into the first part of `workspace`, a caller-owned device buffer
+ * of at least info.workspace_bytes, 256-byte aligned.  Must be called once per
+ * (plan, workspace) pair before any compress / decompress / refresh that uses
+ * the pair; the caller must not write to the workspace afterwards.  The rest
+ * of the workspace is scratch that every call overwrites.  Asynchronous on
+ * `stream`.
+ */
+psgd_status_t psgd_workspace_init(psgd_plan_t plan, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * Aggregation hook: called on the host, in stream order, with a device buffer
+ * of `count` floats that every worker must replace by its mean over workers
+ * (all-reduce-mean).  It must enqueue its work on `stream` (or make the stream
+ * wait for it) and return 0, or return non-zero to abort the call.  Because
+ * the compressor is linear ([N152] Concepts, "Linearity of compressor"),
+ * averaging P and then Q equals compressing the averaged gradient.  A NULL
+ * hook is the single-worker identity.
+ */
+typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void* user);
+
+/*
+ * psgd_compress -- one PowerSGD step over the whole set ([N152] Method; error
+ * feedback per [GLOSS] and [N152] Concepts, "Error feedback").
+ *
+ *   grads  flat, read-only: the stochastic gradients G.
+ *   err    flat, in/out: error memory E of compressed tensors (zero at the
+ *          first step).  On return: the new residual M - P_hat Q^T.  While the
+ *          call runs it holds M = X + E_old; if the call fails after the first
+ *          pass (a hook error or a launch failure) it is left holding M.
+ *   mom    flat, in/out momentum u (all tensors), required iff the plan has
+ *          PSGD_FLAG_MOMENTUM (then X = u <- beta*u + G; else X = G), else NULL.
+ *   q      packed Q buffer: on entry the warm start (the previous step's Q, or a
+ *          random start at the first step); on return the new Q, which is also
+ *          the next step's warm start ([N152] Concepts, "Warm-start subspace
+ *          iteration").
+ *   p      packed P buffer (info.p_buffer_elems): receives P_hat followed by
+ *          the pass-through values.
+ *   mhat   nullable flat buffer: if given, receives the decompressed gradient
+ *          P_hat Q^T for compressed tensors and the aggregated values of the
+ *          pass-through tensors (a fused psgd_decompress).  It may alias
+ *          `grads` (then G is overwritten by the update) but no other buffer.
+ *   hook   nullable aggregation hook, called on (p, p_buffer_elems) after P is
+ *          formed and on (q, q_elems) after Q is formed.
+ *   workspace, workspace_bytes   initialised workspace (psgd_workspace_init).
+ *
+ * Errors: PSGD_ERR_INVALID_ARG for null or not 16-byte aligned buffers, a
+ * missing or unexpected `mom`; PSGD_ERR_WORKSPACE; PSGD_ERR_HOOK if a hook
+ * returns non-zero (no later stage is enqueued); PSGD_ERR_HIP.
+ */
+psgd_status_t psgd_compress(psgd_plan_t plan, const float* grads, float* err, float* mom, float* q,
+                            float* p, float* mhat, psgd_reduce_fn hook, void* user, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * psgd_decompress -- reconstruct G ~ P_hat Q^T ([GLOSS], factorisation
+ * paragraph) for every compressed tensor and copy the pass-through values
+ * from the P buffer, into the flat buffer `out` (may alias the gradients).
+ */
+psgd_status_t psgd_decompress(psgd_plan_t plan, const float* p, const float* q, float* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * psgd_refresh -- PowerSGD+ subspace re-alignment ([PSGD+] Abstract), read as
+ * `iters` rounds of block power iteration with orthonormalisation,
+ * Q <- GS(M^T GS(M Q)), on compressed tensor `tensor` of the flat buffer `m`
+ * (the compressor input), updating that tensor's columns of the packed Q
+ * buffer in place.  On return its Q has orthonormal columns.
+ */
+psgd_status_t psgd_refresh(psgd_plan_t plan, int32_t tensor, const float* m, float* q, int32_t iters,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-stage timing with HIP events recorded on the call's stream.  While
+ * enabled, every compress / decompress / refresh call records one event pair
+ * per stage it runs.  psgd_timing_read waits for the recorded events, adds
+ * the elapsed milliseconds per stage into ms[PSGD_NSTAGES] (and the number of
+ * launches per stage into launches[], nullable), and clears the record.
+ */
+psgd_status_t psgd_timing_enable(psgd_plan_t plan, int32_t enable);
+psgd_status_t psgd_timing_read(psgd_plan_t plan, double* ms, int64_t* launches);
+
+/* A plain device copy dst[i] = src[i], i < n, with 16-byte accesses (n a
+ * multiple of 4, both pointers 16-byte aligned): the bandwidth ceiling and
+ * the byte-counter calibration kernel. */
+psgd_status_t psgd_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);
+
+/* Thread-local message describing the last failure on this thread. */
+const char* psgd_last_error(void);
+
+/* Library version string. */
+const char* psgd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSGD_H_ */

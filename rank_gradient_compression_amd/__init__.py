@@ -1,0 +1,13 @@
+"""PowerSGD gradient compression for AMD Instinct MI355X (gfx950).
+
+The compute path is libpsgd.so (hand-written HIP kernels behind the C ABI of
+include/psgd.h); `binding` exposes it with the same names, and `torch_api`
+holds a thin buffer-owning convenience layer over PyTorch device memory.
+"""
+from . import binding  # noqa: F401  (loads libpsgd.so; raises if it is not built)
+from .binding import (PSGD_FLAG_MOMENTUM, PSGD_KIND_COMPRESSED, PSGD_KIND_PASSTHRU, PSGD_KIND_VECTOR,  # noqa: F401
+                      PsgdError, psgd_compress, psgd_decompress, psgd_last_error, psgd_plan_create,
+                      psgd_plan_destroy, psgd_plan_get_info, psgd_plan_tensor, psgd_refresh, psgd_stream_copy,
+                      psgd_timing_enable, psgd_timing_read, psgd_version, psgd_workspace_init)
+
+__all__ = [n for n in dir() if n.startswith("psgd_") or n.startswith("PSGD_")] + ["PsgdError", "binding"]

@@ -1,0 +1,206 @@
+"""ctypes binding of libpsgd.so: the C ABI of include/psgd.h, same names,
+argument marshalling only.  Device pointers are passed as Python ints (for
+example `tensor.data_ptr()`), streams as raw `hipStream_t` handles (for example
+`torch.cuda.current_stream().cuda_stream`).
+
+Importing this module loads the library; if it has not been built the import
+fails loudly -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Callable, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpsgd.so")
+
+PSGD_OK = 0
+PSGD_ERR_INVALID_ARG = 1
+PSGD_ERR_UNSUPPORTED = 2
+PSGD_ERR_WORKSPACE = 3
+PSGD_ERR_HIP = 4
+PSGD_ERR_HOOK = 5
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP", 5: "HOOK"}
+
+PSGD_MAX_RANK = 64
+PSGD_KIND_VECTOR = 0
+PSGD_KIND_PASSTHRU = 1
+PSGD_KIND_COMPRESSED = 2
+PSGD_FLAG_MOMENTUM = 1
+
+PSGD_STAGE_EF_P = 0
+PSGD_STAGE_GS = 1
+PSGD_STAGE_MTP = 2
+PSGD_STAGE_QREDUCE = 3
+PSGD_STAGE_RESIDUAL = 4
+PSGD_STAGE_PASSTHRU = 5
+PSGD_STAGE_REFRESH = 6
+PSGD_NSTAGES = 7
+STAGE_NAMES = ["ef_p", "gs", "mtp", "qreduce", "residual", "passthru", "refresh"]
+
+# Every symbol include/psgd.h declares.
+EXPORTED = [
+    "psgd_plan_create", "psgd_plan_destroy", "psgd_plan_get_info", "psgd_plan_tensor",
+    "psgd_workspace_init", "psgd_compress", "psgd_decompress", "psgd_refresh",
+    "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy", "psgd_last_error", "psgd_version",
+]
+
+
+class PsgdError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class psgd_plan_info_t(ctypes.Structure):
+    _fields_ = [
+        ("ntensors", ctypes.c_int32), ("ncompressed", ctypes.c_int32), ("rank", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("flat_elems", ctypes.c_size_t), ("p_elems", ctypes.c_size_t),
+        ("passthru_elems", ctypes.c_size_t), ("p_buffer_elems", ctypes.c_size_t), ("q_elems", ctypes.c_size_t),
+        ("payload_elems", ctypes.c_size_t), ("dense_elems", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+psgd_reduce_fn = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+
+# libpsgd.so needs the HIP runtime by soname (libamdhip64.so.7).  PyTorch for
+# ROCm ships its own copy; loading PyTorch first makes the soname resolve to
+# that copy, so that both share one runtime (and PyTorch's streams are valid
+# handles here).
+try:
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - plain C ABI use without PyTorch
+    pass
+lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({l.split()[-1] for l in f if "libamdhip64" in l and "/" in l})
+    except OSError:  # pragma: no cover
+        return []
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process (" + ", ".join(_hip_runtimes()) + "): import "
+                      "rank_gradient_compression_amd before anything that loads another libamdhip64")
+
+_vp = ctypes.c_void_p
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+lib.psgd_plan_create.argtypes = [ctypes.c_int32, _i64p, _i64p, _i64p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float,
+                                 ctypes.POINTER(_vp)]
+lib.psgd_plan_destroy.argtypes = [_vp]
+lib.psgd_plan_destroy.restype = None
+lib.psgd_plan_get_info.argtypes = [_vp, ctypes.POINTER(psgd_plan_info_t)]
+lib.psgd_plan_tensor.argtypes = [_vp, ctypes.c_int32, _i32p, _i64p, _i64p, _i64p]
+lib.psgd_workspace_init.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+lib.psgd_compress.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, psgd_reduce_fn, _vp, _vp, ctypes.c_size_t, _vp]
+lib.psgd_decompress.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+lib.psgd_refresh.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
+lib.psgd_timing_enable.argtypes = [_vp, ctypes.c_int32]
+lib.psgd_timing_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
+lib.psgd_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+lib.psgd_last_error.restype = ctypes.c_char_p
+lib.psgd_version.restype = ctypes.c_char_p
+for _f in ["psgd_plan_create", "psgd_plan_get_info", "psgd_plan_tensor", "psgd_workspace_init", "psgd_compress",
+           "psgd_decompress", "psgd_refresh", "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy"]:
+    getattr(lib, _f).restype = ctypes.c_int
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PSGD_OK:
+        raise PsgdError(fn, status, lib.psgd_last_error().decode(errors="replace"))
+
+
+def _arr64(xs: Optional[Sequence[int]]):
+    if xs is None:
+        return None
+    return (ctypes.c_int64 * len(xs))(*[int(x) for x in xs])
+
+
+def psgd_last_error() -> str:
+    return lib.psgd_last_error().decode(errors="replace")
+
+
+def psgd_version() -> str:
+    return lib.psgd_version().decode()
+
+
+def psgd_plan_create(rows: Sequence[int], cols: Sequence[int], rank: int, flags: int = 0, beta: float = 0.0,
+                     offsets: Optional[Sequence[int]] = None) -> int:
+    if len(rows) != len(cols) or (offsets is not None and len(offsets) != len(rows)):
+        raise ValueError("rows, cols and offsets must have the same length")
+    out = _vp()
+    st = lib.psgd_plan_create(len(rows), _arr64(rows), _arr64(cols), _arr64(offsets), rank, flags, beta,
+                              ctypes.byref(out))
+    _check("psgd_plan_create", st)
+    return out.value
+
+
+def psgd_plan_destroy(plan: int) -> None:
+    lib.psgd_plan_destroy(plan)
+
+
+def psgd_plan_get_info(plan: int) -> dict:
+    info = psgd_plan_info_t()
+    _check("psgd_plan_get_info", lib.psgd_plan_get_info(plan, ctypes.byref(info)))
+    return info.as_dict()
+
+
+def psgd_plan_tensor(plan: int, tensor: int):
+    kind = ctypes.c_int32()
+    off, poff, qoff = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("psgd_plan_tensor", lib.psgd_plan_tensor(plan, tensor, ctypes.byref(kind), ctypes.byref(off),
+                                                    ctypes.byref(poff), ctypes.byref(qoff)))
+    return kind.value, off.value, poff.value, qoff.value
+
+
+def psgd_workspace_init(plan: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+    _check("psgd_workspace_init", lib.psgd_workspace_init(plan, workspace, workspace_bytes, stream))
+
+
+def make_hook(fn: Callable[[int, int, int], int]):
+    """Wraps fn(buf_ptr, count, stream) -> int as a psgd_reduce_fn.  Keep the
+    returned object alive while the library may call it."""
+    return psgd_reduce_fn(lambda buf, count, stream, user: int(fn(buf or 0, count, stream or 0)))
+
+
+def psgd_compress(plan: int, grads: int, err: int, mom: int, q: int, p: int, mhat: int, hook, workspace: int,
+                  workspace_bytes: int, stream: int = 0) -> None:
+    h = hook if hook is not None else psgd_reduce_fn()
+    _check("psgd_compress", lib.psgd_compress(plan, grads, err or None, mom or None, q or None, p, mhat or None, h,
+                                              None, workspace, workspace_bytes, stream))
+
+
+def psgd_decompress(plan: int, p: int, q: int, out: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+    _check("psgd_decompress", lib.psgd_decompress(plan, p, q or None, out, workspace, workspace_bytes, stream))
+
+
+def psgd_refresh(plan: int, tensor: int, m: int, q: int, iters: int, workspace: int, workspace_bytes: int,
+                 stream: int = 0) -> None:
+    _check("psgd_refresh", lib.psgd_refresh(plan, tensor, m, q, iters, workspace, workspace_bytes, stream))
+
+
+def psgd_timing_enable(plan: int, enable: bool) -> None:
+    _check("psgd_timing_enable", lib.psgd_timing_enable(plan, 1 if enable else 0))
+
+
+def psgd_timing_read(plan: int):
+    ms = (ctypes.c_double * PSGD_NSTAGES)()
+    n = (ctypes.c_int64 * PSGD_NSTAGES)()
+    _check("psgd_timing_read", lib.psgd_timing_read(plan, ms, n))
+    return list(ms), list(n)
+
+
+def psgd_stream_copy(dst: int, src: int, n: int, stream: int = 0) -> None:
+    _check("psgd_stream_copy", lib.psgd_stream_copy(dst, src, n, stream))

@@ -1,0 +1,68 @@
+"""Builds libpsgd.so, the HIP library of this package, for gfx950.
+
+Each source is compiled to an object under _build/ (in parallel), then linked
+into rank_gradient_compression_amd/libpsgd.so.  Every call recompiles.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpsgd.so")
+
+SOURCES = ["plan.cpp", "api.hip", "kernels_valu.hip", "kernels_mfma.hip"]
+
+# Packed fp32 instructions are disabled for all device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libpsgd.so")
+    return exe
+
+
+def _compile(src: str, verbose: bool) -> str:
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = [hipcc(), "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+           "-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
+    if src.endswith(".hip"):
+        cmd[1:1] = ["--offload-arch=gfx950", "-x", "hip"] + DEVICE_FLAGS
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{res.stdout}\n{res.stderr}")
+    noisy = [l for l in res.stderr.splitlines() if l.strip() and "packed-fp32-ops" not in l]
+    if verbose and noisy:
+        print("\n".join(noisy), file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    with ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking libpsgd.so failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,299 @@
+// C ABI entry points that touch the device: workspace set-up, the PowerSGD
+// compression step, decompression, refresh, timing and the copy kernel.
+//
+// The step follows the "Method" section of the anthology note on PowerSGD
+// (note 152): P = M Q, all-reduce P, orthogonalise, Q = M^T P_hat, all-reduce
+// Q; the all-reduces are the caller's aggregation hook.  Every call only
+// enqueues work on the caller's stream: no host synchronisation and no
+// device allocation.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "psgd_internal.h"
+#include "psgd_kernels.h"
+
+namespace psgd {
+
+// -------------------------------------------------------------------- timing
+
+struct TimingRecord {
+  int stage;
+  hipEvent_t start, stop;
+};
+
+struct TimingState {
+  bool enabled = false;
+  std::vector<TimingRecord> records;
+  std::vector<hipEvent_t> pool;
+};
+
+static hipEvent_t take_event(TimingState* t) {
+  if (!t->pool.empty()) {
+    hipEvent_t e = t->pool.back();
+    t->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records events around one stage when timing is enabled.
+class StageTimer {
+ public:
+  StageTimer(psgd_plan* p, int stage, hipStream_t s) : p_(p), stage_(stage), s_(s) {
+    if (!p_->timing || !p_->timing->enabled) return;
+    std::lock_guard<std::mutex> lk(p_->timing_mu);
+    start_ = take_event(p_->timing);
+    stop_ = take_event(p_->timing);
+    if (start_ && stop_) (void)hipEventRecord(start_, s_);
+  }
+  ~StageTimer() {
+    if (!start_ || !stop_) return;
+    (void)hipEventRecord(stop_, s_);
+    std::lock_guard<std::mutex> lk(p_->timing_mu);
+    p_->timing->records.push_back({stage_, start_, stop_});
+  }
+
+ private:
+  psgd_plan* p_;
+  int stage_;
+  hipStream_t s_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
+// ------------------------------------------------------------------ helpers
+
+// Buffers are accessed with 16-byte vector instructions from their base.
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static LaunchCtx make_ctx(const psgd_plan* p, void* ws, hipStream_t s) {
+  const WsHeader& h = p->hdr;
+  char* b = static_cast<char*>(ws);
+  LaunchCtx c{};
+  c.stream = s;
+  c.rank = p->rank;
+  c.nmat = h.nmat;
+  c.npass = h.npass;
+  c.wg_rows = h.wg_rows;
+  c.wg_mtp = h.wg_mtp;
+  c.wg_red = h.wg_red;
+  c.wg_pass = h.wg_pass;
+  c.mats = reinterpret_cast<const MatDesc*>(b + h.mat_off);
+  c.pass = reinterpret_cast<const PassDesc*>(b + h.pass_off);
+  c.rows_map = reinterpret_cast<const int32_t*>(b + h.rows_map_off);
+  c.mtp_map = reinterpret_cast<const int32_t*>(b + h.mtp_map_off);
+  c.red_map = reinterpret_cast<const int32_t*>(b + h.red_map_off);
+  c.pass_map = reinterpret_cast<const int32_t*>(b + h.pass_map_off);
+  c.part = reinterpret_cast<float*>(b + h.part_base);
+  c.gram = reinterpret_cast<double*>(b + h.gram_base);
+  c.rscr = reinterpret_cast<float*>(b + h.refresh_base);
+  return c;
+}
+
+static psgd_status_t check_ws(const psgd_plan* p, const void* ws, size_t bytes, const char* fn) {
+  if (!ws) {
+    set_error("%s: workspace is NULL", fn);
+    return PSGD_ERR_WORKSPACE;
+  }
+  if (((uintptr_t)ws & 255u) != 0) {
+    set_error("%s: workspace is not 256-byte aligned", fn);
+    return PSGD_ERR_WORKSPACE;
+  }
+  if (bytes < (size_t)p->hdr.total_bytes) {
+    set_error("%s: workspace of %zu bytes, the plan needs %lld", fn, bytes, (long long)p->hdr.total_bytes);
+    return PSGD_ERR_WORKSPACE;
+  }
+  return PSGD_OK;
+}
+
+static psgd_status_t hip_fail(hipError_t e, const char* what) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return PSGD_ERR_HIP;
+}
+
+#define PSGD_LAUNCH(stage, expr, what)                   \
+  do {                                                   \
+    StageTimer _t(p, stage, stream);                     \
+    const hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return hip_fail(_e, what);     \
+  } while (0)
+
+}  // namespace psgd
+
+using namespace psgd;
+
+extern "C" void psgd_plan_destroy(psgd_plan_t p) {
+  if (!p) return;
+  if (p->timing) {
+    for (auto& r : p->timing->records) {
+      (void)hipEventDestroy(r.start);
+      (void)hipEventDestroy(r.stop);
+    }
+    for (hipEvent_t e : p->timing->pool) (void)hipEventDestroy(e);
+    delete p->timing;
+  }
+  delete p;
+}
+
+extern "C" psgd_status_t psgd_workspace_init(psgd_plan_t p, void* ws, size_t bytes, hipStream_t stream) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_workspace_init: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (psgd_status_t s = check_ws(p, ws, bytes, "psgd_workspace_init")) return s;
+  if (p->tables.empty()) return PSGD_OK;
+  const hipError_t e = hipMemcpyAsync(ws, p->tables.data(), p->tables.size(), hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "psgd_workspace_init: table upload");
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const float* grads, float* err, float* mom, float* q, float* pbuf,
+                                       float* mhat, psgd_reduce_fn hook, void* user, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_compress: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  const bool momentum = (p->flags & PSGD_FLAG_MOMENTUM) != 0;
+  const bool any = p->ntensors > 0;
+  if (any && (!grads || !pbuf || (!p->mats.empty() && (!err || !q)))) {
+    set_error("psgd_compress: a required buffer is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (momentum && any && !mom) {
+    set_error("psgd_compress: the plan compresses momentum but mom is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (!momentum && mom) {
+    set_error("psgd_compress: mom given but the plan has no momentum flag");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (!aligned16(grads) || !aligned16(err) || !aligned16(mom) || !aligned16(q) || !aligned16(pbuf) ||
+      !aligned16(mhat)) {
+    set_error("psgd_compress: buffers must be 16-byte aligned");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (mhat && (mhat == err || mhat == mom)) {
+    set_error("psgd_compress: mhat may alias grads only");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (p->rank > kValuMaxRank) {
+    set_error("psgd_compress: rank %d not available in this build", p->rank);
+    return PSGD_ERR_UNSUPPORTED;
+  }
+  if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_compress")) return s;
+  if (!any) return PSGD_OK;
+
+  const LaunchCtx c = make_ctx(p, ws, stream);
+  float* U = momentum ? mom : nullptr;
+  const float beta = p->beta;
+
+  PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_pack(c, grads, U, beta, pbuf), "pass-through pack");
+  PSGD_LAUNCH(PSGD_STAGE_EF_P, launch_ef_p(c, grads, err, U, beta, q, pbuf), "EF-add + P = M Q");
+  if (hook && hook(pbuf, p->p_elems + p->pt_elems, stream, user) != 0) {
+    set_error("psgd_compress: aggregation hook failed on P");
+    return PSGD_ERR_HOOK;
+  }
+  PSGD_LAUNCH(PSGD_STAGE_GS, launch_orth(c, pbuf), "orthogonalise P");
+  PSGD_LAUNCH(PSGD_STAGE_MTP, launch_mtp(c, err, pbuf, q, c.part), "Q = M^T P_hat");
+  PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, c.part, q), "Q partial reduction");
+  if (hook && hook(q, p->q_elems, stream, user) != 0) {
+    set_error("psgd_compress: aggregation hook failed on Q");
+    return PSGD_ERR_HOOK;
+  }
+  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, launch_recon(c, err, q, pbuf, mhat, true), "residual E = M - P_hat Q^T");
+  if (mhat) PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat), "pass-through unpack");
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_decompress(psgd_plan_t p, const float* pbuf, const float* q, float* out, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_decompress: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (p->ntensors > 0 && (!pbuf || !out || (!p->mats.empty() && !q))) {
+    set_error("psgd_decompress: a required buffer is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (!aligned16(pbuf) || !aligned16(q) || !aligned16(out)) {
+    set_error("psgd_decompress: buffers must be 16-byte aligned");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (p->rank > kValuMaxRank) {
+    set_error("psgd_decompress: rank %d not available in this build", p->rank);
+    return PSGD_ERR_UNSUPPORTED;
+  }
+  if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_decompress")) return s;
+  if (p->ntensors == 0) return PSGD_OK;
+  const LaunchCtx c = make_ctx(p, ws, stream);
+  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, launch_recon(c, nullptr, q, pbuf, out, false), "decompress P_hat Q^T");
+  PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out), "pass-through unpack");
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_refresh(psgd_plan_t p, int32_t tensor, const float* m, float* q, int32_t iters, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  (void)p; (void)tensor; (void)m; (void)q; (void)iters; (void)ws; (void)ws_bytes; (void)stream;
+  set_error("psgd_refresh: not available in this build");
+  return PSGD_ERR_UNSUPPORTED;
+}
+
+extern "C" psgd_status_t psgd_timing_enable(psgd_plan_t p, int32_t enable) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_timing_enable: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lk(p->timing_mu);
+  if (!p->timing) p->timing = new TimingState();
+  p->timing->enabled = enable != 0;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_timing_read(psgd_plan_t p, double* ms, int64_t* launches) {
+  clear_error();
+  if (!p || !ms) {
+    set_error("psgd_timing_read: NULL argument");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < PSGD_NSTAGES; ++i) {
+    ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  std::lock_guard<std::mutex> lk(p->timing_mu);
+  if (!p->timing) return PSGD_OK;
+  psgd_status_t st = PSGD_OK;
+  for (TimingRecord& r : p->timing->records) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess && st == PSGD_OK) st = hip_fail(e, "psgd_timing_read");
+    ms[r.stage] += t;
+    if (launches) launches[r.stage] += 1;
+    p->timing->pool.push_back(r.start);
+    p->timing->pool.push_back(r.stop);
+  }
+  p->timing->records.clear();
+  return st;
+}
+
+extern "C" psgd_status_t psgd_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream) {
+  clear_error();
+  if (!dst || !src || (n & 3u) || ((uintptr_t)dst & 15u) || ((uintptr_t)src & 15u)) {
+    set_error("psgd_stream_copy: need 16-byte aligned pointers and n a multiple of 4");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  const hipError_t e = launch_stream_copy(dst, src, n, stream);
+  if (e != hipSuccess) return hip_fail(e, "psgd_stream_copy");
+  return PSGD_OK;
+}

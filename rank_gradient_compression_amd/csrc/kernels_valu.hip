@@ -1,0 +1,595 @@
+// Streaming kernels of the PowerSGD step for ranks up to 8 (gfx950, wave64).
+//
+// One PowerSGD step per gradient matrix, as the "Method" section of the
+// anthology note on PowerSGD (note 152) describes it: P = M Q with the
+// previous step's Q, aggregate P, orthogonalise P, Q = M^T P_hat, aggregate Q;
+// with error feedback (glossary entry "PowerSGD", error-feedback paragraph)
+// M = G + E before the products and E = M - P_hat Q^T after them.
+//
+// The work is bound by HBM traffic at these ranks (about 2r+1 flops per
+// 4-byte element per pass), so the kernels are organised around streaming
+// each gradient-sized array once per pass with 16-byte accesses:
+//   pass 1  read G, E (and u)  -> write M over E (and u), P = M Q      12 B/el
+//   pass 2  read M             -> Q = M^T P_hat (partials per row block) 4 B/el
+//   pass 3  read M             -> write E = M - P_hat Q^T (and M_hat)  8 B/el
+// Matrices of the whole model share one launch per pass; a per-workgroup
+// table maps each workgroup to its matrix.
+
+#include <hip/hip_runtime.h>
+
+#include "psgd_kernels.h"
+#include "psgd_tables.h"
+
+namespace psgd {
+
+// ---------------------------------------------------------------------------
+// Vector access helpers (VEC = 4, 2 or 1 consecutive floats)
+// ---------------------------------------------------------------------------
+
+template <int VEC>
+struct Vec {
+  float v[VEC];
+};
+
+template <int VEC>
+__device__ __forceinline__ Vec<VEC> ldv(const float* p) {
+  Vec<VEC> r;
+  if constexpr (VEC == 4) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    r.v[0] = t.x; r.v[1] = t.y; r.v[2] = t.z; r.v[3] = t.w;
+  } else if constexpr (VEC == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    r.v[0] = t.x; r.v[1] = t.y;
+  } else {
+    r.v[0] = *p;
+  }
+  return r;
+}
+
+template <int VEC>
+__device__ __forceinline__ void stv(float* p, const Vec<VEC>& a) {
+  if constexpr (VEC == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(a.v[0], a.v[1], a.v[2], a.v[3]);
+  } else if constexpr (VEC == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(a.v[0], a.v[1]);
+  } else {
+    *p = a.v[0];
+  }
+}
+
+// Sum of NV per-lane values over the 64 lanes of a wavefront, transposed: on
+// return lane l holds the total of value (l >> (6 - log2 NV)).  Each butterfly
+// step halves the values a lane carries, so the cost is about NV shuffles
+// instead of 6 NV.
+template <int NV>
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[NV], int lane) {
+  static_assert(NV >= 1 && NV <= 64 && (NV & (NV - 1)) == 0, "NV must be a power of two <= 64");
+  constexpr int LOG = NV >= 64 ? 6 : NV >= 32 ? 5 : NV >= 16 ? 4 : NV >= 8 ? 3 : NV >= 4 ? 2 : NV >= 2 ? 1 : 0;
+#pragma unroll
+  for (int s = 0; s < LOG; ++s) {
+    const int bit = 5 - s;
+    const int half = NV >> (s + 1);
+    const bool up = (lane >> bit) & 1;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = up ? v[i] : v[i + half];
+      const float keep = up ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, 1 << bit);
+    }
+  }
+  float x = v[0];
+#pragma unroll
+  for (int bit = 5 - LOG; bit >= 0; --bit) x += __shfl_xor(x, 1 << bit);
+  return x;
+}
+
+constexpr int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: EF-add (+ momentum) and P = M Q
+// ---------------------------------------------------------------------------
+
+// One wavefront: rows [row0, row0 + kWaveRows) of matrix d, all columns.  Each
+// lane keeps its VEC x R slice of Q in registers for the current column step
+// and reuses it across the wavefront's rows.
+template <int R, int VEC, bool MOM>
+__device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, const float* __restrict__ G,
+                                          float* __restrict__ E, float* __restrict__ U, float beta,
+                                          const float* __restrict__ Q, float* __restrict__ P) {
+  const int m = d.m, n = d.n;
+  const int nrows = min(kWaveRows, m - row0);
+  float acc[kWaveRows][R];
+#pragma unroll
+  for (int rr = 0; rr < kWaveRows; ++rr)
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[rr][k] = 0.f;
+
+  const float* q = Q + d.q_off;
+  const int64_t base = d.off + (int64_t)row0 * n;
+  for (int j = lane * VEC; j < n; j += 64 * VEC) {
+    Vec<VEC> qv[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) qv[k] = ldv<VEC>(q + (int64_t)k * n + j);
+    Vec<VEC> g[kWaveRows], e[kWaveRows];
+#pragma unroll
+    for (int rr = 0; rr < kWaveRows; ++rr) {
+      const int64_t idx = base + (int64_t)min(rr, nrows - 1) * n + j;
+      g[rr] = ldv<VEC>(G + idx);
+      e[rr] = ldv<VEC>(E + idx);
+    }
+    Vec<VEC> u[kWaveRows];
+    if constexpr (MOM) {
+#pragma unroll
+      for (int rr = 0; rr < kWaveRows; ++rr) u[rr] = ldv<VEC>(U + base + (int64_t)min(rr, nrows - 1) * n + j);
+    }
+#pragma unroll
+    for (int rr = 0; rr < kWaveRows; ++rr) {
+      if (rr < nrows) {
+        const int64_t idx = base + (int64_t)rr * n + j;
+        Vec<VEC> mv;
+        if constexpr (MOM) {
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) u[rr].v[c] = fmaf(beta, u[rr].v[c], g[rr].v[c]);
+          stv<VEC>(U + idx, u[rr]);
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) mv.v[c] = u[rr].v[c] + e[rr].v[c];
+        } else {
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) mv.v[c] = g[rr].v[c] + e[rr].v[c];
+        }
+        stv<VEC>(E + idx, mv);
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) acc[rr][k] = fmaf(mv.v[c], qv[k].v[c], acc[rr][k]);
+      }
+    }
+  }
+
+  constexpr int NV = pow2_at_least(kWaveRows * R);
+  float vals[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) vals[i] = i < kWaveRows * R ? acc[i / R][i % R] : 0.f;
+  const float tot = wave_transpose_sum<NV>(vals, lane);
+  constexpr int SHIFT = NV >= 64 ? 0 : NV >= 32 ? 1 : NV >= 16 ? 2 : NV >= 8 ? 3 : NV >= 4 ? 4 : NV >= 2 ? 5 : 6;
+  const int vi = lane >> SHIFT;
+  if ((lane & ((1 << SHIFT) - 1)) == 0 && vi < kWaveRows * R) {
+    const int rr = vi / R, k = vi % R;
+    if (rr < nrows) P[d.p_off + (int64_t)k * m + row0 + rr] = tot;
+  }
+}
+
+template <int R, bool MOM>
+__global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__ mats,
+                                                     const int32_t* __restrict__ map,
+                                                     const float* __restrict__ G, float* __restrict__ E,
+                                                     float* __restrict__ U, float beta,
+                                                     const float* __restrict__ Q, float* __restrict__ P) {
+  const int wg = blockIdx.x;
+  const MatDesc d = mats[map[wg]];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
+  if (row0 >= d.m) return;
+  if (d.vec == 4)
+    ef_p_wave<R, 4, MOM>(d, row0, lane, G, E, U, beta, Q, P);
+  else if (d.vec == 2)
+    ef_p_wave<R, 2, MOM>(d, row0, lane, G, E, U, beta, Q, P);
+  else
+    ef_p_wave<R, 1, MOM>(d, row0, lane, G, E, U, beta, Q, P);
+}
+
+// ---------------------------------------------------------------------------
+// Orthogonalisation of P: Gram-Schmidt carried out on the Gram matrix
+// ---------------------------------------------------------------------------
+//
+// Gram-Schmidt on the columns of P (m x r) in natural order with positive
+// normalisation yields P_hat = P T with T upper triangular.  In exact
+// arithmetic the coefficients follow from the Gram matrix A = P^T P alone:
+// for column k, the projections on the previous P_hat columns are
+// R_jk = T_j^T A e_k, the squared norm after projection is
+// A_kk - sum_j R_jk^2, and T_k = (e_k - sum_j R_jk T_j) / R_kk.  A is formed
+// in fp64 from the fp32 P (each product exact), so the cancellation in the
+// squared norm costs nothing at fp32 output precision and the 1e-4 relative
+// dependence threshold is decided reliably.  One workgroup per matrix: read P
+// once for A, once for P_hat = P T (evaluated in fp64, rounded to fp32).
+
+constexpr int kOrthThreads = 256;
+
+template <int R>
+__global__ __launch_bounds__(kOrthThreads) void k_orth(const MatDesc* __restrict__ mats, float* __restrict__ P,
+                                                       float zero_rel) {
+  constexpr int NG = R * (R + 1) / 2;
+  __shared__ double red[kOrthThreads / 64][NG];
+  __shared__ double T[R][R];
+  const MatDesc d = mats[blockIdx.x];
+  const int m = d.m;
+  float* p = P + d.p_off;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  double g[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) g[i] = 0.0;
+  for (int i = tid; i < m; i += kOrthThreads) {
+    double x[R];
+#pragma unroll
+    for (int a = 0; a < R; ++a) x[a] = (double)p[(int64_t)a * m + i];
+    int t = 0;
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = a; b < R; ++b) {
+        g[t] = fma(x[a], x[b], g[t]);
+        ++t;
+      }
+  }
+  // fixed-order reduction: butterfly within the wavefront, then waves in order
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    double v = g[i];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    g[i] = v;
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < NG; ++i) red[wave][i] = g[i];
+  __syncthreads();
+
+  if (tid == 0) {
+    double A[R][R];
+    int t = 0;
+    for (int a = 0; a < R; ++a)
+      for (int b = a; b < R; ++b) {
+        double s = 0.0;
+        for (int w = 0; w < kOrthThreads / 64; ++w) s += red[w][t];
+        A[a][b] = s;
+        A[b][a] = s;
+        ++t;
+      }
+    double Tl[R][R];
+    for (int a = 0; a < R; ++a)
+      for (int b = 0; b < R; ++b) Tl[a][b] = 0.0;
+    for (int k = 0; k < R; ++k) {
+      // A e_k projected on the previous columns: R_jk = T_j^T A e_k
+      double Rk[R];
+      double nv2 = A[k][k];
+      for (int j = 0; j < k; ++j) {
+        double s = 0.0;
+        for (int l = 0; l <= j; ++l) s = fma(Tl[l][j], A[l][k], s);
+        Rk[j] = s;
+        nv2 = fma(-s, s, nv2);
+      }
+      const double nu0 = sqrt(A[k][k]);
+      const double nv = nv2 > 0.0 ? sqrt(nv2) : 0.0;
+      if (!(nu0 > 0.0) || nv <= (double)zero_rel * nu0) continue;  // zero column
+      const double inv = 1.0 / nv;
+      for (int l = 0; l < k; ++l) {
+        double s = 0.0;
+        for (int j = l; j < k; ++j) s = fma(Rk[j], Tl[l][j], s);
+        Tl[l][k] = -s * inv;
+      }
+      Tl[k][k] = inv;
+    }
+    for (int a = 0; a < R; ++a)
+      for (int b = 0; b < R; ++b) T[a][b] = Tl[a][b];
+  }
+  __syncthreads();
+
+  for (int i = tid; i < m; i += kOrthThreads) {
+    double x[R];
+#pragma unroll
+    for (int a = 0; a < R; ++a) x[a] = (double)p[(int64_t)a * m + i];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      double s = 0.0;
+#pragma unroll
+      for (int a = 0; a <= k; ++a) s = fma(x[a], T[a][k], s);
+      p[(int64_t)k * m + i] = (float)s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: Q = M^T P_hat, partial sums per row block
+// ---------------------------------------------------------------------------
+
+// One wavefront: 64*VEC consecutive columns of one row block.  P_hat values
+// of a row are wavefront-uniform (scalar loads); each lane accumulates VEC x R
+// dot products over the block's rows.
+template <int R, int VEC>
+__device__ __forceinline__ void mtp_wave(const MatDesc& d, int rb, int j, const float* __restrict__ M,
+                                         const float* __restrict__ Ph, float* __restrict__ Q,
+                                         float* __restrict__ part) {
+  const int m = d.m, n = d.n;
+  const int i0 = rb * d.rb_rows;
+  const int i1 = min(m, i0 + d.rb_rows);
+  const float* ph = Ph + d.p_off;
+  const float* mp = M + d.off + j;
+  float acc[VEC][R];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c)
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[c][k] = 0.f;
+
+  constexpr int U = 8;
+  int i = i0;
+  for (; i + U <= i1; i += U) {
+    Vec<VEC> x[U];
+#pragma unroll
+    for (int t = 0; t < U; ++t) x[t] = ldv<VEC>(mp + (int64_t)(i + t) * n);
+#pragma unroll
+    for (int t = 0; t < U; ++t)
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const float w = ph[(int64_t)k * m + i + t];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) acc[c][k] = fmaf(x[t].v[c], w, acc[c][k]);
+      }
+  }
+  for (; i < i1; ++i) {
+    const Vec<VEC> x = ldv<VEC>(mp + (int64_t)i * n);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const float w = ph[(int64_t)k * m + i];
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) acc[c][k] = fmaf(x.v[c], w, acc[c][k]);
+    }
+  }
+  float* out = d.nrb > 1 ? part + d.part_off + (int64_t)rb * R * n : Q + d.q_off;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    Vec<VEC> o;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) o.v[c] = acc[c][k];
+    stv<VEC>(out + (int64_t)k * n + j, o);
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(kWGThreads) void k_mtp(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
+                                                    const float* __restrict__ M, const float* __restrict__ Ph,
+                                                    float* __restrict__ Q, float* __restrict__ part) {
+  const int wg = blockIdx.x;
+  const MatDesc d = mats[map[wg]];
+  const int local = wg - d.wg_mtp0;
+  const int rb = local / d.ncb, cb = local - rb * d.ncb;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = (cb * kMtpWaves + wave) * 64 * d.vec + lane * d.vec;
+  if (j >= d.n) return;
+  if (d.vec == 4)
+    mtp_wave<R, 4>(d, rb, j, M, Ph, Q, part);
+  else if (d.vec == 2)
+    mtp_wave<R, 2>(d, rb, j, M, Ph, Q, part);
+  else
+    mtp_wave<R, 1>(d, rb, j, M, Ph, Q, part);
+}
+
+// Fixed-order sum of the row-block partials: Q[k*n + j] = sum_b part_b[k*n + j].
+__global__ __launch_bounds__(kRedCols) void k_qreduce(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
+                                                      int R, const float* __restrict__ part, float* __restrict__ Q) {
+  const int wg = blockIdx.x;
+  const MatDesc d = mats[map[wg]];
+  const int64_t len = (int64_t)R * d.n;
+  const int64_t idx = (int64_t)(wg - d.wg_red0) * kRedCols + threadIdx.x;
+  if (idx >= len) return;
+  const float* src = part + d.part_off + idx;
+  float s = 0.f;
+  for (int b = 0; b < d.nrb; ++b) s += src[(int64_t)b * len];
+  Q[d.q_off + idx] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: residual E = M - P_hat Q^T (+ M_hat); decompression
+// ---------------------------------------------------------------------------
+
+template <int R, int VEC, bool READ_M, bool WRITE_E, bool WRITE_MHAT>
+__device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane, float* __restrict__ E,
+                                           const float* __restrict__ Q, const float* __restrict__ Ph,
+                                           float* __restrict__ Mhat) {
+  const int m = d.m, n = d.n;
+  const int nrows = min(kWaveRows, m - row0);
+  float ph[kWaveRows][R];
+#pragma unroll
+  for (int rr = 0; rr < kWaveRows; ++rr)
+#pragma unroll
+    for (int k = 0; k < R; ++k) ph[rr][k] = Ph[d.p_off + (int64_t)k * m + row0 + min(rr, nrows - 1)];
+  const float* q = Q + d.q_off;
+  const int64_t base = d.off + (int64_t)row0 * n;
+  for (int j = lane * VEC; j < n; j += 64 * VEC) {
+    Vec<VEC> qv[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) qv[k] = ldv<VEC>(q + (int64_t)k * n + j);
+    Vec<VEC> x[kWaveRows];
+    if constexpr (READ_M) {
+#pragma unroll
+      for (int rr = 0; rr < kWaveRows; ++rr) x[rr] = ldv<VEC>(E + base + (int64_t)min(rr, nrows - 1) * n + j);
+    }
+#pragma unroll
+    for (int rr = 0; rr < kWaveRows; ++rr) {
+      if (rr < nrows) {
+        const int64_t idx = base + (int64_t)rr * n + j;
+        Vec<VEC> mh;
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+          float s = ph[rr][0] * qv[0].v[c];
+#pragma unroll
+          for (int k = 1; k < R; ++k) s = fmaf(ph[rr][k], qv[k].v[c], s);
+          mh.v[c] = s;
+        }
+        if constexpr (WRITE_E) {
+          Vec<VEC> e;
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) e.v[c] = x[rr].v[c] - mh.v[c];
+          stv<VEC>(E + idx, e);
+        }
+        if constexpr (WRITE_MHAT) stv<VEC>(Mhat + idx, mh);
+      }
+    }
+  }
+}
+
+template <int R, bool READ_M, bool WRITE_E, bool WRITE_MHAT>
+__global__ __launch_bounds__(kWGThreads) void k_recon(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
+                                                      float* __restrict__ E, const float* __restrict__ Q,
+                                                      const float* __restrict__ Ph, float* __restrict__ Mhat) {
+  const int wg = blockIdx.x;
+  const MatDesc d = mats[map[wg]];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
+  if (row0 >= d.m) return;
+  if (d.vec == 4)
+    recon_wave<R, 4, READ_M, WRITE_E, WRITE_MHAT>(d, row0, lane, E, Q, Ph, Mhat);
+  else if (d.vec == 2)
+    recon_wave<R, 2, READ_M, WRITE_E, WRITE_MHAT>(d, row0, lane, E, Q, Ph, Mhat);
+  else
+    recon_wave<R, 1, READ_M, WRITE_E, WRITE_MHAT>(d, row0, lane, E, Q, Ph, Mhat);
+}
+
+// ---------------------------------------------------------------------------
+// Pass-through tensors
+// ---------------------------------------------------------------------------
+
+template <bool MOM>
+__global__ __launch_bounds__(256) void k_pass_pack(const PassDesc* __restrict__ pass, const int32_t* __restrict__ map,
+                                                   const float* __restrict__ G, float* __restrict__ U, float beta,
+                                                   float* __restrict__ Pbuf) {
+  const int wg = blockIdx.x;
+  const PassDesc pd = pass[map[wg]];
+  const int64_t c0 = (int64_t)(wg - pd.wg0) * kPassChunk;
+  const int64_t c1 = c0 + kPassChunk < pd.len ? c0 + kPassChunk : pd.len;
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
+    float x = G[pd.off + i];
+    if constexpr (MOM) {
+      x = fmaf(beta, U[pd.off + i], x);
+      U[pd.off + i] = x;
+    }
+    Pbuf[pd.p_off + i] = x;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pass_unpack(const PassDesc* __restrict__ pass, const int32_t* __restrict__ map,
+                                                     const float* __restrict__ Pbuf, float* __restrict__ out) {
+  const int wg = blockIdx.x;
+  const PassDesc pd = pass[map[wg]];
+  const int64_t c0 = (int64_t)(wg - pd.wg0) * kPassChunk;
+  const int64_t c1 = c0 + kPassChunk < pd.len ? c0 + kPassChunk : pd.len;
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) out[pd.off + i] = Pbuf[pd.p_off + i];
+}
+
+// Plain 16-byte copy: the bandwidth ceiling and counter calibration.
+__global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, const float4* __restrict__ src,
+                                                     int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers
+// ---------------------------------------------------------------------------
+
+template <int R>
+static hipError_t launch_ef_p_r(const LaunchCtx& c, const float* G, float* E, float* U, float beta, const float* Q,
+                                float* P) {
+  if (c.wg_rows == 0) return hipSuccess;
+  if (U)
+    hipLaunchKernelGGL((k_ef_p<R, true>), dim3(c.wg_rows), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map, G, E,
+                       U, beta, Q, P);
+  else
+    hipLaunchKernelGGL((k_ef_p<R, false>), dim3(c.wg_rows), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map, G, E,
+                       U, beta, Q, P);
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_orth_r(const LaunchCtx& c, float* P) {
+  if (c.nmat == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_orth<R>), dim3(c.nmat), dim3(kOrthThreads), 0, c.stream, c.mats, P, kZeroColumnRel);
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_mtp_r(const LaunchCtx& c, const float* M, const float* Ph, float* Q, float* part) {
+  if (c.wg_mtp == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_mtp<R>), dim3(c.wg_mtp), dim3(kWGThreads), 0, c.stream, c.mats, c.mtp_map, M, Ph, Q, part);
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_recon_r(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
+                                 bool residual) {
+  if (c.wg_rows == 0) return hipSuccess;
+  const dim3 g(c.wg_rows), b(kWGThreads);
+  if (residual && Mhat)
+    hipLaunchKernelGGL((k_recon<R, true, true, true>), g, b, 0, c.stream, c.mats, c.rows_map, E, Q, Ph, Mhat);
+  else if (residual)
+    hipLaunchKernelGGL((k_recon<R, true, true, false>), g, b, 0, c.stream, c.mats, c.rows_map, E, Q, Ph, Mhat);
+  else
+    hipLaunchKernelGGL((k_recon<R, false, false, true>), g, b, 0, c.stream, c.mats, c.rows_map, E, Q, Ph, Mhat);
+  return hipGetLastError();
+}
+
+#define PSGD_RANK_SWITCH(R_, CALL)  \
+  switch (R_) {                     \
+    case 1: { constexpr int RR = 1; return CALL; } \
+    case 2: { constexpr int RR = 2; return CALL; } \
+    case 3: { constexpr int RR = 3; return CALL; } \
+    case 4: { constexpr int RR = 4; return CALL; } \
+    case 5: { constexpr int RR = 5; return CALL; } \
+    case 6: { constexpr int RR = 6; return CALL; } \
+    case 7: { constexpr int RR = 7; return CALL; } \
+    case 8: { constexpr int RR = 8; return CALL; } \
+    default: return hipErrorInvalidValue;           \
+  }
+
+hipError_t launch_ef_p(const LaunchCtx& c, const float* G, float* E, float* U, float beta, const float* Q, float* P) {
+  PSGD_RANK_SWITCH(c.rank, launch_ef_p_r<RR>(c, G, E, U, beta, Q, P));
+}
+
+hipError_t launch_orth(const LaunchCtx& c, float* P) { PSGD_RANK_SWITCH(c.rank, launch_orth_r<RR>(c, P)); }
+
+hipError_t launch_mtp(const LaunchCtx& c, const float* M, const float* Ph, float* Q, float* part) {
+  PSGD_RANK_SWITCH(c.rank, launch_mtp_r<RR>(c, M, Ph, Q, part));
+}
+
+hipError_t launch_qreduce(const LaunchCtx& c, const float* part, float* Q) {
+  if (c.wg_red == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_qreduce, dim3(c.wg_red), dim3(kRedCols), 0, c.stream, c.mats, c.red_map, c.rank, part, Q);
+  return hipGetLastError();
+}
+
+hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat, bool residual) {
+  PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual));
+}
+
+hipError_t launch_pass_pack(const LaunchCtx& c, const float* G, float* U, float beta, float* Pbuf) {
+  if (c.wg_pass == 0) return hipSuccess;
+  if (U)
+    hipLaunchKernelGGL((k_pass_pack<true>), dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, G, U, beta,
+                       Pbuf);
+  else
+    hipLaunchKernelGGL((k_pass_pack<false>), dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, G, U, beta,
+                       Pbuf);
+  return hipGetLastError();
+}
+
+hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out) {
+  if (c.wg_pass == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pass_unpack, dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, Pbuf, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream) {
+  const int64_t n4 = (int64_t)(n / 4);
+  if (n4 == 0) return hipSuccess;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float4*>(dst),
+                     reinterpret_cast<const float4*>(src), n4);
+  return hipGetLastError();
+}
+
+}  // namespace psgd

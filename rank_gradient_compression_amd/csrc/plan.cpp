@@ -1,0 +1,329 @@
+// Host-only compression plan: classification of a model's tensors, the packed
+// layout of the factors and the workgroup tile tables the kernels consume.
+// Nothing here touches a device.
+//
+// Classification follows the "Method" section of the anthology note on
+// PowerSGD (note 152): each layer's gradient is approximated independently,
+// conv tensors viewed as matrices, bias vectors and small tensors sent
+// uncompressed.  "Small" is read as r*(m+n) >= m*n, i.e. the factors would not
+// be smaller than the matrix (the glossary entry "PowerSGD" gives the payload
+// as O(r(m+n)) instead of O(mn)).
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <numeric>
+
+#include "psgd_internal.h"
+
+namespace psgd {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Rows per row block of the M^T P_hat pass: as long as possible (the partial
+// sums cost 2*rank/rb_rows of the matrix traffic) while the grid still has
+// enough workgroups to cover the chip.
+static int32_t choose_rb_rows(const std::vector<MatDesc>& mats) {
+  const int64_t target_wgs = 2048;
+  int32_t rb = 2048;
+  for (; rb > 64; rb /= 2) {
+    int64_t wgs = 0;
+    for (const MatDesc& d : mats) {
+      const int64_t cols_per_wg = (int64_t)kMtpWaves * 64 * d.vec;
+      wgs += ((d.m + rb - 1) / rb) * ((d.n + cols_per_wg - 1) / cols_per_wg);
+    }
+    if (wgs >= target_wgs) break;
+  }
+  return rb;
+}
+
+}  // namespace psgd
+
+using namespace psgd;
+
+extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows, const int64_t* cols,
+                                          const int64_t* offsets, int32_t rank, uint32_t flags,
+                                          float beta, psgd_plan_t* out) {
+  clear_error();
+  if (!out) {
+    set_error("psgd_plan_create: out is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  *out = nullptr;
+  if (ntensors < 0 || (ntensors > 0 && (!rows || !cols))) {
+    set_error("psgd_plan_create: bad tensor list (ntensors=%d)", ntensors);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (rank < 1) {
+    set_error("psgd_plan_create: rank %d < 1", rank);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (rank > PSGD_MAX_RANK) {
+    set_error("psgd_plan_create: rank %d above the supported maximum %d", rank, PSGD_MAX_RANK);
+    return PSGD_ERR_UNSUPPORTED;
+  }
+  if (flags & ~PSGD_FLAG_MOMENTUM) {
+    set_error("psgd_plan_create: unknown flag bits 0x%x", flags & ~PSGD_FLAG_MOMENTUM);
+    return PSGD_ERR_UNSUPPORTED;
+  }
+  if ((flags & PSGD_FLAG_MOMENTUM) && !(beta == beta)) {
+    set_error("psgd_plan_create: momentum beta is NaN");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  for (int32_t i = 0; i < ntensors; ++i) {
+    if (rows[i] < 1 || cols[i] < 0 || rows[i] > (int64_t)INT32_MAX || cols[i] > (int64_t)INT32_MAX) {
+      set_error("psgd_plan_create: tensor %d has bad shape %lld x %lld", i, (long long)rows[i],
+                (long long)cols[i]);
+      return PSGD_ERR_INVALID_ARG;
+    }
+  }
+
+  psgd_plan* p = new (std::nothrow) psgd_plan();
+  if (!p) {
+    set_error("psgd_plan_create: out of host memory");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  p->ntensors = ntensors;
+  p->rank = rank;
+  p->flags = flags;
+  p->beta = beta;
+  p->rows.assign(rows, rows + ntensors);
+  p->cols.resize(ntensors);
+  p->numel.resize(ntensors);
+  p->kind.resize(ntensors);
+  p->flat_off.resize(ntensors);
+  p->p_off.assign(ntensors, -1);
+  p->q_off.assign(ntensors, -1);
+  const int64_t r = rank;
+
+  for (int32_t i = 0; i < ntensors; ++i) {
+    const int64_t m = rows[i], n = cols[i] < 1 ? 1 : cols[i];
+    p->cols[i] = n;
+    p->numel[i] = m * n;
+    if (cols[i] <= 1)
+      p->kind[i] = PSGD_KIND_VECTOR;
+    else
+      p->kind[i] = (r * (m + n) < m * n) ? PSGD_KIND_COMPRESSED : PSGD_KIND_PASSTHRU;
+  }
+
+  // Flat layout.
+  if (offsets) {
+    std::vector<int32_t> order(ntensors);
+    std::iota(order.begin(), order.end(), 0);
+    for (int32_t i = 0; i < ntensors; ++i) {
+      if (offsets[i] < 0) {
+        set_error("psgd_plan_create: tensor %d has negative offset", i);
+        delete p;
+        return PSGD_ERR_INVALID_ARG;
+      }
+    }
+    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return offsets[a] < offsets[b]; });
+    int64_t end = 0;
+    for (int32_t k = 0; k < ntensors; ++k) {
+      const int32_t i = order[k];
+      if (offsets[i] < end) {
+        set_error("psgd_plan_create: tensor %d overlaps the previous tensor", i);
+        delete p;
+        return PSGD_ERR_INVALID_ARG;
+      }
+      end = offsets[i] + p->numel[i];
+    }
+    for (int32_t i = 0; i < ntensors; ++i) p->flat_off[i] = offsets[i];
+    p->flat_elems = (size_t)end;
+  } else {
+    int64_t off = 0;
+    for (int32_t i = 0; i < ntensors; ++i) {
+      p->flat_off[i] = off;
+      off = align_up(off + p->numel[i], kAlignElems);
+    }
+    p->flat_elems = (size_t)off;
+  }
+
+  // Packed factor layout: P_hat regions, then pass-through values; Q regions.
+  int64_t poff = 0, qoff = 0;
+  for (int32_t i = 0; i < ntensors; ++i) {
+    if (p->kind[i] != PSGD_KIND_COMPRESSED) continue;
+    const int64_t m = p->rows[i], n = p->cols[i];
+    p->p_off[i] = poff;
+    p->q_off[i] = qoff;
+    poff = align_up(poff + r * m, kAlignElems);
+    qoff = align_up(qoff + r * n, kAlignElems);
+    p->payload += (size_t)(r * (m + n));
+    p->dense += (size_t)(m * n);
+    MatDesc d{};
+    d.off = p->flat_off[i];
+    d.p_off = p->p_off[i];
+    d.q_off = p->q_off[i];
+    d.m = (int32_t)m;
+    d.n = (int32_t)n;
+    d.vec = (n % 4 == 0 && d.off % 4 == 0) ? 4 : (n % 2 == 0 && d.off % 2 == 0) ? 2 : 1;
+    p->mats.push_back(d);
+    p->mat_tensor.push_back(i);
+    p->max_m = std::max<int32_t>(p->max_m, (int32_t)m);
+    p->max_n = std::max<int32_t>(p->max_n, (int32_t)n);
+  }
+  p->p_elems = (size_t)poff;
+  p->q_elems = (size_t)qoff;
+  int64_t ptoff = 0;
+  for (int32_t i = 0; i < ntensors; ++i) {
+    if (p->kind[i] == PSGD_KIND_COMPRESSED) continue;
+    p->p_off[i] = poff + ptoff;
+    PassDesc pd{};
+    pd.off = p->flat_off[i];
+    pd.p_off = poff + ptoff;
+    pd.len = p->numel[i];
+    p->pass.push_back(pd);
+    ptoff = align_up(ptoff + p->numel[i], kAlignElems);
+    p->payload += (size_t)p->numel[i];
+  }
+  p->pt_elems = (size_t)ptoff;
+
+  // Tile tables.
+  const int32_t rb = choose_rb_rows(p->mats);
+  int64_t part = 0;
+  int32_t wg_rows = 0, wg_mtp = 0, wg_red = 0;
+  for (size_t k = 0; k < p->mats.size(); ++k) {
+    MatDesc& d = p->mats[k];
+    d.rb_rows = rb;
+    d.nrb = (d.m + rb - 1) / rb;
+    const int32_t cols_per_wg = kMtpWaves * 64 * d.vec;
+    d.ncb = (d.n + cols_per_wg - 1) / cols_per_wg;
+    d.part_off = part;
+    if (d.nrb > 1) part += align_up((int64_t)d.nrb * r * d.n, kAlignElems);
+    d.gram_off = (int64_t)k * r * r;
+    d.wg_rows0 = wg_rows;
+    const int32_t nrow_wg = (d.m + kRowsPerWG - 1) / kRowsPerWG;
+    for (int32_t t = 0; t < nrow_wg; ++t) p->rows_map.push_back((int32_t)k);
+    wg_rows += nrow_wg;
+    d.wg_mtp0 = wg_mtp;
+    for (int32_t t = 0; t < d.nrb * d.ncb; ++t) p->mtp_map.push_back((int32_t)k);
+    wg_mtp += d.nrb * d.ncb;
+    d.wg_red0 = wg_red;
+    if (d.nrb > 1) {
+      const int32_t nred = (int32_t)((r * d.n + kRedCols - 1) / kRedCols);
+      for (int32_t t = 0; t < nred; ++t) p->red_map.push_back((int32_t)k);
+      wg_red += nred;
+    }
+  }
+  int32_t wg_pass = 0;
+  for (size_t k = 0; k < p->pass.size(); ++k) {
+    PassDesc& pd = p->pass[k];
+    pd.wg0 = wg_pass;
+    const int32_t nw = (int32_t)((pd.len + kPassChunk - 1) / kPassChunk);
+    for (int32_t t = 0; t < nw; ++t) p->pass_map.push_back((int32_t)k);
+    wg_pass += nw;
+  }
+
+  // Workspace layout: header and tables, then scratch.
+  WsHeader& h = p->hdr;
+  h.magic = kWsMagic;
+  h.nmat = (int32_t)p->mats.size();
+  h.npass = (int32_t)p->pass.size();
+  h.rank = rank;
+  h.flags = (int32_t)flags;
+  h.wg_rows = wg_rows;
+  h.wg_mtp = wg_mtp;
+  h.wg_red = wg_red;
+  h.wg_pass = wg_pass;
+  int64_t b = align_up(sizeof(WsHeader), 256);
+  h.mat_off = b;
+  b = align_up(b + (int64_t)sizeof(MatDesc) * h.nmat, 256);
+  h.pass_off = b;
+  b = align_up(b + (int64_t)sizeof(PassDesc) * h.npass, 256);
+  h.rows_map_off = b;
+  b = align_up(b + 4 * (int64_t)p->rows_map.size(), 256);
+  h.mtp_map_off = b;
+  b = align_up(b + 4 * (int64_t)p->mtp_map.size(), 256);
+  h.red_map_off = b;
+  b = align_up(b + 4 * (int64_t)p->red_map.size(), 256);
+  h.pass_map_off = b;
+  b = align_up(b + 4 * (int64_t)p->pass_map.size(), 256);
+  h.tables_bytes = b;
+  h.part_base = b;
+  b = align_up(b + 4 * part, 256);
+  h.gram_base = b;
+  b = align_up(b + 8 * (int64_t)h.nmat * r * r, 256);
+  h.refresh_base = b;
+  // refresh scratch: P (m x r) and the partial sums of M^T P_hat for the
+  // largest matrix.
+  int64_t ref = 0;
+  for (const MatDesc& d : p->mats)
+    ref = std::max<int64_t>(ref, align_up((int64_t)d.m * r, kAlignElems) +
+                                     (int64_t)d.nrb * r * d.n);
+  b = align_up(b + 4 * ref, 256);
+  h.total_bytes = b;
+
+  p->tables.assign((size_t)h.tables_bytes, 0);
+  memcpy(p->tables.data(), &h, sizeof h);
+  if (h.nmat) memcpy(p->tables.data() + h.mat_off, p->mats.data(), sizeof(MatDesc) * h.nmat);
+  if (h.npass) memcpy(p->tables.data() + h.pass_off, p->pass.data(), sizeof(PassDesc) * h.npass);
+  if (!p->rows_map.empty())
+    memcpy(p->tables.data() + h.rows_map_off, p->rows_map.data(), 4 * p->rows_map.size());
+  if (!p->mtp_map.empty())
+    memcpy(p->tables.data() + h.mtp_map_off, p->mtp_map.data(), 4 * p->mtp_map.size());
+  if (!p->red_map.empty())
+    memcpy(p->tables.data() + h.red_map_off, p->red_map.data(), 4 * p->red_map.size());
+  if (!p->pass_map.empty())
+    memcpy(p->tables.data() + h.pass_map_off, p->pass_map.data(), 4 * p->pass_map.size());
+
+  *out = p;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_plan_get_info(psgd_plan_t p, psgd_plan_info_t* info) {
+  clear_error();
+  if (!p || !info) {
+    set_error("psgd_plan_get_info: NULL argument");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  memset(info, 0, sizeof *info);
+  info->ntensors = p->ntensors;
+  info->ncompressed = (int32_t)p->mats.size();
+  info->rank = p->rank;
+  info->flags = p->flags;
+  info->flat_elems = p->flat_elems;
+  info->p_elems = p->p_elems;
+  info->passthru_elems = p->pt_elems;
+  info->p_buffer_elems = p->p_elems + p->pt_elems;
+  info->q_elems = p->q_elems;
+  info->payload_elems = p->payload;
+  info->dense_elems = p->dense;
+  info->workspace_bytes = (size_t)p->hdr.total_bytes;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_plan_tensor(psgd_plan_t p, int32_t t, int32_t* kind, int64_t* flat_off,
+                                          int64_t* p_off, int64_t* q_off) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_plan_tensor: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (t < 0 || t >= p->ntensors) {
+    set_error("psgd_plan_tensor: tensor %d out of range [0, %d)", t, p->ntensors);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (kind) *kind = p->kind[t];
+  if (flat_off) *flat_off = p->flat_off[t];
+  if (p_off) *p_off = p->p_off[t];
+  if (q_off) *q_off = p->q_off[t];
+  return PSGD_OK;
+}
+
+extern "C" const char* psgd_last_error(void) { return g_err; }
+
+extern "C" const char* psgd_version(void) { return "psgd-mi355x 0.1 (gfx950)"; }

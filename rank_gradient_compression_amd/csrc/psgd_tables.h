@@ -1,0 +1,82 @@
+// Device tables of a compression plan: the layout the host plan writes into
+// the workspace and the kernels read.  Plain structs, shared by the host-only
+// plan code and the HIP kernels of this library.
+#pragma once
+
+#include <stdint.h>
+
+namespace psgd {
+
+// Rows of a compressed matrix handled by one wavefront in the streaming
+// passes (EF-add + P = M Q, the residual pass and decompression), and the
+// wavefronts of one workgroup.  A workgroup covers kWaveRows * kWavesPerWG
+// consecutive rows of one matrix, every column.
+constexpr int kWaveRows = 8;
+constexpr int kWavesPerWG = 4;
+constexpr int kWGThreads = 64 * kWavesPerWG;
+constexpr int kRowsPerWG = kWaveRows * kWavesPerWG;
+
+// Columns of one M^T P_hat workgroup tile per 4-wide vector lane: each of the
+// four wavefronts owns 64 lanes * vec columns.
+constexpr int kMtpWaves = 4;
+
+// Largest rank the VALU streaming kernels handle; larger ranks use the MFMA
+// kernels.
+constexpr int kValuMaxRank = 8;
+
+// Alignment (elements) of every region the plan lays out.
+constexpr int64_t kAlignElems = 64;
+
+// One compressed matrix.
+struct MatDesc {
+  int64_t off;       // flat element offset of row 0 in grads/err/mom/mhat
+  int64_t p_off;     // P / P_hat: rank columns of m floats from here
+  int64_t q_off;     // Q: rank columns of n floats from here
+  int64_t part_off;  // partial-Q scratch (floats, from the scratch base)
+  int64_t gram_off;  // orthonormalisation scratch (doubles, from its base)
+  int32_t m, n;
+  int32_t vec;       // 4, 2 or 1: widest vector access both n and off allow
+  int32_t nrb;       // row blocks of the M^T P_hat pass
+  int32_t rb_rows;   // rows per row block of the M^T P_hat pass
+  int32_t ncb;       // column tiles of the M^T P_hat pass
+  int32_t wg_rows0;  // first workgroup of this matrix in the row-tile grid
+  int32_t wg_mtp0;   // first workgroup of this matrix in the M^T P_hat grid
+  int32_t wg_red0;   // first workgroup of this matrix in the Q-reduce grid
+  int32_t pad_;
+};
+static_assert(sizeof(MatDesc) == 80, "MatDesc layout");
+
+// One pass-through tensor: `len` elements at flat offset `off`, packed at
+// `p_off` (absolute, in the P buffer).
+struct PassDesc {
+  int64_t off;
+  int64_t p_off;
+  int64_t len;
+  int64_t wg0;  // first workgroup of this tensor in the pass-through grid
+};
+
+constexpr int kPassChunk = 4096;  // elements per pass-through workgroup
+constexpr int kRedCols = 256;     // Q elements per reduce workgroup
+
+// Header at the start of the workspace.
+struct WsHeader {
+  uint64_t magic;
+  int32_t nmat, npass;
+  int32_t rank, flags;
+  int32_t wg_rows, wg_mtp, wg_red, wg_pass;
+  int64_t mat_off;       // bytes from workspace start: MatDesc[nmat]
+  int64_t pass_off;      // PassDesc[npass]
+  int64_t rows_map_off;  // int32 matrix index per row-tile workgroup
+  int64_t mtp_map_off;   // int32 per M^T P_hat workgroup
+  int64_t red_map_off;   // int32 per Q-reduce workgroup
+  int64_t pass_map_off;  // int32 pass-through tensor per pass-through workgroup
+  int64_t tables_bytes;  // bytes of the table part (uploaded by workspace_init)
+  int64_t part_base;     // bytes: partial-Q scratch (float)
+  int64_t gram_base;     // bytes: orthonormalisation scratch (double)
+  int64_t refresh_base;  // bytes: refresh scratch (float)
+  int64_t total_bytes;
+};
+
+constexpr uint64_t kWsMagic = 0x3144474953505350ull;  // "PSPSIGD1"
+
+}  // namespace psgd

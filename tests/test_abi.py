@@ -1,0 +1,226 @@
+"""Host-side tests of libpsgd.so that need no GPU: the library loads and
+exports every symbol include/psgd.h declares, the plan's classification,
+layout and payload, and every argument error path (all of which return before
+any device call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+R = pytest.importorskip("rank_gradient_compression_amd")
+B = R.binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "psgd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(psgd_[a-z_]+)\s*\(", src)) - {"psgd_reduce_fn"})
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTED) == names
+
+
+def test_version():
+    assert "gfx950" in R.psgd_version()
+
+
+def views(tensors):
+    rows, cols = [], []
+    for _, s in tensors:
+        m, n = oracle.matrix_view(s)
+        rows.append(m)
+        cols.append(n if len(s) >= 2 else 1)
+    return rows, cols
+
+
+def golden():
+    out = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "payload_counts.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, r, nm, el, fl, vec = line.split()
+        out[name] = tuple(int(x) for x in (r, nm, el, fl, vec))
+    return out
+
+
+@pytest.mark.parametrize("name,tensors", [("resnet18", W.resnet18_cifar_set()), ("lstm3", W.lstm3_wikitext_set()),
+                                          ("llama7b", W.llama7b_set())])
+def test_plan_matches_oracle_classification_and_payload(name, tensors):
+    r, nm, el, fl, vec = golden()[name]
+    rows, cols = views(tensors)
+    p = R.psgd_plan_create(rows, cols, r)
+    try:
+        info = R.psgd_plan_get_info(p)
+        assert info["ncompressed"] == nm
+        assert info["dense_elems"] == el
+        assert info["payload_elems"] == fl + vec
+        op = oracle.Plan([s for _, s in tensors], r)
+        for i in range(len(tensors)):
+            kind, off, poff, qoff = R.psgd_plan_tensor(p, i)
+            assert kind == op.kinds[i]
+            assert off % 64 == 0
+            if kind == B.PSGD_KIND_COMPRESSED:
+                assert poff % 64 == 0 and qoff % 64 == 0 and poff + r * rows[i] <= info["p_elems"]
+                assert qoff + r * cols[i] <= info["q_elems"]
+            else:
+                assert qoff == -1 and info["p_elems"] <= poff < info["p_buffer_elems"]
+        assert info["flat_elems"] >= sum(a * b for a, b in zip(rows, cols))
+    finally:
+        R.psgd_plan_destroy(p)
+
+
+def test_plan_regions_do_not_overlap():
+    g = np.random.default_rng(0)
+    rows = [int(x) for x in g.integers(1, 300, 40)]
+    cols = [int(x) for x in g.integers(1, 300, 40)]
+    p = R.psgd_plan_create(rows, cols, 3)
+    try:
+        info = R.psgd_plan_get_info(p)
+        flat, pr, qr = [], [], []
+        for i in range(40):
+            kind, off, poff, qoff = R.psgd_plan_tensor(p, i)
+            flat.append((off, off + rows[i] * cols[i]))
+            if kind == B.PSGD_KIND_COMPRESSED:
+                pr.append((poff, poff + 3 * rows[i]))
+                qr.append((qoff, qoff + 3 * cols[i]))
+            else:
+                pr.append((poff, poff + rows[i] * cols[i]))
+        for regs, limit in ((flat, info["flat_elems"]), (pr, info["p_buffer_elems"]), (qr, info["q_elems"])):
+            regs.sort()
+            for (a0, a1), (b0, b1) in zip(regs, regs[1:]):
+                assert a1 <= b0
+            assert not regs or regs[-1][1] <= limit
+    finally:
+        R.psgd_plan_destroy(p)
+
+
+def test_caller_offsets_accepted_and_checked():
+    p = R.psgd_plan_create([10, 20], [30, 1], 2, offsets=[1, 400])
+    try:
+        assert R.psgd_plan_tensor(p, 0)[1] == 1
+        assert R.psgd_plan_get_info(p)["flat_elems"] == 420
+    finally:
+        R.psgd_plan_destroy(p)
+    with pytest.raises(B.PsgdError) as e:
+        R.psgd_plan_create([10, 20], [30, 1], 2, offsets=[0, 100])
+    assert e.value.status == B.PSGD_ERR_INVALID_ARG and "overlap" in str(e.value)
+    with pytest.raises(B.PsgdError):
+        R.psgd_plan_create([10], [30], 2, offsets=[-1])
+
+
+@pytest.mark.parametrize("rows,cols,rank,flags,status", [
+    ([4], [4], 0, 0, B.PSGD_ERR_INVALID_ARG),
+    ([4], [4], 65, 0, B.PSGD_ERR_UNSUPPORTED),
+    ([0], [4], 1, 0, B.PSGD_ERR_INVALID_ARG),
+    ([4], [-1], 1, 0, B.PSGD_ERR_INVALID_ARG),
+    ([4], [4], 1, 6, B.PSGD_ERR_UNSUPPORTED),
+])
+def test_plan_create_errors(rows, cols, rank, flags, status):
+    with pytest.raises(B.PsgdError) as e:
+        R.psgd_plan_create(rows, cols, rank, flags)
+    assert e.value.status == status
+    assert R.psgd_last_error()
+
+
+def test_empty_and_vector_only_plans():
+    p = R.psgd_plan_create([], [], 4)
+    info = R.psgd_plan_get_info(p)
+    assert info["ntensors"] == 0 and info["flat_elems"] == 0 and info["payload_elems"] == 0
+    R.psgd_plan_destroy(p)
+    p = R.psgd_plan_create([5, 7], [1, 1], 2)
+    info = R.psgd_plan_get_info(p)
+    assert info["ncompressed"] == 0 and info["payload_elems"] == 12 and info["p_elems"] == 0
+    R.psgd_plan_destroy(p)
+
+
+def test_tensor_index_checked():
+    p = R.psgd_plan_create([5], [6], 1)
+    with pytest.raises(B.PsgdError):
+        R.psgd_plan_tensor(p, 1)
+    R.psgd_plan_destroy(p)
+
+
+FAKE = 1 << 20  # never dereferenced: every case below fails validation first
+
+
+def _compress(plan, **kw):
+    a = dict(grads=FAKE, err=FAKE, mom=0, q=FAKE, pbuf=FAKE, mhat=0, hook=None, workspace=FAKE * 2,
+             workspace_bytes=1 << 40)
+    a.update(kw)
+    R.psgd_compress(plan, a["grads"], a["err"], a["mom"], a["q"], a["pbuf"], a["mhat"], a["hook"], a["workspace"],
+                    a["workspace_bytes"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(grads=0), B.PSGD_ERR_INVALID_ARG),
+    (dict(err=0), B.PSGD_ERR_INVALID_ARG),
+    (dict(q=0), B.PSGD_ERR_INVALID_ARG),
+    (dict(pbuf=0), B.PSGD_ERR_INVALID_ARG),
+    (dict(grads=FAKE + 2), B.PSGD_ERR_INVALID_ARG),
+    (dict(q=FAKE + 4), B.PSGD_ERR_INVALID_ARG),
+    (dict(mom=FAKE), B.PSGD_ERR_INVALID_ARG),
+    (dict(mhat=FAKE), B.PSGD_ERR_INVALID_ARG),  # aliases err
+    (dict(workspace=0), B.PSGD_ERR_WORKSPACE),
+    (dict(workspace=FAKE + 64), B.PSGD_ERR_WORKSPACE),
+    (dict(workspace_bytes=16), B.PSGD_ERR_WORKSPACE),
+])
+def test_compress_argument_errors(kw, status):
+    p = R.psgd_plan_create([64, 9], [48, 1], 2)
+    try:
+        if "mhat" in kw:
+            kw = dict(kw, err=kw["mhat"])
+        with pytest.raises(B.PsgdError) as e:
+            _compress(p, **kw)
+        assert e.value.status == status
+    finally:
+        R.psgd_plan_destroy(p)
+
+
+def test_momentum_plan_requires_mom():
+    p = R.psgd_plan_create([64], [48], 2, B.PSGD_FLAG_MOMENTUM, 0.9)
+    try:
+        with pytest.raises(B.PsgdError) as e:
+            _compress(p)
+        assert e.value.status == B.PSGD_ERR_INVALID_ARG and "mom" in str(e.value)
+    finally:
+        R.psgd_plan_destroy(p)
+
+
+def test_decompress_and_refresh_argument_errors():
+    p = R.psgd_plan_create([64], [48], 2)
+    try:
+        with pytest.raises(B.PsgdError) as e:
+            R.psgd_decompress(p, FAKE, FAKE, FAKE, 0, 1 << 30, 0)
+        assert e.value.status == B.PSGD_ERR_WORKSPACE
+        with pytest.raises(B.PsgdError) as e:
+            R.psgd_decompress(p, 0, FAKE, FAKE, FAKE * 2, 1 << 30, 0)
+        assert e.value.status == B.PSGD_ERR_INVALID_ARG
+    finally:
+        R.psgd_plan_destroy(p)
+
+
+def test_stream_copy_argument_errors():
+    with pytest.raises(B.PsgdError):
+        R.psgd_stream_copy(FAKE, FAKE + 4, 16)
+    with pytest.raises(B.PsgdError):
+        R.psgd_stream_copy(FAKE, FAKE, 3)
+
+
+def test_timing_read_without_records():
+    p = R.psgd_plan_create([64], [48], 2)
+    ms, n = R.psgd_timing_read(p)
+    assert ms == [0.0] * B.PSGD_NSTAGES and n == [0] * B.PSGD_NSTAGES
+    R.psgd_plan_destroy(p)
