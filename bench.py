@@ -50,6 +50,41 @@ def parse():
     return ap.parse_args()
 
 
+KERNEL_OF_STAGE = {"ef_p": "k_ef_p", "mtp": "k_mtp", "residual": "k_recon"}
+
+
+def source_hash():
+    import hashlib
+
+    csrc = os.path.join(ROOT, "rank_gradient_compression_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage, rank, mhat):
+    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when the summary does not cover
+    this configuration or the library sources changed since it was taken."""
+    if rank != 4 or not mhat:
+        return None
+    path = os.path.join(ROOT, "profiles", "hbm_bytes_llama7b_r4_fused.md")
+    try:
+        text = open(path).read()
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if blob.get("source_hash") != source_hash():
+        return None
+    for name, v in blob["kernels"].items():
+        if KERNEL_OF_STAGE.get(stage, "?") in name:
+            return v["read_bytes"] + v["write_bytes"]
+    return None
+
+
 def stage_roofline(plan, B, n_steps, dense, momentum=False, mhat=True):
     ms, n = B.psgd_timing_read(plan)
     stages = {}
@@ -177,8 +212,11 @@ def main():
     if stages:
         dom = max((s for s in stages if s in B_STAGE), key=lambda s: stages[s]["ms_avg"] * stages[s]["launches"])
         d = stages[dom]
-        result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS,
-                              "unit": "GB/s", "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None}
+        tr = measured_traffic(dom, rank, True)
+        result["roofline"] = {"bound": "hbm", "kernel": KERNEL_OF_STAGE[dom], "achieved": round(d["gbs"], 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d["gbs"] / HBM_PEAK_GBS, 4),
+                              "traffic": round(tr) if tr else None,
+                              "alg_bytes_per_launch": d["bytes_alg"], "avg_launch_ms": round(d["ms_avg"], 4)}
         result["stages"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                             for k, v in stages.items()}
 
