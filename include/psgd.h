@@ -183,17 +183,24 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  *          P_hat Q^T for compressed tensors and the aggregated values of the
  *          pass-through tensors (a fused psgd_decompress).  It may alias
  *          `grads` (then G is overwritten by the update) but no other buffer.
+ *   refresh_iters  0 for a plain step.  k > 0 makes this a PowerSGD+ step
+ *          ([PSGD+] Abstract: the projection subspace is periodically
+ *          re-aligned with the optimal one through an SVD): after the EF-add,
+ *          every warm-start Q is replaced by k rounds of block power iteration
+ *          with orthonormalisation on M, Q <- GS(M^T GS(M Q)), before P = M Q.
+ *          The caller chooses the period (for example every 50th step).
  *   hook   nullable aggregation hook, called on (p, p_buffer_elems) after P is
  *          formed and on (q, q_elems) after Q is formed.
  *   workspace, workspace_bytes   initialised workspace (psgd_workspace_init).
  *
  * Errors: PSGD_ERR_INVALID_ARG for null or not 16-byte aligned buffers, a
- * missing or unexpected `mom`; PSGD_ERR_WORKSPACE; PSGD_ERR_HOOK if a hook
+ * missing or unexpected `mom`, a negative refresh_iters; PSGD_ERR_WORKSPACE;
+ * PSGD_ERR_HOOK if a hook
  * returns non-zero (no later stage is enqueued); PSGD_ERR_HIP.
  */
 psgd_status_t psgd_compress(psgd_plan_t plan, const float* grads, float* err, float* mom, float* q,
-                            float* p, float* mhat, psgd_reduce_fn hook, void* user, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream);
+                            float* p, float* mhat, int32_t refresh_iters, psgd_reduce_fn hook, void* user,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * psgd_decompress -- reconstruct G ~ P_hat Q^T ([GLOSS], factorisation
@@ -208,7 +215,10 @@ psgd_status_t psgd_decompress(psgd_plan_t plan, const float* p, const float* q, 
  * `iters` rounds of block power iteration with orthonormalisation,
  * Q <- GS(M^T GS(M Q)), on compressed tensor `tensor` of the flat buffer `m`
  * (the compressor input), updating that tensor's columns of the packed Q
- * buffer in place.  On return its Q has orthonormal columns.
+ * buffer in place.  On return its Q has orthonormal columns (dependent
+ * columns are zero).  Uses the workspace scratch: not concurrent with a
+ * compress call on the same workspace.  Errors: PSGD_ERR_INVALID_ARG for a
+ * tensor that is not compressed, null or misaligned buffers, iters < 0.
  */
 psgd_status_t psgd_refresh(psgd_plan_t plan, int32_t tensor, const float* m, float* q, int32_t iters,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);

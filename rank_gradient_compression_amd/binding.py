@@ -104,7 +104,8 @@ lib.psgd_plan_destroy.restype = None
 lib.psgd_plan_get_info.argtypes = [_vp, ctypes.POINTER(psgd_plan_info_t)]
 lib.psgd_plan_tensor.argtypes = [_vp, ctypes.c_int32, _i32p, _i64p, _i64p, _i64p]
 lib.psgd_workspace_init.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
-lib.psgd_compress.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, psgd_reduce_fn, _vp, _vp, ctypes.c_size_t, _vp]
+lib.psgd_compress.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, psgd_reduce_fn, _vp, _vp,
+                              ctypes.c_size_t, _vp]
 lib.psgd_decompress.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_refresh.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
 lib.psgd_timing_enable.argtypes = [_vp, ctypes.c_int32]
@@ -175,11 +176,11 @@ def make_hook(fn: Callable[[int, int, int], int]):
     return psgd_reduce_fn(lambda buf, count, stream, user: int(fn(buf or 0, count, stream or 0)))
 
 
-def psgd_compress(plan: int, grads: int, err: int, mom: int, q: int, p: int, mhat: int, hook, workspace: int,
-                  workspace_bytes: int, stream: int = 0) -> None:
+def psgd_compress(plan: int, grads: int, err: int, mom: int, q: int, p: int, mhat: int, refresh_iters: int, hook,
+                  workspace: int, workspace_bytes: int, stream: int = 0) -> None:
     h = hook if hook is not None else psgd_reduce_fn()
-    _check("psgd_compress", lib.psgd_compress(plan, grads, err or None, mom or None, q or None, p, mhat or None, h,
-                                              None, workspace, workspace_bytes, stream))
+    _check("psgd_compress", lib.psgd_compress(plan, grads, err or None, mom or None, q or None, p, mhat or None,
+                                              refresh_iters, h, None, workspace, workspace_bytes, stream))
 
 
 def psgd_decompress(plan: int, p: int, q: int, out: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:

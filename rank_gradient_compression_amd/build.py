@@ -37,6 +37,8 @@ def _compile(src: str, verbose: bool) -> str:
            "-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["--offload-arch=gfx950", "-x", "hip"] + DEVICE_FLAGS
+    else:  # host-only C++ (no device code)
+        cmd[1:1] = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "include")]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

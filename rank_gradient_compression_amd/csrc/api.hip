@@ -11,6 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "psgd_internal.h"
@@ -77,22 +78,77 @@ static LaunchCtx make_ctx(const psgd_plan* p, void* ws, hipStream_t s) {
   LaunchCtx c{};
   c.stream = s;
   c.rank = p->rank;
+  c.rank_pad = h.rank_pad;
+  c.mfma = h.mfma != 0;
   c.nmat = h.nmat;
   c.npass = h.npass;
   c.wg_rows = h.wg_rows;
   c.wg_mtp = h.wg_mtp;
   c.wg_red = h.wg_red;
   c.wg_pass = h.wg_pass;
+  c.wg_pred = h.wg_pred;
+  c.wg_gram = h.wg_gram;
+  c.wg_gramq = h.wg_gramq;
   c.mats = reinterpret_cast<const MatDesc*>(b + h.mat_off);
   c.pass = reinterpret_cast<const PassDesc*>(b + h.pass_off);
+  c.orth = reinterpret_cast<const OrthDesc*>(b + h.orth_off);
   c.rows_map = reinterpret_cast<const int32_t*>(b + h.rows_map_off);
   c.mtp_map = reinterpret_cast<const int32_t*>(b + h.mtp_map_off);
   c.red_map = reinterpret_cast<const int32_t*>(b + h.red_map_off);
   c.pass_map = reinterpret_cast<const int32_t*>(b + h.pass_map_off);
+  c.pred_map = reinterpret_cast<const int32_t*>(b + h.pred_map_off);
+  c.gram_map = reinterpret_cast<const int32_t*>(b + h.gram_map_off);
+  c.gramq_map = reinterpret_cast<const int32_t*>(b + h.gramq_map_off);
   c.part = reinterpret_cast<float*>(b + h.part_base);
+  c.ppart = reinterpret_cast<float*>(b + h.ppart_base);
   c.gram = reinterpret_cast<double*>(b + h.gram_base);
   c.rscr = reinterpret_cast<float*>(b + h.refresh_base);
   return c;
+}
+
+// Workgroups of matrix k in one of the plan's grids.
+static GridRange mat_range(const psgd_plan* p, size_t k, int32_t MatDesc::*first, int total) {
+  const int b = p->mats[k].*first;
+  const int e = k + 1 < p->mats.size() ? p->mats[k + 1].*first : total;
+  return GridRange{b, e - b};
+}
+
+// ---- the stages of one step, dispatched to the vector or matrix-core kernels
+
+// P = M Q for the grid range g (mode as in launch_ef_p), into P at the plan's
+// offsets (p_fixed < 0) or at p_fixed, column-split partials summed.
+static hipError_t stage_mq(const psgd_plan* p, const LaunchCtx& c, const GridRange& g, const GridRange& gp, int mode,
+                           const float* G, float* E, float* U, const float* Q, float* P, int64_t p_fixed) {
+  if (!c.mfma) return launch_ef_p(c, g, mode, G, E, U, p->beta, Q, P, p_fixed);
+  hipError_t e = launch_mfma_p(c, g, mode, G, E, U, p->beta, Q, P, p_fixed);
+  if (e != hipSuccess) return e;
+  return launch_psum(c, gp, P, p_fixed);
+}
+
+// Orthonormalise the P factors of all matrices (P in `base` at the plan's
+// offsets).
+static hipError_t stage_orth_all_p(const LaunchCtx& c, float* base) {
+  if (!c.mfma) return launch_orth(c, 0, c.nmat, base);
+  return launch_gram_orth(c, 0, c.nmat, c.gram_map, c.wg_gram, base);
+}
+
+// Orthonormalise the Q factors of all matrices (the refresh).
+static hipError_t stage_orth_all_q(const LaunchCtx& c, float* q) {
+  if (!c.mfma) return launch_orth(c, 2 * c.nmat, c.nmat, q);
+  return launch_gram_orth(c, 2 * c.nmat, c.nmat, c.gramq_map, c.wg_gramq, q);
+}
+
+// Q = M^T P_hat (row-block partials reduced in fixed order).
+static hipError_t stage_mtp(const LaunchCtx& c, const GridRange& g, const GridRange& gr, const float* M,
+                            const float* Ph, int64_t ph_fixed, float* Q) {
+  hipError_t e = c.mfma ? launch_mfma_qt(c, g, M, Ph, ph_fixed, Q) : launch_mtp(c, g, M, Ph, ph_fixed, Q);
+  if (e != hipSuccess) return e;
+  return launch_qreduce(c, gr, Q);
+}
+
+static hipError_t stage_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
+                              bool residual) {
+  return c.mfma ? launch_mfma_recon(c, E, Q, Ph, Mhat, residual) : launch_recon(c, E, Q, Ph, Mhat, residual);
 }
 
 static psgd_status_t check_ws(const psgd_plan* p, const void* ws, size_t bytes, const char* fn) {
@@ -154,8 +210,8 @@ extern "C" psgd_status_t psgd_workspace_init(psgd_plan_t p, void* ws, size_t byt
 }
 
 extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const float* grads, float* err, float* mom, float* q, float* pbuf,
-                                       float* mhat, psgd_reduce_fn hook, void* user, void* ws, size_t ws_bytes,
-                                       hipStream_t stream) {
+                                       float* mhat, int32_t refresh_iters, psgd_reduce_fn hook, void* user, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
   clear_error();
   if (!p) {
     set_error("psgd_compress: plan is NULL");
@@ -184,31 +240,53 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const float* grads, float*
     set_error("psgd_compress: mhat may alias grads only");
     return PSGD_ERR_INVALID_ARG;
   }
-  if (p->rank > kValuMaxRank) {
-    set_error("psgd_compress: rank %d not available in this build", p->rank);
-    return PSGD_ERR_UNSUPPORTED;
+  if (refresh_iters < 0) {
+    set_error("psgd_compress: negative refresh_iters");
+    return PSGD_ERR_INVALID_ARG;
   }
   if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_compress")) return s;
   if (!any) return PSGD_OK;
 
   const LaunchCtx c = make_ctx(p, ws, stream);
   float* U = momentum ? mom : nullptr;
-  const float beta = p->beta;
+  const GridRange all_rows{0, c.wg_rows}, all_pred{0, c.wg_pred}, all_mtp{0, c.wg_mtp}, all_red{0, c.wg_red};
+  const int mode = momentum ? 2 : 1;
 
-  PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_pack(c, grads, U, beta, pbuf), "pass-through pack");
-  PSGD_LAUNCH(PSGD_STAGE_EF_P, launch_ef_p(c, grads, err, U, beta, q, pbuf), "EF-add + P = M Q");
+  PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_pack(c, grads, U, p->beta, pbuf), "pass-through pack");
+  if (refresh_iters <= 0) {
+    PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, all_rows, all_pred, mode, grads, err, U, q, pbuf, -1),
+                "EF-add + P = M Q");
+  } else {
+    // PowerSGD+ step: M = X + E first, then the subspace refresh of every
+    // warm-start Q on M, then P = M Q with the refreshed Q.
+    PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, all_rows, all_pred, mode, grads, err, U, q, c.rscr, -1),
+                "EF-add");
+    for (int it = 0; it < refresh_iters; ++it) {
+      PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_mq(p, c, all_rows, all_pred, 0, nullptr, err, nullptr, q, c.rscr, -1),
+                  "refresh: P = M Q");
+      PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_orth_all_p(c, c.rscr), "refresh: orthonormalise P");
+      PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_mtp(c, all_mtp, all_red, err, c.rscr, -1, q), "refresh: Q = M^T P");
+      PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_orth_all_q(c, q), "refresh: orthonormalise Q");
+    }
+    PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, all_rows, all_pred, 0, nullptr, err, nullptr, q, pbuf, -1),
+                "P = M Q");
+  }
   if (hook && hook(pbuf, p->p_elems + p->pt_elems, stream, user) != 0) {
     set_error("psgd_compress: aggregation hook failed on P");
     return PSGD_ERR_HOOK;
   }
-  PSGD_LAUNCH(PSGD_STAGE_GS, launch_orth(c, pbuf), "orthogonalise P");
-  PSGD_LAUNCH(PSGD_STAGE_MTP, launch_mtp(c, err, pbuf, q, c.part), "Q = M^T P_hat");
-  PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, c.part, q), "Q partial reduction");
+  PSGD_LAUNCH(PSGD_STAGE_GS, stage_orth_all_p(c, pbuf), "orthogonalise P");
+  {
+    StageTimer _t(p, PSGD_STAGE_MTP, stream);
+    const hipError_t e = c.mfma ? launch_mfma_qt(c, all_mtp, err, pbuf, -1, q) : launch_mtp(c, all_mtp, err, pbuf, -1, q);
+    if (e != hipSuccess) return hip_fail(e, "Q = M^T P_hat");
+  }
+  PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, all_red, q), "Q partial reduction");
   if (hook && hook(q, p->q_elems, stream, user) != 0) {
     set_error("psgd_compress: aggregation hook failed on Q");
     return PSGD_ERR_HOOK;
   }
-  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, launch_recon(c, err, q, pbuf, mhat, true), "residual E = M - P_hat Q^T");
+  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, err, q, pbuf, mhat, true), "residual E = M - P_hat Q^T");
   if (mhat) PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat), "pass-through unpack");
   return PSGD_OK;
 }
@@ -228,14 +306,10 @@ extern "C" psgd_status_t psgd_decompress(psgd_plan_t p, const float* pbuf, const
     set_error("psgd_decompress: buffers must be 16-byte aligned");
     return PSGD_ERR_INVALID_ARG;
   }
-  if (p->rank > kValuMaxRank) {
-    set_error("psgd_decompress: rank %d not available in this build", p->rank);
-    return PSGD_ERR_UNSUPPORTED;
-  }
   if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_decompress")) return s;
   if (p->ntensors == 0) return PSGD_OK;
   const LaunchCtx c = make_ctx(p, ws, stream);
-  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, launch_recon(c, nullptr, q, pbuf, out, false), "decompress P_hat Q^T");
+  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, nullptr, q, pbuf, out, false), "decompress P_hat Q^T");
   PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out), "pass-through unpack");
   return PSGD_OK;
 }
@@ -243,9 +317,44 @@ extern "C" psgd_status_t psgd_decompress(psgd_plan_t p, const float* pbuf, const
 extern "C" psgd_status_t psgd_refresh(psgd_plan_t p, int32_t tensor, const float* m, float* q, int32_t iters, void* ws,
                                       size_t ws_bytes, hipStream_t stream) {
   clear_error();
-  (void)p; (void)tensor; (void)m; (void)q; (void)iters; (void)ws; (void)ws_bytes; (void)stream;
-  set_error("psgd_refresh: not available in this build");
-  return PSGD_ERR_UNSUPPORTED;
+  if (!p) {
+    set_error("psgd_refresh: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (tensor < 0 || tensor >= p->ntensors || p->kind[tensor] != PSGD_KIND_COMPRESSED) {
+    set_error("psgd_refresh: tensor %d is not a compressed tensor of the plan", tensor);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (!m || !q || !aligned16(m) || !aligned16(q)) {
+    set_error("psgd_refresh: m and q must be non-null and 16-byte aligned");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (iters < 0) {
+    set_error("psgd_refresh: negative iteration count");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_refresh")) return s;
+  const size_t k = (size_t)(std::find(p->mat_tensor.begin(), p->mat_tensor.end(), tensor) - p->mat_tensor.begin());
+  const LaunchCtx c = make_ctx(p, ws, stream);
+  const MatDesc& d = p->mats[k];
+  const GridRange rows = mat_range(p, k, &MatDesc::wg_rows0, c.wg_rows);
+  const GridRange mtp = mat_range(p, k, &MatDesc::wg_mtp0, c.wg_mtp);
+  const GridRange red = mat_range(p, k, &MatDesc::wg_red0, c.wg_red);
+  const GridRange pred = c.mfma ? mat_range(p, k, &MatDesc::wg_pred0, c.wg_pred) : GridRange{0, 0};
+  const int op = c.nmat + (int)k, oq = 2 * c.nmat + (int)k;
+  const int nb_p = (d.m + kGramRows - 1) / kGramRows, nb_q = (d.n + kGramRows - 1) / kGramRows;
+  float* M = const_cast<float*>(m);
+  for (int it = 0; it < iters; ++it) {
+    PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_mq(p, c, rows, pred, 0, nullptr, M, nullptr, q, c.rscr, 0),
+                "refresh: P = M Q");
+    PSGD_LAUNCH(PSGD_STAGE_REFRESH,
+                c.mfma ? launch_gram_orth(c, op, 1, nullptr, nb_p, c.rscr) : launch_orth(c, op, 1, c.rscr),
+                "refresh: orthonormalise P");
+    PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_mtp(c, mtp, red, M, c.rscr, 0, q), "refresh: Q = M^T P");
+    PSGD_LAUNCH(PSGD_STAGE_REFRESH, c.mfma ? launch_gram_orth(c, oq, 1, nullptr, nb_q, q) : launch_orth(c, oq, 1, q),
+                "refresh: orthonormalise Q");
+  }
+  return PSGD_OK;
 }
 
 extern "C" psgd_status_t psgd_timing_enable(psgd_plan_t p, int32_t enable) {

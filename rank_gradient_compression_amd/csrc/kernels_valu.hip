@@ -96,10 +96,11 @@ constexpr int pow2_at_least(int x) {
 // One wavefront: rows [row0, row0 + kWaveRows) of matrix d, all columns.  Each
 // lane keeps its VEC x R slice of Q in registers for the current column step
 // and reuses it across the wavefront's rows.
-template <int R, int VEC, bool MOM>
+template <int R, int VEC, int MODE>
 __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, const float* __restrict__ G,
                                           float* __restrict__ E, float* __restrict__ U, float beta,
-                                          const float* __restrict__ Q, float* __restrict__ P) {
+                                          const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed) {
+  constexpr bool MOM = MODE == 2;
   const int m = d.m, n = d.n;
   const int nrows = min(kWaveRows, m - row0);
   float acc[kWaveRows][R];
@@ -118,7 +119,7 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
       const int64_t idx = base + (int64_t)min(rr, nrows - 1) * n + j;
-      g[rr] = ldv<VEC>(G + idx);
+      if constexpr (MODE != 0) g[rr] = ldv<VEC>(G + idx);
       e[rr] = ldv<VEC>(E + idx);
     }
     Vec<VEC> u[kWaveRows];
@@ -131,7 +132,9 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
       if (rr < nrows) {
         const int64_t idx = base + (int64_t)rr * n + j;
         Vec<VEC> mv;
-        if constexpr (MOM) {
+        if constexpr (MODE == 0) {
+          mv = e[rr];
+        } else if constexpr (MOM) {
 #pragma unroll
           for (int c = 0; c < VEC; ++c) u[rr].v[c] = fmaf(beta, u[rr].v[c], g[rr].v[c]);
           stv<VEC>(U + idx, u[rr]);
@@ -141,7 +144,7 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
 #pragma unroll
           for (int c = 0; c < VEC; ++c) mv.v[c] = g[rr].v[c] + e[rr].v[c];
         }
-        stv<VEC>(E + idx, mv);
+        if constexpr (MODE != 0) stv<VEC>(E + idx, mv);
 #pragma unroll
         for (int k = 0; k < R; ++k)
 #pragma unroll
@@ -159,27 +162,28 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
   const int vi = lane >> SHIFT;
   if ((lane & ((1 << SHIFT) - 1)) == 0 && vi < kWaveRows * R) {
     const int rr = vi / R, k = vi % R;
-    if (rr < nrows) P[d.p_off + (int64_t)k * m + row0 + rr] = tot;
+    if (rr < nrows) P[(p_fixed >= 0 ? p_fixed : d.p_off) + (int64_t)k * m + row0 + rr] = tot;
   }
 }
 
-template <int R, bool MOM>
+template <int R, int MODE>
 __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__ mats,
-                                                     const int32_t* __restrict__ map,
+                                                     const int32_t* __restrict__ map, int wg_base,
                                                      const float* __restrict__ G, float* __restrict__ E,
                                                      float* __restrict__ U, float beta,
-                                                     const float* __restrict__ Q, float* __restrict__ P) {
-  const int wg = blockIdx.x;
+                                                     const float* __restrict__ Q, float* __restrict__ P,
+                                                     int64_t p_fixed) {
+  const int wg = blockIdx.x + wg_base;
   const MatDesc d = mats[map[wg]];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
   if (row0 >= d.m) return;
   if (d.vec == 4)
-    ef_p_wave<R, 4, MOM>(d, row0, lane, G, E, U, beta, Q, P);
+    ef_p_wave<R, 4, MODE>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
   else if (d.vec == 2)
-    ef_p_wave<R, 2, MOM>(d, row0, lane, G, E, U, beta, Q, P);
+    ef_p_wave<R, 2, MODE>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
   else
-    ef_p_wave<R, 1, MOM>(d, row0, lane, G, E, U, beta, Q, P);
+    ef_p_wave<R, 1, MODE>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,14 +204,14 @@ __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__
 constexpr int kOrthThreads = 256;
 
 template <int R>
-__global__ __launch_bounds__(kOrthThreads) void k_orth(const MatDesc* __restrict__ mats, float* __restrict__ P,
-                                                       float zero_rel) {
+__global__ __launch_bounds__(kOrthThreads) void k_orth(const OrthDesc* __restrict__ descs, int first,
+                                                       float* __restrict__ base, float zero_rel) {
   constexpr int NG = R * (R + 1) / 2;
   __shared__ double red[kOrthThreads / 64][NG];
   __shared__ double T[R][R];
-  const MatDesc d = mats[blockIdx.x];
-  const int m = d.m;
-  float* p = P + d.p_off;
+  const OrthDesc o = descs[first + blockIdx.x];
+  const int m = o.rows;
+  float* p = base + o.off;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   double g[NG];
@@ -302,12 +306,12 @@ __global__ __launch_bounds__(kOrthThreads) void k_orth(const MatDesc* __restrict
 // dot products over the block's rows.
 template <int R, int VEC>
 __device__ __forceinline__ void mtp_wave(const MatDesc& d, int rb, int j, const float* __restrict__ M,
-                                         const float* __restrict__ Ph, float* __restrict__ Q,
+                                         const float* __restrict__ Ph, int64_t ph_fixed, float* __restrict__ Q,
                                          float* __restrict__ part) {
   const int m = d.m, n = d.n;
   const int i0 = rb * d.rb_rows;
   const int i1 = min(m, i0 + d.rb_rows);
-  const float* ph = Ph + d.p_off;
+  const float* ph = Ph + (ph_fixed >= 0 ? ph_fixed : d.p_off);
   const float* mp = M + d.off + j;
   float acc[VEC][R];
 #pragma unroll
@@ -351,9 +355,10 @@ __device__ __forceinline__ void mtp_wave(const MatDesc& d, int rb, int j, const 
 
 template <int R>
 __global__ __launch_bounds__(kWGThreads) void k_mtp(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
-                                                    const float* __restrict__ M, const float* __restrict__ Ph,
+                                                    int wg_base, const float* __restrict__ M,
+                                                    const float* __restrict__ Ph, int64_t ph_fixed,
                                                     float* __restrict__ Q, float* __restrict__ part) {
-  const int wg = blockIdx.x;
+  const int wg = blockIdx.x + wg_base;
   const MatDesc d = mats[map[wg]];
   const int local = wg - d.wg_mtp0;
   const int rb = local / d.ncb, cb = local - rb * d.ncb;
@@ -361,17 +366,18 @@ __global__ __launch_bounds__(kWGThreads) void k_mtp(const MatDesc* __restrict__ 
   const int j = (cb * kMtpWaves + wave) * 64 * d.vec + lane * d.vec;
   if (j >= d.n) return;
   if (d.vec == 4)
-    mtp_wave<R, 4>(d, rb, j, M, Ph, Q, part);
+    mtp_wave<R, 4>(d, rb, j, M, Ph, ph_fixed, Q, part);
   else if (d.vec == 2)
-    mtp_wave<R, 2>(d, rb, j, M, Ph, Q, part);
+    mtp_wave<R, 2>(d, rb, j, M, Ph, ph_fixed, Q, part);
   else
-    mtp_wave<R, 1>(d, rb, j, M, Ph, Q, part);
+    mtp_wave<R, 1>(d, rb, j, M, Ph, ph_fixed, Q, part);
 }
 
 // Fixed-order sum of the row-block partials: Q[k*n + j] = sum_b part_b[k*n + j].
 __global__ __launch_bounds__(kRedCols) void k_qreduce(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
-                                                      int R, const float* __restrict__ part, float* __restrict__ Q) {
-  const int wg = blockIdx.x;
+                                                      int wg_base, int R, const float* __restrict__ part,
+                                                      float* __restrict__ Q) {
+  const int wg = blockIdx.x + wg_base;
   const MatDesc d = mats[map[wg]];
   const int64_t len = (int64_t)R * d.n;
   const int64_t idx = (int64_t)(wg - d.wg_red0) * kRedCols + threadIdx.x;
@@ -492,29 +498,32 @@ __global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, c
 // ---------------------------------------------------------------------------
 
 template <int R>
-static hipError_t launch_ef_p_r(const LaunchCtx& c, const float* G, float* E, float* U, float beta, const float* Q,
-                                float* P) {
-  if (c.wg_rows == 0) return hipSuccess;
-  if (U)
-    hipLaunchKernelGGL((k_ef_p<R, true>), dim3(c.wg_rows), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map, G, E,
-                       U, beta, Q, P);
+static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+                                float beta, const float* Q, float* P, int64_t p_fixed) {
+  if (g.count == 0) return hipSuccess;
+  const dim3 gr(g.count), b(kWGThreads);
+  if (mode == 2)
+    hipLaunchKernelGGL((k_ef_p<R, 2>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
+  else if (mode == 1)
+    hipLaunchKernelGGL((k_ef_p<R, 1>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
   else
-    hipLaunchKernelGGL((k_ef_p<R, false>), dim3(c.wg_rows), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map, G, E,
-                       U, beta, Q, P);
+    hipLaunchKernelGGL((k_ef_p<R, 0>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
   return hipGetLastError();
 }
 
 template <int R>
-static hipError_t launch_orth_r(const LaunchCtx& c, float* P) {
-  if (c.nmat == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_orth<R>), dim3(c.nmat), dim3(kOrthThreads), 0, c.stream, c.mats, P, kZeroColumnRel);
+static hipError_t launch_orth_r(const LaunchCtx& c, int first, int count, float* base) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_orth<R>), dim3(count), dim3(kOrthThreads), 0, c.stream, c.orth, first, base, kZeroColumnRel);
   return hipGetLastError();
 }
 
 template <int R>
-static hipError_t launch_mtp_r(const LaunchCtx& c, const float* M, const float* Ph, float* Q, float* part) {
-  if (c.wg_mtp == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_mtp<R>), dim3(c.wg_mtp), dim3(kWGThreads), 0, c.stream, c.mats, c.mtp_map, M, Ph, Q, part);
+static hipError_t launch_mtp_r(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph,
+                               int64_t ph_fixed, float* Q) {
+  if (g.count == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_mtp<R>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.mtp_map, g.base, M, Ph,
+                     ph_fixed, Q, c.part);
   return hipGetLastError();
 }
 
@@ -545,19 +554,24 @@ static hipError_t launch_recon_r(const LaunchCtx& c, float* E, const float* Q, c
     default: return hipErrorInvalidValue;           \
   }
 
-hipError_t launch_ef_p(const LaunchCtx& c, const float* G, float* E, float* U, float beta, const float* Q, float* P) {
-  PSGD_RANK_SWITCH(c.rank, launch_ef_p_r<RR>(c, G, E, U, beta, Q, P));
+hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+                       float beta, const float* Q, float* P, int64_t p_fixed) {
+  PSGD_RANK_SWITCH(c.rank, launch_ef_p_r<RR>(c, g, mode, G, E, U, beta, Q, P, p_fixed));
 }
 
-hipError_t launch_orth(const LaunchCtx& c, float* P) { PSGD_RANK_SWITCH(c.rank, launch_orth_r<RR>(c, P)); }
-
-hipError_t launch_mtp(const LaunchCtx& c, const float* M, const float* Ph, float* Q, float* part) {
-  PSGD_RANK_SWITCH(c.rank, launch_mtp_r<RR>(c, M, Ph, Q, part));
+hipError_t launch_orth(const LaunchCtx& c, int first, int count, float* base) {
+  PSGD_RANK_SWITCH(c.rank, launch_orth_r<RR>(c, first, count, base));
 }
 
-hipError_t launch_qreduce(const LaunchCtx& c, const float* part, float* Q) {
-  if (c.wg_red == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_qreduce, dim3(c.wg_red), dim3(kRedCols), 0, c.stream, c.mats, c.red_map, c.rank, part, Q);
+hipError_t launch_mtp(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,
+                      float* Q) {
+  PSGD_RANK_SWITCH(c.rank, launch_mtp_r<RR>(c, g, M, Ph, ph_fixed, Q));
+}
+
+hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q) {
+  if (g.count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_qreduce, dim3(g.count), dim3(kRedCols), 0, c.stream, c.mats, c.red_map, g.base, c.rank, c.part,
+                     Q);
   return hipGetLastError();
 }
 

@@ -193,20 +193,55 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   p->pt_elems = (size_t)ptoff;
 
   // Tile tables.
-  const int32_t rb = choose_rb_rows(p->mats);
-  int64_t part = 0;
-  int32_t wg_rows = 0, wg_mtp = 0, wg_red = 0;
+  const bool mfma = rank > kValuMaxRank;
+  const int64_t rp = mfma ? align_up(r, 16) : r;
+  int32_t rb = choose_rb_rows(p->mats);
+  if (mfma && rb < kMfmaRows) rb = kMfmaRows;
+  // MFMA passes 1 and 3 split the columns until the grid covers the chip.
+  int32_t s1 = 1;
+  if (mfma) {
+    int64_t base = 0;
+    for (const MatDesc& d : p->mats) base += (d.m + kMfmaRows - 1) / kMfmaRows;
+    while (base * s1 < 1024 && s1 < 64) s1 *= 2;
+  }
+  int64_t part = 0, ppart = 0, gram = 0, rscr = 0;
+  int32_t wg_rows = 0, wg_mtp = 0, wg_red = 0, wg_pred = 0, wg_gram = 0;
   for (size_t k = 0; k < p->mats.size(); ++k) {
     MatDesc& d = p->mats[k];
     d.rb_rows = rb;
     d.nrb = (d.m + rb - 1) / rb;
-    const int32_t cols_per_wg = kMtpWaves * 64 * d.vec;
+    const int32_t cols_per_wg = mfma ? kMfmaCols : kMtpWaves * 64 * d.vec;
     d.ncb = (d.n + cols_per_wg - 1) / cols_per_wg;
     d.part_off = part;
     if (d.nrb > 1) part += align_up((int64_t)d.nrb * r * d.n, kAlignElems);
-    d.gram_off = (int64_t)k * r * r;
     d.wg_rows0 = wg_rows;
-    const int32_t nrow_wg = (d.m + kRowsPerWG - 1) / kRowsPerWG;
+    int32_t nrow_wg;
+    if (mfma) {
+      int32_t sm = std::max<int32_t>(1, std::min<int32_t>(s1, d.n / 256));
+      d.s1_cols = (int32_t)align_up((d.n + sm - 1) / sm, 64);
+      d.s1 = (d.n + d.s1_cols - 1) / d.s1_cols;
+      nrow_wg = ((d.m + kMfmaRows - 1) / kMfmaRows) * d.s1;
+      d.ppart_off = ppart;
+      d.wg_pred0 = wg_pred;
+      if (d.s1 > 1) {
+        ppart += align_up((int64_t)d.s1 * r * d.m, kAlignElems);
+        const int32_t np = (int32_t)((r * d.m + kRedCols - 1) / kRedCols);
+        for (int32_t t = 0; t < np; ++t) p->pred_map.push_back((int32_t)k);
+        wg_pred += np;
+      }
+      d.ngb = (d.m + kGramRows - 1) / kGramRows;
+      d.wg_gram0 = wg_gram;
+      for (int32_t t = 0; t < d.ngb; ++t) p->gram_map.push_back((int32_t)k);
+      wg_gram += d.ngb;
+      const int64_t nb = std::max<int64_t>(d.ngb, (d.n + kGramRows - 1) / kGramRows);
+      d.gram_off = gram;
+      d.t_off = gram + nb * rp * rp;
+      gram += (nb + 1) * rp * rp;
+    } else {
+      d.s1 = 1;
+      d.s1_cols = d.n;
+      nrow_wg = (d.m + kRowsPerWG - 1) / kRowsPerWG;
+    }
     for (int32_t t = 0; t < nrow_wg; ++t) p->rows_map.push_back((int32_t)k);
     wg_rows += nrow_wg;
     d.wg_mtp0 = wg_mtp;
@@ -218,7 +253,39 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
       for (int32_t t = 0; t < nred; ++t) p->red_map.push_back((int32_t)k);
       wg_red += nred;
     }
+    // refresh scratch: P of this matrix (rank columns of m rows)
+    rscr = std::max<int64_t>(rscr, align_up((int64_t)d.m * rp, kAlignElems));
   }
+  // orthonormalisation descriptors: P of compress, P and Q of the refresh
+  const size_t nm = p->mats.size();
+  p->orth.resize(3 * nm);
+  int32_t wg_gramq = 0;
+  for (size_t k = 0; k < nm; ++k) {
+    const MatDesc& d = p->mats[k];
+    OrthDesc o{};
+    o.gram_off = d.gram_off;
+    o.t_off = d.t_off;
+    o.rows = d.m;
+    o.ngb = (d.m + kGramRows - 1) / kGramRows;
+    o.off = d.p_off;
+    o.wg0 = d.wg_gram0;
+    p->orth[k] = o;
+    o.off = 0;
+    o.wg0 = 0;
+    p->orth[nm + k] = o;
+    o.rows = d.n;
+    o.ngb = (d.n + kGramRows - 1) / kGramRows;
+    o.off = d.q_off;
+    o.wg0 = wg_gramq;
+    if (mfma) {
+      for (int32_t t = 0; t < o.ngb; ++t) p->gramq_map.push_back((int32_t)k);
+      wg_gramq += o.ngb;
+    }
+    p->orth[2 * nm + k] = o;
+  }
+  // the grouped refresh inside compress keeps its P in the refresh scratch
+  // with the P buffer's layout
+  rscr = std::max<int64_t>(rscr, (int64_t)p->p_elems);
   int32_t wg_pass = 0;
   for (size_t k = 0; k < p->pass.size(); ++k) {
     PassDesc& pd = p->pass[k];
@@ -239,6 +306,11 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   h.wg_mtp = wg_mtp;
   h.wg_red = wg_red;
   h.wg_pass = wg_pass;
+  h.wg_pred = wg_pred;
+  h.wg_gram = wg_gram;
+  h.wg_gramq = wg_gramq;
+  h.rank_pad = (int32_t)rp;
+  h.mfma = mfma ? 1 : 0;
   int64_t b = align_up(sizeof(WsHeader), 256);
   h.mat_off = b;
   b = align_up(b + (int64_t)sizeof(MatDesc) * h.nmat, 256);
@@ -252,19 +324,23 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   b = align_up(b + 4 * (int64_t)p->red_map.size(), 256);
   h.pass_map_off = b;
   b = align_up(b + 4 * (int64_t)p->pass_map.size(), 256);
+  h.pred_map_off = b;
+  b = align_up(b + 4 * (int64_t)p->pred_map.size(), 256);
+  h.gram_map_off = b;
+  b = align_up(b + 4 * (int64_t)p->gram_map.size(), 256);
+  h.gramq_map_off = b;
+  b = align_up(b + 4 * (int64_t)p->gramq_map.size(), 256);
+  h.orth_off = b;
+  b = align_up(b + (int64_t)sizeof(OrthDesc) * (int64_t)p->orth.size(), 256);
   h.tables_bytes = b;
   h.part_base = b;
   b = align_up(b + 4 * part, 256);
+  h.ppart_base = b;
+  b = align_up(b + 4 * ppart, 256);
   h.gram_base = b;
-  b = align_up(b + 8 * (int64_t)h.nmat * r * r, 256);
+  b = align_up(b + 8 * gram, 256);
   h.refresh_base = b;
-  // refresh scratch: P (m x r) and the partial sums of M^T P_hat for the
-  // largest matrix.
-  int64_t ref = 0;
-  for (const MatDesc& d : p->mats)
-    ref = std::max<int64_t>(ref, align_up((int64_t)d.m * r, kAlignElems) +
-                                     (int64_t)d.nrb * r * d.n);
-  b = align_up(b + 4 * ref, 256);
+  b = align_up(b + 4 * rscr, 256);
   h.total_bytes = b;
 
   p->tables.assign((size_t)h.tables_bytes, 0);
@@ -279,6 +355,14 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     memcpy(p->tables.data() + h.red_map_off, p->red_map.data(), 4 * p->red_map.size());
   if (!p->pass_map.empty())
     memcpy(p->tables.data() + h.pass_map_off, p->pass_map.data(), 4 * p->pass_map.size());
+  if (!p->pred_map.empty())
+    memcpy(p->tables.data() + h.pred_map_off, p->pred_map.data(), 4 * p->pred_map.size());
+  if (!p->gram_map.empty())
+    memcpy(p->tables.data() + h.gram_map_off, p->gram_map.data(), 4 * p->gram_map.size());
+  if (!p->gramq_map.empty())
+    memcpy(p->tables.data() + h.gramq_map_off, p->gramq_map.data(), 4 * p->gramq_map.size());
+  if (!p->orth.empty())
+    memcpy(p->tables.data() + h.orth_off, p->orth.data(), sizeof(OrthDesc) * p->orth.size());
 
   *out = p;
   return PSGD_OK;

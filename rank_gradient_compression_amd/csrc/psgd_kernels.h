@@ -16,27 +16,62 @@ constexpr float kZeroColumnRel = 1e-4f;
 // one plan, plus the stream every launch goes to.
 struct LaunchCtx {
   hipStream_t stream;
-  int rank;
+  int rank, rank_pad;
+  bool mfma;
   int nmat, npass;
-  int wg_rows, wg_mtp, wg_red, wg_pass;
+  int wg_rows, wg_mtp, wg_red, wg_pass, wg_pred, wg_gram, wg_gramq;
   const MatDesc* mats;
   const PassDesc* pass;
+  const OrthDesc* orth;
   const int32_t* rows_map;
   const int32_t* mtp_map;
   const int32_t* red_map;
   const int32_t* pass_map;
+  const int32_t* pred_map;
+  const int32_t* gram_map;
+  const int32_t* gramq_map;
   float* part;    // partial-Q scratch
+  float* ppart;   // partial-P scratch (MFMA pass 1 column splits)
   double* gram;   // orthonormalisation scratch
   float* rscr;    // refresh scratch
 };
 
-hipError_t launch_ef_p(const LaunchCtx& c, const float* G, float* E, float* U, float beta, const float* Q, float* P);
-hipError_t launch_orth(const LaunchCtx& c, float* P);
-hipError_t launch_mtp(const LaunchCtx& c, const float* M, const float* Ph, float* Q, float* part);
-hipError_t launch_qreduce(const LaunchCtx& c, const float* part, float* Q);
+// A contiguous range of workgroups of one of the plan's grids (the whole grid
+// for the grouped launches, one matrix's workgroups inside the refresh).
+struct GridRange {
+  int base;
+  int count;
+};
+
+// ---- ranks up to kValuMaxRank (vector ALU kernels)
+// mode 0: P = M Q with M read from E; 1: M = G + E stored over E; 2: also
+// u = beta u + G first.  p_fixed >= 0 replaces the plan's P offset.
+hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+                       float beta, const float* Q, float* P, int64_t p_fixed);
+// Orthonormalise descriptors [first, first + count) of the plan's OrthDesc table.
+hipError_t launch_orth(const LaunchCtx& c, int first, int count, float* base);
+hipError_t launch_mtp(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,
+                      float* Q);
 // residual = true: E <- M - P_hat Q^T (M read from E), M_hat written if non-null.
 // residual = false: Mhat <- P_hat Q^T only (decompression).
 hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat, bool residual);
+
+// ---- ranks above kValuMaxRank (matrix-core kernels)
+hipError_t launch_mfma_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+                         float beta, const float* Q, float* P, int64_t p_fixed);
+hipError_t launch_psum(const LaunchCtx& c, const GridRange& g, float* P, int64_t p_fixed);
+hipError_t launch_mfma_qt(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,
+                          float* Q);
+hipError_t launch_mfma_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
+                             bool residual);
+// With a map: descriptors first + [0, count) over a grouped Gram grid of
+// nblocks workgroups (map gives the matrix of each workgroup).  Without: the
+// single descriptor `first` with nblocks Gram blocks.
+hipError_t launch_gram_orth(const LaunchCtx& c, int first, int count, const int32_t* map, int nblocks,
+                            float* base);
+
+// ---- shared
+hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q);
 hipError_t launch_pass_pack(const LaunchCtx& c, const float* G, float* U, float beta, float* Pbuf);
 hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out);
 hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);

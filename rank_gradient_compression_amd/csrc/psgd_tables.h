@@ -27,13 +27,21 @@ constexpr int kValuMaxRank = 8;
 // Alignment (elements) of every region the plan lays out.
 constexpr int64_t kAlignElems = 64;
 
+// Tiles of the MFMA kernels (ranks above kValuMaxRank, padded to a multiple
+// of 16).
+constexpr int kMfmaRows = 64;      // rows of one MFMA pass-1 / pass-3 workgroup tile
+constexpr int kMfmaCols = 256;     // columns of one MFMA pass-2 workgroup tile
+constexpr int kGramRows = 128;     // rows of one Gram-partial workgroup
+
 // One compressed matrix.
 struct MatDesc {
   int64_t off;       // flat element offset of row 0 in grads/err/mom/mhat
   int64_t p_off;     // P / P_hat: rank columns of m floats from here
   int64_t q_off;     // Q: rank columns of n floats from here
   int64_t part_off;  // partial-Q scratch (floats, from the scratch base)
-  int64_t gram_off;  // orthonormalisation scratch (doubles, from its base)
+  int64_t gram_off;  // Gram partials (doubles, from the Gram scratch base)
+  int64_t ppart_off; // partial-P scratch of the MFMA pass 1 (floats)
+  int64_t t_off;     // triangular factor T (doubles, from the Gram scratch base)
   int32_t m, n;
   int32_t vec;       // 4, 2 or 1: widest vector access both n and off allow
   int32_t nrb;       // row blocks of the M^T P_hat pass
@@ -42,9 +50,14 @@ struct MatDesc {
   int32_t wg_rows0;  // first workgroup of this matrix in the row-tile grid
   int32_t wg_mtp0;   // first workgroup of this matrix in the M^T P_hat grid
   int32_t wg_red0;   // first workgroup of this matrix in the Q-reduce grid
-  int32_t pad_;
+  int32_t s1;        // MFMA passes 1 and 3: column splits
+  int32_t s1_cols;   // MFMA passes 1 and 3: columns per split (multiple of 64)
+  int32_t wg_pred0;  // first workgroup in the P-partial reduce grid (s1 > 1)
+  int32_t wg_gram0;  // first workgroup in the Gram-partial / apply grid
+  int32_t ngb;       // Gram-partial blocks (kGramRows rows each)
+  int32_t pad_[4];
 };
-static_assert(sizeof(MatDesc) == 80, "MatDesc layout");
+static_assert(sizeof(MatDesc) == 128, "MatDesc layout");
 
 // One pass-through tensor: `len` elements at flat offset `off`, packed at
 // `p_off` (absolute, in the P buffer).
@@ -53,6 +66,19 @@ struct PassDesc {
   int64_t p_off;
   int64_t len;
   int64_t wg0;  // first workgroup of this tensor in the pass-through grid
+};
+
+// One factor to orthonormalise (P of a matrix, or Q / P inside the refresh):
+// `rows` x rank, column-major with leading dimension `rows`, from element
+// `off` of the buffer given at launch.
+struct OrthDesc {
+  int64_t off;
+  int64_t gram_off;  // Gram partials (doubles, from the Gram scratch base)
+  int64_t t_off;     // triangular factor T (doubles)
+  int32_t rows;
+  int32_t ngb;       // Gram-partial blocks of kGramRows rows
+  int32_t wg0;       // first workgroup in the grouped Gram grid
+  int32_t pad_;
 };
 
 constexpr int kPassChunk = 4096;  // elements per pass-through workgroup
@@ -64,14 +90,20 @@ struct WsHeader {
   int32_t nmat, npass;
   int32_t rank, flags;
   int32_t wg_rows, wg_mtp, wg_red, wg_pass;
+  int32_t wg_pred, wg_gram, wg_gramq, rank_pad, mfma, pad_;
   int64_t mat_off;       // bytes from workspace start: MatDesc[nmat]
   int64_t pass_off;      // PassDesc[npass]
   int64_t rows_map_off;  // int32 matrix index per row-tile workgroup
   int64_t mtp_map_off;   // int32 per M^T P_hat workgroup
   int64_t red_map_off;   // int32 per Q-reduce workgroup
   int64_t pass_map_off;  // int32 pass-through tensor per pass-through workgroup
+  int64_t pred_map_off;  // int32 per P-partial reduce workgroup (MFMA path)
+  int64_t gram_map_off;  // int32 per Gram-partial / apply workgroup (MFMA path)
+  int64_t gramq_map_off; // int32 per Gram workgroup over the Q factors (refresh)
+  int64_t orth_off;      // OrthDesc[3 * nmat]: P of compress, refresh P, refresh Q
   int64_t tables_bytes;  // bytes of the table part (uploaded by workspace_init)
   int64_t part_base;     // bytes: partial-Q scratch (float)
+  int64_t ppart_base;    // bytes: partial-P scratch (float, MFMA path)
   int64_t gram_base;     // bytes: orthonormalisation scratch (double)
   int64_t refresh_base;  // bytes: refresh scratch (float)
   int64_t total_bytes;

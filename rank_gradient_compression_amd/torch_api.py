@@ -96,12 +96,13 @@ class PowerSGD:
     def _stream() -> int:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
 
-    def compress(self, mhat: bool = False, hook=None, mhat_buf: Optional[torch.Tensor] = None) -> None:
+    def compress(self, mhat: bool = False, hook=None, mhat_buf: Optional[torch.Tensor] = None,
+                 refresh_iters: int = 0) -> None:
         out = mhat_buf if mhat_buf is not None else (self.mhat if mhat else None)
         B.psgd_compress(self.plan, self.grads.data_ptr(), self.err.data_ptr(),
                         self.mom.data_ptr() if self.mom is not None else 0, self.q.data_ptr(), self.p.data_ptr(),
-                        out.data_ptr() if out is not None else 0, hook, self.workspace.data_ptr(), self.ws_bytes,
-                        self._stream())
+                        out.data_ptr() if out is not None else 0, refresh_iters, hook, self.workspace.data_ptr(),
+                        self.ws_bytes, self._stream())
 
     def decompress(self, out: Optional[torch.Tensor] = None) -> torch.Tensor:
         out = out if out is not None else self.mhat

@@ -160,8 +160,8 @@ def _compress(plan, **kw):
     a = dict(grads=FAKE, err=FAKE, mom=0, q=FAKE, pbuf=FAKE, mhat=0, hook=None, workspace=FAKE * 2,
              workspace_bytes=1 << 40)
     a.update(kw)
-    R.psgd_compress(plan, a["grads"], a["err"], a["mom"], a["q"], a["pbuf"], a["mhat"], a["hook"], a["workspace"],
-                    a["workspace_bytes"], 0)
+    R.psgd_compress(plan, a["grads"], a["err"], a["mom"], a["q"], a["pbuf"], a["mhat"], a.get("refresh", 0), a["hook"],
+                    a["workspace"], a["workspace_bytes"], 0)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -176,6 +176,7 @@ def _compress(plan, **kw):
     (dict(workspace=0), B.PSGD_ERR_WORKSPACE),
     (dict(workspace=FAKE + 64), B.PSGD_ERR_WORKSPACE),
     (dict(workspace_bytes=16), B.PSGD_ERR_WORKSPACE),
+    (dict(refresh=-1), B.PSGD_ERR_INVALID_ARG),
 ])
 def test_compress_argument_errors(kw, status):
     p = R.psgd_plan_create([64, 9], [48, 1], 2)
@@ -200,8 +201,22 @@ def test_momentum_plan_requires_mom():
 
 
 def test_decompress_and_refresh_argument_errors():
-    p = R.psgd_plan_create([64], [48], 2)
+    p = R.psgd_plan_create([64, 5], [48, 1], 2)
     try:
+        for args, status in [((0, FAKE, FAKE, 8), B.PSGD_ERR_INVALID_ARG),    # M null
+                             ((1, FAKE, FAKE, 8), B.PSGD_ERR_INVALID_ARG),    # vector tensor
+                             ((2, FAKE, FAKE, 8), B.PSGD_ERR_INVALID_ARG),    # out of range
+                             ((0, FAKE + 4, FAKE, 8), B.PSGD_ERR_INVALID_ARG),
+                             ((0, FAKE, FAKE, -1), B.PSGD_ERR_INVALID_ARG)]:
+            t, mptr, qptr, it = args
+            if args[0] == 0 and mptr == FAKE and it == 8:
+                mptr = 0
+            with pytest.raises(B.PsgdError) as e:
+                R.psgd_refresh(p, t, mptr, qptr, it, FAKE * 2, 1 << 40, 0)
+            assert e.value.status == status, (args, e.value)
+        with pytest.raises(B.PsgdError) as e:
+            R.psgd_refresh(p, 0, FAKE, FAKE, 8, FAKE * 2, 16, 0)
+        assert e.value.status == B.PSGD_ERR_WORKSPACE
         with pytest.raises(B.PsgdError) as e:
             R.psgd_decompress(p, FAKE, FAKE, FAKE, 0, 1 << 30, 0)
         assert e.value.status == B.PSGD_ERR_WORKSPACE
