@@ -1,20 +1,25 @@
 """Throughput of the PowerSGD compression step on one MI355X.
 
-Workload: the 7B-transformer shaped gradient set (32 layers of q,k,v,o
-4096x4096, gate/up 11008x4096, down 4096x11008, plus 32000x4096 embedding and
-head: 226 fp32 matrices, 6,738,149,376 elements), rank 4.  A step is one
-psgd_compress call with the fused decompression: EF-add, P = M Q,
+Default workload: the 7B-transformer shaped gradient set (32 layers of
+q,k,v,o 4096x4096, gate/up 11008x4096, down 4096x11008, plus 32000x4096
+embedding and head: 226 fp32 matrices, 6,738,149,376 elements), rank 4.  A
+step is one psgd_compress call with the fused decompression: EF-add, P = M Q,
 orthogonalisation, Q = M^T P_hat, residual E = M - P_hat Q^T and M_hat, all in
 the library's HIP kernels.  The gradients are synthetic (seeded rank-16 signal
 plus Gaussian noise, unit Frobenius norm per matrix) and resident in HBM
 before timing starts.
 
-Prints ONE JSON line.  `value` is gradient GB compressed per second
-(4 bytes x elements / step time).
+Other workloads (--workload): `sweep` (11008x4096 at ranks 1..64),
+`refresh` (PowerSGD+ refresh, 8 iterations at rank 32 on 8192x8192),
+`resnet18` (rank 2), `lstm3` (rank 4).  Each prints its own JSON line.
+
+Prints ONE JSON line per workload (per rank for the sweep).  `value` is
+gradient GB compressed per second (4 bytes x elements / step time).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -26,11 +31,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "gradient GB compressed/s (EF+P+Q+E) and % HBM peak, 1×MI355X, r=2/4"
 HBM_PEAK_GBS = 8000.0
-# Algorithmic HBM bytes per gradient element for each kernel (fp32):
-#   EF-add + P = M Q: read G, E, write M                  12 (20 with momentum: + read/write u)
-#   Q = M^T P_hat: read M                                  4
-#   residual (+ M_hat): read M, write E (+ write M_hat)    8 (12)
-B_STAGE = {"ef_p": 12.0, "mtp": 4.0, "residual": 8.0}
+MFMA_FP32_PEAK_TFLOPS = 157.3
+KERNEL_OF_STAGE = {"ef_p": "k_ef_p", "mtp": "k_mtp", "residual": "k_recon"}
+KERNEL_OF_STAGE_MFMA = {"ef_p": "k_mfma_p", "mtp": "k_mfma_qt", "residual": "k_mfma_recon"}
 
 
 def log(*a):
@@ -42,20 +45,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rank", type=int, default=4)
+    ap.add_argument("--workload", default="llama7b", choices=["llama7b", "sweep", "refresh", "resnet18", "lstm3"])
+    ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-variants", action="store_true", help="skip the plain-compress and momentum lines")
+    ap.add_argument("--no-variants", action="store_true", help="skip the plain-compress and momentum figures")
     ap.add_argument("--no-stage-timing", action="store_true")
     return ap.parse_args()
 
 
-KERNEL_OF_STAGE = {"ef_p": "k_ef_p", "mtp": "k_mtp", "residual": "k_recon"}
-
-
 def source_hash():
-    import hashlib
-
     csrc = os.path.join(ROOT, "rank_gradient_compression_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
@@ -65,13 +64,11 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(stage, rank, mhat):
-    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None when the summary does not cover
-    this configuration or the library sources changed since it was taken."""
-    if rank != 4 or not mhat:
-        return None
-    path = os.path.join(ROOT, "profiles", "hbm_bytes_llama7b_r4_fused.md")
+def measured_traffic(kernel, profile):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when there is none or the
+    library sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", profile)
     try:
         text = open(path).read()
         blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
@@ -80,170 +77,260 @@ def measured_traffic(stage, rank, mhat):
     if blob.get("source_hash") != source_hash():
         return None
     for name, v in blob["kernels"].items():
-        if KERNEL_OF_STAGE.get(stage, "?") in name:
+        if kernel in name:
             return v["read_bytes"] + v["write_bytes"]
     return None
 
 
-def stage_roofline(plan, B, n_steps, dense, momentum=False, mhat=True):
+def stage_table(B, plan, bytes_per_el, flops_per_el, elems):
+    """Per-stage average launch time from the library's HIP events and the
+    algorithmic bytes / flops of one launch."""
     ms, n = B.psgd_timing_read(plan)
-    stages = {}
+    out = {}
     for i, name in enumerate(B.STAGE_NAMES):
-        if n[i]:
-            stages[name] = {"ms_avg": ms[i] / n[i], "launches": n[i]}
-    b = dict(B_STAGE)
-    if momentum:
-        b["ef_p"] = 20.0
-    if mhat:
-        b["residual"] = 12.0
-    for name, s in stages.items():
-        if name in b:
-            s["bytes_alg"] = b[name] * dense
-            s["gbs"] = s["bytes_alg"] / (s["ms_avg"] * 1e-3) / 1e9
+        if not n[i]:
+            continue
+        s = {"ms_avg": ms[i] / n[i], "launches": n[i]}
+        if name in bytes_per_el:
+            s["bytes_alg"] = bytes_per_el[name] * elems
+            s["flops_alg"] = flops_per_el[name] * elems
+            t = s["ms_avg"] * 1e-3
+            s["gbs"] = s["bytes_alg"] / t / 1e9
+            s["tflops"] = s["flops_alg"] / t / 1e12
             s["frac_hbm"] = s["gbs"] / HBM_PEAK_GBS
-    return stages
+            s["frac_mfma"] = s["tflops"] / MFMA_FP32_PEAK_TFLOPS
+        out[name] = s
+    return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU aggregation is a caller hook "
-                          "(all-reduce of P and Q) and is not benchmarked here", "n_gpus": args.gpus}))
-        sys.exit(2)
+def roofline_of(stages, mfma, profile=None):
+    cand = [s for s in stages if "bytes_alg" in stages[s]]
+    if not cand:
+        return None
+    dom = max(cand, key=lambda s: stages[s]["ms_avg"] * stages[s]["launches"])
+    d = stages[dom]
+    ridge = MFMA_FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    kernel = (KERNEL_OF_STAGE_MFMA if mfma else KERNEL_OF_STAGE)[dom]
+    tr = measured_traffic(kernel, profile) if profile else None
+    if mfma and d["flops_alg"] / d["bytes_alg"] > ridge:
+        return {"bound": "mfma", "kernel": kernel, "achieved": round(d["tflops"], 2), "peak": MFMA_FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(d["frac_mfma"], 4), "traffic": round(tr) if tr else None,
+                "alg_flops_per_launch": d["flops_alg"], "avg_launch_ms": round(d["ms_avg"], 4)}
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(d["frac_hbm"], 4), "traffic": round(tr) if tr else None,
+            "alg_bytes_per_launch": d["bytes_alg"], "avg_launch_ms": round(d["ms_avg"], 4)}
 
-    import torch
 
-    import workloads as W
-    from rank_gradient_compression_amd import binding as B
-    from rank_gradient_compression_amd.torch_api import PowerSGD
+def round_stages(stages):
+    return {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in stages.items()}
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    tensors = W.llama7b_set(args.layers)
-    shapes = [s for _, s in tensors]
-    rank = args.rank
-    log(f"bench: building plan for {len(shapes)} matrices, rank {rank}")
-    ps = PowerSGD(shapes, rank, device=dev, with_mhat=True)
-    dense = ps.info["dense_elems"]
-    log(f"bench: generating {dense} synthetic gradient elements on the device")
-    t0 = time.time()
-    for i, (_, s) in enumerate(tensors):
-        W.llama7b_grad_(ps.view(ps.grads, i), s[0], s[1], i, step=1)
-        ps.set_q(i, W.llama7b_q0(s[1], rank, i, device=dev))
-    torch.cuda.synchronize()
-    log(f"bench: inputs ready in {time.time() - t0:.1f} s")
-    stream = torch.cuda.current_stream()
 
-    def run(label, call, steps, warmup, stage_timing=True):
+class Runner:
+    def __init__(self, torch, B):
+        self.torch, self.B = torch, B
+        self.stream = torch.cuda.current_stream()
+
+    def time(self, label, call, steps, warmup, plan=None):
+        torch, B = self.torch, self.B
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
-        B.psgd_timing_read(ps.plan)  # drop warm-up records
-        if stage_timing:
-            B.psgd_timing_enable(ps.plan, True)
+        if plan is not None:
+            B.psgd_timing_read(plan)  # drop warm-up records
+            B.psgd_timing_enable(plan, True)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
-        ev[0].record(stream)
+        ev[0].record(self.stream)
         for k in range(steps):
             call()
-            ev[k + 1].record(stream)
+            ev[k + 1].record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
-        B.psgd_timing_enable(ps.plan, False)
+        if plan is not None:
+            B.psgd_timing_enable(plan, False)
         per = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
         total_ms = ev[0].elapsed_time(ev[steps])
-        log(f"bench: {label}: {total_ms / steps:.3f} ms/step (median {statistics.median(per):.3f}, "
-            f"wall {wall * 1e3 / steps:.3f})")
+        log(f"bench: {label}: {total_ms / steps:.4f} ms/step (median {statistics.median(per):.4f}, "
+            f"wall {wall * 1e3 / steps:.4f})")
         return total_ms / steps, per
 
-    # stream-copy ceiling on a 4 GiB buffer
-    ncopy = 1 << 30
-    src = torch.empty(ncopy, dtype=torch.float32, device=dev).normal_()
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        B.psgd_stream_copy(dst.data_ptr(), src.data_ptr(), ncopy, stream.cuda_stream)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(5):
-        B.psgd_stream_copy(dst.data_ptr(), src.data_ptr(), ncopy, stream.cuda_stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 5 * 8 * ncopy / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
-    torch.cuda.empty_cache()
-    log(f"bench: stream copy ceiling {copy_gbs:.0f} GB/s")
+    def copy_ceiling(self, n=1 << 30):
+        torch, B = self.torch, self.B
+        src = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        ms, _ = self.time("stream copy 4 GiB", lambda: B.psgd_stream_copy(dst.data_ptr(), src.data_ptr(), n,
+                                                                            self.stream.cuda_stream), 5, 2)
+        del src, dst
+        torch.cuda.empty_cache()
+        return 8 * n / (ms * 1e-3) / 1e9
 
-    # headline: compress + fused decompression
-    fused = lambda: ps.compress(mhat=True)  # noqa: E731
-    ms_step, per = run("compress+decompress (fused)", fused, args.steps, args.warmup,
-                       stage_timing=not args.no_stage_timing)
-    stages = stage_roofline(ps.plan, B, args.steps, dense, mhat=True) if not args.no_stage_timing else {}
-    grad_gbs = 4.0 * dense / (ms_step * 1e-3) / 1e9
-    alg_bytes = 28.0 * dense
-    result = {
-        "metric": METRIC,
-        "value": round(grad_gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": f"7B-shaped gradient set: {len(shapes)} fp32 matrices, {dense} elements, rank {rank}, "
-                        "compress with fused decompression (EF+P+Q+E+M_hat)",
-            "rank": rank,
-            "matrices": len(shapes),
-            "elements": dense,
-            "alg_bytes_per_step": alg_bytes,
-            "step_hbm_frac": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "median_ms": round(statistics.median(per), 4),
-            "p10_ms": round(sorted(per)[max(0, int(0.1 * len(per)) - 0)], 4),
-            "p90_ms": round(sorted(per)[min(len(per) - 1, int(0.9 * len(per)))], 4),
-            "copy_ceiling_gbs": round(copy_gbs, 1),
-        },
-    }
-    if stages:
-        dom = max((s for s in stages if s in B_STAGE), key=lambda s: stages[s]["ms_avg"] * stages[s]["launches"])
-        d = stages[dom]
-        tr = measured_traffic(dom, rank, True)
-        result["roofline"] = {"bound": "hbm", "kernel": KERNEL_OF_STAGE[dom], "achieved": round(d["gbs"], 1),
-                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d["gbs"] / HBM_PEAK_GBS, 4),
-                              "traffic": round(tr) if tr else None,
-                              "alg_bytes_per_launch": d["bytes_alg"], "avg_launch_ms": round(d["ms_avg"], 4)}
-        result["stages"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                            for k, v in stages.items()}
 
+def base_result(args, value, ms_step, per, workload, extra):
+    cfg = {"workload": workload}
+    cfg.update(extra)
+    cfg["median_ms"] = round(statistics.median(per), 4)
+    srt = sorted(per)
+    cfg["p10_ms"] = round(srt[int(0.1 * (len(srt) - 1))], 4)
+    cfg["p90_ms"] = round(srt[int(round(0.9 * (len(srt) - 1)))], 4)
+    return {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg}
+
+
+def step_bytes(rank_mfma, momentum=False, mhat=True):
+    b = {"ef_p": 20.0 if momentum else 12.0, "mtp": 4.0, "residual": 12.0 if mhat else 8.0}
+    return b
+
+
+def step_flops(r, momentum=False):
+    return {"ef_p": 2.0 * r + (3.0 if momentum else 1.0), "mtp": 2.0 * r, "residual": 2.0 * r + 1.0}
+
+
+# --------------------------------------------------------------------------- workloads
+
+def run_llama7b(args, torch, B, W, PowerSGD, R):
+    rank = args.rank or 4
+    tensors = W.llama7b_set(args.layers)
+    shapes = [s for _, s in tensors]
+    log(f"bench: plan for {len(shapes)} matrices, rank {rank}")
+    ps = PowerSGD(shapes, rank, device="cuda", with_mhat=True)
+    dense = ps.info["dense_elems"]
+    t0 = time.time()
+    for i, (_, s) in enumerate(tensors):
+        W.llama7b_grad_(ps.view(ps.grads, i), s[0], s[1], i, step=1)
+        ps.set_q(i, W.llama7b_q0(s[1], rank, i, device="cuda"))
+    torch.cuda.synchronize()
+    log(f"bench: {dense} synthetic gradient elements ready in {time.time() - t0:.1f} s")
+    copy_gbs = R.copy_ceiling()
+    ms, per = R.time("compress + fused decompress", lambda: ps.compress(mhat=True), args.steps, args.warmup,
+                     plan=None if args.no_stage_timing else ps.plan)
+    mfma = rank > 8
+    res = base_result(args, 4.0 * dense / (ms * 1e-3) / 1e9, ms, per,
+                      f"7B-shaped gradient set: {len(shapes)} fp32 matrices, {dense} elements, rank {rank}, "
+                      "compress with fused decompression (EF+P+Q+E+M_hat)",
+                      {"rank": rank, "matrices": len(shapes), "elements": dense, "alg_bytes_per_step": 28.0 * dense,
+                       "step_hbm_frac": round(28.0 * dense / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "copy_ceiling_gbs": round(copy_gbs, 1)})
+    if not args.no_stage_timing:
+        st = stage_table(B, ps.plan, step_bytes(mfma), step_flops(rank), dense)
+        res["roofline"] = roofline_of(st, mfma, "hbm_bytes_llama7b_r4_fused.md" if rank == 4 else None)
+        res["stages"] = round_stages(st)
     if not args.no_variants:
-        ms_c, _ = run("compress only", lambda: ps.compress(mhat=False), max(3, args.steps // 2), 1,
-                      stage_timing=False)
-        result["config"]["compress_only"] = {"ms_per_step": round(ms_c, 4),
-                                             "grad_gbs": round(4.0 * dense / (ms_c * 1e-3) / 1e9, 2),
-                                             "hbm_frac": round(24.0 * dense / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        ms_c, _ = R.time("compress only", lambda: ps.compress(mhat=False), max(3, args.steps // 2), 1)
+        res["config"]["compress_only"] = {"ms_per_step": round(ms_c, 4),
+                                          "grad_gbs": round(4.0 * dense / (ms_c * 1e-3) / 1e9, 2),
+                                          "hbm_frac": round(24.0 * dense / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         ps.close()
         del ps
         torch.cuda.empty_cache()
-        psm = PowerSGD(shapes, rank, device=dev, momentum_beta=0.9, with_mhat=False)
+        psm = PowerSGD(shapes, rank, device="cuda", momentum_beta=0.9, with_mhat=False)
         for i, (_, s) in enumerate(tensors):
             W.llama7b_grad_(psm.view(psm.grads, i), s[0], s[1], i, step=1)
-            psm.set_q(i, W.llama7b_q0(s[1], rank, i, device=dev))
+            psm.set_q(i, W.llama7b_q0(s[1], rank, i, device="cuda"))
         torch.cuda.synchronize()
-        ps = psm
-        ms_m, _ = run("momentum compress", lambda: psm.compress(mhat=False), max(3, args.steps // 2), 1,
-                      stage_timing=False)
-        result["config"]["momentum_compress"] = {"beta": 0.9, "ms_per_step": round(ms_m, 4),
-                                                 "grad_gbs": round(4.0 * dense / (ms_m * 1e-3) / 1e9, 2),
-                                                 "hbm_frac": round(32.0 * dense / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                                                   4)}
+        ms_m, _ = R.time("momentum compress (beta 0.9)", lambda: psm.compress(mhat=False), max(3, args.steps // 2), 1)
+        res["config"]["momentum_compress"] = {"beta": 0.9, "ms_per_step": round(ms_m, 4),
+                                              "grad_gbs": round(4.0 * dense / (ms_m * 1e-3) / 1e9, 2),
+                                              "hbm_frac": round(32.0 * dense / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        psm.close()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(tensors, rank)
-    print(json.dumps(result), flush=True)
+        res["cpu_baseline"] = cpu_baseline(tensors, rank)
+    print(json.dumps(res), flush=True)
+
+
+def device_decaying(torch, W, m, n, seed, K=512):
+    """sigma_k = exp(-k/20) matrix: seeded orthonormal factors from the
+    workload generator's host QR, product formed on the device in fp64."""
+    import numpy as np
+
+    K = min(K, m, n)
+    g = W.rng(seed, m, n)
+    U = torch.from_numpy(W.orthonormal(g, m, K)).cuda()
+    V = torch.from_numpy(W.orthonormal(g, n, K)).cuda()
+    s = torch.from_numpy(np.exp(-np.arange(1, K + 1, dtype=np.float64) / 20.0)).cuda()
+    return ((U * s) @ V.T).float()
+
+
+def run_sweep(args, torch, B, W, PowerSGD, R):
+    m, n = 11008, 4096
+    ranks = [args.rank] if args.rank else [1, 2, 4, 7, 16, 32, 64]
+    A = device_decaying(torch, W, m, n, 5)
+    for r in ranks:
+        ps = PowerSGD([(m, n)], r, device="cuda")
+        ps.view(ps.grads, 0).copy_(A)
+        ps.set_q(0, torch.from_numpy(W.gaussian_q0(n, r, 5)))
+        ms, per = R.time(f"11008x4096 r={r}", lambda: ps.compress(mhat=True), args.steps, args.warmup,
+                         plan=None if args.no_stage_timing else ps.plan)
+        mfma = r > 8
+        res = base_result(args, 4.0 * m * n / (ms * 1e-3) / 1e9, ms, per,
+                          f"one 11008x4096 fp32 matrix (sigma_k = exp(-k/20)), rank {r}, compress with fused "
+                          "decompression", {"rank": r, "elements": m * n, "path": "mfma" if mfma else "valu",
+                                            "step_hbm_frac": round(28.0 * m * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                                                   4)})
+        if not args.no_stage_timing:
+            st = stage_table(B, ps.plan, step_bytes(mfma), step_flops(r), m * n)
+            res["roofline"] = roofline_of(st, mfma)
+            res["stages"] = round_stages(st)
+        print(json.dumps(res), flush=True)
+        ps.close()
+
+
+def run_refresh(args, torch, B, W, PowerSGD, R):
+    m = n = 8192
+    r = args.rank or 32
+    iters = 8
+    A = device_decaying(torch, W, m, n, 5)
+    ps = PowerSGD([(m, n)], r, device="cuda")
+    mbuf = torch.zeros_like(ps.grads)
+    ps.view(mbuf, 0).copy_(A)
+    q0 = torch.from_numpy(W.gaussian_q0(n, r, 5)).cuda()
+
+    def call():
+        ps.set_q(0, q0)
+        ps.refresh(0, mbuf, iters)
+
+    ms, per = R.time(f"refresh 8192^2 r={r} x{iters}", call, args.steps, args.warmup,
+                     plan=None if args.no_stage_timing else ps.plan)
+    flops = iters * 4.0 * m * n * r
+    res = base_result(args, 4.0 * m * n / (ms * 1e-3) / 1e9, ms, per,
+                      f"PowerSGD+ subspace refresh: {iters} rounds of orthonormalised block power iteration at rank "
+                      f"{r} on one 8192x8192 fp32 matrix (sigma_k = exp(-k/20))",
+                      {"rank": r, "iterations": iters, "elements": m * n, "alg_flops": flops,
+                       "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                       "alg_bytes": iters * 8.0 * m * n,
+                       "hbm_frac": round(iters * 8.0 * m * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    if not args.no_stage_timing:
+        st = stage_table(B, ps.plan, {"ef_p": 4.0, "mtp": 4.0}, {"ef_p": 2.0 * r, "mtp": 2.0 * r}, m * n)
+        res["roofline"] = roofline_of(st, r > 8)
+        res["stages"] = round_stages(st)
+    print(json.dumps(res), flush=True)
+
+
+def run_small_set(args, torch, B, W, PowerSGD, R, name):
+    if name == "resnet18":
+        tensors, kind, seed, rank = W.resnet18_cifar_set(), "resnet18", 2, args.rank or 2
+    else:
+        tensors, kind, seed, rank = W.lstm3_wikitext_set(), "lstm3", 3, args.rank or 4
+    wl = W.ModelSetWorkload(tensors, kind, seed)
+    shapes = [s for _, s in tensors]
+    ps = PowerSGD(shapes, rank, device="cuda")
+    for i in range(len(shapes)):
+        ps.view(ps.grads, i).copy_(torch.from_numpy(wl.grad(i, 1)).cuda())
+        if ps.kind(i) == B.PSGD_KIND_COMPRESSED:
+            ps.set_q(i, wl.q0(i, rank))
+    dense = ps.info["dense_elems"]
+    ms, per = R.time(f"{name} r={rank}", lambda: ps.compress(mhat=True), args.steps, args.warmup,
+                     plan=None if args.no_stage_timing else ps.plan)
+    res = base_result(args, 4.0 * dense / (ms * 1e-3) / 1e9, ms, per,
+                      f"{name}-shaped gradient set, rank {rank}, compress with fused decompression (working set "
+                      "fits the 256 MB last-level cache)", {"rank": rank, "elements": dense,
+                                                           "tensors": len(shapes)})
+    if not args.no_stage_timing:
+        st = stage_table(B, ps.plan, step_bytes(False), step_flops(rank), dense)
+        res["roofline"] = roofline_of(st, rank > 8)
+        res["stages"] = round_stages(st)
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(tensors, rank):
@@ -278,13 +365,37 @@ def cpu_baseline(tensors, rank):
         del res, G, E
         detail[f"{m}x{n}"] = {"s": round(dt, 3), "count": c}
         total += dt * c
-    dense = sum(a * b for (a, b), c in counts.items() for _ in range(c))
+    dense = sum(a * b * c for (a, b), c in counts.items())
     return {"value": round(4.0 * dense / total / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": "one fp64 oracle step per distinct matrix shape (" + ", ".join(detail) + "), "
-                      f"scaled by shape counts to the {len(tensors)}-matrix set: extrapolated "
-                      f"{total:.1f} s per step",
+            "sample": "one fp64 oracle step (EF-add, P, Gram-Schmidt, Q, residual) per distinct matrix shape ("
+                      + ", ".join(detail) + f"), scaled by the shape counts to the {len(tensors)}-matrix set: "
+                      f"extrapolated {total:.1f} s per step",
             "host_cores": cores, "detail": detail}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the aggregation between workers is a caller hook "
+                          "(all-reduce of P and Q) and is not benchmarked here", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import workloads as W
+    from rank_gradient_compression_amd import binding as B
+    from rank_gradient_compression_amd.torch_api import PowerSGD
+
+    torch.cuda.set_device(0)
+    R = Runner(torch, B)
+    if args.workload == "llama7b":
+        run_llama7b(args, torch, B, W, PowerSGD, R)
+    elif args.workload == "sweep":
+        run_sweep(args, torch, B, W, PowerSGD, R)
+    elif args.workload == "refresh":
+        run_refresh(args, torch, B, W, PowerSGD, R)
+    else:
+        run_small_set(args, torch, B, W, PowerSGD, R, args.workload)
 
 
 if __name__ == "__main__":

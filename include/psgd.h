@@ -78,7 +78,7 @@ typedef enum psgd_status {
 #define PSGD_STAGE_QREDUCE 3   /* fixed-order reduction of the partials      */
 #define PSGD_STAGE_RESIDUAL 4  /* E = M - P_hat Q^T (+ M_hat)                */
 #define PSGD_STAGE_PASSTHRU 5  /* pass-through packing / unpacking           */
-#define PSGD_STAGE_REFRESH 6   /* PowerSGD+ subspace refresh                 */
+#define PSGD_STAGE_REFRESH 6   /* PowerSGD+ refresh inside psgd_compress      */
 #define PSGD_NSTAGES 7
 
 typedef struct psgd_plan* psgd_plan_t;
@@ -226,7 +226,8 @@ psgd_status_t psgd_refresh(psgd_plan_t plan, int32_t tensor, const float* m, flo
 /*
  * Per-stage timing with HIP events recorded on the call's stream.  While
  * enabled, every compress / decompress / refresh call records one event pair
- * per stage it runs.  psgd_timing_read waits for the recorded events, adds
+ * per stage it runs (psgd_refresh records its products under EF_P, MTP and
+ * QREDUCE and its orthonormalisations under GS).  psgd_timing_read waits for the recorded events, adds
  * the elapsed milliseconds per stage into ms[PSGD_NSTAGES] (and the number of
  * launches per stage into launches[], nullable), and clears the record.
  */

@@ -128,13 +128,11 @@ static hipError_t stage_mq(const psgd_plan* p, const LaunchCtx& c, const GridRan
 // Orthonormalise the P factors of all matrices (P in `base` at the plan's
 // offsets).
 static hipError_t stage_orth_all_p(const LaunchCtx& c, float* base) {
-  if (!c.mfma) return launch_orth(c, 0, c.nmat, base);
   return launch_gram_orth(c, 0, c.nmat, c.gram_map, c.wg_gram, base);
 }
 
 // Orthonormalise the Q factors of all matrices (the refresh).
 static hipError_t stage_orth_all_q(const LaunchCtx& c, float* q) {
-  if (!c.mfma) return launch_orth(c, 2 * c.nmat, c.nmat, q);
   return launch_gram_orth(c, 2 * c.nmat, c.nmat, c.gramq_map, c.wg_gramq, q);
 }
 
@@ -344,15 +342,19 @@ extern "C" psgd_status_t psgd_refresh(psgd_plan_t p, int32_t tensor, const float
   const int op = c.nmat + (int)k, oq = 2 * c.nmat + (int)k;
   const int nb_p = (d.m + kGramRows - 1) / kGramRows, nb_q = (d.n + kGramRows - 1) / kGramRows;
   float* M = const_cast<float*>(m);
+  // Stages are recorded under the step's own stage ids (M Q under EF_P,
+  // M^T P under MTP / QREDUCE, orthonormalisations under GS).
   for (int it = 0; it < iters; ++it) {
-    PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_mq(p, c, rows, pred, 0, nullptr, M, nullptr, q, c.rscr, 0),
+    PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, rows, pred, 0, nullptr, M, nullptr, q, c.rscr, 0),
                 "refresh: P = M Q");
-    PSGD_LAUNCH(PSGD_STAGE_REFRESH,
-                c.mfma ? launch_gram_orth(c, op, 1, nullptr, nb_p, c.rscr) : launch_orth(c, op, 1, c.rscr),
-                "refresh: orthonormalise P");
-    PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_mtp(c, mtp, red, M, c.rscr, 0, q), "refresh: Q = M^T P");
-    PSGD_LAUNCH(PSGD_STAGE_REFRESH, c.mfma ? launch_gram_orth(c, oq, 1, nullptr, nb_q, q) : launch_orth(c, oq, 1, q),
-                "refresh: orthonormalise Q");
+    PSGD_LAUNCH(PSGD_STAGE_GS, launch_gram_orth(c, op, 1, nullptr, nb_p, c.rscr), "refresh: orthonormalise P");
+    {
+      StageTimer _t(p, PSGD_STAGE_MTP, stream);
+      const hipError_t e = c.mfma ? launch_mfma_qt(c, mtp, M, c.rscr, 0, q) : launch_mtp(c, mtp, M, c.rscr, 0, q);
+      if (e != hipSuccess) return hip_fail(e, "refresh: Q = M^T P");
+    }
+    PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, red, q), "refresh: Q partial reduction");
+    PSGD_LAUNCH(PSGD_STAGE_GS, launch_gram_orth(c, oq, 1, nullptr, nb_q, q), "refresh: orthonormalise Q");
   }
   return PSGD_OK;
 }

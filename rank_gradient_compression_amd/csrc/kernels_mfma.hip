@@ -173,9 +173,14 @@ __global__ __launch_bounds__(kRedCols) void k_psum(const MatDesc* __restrict__ m
   const int64_t idx = (int64_t)(wg - d.wg_pred0) * kRedCols + threadIdx.x;
   if (idx >= len) return;
   const float* src = ppart + d.ppart_off + idx;
-  float s = 0.f;
-  for (int b = 0; b < d.s1; ++b) s += src[(int64_t)b * len];
-  P[(p_fixed >= 0 ? p_fixed : d.p_off) + idx] = s;
+  float s0 = 0.f, s1 = 0.f;
+  int b = 0;
+  for (; b + 2 <= d.s1; b += 2) {
+    s0 += src[(int64_t)b * len];
+    s1 += src[(int64_t)(b + 1) * len];
+  }
+  if (b < d.s1) s0 += src[(int64_t)b * len];
+  P[(p_fixed >= 0 ? p_fixed : d.p_off) + idx] = s0 + s1;
 }
 
 // ---------------------------------------------------------------------------
@@ -323,10 +328,24 @@ __global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Orthonormalisation for ranks above 8: fp64 Gram matrix of P, Gram-Schmidt
-// coefficients from it, P_hat = P T.  (Same arithmetic as the one-workgroup
-// version of the small ranks, spread over many workgroups.)
+// Orthonormalisation: Gram-Schmidt carried out on the fp64 Gram matrix
 // ---------------------------------------------------------------------------
+//
+// Gram-Schmidt on the columns of P (rows x r) in natural order with positive
+// normalisation gives P_hat = P T, T upper triangular.  In exact arithmetic
+// its coefficients are those of the Cholesky factor R of A = P^T P: the norm
+// of column k after projection on the previous P_hat columns is R_kk, and
+// R_kj = P_hat_k^T P_j.  A column whose norm after projection is at most
+// 1e-4 of its norm before (sqrt(A_kk)), or whose norm is zero, is dependent:
+// its P_hat column is zero and nothing is projected on it (row k of R is
+// zero).  A is accumulated in fp64 from the fp32 P (each product exact), so
+// the cancellation in R_kk^2 = A_kk - sum_j R_jk^2 is harmless at fp32 output
+// precision and the threshold is decided reliably.  Four launches, all
+// grouped over the matrices:
+//   k_gram_partial  A_b = P_b^T P_b over blocks of kGramRows rows
+//   k_gram_reduce   A = sum_b A_b in block order
+//   k_gram_solve    R (right-looking Cholesky) and T = R^-1, one wavefront
+//   k_apply_t       P_hat = P T row by row in fp64, rounded to fp32
 
 // Descriptor of this workgroup: first + map[wg] over a grouped grid, or the
 // single descriptor `first`.
@@ -340,99 +359,129 @@ __device__ __forceinline__ int orth_idx(const OrthDesc* descs, const int32_t* ma
   return first;
 }
 
-// Partial Gram matrix of kGramRows rows: A_b = P_b^T P_b (RP x RP, fp64).
+constexpr int kGramChunk = 128;  // rows staged in LDS at a time
+
 template <int RP>
 __global__ __launch_bounds__(256) void k_gram_partial(const OrthDesc* __restrict__ descs, const int32_t* __restrict__ map,
-                                                      int single, int r, const float* __restrict__ base,
+                                                      int first, int r, const float* __restrict__ base,
                                                       double* __restrict__ gram) {
   constexpr int LS = RP + 1;
-  __shared__ float Pl[kGramRows * LS];
+  constexpr int BF = RP / 16;  // each of the 16 x 16 threads owns a BF x BF block of A
+  __shared__ float Pl[kGramChunk * LS];
   int local;
-  const OrthDesc o = descs[orth_idx(descs, map, single, local)];
-  const int r0 = local * kGramRows;
+  const OrthDesc o = descs[orth_idx(descs, map, first, local)];
   const float* p = base + o.off;
-  for (int e = threadIdx.x; e < kGramRows * RP; e += 256) {
-    const int i = e % kGramRows, t = e / kGramRows;
-    Pl[i * LS + t] = (t < r && r0 + i < o.rows) ? p[(int64_t)t * o.rows + r0 + i] : 0.f;
-  }
-  __syncthreads();
-  constexpr int NB = RP / 4;  // 4x4 blocks per dimension
-  const int tid = threadIdx.x;
-  if (tid < NB * NB) {
-    const int ba = tid / NB, bb = tid % NB;
-    double acc[4][4];
+  const int ta = threadIdx.x >> 4, tb = threadIdx.x & 15;
+  double acc[BF][BF];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < BF; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-    for (int i = 0; i < kGramRows; ++i) {
-      double xa[4], xb[4];
+    for (int b = 0; b < BF; ++b) acc[a][b] = 0.0;
+  for (int r0 = local * kGramRows; r0 < min(o.rows, (local + 1) * kGramRows); r0 += kGramChunk) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kGramChunk * RP; e += 256) {
+      const int i = e % kGramChunk, t = e / kGramChunk;
+      Pl[i * LS + t] = (t < r && r0 + i < o.rows) ? p[(int64_t)t * o.rows + r0 + i] : 0.f;
+    }
+    __syncthreads();
+    for (int i = 0; i < kGramChunk; ++i) {
+      double xa[BF], xb[BF];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        xa[a] = (double)Pl[i * LS + 4 * ba + a];
-        xb[a] = (double)Pl[i * LS + 4 * bb + a];
+      for (int a = 0; a < BF; ++a) {
+        xa[a] = (double)Pl[i * LS + ta * BF + a];
+        xb[a] = (double)Pl[i * LS + tb * BF + a];
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < BF; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(xa[a], xb[b], acc[a][b]);
+        for (int b = 0; b < BF; ++b) acc[a][b] = fma(xa[a], xb[b], acc[a][b]);
     }
-    double* g = gram + o.gram_off + (int64_t)local * RP * RP;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) g[(4 * ba + a) * RP + 4 * bb + b] = acc[a][b];
   }
+  double* g = gram + o.gram_off + (int64_t)local * RP * RP;
+#pragma unroll
+  for (int a = 0; a < BF; ++a)
+#pragma unroll
+    for (int b = 0; b < BF; ++b) g[(ta * BF + a) * RP + tb * BF + b] = acc[a][b];
 }
 
-// One wavefront per factor: sum the Gram blocks in order, then the
-// Gram-Schmidt coefficients column by column (lane j handles index j):
-// R_jk = T_j^T A e_k, squared norm after projection A_kk - sum_j R_jk^2, and
-// T_k = (e_k - sum_j R_jk T_j) / R_kk, or the zero column below the
-// dependence threshold.
+// Fixed-order block sum: A (at t_off) = sum_b A_b.  Four running sums over
+// interleaved blocks keep several loads in flight; they are combined in a
+// fixed order, so the result is deterministic.
 template <int RP>
-__global__ __launch_bounds__(64) void k_gram_finish(const OrthDesc* __restrict__ descs, int first, int r,
-                                                    double* __restrict__ gram, float zero_rel) {
-  __shared__ double A[RP * RP];
-  __shared__ double T[RP * RP];
-  __shared__ double Rk[RP];
+__global__ __launch_bounds__(256) void k_gram_reduce(const OrthDesc* __restrict__ descs, int first,
+                                                     double* __restrict__ gram) {
+  constexpr int WPD = RP * RP / 256;  // workgroups per descriptor
+  const OrthDesc o = descs[first + blockIdx.x / WPD];
+  const int e = (blockIdx.x % WPD) * 256 + threadIdx.x;
+  const double* g = gram + o.gram_off + e;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int b = 0;
+  for (; b + 4 <= o.ngb; b += 4) {
+    s0 += g[(int64_t)b * RP * RP];
+    s1 += g[(int64_t)(b + 1) * RP * RP];
+    s2 += g[(int64_t)(b + 2) * RP * RP];
+    s3 += g[(int64_t)(b + 3) * RP * RP];
+  }
+  for (; b < o.ngb; ++b) s0 += g[(int64_t)b * RP * RP];
+  gram[o.t_off + e] = (s0 + s1) + (s2 + s3);
+}
+
+// One wavefront per factor: Cholesky of A with the dependence rule, then
+// T = R^-1 (lane l computes row l of T, which depends on no other row).
+template <int RP>
+__global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
+                                                   double* __restrict__ gram, float zero_rel) {
+  constexpr int SS = RP + 1;
+  __shared__ double S[RP * SS];   // Schur complement; row k becomes row k of R
+  __shared__ double dg[RP];       // diagonal of A (norms before projection)
+  __shared__ double rkk[RP];      // R_kk, 0 for dependent columns
   const OrthDesc o = descs[first + blockIdx.x];
   const int lane = threadIdx.x;
-  const double* g = gram + o.gram_off;
-  for (int e = lane; e < RP * RP; e += 64) {
-    double s = 0.0;
-    for (int b = 0; b < o.ngb; ++b) s += g[(int64_t)b * RP * RP + e];
-    A[e] = s;
-    T[e] = 0.0;
-  }
+  double* a = gram + o.t_off;
+  for (int e = lane; e < RP * RP; e += 64) S[(e / RP) * SS + e % RP] = a[e];
+  __syncthreads();
+  if (lane < RP) dg[lane] = S[lane * SS + lane];
   __syncthreads();
   for (int k = 0; k < r; ++k) {
-    double rk = 0.0;
-    if (lane < k) {
-      for (int l = 0; l <= lane; ++l) rk = fma(T[l * RP + lane], A[l * RP + k], rk);
-    }
-    if (lane < RP) Rk[lane] = rk;
-    double sq = rk * rk;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
-    __syncthreads();
-    const double akk = A[k * RP + k];
-    const double nv2 = akk - sq;
-    const double nu0 = sqrt(akk);
-    const double nv = nv2 > 0.0 ? sqrt(nv2) : 0.0;
+    const double d = S[k * SS + k];
+    const double nu0 = sqrt(dg[k]);
+    const double nv = d > 0.0 ? sqrt(d) : 0.0;
     const bool zero = !(nu0 > 0.0) || nv <= (double)zero_rel * nu0;
     const double inv = zero ? 0.0 : 1.0 / nv;
-    if (lane < k) {
-      double s = 0.0;
-      for (int j = lane; j < k; ++j) s = fma(Rk[j], T[lane * RP + j], s);
-      T[lane * RP + k] = -s * inv;
-    } else if (lane == k) {
-      T[k * RP + k] = inv;
+    __syncthreads();
+    if (lane > k && lane < r) S[k * SS + lane] *= inv;
+    if (lane == 0) {
+      rkk[k] = zero ? 0.0 : nv;
+      S[k * SS + k] = zero ? 0.0 : nv;
+    }
+    __syncthreads();
+    const int w = r - k - 1;
+    for (int e = lane; e < w * w; e += 64) {
+      const int i = k + 1 + e / w, j = k + 1 + e % w;
+      if (i <= j) S[i * SS + j] = fma(-S[k * SS + i], S[k * SS + j], S[i * SS + j]);
     }
     __syncthreads();
   }
-  double* t = gram + o.t_off;
-  for (int e = lane; e < RP * RP; e += 64) t[e] = T[e];
+  // T = R^-1 on the non-dependent columns: T_lk = (delta_lk - sum_{l<=j<k}
+  // T_lj R_jk) / R_kk, zero for dependent k.  Row l of T uses only row l.
+  double* t = a;  // overwrite A with T
+  if (lane < RP) {
+    double trow[RP];
+#pragma unroll
+    for (int k = 0; k < RP; ++k) trow[k] = 0.0;
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      if (k < r && k >= lane) {
+        double s = k == lane ? 1.0 : 0.0;
+#pragma unroll
+        for (int j = 0; j < RP; ++j)
+          if (j >= lane && j < k) s = fma(-trow[j], S[j * SS + k], s);
+        trow[k] = rkk[k] > 0.0 ? s / rkk[k] : 0.0;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RP; ++k) t[lane * RP + k] = trow[k];
+  }
 }
 
 // P_hat = P T, rows in parallel, evaluated in fp64 and rounded to fp32.
@@ -441,16 +490,16 @@ __global__ __launch_bounds__(64) void k_gram_finish(const OrthDesc* __restrict__
 // columns no later block reads.
 template <int RP>
 __global__ __launch_bounds__(256) void k_apply_t(const OrthDesc* __restrict__ descs, const int32_t* __restrict__ map,
-                                                 int single, int r, float* __restrict__ base,
+                                                 int first, int r, float* __restrict__ base,
                                                  const double* __restrict__ gram) {
   __shared__ double T[RP * RP];
   int local;
-  const OrthDesc o = descs[orth_idx(descs, map, single, local)];
+  const OrthDesc o = descs[orth_idx(descs, map, first, local)];
   const double* t = gram + o.t_off;
   for (int e = threadIdx.x; e < RP * RP; e += 256) T[e] = t[e];
   __syncthreads();
   const int i = local * kGramRows + threadIdx.x;
-  if (threadIdx.x >= kGramRows || i >= o.rows) return;
+  if (i >= o.rows) return;
   float* p = base + o.off + i;
   const int64_t ld = o.rows;
   for (int k0 = (r - 1) / 16 * 16; k0 >= 0; k0 -= 16) {
@@ -557,7 +606,11 @@ static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const i
                      c.gram);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gram_finish<RP>), dim3(count), dim3(64), 0, c.stream, c.orth, first, c.rank, c.gram,
+  hipLaunchKernelGGL((k_gram_reduce<RP>), dim3(count * (RP * RP / 256)), dim3(256), 0, c.stream, c.orth, first,
+                     c.gram);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(64), 0, c.stream, c.orth, first, c.rank, c.gram,
                      kZeroColumnRel);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -1,4 +1,5 @@
-// Streaming kernels of the PowerSGD step for ranks up to 8 (gfx950, wave64).
+// Streaming kernels of the PowerSGD step for ranks up to 8 (gfx950, wave64);
+// the orthonormalisation for every rank is in kernels_mfma.hip.
 //
 // One PowerSGD step per gradient matrix, as the "Method" section of the
 // anthology note on PowerSGD (note 152) describes it: P = M Q with the
@@ -187,117 +188,6 @@ __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Orthogonalisation of P: Gram-Schmidt carried out on the Gram matrix
-// ---------------------------------------------------------------------------
-//
-// Gram-Schmidt on the columns of P (m x r) in natural order with positive
-// normalisation yields P_hat = P T with T upper triangular.  In exact
-// arithmetic the coefficients follow from the Gram matrix A = P^T P alone:
-// for column k, the projections on the previous P_hat columns are
-// R_jk = T_j^T A e_k, the squared norm after projection is
-// A_kk - sum_j R_jk^2, and T_k = (e_k - sum_j R_jk T_j) / R_kk.  A is formed
-// in fp64 from the fp32 P (each product exact), so the cancellation in the
-// squared norm costs nothing at fp32 output precision and the 1e-4 relative
-// dependence threshold is decided reliably.  One workgroup per matrix: read P
-// once for A, once for P_hat = P T (evaluated in fp64, rounded to fp32).
-
-constexpr int kOrthThreads = 256;
-
-template <int R>
-__global__ __launch_bounds__(kOrthThreads) void k_orth(const OrthDesc* __restrict__ descs, int first,
-                                                       float* __restrict__ base, float zero_rel) {
-  constexpr int NG = R * (R + 1) / 2;
-  __shared__ double red[kOrthThreads / 64][NG];
-  __shared__ double T[R][R];
-  const OrthDesc o = descs[first + blockIdx.x];
-  const int m = o.rows;
-  float* p = base + o.off;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  double g[NG];
-#pragma unroll
-  for (int i = 0; i < NG; ++i) g[i] = 0.0;
-  for (int i = tid; i < m; i += kOrthThreads) {
-    double x[R];
-#pragma unroll
-    for (int a = 0; a < R; ++a) x[a] = (double)p[(int64_t)a * m + i];
-    int t = 0;
-#pragma unroll
-    for (int a = 0; a < R; ++a)
-#pragma unroll
-      for (int b = a; b < R; ++b) {
-        g[t] = fma(x[a], x[b], g[t]);
-        ++t;
-      }
-  }
-  // fixed-order reduction: butterfly within the wavefront, then waves in order
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    double v = g[i];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    g[i] = v;
-  }
-  if (lane == 0)
-#pragma unroll
-    for (int i = 0; i < NG; ++i) red[wave][i] = g[i];
-  __syncthreads();
-
-  if (tid == 0) {
-    double A[R][R];
-    int t = 0;
-    for (int a = 0; a < R; ++a)
-      for (int b = a; b < R; ++b) {
-        double s = 0.0;
-        for (int w = 0; w < kOrthThreads / 64; ++w) s += red[w][t];
-        A[a][b] = s;
-        A[b][a] = s;
-        ++t;
-      }
-    double Tl[R][R];
-    for (int a = 0; a < R; ++a)
-      for (int b = 0; b < R; ++b) Tl[a][b] = 0.0;
-    for (int k = 0; k < R; ++k) {
-      // A e_k projected on the previous columns: R_jk = T_j^T A e_k
-      double Rk[R];
-      double nv2 = A[k][k];
-      for (int j = 0; j < k; ++j) {
-        double s = 0.0;
-        for (int l = 0; l <= j; ++l) s = fma(Tl[l][j], A[l][k], s);
-        Rk[j] = s;
-        nv2 = fma(-s, s, nv2);
-      }
-      const double nu0 = sqrt(A[k][k]);
-      const double nv = nv2 > 0.0 ? sqrt(nv2) : 0.0;
-      if (!(nu0 > 0.0) || nv <= (double)zero_rel * nu0) continue;  // zero column
-      const double inv = 1.0 / nv;
-      for (int l = 0; l < k; ++l) {
-        double s = 0.0;
-        for (int j = l; j < k; ++j) s = fma(Rk[j], Tl[l][j], s);
-        Tl[l][k] = -s * inv;
-      }
-      Tl[k][k] = inv;
-    }
-    for (int a = 0; a < R; ++a)
-      for (int b = 0; b < R; ++b) T[a][b] = Tl[a][b];
-  }
-  __syncthreads();
-
-  for (int i = tid; i < m; i += kOrthThreads) {
-    double x[R];
-#pragma unroll
-    for (int a = 0; a < R; ++a) x[a] = (double)p[(int64_t)a * m + i];
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      double s = 0.0;
-#pragma unroll
-      for (int a = 0; a <= k; ++a) s = fma(x[a], T[a][k], s);
-      p[(int64_t)k * m + i] = (float)s;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Pass 2: Q = M^T P_hat, partial sums per row block
 // ---------------------------------------------------------------------------
 
@@ -383,9 +273,18 @@ __global__ __launch_bounds__(kRedCols) void k_qreduce(const MatDesc* __restrict_
   const int64_t idx = (int64_t)(wg - d.wg_red0) * kRedCols + threadIdx.x;
   if (idx >= len) return;
   const float* src = part + d.part_off + idx;
-  float s = 0.f;
-  for (int b = 0; b < d.nrb; ++b) s += src[(int64_t)b * len];
-  Q[d.q_off + idx] = s;
+  // four running sums over interleaved blocks (several loads in flight),
+  // combined in a fixed order: deterministic
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int b = 0;
+  for (; b + 4 <= d.nrb; b += 4) {
+    s0 += src[(int64_t)b * len];
+    s1 += src[(int64_t)(b + 1) * len];
+    s2 += src[(int64_t)(b + 2) * len];
+    s3 += src[(int64_t)(b + 3) * len];
+  }
+  for (; b < d.nrb; ++b) s0 += src[(int64_t)b * len];
+  Q[d.q_off + idx] = (s0 + s1) + (s2 + s3);
 }
 
 // ---------------------------------------------------------------------------
@@ -512,13 +411,6 @@ static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode
 }
 
 template <int R>
-static hipError_t launch_orth_r(const LaunchCtx& c, int first, int count, float* base) {
-  if (count == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_orth<R>), dim3(count), dim3(kOrthThreads), 0, c.stream, c.orth, first, base, kZeroColumnRel);
-  return hipGetLastError();
-}
-
-template <int R>
 static hipError_t launch_mtp_r(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph,
                                int64_t ph_fixed, float* Q) {
   if (g.count == 0) return hipSuccess;
@@ -557,10 +449,6 @@ static hipError_t launch_recon_r(const LaunchCtx& c, float* E, const float* Q, c
 hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
                        float beta, const float* Q, float* P, int64_t p_fixed) {
   PSGD_RANK_SWITCH(c.rank, launch_ef_p_r<RR>(c, g, mode, G, E, U, beta, Q, P, p_fixed));
-}
-
-hipError_t launch_orth(const LaunchCtx& c, int first, int count, float* base) {
-  PSGD_RANK_SWITCH(c.rank, launch_orth_r<RR>(c, first, count, base));
 }
 
 hipError_t launch_mtp(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,

@@ -34,16 +34,19 @@ void clear_error() { g_err[0] = 0; }
 
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Rows per row block of the M^T P_hat pass: as long as possible (the partial
-// sums cost 2*rank/rb_rows of the matrix traffic) while the grid still has
-// enough workgroups to cover the chip.
-static int32_t choose_rb_rows(const std::vector<MatDesc>& mats) {
+// Rows per row block of the M^T P_hat pass.  The row-block partial sums cost
+// 2*rank/rb_rows of that pass's matrix traffic, so a block has at least
+// 8*rank rows (at most 1/4 extra on the pass); above that, blocks are as long
+// as possible while the grid still has enough workgroups to cover the chip.
+static int32_t choose_rb_rows(const std::vector<MatDesc>& mats, int64_t rank, bool mfma) {
   const int64_t target_wgs = 2048;
+  int32_t rb_min = 64;
+  while (rb_min < 8 * rank) rb_min *= 2;
   int32_t rb = 2048;
-  for (; rb > 64; rb /= 2) {
+  for (; rb > rb_min; rb /= 2) {
     int64_t wgs = 0;
     for (const MatDesc& d : mats) {
-      const int64_t cols_per_wg = (int64_t)kMtpWaves * 64 * d.vec;
+      const int64_t cols_per_wg = mfma ? kMfmaCols : (int64_t)kMtpWaves * 64 * d.vec;
       wgs += ((d.m + rb - 1) / rb) * ((d.n + cols_per_wg - 1) / cols_per_wg);
     }
     if (wgs >= target_wgs) break;
@@ -194,9 +197,8 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
 
   // Tile tables.
   const bool mfma = rank > kValuMaxRank;
-  const int64_t rp = mfma ? align_up(r, 16) : r;
-  int32_t rb = choose_rb_rows(p->mats);
-  if (mfma && rb < kMfmaRows) rb = kMfmaRows;
+  const int64_t rp = align_up(r, 16);  // rank padding of the matrix-core and Gram kernels
+  const int32_t rb = choose_rb_rows(p->mats, r, mfma);
   // MFMA passes 1 and 3 split the columns until the grid covers the chip.
   int32_t s1 = 1;
   if (mfma) {
@@ -229,14 +231,6 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
         for (int32_t t = 0; t < np; ++t) p->pred_map.push_back((int32_t)k);
         wg_pred += np;
       }
-      d.ngb = (d.m + kGramRows - 1) / kGramRows;
-      d.wg_gram0 = wg_gram;
-      for (int32_t t = 0; t < d.ngb; ++t) p->gram_map.push_back((int32_t)k);
-      wg_gram += d.ngb;
-      const int64_t nb = std::max<int64_t>(d.ngb, (d.n + kGramRows - 1) / kGramRows);
-      d.gram_off = gram;
-      d.t_off = gram + nb * rp * rp;
-      gram += (nb + 1) * rp * rp;
     } else {
       d.s1 = 1;
       d.s1_cols = d.n;
@@ -244,6 +238,16 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     }
     for (int32_t t = 0; t < nrow_wg; ++t) p->rows_map.push_back((int32_t)k);
     wg_rows += nrow_wg;
+    // Gram grid (orthonormalisation of P) and the Gram scratch, sized for P
+    // (m rows) and for the refresh's Q (n rows)
+    d.ngb = (d.m + kGramRows - 1) / kGramRows;
+    d.wg_gram0 = wg_gram;
+    for (int32_t t = 0; t < d.ngb; ++t) p->gram_map.push_back((int32_t)k);
+    wg_gram += d.ngb;
+    const int64_t nb = std::max<int64_t>(d.ngb, (d.n + kGramRows - 1) / kGramRows);
+    d.gram_off = gram;
+    d.t_off = gram + nb * rp * rp;
+    gram += (nb + 1) * rp * rp;
     d.wg_mtp0 = wg_mtp;
     for (int32_t t = 0; t < d.nrb * d.ncb; ++t) p->mtp_map.push_back((int32_t)k);
     wg_mtp += d.nrb * d.ncb;
@@ -277,10 +281,8 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     o.ngb = (d.n + kGramRows - 1) / kGramRows;
     o.off = d.q_off;
     o.wg0 = wg_gramq;
-    if (mfma) {
-      for (int32_t t = 0; t < o.ngb; ++t) p->gramq_map.push_back((int32_t)k);
-      wg_gramq += o.ngb;
-    }
+    for (int32_t t = 0; t < o.ngb; ++t) p->gramq_map.push_back((int32_t)k);
+    wg_gramq += o.ngb;
     p->orth[2 * nm + k] = o;
   }
   // the grouped refresh inside compress keeps its P in the refresh scratch

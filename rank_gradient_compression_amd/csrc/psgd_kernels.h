@@ -48,8 +48,6 @@ struct GridRange {
 // u = beta u + G first.  p_fixed >= 0 replaces the plan's P offset.
 hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
                        float beta, const float* Q, float* P, int64_t p_fixed);
-// Orthonormalise descriptors [first, first + count) of the plan's OrthDesc table.
-hipError_t launch_orth(const LaunchCtx& c, int first, int count, float* base);
 hipError_t launch_mtp(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,
                       float* Q);
 // residual = true: E <- M - P_hat Q^T (M read from E), M_hat written if non-null.
