@@ -58,6 +58,41 @@ __device__ __forceinline__ void stv(float* p, const Vec<VEC>& a) {
   }
 }
 
+// Non-temporal (streaming) variants: the nt bit on the access tells the
+// caches the line will not be reused soon.  Measured on the grouped 7B-shaped
+// set: streaming loads of G and of M in the residual pass and a streaming
+// store of M_hat shave about 2% off a step; a streaming store of E or M costs.
+typedef float v4f_nt __attribute__((ext_vector_type(4)));
+typedef float v2f_nt __attribute__((ext_vector_type(2)));
+
+template <int VEC>
+__device__ __forceinline__ void stv_nt(float* p, const Vec<VEC>& a) {
+  if constexpr (VEC == 4) {
+    v4f_nt t = {a.v[0], a.v[1], a.v[2], a.v[3]};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4f_nt*>(p));
+  } else if constexpr (VEC == 2) {
+    v2f_nt t = {a.v[0], a.v[1]};
+    __builtin_nontemporal_store(t, reinterpret_cast<v2f_nt*>(p));
+  } else {
+    __builtin_nontemporal_store(a.v[0], p);
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ Vec<VEC> ldv_nt(const float* p) {
+  Vec<VEC> r;
+  if constexpr (VEC == 4) {
+    const v4f_nt t = __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(p));
+    r.v[0] = t[0]; r.v[1] = t[1]; r.v[2] = t[2]; r.v[3] = t[3];
+  } else if constexpr (VEC == 2) {
+    const v2f_nt t = __builtin_nontemporal_load(reinterpret_cast<const v2f_nt*>(p));
+    r.v[0] = t[0]; r.v[1] = t[1];
+  } else {
+    r.v[0] = __builtin_nontemporal_load(p);
+  }
+  return r;
+}
+
 // Sum of NV per-lane values over the 64 lanes of a wavefront, transposed: on
 // return lane l holds the total of value (l >> (6 - log2 NV)).  Each butterfly
 // step halves the values a lane carries, so the cost is about NV shuffles
@@ -120,7 +155,7 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
       const int64_t idx = base + (int64_t)min(rr, nrows - 1) * n + j;
-      if constexpr (MODE != 0) g[rr] = ldv<VEC>(G + idx);
+      if constexpr (MODE != 0) g[rr] = ldv_nt<VEC>(G + idx);  // read once per step: streaming hint
       e[rr] = ldv<VEC>(E + idx);
     }
     Vec<VEC> u[kWaveRows];
@@ -311,7 +346,7 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane,
     Vec<VEC> x[kWaveRows];
     if constexpr (READ_M) {
 #pragma unroll
-      for (int rr = 0; rr < kWaveRows; ++rr) x[rr] = ldv<VEC>(E + base + (int64_t)min(rr, nrows - 1) * n + j);
+      for (int rr = 0; rr < kWaveRows; ++rr) x[rr] = ldv_nt<VEC>(E + base + (int64_t)min(rr, nrows - 1) * n + j);
     }
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
@@ -331,7 +366,9 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane,
           for (int c = 0; c < VEC; ++c) e.v[c] = x[rr].v[c] - mh.v[c];
           stv<VEC>(E + idx, e);
         }
-        if constexpr (WRITE_MHAT) stv<VEC>(Mhat + idx, mh);
+        // M_hat is consumed by the optimizer after the step, not by this
+        // pipeline: streaming store.
+        if constexpr (WRITE_MHAT) stv_nt<VEC>(Mhat + idx, mh);
       }
     }
   }
