@@ -130,7 +130,10 @@ class Runner:
         self.torch, self.B = torch, B
         self.stream = torch.cuda.current_stream()
 
-    def time(self, label, call, steps, warmup, plan=None):
+    def time(self, label, call, steps, warmup, plan=None, per_step=True):
+        """K timed steps between one pair of events (the headline figure),
+        with the library's per-stage events on when `plan` is given; then,
+        separately, K steps with an event after each one for the spread."""
         torch, B = self.torch, self.B
         for _ in range(warmup):
             call()
@@ -138,20 +141,28 @@ class Runner:
         if plan is not None:
             B.psgd_timing_read(plan)  # drop warm-up records
             B.psgd_timing_enable(plan, True)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
-        ev[0].record(self.stream)
-        for k in range(steps):
+        e0.record(self.stream)
+        for _ in range(steps):
             call()
-            ev[k + 1].record(self.stream)
+        e1.record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
         if plan is not None:
             B.psgd_timing_enable(plan, False)
-        per = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
-        total_ms = ev[0].elapsed_time(ev[steps])
-        log(f"bench: {label}: {total_ms / steps:.4f} ms/step (median {statistics.median(per):.4f}, "
+        total_ms = e0.elapsed_time(e1)
+        per = [total_ms / steps]
+        if per_step:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            ev[0].record(self.stream)
+            for k in range(steps):
+                call()
+                ev[k + 1].record(self.stream)
+            torch.cuda.synchronize()
+            per = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
+        log(f"bench: {label}: {total_ms / steps:.4f} ms/step (per-step median {statistics.median(per):.4f}, "
             f"wall {wall * 1e3 / steps:.4f})")
         return total_ms / steps, per
 
@@ -160,7 +171,8 @@ class Runner:
         src = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
         dst = torch.empty_like(src)
         ms, _ = self.time("stream copy 4 GiB", lambda: B.psgd_stream_copy(dst.data_ptr(), src.data_ptr(), n,
-                                                                            self.stream.cuda_stream), 5, 2)
+                                                                            self.stream.cuda_stream), 5, 2,
+                          per_step=False)
         del src, dst
         torch.cuda.empty_cache()
         return 8 * n / (ms * 1e-3) / 1e9
@@ -217,7 +229,8 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
         res["roofline"] = roofline_of(st, mfma, "hbm_bytes_llama7b_r4_fused.md" if rank == 4 else None)
         res["stages"] = round_stages(st)
     if not args.no_variants:
-        ms_c, _ = R.time("compress only", lambda: ps.compress(mhat=False), max(3, args.steps // 2), 1)
+        ms_c, _ = R.time("compress only", lambda: ps.compress(mhat=False), max(3, args.steps // 2), 1,
+                         per_step=False)
         res["config"]["compress_only"] = {"ms_per_step": round(ms_c, 4),
                                           "grad_gbs": round(4.0 * dense / (ms_c * 1e-3) / 1e9, 2),
                                           "hbm_frac": round(24.0 * dense / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -229,7 +242,8 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
             W.llama7b_grad_(psm.view(psm.grads, i), s[0], s[1], i, step=1)
             psm.set_q(i, W.llama7b_q0(s[1], rank, i, device="cuda"))
         torch.cuda.synchronize()
-        ms_m, _ = R.time("momentum compress (beta 0.9)", lambda: psm.compress(mhat=False), max(3, args.steps // 2), 1)
+        ms_m, _ = R.time("momentum compress (beta 0.9)", lambda: psm.compress(mhat=False), max(3, args.steps // 2), 1,
+                         per_step=False)
         res["config"]["momentum_compress"] = {"beta": 0.9, "ms_per_step": round(ms_m, 4),
                                               "grad_gbs": round(4.0 * dense / (ms_m * 1e-3) / 1e9, 2),
                                               "hbm_frac": round(32.0 * dense / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -38,8 +38,10 @@ static hipEvent_t take_event(TimingState* t) {
     t->pool.pop_back();
     return e;
   }
+  // Timing-only events: no system-scope fence (cache writeback and
+  // invalidation) when recorded, so that timing does not perturb the stages.
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

@@ -38,6 +38,11 @@ __device__ __forceinline__ v4f mfma16x16x4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wavefront's LDS
+// accesses (lgkmcnt) but, unlike __syncthreads(), not for its outstanding
+// global loads, so loads issued before the barrier stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Four consecutive floats of a row from column `col` (zero past the row end).
 __device__ __forceinline__ float4 ld4(const float* p, int col, int n, bool vec4) {
   if (vec4) return col < n ? *reinterpret_cast<const float4*>(p + col) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -60,6 +65,25 @@ __device__ __forceinline__ void st4(float* p, int col, int n, bool vec4, float4 
   if (col + 3 < n) p[col + 3] = v.w;
 }
 
+// Rows whose length and start allow 16-byte accesses (VEC4) load at a
+// clamped, always valid column and zero the value when out of range: no
+// branches, so every load of a step can be in flight at once.  Other rows
+// take the guarded scalar path.
+template <bool VEC4>
+__device__ __forceinline__ float4 ldq(const float* rowp, int col, bool ok, int col_safe, int n) {
+  if constexpr (VEC4) {
+    const float4 v = *reinterpret_cast<const float4*>(rowp + (ok ? col : col_safe));
+    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    return ld4(rowp, ok ? col : n, n, false);
+  }
+}
+
+template <bool VEC4>
+__device__ __forceinline__ void stq(float* rowp, int col, int n, float4 v) {
+  st4(rowp, col, n, VEC4, v);
+}
+
 __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) {
   const int wg = blockIdx.x + wg_base;
   idx = map[wg];
@@ -71,19 +95,13 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 // 2: u = beta u + G, M = u + E)
 // ---------------------------------------------------------------------------
 
-template <int RP, int MODE>
-__global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
-                                                int wg_base, int r, const float* __restrict__ G,
-                                                float* __restrict__ E, float* __restrict__ U, float beta,
-                                                const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed,
-                                                float* __restrict__ ppart) {
+template <int RP, int MODE, bool VEC4>
+__device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, const float* __restrict__ G,
+                                            float* __restrict__ E, float* __restrict__ U, float beta,
+                                            const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed,
+                                            float* __restrict__ ppart, float* Qs) {
   constexpr int QS = RP + 4;  // LDS row stride: conflict-free B-operand reads
-  __shared__ float Qs[64 * QS];
-  int mi;
-  const int wg = wg_of(map, wg_base, mi);
-  const MatDesc d = mats[mi];
   const int m = d.m, n = d.n;
-  const bool vec4 = d.vec == 4;
   const int local = wg - d.wg_rows0;
   const int rb = local / d.s1, split = local - rb * d.s1;
   const int c_begin = split * d.s1_cols;
@@ -101,40 +119,42 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
   for (int T = 0; T < RP / 16; ++T) acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int c0 = c_begin; c0 < c_end; c0 += 64) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * RP; e += 256) {
-      const int c = e & 63, t = e >> 6;
-      float v = 0.f;
-      if (t < r && c0 + c < c_end) v = q[(int64_t)t * n + c0 + c];
-      Qs[c * QS + t] = v;
-    }
-    __syncthreads();
+    // M loads (and the EF-add write-back) are issued before the barriers of
+    // the Q staging so that both latencies overlap.
     float4 x[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int col = c0 + 16 * qq + 4 * ls;
       const bool col_ok = col < c_end;
       if constexpr (MODE == 0) {
-        x[qq] = ld4(E + roff, col_ok ? col : n, n, vec4);
+        x[qq] = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
       } else {
-        const float4 g = ld4(G + roff, col_ok ? col : n, n, vec4);
-        const float4 e = ld4(E + roff, col_ok ? col : n, n, vec4);
+        const float4 g = ldq<VEC4>(G + roff, col, col_ok, c_begin, n);
+        const float4 e = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
         float4 s;
         if constexpr (MODE == 2) {
-          float4 u = ld4(U + roff, col_ok ? col : n, n, vec4);
+          float4 u = ldq<VEC4>(U + roff, col, col_ok, c_begin, n);
           u.x = fmaf(beta, u.x, g.x);
           u.y = fmaf(beta, u.y, g.y);
           u.z = fmaf(beta, u.z, g.z);
           u.w = fmaf(beta, u.w, g.w);
-          if (row_ok && col_ok) st4(U + roff, col, n, vec4, u);
+          if (row_ok && col_ok) stq<VEC4>(U + roff, col, n, u);
           s = make_float4(u.x + e.x, u.y + e.y, u.z + e.z, u.w + e.w);
         } else {
           s = make_float4(g.x + e.x, g.y + e.y, g.z + e.z, g.w + e.w);
         }
-        if (row_ok && col_ok) st4(E + roff, col, n, vec4, s);
+        if (row_ok && col_ok) stq<VEC4>(E + roff, col, n, s);
         x[qq] = s;
       }
     }
+    lds_barrier();  // previous step's reads of Qs are done
+    for (int e = threadIdx.x; e < 64 * RP; e += 256) {
+      const int c = e & 63, t = e >> 6;
+      float v = 0.f;
+      if (t < r && c0 + c < c_end) v = q[(int64_t)t * n + c0 + c];
+      Qs[c * QS + t] = v;
+    }
+    lds_barrier();
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const float xv[4] = {x[qq].x, x[qq].y, x[qq].z, x[qq].w};
@@ -148,18 +168,43 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
     }
   }
 
+  // Results leave through LDS so that each store instruction writes
+  // consecutive rows of one P column (D holds 16 columns x 4 rows per lane
+  // group, which would otherwise scatter 4-byte stores).
   float* dst = d.s1 > 1 ? ppart + d.ppart_off + (int64_t)split * r * m : P + (p_fixed >= 0 ? p_fixed : d.p_off);
+  constexpr int OS = kMfmaRows + 1;
+  float* Os = Qs;  // 16 x OS floats fit in the Q staging buffer
+  const int rbase = rb * kMfmaRows;
 #pragma unroll
   for (int T = 0; T < RP / 16; ++T) {
-    const int t = 16 * T + li;
-    if (t < r) {
+    __syncthreads();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = i0 + 4 * ls + e;
-        if (rr < m) dst[(int64_t)t * m + rr] = acc[T][e];
-      }
+    for (int e = 0; e < 4; ++e) Os[li * OS + wave * 16 + 4 * ls + e] = acc[T][e];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * kMfmaRows; idx += 256) {
+      const int tl = idx / kMfmaRows, rl = idx % kMfmaRows;
+      const int t = 16 * T + tl, rr = rbase + rl;
+      if (t < r && rr < m) dst[(int64_t)t * m + rr] = Os[tl * OS + rl];
     }
   }
+}
+
+template <int RP, int MODE>
+__global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
+                                                int wg_base, int r, const float* __restrict__ G,
+                                                float* __restrict__ E, float* __restrict__ U, float beta,
+                                                const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed,
+                                                float* __restrict__ ppart) {
+  constexpr int QS = RP + 4;
+  static_assert(16 * (kMfmaRows + 1) <= 64 * QS, "output staging does not fit");
+  __shared__ float Qs[64 * QS];
+  int mi;
+  const int wg = wg_of(map, wg_base, mi);
+  const MatDesc d = mats[mi];
+  if (d.vec == 4)
+    mfma_p_body<RP, MODE, true>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs);
+  else
+    mfma_p_body<RP, MODE, false>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs);
 }
 
 // Fixed-order sum of the column-split partials of pass 1.
@@ -188,18 +233,12 @@ __global__ __launch_bounds__(kRedCols) void k_psum(const MatDesc* __restrict__ m
 // several row blocks)
 // ---------------------------------------------------------------------------
 
-template <int RP>
-__global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
-                                                 int wg_base, int r, const float* __restrict__ M,
-                                                 const float* __restrict__ Ph, int64_t ph_fixed,
-                                                 float* __restrict__ Q, float* __restrict__ part) {
+template <int RP, bool VEC4>
+__device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, const float* __restrict__ M,
+                                             const float* __restrict__ Ph, int64_t ph_fixed, float* __restrict__ Q,
+                                             float* __restrict__ part, float* Ps, float* Os) {
   constexpr int PS = RP == 16 ? 16 : 80;  // LDS row stride: conflict-free B-operand reads
-  __shared__ float Ps[64 * PS];
-  int mi;
-  const int wg = wg_of(map, wg_base, mi);
-  const MatDesc d = mats[mi];
   const int m = d.m, n = d.n;
-  const bool vec4 = d.vec == 4;
   const int local = wg - d.wg_mtp0;
   const int rb = local / d.ncb, cb = local - rb * d.ncb;
   const int i0 = rb * d.rb_rows;
@@ -217,20 +256,22 @@ __global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mat
     for (int T = 0; T < RP / 16; ++T) acc[v][T] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int ib = i0; ib < i1; ib += 64) {
-    __syncthreads();
+    // M loads first: they overlap the P_hat staging below.
+    float4 x[16];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int rrow = ib + 4 * kk + ls;
+      const bool ok = rrow < i1 && col < n;
+      x[kk] = ldq<VEC4>(M + d.off + (int64_t)(rrow < i1 ? rrow : i0) * n, col, ok, 0, n);
+    }
+    lds_barrier();  // previous chunk's reads of Ps are done
     for (int e = threadIdx.x; e < 64 * RP; e += 256) {
       const int k = e & 63, t = e >> 6;
       float v = 0.f;
       if (t < r && ib + k < i1) v = ph[(int64_t)t * m + ib + k];
       Ps[k * PS + t] = v;
     }
-    __syncthreads();
-    float4 x[16];
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const int rrow = ib + 4 * kk + ls;
-      x[kk] = rrow < i1 ? ld4(M + d.off + (int64_t)rrow * n, col, n, vec4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    lds_barrier();
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const float xv[4] = {x[kk].x, x[kk].y, x[kk].z, x[kk].w};
@@ -244,20 +285,42 @@ __global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mat
     }
   }
 
+  // Results leave through LDS so that each store instruction writes
+  // consecutive columns of one Q column (rank index).
   float* out = d.nrb > 1 ? part + d.part_off + (int64_t)rb * r * n : Q + d.q_off;
+  constexpr int OS = kMfmaCols + 1;
+  const int cbase = cb * kMfmaCols;
 #pragma unroll
   for (int T = 0; T < RP / 16; ++T) {
-    const int t = 16 * T + li;
-    if (t < r) {
+    __syncthreads();
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = j0 + 4 * (4 * ls + e) + v;
-          if (c < n) out[(int64_t)t * n + c] = acc[v][T][e];
-        }
+      for (int e = 0; e < 4; ++e) Os[li * OS + wave * 64 + 4 * (4 * ls + e) + v] = acc[v][T][e];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * kMfmaCols; idx += 256) {
+      const int tl = idx / kMfmaCols, cl = idx % kMfmaCols;
+      const int t = 16 * T + tl, c = cbase + cl;
+      if (t < r && c < n) out[(int64_t)t * n + c] = Os[tl * OS + cl];
     }
   }
+}
+
+template <int RP>
+__global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
+                                                 int wg_base, int r, const float* __restrict__ M,
+                                                 const float* __restrict__ Ph, int64_t ph_fixed,
+                                                 float* __restrict__ Q, float* __restrict__ part) {
+  constexpr int PS = RP == 16 ? 16 : 80;
+  __shared__ float Ps[64 * PS];
+  __shared__ float Os[16 * (kMfmaCols + 1)];
+  int mi;
+  const int wg = wg_of(map, wg_base, mi);
+  const MatDesc d = mats[mi];
+  if (d.vec == 4)
+    mfma_qt_body<RP, true>(d, wg, r, M, Ph, ph_fixed, Q, part, Ps, Os);
+  else
+    mfma_qt_body<RP, false>(d, wg, r, M, Ph, ph_fixed, Q, part, Ps, Os);
 }
 
 // ---------------------------------------------------------------------------
@@ -266,17 +329,12 @@ __global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mat
 // 16-column tile of the workgroup's column split.
 // ---------------------------------------------------------------------------
 
-template <int RP, bool READ_M, bool WRITE_E, bool WRITE_MHAT>
-__global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
-                                                    int wg_base, int r, float* __restrict__ E,
-                                                    const float* __restrict__ Q, const float* __restrict__ Ph,
-                                                    float* __restrict__ Mhat) {
+template <int RP, bool READ_M, bool WRITE_E, bool WRITE_MHAT, bool VEC4>
+__device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r, float* __restrict__ E,
+                                                const float* __restrict__ Q, const float* __restrict__ Ph,
+                                                float* __restrict__ Mhat) {
   constexpr int KS = RP / 4;  // k-steps of 4 rank columns
-  int mi;
-  const int wg = wg_of(map, wg_base, mi);
-  const MatDesc d = mats[mi];
   const int m = d.m, n = d.n;
-  const bool vec4 = d.vec == 4;
   const int local = wg - d.wg_rows0;
   const int rb = local / d.s1, split = local - rb * d.s1;
   const int c_begin = split * d.s1_cols;
@@ -307,6 +365,14 @@ __global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ 
     }
     const int col = j0 + 4 * ls;
     const bool col_ok = col < c_end;
+    float4 xm[4];
+    if constexpr (READ_M) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int rr = i0 + 16 * rt + li;
+        xm[rt] = ldq<VEC4>(E + d.off + (int64_t)min(rr, m - 1) * n, col, rr < m && col_ok, c_begin, n);
+      }
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -316,15 +382,28 @@ __global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ 
       if (rr < m && col_ok) {
         float* rowp = E + d.off + (int64_t)rr * n;
         const float4 mh = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        if constexpr (READ_M) {
-          const float4 x = ld4(rowp, col, n, vec4);
-          if constexpr (WRITE_E)
-            st4(rowp, col, n, vec4, make_float4(x.x - mh.x, x.y - mh.y, x.z - mh.z, x.w - mh.w));
+        if constexpr (READ_M && WRITE_E) {
+          const float4 x = xm[rt];
+          stq<VEC4>(rowp, col, n, make_float4(x.x - mh.x, x.y - mh.y, x.z - mh.z, x.w - mh.w));
         }
-        if constexpr (WRITE_MHAT) st4(Mhat + d.off + (int64_t)rr * n, col, n, vec4, mh);
+        if constexpr (WRITE_MHAT) stq<VEC4>(Mhat + d.off + (int64_t)rr * n, col, n, mh);
       }
     }
   }
+}
+
+template <int RP, bool READ_M, bool WRITE_E, bool WRITE_MHAT>
+__global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
+                                                    int wg_base, int r, float* __restrict__ E,
+                                                    const float* __restrict__ Q, const float* __restrict__ Ph,
+                                                    float* __restrict__ Mhat) {
+  int mi;
+  const int wg = wg_of(map, wg_base, mi);
+  const MatDesc d = mats[mi];
+  if (d.vec == 4)
+    mfma_recon_body<RP, READ_M, WRITE_E, WRITE_MHAT, true>(d, wg, r, E, Q, Ph, Mhat);
+  else
+    mfma_recon_body<RP, READ_M, WRITE_E, WRITE_MHAT, false>(d, wg, r, E, Q, Ph, Mhat);
 }
 
 // ---------------------------------------------------------------------------
@@ -344,8 +423,9 @@ __global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ 
 // grouped over the matrices:
 //   k_gram_partial  A_b = P_b^T P_b over blocks of kGramRows rows
 //   k_gram_reduce   A = sum_b A_b in block order
-//   k_gram_solve    R (right-looking Cholesky) and T = R^-1, one wavefront
-//   k_apply_t       P_hat = P T row by row in fp64, rounded to fp32
+//   k_gram_solve    R by right-looking Cholesky with the dependence rule
+//   k_apply_t       P_hat rows by forward substitution, x R = p, in fp64
+//                   registers, rounded to fp32
 
 // Descriptor of this workgroup: first + map[wg] over a grouped grid, or the
 // single descriptor `first`.
@@ -359,7 +439,7 @@ __device__ __forceinline__ int orth_idx(const OrthDesc* descs, const int32_t* ma
   return first;
 }
 
-constexpr int kGramChunk = 128;  // rows staged in LDS at a time
+constexpr int kGramChunk = kGramRows;  // rows staged in LDS at a time
 
 template <int RP>
 __global__ __launch_bounds__(256) void k_gram_partial(const OrthDesc* __restrict__ descs, const int32_t* __restrict__ map,
@@ -426,97 +506,84 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const OrthDesc* __restrict_
   gram[o.t_off + e] = (s0 + s1) + (s2 + s3);
 }
 
-// One wavefront per factor: Cholesky of A with the dependence rule, then
-// T = R^-1 (lane l computes row l of T, which depends on no other row).
+// One workgroup per factor: right-looking Cholesky of A with the dependence
+// rule.  Each thread keeps RP*RP/256 elements of the (symmetric) Schur
+// complement in registers; at step k the pivot row goes through LDS and every
+// thread applies S_ij -= S_ki S_kj / S_kk to its elements.  Row k of R is
+// S_k. / sqrt(S_kk) (zero for a dependent column).  The upper triangle of the
+// factor's A slot is overwritten with R.
 template <int RP>
-__global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
-                                                   double* __restrict__ gram, float zero_rel) {
-  constexpr int SS = RP + 1;
-  __shared__ double S[RP * SS];   // Schur complement; row k becomes row k of R
-  __shared__ double dg[RP];       // diagonal of A (norms before projection)
-  __shared__ double rkk[RP];      // R_kk, 0 for dependent columns
+__global__ __launch_bounds__(256) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
+                                                    double* __restrict__ gram, float zero_rel) {
+  constexpr int NE = RP * RP / 256;  // elements per thread: e = tid + 256 q
+  __shared__ double row[RP];
+  __shared__ double dg[RP];  // diagonal of A: squared norms before projection
+  __shared__ double rout[RP * RP];
   const OrthDesc o = descs[first + blockIdx.x];
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   double* a = gram + o.t_off;
-  for (int e = lane; e < RP * RP; e += 64) S[(e / RP) * SS + e % RP] = a[e];
-  __syncthreads();
-  if (lane < RP) dg[lane] = S[lane * SS + lane];
-  __syncthreads();
+  double sv[NE];
+#pragma unroll
+  for (int q = 0; q < NE; ++q) sv[q] = a[tid + 256 * q];
+  if (tid < RP) dg[tid] = a[tid * RP + tid];
+  for (int e = tid; e < RP * RP; e += 256) rout[e] = 0.0;
   for (int k = 0; k < r; ++k) {
-    const double d = S[k * SS + k];
-    const double nu0 = sqrt(dg[k]);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+      const int e = tid + 256 * q;
+      if (e / RP == k) row[e % RP] = sv[q];
+    }
+    __syncthreads();
+    const double d = row[k];
+    const double nu0 = sqrt(dg[k]);  // norm before projection
     const double nv = d > 0.0 ? sqrt(d) : 0.0;
     const bool zero = !(nu0 > 0.0) || nv <= (double)zero_rel * nu0;
     const double inv = zero ? 0.0 : 1.0 / nv;
-    __syncthreads();
-    if (lane > k && lane < r) S[k * SS + lane] *= inv;
-    if (lane == 0) {
-      rkk[k] = zero ? 0.0 : nv;
-      S[k * SS + k] = zero ? 0.0 : nv;
+    if (tid < r && tid >= k) rout[k * RP + tid] = tid == k ? (zero ? 0.0 : nv) : row[tid] * inv;
+    const double inv2 = inv * inv;
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+      const int e = tid + 256 * q;
+      const int i = e / RP, j = e % RP;
+      if (i > k && j > k && i < r && j < r) sv[q] = fma(-row[i] * inv2, row[j], sv[q]);
     }
-    __syncthreads();
-    const int w = r - k - 1;
-    for (int e = lane; e < w * w; e += 64) {
-      const int i = k + 1 + e / w, j = k + 1 + e % w;
-      if (i <= j) S[i * SS + j] = fma(-S[k * SS + i], S[k * SS + j], S[i * SS + j]);
-    }
-    __syncthreads();
   }
-  // T = R^-1 on the non-dependent columns: T_lk = (delta_lk - sum_{l<=j<k}
-  // T_lj R_jk) / R_kk, zero for dependent k.  Row l of T uses only row l.
-  double* t = a;  // overwrite A with T
-  if (lane < RP) {
-    double trow[RP];
-#pragma unroll
-    for (int k = 0; k < RP; ++k) trow[k] = 0.0;
-#pragma unroll
-    for (int k = 0; k < RP; ++k) {
-      if (k < r && k >= lane) {
-        double s = k == lane ? 1.0 : 0.0;
-#pragma unroll
-        for (int j = 0; j < RP; ++j)
-          if (j >= lane && j < k) s = fma(-trow[j], S[j * SS + k], s);
-        trow[k] = rkk[k] > 0.0 ? s / rkk[k] : 0.0;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < RP; ++k) t[lane * RP + k] = trow[k];
-  }
+  __syncthreads();
+  for (int e = tid; e < RP * RP; e += 256) a[e] = rout[e];
 }
 
-// P_hat = P T, rows in parallel, evaluated in fp64 and rounded to fp32.
-// Column block k0..k0+15 of P_hat needs the columns a <= k0+15 of P, so the
-// blocks are produced from the last to the first and each overwrites only
-// columns no later block reads.
+// P_hat = P R^-1, one row per thread: x R = p by forward substitution,
+// x_k = (p_k - sum_{j<k} x_j R_jk) / R_kk, x_k = 0 for a dependent column;
+// x is kept in fp64 registers and rounded to fp32 when stored (in place: p_k
+// is read before x_k overwrites it).
 template <int RP>
-__global__ __launch_bounds__(256) void k_apply_t(const OrthDesc* __restrict__ descs, const int32_t* __restrict__ map,
-                                                 int first, int r, float* __restrict__ base,
-                                                 const double* __restrict__ gram) {
-  __shared__ double T[RP * RP];
+__global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restrict__ descs,
+                                                       const int32_t* __restrict__ map, int first, int r,
+                                                       float* __restrict__ base, const double* __restrict__ gram) {
+  __shared__ double Rs[RP * RP];
   int local;
   const OrthDesc o = descs[orth_idx(descs, map, first, local)];
-  const double* t = gram + o.t_off;
-  for (int e = threadIdx.x; e < RP * RP; e += 256) T[e] = t[e];
+  const double* rg = gram + o.t_off;
+  for (int e = threadIdx.x; e < RP * RP; e += kGramRows) Rs[e] = rg[e];
   __syncthreads();
   const int i = local * kGramRows + threadIdx.x;
   if (i >= o.rows) return;
   float* p = base + o.off + i;
   const int64_t ld = o.rows;
-  for (int k0 = (r - 1) / 16 * 16; k0 >= 0; k0 -= 16) {
-    double s[16];
+  double x[RP];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) s[c] = 0.0;
-    const int amax = min(r, k0 + 16);
-#pragma unroll 2
-    for (int a = 0; a < amax; ++a) {
-      const double xa = (double)p[a * ld];
-      const double* trow = &T[a * RP + k0];
+  for (int k = 0; k < RP; ++k) {
+    if (k < r) {
+      double s = (double)p[k * ld];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) s[c] = fma(xa, trow[c], s[c]);
+      for (int j = 0; j < k; ++j) s = fma(-x[j], Rs[j * RP + k], s);
+      const double rkk = Rs[k * RP + k];
+      x[k] = rkk > 0.0 ? s / rkk : 0.0;
+      p[k * ld] = (float)x[k];
+    } else {
+      x[k] = 0.0;
     }
-#pragma unroll
-    for (int c = 0; c < 16; ++c)
-      if (k0 + c < r) p[(k0 + c) * ld] = (float)s[c];
   }
 }
 
@@ -610,11 +677,12 @@ static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const i
                      c.gram);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(64), 0, c.stream, c.orth, first, c.rank, c.gram,
+  hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(256), 0, c.stream, c.orth, first, c.rank, c.gram,
                      kZeroColumnRel);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_apply_t<RP>), dim3(nblocks), dim3(256), 0, c.stream, c.orth, map, first, c.rank, base, c.gram);
+  hipLaunchKernelGGL((k_apply_t<RP>), dim3(nblocks), dim3(kGramRows), 0, c.stream, c.orth, map, first, c.rank, base,
+                     c.gram);
   return hipGetLastError();
 }
 

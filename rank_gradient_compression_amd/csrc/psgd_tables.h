@@ -31,7 +31,7 @@ constexpr int64_t kAlignElems = 64;
 // of 16).
 constexpr int kMfmaRows = 64;      // rows of one MFMA pass-1 / pass-3 workgroup tile
 constexpr int kMfmaCols = 256;     // columns of one MFMA pass-2 workgroup tile
-constexpr int kGramRows = 256;     // rows of one Gram-partial / apply workgroup
+constexpr int kGramRows = 128;     // rows of one Gram-partial / apply workgroup
 
 // One compressed matrix.
 struct MatDesc {
