@@ -83,6 +83,45 @@ typedef enum psgd_status {
 
 typedef struct psgd_plan* psgd_plan_t;
 
+/* Step flags (psgd_step_opts_t.flags). */
+#define PSGD_STEP_NO_ERROR_FEEDBACK 1u /* ablation: compress X alone, M = X; the error
+                                          memory is neither read nor accumulated ([N152]
+                                          Recommendations: error feedback is not optional) */
+
+/*
+ * Options of one psgd_compress call; a NULL pointer means all defaults.
+ *   power_iters    subspace iterations in the step (0 or 1: the single
+ *                  warm-started iteration of [N152] Method; k > 1 repeats
+ *                  P = M Q, P_hat = GS(P), Q = M^T P_hat k times, with both
+ *                  hooks called in every iteration -- the glossary's "one or
+ *                  two power iterations").
+ *   refresh_iters  0 for a plain step.  k > 0 makes this a PowerSGD+ step
+ *                  ([PSGD+] Abstract: the projection subspace is periodically
+ *                  re-aligned with the optimal one through an SVD): after the
+ *                  EF-add, every warm-start Q is replaced by k rounds of block
+ *                  power iteration with orthonormalisation on M,
+ *                  Q <- GS(M^T GS(M Q)), before P = M Q.  The caller chooses
+ *                  the period (for example every 50th step).
+ *   flags          PSGD_STEP_NO_ERROR_FEEDBACK or 0.
+ *   params, sgd_buf, sgd_lr, sgd_momentum
+ *                  fused post-compression momentum SGD ([N152] Concepts,
+ *                  "Post-compression momentum"): when params is non-NULL, the
+ *                  decompressed (aggregated) update D of every tensor is
+ *                  applied in the residual pass as heavy-ball SGD,
+ *                  m <- sgd_momentum * m + D, x <- x - sgd_lr * m, on the flat
+ *                  parameter buffer `params` and the flat buffer `sgd_buf`
+ *                  (both in/out, plan layout, required together).
+ */
+typedef struct psgd_step_opts {
+  int32_t power_iters;
+  int32_t refresh_iters;
+  uint32_t flags;
+  float sgd_lr;
+  float sgd_momentum;
+  float* params;
+  float* sgd_buf;
+} psgd_step_opts_t;
+
 /* Sizes derived from a plan.  Element counts are fp32 elements. */
 typedef struct psgd_plan_info {
   int32_t ntensors;
@@ -183,24 +222,22 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  *          P_hat Q^T for compressed tensors and the aggregated values of the
  *          pass-through tensors (a fused psgd_decompress).  It may alias
  *          `grads` (then G is overwritten by the update) but no other buffer.
- *   refresh_iters  0 for a plain step.  k > 0 makes this a PowerSGD+ step
- *          ([PSGD+] Abstract: the projection subspace is periodically
- *          re-aligned with the optimal one through an SVD): after the EF-add,
- *          every warm-start Q is replaced by k rounds of block power iteration
- *          with orthonormalisation on M, Q <- GS(M^T GS(M Q)), before P = M Q.
- *          The caller chooses the period (for example every 50th step).
+ *   opts   nullable step options (psgd_step_opts_t): power iterations,
+ *          PowerSGD+ refresh, the no-error-feedback ablation, fused
+ *          post-compression momentum SGD.
  *   hook   nullable aggregation hook, called on (p, p_buffer_elems) after P is
  *          formed and on (q, q_elems) after Q is formed.
  *   workspace, workspace_bytes   initialised workspace (psgd_workspace_init).
  *
  * Errors: PSGD_ERR_INVALID_ARG for null or not 16-byte aligned buffers, a
- * missing or unexpected `mom`, a negative refresh_iters; PSGD_ERR_WORKSPACE;
+ * missing or unexpected `mom`, negative iteration counts, `params` without
+ * `sgd_buf` (or misaligned), unknown step flags; PSGD_ERR_WORKSPACE;
  * PSGD_ERR_HOOK if a hook
  * returns non-zero (no later stage is enqueued); PSGD_ERR_HIP.
  */
 psgd_status_t psgd_compress(psgd_plan_t plan, const float* grads, float* err, float* mom, float* q,
-                            float* p, float* mhat, int32_t refresh_iters, psgd_reduce_fn hook, void* user,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+                            float* p, float* mhat, const psgd_step_opts_t* opts, psgd_reduce_fn hook,
+                            void* user, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * psgd_decompress -- reconstruct G ~ P_hat Q^T ([GLOSS], factorisation

@@ -5,4 +5,4 @@ from .powersgd import *  # noqa: F401,F403
 from .powersgd import (KIND_COMPRESSED, KIND_PASSTHRU, KIND_VECTOR, Plan, SetResult, SetState,  # noqa: F401
                        ZERO_COLUMN_REL, classify, compress_matrix, compress_workers, decompress,
                        gram_schmidt, init_state, matrix_view, momentum_input, orthonormality_error,
-                       principal_angle_sines, refresh, step_set)
+                       principal_angle_sines, refresh, sgd_momentum_step, step_set)

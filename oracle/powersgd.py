@@ -35,6 +35,11 @@ design notes of the repository):
   R7  PowerSGD+ refresh: at a refresh step, before P = M Q, repeat `iters`
       times Q <- GS(M^T GS(M Q)) on the current M, starting from the current
       warm-start Q; the normal step then follows from the refreshed Q.
+  R8  several power iterations in one step (the glossary's "one or two"):
+      P = M Q, aggregate, P_hat = GS(P), Q = M^T P_hat, aggregate, repeated,
+      each iteration starting from the previous one's Q.
+  R9  post-compression momentum ([N152] Concepts): heavy-ball SGD on the
+      decompressed, aggregated update D: m <- mu m + D, x <- x - lr m.
 """
 from __future__ import annotations
 
@@ -147,21 +152,23 @@ class MatrixResult:
 
 
 def compress_matrix(M: np.ndarray, Q_warm: np.ndarray, hook_p: Hook = None,
-                    hook_q: Hook = None) -> MatrixResult:
+                    hook_q: Hook = None, power_iters: int = 1) -> MatrixResult:
     """One warm-started subspace iteration on M ([N152] Method):
     right multiply P = M Q, aggregate P, orthogonalise to P_hat, left multiply
     Q = M^T P_hat, aggregate Q.  Then the reconstruction P_hat Q^T and the
     error-feedback residual M - P_hat Q^T ([GLOSS] error-feedback paragraph;
-    [N152] Concepts, "Error feedback")."""
+    [N152] Concepts, "Error feedback").  power_iters > 1 repeats the
+    iteration from the new Q (reading R8)."""
     M = np.asarray(M, dtype=np.float64)
-    Qw = np.asarray(Q_warm, dtype=np.float64)
-    P = M @ Qw
-    if hook_p is not None:
-        P = hook_p(P)
-    P_hat = gram_schmidt(P)
-    Q = M.T @ P_hat
-    if hook_q is not None:
-        Q = hook_q(Q)
+    Q = np.asarray(Q_warm, dtype=np.float64)
+    for _ in range(max(1, power_iters)):
+        P = M @ Q
+        if hook_p is not None:
+            P = hook_p(P)
+        P_hat = gram_schmidt(P)
+        Q = M.T @ P_hat
+        if hook_q is not None:
+            Q = hook_q(Q)
     M_hat = P_hat @ Q.T
     E = M - M_hat
     return MatrixResult(P_hat=P_hat, Q=Q, M_hat=M_hat, E=E, P=P)
@@ -182,6 +189,13 @@ def refresh(M: np.ndarray, Q: np.ndarray, iters: int) -> np.ndarray:
         P_hat = gram_schmidt(M @ Q)
         Q = gram_schmidt(M.T @ P_hat)
     return Q
+
+
+def sgd_momentum_step(x: np.ndarray, m: np.ndarray, D: np.ndarray, lr: float, mu: float):
+    """Post-compression momentum ([N152] Concepts; reading R9): heavy-ball
+    SGD with the decompressed update D.  Returns (x, m)."""
+    m = mu * np.asarray(m, np.float64) + np.asarray(D, np.float64)
+    return np.asarray(x, np.float64) - lr * m, m
 
 
 def momentum_input(u: np.ndarray, G: np.ndarray, beta: float) -> np.ndarray:
@@ -231,12 +245,14 @@ class SetResult:
 
 
 def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: float = 0.0,
-             refresh_iters: int = 0, hook_p: Hook = None, hook_q: Hook = None) -> SetResult:
+             refresh_iters: int = 0, hook_p: Hook = None, hook_q: Hook = None, power_iters: int = 1,
+             error_feedback: bool = True) -> SetResult:
     """One compression step over a model's set, updating `state` in place.
 
-    Per compressed matrix: X = G (or the momentum u), M = X + E, optional
-    refresh of the warm-start Q, then `compress_matrix`; E and Q are replaced by
-    the new residual and Q.  Pass-through tensors send X unchanged."""
+    Per compressed matrix: X = G (or the momentum u), M = X + E (M = X when
+    error feedback is off, an ablation), optional refresh of the warm-start
+    Q, then `compress_matrix`; E and Q are replaced by the new residual and Q.
+    Pass-through tensors send X unchanged."""
     Ph: List[Optional[np.ndarray]] = []
     Qs: List[Optional[np.ndarray]] = []
     Mh: List[np.ndarray] = []
@@ -254,11 +270,11 @@ def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: flo
             Mh.append(X.copy())
             Ms.append(None)
             continue
-        M = X + state.E[i]
+        M = X + state.E[i] if error_feedback else X.copy()
         Qw = state.Q[i]
         if refresh_iters > 0:
             Qw = refresh(M, Qw, refresh_iters)
-        res = compress_matrix(M, Qw, hook_p, hook_q)
+        res = compress_matrix(M, Qw, hook_p, hook_q, power_iters=power_iters)
         state.E[i] = res.E
         state.Q[i] = res.Q
         Ph.append(res.P_hat)

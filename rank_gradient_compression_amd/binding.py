@@ -65,6 +65,22 @@ class psgd_plan_info_t(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+PSGD_STEP_NO_ERROR_FEEDBACK = 1
+
+
+class psgd_step_opts_t(ctypes.Structure):
+    _fields_ = [
+        ("power_iters", ctypes.c_int32), ("refresh_iters", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("sgd_lr", ctypes.c_float), ("sgd_momentum", ctypes.c_float), ("params", ctypes.c_void_p),
+        ("sgd_buf", ctypes.c_void_p),
+    ]
+
+
+def step_opts(power_iters: int = 0, refresh_iters: int = 0, flags: int = 0, sgd_lr: float = 0.0,
+              sgd_momentum: float = 0.0, params: int = 0, sgd_buf: int = 0) -> psgd_step_opts_t:
+    return psgd_step_opts_t(power_iters, refresh_iters, flags, sgd_lr, sgd_momentum, params or None, sgd_buf or None)
+
+
 psgd_reduce_fn = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p)
 
 if not os.path.exists(LIB_PATH):
@@ -104,8 +120,8 @@ lib.psgd_plan_destroy.restype = None
 lib.psgd_plan_get_info.argtypes = [_vp, ctypes.POINTER(psgd_plan_info_t)]
 lib.psgd_plan_tensor.argtypes = [_vp, ctypes.c_int32, _i32p, _i64p, _i64p, _i64p]
 lib.psgd_workspace_init.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
-lib.psgd_compress.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, psgd_reduce_fn, _vp, _vp,
-                              ctypes.c_size_t, _vp]
+lib.psgd_compress.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(psgd_step_opts_t), psgd_reduce_fn,
+                              _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_decompress.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_refresh.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
 lib.psgd_timing_enable.argtypes = [_vp, ctypes.c_int32]
@@ -176,11 +192,12 @@ def make_hook(fn: Callable[[int, int, int], int]):
     return psgd_reduce_fn(lambda buf, count, stream, user: int(fn(buf or 0, count, stream or 0)))
 
 
-def psgd_compress(plan: int, grads: int, err: int, mom: int, q: int, p: int, mhat: int, refresh_iters: int, hook,
-                  workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+def psgd_compress(plan: int, grads: int, err: int, mom: int, q: int, p: int, mhat: int,
+                  opts: Optional[psgd_step_opts_t], hook, workspace: int, workspace_bytes: int, stream: int = 0) -> None:
     h = hook if hook is not None else psgd_reduce_fn()
-    _check("psgd_compress", lib.psgd_compress(plan, grads, err or None, mom or None, q or None, p, mhat or None,
-                                              refresh_iters, h, None, workspace, workspace_bytes, stream))
+    o = ctypes.byref(opts) if opts is not None else None
+    _check("psgd_compress", lib.psgd_compress(plan, grads, err or None, mom or None, q or None, p, mhat or None, o,
+                                              h, None, workspace, workspace_bytes, stream))
 
 
 def psgd_decompress(plan: int, p: int, q: int, out: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:

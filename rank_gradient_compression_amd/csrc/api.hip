@@ -147,8 +147,8 @@ static hipError_t stage_mtp(const LaunchCtx& c, const GridRange& g, const GridRa
 }
 
 static hipError_t stage_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
-                              bool residual) {
-  return c.mfma ? launch_mfma_recon(c, E, Q, Ph, Mhat, residual) : launch_recon(c, E, Q, Ph, Mhat, residual);
+                              bool residual, const SgdArgs& sg) {
+  return c.mfma ? launch_mfma_recon(c, E, Q, Ph, Mhat, residual, sg) : launch_recon(c, E, Q, Ph, Mhat, residual, sg);
 }
 
 static psgd_status_t check_ws(const psgd_plan* p, const void* ws, size_t bytes, const char* fn) {
@@ -210,8 +210,8 @@ extern "C" psgd_status_t psgd_workspace_init(psgd_plan_t p, void* ws, size_t byt
 }
 
 extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const float* grads, float* err, float* mom, float* q, float* pbuf,
-                                       float* mhat, int32_t refresh_iters, psgd_reduce_fn hook, void* user, void* ws,
-                                       size_t ws_bytes, hipStream_t stream) {
+                                       float* mhat, const psgd_step_opts_t* opts, psgd_reduce_fn hook, void* user,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   if (!p) {
     set_error("psgd_compress: plan is NULL");
@@ -240,17 +240,36 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const float* grads, float*
     set_error("psgd_compress: mhat may alias grads only");
     return PSGD_ERR_INVALID_ARG;
   }
-  if (refresh_iters < 0) {
-    set_error("psgd_compress: negative refresh_iters");
+  psgd_step_opts_t o{};
+  if (opts) o = *opts;
+  if (o.power_iters < 0 || o.refresh_iters < 0) {
+    set_error("psgd_compress: negative iteration count");
     return PSGD_ERR_INVALID_ARG;
   }
+  if (o.flags & ~PSGD_STEP_NO_ERROR_FEEDBACK) {
+    set_error("psgd_compress: unknown step flag bits 0x%x", o.flags & ~PSGD_STEP_NO_ERROR_FEEDBACK);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if ((o.params != nullptr) != (o.sgd_buf != nullptr) || !aligned16(o.params) || !aligned16(o.sgd_buf)) {
+    set_error("psgd_compress: params and sgd_buf must be given together, 16-byte aligned");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (o.params && (o.params == err || o.params == mom || o.params == mhat || o.sgd_buf == err ||
+                   o.sgd_buf == mom || o.sgd_buf == mhat || o.params == o.sgd_buf)) {
+    set_error("psgd_compress: params / sgd_buf must not alias the other buffers");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  const int refresh_iters = o.refresh_iters;
+  const int power_iters = o.power_iters > 1 ? o.power_iters : 1;
+  const bool ef = (o.flags & PSGD_STEP_NO_ERROR_FEEDBACK) == 0;
+  const SgdArgs sg{o.params, o.sgd_buf, o.sgd_lr, o.sgd_momentum};
   if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_compress")) return s;
   if (!any) return PSGD_OK;
 
   const LaunchCtx c = make_ctx(p, ws, stream);
   float* U = momentum ? mom : nullptr;
   const GridRange all_rows{0, c.wg_rows}, all_pred{0, c.wg_pred}, all_mtp{0, c.wg_mtp}, all_red{0, c.wg_red};
-  const int mode = momentum ? 2 : 1;
+  const int mode = ef ? (momentum ? 2 : 1) : (momentum ? 4 : 3);
 
   PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_pack(c, grads, U, p->beta, pbuf), "pass-through pack");
   if (refresh_iters <= 0) {
@@ -271,23 +290,32 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const float* grads, float*
     PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, all_rows, all_pred, 0, nullptr, err, nullptr, q, pbuf, -1),
                 "P = M Q");
   }
-  if (hook && hook(pbuf, p->p_elems + p->pt_elems, stream, user) != 0) {
-    set_error("psgd_compress: aggregation hook failed on P");
-    return PSGD_ERR_HOOK;
+  // One (or power_iters) subspace iterations, with both aggregation hooks in
+  // each; later iterations start again from P = M Q with the new Q.
+  for (int it = 0; it < power_iters; ++it) {
+    if (it > 0)
+      PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, all_rows, all_pred, 0, nullptr, err, nullptr, q, pbuf, -1),
+                  "P = M Q");
+    if (hook && hook(pbuf, p->p_elems + p->pt_elems, stream, user) != 0) {
+      set_error("psgd_compress: aggregation hook failed on P");
+      return PSGD_ERR_HOOK;
+    }
+    PSGD_LAUNCH(PSGD_STAGE_GS, stage_orth_all_p(c, pbuf), "orthogonalise P");
+    {
+      StageTimer _t(p, PSGD_STAGE_MTP, stream);
+      const hipError_t e =
+          c.mfma ? launch_mfma_qt(c, all_mtp, err, pbuf, -1, q) : launch_mtp(c, all_mtp, err, pbuf, -1, q);
+      if (e != hipSuccess) return hip_fail(e, "Q = M^T P_hat");
+    }
+    PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, all_red, q), "Q partial reduction");
+    if (hook && hook(q, p->q_elems, stream, user) != 0) {
+      set_error("psgd_compress: aggregation hook failed on Q");
+      return PSGD_ERR_HOOK;
+    }
   }
-  PSGD_LAUNCH(PSGD_STAGE_GS, stage_orth_all_p(c, pbuf), "orthogonalise P");
-  {
-    StageTimer _t(p, PSGD_STAGE_MTP, stream);
-    const hipError_t e = c.mfma ? launch_mfma_qt(c, all_mtp, err, pbuf, -1, q) : launch_mtp(c, all_mtp, err, pbuf, -1, q);
-    if (e != hipSuccess) return hip_fail(e, "Q = M^T P_hat");
-  }
-  PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, all_red, q), "Q partial reduction");
-  if (hook && hook(q, p->q_elems, stream, user) != 0) {
-    set_error("psgd_compress: aggregation hook failed on Q");
-    return PSGD_ERR_HOOK;
-  }
-  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, err, q, pbuf, mhat, true), "residual E = M - P_hat Q^T");
-  if (mhat) PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat), "pass-through unpack");
+  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, err, q, pbuf, mhat, true, sg), "residual E = M - P_hat Q^T");
+  if (mhat || sg.x)
+    PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat, sg), "pass-through unpack");
   return PSGD_OK;
 }
 
@@ -309,8 +337,9 @@ extern "C" psgd_status_t psgd_decompress(psgd_plan_t p, const float* pbuf, const
   if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_decompress")) return s;
   if (p->ntensors == 0) return PSGD_OK;
   const LaunchCtx c = make_ctx(p, ws, stream);
-  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, nullptr, q, pbuf, out, false), "decompress P_hat Q^T");
-  PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out), "pass-through unpack");
+  const SgdArgs none{nullptr, nullptr, 0.f, 0.f};
+  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, nullptr, q, pbuf, out, false, none), "decompress P_hat Q^T");
+  PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out, none), "pass-through unpack");
   return PSGD_OK;
 }
 

@@ -92,7 +92,8 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 
 // ---------------------------------------------------------------------------
 // Pass 1: P = M Q (MODE 0: M read as is; 1: M = G + E stored over E;
-// 2: u = beta u + G, M = u + E)
+// 2: u = beta u + G, M = u + E; 3: M = G; 4: u = beta u + G, M = u --
+// modes 3 and 4 without error feedback, M still stored over E)
 // ---------------------------------------------------------------------------
 
 template <int RP, int MODE, bool VEC4>
@@ -129,10 +130,11 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
       if constexpr (MODE == 0) {
         x[qq] = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
       } else {
+        constexpr bool LOAD_E = MODE <= 2;
         const float4 g = ldq<VEC4>(G + roff, col, col_ok, c_begin, n);
-        const float4 e = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
+        const float4 e = LOAD_E ? ldq<VEC4>(E + roff, col, col_ok, c_begin, n) : make_float4(0.f, 0.f, 0.f, 0.f);
         float4 s;
-        if constexpr (MODE == 2) {
+        if constexpr (MODE == 2 || MODE == 4) {
           float4 u = ldq<VEC4>(U + roff, col, col_ok, c_begin, n);
           u.x = fmaf(beta, u.x, g.x);
           u.y = fmaf(beta, u.y, g.y);
@@ -329,10 +331,10 @@ __global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mat
 // 16-column tile of the workgroup's column split.
 // ---------------------------------------------------------------------------
 
-template <int RP, bool READ_M, bool WRITE_E, bool WRITE_MHAT, bool VEC4>
+template <int RP, bool READ_M, bool WRITE_E, bool WRITE_MHAT, bool SGD, bool VEC4>
 __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r, float* __restrict__ E,
                                                 const float* __restrict__ Q, const float* __restrict__ Ph,
-                                                float* __restrict__ Mhat) {
+                                                float* __restrict__ Mhat, const SgdArgs& sg) {
   constexpr int KS = RP / 4;  // k-steps of 4 rank columns
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_rows0;
@@ -365,12 +367,15 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
     }
     const int col = j0 + 4 * ls;
     const bool col_ok = col < c_end;
-    float4 xm[4];
-    if constexpr (READ_M) {
+    float4 xm[4], xx[4], xb[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int rr = i0 + 16 * rt + li;
-        xm[rt] = ldq<VEC4>(E + d.off + (int64_t)min(rr, m - 1) * n, col, rr < m && col_ok, c_begin, n);
+    for (int rt = 0; rt < 4; ++rt) {
+      const int rr = i0 + 16 * rt + li;
+      const int64_t ro = d.off + (int64_t)min(rr, m - 1) * n;
+      if constexpr (READ_M) xm[rt] = ldq<VEC4>(E + ro, col, rr < m && col_ok, c_begin, n);
+      if constexpr (SGD) {
+        xx[rt] = ldq<VEC4>(sg.x + ro, col, rr < m && col_ok, c_begin, n);
+        xb[rt] = ldq<VEC4>(sg.m + ro, col, rr < m && col_ok, c_begin, n);
       }
     }
 #pragma unroll
@@ -387,23 +392,36 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
           stq<VEC4>(rowp, col, n, make_float4(x.x - mh.x, x.y - mh.y, x.z - mh.z, x.w - mh.w));
         }
         if constexpr (WRITE_MHAT) stq<VEC4>(Mhat + d.off + (int64_t)rr * n, col, n, mh);
+        if constexpr (SGD) {
+          float4 mm = xb[rt], xp = xx[rt];
+          mm.x = fmaf(sg.mu, mm.x, mh.x);
+          mm.y = fmaf(sg.mu, mm.y, mh.y);
+          mm.z = fmaf(sg.mu, mm.z, mh.z);
+          mm.w = fmaf(sg.mu, mm.w, mh.w);
+          xp.x = fmaf(-sg.lr, mm.x, xp.x);
+          xp.y = fmaf(-sg.lr, mm.y, xp.y);
+          xp.z = fmaf(-sg.lr, mm.z, xp.z);
+          xp.w = fmaf(-sg.lr, mm.w, xp.w);
+          stq<VEC4>(sg.m + d.off + (int64_t)rr * n, col, n, mm);
+          stq<VEC4>(sg.x + d.off + (int64_t)rr * n, col, n, xp);
+        }
       }
     }
   }
 }
 
-template <int RP, bool READ_M, bool WRITE_E, bool WRITE_MHAT>
+template <int RP, bool RESID, bool WRITE_MHAT, bool SGD>
 __global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
                                                     int wg_base, int r, float* __restrict__ E,
                                                     const float* __restrict__ Q, const float* __restrict__ Ph,
-                                                    float* __restrict__ Mhat) {
+                                                    float* __restrict__ Mhat, SgdArgs sg) {
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
   if (d.vec == 4)
-    mfma_recon_body<RP, READ_M, WRITE_E, WRITE_MHAT, true>(d, wg, r, E, Q, Ph, Mhat);
+    mfma_recon_body<RP, RESID, RESID, WRITE_MHAT, SGD, true>(d, wg, r, E, Q, Ph, Mhat, sg);
   else
-    mfma_recon_body<RP, READ_M, WRITE_E, WRITE_MHAT, false>(d, wg, r, E, Q, Ph, Mhat);
+    mfma_recon_body<RP, RESID, RESID, WRITE_MHAT, SGD, false>(d, wg, r, E, Q, Ph, Mhat, sg);
 }
 
 // ---------------------------------------------------------------------------
@@ -611,8 +629,14 @@ static hipError_t mfma_p_rp(const LaunchCtx& c, const GridRange& g, int mode, co
   else if (mode == 1)
     hipLaunchKernelGGL((k_mfma_p<RP, 1>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
                        P, p_fixed, c.ppart);
-  else
+  else if (mode == 2)
     hipLaunchKernelGGL((k_mfma_p<RP, 2>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
+                       P, p_fixed, c.ppart);
+  else if (mode == 3)
+    hipLaunchKernelGGL((k_mfma_p<RP, 3>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
+                       P, p_fixed, c.ppart);
+  else
+    hipLaunchKernelGGL((k_mfma_p<RP, 4>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
                        P, p_fixed, c.ppart);
   return hipGetLastError();
 }
@@ -645,24 +669,31 @@ hipError_t launch_mfma_qt(const LaunchCtx& c, const GridRange& g, const float* M
 
 template <int RP>
 static hipError_t mfma_recon_rp(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
-                                bool residual) {
+                                bool residual, const SgdArgs& sg) {
   if (c.wg_rows == 0) return hipSuccess;
   const dim3 g(c.wg_rows), b(256);
-  if (residual && Mhat)
-    hipLaunchKernelGGL((k_mfma_recon<RP, true, true, true>), g, b, 0, c.stream, c.mats, c.rows_map, 0, c.rank, E, Q,
-                       Ph, Mhat);
-  else if (residual)
-    hipLaunchKernelGGL((k_mfma_recon<RP, true, true, false>), g, b, 0, c.stream, c.mats, c.rows_map, 0, c.rank, E, Q,
-                       Ph, Mhat);
-  else
-    hipLaunchKernelGGL((k_mfma_recon<RP, false, false, true>), g, b, 0, c.stream, c.mats, c.rows_map, 0, c.rank, E,
-                       Q, Ph, Mhat);
+  const bool mh = Mhat != nullptr, sgd = sg.x != nullptr;
+#define PSGD_MRECON(RS, MH, SG)                                                                              \
+  hipLaunchKernelGGL((k_mfma_recon<RP, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rows_map, 0, c.rank, E, Q, Ph, \
+                     Mhat, sg)
+  if (residual) {
+    if (mh && sgd) PSGD_MRECON(true, true, true);
+    else if (mh) PSGD_MRECON(true, true, false);
+    else if (sgd) PSGD_MRECON(true, false, true);
+    else PSGD_MRECON(true, false, false);
+  } else {
+    if (mh && sgd) PSGD_MRECON(false, true, true);
+    else if (mh) PSGD_MRECON(false, true, false);
+    else if (sgd) PSGD_MRECON(false, false, true);
+    else return hipSuccess;
+  }
+#undef PSGD_MRECON
   return hipGetLastError();
 }
 
 hipError_t launch_mfma_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
-                             bool residual) {
-  PSGD_RP_SWITCH(c.rank_pad, mfma_recon_rp<RPV>(c, E, Q, Ph, Mhat, residual));
+                             bool residual, const SgdArgs& sg) {
+  PSGD_RP_SWITCH(c.rank_pad, mfma_recon_rp<RPV>(c, E, Q, Ph, Mhat, residual, sg));
 }
 
 template <int RP>

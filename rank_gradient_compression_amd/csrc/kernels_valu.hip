@@ -132,11 +132,15 @@ constexpr int pow2_at_least(int x) {
 // One wavefront: rows [row0, row0 + kWaveRows) of matrix d, all columns.  Each
 // lane keeps its VEC x R slice of Q in registers for the current column step
 // and reuses it across the wavefront's rows.
+// MODE 0: M read from E (plain M Q); 1: M = G + E; 2: u = beta u + G,
+// M = u + E; 3: M = G (no error feedback); 4: u = beta u + G, M = u.  Modes
+// 1..4 store M over E.
 template <int R, int VEC, int MODE>
 __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, const float* __restrict__ G,
                                           float* __restrict__ E, float* __restrict__ U, float beta,
                                           const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed) {
-  constexpr bool MOM = MODE == 2;
+  constexpr bool MOM = MODE == 2 || MODE == 4;
+  constexpr bool LOAD_E = MODE <= 2;
   const int m = d.m, n = d.n;
   const int nrows = min(kWaveRows, m - row0);
   float acc[kWaveRows][R];
@@ -156,7 +160,7 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
     for (int rr = 0; rr < kWaveRows; ++rr) {
       const int64_t idx = base + (int64_t)min(rr, nrows - 1) * n + j;
       if constexpr (MODE != 0) g[rr] = ldv_nt<VEC>(G + idx);  // read once per step: streaming hint
-      e[rr] = ldv<VEC>(E + idx);
+      if constexpr (LOAD_E) e[rr] = ldv<VEC>(E + idx);
     }
     Vec<VEC> u[kWaveRows];
     if constexpr (MOM) {
@@ -175,10 +179,10 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
           for (int c = 0; c < VEC; ++c) u[rr].v[c] = fmaf(beta, u[rr].v[c], g[rr].v[c]);
           stv<VEC>(U + idx, u[rr]);
 #pragma unroll
-          for (int c = 0; c < VEC; ++c) mv.v[c] = u[rr].v[c] + e[rr].v[c];
+          for (int c = 0; c < VEC; ++c) mv.v[c] = LOAD_E ? u[rr].v[c] + e[rr].v[c] : u[rr].v[c];
         } else {
 #pragma unroll
-          for (int c = 0; c < VEC; ++c) mv.v[c] = g[rr].v[c] + e[rr].v[c];
+          for (int c = 0; c < VEC; ++c) mv.v[c] = LOAD_E ? g[rr].v[c] + e[rr].v[c] : g[rr].v[c];
         }
         if constexpr (MODE != 0) stv<VEC>(E + idx, mv);
 #pragma unroll
@@ -326,10 +330,13 @@ __global__ __launch_bounds__(kRedCols) void k_qreduce(const MatDesc* __restrict_
 // Pass 3: residual E = M - P_hat Q^T (+ M_hat); decompression
 // ---------------------------------------------------------------------------
 
-template <int R, int VEC, bool READ_M, bool WRITE_E, bool WRITE_MHAT>
+// RESID: E <- M - M_hat (M read from E).  WRITE_MHAT: M_hat stored.  SGD:
+// post-compression heavy-ball step with the decompressed update M_hat,
+// m <- mu m + M_hat, x <- x - lr m (X = parameters, Mb = momentum buffer).
+template <int R, int VEC, bool RESID, bool WRITE_MHAT, bool SGD>
 __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane, float* __restrict__ E,
                                            const float* __restrict__ Q, const float* __restrict__ Ph,
-                                           float* __restrict__ Mhat) {
+                                           float* __restrict__ Mhat, const SgdArgs& sg) {
   const int m = d.m, n = d.n;
   const int nrows = min(kWaveRows, m - row0);
   float ph[kWaveRows][R];
@@ -343,10 +350,15 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane,
     Vec<VEC> qv[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) qv[k] = ldv<VEC>(q + (int64_t)k * n + j);
-    Vec<VEC> x[kWaveRows];
-    if constexpr (READ_M) {
+    Vec<VEC> x[kWaveRows], xp[kWaveRows], xm[kWaveRows];
 #pragma unroll
-      for (int rr = 0; rr < kWaveRows; ++rr) x[rr] = ldv_nt<VEC>(E + base + (int64_t)min(rr, nrows - 1) * n + j);
+    for (int rr = 0; rr < kWaveRows; ++rr) {
+      const int64_t idx = base + (int64_t)min(rr, nrows - 1) * n + j;
+      if constexpr (RESID) x[rr] = ldv_nt<VEC>(E + idx);
+      if constexpr (SGD) {
+        xp[rr] = ldv<VEC>(sg.x + idx);
+        xm[rr] = ldv<VEC>(sg.m + idx);
+      }
     }
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
@@ -360,7 +372,7 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane,
           for (int k = 1; k < R; ++k) s = fmaf(ph[rr][k], qv[k].v[c], s);
           mh.v[c] = s;
         }
-        if constexpr (WRITE_E) {
+        if constexpr (RESID) {
           Vec<VEC> e;
 #pragma unroll
           for (int c = 0; c < VEC; ++c) e.v[c] = x[rr].v[c] - mh.v[c];
@@ -369,26 +381,36 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane,
         // M_hat is consumed by the optimizer after the step, not by this
         // pipeline: streaming store.
         if constexpr (WRITE_MHAT) stv_nt<VEC>(Mhat + idx, mh);
+        if constexpr (SGD) {
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) {
+            xm[rr].v[c] = fmaf(sg.mu, xm[rr].v[c], mh.v[c]);
+            xp[rr].v[c] = fmaf(-sg.lr, xm[rr].v[c], xp[rr].v[c]);
+          }
+          stv<VEC>(sg.m + idx, xm[rr]);
+          stv<VEC>(sg.x + idx, xp[rr]);
+        }
       }
     }
   }
 }
 
-template <int R, bool READ_M, bool WRITE_E, bool WRITE_MHAT>
+template <int R, bool RESID, bool WRITE_MHAT, bool SGD>
 __global__ __launch_bounds__(kWGThreads) void k_recon(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
                                                       float* __restrict__ E, const float* __restrict__ Q,
-                                                      const float* __restrict__ Ph, float* __restrict__ Mhat) {
+                                                      const float* __restrict__ Ph, float* __restrict__ Mhat,
+                                                      SgdArgs sg) {
   const int wg = blockIdx.x;
   const MatDesc d = mats[map[wg]];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
   if (row0 >= d.m) return;
   if (d.vec == 4)
-    recon_wave<R, 4, READ_M, WRITE_E, WRITE_MHAT>(d, row0, lane, E, Q, Ph, Mhat);
+    recon_wave<R, 4, RESID, WRITE_MHAT, SGD>(d, row0, lane, E, Q, Ph, Mhat, sg);
   else if (d.vec == 2)
-    recon_wave<R, 2, READ_M, WRITE_E, WRITE_MHAT>(d, row0, lane, E, Q, Ph, Mhat);
+    recon_wave<R, 2, RESID, WRITE_MHAT, SGD>(d, row0, lane, E, Q, Ph, Mhat, sg);
   else
-    recon_wave<R, 1, READ_M, WRITE_E, WRITE_MHAT>(d, row0, lane, E, Q, Ph, Mhat);
+    recon_wave<R, 1, RESID, WRITE_MHAT, SGD>(d, row0, lane, E, Q, Ph, Mhat, sg);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,13 +435,25 @@ __global__ __launch_bounds__(256) void k_pass_pack(const PassDesc* __restrict__ 
   }
 }
 
+// Aggregated pass-through values back to flat buffers: into `out` (if
+// non-null) and/or as the update of the fused SGD step.
+template <bool SGD>
 __global__ __launch_bounds__(256) void k_pass_unpack(const PassDesc* __restrict__ pass, const int32_t* __restrict__ map,
-                                                     const float* __restrict__ Pbuf, float* __restrict__ out) {
+                                                     const float* __restrict__ Pbuf, float* __restrict__ out,
+                                                     SgdArgs sg) {
   const int wg = blockIdx.x;
   const PassDesc pd = pass[map[wg]];
   const int64_t c0 = (int64_t)(wg - pd.wg0) * kPassChunk;
   const int64_t c1 = c0 + kPassChunk < pd.len ? c0 + kPassChunk : pd.len;
-  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) out[pd.off + i] = Pbuf[pd.p_off + i];
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
+    const float v = Pbuf[pd.p_off + i];
+    if (out) out[pd.off + i] = v;
+    if constexpr (SGD) {
+      const float mm = fmaf(sg.mu, sg.m[pd.off + i], v);
+      sg.m[pd.off + i] = mm;
+      sg.x[pd.off + i] = fmaf(-sg.lr, mm, sg.x[pd.off + i]);
+    }
+  }
 }
 
 // Plain 16-byte copy: the bandwidth ceiling and counter calibration.
@@ -438,7 +472,11 @@ static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode
                                 float beta, const float* Q, float* P, int64_t p_fixed) {
   if (g.count == 0) return hipSuccess;
   const dim3 gr(g.count), b(kWGThreads);
-  if (mode == 2)
+  if (mode == 4)
+    hipLaunchKernelGGL((k_ef_p<R, 4>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
+  else if (mode == 3)
+    hipLaunchKernelGGL((k_ef_p<R, 3>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
+  else if (mode == 2)
     hipLaunchKernelGGL((k_ef_p<R, 2>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
   else if (mode == 1)
     hipLaunchKernelGGL((k_ef_p<R, 1>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
@@ -458,15 +496,24 @@ static hipError_t launch_mtp_r(const LaunchCtx& c, const GridRange& g, const flo
 
 template <int R>
 static hipError_t launch_recon_r(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
-                                 bool residual) {
+                                 bool residual, const SgdArgs& sg) {
   if (c.wg_rows == 0) return hipSuccess;
   const dim3 g(c.wg_rows), b(kWGThreads);
-  if (residual && Mhat)
-    hipLaunchKernelGGL((k_recon<R, true, true, true>), g, b, 0, c.stream, c.mats, c.rows_map, E, Q, Ph, Mhat);
-  else if (residual)
-    hipLaunchKernelGGL((k_recon<R, true, true, false>), g, b, 0, c.stream, c.mats, c.rows_map, E, Q, Ph, Mhat);
-  else
-    hipLaunchKernelGGL((k_recon<R, false, false, true>), g, b, 0, c.stream, c.mats, c.rows_map, E, Q, Ph, Mhat);
+  const bool mh = Mhat != nullptr, sgd = sg.x != nullptr;
+#define PSGD_RECON(RS, MH, SG)                                                                                  \
+  hipLaunchKernelGGL((k_recon<R, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rows_map, E, Q, Ph, Mhat, sg)
+  if (residual) {
+    if (mh && sgd) PSGD_RECON(true, true, true);
+    else if (mh) PSGD_RECON(true, true, false);
+    else if (sgd) PSGD_RECON(true, false, true);
+    else PSGD_RECON(true, false, false);
+  } else {
+    if (mh && sgd) PSGD_RECON(false, true, true);
+    else if (mh) PSGD_RECON(false, true, false);
+    else if (sgd) PSGD_RECON(false, false, true);
+    else return hipSuccess;
+  }
+#undef PSGD_RECON
   return hipGetLastError();
 }
 
@@ -500,8 +547,9 @@ hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q) {
   return hipGetLastError();
 }
 
-hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat, bool residual) {
-  PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual));
+hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat, bool residual,
+                        const SgdArgs& sg) {
+  PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual, sg));
 }
 
 hipError_t launch_pass_pack(const LaunchCtx& c, const float* G, float* U, float beta, float* Pbuf) {
@@ -515,9 +563,14 @@ hipError_t launch_pass_pack(const LaunchCtx& c, const float* G, float* U, float 
   return hipGetLastError();
 }
 
-hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out) {
-  if (c.wg_pass == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pass_unpack, dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, Pbuf, out);
+hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out, const SgdArgs& sg) {
+  if (c.wg_pass == 0 || (!out && !sg.x)) return hipSuccess;
+  if (sg.x)
+    hipLaunchKernelGGL((k_pass_unpack<true>), dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, Pbuf, out,
+                       sg);
+  else
+    hipLaunchKernelGGL((k_pass_unpack<false>), dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, Pbuf, out,
+                       sg);
   return hipGetLastError();
 }
 

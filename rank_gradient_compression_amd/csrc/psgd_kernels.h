@@ -36,6 +36,15 @@ struct LaunchCtx {
   float* rscr;    // refresh scratch
 };
 
+// Fused post-compression momentum SGD (x = parameters, m = momentum buffer,
+// flat plan layout); x == nullptr disables it.
+struct SgdArgs {
+  float* x;
+  float* m;
+  float lr;
+  float mu;
+};
+
 // A contiguous range of workgroups of one of the plan's grids (the whole grid
 // for the grouped launches, one matrix's workgroups inside the refresh).
 struct GridRange {
@@ -45,14 +54,16 @@ struct GridRange {
 
 // ---- ranks up to kValuMaxRank (vector ALU kernels)
 // mode 0: P = M Q with M read from E; 1: M = G + E stored over E; 2: also
-// u = beta u + G first.  p_fixed >= 0 replaces the plan's P offset.
+// u = beta u + G first (M = u + E); 3: M = G; 4: u = beta u + G, M = u
+// (3 and 4: no error feedback).  p_fixed >= 0 replaces the plan's P offset.
 hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
                        float beta, const float* Q, float* P, int64_t p_fixed);
 hipError_t launch_mtp(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,
                       float* Q);
-// residual = true: E <- M - P_hat Q^T (M read from E), M_hat written if non-null.
-// residual = false: Mhat <- P_hat Q^T only (decompression).
-hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat, bool residual);
+// residual = true: E <- M - P_hat Q^T (M read from E); residual = false:
+// decompression only.  M_hat written if non-null; fused SGD if sg.x.
+hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat, bool residual,
+                        const SgdArgs& sg);
 
 // ---- ranks above kValuMaxRank (matrix-core kernels)
 hipError_t launch_mfma_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
@@ -61,7 +72,7 @@ hipError_t launch_psum(const LaunchCtx& c, const GridRange& g, float* P, int64_t
 hipError_t launch_mfma_qt(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,
                           float* Q);
 hipError_t launch_mfma_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
-                             bool residual);
+                             bool residual, const SgdArgs& sg);
 // With a map: descriptors first + [0, count) over a grouped Gram grid of
 // nblocks workgroups (map gives the matrix of each workgroup).  Without: the
 // single descriptor `first` with nblocks Gram blocks.
@@ -71,7 +82,7 @@ hipError_t launch_gram_orth(const LaunchCtx& c, int first, int count, const int3
 // ---- shared
 hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q);
 hipError_t launch_pass_pack(const LaunchCtx& c, const float* G, float* U, float beta, float* Pbuf);
-hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out);
+hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out, const SgdArgs& sg);
 hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);
 
 }  // namespace psgd

@@ -97,11 +97,18 @@ class PowerSGD:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
 
     def compress(self, mhat: bool = False, hook=None, mhat_buf: Optional[torch.Tensor] = None,
-                 refresh_iters: int = 0) -> None:
+                 refresh_iters: int = 0, power_iters: int = 0, error_feedback: bool = True,
+                 params: Optional[torch.Tensor] = None, sgd_buf: Optional[torch.Tensor] = None, sgd_lr: float = 0.0,
+                 sgd_momentum: float = 0.0) -> None:
         out = mhat_buf if mhat_buf is not None else (self.mhat if mhat else None)
+        opts = None
+        if refresh_iters or power_iters or not error_feedback or params is not None:
+            opts = B.step_opts(power_iters, refresh_iters, 0 if error_feedback else B.PSGD_STEP_NO_ERROR_FEEDBACK,
+                               sgd_lr, sgd_momentum, params.data_ptr() if params is not None else 0,
+                               sgd_buf.data_ptr() if sgd_buf is not None else 0)
         B.psgd_compress(self.plan, self.grads.data_ptr(), self.err.data_ptr(),
                         self.mom.data_ptr() if self.mom is not None else 0, self.q.data_ptr(), self.p.data_ptr(),
-                        out.data_ptr() if out is not None else 0, refresh_iters, hook, self.workspace.data_ptr(),
+                        out.data_ptr() if out is not None else 0, opts, hook, self.workspace.data_ptr(),
                         self.ws_bytes, self._stream())
 
     def decompress(self, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -160,7 +160,8 @@ def _compress(plan, **kw):
     a = dict(grads=FAKE, err=FAKE, mom=0, q=FAKE, pbuf=FAKE, mhat=0, hook=None, workspace=FAKE * 2,
              workspace_bytes=1 << 40)
     a.update(kw)
-    R.psgd_compress(plan, a["grads"], a["err"], a["mom"], a["q"], a["pbuf"], a["mhat"], a.get("refresh", 0), a["hook"],
+    opts = a.get("opts")
+    R.psgd_compress(plan, a["grads"], a["err"], a["mom"], a["q"], a["pbuf"], a["mhat"], opts, a["hook"],
                     a["workspace"], a["workspace_bytes"], 0)
 
 
@@ -176,7 +177,12 @@ def _compress(plan, **kw):
     (dict(workspace=0), B.PSGD_ERR_WORKSPACE),
     (dict(workspace=FAKE + 64), B.PSGD_ERR_WORKSPACE),
     (dict(workspace_bytes=16), B.PSGD_ERR_WORKSPACE),
-    (dict(refresh=-1), B.PSGD_ERR_INVALID_ARG),
+    (dict(opts=B.step_opts(refresh_iters=-1)), B.PSGD_ERR_INVALID_ARG),
+    (dict(opts=B.step_opts(power_iters=-2)), B.PSGD_ERR_INVALID_ARG),
+    (dict(opts=B.step_opts(flags=4)), B.PSGD_ERR_INVALID_ARG),
+    (dict(opts=B.step_opts(params=FAKE * 4)), B.PSGD_ERR_INVALID_ARG),            # params without sgd_buf
+    (dict(opts=B.step_opts(params=FAKE * 4, sgd_buf=FAKE * 4)), B.PSGD_ERR_INVALID_ARG),  # aliasing
+    (dict(opts=B.step_opts(params=FAKE * 4 + 8, sgd_buf=FAKE * 8)), B.PSGD_ERR_INVALID_ARG),  # misaligned
 ])
 def test_compress_argument_errors(kw, status):
     p = R.psgd_plan_create([64, 9], [48, 1], 2)

@@ -118,3 +118,61 @@ def test_powersgd_plus_step(rank):
         torch.cuda.synchronize()
         res = oracle.step_set(oplan, grads, ost, refresh_iters=it)
         compare_set(ps, oplan, res, ost, tag=f"powersgd+ r={rank} step {t}")
+
+
+# ------------------------------------------------- step options on the GPU
+
+def _options_case(shapes, rank, seed, steps, beta=None, power_iters=1, error_feedback=True, sgd=False, tag=""):
+    from gpu_util import compare_set
+    tensors = [(str(i), s) for i, s in enumerate(shapes)]
+    wl = W.ModelSetWorkload(tensors, "plain", seed=seed)
+    ps = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta)
+    oplan = oracle.Plan(shapes, rank)
+    q0 = [wl.q0(i, rank) if oplan.kinds[i] == oracle.KIND_COMPRESSED else None for i in range(len(shapes))]
+    ost = oracle.init_state(oplan, q0, momentum=beta is not None)
+    for i in ps.compressed():
+        ps.set_q(i, q0[i])
+    lr, mu = 0.05, 0.9
+    params = torch.zeros_like(ps.grads)
+    sbuf = torch.zeros_like(ps.grads)
+    gx = np.random.default_rng(seed + 1000)
+    xo, mo = [], []
+    for i in range(len(shapes)):
+        x0 = gx.standard_normal(oplan.views[i] if len(shapes[i]) >= 2 else shapes[i]).astype(np.float32)
+        ps.view(params, i).copy_(torch.from_numpy(x0).to(DEV))
+        xo.append(x0.astype(np.float64))
+        mo.append(np.zeros_like(xo[-1]))
+    for t in range(1, steps + 1):
+        grads = [wl.grad(i, t) for i in range(len(shapes))]
+        for i, g in enumerate(grads):
+            ps.view(ps.grads, i).copy_(torch.from_numpy(g).to(DEV))
+        say(f"[{tag}] step {t}")
+        ps.compress(mhat=True, power_iters=power_iters, error_feedback=error_feedback,
+                    params=params if sgd else None, sgd_buf=sbuf if sgd else None, sgd_lr=lr, sgd_momentum=mu)
+        torch.cuda.synchronize()
+        res = oracle.step_set(oplan, grads, ost, beta=beta or 0.0, power_iters=power_iters,
+                              error_feedback=error_feedback)
+        compare_set(ps, oplan, res, ost, tag=f"{tag} step {t}")
+        if sgd:
+            for i in range(len(shapes)):
+                D = np.asarray(res.M_hat[i]).reshape(xo[i].shape)
+                xo[i], mo[i] = oracle.sgd_momentum_step(xo[i], mo[i], D, lr, mu)
+                assert rel(cpu(ps.view(params, i)), xo[i]) <= REL_TOL, (tag, i, "params")
+                assert rel(cpu(ps.view(sbuf, i)), mo[i]) <= REL_TOL, (tag, i, "sgd momentum")
+
+
+@pytest.mark.parametrize("rank", [3, 16])
+def test_power_iterations(rank):
+    _options_case([(300, 650), (257, 1024), (33, 27), (7,)], rank, 70 + rank, 2, power_iters=3,
+                  tag=f"power x3 r={rank}")
+
+
+@pytest.mark.parametrize("rank,beta", [(4, None), (4, 0.9), (32, 0.9)])
+def test_no_error_feedback(rank, beta):
+    _options_case([(300, 650), (400, 512), (9,)], rank, 80 + rank, 2, beta=beta, error_feedback=False,
+                  tag=f"no-EF r={rank} beta={beta}")
+
+
+@pytest.mark.parametrize("rank", [2, 5, 16, 64])
+def test_fused_post_compression_sgd(rank):
+    _options_case([(300, 650), (500, 1024), (2, 2), (11,)], rank, 90 + rank, 3, sgd=True, tag=f"sgd r={rank}")

@@ -456,8 +456,8 @@ def test_planted_mistakes_are_caught(monkeypatch):
     st = oracle.init_state(plan, [wl.Q0])
     orig = O.compress_matrix
 
-    def no_ef(Mx, Qw, hp=None, hq=None):
-        return orig(Mx - st.E[0], Qw, hp, hq)
+    def no_ef(Mx, Qw, hp=None, hq=None, power_iters=1):
+        return orig(Mx - st.E[0], Qw, hp, hq, power_iters=power_iters)
 
     monkeypatch.setattr(O, "compress_matrix", no_ef)
     acc = np.zeros((256, 128))
@@ -467,3 +467,77 @@ def test_planted_mistakes_are_caught(monkeypatch):
         acc += res.M_hat[0]
         gsum += wl.grads[t]
     assert np.linalg.norm(acc + st.E[0] - gsum) > 1e-3 * np.linalg.norm(gsum)
+
+
+# ------------------------------------------- power iterations, ablations, SGD
+
+def test_power_iterations_equal_repeated_single_iterations():
+    # k iterations in one step = k warm-started single iterations on the same
+    # M with the error memory reset (reading R8).
+    g = np.random.default_rng(61)
+    M = rand(g, 80, 60)
+    Q = rand(g, 60, 3)
+    multi = oracle.compress_matrix(M, Q, power_iters=4)
+    q = Q
+    for _ in range(4):
+        single = oracle.compress_matrix(M, q)
+        q = single.Q
+    assert np.abs(multi.Q - single.Q).max() <= 1e-12
+    assert np.abs(multi.P_hat - single.P_hat).max() <= 1e-12
+    assert np.abs(multi.E - single.E).max() <= 1e-12
+
+
+def _approx_error(kind, iters, seed, steps=30, m=256, n=128, r=2):
+    g = np.random.default_rng(seed)
+    U = W.orthonormal(g, m, 16)
+    V = W.orthonormal(g, n, 16)
+    S = (U / np.arange(1, 17)) @ V.T
+    Q = g.standard_normal((n, r))
+    errs = []
+    for _ in range(steps):
+        M = S + 0.01 * g.standard_normal((m, n))
+        if kind == "cold":
+            Q = g.standard_normal((n, r))
+        res = oracle.compress_matrix(M, Q, power_iters=iters)
+        Q = res.Q
+        errs.append(np.linalg.norm(M - res.M_hat) / np.linalg.norm(M))
+    return float(np.mean(errs[5:]))
+
+
+def test_warm_start_matches_several_cold_iterations():
+    # Glossary entry "PowerSGD", temporal-coherence paragraph: one warm-started
+    # power iteration matches the accuracy of 2-4 iterations from scratch.
+    # Fixed rank-16 signal (sigma ~ 1/j) plus fresh noise, rank 2, no error
+    # feedback (approximation quality alone).
+    for seed in range(3):
+        warm1 = _approx_error("warm", 1, seed)
+        cold1, cold2, cold4 = (_approx_error("cold", k, seed) for k in (1, 2, 4))
+        assert warm1 < cold1 and warm1 <= cold2
+        assert warm1 <= cold4 * 1.001
+
+
+def test_no_error_feedback_ignores_memory():
+    g = np.random.default_rng(62)
+    plan = oracle.Plan([(40, 30)], 2)
+    q0 = rand(g, 30, 2)
+    st = oracle.init_state(plan, [q0])
+    st.E[0] = rand(g, 40, 30)  # would be added with error feedback on
+    G = rand(g, 40, 30)
+    res = oracle.step_set(plan, [G], st, error_feedback=False)
+    ref = oracle.compress_matrix(G, q0)
+    assert np.abs(res.M_hat[0] - ref.M_hat).max() <= 1e-13
+    assert np.abs(st.E[0] - ref.E).max() <= 1e-13
+
+
+def test_sgd_momentum_closed_form():
+    # Constant update D: m_t = D (1 - mu^t)/(1 - mu), x_t = x_0 - lr sum_t m_t.
+    D = np.linspace(-1.0, 1.0, 7)
+    x = np.ones(7)
+    m = np.zeros(7)
+    lr, mu = 0.1, 0.9
+    xs = x.copy()
+    for t in range(1, 6):
+        x, m = oracle.sgd_momentum_step(x, m, D, lr, mu)
+        np.testing.assert_allclose(m, D * (1 - mu ** t) / (1 - mu), rtol=1e-14)
+        xs = xs - lr * D * (1 - mu ** t) / (1 - mu)
+        np.testing.assert_allclose(x, xs, rtol=1e-13, atol=1e-15)
