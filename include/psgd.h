@@ -68,8 +68,11 @@ typedef enum psgd_status {
 #define PSGD_KIND_COMPRESSED 2 /* matrix compressed to rank r                  */
 
 /* Plan flags. */
-#define PSGD_FLAG_MOMENTUM 1u /* compress u <- beta*u + G instead of G ([GLOSS],
-                                 momentum paragraph); needs the `mom` buffer  */
+#define PSGD_FLAG_MOMENTUM 1u   /* compress u <- beta*u + G instead of G ([GLOSS],
+                                   momentum paragraph); needs the `mom` buffer   */
+#define PSGD_FLAG_GRADS_BF16 2u /* the gradient buffer holds bfloat16 values
+                                   (mixed-precision training); everything else,
+                                   including the error memory, stays fp32      */
 
 /* Pipeline stages, for psgd_timing_read. */
 #define PSGD_STAGE_EF_P 0      /* EF-add (+momentum) and P = M Q            */
@@ -152,7 +155,7 @@ typedef struct psgd_plan_info {
  *              not overlap; any alignment is accepted (unaligned rows use
  *              narrower loads).
  *   rank       r, 1 <= r <= PSGD_MAX_RANK.
- *   flags      0 or PSGD_FLAG_MOMENTUM.
+ *   flags      PSGD_FLAG_MOMENTUM and / or PSGD_FLAG_GRADS_BF16, or 0.
  *   beta       momentum coefficient (used only with PSGD_FLAG_MOMENTUM).
  *   out        receives the plan; release it with psgd_plan_destroy.
  *
@@ -205,7 +208,8 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  * psgd_compress -- one PowerSGD step over the whole set ([N152] Method; error
  * feedback per [GLOSS] and [N152] Concepts, "Error feedback").
  *
- *   grads  flat, read-only: the stochastic gradients G.
+ *   grads  flat, read-only: the stochastic gradients G, fp32 (or bfloat16
+ *          with PSGD_FLAG_GRADS_BF16, widened exactly to fp32 on load).
  *   err    flat, in/out: error memory E of compressed tensors (zero at the
  *          first step).  On return: the new residual M - P_hat Q^T.  While the
  *          call runs it holds M = X + E_old; if the call fails after the first
@@ -221,7 +225,8 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  *   mhat   nullable flat buffer: if given, receives the decompressed gradient
  *          P_hat Q^T for compressed tensors and the aggregated values of the
  *          pass-through tensors (a fused psgd_decompress).  It may alias
- *          `grads` (then G is overwritten by the update) but no other buffer.
+ *          fp32 `grads` (then G is overwritten by the update) but no other
+ *          buffer.
  *   opts   nullable step options (psgd_step_opts_t): power iterations,
  *          PowerSGD+ refresh, the no-error-feedback ablation, fused
  *          post-compression momentum SGD.
@@ -235,7 +240,7 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  * PSGD_ERR_HOOK if a hook
  * returns non-zero (no later stage is enqueued); PSGD_ERR_HIP.
  */
-psgd_status_t psgd_compress(psgd_plan_t plan, const float* grads, float* err, float* mom, float* q,
+psgd_status_t psgd_compress(psgd_plan_t plan, const void* grads, float* err, float* mom, float* q,
                             float* p, float* mhat, const psgd_step_opts_t* opts, psgd_reduce_fn hook,
                             void* user, void* workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -28,6 +28,7 @@ PSGD_KIND_VECTOR = 0
 PSGD_KIND_PASSTHRU = 1
 PSGD_KIND_COMPRESSED = 2
 PSGD_FLAG_MOMENTUM = 1
+PSGD_FLAG_GRADS_BF16 = 2
 
 PSGD_STAGE_EF_P = 0
 PSGD_STAGE_GS = 1

@@ -82,6 +82,7 @@ static LaunchCtx make_ctx(const psgd_plan* p, void* ws, hipStream_t s) {
   c.rank = p->rank;
   c.rank_pad = h.rank_pad;
   c.mfma = h.mfma != 0;
+  c.g_bf16 = (p->flags & PSGD_FLAG_GRADS_BF16) != 0;
   c.nmat = h.nmat;
   c.npass = h.npass;
   c.wg_rows = h.wg_rows;
@@ -120,7 +121,7 @@ static GridRange mat_range(const psgd_plan* p, size_t k, int32_t MatDesc::*first
 // P = M Q for the grid range g (mode as in launch_ef_p), into P at the plan's
 // offsets (p_fixed < 0) or at p_fixed, column-split partials summed.
 static hipError_t stage_mq(const psgd_plan* p, const LaunchCtx& c, const GridRange& g, const GridRange& gp, int mode,
-                           const float* G, float* E, float* U, const float* Q, float* P, int64_t p_fixed) {
+                           const void* G, float* E, float* U, const float* Q, float* P, int64_t p_fixed) {
   if (!c.mfma) return launch_ef_p(c, g, mode, G, E, U, p->beta, Q, P, p_fixed);
   hipError_t e = launch_mfma_p(c, g, mode, G, E, U, p->beta, Q, P, p_fixed);
   if (e != hipSuccess) return e;
@@ -209,7 +210,7 @@ extern "C" psgd_status_t psgd_workspace_init(psgd_plan_t p, void* ws, size_t byt
   return PSGD_OK;
 }
 
-extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const float* grads, float* err, float* mom, float* q, float* pbuf,
+extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* err, float* mom, float* q, float* pbuf,
                                        float* mhat, const psgd_step_opts_t* opts, psgd_reduce_fn hook, void* user,
                                        void* ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
@@ -238,6 +239,10 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const float* grads, float*
   }
   if (mhat && (mhat == err || mhat == mom)) {
     set_error("psgd_compress: mhat may alias grads only");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (mhat && (p->flags & PSGD_FLAG_GRADS_BF16) && (const void*)mhat == grads) {
+    set_error("psgd_compress: mhat (fp32) cannot alias bfloat16 gradients");
     return PSGD_ERR_INVALID_ARG;
   }
   psgd_step_opts_t o{};

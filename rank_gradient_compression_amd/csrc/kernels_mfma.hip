@@ -79,6 +79,24 @@ __device__ __forceinline__ float4 ldq(const float* rowp, int col, bool ok, int c
   }
 }
 
+// Four bfloat16 gradients widened to fp32 (same masking as ldq).
+template <bool VEC4>
+__device__ __forceinline__ float4 ldq_bf16(const uint16_t* rowp, int col, bool ok, int col_safe, int n) {
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (VEC4) {
+    const uint2 t = *reinterpret_cast<const uint2*>(rowp + (ok ? col : col_safe));
+    if (ok)
+      r = make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u), __uint_as_float(t.y << 16),
+                      __uint_as_float(t.y & 0xffff0000u));
+  } else if (ok) {
+    if (col < n) r.x = __uint_as_float((uint32_t)rowp[col] << 16);
+    if (col + 1 < n) r.y = __uint_as_float((uint32_t)rowp[col + 1] << 16);
+    if (col + 2 < n) r.z = __uint_as_float((uint32_t)rowp[col + 2] << 16);
+    if (col + 3 < n) r.w = __uint_as_float((uint32_t)rowp[col + 3] << 16);
+  }
+  return r;
+}
+
 template <bool VEC4>
 __device__ __forceinline__ void stq(float* rowp, int col, int n, float4 v) {
   st4(rowp, col, n, VEC4, v);
@@ -96,8 +114,8 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 // modes 3 and 4 without error feedback, M still stored over E)
 // ---------------------------------------------------------------------------
 
-template <int RP, int MODE, bool VEC4>
-__device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, const float* __restrict__ G,
+template <int RP, int MODE, bool VEC4, bool GBF16>
+__device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
                                             float* __restrict__ E, float* __restrict__ U, float beta,
                                             const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed,
                                             float* __restrict__ ppart, float* Qs) {
@@ -131,7 +149,11 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
         x[qq] = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
       } else {
         constexpr bool LOAD_E = MODE <= 2;
-        const float4 g = ldq<VEC4>(G + roff, col, col_ok, c_begin, n);
+        float4 g;
+        if constexpr (GBF16)
+          g = ldq_bf16<VEC4>(static_cast<const uint16_t*>(G) + roff, col, col_ok, c_begin, n);
+        else
+          g = ldq<VEC4>(static_cast<const float*>(G) + roff, col, col_ok, c_begin, n);
         const float4 e = LOAD_E ? ldq<VEC4>(E + roff, col, col_ok, c_begin, n) : make_float4(0.f, 0.f, 0.f, 0.f);
         float4 s;
         if constexpr (MODE == 2 || MODE == 4) {
@@ -191,9 +213,9 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
   }
 }
 
-template <int RP, int MODE>
+template <int RP, int MODE, bool GBF16>
 __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
-                                                int wg_base, int r, const float* __restrict__ G,
+                                                int wg_base, int r, const void* __restrict__ G,
                                                 float* __restrict__ E, float* __restrict__ U, float beta,
                                                 const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed,
                                                 float* __restrict__ ppart) {
@@ -204,9 +226,9 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
   if (d.vec == 4)
-    mfma_p_body<RP, MODE, true>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs);
+    mfma_p_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs);
   else
-    mfma_p_body<RP, MODE, false>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs);
+    mfma_p_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs);
 }
 
 // Fixed-order sum of the column-split partials of pass 1.
@@ -618,30 +640,37 @@ __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restric
     default: return hipErrorInvalidValue;             \
   }
 
-template <int RP>
-static hipError_t mfma_p_rp(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
-                            float beta, const float* Q, float* P, int64_t p_fixed) {
-  if (g.count == 0) return hipSuccess;
+template <int RP, bool GBF16>
+static hipError_t mfma_p_rpg(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
+                             float beta, const float* Q, float* P, int64_t p_fixed) {
   const dim3 gr(g.count), b(256);
-  if (mode == 0)
-    hipLaunchKernelGGL((k_mfma_p<RP, 0>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
-                       P, p_fixed, c.ppart);
-  else if (mode == 1)
-    hipLaunchKernelGGL((k_mfma_p<RP, 1>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
-                       P, p_fixed, c.ppart);
-  else if (mode == 2)
-    hipLaunchKernelGGL((k_mfma_p<RP, 2>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
-                       P, p_fixed, c.ppart);
-  else if (mode == 3)
-    hipLaunchKernelGGL((k_mfma_p<RP, 3>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
-                       P, p_fixed, c.ppart);
-  else
-    hipLaunchKernelGGL((k_mfma_p<RP, 4>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, beta, Q,
-                       P, p_fixed, c.ppart);
+#define PSGD_MP(MD)                                                                                          \
+  hipLaunchKernelGGL((k_mfma_p<RP, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, \
+                     beta, Q, P, p_fixed, c.ppart)
+  switch (mode) {
+    case 1: PSGD_MP(1); break;
+    case 2: PSGD_MP(2); break;
+    case 3: PSGD_MP(3); break;
+    default: PSGD_MP(4); break;
+  }
+#undef PSGD_MP
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+template <int RP>
+static hipError_t mfma_p_rp(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
+                            float beta, const float* Q, float* P, int64_t p_fixed) {
+  if (g.count == 0) return hipSuccess;
+  if (mode == 0) {  // M read from E: no gradient involved
+    hipLaunchKernelGGL((k_mfma_p<RP, 0, false>), dim3(g.count), dim3(256), 0, c.stream, c.mats, c.rows_map, g.base,
+                       c.rank, G, E, U, beta, Q, P, p_fixed, c.ppart);
+    return hipGetLastError();
+  }
+  return c.g_bf16 ? mfma_p_rpg<RP, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)
+                  : mfma_p_rpg<RP, false>(c, g, mode, G, E, U, beta, Q, P, p_fixed);
+}
+
+hipError_t launch_mfma_p(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                          float beta, const float* Q, float* P, int64_t p_fixed) {
   PSGD_RP_SWITCH(c.rank_pad, mfma_p_rp<RPV>(c, g, mode, G, E, U, beta, Q, P, p_fixed));
 }

@@ -64,6 +64,7 @@ __device__ __forceinline__ void stv(float* p, const Vec<VEC>& a) {
 // store of M_hat shave about 2% off a step; a streaming store of E or M costs.
 typedef float v4f_nt __attribute__((ext_vector_type(4)));
 typedef float v2f_nt __attribute__((ext_vector_type(2)));
+typedef uint32_t v2u_nt __attribute__((ext_vector_type(2)));
 
 template <int VEC>
 __device__ __forceinline__ void stv_nt(float* p, const Vec<VEC>& a) {
@@ -91,6 +92,34 @@ __device__ __forceinline__ Vec<VEC> ldv_nt(const float* p) {
     r.v[0] = __builtin_nontemporal_load(p);
   }
   return r;
+}
+
+// Gradient loads: fp32, or bfloat16 widened exactly to fp32 (the upper 16
+// bits of the fp32 pattern).  Both are read once per step: streaming hint.
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+template <int VEC, bool BF16>
+__device__ __forceinline__ Vec<VEC> ldg(const void* G, int64_t idx) {
+  if constexpr (!BF16) {
+    return ldv_nt<VEC>(static_cast<const float*>(G) + idx);
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(G) + idx;
+    Vec<VEC> r;
+    if constexpr (VEC == 4) {
+      const v2u_nt t = __builtin_nontemporal_load(reinterpret_cast<const v2u_nt*>(p));
+      r.v[0] = bf16_to_f32(t[0] & 0xffffu);
+      r.v[1] = bf16_to_f32(t[0] >> 16);
+      r.v[2] = bf16_to_f32(t[1] & 0xffffu);
+      r.v[3] = bf16_to_f32(t[1] >> 16);
+    } else if constexpr (VEC == 2) {
+      const uint32_t t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+      r.v[0] = bf16_to_f32(t & 0xffffu);
+      r.v[1] = bf16_to_f32(t >> 16);
+    } else {
+      r.v[0] = bf16_to_f32(*p);
+    }
+    return r;
+  }
 }
 
 // Sum of NV per-lane values over the 64 lanes of a wavefront, transposed: on
@@ -135,8 +164,8 @@ constexpr int pow2_at_least(int x) {
 // MODE 0: M read from E (plain M Q); 1: M = G + E; 2: u = beta u + G,
 // M = u + E; 3: M = G (no error feedback); 4: u = beta u + G, M = u.  Modes
 // 1..4 store M over E.
-template <int R, int VEC, int MODE>
-__device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, const float* __restrict__ G,
+template <int R, int VEC, int MODE, bool GBF16>
+__device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, const void* __restrict__ G,
                                           float* __restrict__ E, float* __restrict__ U, float beta,
                                           const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed) {
   constexpr bool MOM = MODE == 2 || MODE == 4;
@@ -159,7 +188,7 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
       const int64_t idx = base + (int64_t)min(rr, nrows - 1) * n + j;
-      if constexpr (MODE != 0) g[rr] = ldv_nt<VEC>(G + idx);  // read once per step: streaming hint
+      if constexpr (MODE != 0) g[rr] = ldg<VEC, GBF16>(G, idx);
       if constexpr (LOAD_E) e[rr] = ldv<VEC>(E + idx);
     }
     Vec<VEC> u[kWaveRows];
@@ -206,10 +235,10 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
   }
 }
 
-template <int R, int MODE>
+template <int R, int MODE, bool GBF16>
 __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__ mats,
                                                      const int32_t* __restrict__ map, int wg_base,
-                                                     const float* __restrict__ G, float* __restrict__ E,
+                                                     const void* __restrict__ G, float* __restrict__ E,
                                                      float* __restrict__ U, float beta,
                                                      const float* __restrict__ Q, float* __restrict__ P,
                                                      int64_t p_fixed) {
@@ -219,11 +248,11 @@ __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__
   const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
   if (row0 >= d.m) return;
   if (d.vec == 4)
-    ef_p_wave<R, 4, MODE>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
+    ef_p_wave<R, 4, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
   else if (d.vec == 2)
-    ef_p_wave<R, 2, MODE>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
+    ef_p_wave<R, 2, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
   else
-    ef_p_wave<R, 1, MODE>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
+    ef_p_wave<R, 1, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
 }
 
 // ---------------------------------------------------------------------------
@@ -417,16 +446,20 @@ __global__ __launch_bounds__(kWGThreads) void k_recon(const MatDesc* __restrict_
 // Pass-through tensors
 // ---------------------------------------------------------------------------
 
-template <bool MOM>
+template <bool MOM, bool GBF16>
 __global__ __launch_bounds__(256) void k_pass_pack(const PassDesc* __restrict__ pass, const int32_t* __restrict__ map,
-                                                   const float* __restrict__ G, float* __restrict__ U, float beta,
+                                                   const void* __restrict__ G, float* __restrict__ U, float beta,
                                                    float* __restrict__ Pbuf) {
   const int wg = blockIdx.x;
   const PassDesc pd = pass[map[wg]];
   const int64_t c0 = (int64_t)(wg - pd.wg0) * kPassChunk;
   const int64_t c1 = c0 + kPassChunk < pd.len ? c0 + kPassChunk : pd.len;
   for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
-    float x = G[pd.off + i];
+    float x;
+    if constexpr (GBF16)
+      x = bf16_to_f32(static_cast<const uint16_t*>(G)[pd.off + i]);
+    else
+      x = static_cast<const float*>(G)[pd.off + i];
     if constexpr (MOM) {
       x = fmaf(beta, U[pd.off + i], x);
       U[pd.off + i] = x;
@@ -467,22 +500,34 @@ __global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, c
 // Host-side launchers
 // ---------------------------------------------------------------------------
 
+template <int R, bool GBF16>
+static hipError_t launch_ef_p_rg(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
+                                 float beta, const float* Q, float* P, int64_t p_fixed) {
+  const dim3 gr(g.count), b(kWGThreads);
+#define PSGD_EFP(MD)                                                                                            \
+  hipLaunchKernelGGL((k_ef_p<R, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, \
+                     p_fixed)
+  switch (mode) {
+    case 1: PSGD_EFP(1); break;
+    case 2: PSGD_EFP(2); break;
+    case 3: PSGD_EFP(3); break;
+    default: PSGD_EFP(4); break;
+  }
+#undef PSGD_EFP
+  return hipGetLastError();
+}
+
 template <int R>
-static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                                 float beta, const float* Q, float* P, int64_t p_fixed) {
   if (g.count == 0) return hipSuccess;
-  const dim3 gr(g.count), b(kWGThreads);
-  if (mode == 4)
-    hipLaunchKernelGGL((k_ef_p<R, 4>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
-  else if (mode == 3)
-    hipLaunchKernelGGL((k_ef_p<R, 3>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
-  else if (mode == 2)
-    hipLaunchKernelGGL((k_ef_p<R, 2>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
-  else if (mode == 1)
-    hipLaunchKernelGGL((k_ef_p<R, 1>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
-  else
-    hipLaunchKernelGGL((k_ef_p<R, 0>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed);
-  return hipGetLastError();
+  if (mode == 0) {  // P = M Q with M read from E: no gradient involved
+    hipLaunchKernelGGL((k_ef_p<R, 0, false>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map,
+                       g.base, G, E, U, beta, Q, P, p_fixed);
+    return hipGetLastError();
+  }
+  return c.g_bf16 ? launch_ef_p_rg<R, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)
+                  : launch_ef_p_rg<R, false>(c, g, mode, G, E, U, beta, Q, P, p_fixed);
 }
 
 template <int R>
@@ -530,7 +575,7 @@ static hipError_t launch_recon_r(const LaunchCtx& c, float* E, const float* Q, c
     default: return hipErrorInvalidValue;           \
   }
 
-hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                        float beta, const float* Q, float* P, int64_t p_fixed) {
   PSGD_RANK_SWITCH(c.rank, launch_ef_p_r<RR>(c, g, mode, G, E, U, beta, Q, P, p_fixed));
 }
@@ -552,14 +597,17 @@ hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const floa
   PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual, sg));
 }
 
-hipError_t launch_pass_pack(const LaunchCtx& c, const float* G, float* U, float beta, float* Pbuf) {
+hipError_t launch_pass_pack(const LaunchCtx& c, const void* G, float* U, float beta, float* Pbuf) {
   if (c.wg_pass == 0) return hipSuccess;
-  if (U)
-    hipLaunchKernelGGL((k_pass_pack<true>), dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, G, U, beta,
-                       Pbuf);
+  const dim3 g(c.wg_pass), b(256);
+  if (U && c.g_bf16)
+    hipLaunchKernelGGL((k_pass_pack<true, true>), g, b, 0, c.stream, c.pass, c.pass_map, G, U, beta, Pbuf);
+  else if (U)
+    hipLaunchKernelGGL((k_pass_pack<true, false>), g, b, 0, c.stream, c.pass, c.pass_map, G, U, beta, Pbuf);
+  else if (c.g_bf16)
+    hipLaunchKernelGGL((k_pass_pack<false, true>), g, b, 0, c.stream, c.pass, c.pass_map, G, U, beta, Pbuf);
   else
-    hipLaunchKernelGGL((k_pass_pack<false>), dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, G, U, beta,
-                       Pbuf);
+    hipLaunchKernelGGL((k_pass_pack<false, false>), g, b, 0, c.stream, c.pass, c.pass_map, G, U, beta, Pbuf);
   return hipGetLastError();
 }
 

@@ -79,8 +79,8 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     set_error("psgd_plan_create: rank %d above the supported maximum %d", rank, PSGD_MAX_RANK);
     return PSGD_ERR_UNSUPPORTED;
   }
-  if (flags & ~PSGD_FLAG_MOMENTUM) {
-    set_error("psgd_plan_create: unknown flag bits 0x%x", flags & ~PSGD_FLAG_MOMENTUM);
+  if (flags & ~(PSGD_FLAG_MOMENTUM | PSGD_FLAG_GRADS_BF16)) {
+    set_error("psgd_plan_create: unknown flag bits 0x%x", flags & ~(PSGD_FLAG_MOMENTUM | PSGD_FLAG_GRADS_BF16));
     return PSGD_ERR_UNSUPPORTED;
   }
   if ((flags & PSGD_FLAG_MOMENTUM) && !(beta == beta)) {

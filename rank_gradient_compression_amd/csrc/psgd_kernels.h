@@ -18,6 +18,7 @@ struct LaunchCtx {
   hipStream_t stream;
   int rank, rank_pad;
   bool mfma;
+  bool g_bf16;  // gradients stored as bfloat16
   int nmat, npass;
   int wg_rows, wg_mtp, wg_red, wg_pass, wg_pred, wg_gram, wg_gramq;
   const MatDesc* mats;
@@ -56,7 +57,7 @@ struct GridRange {
 // mode 0: P = M Q with M read from E; 1: M = G + E stored over E; 2: also
 // u = beta u + G first (M = u + E); 3: M = G; 4: u = beta u + G, M = u
 // (3 and 4: no error feedback).  p_fixed >= 0 replaces the plan's P offset.
-hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                        float beta, const float* Q, float* P, int64_t p_fixed);
 hipError_t launch_mtp(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,
                       float* Q);
@@ -66,7 +67,7 @@ hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const floa
                         const SgdArgs& sg);
 
 // ---- ranks above kValuMaxRank (matrix-core kernels)
-hipError_t launch_mfma_p(const LaunchCtx& c, const GridRange& g, int mode, const float* G, float* E, float* U,
+hipError_t launch_mfma_p(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                          float beta, const float* Q, float* P, int64_t p_fixed);
 hipError_t launch_psum(const LaunchCtx& c, const GridRange& g, float* P, int64_t p_fixed);
 hipError_t launch_mfma_qt(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,
@@ -81,7 +82,7 @@ hipError_t launch_gram_orth(const LaunchCtx& c, int first, int count, const int3
 
 // ---- shared
 hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q);
-hipError_t launch_pass_pack(const LaunchCtx& c, const float* G, float* U, float beta, float* Pbuf);
+hipError_t launch_pass_pack(const LaunchCtx& c, const void* G, float* U, float beta, float* Pbuf);
 hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out, const SgdArgs& sg);
 hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);
 

@@ -27,7 +27,8 @@ def matrix_view(shape: Sequence[int]) -> Tuple[int, int]:
 class PowerSGD:
     """A plan plus the flat buffers one worker owns for it.
 
-    grads  flat gradient buffer (write the gradients here, or pass your own)
+    grads  flat gradient buffer (write the gradients here, or pass your own);
+           float32, or bfloat16 with grads_dtype=torch.bfloat16
     err    error-feedback memory (zero-initialised)
     mom    momentum buffer (momentum variant only, zero-initialised)
     q      packed warm-start / output Q
@@ -36,11 +37,16 @@ class PowerSGD:
     """
 
     def __init__(self, shapes: Sequence[Sequence[int]], rank: int, device="cuda", momentum_beta: Optional[float] = None,
-                 offsets: Optional[Sequence[int]] = None, with_mhat: bool = True, grads: Optional[torch.Tensor] = None):
+                 offsets: Optional[Sequence[int]] = None, with_mhat: bool = True, grads: Optional[torch.Tensor] = None,
+                 grads_dtype: torch.dtype = torch.float32):
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.views = [matrix_view(s) for s in self.shapes]
         self.rank = int(rank)
+        if grads_dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("gradients must be float32 or bfloat16")
         flags = B.PSGD_FLAG_MOMENTUM if momentum_beta is not None else 0
+        if grads_dtype == torch.bfloat16:
+            flags |= B.PSGD_FLAG_GRADS_BF16
         self.plan = B.psgd_plan_create([v[0] for v in self.views],
                                        [v[1] if len(s) >= 2 else 1 for v, s in zip(self.views, self.shapes)],
                                        self.rank, flags, float(momentum_beta or 0.0), offsets)
@@ -49,8 +55,8 @@ class PowerSGD:
         self.device = torch.device(device)
         n = self.info["flat_elems"]
         f32 = dict(dtype=torch.float32, device=self.device)
-        self.grads = grads if grads is not None else torch.zeros(n, **f32)
-        assert self.grads.numel() >= n and self.grads.dtype == torch.float32
+        self.grads = grads if grads is not None else torch.zeros(n, dtype=grads_dtype, device=self.device)
+        assert self.grads.numel() >= n and self.grads.dtype == grads_dtype
         self.err = torch.zeros(n, **f32)
         self.mom = torch.zeros(n, **f32) if momentum_beta is not None else None
         self.q = torch.zeros(max(1, self.info["q_elems"]), **f32)

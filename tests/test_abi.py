@@ -196,6 +196,22 @@ def test_compress_argument_errors(kw, status):
         R.psgd_plan_destroy(p)
 
 
+def test_bf16_gradient_plan():
+    # bfloat16 gradients: accepted alone or with momentum; the fp32 M_hat may
+    # not be written over them.
+    for flags in (B.PSGD_FLAG_GRADS_BF16, B.PSGD_FLAG_GRADS_BF16 | B.PSGD_FLAG_MOMENTUM):
+        p = R.psgd_plan_create([64], [48], 2, flags, 0.9)
+        assert R.psgd_plan_get_info(p)["flags"] == flags
+        R.psgd_plan_destroy(p)
+    p = R.psgd_plan_create([64, 9], [48, 1], 2, B.PSGD_FLAG_GRADS_BF16)
+    try:
+        with pytest.raises(B.PsgdError) as e:
+            _compress(p, mhat=FAKE * 4, grads=FAKE * 4)
+        assert e.value.status == B.PSGD_ERR_INVALID_ARG and "bfloat16" in str(e.value)
+    finally:
+        R.psgd_plan_destroy(p)
+
+
 def test_momentum_plan_requires_mom():
     p = R.psgd_plan_create([64], [48], 2, B.PSGD_FLAG_MOMENTUM, 0.9)
     try:

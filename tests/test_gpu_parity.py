@@ -21,10 +21,16 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def run_set_parity(tensors, rank, steps, grad_fn, q0_fn, beta=None, tag="", check_every=1, offsets=None):
+def run_set_parity(tensors, rank, steps, grad_fn, q0_fn, beta=None, tag="", check_every=1, offsets=None,
+                   grads_dtype=None, power_iters=0, error_feedback=True):
+    """Run `steps` compress calls on the GPU and the oracle's step on the same
+    inputs, comparing every `check_every` steps.  With grads_dtype=bfloat16 the
+    gradients are rounded to bfloat16 on the host first and the oracle gets
+    the rounded values, widened exactly."""
     shapes = [s for _, s in tensors]
     say(f"[{tag}] plan: {len(shapes)} tensors, rank {rank}, {steps} steps")
-    ps = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta, offsets=offsets)
+    gdt = grads_dtype or torch.float32
+    ps = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta, offsets=offsets, grads_dtype=gdt)
     oplan = oracle.Plan(shapes, rank)
     q0 = [q0_fn(i) if oplan.kinds[i] == oracle.KIND_COMPRESSED else None for i in range(len(shapes))]
     ost = oracle.init_state(oplan, q0, momentum=beta is not None)
@@ -33,12 +39,18 @@ def run_set_parity(tensors, rank, steps, grad_fn, q0_fn, beta=None, tag="", chec
     worst = {}
     for t in range(1, steps + 1):
         grads = [grad_fn(i, t) for i in range(len(shapes))]
-        for i, g in enumerate(grads):
-            ps.view(ps.grads, i).copy_(torch.from_numpy(np.ascontiguousarray(g)).to(DEV))
+        if gdt != torch.float32:
+            host = [torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to(gdt) for g in grads]
+            grads = [h.double().numpy() for h in host]
+        else:
+            host = [torch.from_numpy(np.ascontiguousarray(g)) for g in grads]
+        for i, h in enumerate(host):
+            ps.view(ps.grads, i).copy_(h.to(DEV))
         say(f"[{tag}] step {t}: compress")
-        ps.compress(mhat=True)
+        ps.compress(mhat=True, power_iters=power_iters, error_feedback=error_feedback)
         torch.cuda.synchronize()
-        ores = oracle.step_set(oplan, grads, ost, beta=beta or 0.0)
+        ores = oracle.step_set(oplan, grads, ost, beta=beta or 0.0, power_iters=max(1, power_iters),
+                               error_feedback=error_feedback)
         if t % check_every == 0 or t == steps:
             w = compare_set(ps, oplan, ores, ost, tag=f"{tag} step {t}")
             for k, v in w.items():
