@@ -39,7 +39,11 @@ design notes of the repository):
       P = M Q, aggregate, P_hat = GS(P), Q = M^T P_hat, aggregate, repeated,
       each iteration starting from the previous one's Q.
   R9  post-compression momentum ([N152] Concepts): heavy-ball SGD on the
-      decompressed, aggregated update D: m <- mu m + D, x <- x - lr m.
+      decompressed, aggregated update D: m <- mu m + D, x <- x - lr m; with
+      the Nesterov option of standard SGD ([GLOSS], momentum paragraph: the
+      scheme works with the usual optimizers), x <- x - lr (D + mu m).
+  R10 the first Q, and a cold start's fresh Q every step, is i.i.d. N(0, 1)
+      from a seeded counter-based generator (module philox).
 """
 from __future__ import annotations
 
@@ -191,11 +195,13 @@ def refresh(M: np.ndarray, Q: np.ndarray, iters: int) -> np.ndarray:
     return Q
 
 
-def sgd_momentum_step(x: np.ndarray, m: np.ndarray, D: np.ndarray, lr: float, mu: float):
-    """Post-compression momentum ([N152] Concepts; reading R9): heavy-ball
-    SGD with the decompressed update D.  Returns (x, m)."""
-    m = mu * np.asarray(m, np.float64) + np.asarray(D, np.float64)
-    return np.asarray(x, np.float64) - lr * m, m
+def sgd_momentum_step(x: np.ndarray, m: np.ndarray, D: np.ndarray, lr: float, mu: float, nesterov: bool = False):
+    """Post-compression momentum ([N152] Concepts; reading R9): SGD with
+    momentum on the decompressed update D.  Returns (x, m)."""
+    D = np.asarray(D, np.float64)
+    m = mu * np.asarray(m, np.float64) + D
+    direction = D + mu * m if nesterov else m
+    return np.asarray(x, np.float64) - lr * direction, m
 
 
 def momentum_input(u: np.ndarray, G: np.ndarray, beta: float) -> np.ndarray:

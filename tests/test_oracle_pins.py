@@ -541,3 +541,98 @@ def test_sgd_momentum_closed_form():
         np.testing.assert_allclose(m, D * (1 - mu ** t) / (1 - mu), rtol=1e-14)
         xs = xs - lr * D * (1 - mu ** t) / (1 - mu)
         np.testing.assert_allclose(x, xs, rtol=1e-13, atol=1e-15)
+
+
+def test_sgd_nesterov_closed_form():
+    # Constant D: the Nesterov direction D + mu m_t equals D (1 - mu^(t+1))/(1 - mu).
+    D = np.linspace(-1.0, 1.0, 7)
+    x = np.ones(7)
+    m = np.zeros(7)
+    lr, mu = 0.1, 0.9
+    xs = x.copy()
+    for t in range(1, 6):
+        x, m = oracle.sgd_momentum_step(x, m, D, lr, mu, nesterov=True)
+        np.testing.assert_allclose(m, D * (1 - mu ** t) / (1 - mu), rtol=1e-14)
+        xs = xs - lr * D * (1 - mu ** (t + 1)) / (1 - mu)
+        np.testing.assert_allclose(x, xs, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("nesterov", [False, True])
+def test_sgd_matches_torch_optimizer(nesterov):
+    # Library routine: torch.optim.SGD (dampening 0) on the CPU in float64,
+    # fed the same sequence of updates.
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(17)
+    x0 = g.standard_normal(11)
+    lr, mu = 0.05, 0.8
+    p = torch.nn.Parameter(torch.from_numpy(x0.copy()))
+    opt = torch.optim.SGD([p], lr=lr, momentum=mu, nesterov=nesterov)
+    x, m = x0.copy(), np.zeros(11)
+    for _ in range(6):
+        D = g.standard_normal(11)
+        p.grad = torch.from_numpy(D.copy())
+        opt.step()
+        x, m = oracle.sgd_momentum_step(x, m, D, lr, mu, nesterov=nesterov)
+        np.testing.assert_allclose(x, p.detach().numpy(), rtol=1e-14, atol=1e-15)
+
+
+# ------------------------------------------------------- seeded start for Q
+
+@pytest.mark.parametrize("key,counter", [
+    ((5, 7), (0, 0, 0, 0)),
+    ((0, 0), (0, 0, 0, 0)),
+    ((2 ** 64 - 1, 2 ** 64 - 1), (2 ** 64 - 2, 3, 2 ** 63, 9)),
+    ((1234, 17), (2 ** 64 - 1, 0, 0, 0)),  # the library's counter carries into word 1
+])
+def test_philox_matches_numpy_bit_generator(key, counter):
+    # numpy's Philox is Philox-4x64-10; it advances its 256-bit counter by one
+    # before producing each block of four words.
+    from oracle import philox as PH
+    bg = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(counter, dtype=np.uint64))
+    raw = [int(v) for v in bg.random_raw(12)]
+    c = sum(int(w) << (64 * i) for i, w in enumerate(counter))
+    for blk in range(3):
+        cc = (c + 1 + blk) % (1 << 256)
+        words = [(cc >> (64 * i)) & PH.MASK64 for i in range(4)]
+        assert list(PH.philox4x64(words, key)) == raw[4 * blk: 4 * blk + 4]
+
+
+def test_box_muller_inverts_to_its_uniforms():
+    # From each pair (z0, z1): exp(-(z0^2 + z1^2)/2) is u1 and the polar angle
+    # is 2 pi u2, for the uniforms built from the block's words.
+    from oracle import philox as PH
+    for b in range(50):
+        w = PH.philox4x64((b, 0, 0, 0), (99, 3))
+        z = PH.normal_stream(99, 3, 4 * b + 4)[4 * b: 4 * b + 4]
+        for (wa, wb), (z0, z1) in (((w[0], w[1]), z[:2]), ((w[2], w[3]), z[2:])):
+            u1 = 1.0 - (wa >> 11) / 2.0 ** 53
+            u2 = (wb >> 11) / 2.0 ** 53
+            assert abs(np.exp(-(z0 * z0 + z1 * z1) / 2) - u1) <= 1e-12
+            ang = np.arctan2(z1, z0) % (2 * np.pi)
+            assert min(abs(ang - 2 * np.pi * u2), 2 * np.pi - abs(ang - 2 * np.pi * u2)) <= 1e-9
+
+
+def test_seeded_q_is_standard_normal():
+    # Kolmogorov-Smirnov against N(0, 1) over 2^16 draws of one stream, and
+    # between-stream independence: correlation of two keys' streams.
+    scipy_stats = pytest.importorskip("scipy.stats")
+    z = oracle.normal_stream(2024, 0, 1 << 16)
+    assert scipy_stats.kstest(z, "norm").pvalue > 1e-3
+    assert abs(z.mean()) < 5 / np.sqrt(z.size) and abs(z.var() - 1) < 0.03
+    z2 = oracle.normal_stream(2024, 1, 1 << 16)
+    assert abs(np.corrcoef(z, z2)[0, 1]) < 5 / np.sqrt(z.size)
+
+
+def test_seeded_q_layout():
+    # Column c of the n x r start Q is the stream's slice [c n, (c + 1) n): the
+    # same column at every rank, different for another seed or tensor.
+    q4 = oracle.init_q(37, 4, 7, 2)
+    q9 = oracle.init_q(37, 9, 7, 2)
+    s = oracle.normal_stream(7, 2, 37 * 9)
+    assert np.array_equal(q9[:, :4], q4)
+    assert np.array_equal(q9, s.reshape(9, 37).T)
+    assert not np.array_equal(oracle.init_q(37, 4, 8, 2), q4)
+    assert not np.array_equal(oracle.init_q(37, 4, 7, 3), q4)
+    plan = oracle.Plan([(300, 40), (5,), (2, 2)], 4)
+    qs = oracle.init_q_set(plan, 11)
+    assert qs[1] is None and qs[2] is None and np.array_equal(qs[0], oracle.init_q(40, 4, 11, 0))
