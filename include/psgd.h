@@ -90,6 +90,8 @@ typedef struct psgd_plan* psgd_plan_t;
 #define PSGD_STEP_NO_ERROR_FEEDBACK 1u /* ablation: compress X alone, M = X; the error
                                           memory is neither read nor accumulated ([N152]
                                           Recommendations: error feedback is not optional) */
+#define PSGD_STEP_NESTEROV 2u          /* fused SGD steps along D + sgd_momentum * m
+                                          (Nesterov form) instead of m */
 
 /*
  * Options of one psgd_compress call; a NULL pointer means all defaults.
@@ -105,14 +107,15 @@ typedef struct psgd_plan* psgd_plan_t;
  *                  power iteration with orthonormalisation on M,
  *                  Q <- GS(M^T GS(M Q)), before P = M Q.  The caller chooses
  *                  the period (for example every 50th step).
- *   flags          PSGD_STEP_NO_ERROR_FEEDBACK or 0.
+ *   flags          PSGD_STEP_NO_ERROR_FEEDBACK and / or PSGD_STEP_NESTEROV, or 0.
  *   params, sgd_buf, sgd_lr, sgd_momentum
  *                  fused post-compression momentum SGD ([N152] Concepts,
  *                  "Post-compression momentum"): when params is non-NULL, the
  *                  decompressed (aggregated) update D of every tensor is
  *                  applied in the residual pass as heavy-ball SGD,
- *                  m <- sgd_momentum * m + D, x <- x - sgd_lr * m, on the flat
- *                  parameter buffer `params` and the flat buffer `sgd_buf`
+ *                  m <- sgd_momentum * m + D, x <- x - sgd_lr * m (with
+ *                  PSGD_STEP_NESTEROV: x <- x - sgd_lr * (D + sgd_momentum * m)),
+ *                  on the flat parameter buffer `params` and the flat buffer `sgd_buf`
  *                  (both in/out, plan layout, required together).
  */
 typedef struct psgd_step_opts {
@@ -264,6 +267,25 @@ psgd_status_t psgd_decompress(psgd_plan_t plan, const float* p, const float* q, 
  */
 psgd_status_t psgd_refresh(psgd_plan_t plan, int32_t tensor, const float* m, float* q, int32_t iters,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * psgd_init_q -- seeded start for the warm-start factors: every compressed
+ * tensor's columns of the packed Q buffer get i.i.d. N(0, 1) values.  The
+ * pages warm-start each step from the previous Q ([GLOSS], temporal-coherence
+ * paragraph; [N152] Method) and leave the first Q open; calling this before
+ * every step gives the cold-start ablation.  Element c*n + j (row j, column c)
+ * of tensor t's n x rank Q is normal number c*n + j of the stream keyed
+ * (seed, t): Philox-4x64-10 block (c*n + j)/4 at counter ((c*n + j)/4, 0, 0, 0)
+ * and key (seed, t) (Salmon et al., "Parallel random numbers: as easy as
+ * 1, 2, 3", SC'11), words 0,1 and 2,3 turned into two normals each by the
+ * Box-Muller transform in fp64 (u1 = 1 - (w0 >> 11) 2^-53, u2 = (w1 >> 11)
+ * 2^-53), rounded to fp32.  The values depend only on (seed, t, c, j): every
+ * worker with the same seed starts from the same Q, and a column is the
+ * same at every rank.  Other parts of q are not written.  Errors:
+ * PSGD_ERR_INVALID_ARG (null or misaligned q), PSGD_ERR_WORKSPACE.
+ */
+psgd_status_t psgd_init_q(psgd_plan_t plan, float* q, uint64_t seed, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * Per-stage timing with HIP events recorded on the call's stream.  While

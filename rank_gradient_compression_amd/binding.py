@@ -29,6 +29,8 @@ PSGD_KIND_PASSTHRU = 1
 PSGD_KIND_COMPRESSED = 2
 PSGD_FLAG_MOMENTUM = 1
 PSGD_FLAG_GRADS_BF16 = 2
+PSGD_STEP_NO_ERROR_FEEDBACK = 1
+PSGD_STEP_NESTEROV = 2
 
 PSGD_STAGE_EF_P = 0
 PSGD_STAGE_GS = 1
@@ -43,7 +45,7 @@ STAGE_NAMES = ["ef_p", "gs", "mtp", "qreduce", "residual", "passthru", "refresh"
 # Every symbol include/psgd.h declares.
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_destroy", "psgd_plan_get_info", "psgd_plan_tensor",
-    "psgd_workspace_init", "psgd_compress", "psgd_decompress", "psgd_refresh",
+    "psgd_workspace_init", "psgd_compress", "psgd_decompress", "psgd_refresh", "psgd_init_q",
     "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy", "psgd_last_error", "psgd_version",
 ]
 
@@ -64,9 +66,6 @@ class psgd_plan_info_t(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
-
-
-PSGD_STEP_NO_ERROR_FEEDBACK = 1
 
 
 class psgd_step_opts_t(ctypes.Structure):
@@ -125,13 +124,14 @@ lib.psgd_compress.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(
                               _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_decompress.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_refresh.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
+lib.psgd_init_q.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, ctypes.c_size_t, _vp]
 lib.psgd_timing_enable.argtypes = [_vp, ctypes.c_int32]
 lib.psgd_timing_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
 lib.psgd_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_last_error.restype = ctypes.c_char_p
 lib.psgd_version.restype = ctypes.c_char_p
 for _f in ["psgd_plan_create", "psgd_plan_get_info", "psgd_plan_tensor", "psgd_workspace_init", "psgd_compress",
-           "psgd_decompress", "psgd_refresh", "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy"]:
+           "psgd_decompress", "psgd_refresh", "psgd_init_q", "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy"]:
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -208,6 +208,11 @@ def psgd_decompress(plan: int, p: int, q: int, out: int, workspace: int, workspa
 def psgd_refresh(plan: int, tensor: int, m: int, q: int, iters: int, workspace: int, workspace_bytes: int,
                  stream: int = 0) -> None:
     _check("psgd_refresh", lib.psgd_refresh(plan, tensor, m, q, iters, workspace, workspace_bytes, stream))
+
+
+def psgd_init_q(plan: int, q: int, seed: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+    _check("psgd_init_q", lib.psgd_init_q(plan, q or None, seed & ((1 << 64) - 1), workspace, workspace_bytes,
+                                          stream))
 
 
 def psgd_timing_enable(plan: int, enable: bool) -> None:

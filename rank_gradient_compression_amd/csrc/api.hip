@@ -251,8 +251,9 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
     set_error("psgd_compress: negative iteration count");
     return PSGD_ERR_INVALID_ARG;
   }
-  if (o.flags & ~PSGD_STEP_NO_ERROR_FEEDBACK) {
-    set_error("psgd_compress: unknown step flag bits 0x%x", o.flags & ~PSGD_STEP_NO_ERROR_FEEDBACK);
+  constexpr uint32_t kKnownStepFlags = PSGD_STEP_NO_ERROR_FEEDBACK | PSGD_STEP_NESTEROV;
+  if (o.flags & ~kKnownStepFlags) {
+    set_error("psgd_compress: unknown step flag bits 0x%x", o.flags & ~kKnownStepFlags);
     return PSGD_ERR_INVALID_ARG;
   }
   if ((o.params != nullptr) != (o.sgd_buf != nullptr) || !aligned16(o.params) || !aligned16(o.sgd_buf)) {
@@ -267,7 +268,7 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
   const int refresh_iters = o.refresh_iters;
   const int power_iters = o.power_iters > 1 ? o.power_iters : 1;
   const bool ef = (o.flags & PSGD_STEP_NO_ERROR_FEEDBACK) == 0;
-  const SgdArgs sg{o.params, o.sgd_buf, o.sgd_lr, o.sgd_momentum};
+  const SgdArgs sg{o.params, o.sgd_buf, o.sgd_lr, o.sgd_momentum, (o.flags & PSGD_STEP_NESTEROV) ? 1 : 0};
   if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_compress")) return s;
   if (!any) return PSGD_OK;
 
@@ -392,6 +393,27 @@ extern "C" psgd_status_t psgd_refresh(psgd_plan_t p, int32_t tensor, const float
     PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, red, q), "refresh: Q partial reduction");
     PSGD_LAUNCH(PSGD_STAGE_GS, launch_gram_orth(c, oq, 1, nullptr, nb_q, q), "refresh: orthonormalise Q");
   }
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_init_q(psgd_plan_t p, float* q, uint64_t seed, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_init_q: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (!p->mats.empty() && (!q || !aligned16(q))) {
+    set_error("psgd_init_q: q must be non-null and 16-byte aligned");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_init_q")) return s;
+  if (p->mats.empty()) return PSGD_OK;
+  const LaunchCtx c = make_ctx(p, ws, stream);
+  int64_t max_blocks = 0;
+  for (const MatDesc& d : p->mats) max_blocks = std::max<int64_t>(max_blocks, ((int64_t)d.n * p->rank + 3) / 4);
+  const hipError_t e = launch_init_q(c, q, seed, max_blocks);
+  if (e != hipSuccess) return hip_fail(e, "psgd_init_q");
   return PSGD_OK;
 }
 

@@ -420,10 +420,17 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
           mm.y = fmaf(sg.mu, mm.y, mh.y);
           mm.z = fmaf(sg.mu, mm.z, mh.z);
           mm.w = fmaf(sg.mu, mm.w, mh.w);
-          xp.x = fmaf(-sg.lr, mm.x, xp.x);
-          xp.y = fmaf(-sg.lr, mm.y, xp.y);
-          xp.z = fmaf(-sg.lr, mm.z, xp.z);
-          xp.w = fmaf(-sg.lr, mm.w, xp.w);
+          if (sg.nesterov) {
+            xp.x = fmaf(-sg.lr, fmaf(sg.mu, mm.x, mh.x), xp.x);
+            xp.y = fmaf(-sg.lr, fmaf(sg.mu, mm.y, mh.y), xp.y);
+            xp.z = fmaf(-sg.lr, fmaf(sg.mu, mm.z, mh.z), xp.z);
+            xp.w = fmaf(-sg.lr, fmaf(sg.mu, mm.w, mh.w), xp.w);
+          } else {
+            xp.x = fmaf(-sg.lr, mm.x, xp.x);
+            xp.y = fmaf(-sg.lr, mm.y, xp.y);
+            xp.z = fmaf(-sg.lr, mm.z, xp.z);
+            xp.w = fmaf(-sg.lr, mm.w, xp.w);
+          }
           stq<VEC4>(sg.m + d.off + (int64_t)rr * n, col, n, mm);
           stq<VEC4>(sg.x + d.off + (int64_t)rr * n, col, n, xp);
         }

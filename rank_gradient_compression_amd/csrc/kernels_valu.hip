@@ -414,7 +414,8 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane,
 #pragma unroll
           for (int c = 0; c < VEC; ++c) {
             xm[rr].v[c] = fmaf(sg.mu, xm[rr].v[c], mh.v[c]);
-            xp[rr].v[c] = fmaf(-sg.lr, xm[rr].v[c], xp[rr].v[c]);
+            const float dir = sg.nesterov ? fmaf(sg.mu, xm[rr].v[c], mh.v[c]) : xm[rr].v[c];
+            xp[rr].v[c] = fmaf(-sg.lr, dir, xp[rr].v[c]);
           }
           stv<VEC>(sg.m + idx, xm[rr]);
           stv<VEC>(sg.x + idx, xp[rr]);
@@ -484,7 +485,8 @@ __global__ __launch_bounds__(256) void k_pass_unpack(const PassDesc* __restrict_
     if constexpr (SGD) {
       const float mm = fmaf(sg.mu, sg.m[pd.off + i], v);
       sg.m[pd.off + i] = mm;
-      sg.x[pd.off + i] = fmaf(-sg.lr, mm, sg.x[pd.off + i]);
+      const float dir = sg.nesterov ? fmaf(sg.mu, mm, v) : mm;
+      sg.x[pd.off + i] = fmaf(-sg.lr, dir, sg.x[pd.off + i]);
     }
   }
 }

@@ -173,6 +173,7 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     d.q_off = p->q_off[i];
     d.m = (int32_t)m;
     d.n = (int32_t)n;
+    d.tensor = i;
     d.vec = (n % 4 == 0 && d.off % 4 == 0) ? 4 : (n % 2 == 0 && d.off % 2 == 0) ? 2 : 1;
     p->mats.push_back(d);
     p->mat_tensor.push_back(i);

@@ -44,6 +44,7 @@ struct SgdArgs {
   float* m;
   float lr;
   float mu;
+  int nesterov;  // step along D + mu m instead of m
 };
 
 // A contiguous range of workgroups of one of the plan's grids (the whole grid
@@ -84,6 +85,10 @@ hipError_t launch_gram_orth(const LaunchCtx& c, int first, int count, const int3
 hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q);
 hipError_t launch_pass_pack(const LaunchCtx& c, const void* G, float* U, float beta, float* Pbuf);
 hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out, const SgdArgs& sg);
+// Seeded N(0, 1) start Q of every compressed tensor (max_blocks: the largest
+// ceil(n * rank / 4) over the matrices).
+hipError_t launch_init_q(const LaunchCtx& c, float* Q, uint64_t seed, int64_t max_blocks);
+
 hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);
 
 }  // namespace psgd

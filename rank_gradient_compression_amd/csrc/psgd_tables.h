@@ -55,7 +55,8 @@ struct MatDesc {
   int32_t wg_pred0;  // first workgroup in the P-partial reduce grid (s1 > 1)
   int32_t wg_gram0;  // first workgroup in the Gram-partial / apply grid
   int32_t ngb;       // Gram-partial blocks (kGramRows rows each)
-  int32_t pad_[4];
+  int32_t tensor;    // index of the tensor in the plan
+  int32_t pad_[3];
 };
 static_assert(sizeof(MatDesc) == 128, "MatDesc layout");
 

@@ -105,12 +105,12 @@ class PowerSGD:
     def compress(self, mhat: bool = False, hook=None, mhat_buf: Optional[torch.Tensor] = None,
                  refresh_iters: int = 0, power_iters: int = 0, error_feedback: bool = True,
                  params: Optional[torch.Tensor] = None, sgd_buf: Optional[torch.Tensor] = None, sgd_lr: float = 0.0,
-                 sgd_momentum: float = 0.0) -> None:
+                 sgd_momentum: float = 0.0, nesterov: bool = False) -> None:
         out = mhat_buf if mhat_buf is not None else (self.mhat if mhat else None)
         opts = None
-        if refresh_iters or power_iters or not error_feedback or params is not None:
-            opts = B.step_opts(power_iters, refresh_iters, 0 if error_feedback else B.PSGD_STEP_NO_ERROR_FEEDBACK,
-                               sgd_lr, sgd_momentum, params.data_ptr() if params is not None else 0,
+        flags = (0 if error_feedback else B.PSGD_STEP_NO_ERROR_FEEDBACK) | (B.PSGD_STEP_NESTEROV if nesterov else 0)
+        if refresh_iters or power_iters or flags or params is not None:
+            opts = B.step_opts(power_iters, refresh_iters, flags, sgd_lr, sgd_momentum, params.data_ptr() if params is not None else 0,
                                sgd_buf.data_ptr() if sgd_buf is not None else 0)
         B.psgd_compress(self.plan, self.grads.data_ptr(), self.err.data_ptr(),
                         self.mom.data_ptr() if self.mom is not None else 0, self.q.data_ptr(), self.p.data_ptr(),
@@ -122,6 +122,11 @@ class PowerSGD:
         B.psgd_decompress(self.plan, self.p.data_ptr(), self.q.data_ptr(), out.data_ptr(), self.workspace.data_ptr(),
                           self.ws_bytes, self._stream())
         return out
+
+    def init_q(self, seed: int) -> None:
+        """Seeded N(0, 1) start Q for every compressed tensor (psgd_init_q)."""
+        B.psgd_init_q(self.plan, self.q.data_ptr(), int(seed), self.workspace.data_ptr(), self.ws_bytes,
+                      self._stream())
 
     def refresh(self, i: int, m_buf: torch.Tensor, iters: int) -> None:
         B.psgd_refresh(self.plan, i, m_buf.data_ptr(), self.q.data_ptr(), iters, self.workspace.data_ptr(),

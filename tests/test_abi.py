@@ -261,3 +261,27 @@ def test_timing_read_without_records():
     ms, n = R.psgd_timing_read(p)
     assert ms == [0.0] * B.PSGD_NSTAGES and n == [0] * B.PSGD_NSTAGES
     R.psgd_plan_destroy(p)
+
+
+@pytest.mark.parametrize("q,ws,wsb,status", [
+    (0, FAKE * 2, 1 << 40, B.PSGD_ERR_INVALID_ARG),
+    (FAKE + 4, FAKE * 2, 1 << 40, B.PSGD_ERR_INVALID_ARG),
+    (FAKE, 0, 1 << 40, B.PSGD_ERR_WORKSPACE),
+    (FAKE, FAKE * 2, 16, B.PSGD_ERR_WORKSPACE),
+])
+def test_init_q_argument_errors(q, ws, wsb, status):
+    p = R.psgd_plan_create([64, 9], [48, 1], 2)
+    try:
+        with pytest.raises(B.PsgdError) as e:
+            R.psgd_init_q(p, q, 7, ws, wsb)
+        assert e.value.status == status
+    finally:
+        R.psgd_plan_destroy(p)
+
+
+def test_init_q_without_matrices_is_a_no_op():
+    p = R.psgd_plan_create([5, 7], [1, 1], 2)
+    try:
+        R.psgd_init_q(p, 0, 7, FAKE * 2, 1 << 20)  # nothing to write, nothing launched
+    finally:
+        R.psgd_plan_destroy(p)

@@ -122,7 +122,8 @@ def test_powersgd_plus_step(rank):
 
 # ------------------------------------------------- step options on the GPU
 
-def _options_case(shapes, rank, seed, steps, beta=None, power_iters=1, error_feedback=True, sgd=False, tag=""):
+def _options_case(shapes, rank, seed, steps, beta=None, power_iters=1, error_feedback=True, sgd=False, tag="",
+                  nesterov=False):
     from gpu_util import compare_set
     tensors = [(str(i), s) for i, s in enumerate(shapes)]
     wl = W.ModelSetWorkload(tensors, "plain", seed=seed)
@@ -148,7 +149,8 @@ def _options_case(shapes, rank, seed, steps, beta=None, power_iters=1, error_fee
             ps.view(ps.grads, i).copy_(torch.from_numpy(g).to(DEV))
         say(f"[{tag}] step {t}")
         ps.compress(mhat=True, power_iters=power_iters, error_feedback=error_feedback,
-                    params=params if sgd else None, sgd_buf=sbuf if sgd else None, sgd_lr=lr, sgd_momentum=mu)
+                    params=params if sgd else None, sgd_buf=sbuf if sgd else None, sgd_lr=lr, sgd_momentum=mu,
+                    nesterov=nesterov)
         torch.cuda.synchronize()
         res = oracle.step_set(oplan, grads, ost, beta=beta or 0.0, power_iters=power_iters,
                               error_feedback=error_feedback)
@@ -156,7 +158,7 @@ def _options_case(shapes, rank, seed, steps, beta=None, power_iters=1, error_fee
         if sgd:
             for i in range(len(shapes)):
                 D = np.asarray(res.M_hat[i]).reshape(xo[i].shape)
-                xo[i], mo[i] = oracle.sgd_momentum_step(xo[i], mo[i], D, lr, mu)
+                xo[i], mo[i] = oracle.sgd_momentum_step(xo[i], mo[i], D, lr, mu, nesterov=nesterov)
                 assert rel(cpu(ps.view(params, i)), xo[i]) <= REL_TOL, (tag, i, "params")
                 assert rel(cpu(ps.view(sbuf, i)), mo[i]) <= REL_TOL, (tag, i, "sgd momentum")
 
@@ -176,3 +178,9 @@ def test_no_error_feedback(rank, beta):
 @pytest.mark.parametrize("rank", [2, 5, 16, 64])
 def test_fused_post_compression_sgd(rank):
     _options_case([(300, 650), (500, 1024), (2, 2), (11,)], rank, 90 + rank, 3, sgd=True, tag=f"sgd r={rank}")
+
+
+@pytest.mark.parametrize("rank", [4, 32])
+def test_fused_post_compression_sgd_nesterov(rank):
+    _options_case([(300, 650), (257, 1030), (2, 2), (11,)], rank, 95 + rank, 3, sgd=True, nesterov=True,
+                  tag=f"sgd nesterov r={rank}")
