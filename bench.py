@@ -234,6 +234,22 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
         res["config"]["compress_only"] = {"ms_per_step": round(ms_c, 4),
                                           "grad_gbs": round(4.0 * dense / (ms_c * 1e-3) / 1e9, 2),
                                           "hbm_frac": round(24.0 * dense / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # Deferred residual: E = M - P_hat Q^T is formed inside the next
+        # step's EF-add pass instead of being stored (20 / 16 B per element).
+        ps.compress(mhat=True, defer_residual=True)
+        ms_d, _ = R.time("deferred residual, compress + fused decompress",
+                         lambda: ps.compress(mhat=True, defer_residual=True, residual_deferred=True),
+                         max(3, args.steps // 2), 1, per_step=False)
+        ms_dc, _ = R.time("deferred residual, compress only",
+                          lambda: ps.compress(mhat=False, defer_residual=True, residual_deferred=True),
+                          max(3, args.steps // 2), 1, per_step=False)
+        res["config"]["deferred_residual"] = {
+            "fused": {"ms_per_step": round(ms_d, 4), "grad_gbs": round(4.0 * dense / (ms_d * 1e-3) / 1e9, 2),
+                      "bytes_per_el": 20.0,
+                      "hbm_frac": round(20.0 * dense / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "compress_only": {"ms_per_step": round(ms_dc, 4),
+                              "grad_gbs": round(4.0 * dense / (ms_dc * 1e-3) / 1e9, 2), "bytes_per_el": 16.0,
+                              "hbm_frac": round(16.0 * dense / (ms_dc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
         ps.close()
         del ps
         torch.cuda.empty_cache()

@@ -92,6 +92,23 @@ typedef struct psgd_plan* psgd_plan_t;
                                           Recommendations: error feedback is not optional) */
 #define PSGD_STEP_NESTEROV 2u          /* fused SGD steps along D + sgd_momentum * m
                                           (Nesterov form) instead of m */
+/*
+ * Deferred residual (vector-ALU ranks, rank <= 8; error feedback on).  The
+ * residual E = M - P_hat Q^T ([GLOSS], error-feedback paragraph) is only read
+ * by the next step's EF-add, so it need not be stored: with
+ * PSGD_STEP_DEFER_RESIDUAL the call leaves M itself in `err` (P_hat and Q of
+ * the step are in `p` and `q` anyway) and skips the residual pass (M_hat, if
+ * requested, is still written, by a write-only pass).  The next call passes
+ * PSGD_STEP_RESIDUAL_DEFERRED and forms E = M_prev - P_hat_prev Q_prev^T
+ * inside its EF-add pass, reading P_hat_prev and Q_prev from `p` and `q`
+ * (which must hold the previous call's outputs, unchanged).  Steady state
+ * passes both flags; a call with only RESIDUAL_DEFERRED ends with an explicit
+ * E again (for a checkpoint).  Per element this removes the residual pass's
+ * read of M and write of E: 16 instead of 24 bytes for a compress step.
+ * The same E is formed, with the same operations in the same order.
+ */
+#define PSGD_STEP_DEFER_RESIDUAL 4u
+#define PSGD_STEP_RESIDUAL_DEFERRED 8u
 
 /*
  * Options of one psgd_compress call; a NULL pointer means all defaults.
@@ -107,7 +124,8 @@ typedef struct psgd_plan* psgd_plan_t;
  *                  power iteration with orthonormalisation on M,
  *                  Q <- GS(M^T GS(M Q)), before P = M Q.  The caller chooses
  *                  the period (for example every 50th step).
- *   flags          PSGD_STEP_NO_ERROR_FEEDBACK and / or PSGD_STEP_NESTEROV, or 0.
+ *   flags          any of PSGD_STEP_NO_ERROR_FEEDBACK, PSGD_STEP_NESTEROV,
+ *                  PSGD_STEP_DEFER_RESIDUAL, PSGD_STEP_RESIDUAL_DEFERRED, or 0.
  *   params, sgd_buf, sgd_lr, sgd_momentum
  *                  fused post-compression momentum SGD ([N152] Concepts,
  *                  "Post-compression momentum"): when params is non-NULL, the
@@ -217,6 +235,8 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  *          first step).  On return: the new residual M - P_hat Q^T.  While the
  *          call runs it holds M = X + E_old; if the call fails after the first
  *          pass (a hook error or a launch failure) it is left holding M.
+ *          With the deferred-residual flags it holds M on entry and / or on
+ *          return instead (see PSGD_STEP_DEFER_RESIDUAL).
  *   mom    flat, in/out momentum u (all tensors), required iff the plan has
  *          PSGD_FLAG_MOMENTUM (then X = u <- beta*u + G; else X = G), else NULL.
  *   q      packed Q buffer: on entry the warm start (the previous step's Q, or a
@@ -239,7 +259,9 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  *
  * Errors: PSGD_ERR_INVALID_ARG for null or not 16-byte aligned buffers, a
  * missing or unexpected `mom`, negative iteration counts, `params` without
- * `sgd_buf` (or misaligned), unknown step flags; PSGD_ERR_WORKSPACE;
+ * `sgd_buf` (or misaligned), unknown step flags, deferred-residual flags
+ * without error feedback; PSGD_ERR_UNSUPPORTED for deferred-residual flags
+ * at ranks above 8; PSGD_ERR_WORKSPACE;
  * PSGD_ERR_HOOK if a hook
  * returns non-zero (no later stage is enqueued); PSGD_ERR_HIP.
  */

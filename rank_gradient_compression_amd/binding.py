@@ -31,6 +31,8 @@ PSGD_FLAG_MOMENTUM = 1
 PSGD_FLAG_GRADS_BF16 = 2
 PSGD_STEP_NO_ERROR_FEEDBACK = 1
 PSGD_STEP_NESTEROV = 2
+PSGD_STEP_DEFER_RESIDUAL = 4
+PSGD_STEP_RESIDUAL_DEFERRED = 8
 
 PSGD_STAGE_EF_P = 0
 PSGD_STAGE_GS = 1

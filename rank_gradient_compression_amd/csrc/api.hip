@@ -251,10 +251,21 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
     set_error("psgd_compress: negative iteration count");
     return PSGD_ERR_INVALID_ARG;
   }
-  constexpr uint32_t kKnownStepFlags = PSGD_STEP_NO_ERROR_FEEDBACK | PSGD_STEP_NESTEROV;
+  constexpr uint32_t kKnownStepFlags =
+      PSGD_STEP_NO_ERROR_FEEDBACK | PSGD_STEP_NESTEROV | PSGD_STEP_DEFER_RESIDUAL | PSGD_STEP_RESIDUAL_DEFERRED;
   if (o.flags & ~kKnownStepFlags) {
     set_error("psgd_compress: unknown step flag bits 0x%x", o.flags & ~kKnownStepFlags);
     return PSGD_ERR_INVALID_ARG;
+  }
+  const bool defer_out = (o.flags & PSGD_STEP_DEFER_RESIDUAL) != 0;
+  const bool defer_in = (o.flags & PSGD_STEP_RESIDUAL_DEFERRED) != 0;
+  if ((defer_out || defer_in) && (o.flags & PSGD_STEP_NO_ERROR_FEEDBACK)) {
+    set_error("psgd_compress: a deferred residual needs error feedback");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if ((defer_out || defer_in) && p->rank > kValuMaxRank) {
+    set_error("psgd_compress: the deferred residual is implemented for ranks up to %d", kValuMaxRank);
+    return PSGD_ERR_UNSUPPORTED;
   }
   if ((o.params != nullptr) != (o.sgd_buf != nullptr) || !aligned16(o.params) || !aligned16(o.sgd_buf)) {
     set_error("psgd_compress: params and sgd_buf must be given together, 16-byte aligned");
@@ -272,10 +283,11 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
   if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_compress")) return s;
   if (!any) return PSGD_OK;
 
-  const LaunchCtx c = make_ctx(p, ws, stream);
+  LaunchCtx c = make_ctx(p, ws, stream);
+  c.p_prev = pbuf;
   float* U = momentum ? mom : nullptr;
   const GridRange all_rows{0, c.wg_rows}, all_pred{0, c.wg_pred}, all_mtp{0, c.wg_mtp}, all_red{0, c.wg_red};
-  const int mode = ef ? (momentum ? 2 : 1) : (momentum ? 4 : 3);
+  const int mode = !ef ? (momentum ? 4 : 3) : defer_in ? (momentum ? 6 : 5) : (momentum ? 2 : 1);
 
   PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_pack(c, grads, U, p->beta, pbuf), "pass-through pack");
   if (refresh_iters <= 0) {
@@ -319,7 +331,10 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
       return PSGD_ERR_HOOK;
     }
   }
-  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, err, q, pbuf, mhat, true, sg), "residual E = M - P_hat Q^T");
+  if (!defer_out)
+    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, err, q, pbuf, mhat, true, sg), "residual E = M - P_hat Q^T");
+  else if (mhat || sg.x)  // err keeps M; only the decompressed update is written
+    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, nullptr, q, pbuf, mhat, false, sg), "decompress P_hat Q^T");
   if (mhat || sg.x)
     PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat, sg), "pass-through unpack");
   return PSGD_OK;

@@ -658,7 +658,8 @@ static hipError_t mfma_p_rpg(const LaunchCtx& c, const GridRange& g, int mode, c
     case 1: PSGD_MP(1); break;
     case 2: PSGD_MP(2); break;
     case 3: PSGD_MP(3); break;
-    default: PSGD_MP(4); break;
+    case 4: PSGD_MP(4); break;
+    default: return hipErrorInvalidValue;  // deferred-residual modes: vector-ALU ranks only
   }
 #undef PSGD_MP
   return hipGetLastError();

@@ -161,15 +161,37 @@ constexpr int pow2_at_least(int x) {
 // One wavefront: rows [row0, row0 + kWaveRows) of matrix d, all columns.  Each
 // lane keeps its VEC x R slice of Q in registers for the current column step
 // and reuses it across the wavefront's rows.
+// Row `rr` of P_hat Q^T at the lane's VEC columns: the reconstruction of the
+// residual pass, in one fixed summation order.  The leading product is kept a
+// separately rounded multiply (no contraction into a later subtraction), so
+// every kernel that forms M - P_hat Q^T rounds the same way.
+template <int R, int VEC>
+__device__ __forceinline__ Vec<VEC> recon_row(const float (&ph)[R], const Vec<VEC> (&qv)[R]) {
+#pragma clang fp contract(off)
+  Vec<VEC> mh;
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) {
+    float s = ph[0] * qv[0].v[c];
+#pragma unroll
+    for (int k = 1; k < R; ++k) s = fmaf(ph[k], qv[k].v[c], s);
+    mh.v[c] = s;
+  }
+  return mh;
+}
+
 // MODE 0: M read from E (plain M Q); 1: M = G + E; 2: u = beta u + G,
-// M = u + E; 3: M = G (no error feedback); 4: u = beta u + G, M = u.  Modes
-// 1..4 store M over E.
+// M = u + E; 3: M = G (no error feedback); 4: u = beta u + G, M = u.
+// Deferred residual: E holds the previous step's M and Pold / Q its P_hat and
+// Q, so E = M_prev - P_hat Q^T is formed here on the fly; 5: M = G + E,
+// 6: u = beta u + G, M = u + E.  Modes 1..6 store M over E.  Pold may be P
+// itself: each wavefront reads its rows of Pold before writing them in P.
 template <int R, int VEC, int MODE, bool GBF16>
 __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, const void* __restrict__ G,
                                           float* __restrict__ E, float* __restrict__ U, float beta,
-                                          const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed) {
-  constexpr bool MOM = MODE == 2 || MODE == 4;
-  constexpr bool LOAD_E = MODE <= 2;
+                                          const float* __restrict__ Q, float* P, int64_t p_fixed, const float* Pold) {
+  constexpr bool MOM = MODE == 2 || MODE == 4 || MODE == 6;
+  constexpr bool LOAD_E = MODE <= 2 || MODE >= 5;
+  constexpr bool DEFERRED = MODE >= 5;
   const int m = d.m, n = d.n;
   const int nrows = min(kWaveRows, m - row0);
   float acc[kWaveRows][R];
@@ -177,6 +199,13 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
   for (int rr = 0; rr < kWaveRows; ++rr)
 #pragma unroll
     for (int k = 0; k < R; ++k) acc[rr][k] = 0.f;
+  float ph[kWaveRows][R];
+  if constexpr (DEFERRED) {
+#pragma unroll
+    for (int rr = 0; rr < kWaveRows; ++rr)
+#pragma unroll
+      for (int k = 0; k < R; ++k) ph[rr][k] = Pold[d.p_off + (int64_t)k * m + row0 + min(rr, nrows - 1)];
+  }
 
   const float* q = Q + d.q_off;
   const int64_t base = d.off + (int64_t)row0 * n;
@@ -201,6 +230,11 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
       if (rr < nrows) {
         const int64_t idx = base + (int64_t)rr * n + j;
         Vec<VEC> mv;
+        if constexpr (DEFERRED) {
+          const Vec<VEC> mh = recon_row<R, VEC>(ph[rr], qv);
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) e[rr].v[c] = e[rr].v[c] - mh.v[c];
+        }
         if constexpr (MODE == 0) {
           mv = e[rr];
         } else if constexpr (MOM) {
@@ -240,19 +274,19 @@ __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__
                                                      const int32_t* __restrict__ map, int wg_base,
                                                      const void* __restrict__ G, float* __restrict__ E,
                                                      float* __restrict__ U, float beta,
-                                                     const float* __restrict__ Q, float* __restrict__ P,
-                                                     int64_t p_fixed) {
+                                                     const float* __restrict__ Q, float* P, int64_t p_fixed,
+                                                     const float* Pold) {
   const int wg = blockIdx.x + wg_base;
   const MatDesc d = mats[map[wg]];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
   if (row0 >= d.m) return;
   if (d.vec == 4)
-    ef_p_wave<R, 4, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
+    ef_p_wave<R, 4, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed, Pold);
   else if (d.vec == 2)
-    ef_p_wave<R, 2, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
+    ef_p_wave<R, 2, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed, Pold);
   else
-    ef_p_wave<R, 1, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed);
+    ef_p_wave<R, 1, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed, Pold);
 }
 
 // ---------------------------------------------------------------------------
@@ -393,14 +427,7 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane,
     for (int rr = 0; rr < kWaveRows; ++rr) {
       if (rr < nrows) {
         const int64_t idx = base + (int64_t)rr * n + j;
-        Vec<VEC> mh;
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-          float s = ph[rr][0] * qv[0].v[c];
-#pragma unroll
-          for (int k = 1; k < R; ++k) s = fmaf(ph[rr][k], qv[k].v[c], s);
-          mh.v[c] = s;
-        }
+        const Vec<VEC> mh = recon_row<R, VEC>(ph[rr], qv);
         if constexpr (RESID) {
           Vec<VEC> e;
 #pragma unroll
@@ -508,12 +535,14 @@ static hipError_t launch_ef_p_rg(const LaunchCtx& c, const GridRange& g, int mod
   const dim3 gr(g.count), b(kWGThreads);
 #define PSGD_EFP(MD)                                                                                            \
   hipLaunchKernelGGL((k_ef_p<R, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, \
-                     p_fixed)
+                     p_fixed, c.p_prev)
   switch (mode) {
     case 1: PSGD_EFP(1); break;
     case 2: PSGD_EFP(2); break;
     case 3: PSGD_EFP(3); break;
-    default: PSGD_EFP(4); break;
+    case 4: PSGD_EFP(4); break;
+    case 5: PSGD_EFP(5); break;
+    default: PSGD_EFP(6); break;
   }
 #undef PSGD_EFP
   return hipGetLastError();
@@ -525,7 +554,7 @@ static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode
   if (g.count == 0) return hipSuccess;
   if (mode == 0) {  // P = M Q with M read from E: no gradient involved
     hipLaunchKernelGGL((k_ef_p<R, 0, false>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map,
-                       g.base, G, E, U, beta, Q, P, p_fixed);
+                       g.base, G, E, U, beta, Q, P, p_fixed, nullptr);
     return hipGetLastError();
   }
   return c.g_bf16 ? launch_ef_p_rg<R, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)

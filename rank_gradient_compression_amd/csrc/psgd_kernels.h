@@ -19,6 +19,7 @@ struct LaunchCtx {
   int rank, rank_pad;
   bool mfma;
   bool g_bf16;  // gradients stored as bfloat16
+  const float* p_prev;  // deferred residual: the previous step's P_hat (plan offsets)
   int nmat, npass;
   int wg_rows, wg_mtp, wg_red, wg_pass, wg_pred, wg_gram, wg_gramq;
   const MatDesc* mats;
@@ -57,7 +58,9 @@ struct GridRange {
 // ---- ranks up to kValuMaxRank (vector ALU kernels)
 // mode 0: P = M Q with M read from E; 1: M = G + E stored over E; 2: also
 // u = beta u + G first (M = u + E); 3: M = G; 4: u = beta u + G, M = u
-// (3 and 4: no error feedback).  p_fixed >= 0 replaces the plan's P offset.
+// (3 and 4: no error feedback); 5 and 6: as 1 and 2 with E formed from a
+// deferred residual, E = E_in - p_prev Q^T (vector-ALU ranks only).
+// p_fixed >= 0 replaces the plan's P offset.
 hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                        float beta, const float* Q, float* P, int64_t p_fixed);
 hipError_t launch_mtp(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph, int64_t ph_fixed,

@@ -179,7 +179,11 @@ def _compress(plan, **kw):
     (dict(workspace_bytes=16), B.PSGD_ERR_WORKSPACE),
     (dict(opts=B.step_opts(refresh_iters=-1)), B.PSGD_ERR_INVALID_ARG),
     (dict(opts=B.step_opts(power_iters=-2)), B.PSGD_ERR_INVALID_ARG),
-    (dict(opts=B.step_opts(flags=4)), B.PSGD_ERR_INVALID_ARG),
+    (dict(opts=B.step_opts(flags=16)), B.PSGD_ERR_INVALID_ARG),
+    (dict(opts=B.step_opts(flags=B.PSGD_STEP_DEFER_RESIDUAL | B.PSGD_STEP_NO_ERROR_FEEDBACK)),
+     B.PSGD_ERR_INVALID_ARG),
+    (dict(opts=B.step_opts(flags=B.PSGD_STEP_RESIDUAL_DEFERRED | B.PSGD_STEP_NO_ERROR_FEEDBACK)),
+     B.PSGD_ERR_INVALID_ARG),
     (dict(opts=B.step_opts(params=FAKE * 4)), B.PSGD_ERR_INVALID_ARG),            # params without sgd_buf
     (dict(opts=B.step_opts(params=FAKE * 4, sgd_buf=FAKE * 4)), B.PSGD_ERR_INVALID_ARG),  # aliasing
     (dict(opts=B.step_opts(params=FAKE * 4 + 8, sgd_buf=FAKE * 8)), B.PSGD_ERR_INVALID_ARG),  # misaligned
@@ -283,5 +287,16 @@ def test_init_q_without_matrices_is_a_no_op():
     p = R.psgd_plan_create([5, 7], [1, 1], 2)
     try:
         R.psgd_init_q(p, 0, 7, FAKE * 2, 1 << 20)  # nothing to write, nothing launched
+    finally:
+        R.psgd_plan_destroy(p)
+
+
+@pytest.mark.parametrize("flags", [B.PSGD_STEP_DEFER_RESIDUAL, B.PSGD_STEP_RESIDUAL_DEFERRED])
+def test_deferred_residual_needs_vector_alu_rank(flags):
+    p = R.psgd_plan_create([640], [480], 16)
+    try:
+        with pytest.raises(B.PsgdError) as e:
+            _compress(p, opts=B.step_opts(flags=flags))
+        assert e.value.status == B.PSGD_ERR_UNSUPPORTED
     finally:
         R.psgd_plan_destroy(p)

@@ -1,0 +1,84 @@
+"""Deferred residual (PSGD_STEP_DEFER_RESIDUAL / PSGD_STEP_RESIDUAL_DEFERRED)
+against the fp64 oracle's ordinary step: P_hat, Q and M_hat every step, the
+M left in the error buffer against the oracle's compressor input, and the
+explicit E once a call ends without deferring.  Also bit-for-bit equality with
+the explicit-residual path on the GPU, since both form the same E with the
+same operations."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from gpu_util import REL_TOL, compare_set, cpu, rel, say  # noqa: E402
+from rank_gradient_compression_amd.torch_api import PowerSGD  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+SHAPES = [(300, 650), (257, 4099), (97, 1030), (33, 27), (5,), (640, 512), (2, 2)]
+
+
+def _run(shapes, rank, steps, beta=None, grads_dtype=torch.float32, seed=0, offsets=None, sgd=False):
+    tensors = [(str(i), s) for i, s in enumerate(shapes)]
+    wl = W.ModelSetWorkload(tensors, "lstm3" if beta is None else "plain", seed=seed)
+    ps = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta, offsets=offsets, grads_dtype=grads_dtype)
+    ref = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta, offsets=offsets, grads_dtype=grads_dtype)
+    oplan = oracle.Plan(shapes, rank)
+    q0 = [wl.q0(i, rank) if oplan.kinds[i] == oracle.KIND_COMPRESSED else None for i in range(len(shapes))]
+    ost = oracle.init_state(oplan, q0, momentum=beta is not None)
+    for i in ps.compressed():
+        ps.set_q(i, q0[i])
+        ref.set_q(i, q0[i])
+    sgd_kw = {}
+    if sgd:
+        x = torch.randn(ps.grads.numel(), device=DEV)
+        sgd_kw = dict(params=x.clone(), sgd_buf=torch.zeros_like(x), sgd_lr=0.05, sgd_momentum=0.9)
+        sgd_ref = dict(params=x.clone(), sgd_buf=torch.zeros_like(x), sgd_lr=0.05, sgd_momentum=0.9)
+    for t in range(1, steps + 1):
+        grads = [wl.grad(i, t) for i in range(len(shapes))]
+        host = [torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to(grads_dtype) for g in grads]
+        grads = [h.double().numpy() for h in host]
+        for i, h in enumerate(host):
+            ps.view(ps.grads, i).copy_(h.to(DEV))
+            ref.view(ref.grads, i).copy_(h.to(DEV))
+        last = t == steps
+        say(f"[deferred r={rank} beta={beta}] step {t}{' (explicit E at the end)' if last else ''}")
+        ps.compress(mhat=True, defer_residual=not last, residual_deferred=t > 1, **sgd_kw)
+        ref.compress(mhat=True, **(sgd_ref if sgd else {}))
+        torch.cuda.synchronize()
+        res = oracle.step_set(oplan, grads, ost, beta=beta or 0.0)
+        if last:
+            compare_set(ps, oplan, res, ost, tag=f"deferred r={rank} step {t}")
+        else:
+            compare_set(ps, oplan, res, ost, tag=f"deferred r={rank} step {t}", check_e=False)
+            for i in ps.compressed():
+                e = rel(cpu(ps.view(ps.err, i)), res.M[i])
+                assert e <= REL_TOL, f"step {t} tensor {i}: M left in err, rel err {e:.3e}"
+        # the same operations in the same order as the explicit path
+        assert torch.equal(ps.p, ref.p) and torch.equal(ps.q, ref.q), f"step {t}: factors differ"
+        assert torch.equal(ps.mhat, ref.mhat), f"step {t}: M_hat differs"
+        if sgd:
+            assert torch.equal(sgd_kw["params"], sgd_ref["params"]), f"step {t}: params differ"
+        if last:
+            assert torch.equal(ps.err, ref.err), "explicit E differs"
+        if beta is not None:
+            assert torch.equal(ps.mom, ref.mom)
+
+
+@pytest.mark.parametrize("rank", [1, 2, 4, 7, 8])
+def test_deferred_residual_ranks(rank):
+    _run(SHAPES, rank, 4, seed=150 + rank)
+
+
+def test_deferred_residual_momentum_bf16_odd_offsets():
+    shapes = [(300, 512), (200, 650), (13,)]
+    offsets = [1, 300 * 512 + 3, 300 * 512 + 3 + 200 * 650 + 2]
+    _run(shapes, 4, 4, beta=0.9, grads_dtype=torch.bfloat16, seed=160, offsets=offsets)
+
+
+def test_deferred_residual_with_fused_sgd():
+    _run([(300, 650), (400, 512), (11,)], 4, 3, seed=170, sgd=True)
