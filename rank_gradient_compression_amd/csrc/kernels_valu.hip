@@ -278,7 +278,8 @@ __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__
                                                      const float* Pold) {
   const int wg = blockIdx.x + wg_base;
   const MatDesc d = mats[map[wg]];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index made provably uniform: row addressing and P_hat loads go scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
   if (row0 >= d.m) return;
   if (d.vec == 4)
@@ -354,7 +355,8 @@ __global__ __launch_bounds__(kWGThreads) void k_mtp(const MatDesc* __restrict__ 
   const MatDesc d = mats[map[wg]];
   const int local = wg - d.wg_mtp0;
   const int rb = local / d.ncb, cb = local - rb * d.ncb;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index made provably uniform: row addressing and P_hat loads go scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = (cb * kMtpWaves + wave) * 64 * d.vec + lane * d.vec;
   if (j >= d.n) return;
   if (d.vec == 4)
@@ -459,7 +461,8 @@ __global__ __launch_bounds__(kWGThreads) void k_recon(const MatDesc* __restrict_
                                                       SgdArgs sg) {
   const int wg = blockIdx.x;
   const MatDesc d = mats[map[wg]];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index made provably uniform: row addressing and P_hat loads go scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
   if (row0 >= d.m) return;
   if (d.vec == 4)
