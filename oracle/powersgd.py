@@ -44,6 +44,12 @@ design notes of the repository):
       scheme works with the usual optimizers), x <- x - lr (D + mu m).
   R10 the first Q, and a cold start's fresh Q every step, is i.i.d. N(0, 1)
       from a seeded counter-based generator (module philox).
+  R11 compound compression ([GLOSS]: the factors PowerSGD produces can
+      themselves be quantised): the two transmitted factors, P before its
+      aggregation and Q before its aggregation, are rounded to bfloat16 from
+      their fp32 values (round to nearest, ties to even); everything after a
+      hook uses the values as received, so the residual, and with it the
+      error memory, carries the quantisation error too.
 """
 from __future__ import annotations
 
@@ -155,22 +161,46 @@ class MatrixResult:
     P: np.ndarray       # P = M Q_warm (after the P hook), before GS
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Payload quantiser of reading R11: the value as the kernels hold it
+    (fp32), rounded to the nearest bfloat16 with ties to even, returned in
+    fp64.  bfloat16 keeps fp32's exponent range and 8 significant bits, so the
+    spacing at |x| in [2^e, 2^(e+1)) is 2^(e-7), and 2^-133 below 2^-126 (the
+    subnormal range); np.rint rounds halves to even.  Finite inputs only."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    out = np.zeros_like(f)
+    nz = f != 0.0
+    e = np.floor(np.log2(np.abs(f[nz])))
+    # guard the binade against log2 rounding at exact powers of two
+    e = np.where(np.abs(f[nz]) < 2.0 ** e, e - 1, e)
+    e = np.where(np.abs(f[nz]) >= 2.0 ** (e + 1), e + 1, e)
+    step = 2.0 ** np.maximum(e - 7, -133)
+    out[nz] = np.rint(f[nz] / step) * step
+    return out
+
+
 def compress_matrix(M: np.ndarray, Q_warm: np.ndarray, hook_p: Hook = None,
-                    hook_q: Hook = None, power_iters: int = 1) -> MatrixResult:
+                    hook_q: Hook = None, power_iters: int = 1,
+                    quantize: Optional[Callable[[np.ndarray], np.ndarray]] = None) -> MatrixResult:
     """One warm-started subspace iteration on M ([N152] Method):
     right multiply P = M Q, aggregate P, orthogonalise to P_hat, left multiply
     Q = M^T P_hat, aggregate Q.  Then the reconstruction P_hat Q^T and the
     error-feedback residual M - P_hat Q^T ([GLOSS] error-feedback paragraph;
     [N152] Concepts, "Error feedback").  power_iters > 1 repeats the
-    iteration from the new Q (reading R8)."""
+    iteration from the new Q (reading R8).  `quantize` (reading R11) is
+    applied to P and to Q as they are formed, before their hooks."""
     M = np.asarray(M, dtype=np.float64)
     Q = np.asarray(Q_warm, dtype=np.float64)
     for _ in range(max(1, power_iters)):
         P = M @ Q
+        if quantize is not None:
+            P = quantize(P)
         if hook_p is not None:
             P = hook_p(P)
         P_hat = gram_schmidt(P)
         Q = M.T @ P_hat
+        if quantize is not None:
+            Q = quantize(Q)
         if hook_q is not None:
             Q = hook_q(Q)
     M_hat = P_hat @ Q.T
@@ -252,7 +282,7 @@ class SetResult:
 
 def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: float = 0.0,
              refresh_iters: int = 0, hook_p: Hook = None, hook_q: Hook = None, power_iters: int = 1,
-             error_feedback: bool = True) -> SetResult:
+             error_feedback: bool = True, quantize: Optional[Callable[[np.ndarray], np.ndarray]] = None) -> SetResult:
     """One compression step over a model's set, updating `state` in place.
 
     Per compressed matrix: X = G (or the momentum u), M = X + E (M = X when
@@ -280,7 +310,7 @@ def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: flo
         Qw = state.Q[i]
         if refresh_iters > 0:
             Qw = refresh(M, Qw, refresh_iters)
-        res = compress_matrix(M, Qw, hook_p, hook_q, power_iters=power_iters)
+        res = compress_matrix(M, Qw, hook_p, hook_q, power_iters=power_iters, quantize=quantize)
         state.E[i] = res.E
         state.Q[i] = res.Q
         Ph.append(res.P_hat)

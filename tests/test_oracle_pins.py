@@ -456,8 +456,8 @@ def test_planted_mistakes_are_caught(monkeypatch):
     st = oracle.init_state(plan, [wl.Q0])
     orig = O.compress_matrix
 
-    def no_ef(Mx, Qw, hp=None, hq=None, power_iters=1):
-        return orig(Mx - st.E[0], Qw, hp, hq, power_iters=power_iters)
+    def no_ef(Mx, Qw, hp=None, hq=None, power_iters=1, quantize=None):
+        return orig(Mx - st.E[0], Qw, hp, hq, power_iters=power_iters, quantize=quantize)
 
     monkeypatch.setattr(O, "compress_matrix", no_ef)
     acc = np.zeros((256, 128))
@@ -636,3 +636,46 @@ def test_seeded_q_layout():
     plan = oracle.Plan([(300, 40), (5,), (2, 2)], 4)
     qs = oracle.init_q_set(plan, 11)
     assert qs[1] is None and qs[2] is None and np.array_equal(qs[0], oracle.init_q(40, 4, 11, 0))
+
+
+# ------------------------------------------------- bfloat16 payload (R11)
+
+def test_round_bf16_matches_torch_conversion():
+    # Library routine: torch's float32 -> bfloat16 conversion (round to
+    # nearest even) on the CPU, over normal, subnormal, tie and carry cases.
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(23)
+    x = np.concatenate([
+        g.standard_normal(20000) * 10.0 ** g.integers(-30, 30, 20000),
+        g.standard_normal(2000) * 1e-39,                       # fp32 subnormals
+        np.array([1.0, -1.0, 2.0 ** -126, 3.0, 0.0, 65280.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8,
+                  -(1.0 + 2 ** -8), 255.5, 2.0 ** -133, 1.5 * 2.0 ** -133, 2.5 * 2.0 ** -133]),
+    ]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(x)
+    assert np.array_equal(got, want)
+
+
+def test_quantised_payload_rounds_both_factors_before_the_hooks():
+    # The hooks see bfloat16-representable factors; the residual is formed
+    # from the received factors, so M_hat + E = M still holds.
+    g = np.random.default_rng(24)
+    M = rand(g, 40, 30)
+    Q0 = rand(g, 30, 3)
+    seen = {}
+
+    def keep(name):
+        def h(X):
+            seen[name] = X.copy()
+            return X
+        return h
+
+    res = oracle.compress_matrix(M, Q0, keep("P"), keep("Q"), quantize=oracle.round_bf16)
+    for name in ("P", "Q"):
+        assert np.array_equal(oracle.round_bf16(seen[name]), seen[name])
+    np.testing.assert_array_equal(seen["P"], oracle.round_bf16(M @ Q0))
+    np.testing.assert_allclose(res.M_hat + res.E, M, rtol=0, atol=1e-14)
+    plain = oracle.compress_matrix(M, Q0)
+    # bfloat16 keeps about 3 significant digits: close to, but not equal to, fp64
+    d = np.linalg.norm(res.M_hat - plain.M_hat) / np.linalg.norm(plain.M_hat)
+    assert 1e-5 < d < 2e-2
