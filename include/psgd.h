@@ -109,6 +109,16 @@ typedef struct psgd_plan* psgd_plan_t;
  */
 #define PSGD_STEP_DEFER_RESIDUAL 4u
 #define PSGD_STEP_RESIDUAL_DEFERRED 8u
+/*
+ * Compound compression ([GLOSS]: the factors can themselves be quantised):
+ * P and Q are rounded to bfloat16 values (nearest, ties to even; kept in the
+ * fp32 buffers) as soon as they are formed, before their hooks, so a hook can
+ * send them as bfloat16 without further loss, halving the exchanged bytes.
+ * Everything after a hook uses the factors as received: the residual, and
+ * with it the error memory, carries the quantisation error.  The
+ * pass-through values in the P buffer are not rounded.
+ */
+#define PSGD_STEP_PAYLOAD_BF16 16u
 
 /*
  * Options of one psgd_compress call; a NULL pointer means all defaults.
@@ -125,7 +135,8 @@ typedef struct psgd_plan* psgd_plan_t;
  *                  Q <- GS(M^T GS(M Q)), before P = M Q.  The caller chooses
  *                  the period (for example every 50th step).
  *   flags          any of PSGD_STEP_NO_ERROR_FEEDBACK, PSGD_STEP_NESTEROV,
- *                  PSGD_STEP_DEFER_RESIDUAL, PSGD_STEP_RESIDUAL_DEFERRED, or 0.
+ *                  PSGD_STEP_DEFER_RESIDUAL, PSGD_STEP_RESIDUAL_DEFERRED,
+ *                  PSGD_STEP_PAYLOAD_BF16, or 0.
  *   params, sgd_buf, sgd_lr, sgd_momentum
  *                  fused post-compression momentum SGD ([N152] Concepts,
  *                  "Post-compression momentum"): when params is non-NULL, the

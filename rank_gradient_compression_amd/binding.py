@@ -33,6 +33,7 @@ PSGD_STEP_NO_ERROR_FEEDBACK = 1
 PSGD_STEP_NESTEROV = 2
 PSGD_STEP_DEFER_RESIDUAL = 4
 PSGD_STEP_RESIDUAL_DEFERRED = 8
+PSGD_STEP_PAYLOAD_BF16 = 16
 
 PSGD_STAGE_EF_P = 0
 PSGD_STAGE_GS = 1

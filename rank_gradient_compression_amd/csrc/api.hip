@@ -252,7 +252,8 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
     return PSGD_ERR_INVALID_ARG;
   }
   constexpr uint32_t kKnownStepFlags =
-      PSGD_STEP_NO_ERROR_FEEDBACK | PSGD_STEP_NESTEROV | PSGD_STEP_DEFER_RESIDUAL | PSGD_STEP_RESIDUAL_DEFERRED;
+      PSGD_STEP_NO_ERROR_FEEDBACK | PSGD_STEP_NESTEROV | PSGD_STEP_DEFER_RESIDUAL | PSGD_STEP_RESIDUAL_DEFERRED |
+      PSGD_STEP_PAYLOAD_BF16;
   if (o.flags & ~kKnownStepFlags) {
     set_error("psgd_compress: unknown step flag bits 0x%x", o.flags & ~kKnownStepFlags);
     return PSGD_ERR_INVALID_ARG;
@@ -279,6 +280,7 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
   const int refresh_iters = o.refresh_iters;
   const int power_iters = o.power_iters > 1 ? o.power_iters : 1;
   const bool ef = (o.flags & PSGD_STEP_NO_ERROR_FEEDBACK) == 0;
+  const bool payload_bf16 = (o.flags & PSGD_STEP_PAYLOAD_BF16) != 0;
   const SgdArgs sg{o.params, o.sgd_buf, o.sgd_lr, o.sgd_momentum, (o.flags & PSGD_STEP_NESTEROV) ? 1 : 0};
   if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_compress")) return s;
   if (!any) return PSGD_OK;
@@ -314,6 +316,8 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
     if (it > 0)
       PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, all_rows, all_pred, 0, nullptr, err, nullptr, q, pbuf, -1),
                   "P = M Q");
+    if (payload_bf16)  // the factors only; pass-through values stay fp32
+      PSGD_LAUNCH(PSGD_STAGE_EF_P, launch_round_bf16(pbuf, (int64_t)p->p_elems, stream), "round P to bfloat16");
     if (hook && hook(pbuf, p->p_elems + p->pt_elems, stream, user) != 0) {
       set_error("psgd_compress: aggregation hook failed on P");
       return PSGD_ERR_HOOK;
@@ -326,6 +330,8 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
       if (e != hipSuccess) return hip_fail(e, "Q = M^T P_hat");
     }
     PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, all_red, q), "Q partial reduction");
+    if (payload_bf16)
+      PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_round_bf16(q, (int64_t)p->q_elems, stream), "round Q to bfloat16");
     if (hook && hook(q, p->q_elems, stream, user) != 0) {
       set_error("psgd_compress: aggregation hook failed on Q");
       return PSGD_ERR_HOOK;

@@ -528,6 +528,32 @@ __global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, c
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
 }
 
+// Payload quantiser: every value rounded to the nearest bfloat16 (ties to
+// even), kept in fp32 storage.  Adding 0x7fff plus the lowest kept bit to the
+// fp32 pattern and clearing the low half rounds the magnitude to 8
+// significant bits with ties to even (a carry moves into the exponent, which
+// is the next binade).  Inf and NaN are left as they are.
+__device__ __forceinline__ float round_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7f800000u) == 0x7f800000u) return x;
+  return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+}
+
+__global__ __launch_bounds__(256) void k_round_bf16(float* __restrict__ buf, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t n4 = n / 4;
+  float4* b4 = reinterpret_cast<float4*>(buf);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    float4 v = b4[i];
+    v.x = round_bf16(v.x);
+    v.y = round_bf16(v.y);
+    v.z = round_bf16(v.z);
+    v.w = round_bf16(v.w);
+    b4[i] = v;
+  }
+  for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) buf[i] = round_bf16(buf[i]);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
@@ -663,6 +689,15 @@ hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_
   if (blocks > 256 * 64) blocks = 256 * 64;
   hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float4*>(dst),
                      reinterpret_cast<const float4*>(src), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_round_bf16(float* buf, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_round_bf16, dim3((unsigned)blocks), dim3(256), 0, stream, buf, n);
   return hipGetLastError();
 }
 

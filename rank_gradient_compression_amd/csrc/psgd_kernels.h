@@ -92,6 +92,9 @@ hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out,
 // ceil(n * rank / 4) over the matrices).
 hipError_t launch_init_q(const LaunchCtx& c, float* Q, uint64_t seed, int64_t max_blocks);
 
+// Round n floats (16-byte aligned) to bfloat16 values in place.
+hipError_t launch_round_bf16(float* buf, int64_t n, hipStream_t stream);
+
 hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);
 
 }  // namespace psgd

@@ -106,12 +106,13 @@ class PowerSGD:
                  refresh_iters: int = 0, power_iters: int = 0, error_feedback: bool = True,
                  params: Optional[torch.Tensor] = None, sgd_buf: Optional[torch.Tensor] = None, sgd_lr: float = 0.0,
                  sgd_momentum: float = 0.0, nesterov: bool = False, defer_residual: bool = False,
-                 residual_deferred: bool = False) -> None:
+                 residual_deferred: bool = False, payload_bf16: bool = False) -> None:
         out = mhat_buf if mhat_buf is not None else (self.mhat if mhat else None)
         opts = None
         flags = (0 if error_feedback else B.PSGD_STEP_NO_ERROR_FEEDBACK) | (B.PSGD_STEP_NESTEROV if nesterov else 0)
         flags |= (B.PSGD_STEP_DEFER_RESIDUAL if defer_residual else 0)
         flags |= (B.PSGD_STEP_RESIDUAL_DEFERRED if residual_deferred else 0)
+        flags |= (B.PSGD_STEP_PAYLOAD_BF16 if payload_bf16 else 0)
         if refresh_iters or power_iters or flags or params is not None:
             opts = B.step_opts(power_iters, refresh_iters, flags, sgd_lr, sgd_momentum, params.data_ptr() if params is not None else 0,
                                sgd_buf.data_ptr() if sgd_buf is not None else 0)

@@ -179,7 +179,7 @@ def _compress(plan, **kw):
     (dict(workspace_bytes=16), B.PSGD_ERR_WORKSPACE),
     (dict(opts=B.step_opts(refresh_iters=-1)), B.PSGD_ERR_INVALID_ARG),
     (dict(opts=B.step_opts(power_iters=-2)), B.PSGD_ERR_INVALID_ARG),
-    (dict(opts=B.step_opts(flags=16)), B.PSGD_ERR_INVALID_ARG),
+    (dict(opts=B.step_opts(flags=32)), B.PSGD_ERR_INVALID_ARG),
     (dict(opts=B.step_opts(flags=B.PSGD_STEP_DEFER_RESIDUAL | B.PSGD_STEP_NO_ERROR_FEEDBACK)),
      B.PSGD_ERR_INVALID_ARG),
     (dict(opts=B.step_opts(flags=B.PSGD_STEP_RESIDUAL_DEFERRED | B.PSGD_STEP_NO_ERROR_FEEDBACK)),
