@@ -553,51 +553,48 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const OrthDesc* __restrict_
   gram[o.t_off + e] = (s0 + s1) + (s2 + s3);
 }
 
-// One workgroup per factor: right-looking Cholesky of A with the dependence
-// rule.  Each thread keeps RP*RP/256 elements of the (symmetric) Schur
-// complement in registers; at step k the pivot row goes through LDS and every
-// thread applies S_ij -= S_ki S_kj / S_kk to its elements.  Row k of R is
-// S_k. / sqrt(S_kk) (zero for a dependent column).  The upper triangle of the
-// factor's A slot is overwritten with R.
+// One wavefront per factor: right-looking Cholesky of A with the dependence
+// rule.  Lane j keeps column j of the (symmetric) Schur complement S in fp64
+// registers; at step k every lane publishes S_kj through LDS, reads the pivot
+// S_kk and the row S_k. back as broadcasts, and updates
+// S_ij -= S_ki S_kj / S_kk for i > k.  Row k of R is S_k. / sqrt(S_kk) (zero
+// for a dependent column, judged against the norm before projection, the
+// original A_kk).  No cross-wavefront barrier, no divergence: the step is a
+// chain of broadcast LDS reads and fp64 FMAs.  The upper triangle of the
+// factor's A slot is overwritten with R (A is read completely first).
 template <int RP>
-__global__ __launch_bounds__(256) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
-                                                    double* __restrict__ gram, float zero_rel) {
-  constexpr int NE = RP * RP / 256;  // elements per thread: e = tid + 256 q
-  __shared__ double row[RP];
-  __shared__ double dg[RP];  // diagonal of A: squared norms before projection
-  __shared__ double rout[RP * RP];
+__global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
+                                                   double* __restrict__ gram, float zero_rel) {
+  __shared__ double rowbuf[RP];
+  __shared__ double dgs[RP];
   const OrthDesc o = descs[first + blockIdx.x];
-  const int tid = threadIdx.x;
+  const int j = threadIdx.x;
+  const bool own = j < RP;
   double* a = gram + o.t_off;
-  double sv[NE];
+  double sc[RP];
 #pragma unroll
-  for (int q = 0; q < NE; ++q) sv[q] = a[tid + 256 * q];
-  if (tid < RP) dg[tid] = a[tid * RP + tid];
-  for (int e = tid; e < RP * RP; e += 256) rout[e] = 0.0;
-  for (int k = 0; k < r; ++k) {
-    __syncthreads();
+  for (int i = 0; i < RP; ++i) sc[i] = own ? a[i * RP + j] : 0.0;
+  if (own) dgs[j] = a[j * RP + j];
+  __syncthreads();
+  // Fully unrolled so that sc[] stays in registers; steps k >= r are skipped
+  // by a uniform branch.
 #pragma unroll
-    for (int q = 0; q < NE; ++q) {
-      const int e = tid + 256 * q;
-      if (e / RP == k) row[e % RP] = sv[q];
-    }
-    __syncthreads();
-    const double d = row[k];
-    const double nu0 = sqrt(dg[k]);  // norm before projection
-    const double nv = d > 0.0 ? sqrt(d) : 0.0;
-    const bool zero = !(nu0 > 0.0) || nv <= (double)zero_rel * nu0;
-    const double inv = zero ? 0.0 : 1.0 / nv;
-    if (tid < r && tid >= k) rout[k * RP + tid] = tid == k ? (zero ? 0.0 : nv) : row[tid] * inv;
-    const double inv2 = inv * inv;
+  for (int k = 0; k < RP; ++k) {
+    if (k < r) {
+      if (own) rowbuf[j] = sc[k];
+      __syncthreads();
+      const double d = rowbuf[k];
+      const double nu0 = sqrt(dgs[k]);
+      const double nv = d > 0.0 ? sqrt(d) : 0.0;
+      const bool zero = !(nu0 > 0.0) || nv <= (double)zero_rel * nu0;
+      const double inv = zero ? 0.0 : 1.0 / nv;
+      const double c = sc[k] * (inv * inv);  // S_kj / S_kk
+      if (own && j >= k && j < r) a[k * RP + j] = j == k ? (zero ? 0.0 : nv) : sc[k] * inv;
 #pragma unroll
-    for (int q = 0; q < NE; ++q) {
-      const int e = tid + 256 * q;
-      const int i = e / RP, j = e % RP;
-      if (i > k && j > k && i < r && j < r) sv[q] = fma(-row[i] * inv2, row[j], sv[q]);
+      for (int i = k + 1; i < RP; ++i) sc[i] = fma(-rowbuf[i], c, sc[i]);
+      __syncthreads();  // rowbuf is rewritten at the next step
     }
   }
-  __syncthreads();
-  for (int e = tid; e < RP * RP; e += 256) a[e] = rout[e];
 }
 
 // P_hat = P R^-1, one row per thread: x R = p by forward substitution,
@@ -745,7 +742,7 @@ static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const i
                      c.gram);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(256), 0, c.stream, c.orth, first, c.rank, c.gram,
+  hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(64), 0, c.stream, c.orth, first, c.rank, c.gram,
                      kZeroColumnRel);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
