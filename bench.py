@@ -19,7 +19,6 @@ gradient GB compressed per second (4 bytes x elements / step time).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -51,35 +50,31 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the plain-compress and momentum figures")
     ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--residual", default="explicit", choices=["explicit", "deferred"],
+                    help="7B workload: time the step that writes E (default) or the steady-state step with the "
+                         "residual deferred into the next step's first pass")
     return ap.parse_args()
-
-
-def source_hash():
-    csrc = os.path.join(ROOT, "rank_gradient_compression_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, profile):
     """HBM bytes per launch of `kernel` from a committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary, or None when there is none or the
-    library sources changed since the counters were taken."""
+    kernel's source changed since the counters were taken."""
+    from rank_gradient_compression_amd.profile_summary import source_hash
+
     path = os.path.join(ROOT, "profiles", profile)
     try:
         text = open(path).read()
         blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
         return None
-    if blob.get("source_hash") != source_hash():
+    # the most-launched instantiation of the kernel in the profiled run
+    hits = [v for name, v in blob["kernels"].items()
+            if name.split("<")[0].split()[-1] == kernel and v.get("source_hash") == source_hash(name)]
+    if not hits:
         return None
-    for name, v in blob["kernels"].items():
-        if kernel in name:
-            return v["read_bytes"] + v["write_bytes"]
-    return None
+    v = max(hits, key=lambda h: h.get("launches", 0))
+    return v["read_bytes"] + v["write_bytes"]
 
 
 def stage_table(B, plan, bytes_per_el, flops_per_el, elems):
@@ -190,12 +185,15 @@ def base_result(args, value, ms_step, per, workload, extra):
             "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg}
 
 
-def step_bytes(rank_mfma, momentum=False, mhat=True):
-    b = {"ef_p": 20.0 if momentum else 12.0, "mtp": 4.0, "residual": 12.0 if mhat else 8.0}
-    return b
+def step_bytes(rank_mfma, momentum=False, mhat=True, deferred=False):
+    if deferred:  # pass 1 rebuilds E from M_prev; the last pass only writes M_hat
+        return {"ef_p": 20.0 if momentum else 12.0, "mtp": 4.0, "residual": 4.0}
+    return {"ef_p": 20.0 if momentum else 12.0, "mtp": 4.0, "residual": 12.0 if mhat else 8.0}
 
 
-def step_flops(r, momentum=False):
+def step_flops(r, momentum=False, deferred=False):
+    if deferred:
+        return {"ef_p": 4.0 * r + (4.0 if momentum else 2.0), "mtp": 2.0 * r, "residual": 2.0 * r}
     return {"ef_p": 2.0 * r + (3.0 if momentum else 1.0), "mtp": 2.0 * r, "residual": 2.0 * r + 1.0}
 
 
@@ -215,20 +213,33 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
     torch.cuda.synchronize()
     log(f"bench: {dense} synthetic gradient elements ready in {time.time() - t0:.1f} s")
     copy_gbs = R.copy_ceiling()
-    ms, per = R.time("compress + fused decompress", lambda: ps.compress(mhat=True), args.steps, args.warmup,
-                     plan=None if args.no_stage_timing else ps.plan)
+    deferred = args.residual == "deferred"
+    if deferred:
+        ps.compress(mhat=True, defer_residual=True)  # leaves M in err: the steady state below
+
+        def step():
+            ps.compress(mhat=True, defer_residual=True, residual_deferred=True)
+    else:
+        def step():
+            ps.compress(mhat=True)
+    ms, per = R.time("compress + fused decompress" + (" (deferred residual)" if deferred else ""), step, args.steps,
+                     args.warmup, plan=None if args.no_stage_timing else ps.plan)
     mfma = rank > 8
+    bpe = 20.0 if deferred else 28.0
     res = base_result(args, 4.0 * dense / (ms * 1e-3) / 1e9, ms, per,
                       f"7B-shaped gradient set: {len(shapes)} fp32 matrices, {dense} elements, rank {rank}, "
-                      "compress with fused decompression (EF+P+Q+E+M_hat)",
-                      {"rank": rank, "matrices": len(shapes), "elements": dense, "alg_bytes_per_step": 28.0 * dense,
-                       "step_hbm_frac": round(28.0 * dense / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "compress with fused decompression (EF+P+Q+E+M_hat)"
+                      + (", residual deferred into the next step's first pass" if deferred else ""),
+                      {"rank": rank, "matrices": len(shapes), "elements": dense, "residual": args.residual,
+                       "alg_bytes_per_step": bpe * dense,
+                       "step_hbm_frac": round(bpe * dense / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                        "copy_ceiling_gbs": round(copy_gbs, 1)})
     if not args.no_stage_timing:
-        st = stage_table(B, ps.plan, step_bytes(mfma), step_flops(rank), dense)
-        res["roofline"] = roofline_of(st, mfma, "hbm_bytes_llama7b_r4_fused.md" if rank == 4 else None)
+        st = stage_table(B, ps.plan, step_bytes(mfma, deferred=deferred), step_flops(rank, deferred=deferred), dense)
+        prof = f"hbm_bytes_llama7b_r4_{'deferred' if deferred else 'fused'}.md" if rank == 4 else None
+        res["roofline"] = roofline_of(st, mfma, prof)
         res["stages"] = round_stages(st)
-    if not args.no_variants:
+    if not args.no_variants and not deferred:
         ms_c, _ = R.time("compress only", lambda: ps.compress(mhat=False), max(3, args.steps // 2), 1,
                          per_step=False)
         res["config"]["compress_only"] = {"ms_per_step": round(ms_c, 4),

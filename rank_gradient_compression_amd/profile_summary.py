@@ -1,0 +1,119 @@
+"""Short markdown summaries of rocprofv3 output for the library's kernels.
+
+    python -m rank_gradient_compression_amd.profile_summary trace STATS_CSV "COMMAND" "TITLE"
+    python -m rank_gradient_compression_amd.profile_summary bytes FETCH_CSV WRITE_CSV "CMD_FETCH" "CMD_WRITE" "TITLE"
+
+`trace` reads a `--kernel-trace --stats` kernel_stats.csv; `bytes` reads the
+counter_collection.csv of one `--pmc FETCH_SIZE` run and one `--pmc
+WRITE_SIZE` run of the same program.  The byte counters are calibrated with
+the library's 16-byte copy kernel over 4 GiB (`psgd_stream_copy`, which the
+benchmark runs first): each counter is scaled so that the copy reads and
+writes exactly 4 GiB.  The machine-readable block records, per kernel, the
+scaled bytes per launch and a hash of the source file that defines the kernel
+(with the shared headers), so a reader can tell when the counters no longer
+describe the code.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+SHARED_HEADERS = ("psgd_kernels.h", "psgd_tables.h")
+COPY_BYTES = 4 * (1 << 30)
+
+
+def source_file(kernel: str) -> str:
+    """The source file that defines a library kernel (by its name)."""
+    k = kernel.replace("psgd::", "")
+    if k.startswith(("k_mfma", "k_psum", "k_gram", "k_apply")) or "k_mfma" in k or "k_gram" in k:
+        return "kernels_mfma.hip"
+    if "k_init_q" in k:
+        return "kernels_rng.hip"
+    return "kernels_valu.hip"
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in (source_file(kernel),) + SHARED_HEADERS:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short(k: str) -> str:
+    k = k.replace("psgd::", "")
+    i = k.find("(")
+    return k[:i] if i > 0 else k
+
+
+def trace(stats_csv: str, cmd: str, title: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = [f"# {title}\n", "Command:\n", f"```\n{cmd}\n```\n",
+           "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        if "psgd" not in r["Name"]:
+            continue
+        out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    out.append(f"\nSummarised from `{os.path.basename(stats_csv)}` by "
+               "`python -m rank_gradient_compression_amd.profile_summary trace`.")
+    return "\n".join(out) + "\n"
+
+
+def _counters(path: str, counter: str):
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def hbm_bytes(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, title: str) -> str:
+    f = _counters(fetch_csv, "FETCH_SIZE")
+    w = _counters(write_csv, "WRITE_SIZE")
+    copy = [k for k in f if "k_stream_copy" in k][0]
+    ff = COPY_BYTES / 1024 / statistics.mean(f[copy])
+    wf = COPY_BYTES / 1024 / statistics.mean(w[copy])
+    out = [f"# {title}\n", "Commands (one counter per run):\n", f"```\n{cmd_f}\n{cmd_w}\n```\n",
+           f"Calibration: `k_stream_copy` over 4 GiB (reads 4 GiB, writes 4 GiB) reads FETCH_SIZE = "
+           f"{statistics.mean(f[copy]):.4g} KiB and WRITE_SIZE = {statistics.mean(w[copy]):.4g} KiB per launch, so "
+           f"FETCH_SIZE is scaled by {ff:.3f} and WRITE_SIZE by {wf:.3f} below.\n",
+           "| kernel | launches | FETCH_SIZE (KiB, raw) | WRITE_SIZE (KiB, raw) | read GB (scaled) | write GB (scaled) |",
+           "|---|---|---|---|---|---|"]
+    blob = {}
+    for k in f:
+        if "psgd" not in k or k == copy:
+            continue
+        fr = statistics.mean(f[k])
+        wr = statistics.mean(w.get(k, [0.0]))
+        out.append(f"| `{short(k)}` | {len(f[k])} | {fr:.6g} | {wr:.6g} | {fr * ff * 1024 / 1e9:.3f} | "
+                   f"{wr * wf * 1024 / 1e9:.3f} |")
+        blob[short(k)] = {"launches": len(f[k]), "read_bytes": fr * ff * 1024, "write_bytes": wr * wf * 1024,
+                          "source": source_file(k), "source_hash": source_hash(k)}
+    out.append("\nMachine-readable (per launch, scaled bytes; `source_hash` = sha256 prefix of the kernel's source "
+               "file and the shared headers when the counters were taken):\n")
+    out.append("```json\n" + json.dumps({"fetch_scale": ff, "write_scale": wf, "kernels": blob}) + "\n```")
+    out.append("\nSummarised from the two runs' `counter_collection.csv` by "
+               "`python -m rank_gradient_compression_amd.profile_summary bytes`.")
+    return "\n".join(out) + "\n"
+
+
+def main(argv) -> int:
+    if len(argv) >= 5 and argv[1] == "trace":
+        sys.stdout.write(trace(argv[2], argv[3], argv[4]))
+        return 0
+    if len(argv) >= 7 and argv[1] == "bytes":
+        sys.stdout.write(hbm_bytes(*argv[2:7]))
+        return 0
+    sys.stderr.write(__doc__)
+    return 2
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))
