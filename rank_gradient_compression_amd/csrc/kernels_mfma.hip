@@ -125,7 +125,7 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
   const int rb = local / d.s1, split = local - rb * d.s1;
   const int c_begin = split * d.s1_cols;
   const int c_end = min(n, c_begin + d.s1_cols);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
   const int i0 = rb * kMfmaRows + wave * 16;
   const int row = i0 + li;
@@ -137,27 +137,55 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
 #pragma unroll
   for (int T = 0; T < RP / 16; ++T) acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // Raw loads of one 64-column step (G, E and u as the mode needs).  At rank
+  // 16 the next step's loads are issued before the current step's EF-add, Q
+  // staging and matrix products, so two steps of loads are in flight per
+  // wavefront (measured: 6% faster there; neutral or slower at higher ranks
+  // and for the plain M Q of the refresh, where it is left out).
+  constexpr bool PREFETCH = MODE != 0 && RP <= 16;
+  constexpr bool LOAD_G = MODE != 0;
+  constexpr bool LOAD_E = MODE <= 2;
+  constexpr bool MOM = MODE == 2 || MODE == 4;
+  struct Step {
+    float4 g[4], e[4], u[4];
+  };
+  auto load = [&](int c0, Step& st) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int col = c0 + 16 * qq + 4 * ls;
+      const bool col_ok = col < c_end;
+      if constexpr (LOAD_G) {
+        if constexpr (GBF16)
+          st.g[qq] = ldq_bf16<VEC4>(static_cast<const uint16_t*>(G) + roff, col, col_ok, c_begin, n);
+        else
+          st.g[qq] = ldq<VEC4>(static_cast<const float*>(G) + roff, col, col_ok, c_begin, n);
+      }
+      if constexpr (LOAD_E) st.e[qq] = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
+      if constexpr (MOM) st.u[qq] = ldq<VEC4>(U + roff, col, col_ok, c_begin, n);
+    }
+  };
+
+  Step cur, nxt;
+  if (PREFETCH && c_begin < c_end) load(c_begin, cur);
   for (int c0 = c_begin; c0 < c_end; c0 += 64) {
-    // M loads (and the EF-add write-back) are issued before the barriers of
-    // the Q staging so that both latencies overlap.
+    if constexpr (PREFETCH) {
+      if (c0 + 64 < c_end) load(c0 + 64, nxt);
+    } else {
+      load(c0, cur);
+    }
     float4 x[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int col = c0 + 16 * qq + 4 * ls;
       const bool col_ok = col < c_end;
       if constexpr (MODE == 0) {
-        x[qq] = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
+        x[qq] = cur.e[qq];
       } else {
-        constexpr bool LOAD_E = MODE <= 2;
-        float4 g;
-        if constexpr (GBF16)
-          g = ldq_bf16<VEC4>(static_cast<const uint16_t*>(G) + roff, col, col_ok, c_begin, n);
-        else
-          g = ldq<VEC4>(static_cast<const float*>(G) + roff, col, col_ok, c_begin, n);
-        const float4 e = LOAD_E ? ldq<VEC4>(E + roff, col, col_ok, c_begin, n) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 g = cur.g[qq];
+        const float4 e = LOAD_E ? cur.e[qq] : make_float4(0.f, 0.f, 0.f, 0.f);
         float4 s;
-        if constexpr (MODE == 2 || MODE == 4) {
-          float4 u = ldq<VEC4>(U + roff, col, col_ok, c_begin, n);
+        if constexpr (MOM) {
+          float4 u = cur.u[qq];
           u.x = fmaf(beta, u.x, g.x);
           u.y = fmaf(beta, u.y, g.y);
           u.z = fmaf(beta, u.z, g.z);
@@ -190,6 +218,7 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
         for (int T = 0; T < RP / 16; ++T) acc[T] = mfma16x16x4(a, qrow[16 * T], acc[T]);
       }
     }
+    if constexpr (PREFETCH) cur = nxt;
   }
 
   // Results leave through LDS so that each store instruction writes
@@ -255,23 +284,37 @@ __global__ __launch_bounds__(kRedCols) void k_psum(const MatDesc* __restrict__ m
 // ---------------------------------------------------------------------------
 // Pass 2: Q = M^T P_hat over one row block (partials when the matrix has
 // several row blocks)
+//
+// A workgroup owns 64 columns of one row block; its four wavefronts take
+// interleaved 64-row chunks of the block and are combined in LDS at the end
+// (in wavefront order).  The summation index of matrix-core step kk of a
+// chunk is bound, for lane (li, ls), to row
+//   rho(kk, ls) = ib + 16 (kk / 4) + 4 ls + kk % 4,
+// so that lane holds columns 4 li .. 4 li + 3 of those rows (one 16-byte load
+// per row; each load instruction covers four rows of 256 bytes) and its B
+// operands P_hat[rho][16 T + li] for kk = 4 qq .. 4 qq + 3 are four
+// consecutive rows of one P_hat column: one 16-byte load, and the four lanes
+// ls together read 64 contiguous bytes of that column.  No LDS staging and
+// no barrier inside the row loop.
 // ---------------------------------------------------------------------------
 
 template <int RP, bool VEC4>
 __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, const float* __restrict__ M,
                                              const float* __restrict__ Ph, int64_t ph_fixed, float* __restrict__ Q,
-                                             float* __restrict__ part, float* Ps, float* Os) {
-  constexpr int PS = RP == 16 ? 16 : 80;  // LDS row stride: conflict-free B-operand reads
+                                             float* __restrict__ part, float* red) {
+  constexpr int RS = 65;  // LDS row stride of the [rank][64 columns] reduction tile
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_mtp0;
   const int rb = local / d.ncb, cb = local - rb * d.ncb;
   const int i0 = rb * d.rb_rows;
   const int i1 = min(m, i0 + d.rb_rows);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
-  const int j0 = cb * kMfmaCols + wave * 64;
-  const int col = j0 + 4 * li;
+  const int cbase = cb * 64;
+  const int col = cbase + 4 * li;
+  const bool col_ok = col < n;
   const float* ph = Ph + (ph_fixed >= 0 ? ph_fixed : d.p_off);
+  const bool ph4 = (m & 3) == 0;  // P_hat columns start 16-byte aligned
 
   v4f acc[4][RP / 16];
 #pragma unroll
@@ -279,54 +322,67 @@ __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, co
 #pragma unroll
     for (int T = 0; T < RP / 16; ++T) acc[v][T] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int ib = i0; ib < i1; ib += 64) {
-    // M loads first: they overlap the P_hat staging below.
+  for (int ib = i0 + 64 * wave; ib < i1; ib += 256) {
     float4 x[16];
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      const int rrow = ib + 4 * kk + ls;
-      const bool ok = rrow < i1 && col < n;
-      x[kk] = ldq<VEC4>(M + d.off + (int64_t)(rrow < i1 ? rrow : i0) * n, col, ok, 0, n);
+      const int rr = ib + 16 * (kk >> 2) + 4 * ls + (kk & 3);
+      const bool ok = rr < i1 && col_ok;
+      x[kk] = ldq<VEC4>(M + d.off + (int64_t)(rr < i1 ? rr : i0) * n, col, ok, 0, n);
     }
-    lds_barrier();  // previous chunk's reads of Ps are done
-    for (int e = threadIdx.x; e < 64 * RP; e += 256) {
-      const int k = e & 63, t = e >> 6;
-      float v = 0.f;
-      if (t < r && ib + k < i1) v = ph[(int64_t)t * m + ib + k];
-      Ps[k * PS + t] = v;
-    }
-    lds_barrier();
+    float4 pb[RP / 16][4];
+#pragma unroll
+    for (int T = 0; T < RP / 16; ++T)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int t = 16 * T + li, r0 = ib + 16 * qq + 4 * ls;
+        const float* pp = ph + (int64_t)(t < r ? t : 0) * m + r0;
+        if (t < r && ph4 && r0 + 3 < i1) {
+          pb[T][qq] = *reinterpret_cast<const float4*>(pp);
+        } else {
+          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (t < r) {
+            if (r0 < i1) v.x = pp[0];
+            if (r0 + 1 < i1) v.y = pp[1];
+            if (r0 + 2 < i1) v.z = pp[2];
+            if (r0 + 3 < i1) v.w = pp[3];
+          }
+          pb[T][qq] = v;
+        }
+      }
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const float xv[4] = {x[kk].x, x[kk].y, x[kk].z, x[kk].w};
-      const float* prow = &Ps[(4 * kk + ls) * PS + li];
 #pragma unroll
       for (int T = 0; T < RP / 16; ++T) {
-        const float b = prow[16 * T];
+        const float4 pq = pb[T][kk >> 2];
+        const float b = (kk & 3) == 0 ? pq.x : (kk & 3) == 1 ? pq.y : (kk & 3) == 2 ? pq.z : pq.w;
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[v][T] = mfma16x16x4(xv[v], b, acc[v][T]);
       }
     }
   }
 
-  // Results leave through LDS so that each store instruction writes
-  // consecutive columns of one Q column (rank index).
-  float* out = d.nrb > 1 ? part + d.part_off + (int64_t)rb * r * n : Q + d.q_off;
-  constexpr int OS = kMfmaCols + 1;
-  const int cbase = cb * kMfmaCols;
+  // Wavefront partials summed in LDS in wavefront order.  acc[v][T][e] of
+  // lane (li, ls) is Q[cbase + 4 (4 ls + e) + v][16 T + li].
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
 #pragma unroll
-  for (int T = 0; T < RP / 16; ++T) {
-    __syncthreads();
+      for (int T = 0; T < RP / 16; ++T)
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Os[li * OS + wave * 64 + 4 * (4 * ls + e) + v] = acc[v][T][e];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * kMfmaCols; idx += 256) {
-      const int tl = idx / kMfmaCols, cl = idx % kMfmaCols;
-      const int t = 16 * T + tl, c = cbase + cl;
-      if (t < r && c < n) out[(int64_t)t * n + c] = Os[tl * OS + cl];
+          for (int e = 0; e < 4; ++e) {
+            float* slot = &red[(16 * T + li) * RS + 4 * (4 * ls + e) + v];
+            *slot = w == 0 ? acc[v][T][e] : *slot + acc[v][T][e];
+          }
     }
+    __syncthreads();
+  }
+  float* out = d.nrb > 1 ? part + d.part_off + (int64_t)rb * r * n : Q + d.q_off;
+  for (int idx = threadIdx.x; idx < RP * 64; idx += 256) {
+    const int t = idx >> 6, c = idx & 63;
+    if (t < r && cbase + c < n) out[(int64_t)t * n + cbase + c] = red[t * RS + c];
   }
 }
 
@@ -335,16 +391,14 @@ __global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mat
                                                  int wg_base, int r, const float* __restrict__ M,
                                                  const float* __restrict__ Ph, int64_t ph_fixed,
                                                  float* __restrict__ Q, float* __restrict__ part) {
-  constexpr int PS = RP == 16 ? 16 : 80;
-  __shared__ float Ps[64 * PS];
-  __shared__ float Os[16 * (kMfmaCols + 1)];
+  __shared__ float red[RP * 65];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
   if (d.vec == 4)
-    mfma_qt_body<RP, true>(d, wg, r, M, Ph, ph_fixed, Q, part, Ps, Os);
+    mfma_qt_body<RP, true>(d, wg, r, M, Ph, ph_fixed, Q, part, red);
   else
-    mfma_qt_body<RP, false>(d, wg, r, M, Ph, ph_fixed, Q, part, Ps, Os);
+    mfma_qt_body<RP, false>(d, wg, r, M, Ph, ph_fixed, Q, part, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -363,7 +417,7 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
   const int rb = local / d.s1, split = local - rb * d.s1;
   const int c_begin = split * d.s1_cols;
   const int c_end = min(n, c_begin + d.s1_cols);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
   const int i0 = rb * kMfmaRows;
   const float* ph = Ph + d.p_off;
@@ -379,43 +433,57 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
       bfr[rt][kk] = (rr < m && t < r) ? ph[(int64_t)t * m + rr] : 0.f;
     }
 
-  for (int j0 = c_begin + 16 * wave; j0 < c_end; j0 += 64) {
-    // A operand: Q, lane (li, ls) holds Q[j0 + li][4 kk + ls]
+  // Operands of one 16-column step: A = Q (lane (li, ls) holds
+  // Q[j0 + li][4 kk + ls]) and the matching row segments of M and of the SGD
+  // state.  The next step's loads are issued before the current step's matrix
+  // products and stores, so every wavefront keeps two steps of loads in flight.
+  struct Step {
     float afr[KS];
+    float4 xm[4], xx[4], xb[4];
+  };
+  auto load = [&](int j0, Step& st) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int t = 4 * kk + ls, c = j0 + li;
-      afr[kk] = (t < r && c < c_end) ? q[(int64_t)t * n + c] : 0.f;
+      st.afr[kk] = (t < r && c < c_end) ? q[(int64_t)t * n + c] : 0.f;
     }
     const int col = j0 + 4 * ls;
     const bool col_ok = col < c_end;
-    float4 xm[4], xx[4], xb[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int rr = i0 + 16 * rt + li;
       const int64_t ro = d.off + (int64_t)min(rr, m - 1) * n;
-      if constexpr (READ_M) xm[rt] = ldq<VEC4>(E + ro, col, rr < m && col_ok, c_begin, n);
+      if constexpr (READ_M) st.xm[rt] = ldq<VEC4>(E + ro, col, rr < m && col_ok, c_begin, n);
       if constexpr (SGD) {
-        xx[rt] = ldq<VEC4>(sg.x + ro, col, rr < m && col_ok, c_begin, n);
-        xb[rt] = ldq<VEC4>(sg.m + ro, col, rr < m && col_ok, c_begin, n);
+        st.xx[rt] = ldq<VEC4>(sg.x + ro, col, rr < m && col_ok, c_begin, n);
+        st.xb[rt] = ldq<VEC4>(sg.m + ro, col, rr < m && col_ok, c_begin, n);
       }
     }
+  };
+
+  Step cur, nxt;
+  int j0 = c_begin + 16 * wave;
+  if (j0 < c_end) load(j0, cur);
+  for (; j0 < c_end; j0 += 64) {
+    if (j0 + 64 < c_end) load(j0 + 64, nxt);
+    const int col = j0 + 4 * ls;
+    const bool col_ok = col < c_end;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) acc = mfma16x16x4(afr[kk], bfr[rt][kk], acc);
+      for (int kk = 0; kk < KS; ++kk) acc = mfma16x16x4(cur.afr[kk], bfr[rt][kk], acc);
       const int rr = i0 + 16 * rt + li;
       if (rr < m && col_ok) {
         float* rowp = E + d.off + (int64_t)rr * n;
         const float4 mh = make_float4(acc[0], acc[1], acc[2], acc[3]);
         if constexpr (READ_M && WRITE_E) {
-          const float4 x = xm[rt];
+          const float4 x = cur.xm[rt];
           stq<VEC4>(rowp, col, n, make_float4(x.x - mh.x, x.y - mh.y, x.z - mh.z, x.w - mh.w));
         }
         if constexpr (WRITE_MHAT) stq<VEC4>(Mhat + d.off + (int64_t)rr * n, col, n, mh);
         if constexpr (SGD) {
-          float4 mm = xb[rt], xp = xx[rt];
+          float4 mm = cur.xb[rt], xp = cur.xx[rt];
           mm.x = fmaf(sg.mu, mm.x, mh.x);
           mm.y = fmaf(sg.mu, mm.y, mh.y);
           mm.z = fmaf(sg.mu, mm.z, mh.z);
@@ -436,6 +504,7 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
         }
       }
     }
+    cur = nxt;
   }
 }
 
