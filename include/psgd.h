@@ -93,7 +93,7 @@ typedef struct psgd_plan* psgd_plan_t;
 #define PSGD_STEP_NESTEROV 2u          /* fused SGD steps along D + sgd_momentum * m
                                           (Nesterov form) instead of m */
 /*
- * Deferred residual (vector-ALU ranks, rank <= 8; error feedback on).  The
+ * Deferred residual (error feedback on).  The
  * residual E = M - P_hat Q^T ([GLOSS], error-feedback paragraph) is only read
  * by the next step's EF-add, so it need not be stored: with
  * PSGD_STEP_DEFER_RESIDUAL the call leaves M itself in `err` (P_hat and Q of
@@ -271,8 +271,7 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  * Errors: PSGD_ERR_INVALID_ARG for null or not 16-byte aligned buffers, a
  * missing or unexpected `mom`, negative iteration counts, `params` without
  * `sgd_buf` (or misaligned), unknown step flags, deferred-residual flags
- * without error feedback; PSGD_ERR_UNSUPPORTED for deferred-residual flags
- * at ranks above 8; PSGD_ERR_WORKSPACE;
+ * without error feedback; PSGD_ERR_WORKSPACE;
  * PSGD_ERR_HOOK if a hook
  * returns non-zero (no later stage is enqueued); PSGD_ERR_HIP.
  */

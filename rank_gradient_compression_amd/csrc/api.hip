@@ -264,10 +264,6 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
     set_error("psgd_compress: a deferred residual needs error feedback");
     return PSGD_ERR_INVALID_ARG;
   }
-  if ((defer_out || defer_in) && p->rank > kValuMaxRank) {
-    set_error("psgd_compress: the deferred residual is implemented for ranks up to %d", kValuMaxRank);
-    return PSGD_ERR_UNSUPPORTED;
-  }
   if ((o.params != nullptr) != (o.sgd_buf != nullptr) || !aligned16(o.params) || !aligned16(o.sgd_buf)) {
     set_error("psgd_compress: params and sgd_buf must be given together, 16-byte aligned");
     return PSGD_ERR_INVALID_ARG;

@@ -111,14 +111,21 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 // ---------------------------------------------------------------------------
 // Pass 1: P = M Q (MODE 0: M read as is; 1: M = G + E stored over E;
 // 2: u = beta u + G, M = u + E; 3: M = G; 4: u = beta u + G, M = u --
-// modes 3 and 4 without error feedback, M still stored over E)
+// modes 3 and 4 without error feedback, M still stored over E; 5 and 6: as 1
+// and 2 with a deferred residual, E = E_in - Pold Q^T formed here)
+//
+// With a deferred residual the reconstruction of a 16 x 16 tile is the same
+// sequence of matrix-core steps as in the residual pass (A = Q, B = P_hat^T,
+// summed over the rank in order), and its result layout -- lane (li, ls)
+// holds row li, columns 4 ls .. 4 ls + 3 -- is the layout this pass loads M
+// in, so E is formed bit for bit as the residual pass would have stored it.
 // ---------------------------------------------------------------------------
 
 template <int RP, int MODE, bool VEC4, bool GBF16>
 __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
                                             float* __restrict__ E, float* __restrict__ U, float beta,
-                                            const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed,
-                                            float* __restrict__ ppart, float* Qs) {
+                                            const float* __restrict__ Q, float* P, int64_t p_fixed,
+                                            float* __restrict__ ppart, float* Qs, const float* Pold) {
   constexpr int QS = RP + 4;  // LDS row stride: conflict-free B-operand reads
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_rows0;
@@ -144,8 +151,21 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
   // and for the plain M Q of the refresh, where it is left out).
   constexpr bool PREFETCH = MODE != 0 && RP <= 16;
   constexpr bool LOAD_G = MODE != 0;
-  constexpr bool LOAD_E = MODE <= 2;
-  constexpr bool MOM = MODE == 2 || MODE == 4;
+  constexpr bool DEFERRED = MODE >= 5;
+  constexpr bool LOAD_E = MODE <= 2 || DEFERRED;
+  constexpr bool MOM = MODE == 2 || MODE == 4 || MODE == 6;
+  constexpr int KS = RP / 4;
+  // Deferred residual: B operand P_hat_old^T of this wavefront's 16 rows,
+  // lane (li, ls) holding Pold[row][4 kk + ls] (read before any P is written).
+  float bfr[DEFERRED ? KS : 1];
+  if constexpr (DEFERRED) {
+    const float* po = Pold + d.p_off;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int t = 4 * kk + ls;
+      bfr[kk] = (row_ok && t < r) ? po[(int64_t)t * m + row] : 0.f;
+    }
+  }
   struct Step {
     float4 g[4], e[4], u[4];
   };
@@ -173,6 +193,29 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
     } else {
       load(c0, cur);
     }
+    auto stage_q = [&]() {
+      lds_barrier();  // previous step's reads of Qs are done
+      for (int e = threadIdx.x; e < 64 * RP; e += 256) {
+        const int c = e & 63, t = e >> 6;
+        float v = 0.f;
+        if (t < r && c0 + c < c_end) v = q[(int64_t)t * n + c0 + c];
+        Qs[c * QS + t] = v;
+      }
+      lds_barrier();
+    };
+    float4 mh[DEFERRED ? 4 : 1];
+    if constexpr (DEFERRED) {
+      // Q first: the reconstruction of the previous step needs it before the
+      // EF-add; A = Q[c0 + 16 qq + li][4 kk + ls] from the staged tile.
+      stage_q();
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        v4f a4 = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) a4 = mfma16x16x4(Qs[(16 * qq + li) * QS + 4 * kk + ls], bfr[kk], a4);
+        mh[qq] = make_float4(a4[0], a4[1], a4[2], a4[3]);
+      }
+    }
     float4 x[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
@@ -182,7 +225,9 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
         x[qq] = cur.e[qq];
       } else {
         const float4 g = cur.g[qq];
-        const float4 e = LOAD_E ? cur.e[qq] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 e = LOAD_E ? cur.e[qq] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (DEFERRED)
+          e = make_float4(e.x - mh[qq].x, e.y - mh[qq].y, e.z - mh[qq].z, e.w - mh[qq].w);
         float4 s;
         if constexpr (MOM) {
           float4 u = cur.u[qq];
@@ -199,14 +244,7 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
         x[qq] = s;
       }
     }
-    lds_barrier();  // previous step's reads of Qs are done
-    for (int e = threadIdx.x; e < 64 * RP; e += 256) {
-      const int c = e & 63, t = e >> 6;
-      float v = 0.f;
-      if (t < r && c0 + c < c_end) v = q[(int64_t)t * n + c0 + c];
-      Qs[c * QS + t] = v;
-    }
-    lds_barrier();
+    if constexpr (!DEFERRED) stage_q();
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const float xv[4] = {x[qq].x, x[qq].y, x[qq].z, x[qq].w};
@@ -246,8 +284,8 @@ template <int RP, int MODE, bool GBF16>
 __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
                                                 int wg_base, int r, const void* __restrict__ G,
                                                 float* __restrict__ E, float* __restrict__ U, float beta,
-                                                const float* __restrict__ Q, float* __restrict__ P, int64_t p_fixed,
-                                                float* __restrict__ ppart) {
+                                                const float* __restrict__ Q, float* P, int64_t p_fixed,
+                                                float* __restrict__ ppart, const float* Pold) {
   constexpr int QS = RP + 4;
   static_assert(16 * (kMfmaRows + 1) <= 64 * QS, "output staging does not fit");
   __shared__ float Qs[64 * QS];
@@ -255,9 +293,9 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
   if (d.vec == 4)
-    mfma_p_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs);
+    mfma_p_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs, Pold);
   else
-    mfma_p_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs);
+    mfma_p_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs, Pold);
 }
 
 // Fixed-order sum of the column-split partials of pass 1.
@@ -719,13 +757,15 @@ static hipError_t mfma_p_rpg(const LaunchCtx& c, const GridRange& g, int mode, c
   const dim3 gr(g.count), b(256);
 #define PSGD_MP(MD)                                                                                          \
   hipLaunchKernelGGL((k_mfma_p<RP, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, \
-                     beta, Q, P, p_fixed, c.ppart)
+                     beta, Q, P, p_fixed, c.ppart, c.p_prev)
   switch (mode) {
     case 1: PSGD_MP(1); break;
     case 2: PSGD_MP(2); break;
     case 3: PSGD_MP(3); break;
     case 4: PSGD_MP(4); break;
-    default: return hipErrorInvalidValue;  // deferred-residual modes: vector-ALU ranks only
+    case 5: PSGD_MP(5); break;
+    case 6: PSGD_MP(6); break;
+    default: return hipErrorInvalidValue;
   }
 #undef PSGD_MP
   return hipGetLastError();
@@ -737,7 +777,7 @@ static hipError_t mfma_p_rp(const LaunchCtx& c, const GridRange& g, int mode, co
   if (g.count == 0) return hipSuccess;
   if (mode == 0) {  // M read from E: no gradient involved
     hipLaunchKernelGGL((k_mfma_p<RP, 0, false>), dim3(g.count), dim3(256), 0, c.stream, c.mats, c.rows_map, g.base,
-                       c.rank, G, E, U, beta, Q, P, p_fixed, c.ppart);
+                       c.rank, G, E, U, beta, Q, P, p_fixed, c.ppart, nullptr);
     return hipGetLastError();
   }
   return c.g_bf16 ? mfma_p_rpg<RP, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)

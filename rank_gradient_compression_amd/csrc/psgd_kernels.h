@@ -59,7 +59,7 @@ struct GridRange {
 // mode 0: P = M Q with M read from E; 1: M = G + E stored over E; 2: also
 // u = beta u + G first (M = u + E); 3: M = G; 4: u = beta u + G, M = u
 // (3 and 4: no error feedback); 5 and 6: as 1 and 2 with E formed from a
-// deferred residual, E = E_in - p_prev Q^T (vector-ALU ranks only).
+// deferred residual, E = E_in - p_prev Q^T (also in launch_mfma_p).
 // p_fixed >= 0 replaces the plan's P offset.
 hipError_t launch_ef_p(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                        float beta, const float* Q, float* P, int64_t p_fixed);

@@ -289,14 +289,3 @@ def test_init_q_without_matrices_is_a_no_op():
         R.psgd_init_q(p, 0, 7, FAKE * 2, 1 << 20)  # nothing to write, nothing launched
     finally:
         R.psgd_plan_destroy(p)
-
-
-@pytest.mark.parametrize("flags", [B.PSGD_STEP_DEFER_RESIDUAL, B.PSGD_STEP_RESIDUAL_DEFERRED])
-def test_deferred_residual_needs_vector_alu_rank(flags):
-    p = R.psgd_plan_create([640], [480], 16)
-    try:
-        with pytest.raises(B.PsgdError) as e:
-            _compress(p, opts=B.step_opts(flags=flags))
-        assert e.value.status == B.PSGD_ERR_UNSUPPORTED
-    finally:
-        R.psgd_plan_destroy(p)

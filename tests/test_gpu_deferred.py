@@ -24,7 +24,11 @@ SHAPES = [(300, 650), (257, 4099), (97, 1030), (33, 27), (5,), (640, 512), (2, 2
 
 def _run(shapes, rank, steps, beta=None, grads_dtype=torch.float32, seed=0, offsets=None, sgd=False):
     tensors = [(str(i), s) for i, s in enumerate(shapes)]
-    wl = W.ModelSetWorkload(tensors, "lstm3" if beta is None else "plain", seed=seed)
+    # The k^-1.5 spectrum at ranks above 8 on the 97-row matrix makes P
+    # ill-conditioned enough that fp32 and fp64 differ near the tolerance on
+    # both paths alike; the matrix-core ranks use well-conditioned Gaussian
+    # gradients, as in the other matrix-core parity tests.
+    wl = W.ModelSetWorkload(tensors, "lstm3" if beta is None and rank <= 8 else "plain", seed=seed)
     ps = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta, offsets=offsets, grads_dtype=grads_dtype)
     ref = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta, offsets=offsets, grads_dtype=grads_dtype)
     oplan = oracle.Plan(shapes, rank)
@@ -50,14 +54,6 @@ def _run(shapes, rank, steps, beta=None, grads_dtype=torch.float32, seed=0, offs
         ps.compress(mhat=True, defer_residual=not last, residual_deferred=t > 1, **sgd_kw)
         ref.compress(mhat=True, **(sgd_ref if sgd else {}))
         torch.cuda.synchronize()
-        res = oracle.step_set(oplan, grads, ost, beta=beta or 0.0)
-        if last:
-            compare_set(ps, oplan, res, ost, tag=f"deferred r={rank} step {t}")
-        else:
-            compare_set(ps, oplan, res, ost, tag=f"deferred r={rank} step {t}", check_e=False)
-            for i in ps.compressed():
-                e = rel(cpu(ps.view(ps.err, i)), res.M[i])
-                assert e <= REL_TOL, f"step {t} tensor {i}: M left in err, rel err {e:.3e}"
         # the same operations in the same order as the explicit path
         assert torch.equal(ps.p, ref.p) and torch.equal(ps.q, ref.q), f"step {t}: factors differ"
         assert torch.equal(ps.mhat, ref.mhat), f"step {t}: M_hat differs"
@@ -67,18 +63,28 @@ def _run(shapes, rank, steps, beta=None, grads_dtype=torch.float32, seed=0, offs
             assert torch.equal(ps.err, ref.err), "explicit E differs"
         if beta is not None:
             assert torch.equal(ps.mom, ref.mom)
+        res = oracle.step_set(oplan, grads, ost, beta=beta or 0.0)
+        if last:
+            compare_set(ps, oplan, res, ost, tag=f"deferred r={rank} step {t}")
+        else:
+            compare_set(ps, oplan, res, ost, tag=f"deferred r={rank} step {t}", check_e=False)
+            for i in ps.compressed():
+                e = rel(cpu(ps.view(ps.err, i)), res.M[i])
+                assert e <= REL_TOL, f"step {t} tensor {i}: M left in err, rel err {e:.3e}"
 
 
-@pytest.mark.parametrize("rank", [1, 2, 4, 7, 8])
+@pytest.mark.parametrize("rank", [1, 2, 4, 7, 8, 16, 32, 64])
 def test_deferred_residual_ranks(rank):
     _run(SHAPES, rank, 4, seed=150 + rank)
 
 
-def test_deferred_residual_momentum_bf16_odd_offsets():
+@pytest.mark.parametrize("rank", [4, 32])
+def test_deferred_residual_momentum_bf16_odd_offsets(rank):
     shapes = [(300, 512), (200, 650), (13,)]
     offsets = [1, 300 * 512 + 3, 300 * 512 + 3 + 200 * 650 + 2]
-    _run(shapes, 4, 4, beta=0.9, grads_dtype=torch.bfloat16, seed=160, offsets=offsets)
+    _run(shapes, rank, 4, beta=0.9, grads_dtype=torch.bfloat16, seed=160 + rank, offsets=offsets)
 
 
-def test_deferred_residual_with_fused_sgd():
-    _run([(300, 650), (400, 512), (11,)], 4, 3, seed=170, sgd=True)
+@pytest.mark.parametrize("rank", [4, 16])
+def test_deferred_residual_with_fused_sgd(rank):
+    _run([(300, 650), (400, 512), (11,)], rank, 3, seed=170 + rank, sgd=True)
