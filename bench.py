@@ -42,7 +42,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b", choices=["llama7b", "sweep", "refresh", "resnet18", "lstm3"])
     ap.add_argument("--rank", type=int, default=None)
@@ -245,6 +245,11 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
         res["config"]["compress_only"] = {"ms_per_step": round(ms_c, 4),
                                           "grad_gbs": round(4.0 * dense / (ms_c * 1e-3) / 1e9, 2),
                                           "hbm_frac": round(24.0 * dense / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # Standalone decompression M_hat = P_hat Q^T of the whole set: a
+        # write-only pass (4 B per element).
+        ms_dd, _ = R.time("decompress", lambda: ps.decompress(), max(3, args.steps // 2), 1, per_step=False)
+        res["config"]["decompress"] = {"ms_per_step": round(ms_dd, 4),
+                                       "hbm_frac": round(4.0 * dense / (ms_dd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # Deferred residual: E = M - P_hat Q^T is formed inside the next
         # step's EF-add pass instead of being stored (20 / 16 B per element).
         ps.compress(mhat=True, defer_residual=True)
@@ -391,10 +396,23 @@ def run_small_set(args, torch, B, W, PowerSGD, R, name):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(tensors, rank):
-    """The fp64 oracle on the host cores: one step of each distinct matrix
-    shape of the set, scaled by how often the shape occurs (an extrapolated
-    whole-set step)."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(tensors, rank, budget_s=10.0, cap_s=30.0):
+    """The fp64 oracle on the host cores: steps of each distinct matrix shape
+    of the set, repeated round-robin for about `budget_s` seconds (at least
+    three runs per shape), the median per shape scaled by how often the shape
+    occurs (an extrapolated whole-set step)."""
+    import statistics
+
     import numpy as np
 
     import oracle
@@ -410,26 +428,35 @@ def cpu_baseline(tensors, rank):
     for _, s in tensors:
         counts[tuple(s)] = counts.get(tuple(s), 0) + 1
     g = np.random.default_rng(0)
+    inputs = {}
+    for shape in counts:
+        m, n = shape
+        inputs[shape] = (g.standard_normal((m, n), dtype=np.float32), np.zeros((m, n)), g.standard_normal((n, rank)))
+    runs = {shape: [] for shape in counts}
+    t_start = time.perf_counter()
+    while True:
+        for shape, (G, E, Q) in inputs.items():
+            t0 = time.perf_counter()
+            res = oracle.compress_matrix(G.astype(np.float64) + E, Q)
+            runs[shape].append(time.perf_counter() - t0)
+            del res
+        spent = time.perf_counter() - t_start
+        if spent >= cap_s or (spent >= budget_s and min(len(v) for v in runs.values()) >= 3):
+            break
+    del inputs
     total = 0.0
     detail = {}
-    for shape, c in counts.items():
-        m, n = shape
-        G = g.standard_normal((m, n), dtype=np.float32)
-        E = np.zeros((m, n))
-        Q = g.standard_normal((n, rank))
-        t0 = time.perf_counter()
-        res = oracle.compress_matrix(G.astype(np.float64) + E, Q)
-        dt = time.perf_counter() - t0
-        del res, G, E
-        detail[f"{m}x{n}"] = {"s": round(dt, 3), "count": c}
-        total += dt * c
+    for (m, n), c in counts.items():
+        med = statistics.median(runs[(m, n)])
+        detail[f"{m}x{n}"] = {"s_median": round(med, 4), "runs": len(runs[(m, n)]), "count": c}
+        total += med * c
     dense = sum(a * b * c for (a, b), c in counts.items())
     return {"value": round(4.0 * dense / total / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": "one fp64 oracle step (EF-add, P, Gram-Schmidt, Q, residual) per distinct matrix shape ("
-                      + ", ".join(detail) + f"), scaled by the shape counts to the {len(tensors)}-matrix set: "
-                      f"extrapolated {total:.1f} s per step",
-            "host_cores": cores, "detail": detail}
+            "sample": "fp64 oracle steps (EF-add, P, Gram-Schmidt, Q, residual) of each distinct matrix shape ("
+                      + ", ".join(detail) + f"), round-robin for {spent:.1f} s; the median per shape scaled by the "
+                      f"shape counts to the {len(tensors)}-matrix set: extrapolated {total:.1f} s per step",
+            "host_cores": cores, "cpu_model": cpu_model(), "detail": detail}
 
 
 def main():

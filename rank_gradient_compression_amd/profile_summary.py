@@ -9,9 +9,9 @@ WRITE_SIZE` run of the same program.  The byte counters are calibrated with
 the library's 16-byte copy kernel over 4 GiB (`psgd_stream_copy`, which the
 benchmark runs first): each counter is scaled so that the copy reads and
 writes exactly 4 GiB.  The machine-readable block records, per kernel, the
-scaled bytes per launch and a hash of the source file that defines the kernel
-(with the shared headers), so a reader can tell when the counters no longer
-describe the code.
+scaled bytes per launch and a hash of the code (comments stripped) of the
+source file that defines the kernel and of the shared headers, so a reader can
+tell when the counters no longer describe the code.
 """
 from __future__ import annotations
 
@@ -20,6 +20,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -38,11 +39,22 @@ def source_file(kernel: str) -> str:
     return "kernels_valu.hip"
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank-line / trailing-space noise, so
+    that editing a comment does not count as changing the kernel.  (The
+    kernel sources hold no string literals with comment markers.)"""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_hash(kernel: str) -> str:
+    """Hash of the code (comments stripped) of the file that defines the
+    kernel and of the shared headers."""
     h = hashlib.sha256()
     for f in (source_file(kernel),) + SHARED_HEADERS:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
