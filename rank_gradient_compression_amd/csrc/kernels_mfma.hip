@@ -660,20 +660,27 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const OrthDesc* __restrict_
   gram[o.t_off + e] = (s0 + s1) + (s2 + s3);
 }
 
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b & 0xffffffffull), l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 // One wavefront per factor: right-looking Cholesky of A with the dependence
 // rule.  Lane j keeps column j of the (symmetric) Schur complement S in fp64
-// registers; at step k every lane publishes S_kj through LDS, reads the pivot
-// S_kk and the row S_k. back as broadcasts, and updates
-// S_ij -= S_ki S_kj / S_kk for i > k.  Row k of R is S_k. / sqrt(S_kk) (zero
-// for a dependent column, judged against the norm before projection, the
-// original A_kk).  No cross-wavefront barrier, no divergence: the step is a
-// chain of broadcast LDS reads and fp64 FMAs.  The upper triangle of the
-// factor's A slot is overwritten with R (A is read completely first).
+// registers.  At step k the pivot S_kk comes from lane k's registers
+// (readlane), every lane publishes S_kj through LDS and reads the row S_k.
+// back as broadcasts, and updates S_ij -= S_ki (S_kj / S_kk) for i > k; only
+// the one reciprocal 1 / S_kk is on the step-to-step path.  Row k of R is
+// S_k. / sqrt(S_kk), zero for a dependent column: sqrt(S_kk) <= 1e-4 of the
+// norm before projection sqrt(A_kk), tested squared.  A single wavefront
+// needs no barrier: its LDS accesses complete in program order.  The upper
+// triangle of the factor's A slot is overwritten with R (A is read first).
 template <int RP>
 __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
                                                    double* __restrict__ gram, float zero_rel) {
   __shared__ double rowbuf[RP];
-  __shared__ double dgs[RP];
   const OrthDesc o = descs[first + blockIdx.x];
   const int j = threadIdx.x;
   const bool own = j < RP;
@@ -681,25 +688,23 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
   double sc[RP];
 #pragma unroll
   for (int i = 0; i < RP; ++i) sc[i] = own ? a[i * RP + j] : 0.0;
-  if (own) dgs[j] = a[j * RP + j];
-  __syncthreads();
+  const double dgj = own ? a[j * RP + j] : 0.0;  // A_jj: squared norm before projection
+  const double zr2 = (double)zero_rel * (double)zero_rel;
   // Fully unrolled so that sc[] stays in registers; steps k >= r are skipped
   // by a uniform branch.
 #pragma unroll
   for (int k = 0; k < RP; ++k) {
     if (k < r) {
       if (own) rowbuf[j] = sc[k];
-      __syncthreads();
-      const double d = rowbuf[k];
-      const double nu0 = sqrt(dgs[k]);
-      const double nv = d > 0.0 ? sqrt(d) : 0.0;
-      const bool zero = !(nu0 > 0.0) || nv <= (double)zero_rel * nu0;
-      const double inv = zero ? 0.0 : 1.0 / nv;
-      const double c = sc[k] * (inv * inv);  // S_kj / S_kk
-      if (own && j >= k && j < r) a[k * RP + j] = j == k ? (zero ? 0.0 : nv) : sc[k] * inv;
+      const double d = readlane_f64(sc[k], k);
+      const double dg = readlane_f64(dgj, k);
+      const bool zero = !(dg > 0.0) || !(d > 0.0) || d <= zr2 * dg;
+      const double inv2 = zero ? 0.0 : 1.0 / d;
+      const double c = sc[k] * inv2;  // S_kj / S_kk
+      const double nv = zero ? 0.0 : sqrt(d);
+      if (own && j >= k && j < r) a[k * RP + j] = j == k ? nv : sc[k] * (nv * inv2);
 #pragma unroll
       for (int i = k + 1; i < RP; ++i) sc[i] = fma(-rowbuf[i], c, sc[i]);
-      __syncthreads();  // rowbuf is rewritten at the next step
     }
   }
 }
@@ -707,16 +712,23 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
 // P_hat = P R^-1, one row per thread: x R = p by forward substitution,
 // x_k = (p_k - sum_{j<k} x_j R_jk) / R_kk, x_k = 0 for a dependent column;
 // x is kept in fp64 registers and rounded to fp32 when stored (in place: p_k
-// is read before x_k overwrites it).
+// is read before x_k overwrites it).  The sum runs in four interleaved
+// partial sums and the diagonal is applied as a reciprocal, so a row is not
+// one long chain of dependent operations.
 template <int RP>
 __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restrict__ descs,
                                                        const int32_t* __restrict__ map, int first, int r,
                                                        float* __restrict__ base, const double* __restrict__ gram) {
   __shared__ double Rs[RP * RP];
+  __shared__ double rinv[RP];
   int local;
   const OrthDesc o = descs[orth_idx(descs, map, first, local)];
   const double* rg = gram + o.t_off;
   for (int e = threadIdx.x; e < RP * RP; e += kGramRows) Rs[e] = rg[e];
+  for (int k = threadIdx.x; k < RP; k += kGramRows) {
+    const double d = rg[k * RP + k];
+    rinv[k] = d > 0.0 ? 1.0 / d : 0.0;
+  }
   __syncthreads();
   const int i = local * kGramRows + threadIdx.x;
   if (i >= o.rows) return;
@@ -724,16 +736,21 @@ __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restric
   const int64_t ld = o.rows;
   double x[RP];
 #pragma unroll
+  for (int k = 0; k < RP; ++k) x[k] = k < r ? (double)p[k * ld] : 0.0;
+#pragma unroll
   for (int k = 0; k < RP; ++k) {
     if (k < r) {
-      double s = (double)p[k * ld];
+      double s0 = x[k], s1 = 0.0, s2 = 0.0, s3 = 0.0;
 #pragma unroll
-      for (int j = 0; j < k; ++j) s = fma(-x[j], Rs[j * RP + k], s);
-      const double rkk = Rs[k * RP + k];
-      x[k] = rkk > 0.0 ? s / rkk : 0.0;
+      for (int jj = 0; jj < k; ++jj) {
+        const double t = -x[jj] * Rs[jj * RP + k];
+        if ((jj & 3) == 0) s0 += t;
+        else if ((jj & 3) == 1) s1 += t;
+        else if ((jj & 3) == 2) s2 += t;
+        else s3 += t;
+      }
+      x[k] = ((s0 + s1) + (s2 + s3)) * rinv[k];
       p[k * ld] = (float)x[k];
-    } else {
-      x[k] = 0.0;
     }
   }
 }
