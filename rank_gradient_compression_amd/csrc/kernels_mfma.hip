@@ -719,12 +719,12 @@ template <int RP>
 __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restrict__ descs,
                                                        const int32_t* __restrict__ map, int first, int r,
                                                        float* __restrict__ base, const double* __restrict__ gram) {
-  __shared__ double Rs[RP * RP];
+  __shared__ double Rt[RP * RP];  // R transposed: column k of R is contiguous
   __shared__ double rinv[RP];
   int local;
   const OrthDesc o = descs[orth_idx(descs, map, first, local)];
   const double* rg = gram + o.t_off;
-  for (int e = threadIdx.x; e < RP * RP; e += kGramRows) Rs[e] = rg[e];
+  for (int e = threadIdx.x; e < RP * RP; e += kGramRows) Rt[(e % RP) * RP + e / RP] = rg[e];
   for (int k = threadIdx.x; k < RP; k += kGramRows) {
     const double d = rg[k * RP + k];
     rinv[k] = d > 0.0 ? 1.0 / d : 0.0;
@@ -743,7 +743,7 @@ __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restric
       double s0 = x[k], s1 = 0.0, s2 = 0.0, s3 = 0.0;
 #pragma unroll
       for (int jj = 0; jj < k; ++jj) {
-        const double t = -x[jj] * Rs[jj * RP + k];
+        const double t = -x[jj] * Rt[k * RP + jj];
         if ((jj & 3) == 0) s0 += t;
         else if ((jj & 3) == 1) s1 += t;
         else if ((jj & 3) == 2) s2 += t;
