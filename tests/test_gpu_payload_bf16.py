@@ -2,12 +2,13 @@
 
 Where a rounded value is decided by floating point, GPU (fp32 sums) and
 oracle (fp64) can land on opposite sides of a rounding midpoint.  So each
-factor the hook receives is checked as a valid rounding: bfloat16-valued,
-equal to the oracle's rounding everywhere except at elements whose exact
-value lies within fp32 accumulation error of a midpoint, and there exactly
-one bfloat16 step away.  The oracle then continues from the factors the GPU
-sent (teacher forcing at the hooks, which is what an aggregation would hand
-every worker), and P_hat, E and M_hat are compared to the usual tolerance.
+factor the hook receives is checked as a valid rounding: bfloat16-valued and
+within half a bfloat16 step of a value inside the fp32 accumulation error of
+the oracle's exact value (so equal to the oracle's rounding except next to a
+midpoint, or for entries far below the factor's scale).  The oracle then
+continues from the factors the GPU sent (teacher forcing at the hooks, which
+is what an aggregation would hand every worker), and P_hat, E and M_hat are
+compared to the usual tolerance.
 """
 import numpy as np
 import pytest
