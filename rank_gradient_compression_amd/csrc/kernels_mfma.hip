@@ -121,6 +121,11 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 // in, so E is formed bit for bit as the residual pass would have stored it.
 // ---------------------------------------------------------------------------
 
+// EF-add modes: the workgroup's four wavefronts take 16 rows each of the
+// 64-row tile and walk the column split in 64-column steps; each Q chunk is
+// staged once in LDS and shared by the four wavefronts (the EF-add modes run
+// best this way: the Q chunk is read from L2 once per 64 rows).
+
 template <int RP, int MODE, bool VEC4, bool GBF16>
 __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
                                             float* __restrict__ E, float* __restrict__ U, float beta,
@@ -280,6 +285,103 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
   }
 }
 
+// Plain M Q (read only: the subspace refresh and the extra power
+// iterations).  A workgroup owns a 64-row tile and one column split; each
+// wavefront takes two 16-row MFMA tiles (a row half) and every second
+// 64-column chunk of the split, and the two wavefronts of a row half are
+// summed in LDS at the end in fixed order.  In a chunk, lane (li, ls) loads
+// 16 bytes -- columns c0 + 16 qq + 4 ls .. + 3 -- of its row in each tile
+// (the A operands of four k-steps), and the matching B operands
+// Q[c0 + 16 qq + 4 ls + v][16 T + li], v = 0..3, are one 16-byte load from
+// the column-major Q, shared by both tiles.  No LDS staging and no barrier in
+// the column loop (measured 19% faster than the staged form for this
+// read-only pass; slower for the EF-add modes, which keep the staged form).
+template <int RP, bool VEC4>
+__device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, const float* __restrict__ M,
+                                             const float* __restrict__ Q, float* P, int64_t p_fixed,
+                                             float* __restrict__ ppart, float* red) {
+  constexpr int RS = kMfmaRows + 1;  // LDS row stride of the [rank][64 rows] reduction tile
+  constexpr int NT = 2;              // 16-row tiles per wavefront
+  const int m = d.m, n = d.n;
+  const int local = wg - d.wg_rows0;
+  const int rb = local / d.s1, split = local - rb * d.s1;
+  const int c_begin = split * d.s1_cols;
+  const int c_end = min(n, c_begin + d.s1_cols);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, ls = lane >> 4;
+  const int half = wave & 1, phase = wave >> 1;
+  const int tbase = rb * kMfmaRows + 32 * half;
+  bool row_ok[NT];
+  int64_t roff[NT];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    const int row = tbase + 16 * tl + li;
+    row_ok[tl] = row < m;
+    roff[tl] = d.off + (int64_t)min(row, m - 1) * n;
+  }
+  const float* q = Q + d.q_off;
+
+  v4f acc[NT][RP / 16];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl)
+#pragma unroll
+    for (int T = 0; T < RP / 16; ++T) acc[tl][T] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = c_begin + 64 * phase; c0 < c_end; c0 += 128) {
+    float4 x[NT][4], qb[4][RP / 16];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int col = c0 + 16 * qq + 4 * ls;
+      const bool col_ok = col < c_end;
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl) x[tl][qq] = ldq<VEC4>(M + roff[tl], col, col_ok, c_begin, n);
+#pragma unroll
+      for (int T = 0; T < RP / 16; ++T) {
+        const int t = 16 * T + li;
+        qb[qq][T] = ldq<VEC4>(q + (int64_t)(t < r ? t : 0) * n, col, col_ok && t < r, c_begin, n);
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int T = 0; T < RP / 16; ++T) {
+          const float4 bq = qb[qq][T];
+          const float b = v == 0 ? bq.x : v == 1 ? bq.y : v == 2 ? bq.z : bq.w;
+#pragma unroll
+          for (int tl = 0; tl < NT; ++tl) {
+            const float4 xq = x[tl][qq];
+            const float a = row_ok[tl] ? (v == 0 ? xq.x : v == 1 ? xq.y : v == 2 ? xq.z : xq.w) : 0.f;
+            acc[tl][T] = mfma16x16x4(a, b, acc[tl][T]);
+          }
+        }
+  }
+
+  // The two column phases of each row half summed in LDS in phase order;
+  // acc[tl][T][e] of lane (li, ls) is P[tbase + 16 tl + 4 ls + e][16 T + li].
+  for (int ph = 0; ph < 2; ++ph) {
+    if (phase == ph) {
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl)
+#pragma unroll
+        for (int T = 0; T < RP / 16; ++T)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float* slot = &red[(16 * T + li) * RS + 32 * half + 16 * tl + 4 * ls + e];
+            *slot = ph == 0 ? acc[tl][T][e] : *slot + acc[tl][T][e];
+          }
+    }
+    __syncthreads();
+  }
+  float* dst = d.s1 > 1 ? ppart + d.ppart_off + (int64_t)split * r * m : P + (p_fixed >= 0 ? p_fixed : d.p_off);
+  const int rbase = rb * kMfmaRows;
+  for (int idx = threadIdx.x; idx < RP * kMfmaRows; idx += 256) {
+    const int t = idx / kMfmaRows, rl = idx % kMfmaRows;
+    if (t < r && rbase + rl < m) dst[(int64_t)t * m + rbase + rl] = red[t * RS + rl];
+  }
+}
+
 template <int RP, int MODE, bool GBF16>
 __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
                                                 int wg_base, int r, const void* __restrict__ G,
@@ -288,14 +390,22 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
                                                 float* __restrict__ ppart, const float* Pold) {
   constexpr int QS = RP + 4;
   static_assert(16 * (kMfmaRows + 1) <= 64 * QS, "output staging does not fit");
-  __shared__ float Qs[64 * QS];
+  constexpr int SMEM = MODE == 0 ? RP * (kMfmaRows + 1) : 64 * QS;
+  __shared__ float smem[SMEM];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
-  if (d.vec == 4)
-    mfma_p_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs, Pold);
-  else
-    mfma_p_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, Qs, Pold);
+  if constexpr (MODE == 0) {
+    if (d.vec == 4)
+      mfma_mq_body<RP, true>(d, wg, r, E, Q, P, p_fixed, ppart, smem);
+    else
+      mfma_mq_body<RP, false>(d, wg, r, E, Q, P, p_fixed, ppart, smem);
+  } else {
+    if (d.vec == 4)
+      mfma_p_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
+    else
+      mfma_p_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
+  }
 }
 
 // Fixed-order sum of the column-split partials of pass 1.
