@@ -19,7 +19,8 @@
  *
  * Conventions shared by every entry point
  * ----------------------------------------
- * - All floating-point data is fp32.  Device pointers are plain HIP device
+ * - All floating-point data is fp32 (the gradients may be bfloat16, see
+ *   PSGD_FLAG_GRADS_BF16).  Device pointers are plain HIP device
  *   addresses, 16-byte aligned; the caller allocates and owns every device
  *   buffer.  The library allocates no device memory.
  * - Gradient-shaped buffers (grads, err, mom, mhat/out) are FLAT: one buffer

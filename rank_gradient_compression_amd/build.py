@@ -63,7 +63,28 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"linking libpsgd.so failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_c_smoke(verbose)
     return LIB
+
+
+C_SMOKE = os.path.join(PKG, "psgd_c_smoke")
+
+
+def build_c_smoke(verbose: bool = False) -> str:
+    """The plain C client (csrc/c_smoke.c), linked against libpsgd.so and the
+    HIP runtime with gcc: no HIP compiler, no Python."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(rocm, "include"), os.path.join(CSRC, "c_smoke.c"), "-o", C_SMOKE + ".tmp",
+           "-L", PKG, "-lpsgd", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"building the C client failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(C_SMOKE + ".tmp", C_SMOKE)
+    return C_SMOKE
 
 
 if __name__ == "__main__":

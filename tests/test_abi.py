@@ -289,3 +289,14 @@ def test_init_q_without_matrices_is_a_no_op():
         R.psgd_init_q(p, 0, 7, FAKE * 2, 1 << 20)  # nothing to write, nothing launched
     finally:
         R.psgd_plan_destroy(p)
+
+
+def test_c_client_is_built_against_the_library():
+    # build() links the plain C client (csrc/c_smoke.c) with gcc against
+    # libpsgd.so and the HIP runtime only; the GPU test runs it.
+    import subprocess
+    exe = os.path.join(os.path.dirname(R.__file__), "psgd_c_smoke")
+    assert os.path.exists(exe), "build() did not produce the C client"
+    out = subprocess.run(["ldd", exe], capture_output=True, text=True).stdout
+    assert "libpsgd.so" in out and "libamdhip64" in out
+    assert "torch" not in out and "python" not in out
