@@ -395,6 +395,14 @@ def run_small_set(args, torch, B, W, PowerSGD, R, name):
         st = stage_table(B, ps.plan, step_bytes(False), step_flops(rank), dense)
         res["roofline"] = roofline_of(st, rank > 8)
         res["stages"] = round_stages(st)
+    # The same step captured once in a HIP graph and replayed: these sets are
+    # launch-bound, and a replay issues all of the step's kernels at once.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ps.compress(mhat=True)
+    ms_g, _ = R.time(f"{name} r={rank}, graph replay", graph.replay, args.steps, args.warmup, per_step=False)
+    res["config"]["graph_replay"] = {"ms_per_step": round(ms_g, 4),
+                                     "grad_gbs": round(4.0 * dense / (ms_g * 1e-3) / 1e9, 2)}
     print(json.dumps(res), flush=True)
 
 

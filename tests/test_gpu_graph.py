@@ -1,0 +1,47 @@
+"""psgd_compress captured in a HIP graph (no hook, timing off: the call then
+only enqueues kernels) and replayed: every replay, with eager work and
+synchronisations in between, must give bit for bit what the same sequence of
+eager calls gives on an identical twin (the kernels are deterministic)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import workloads as W  # noqa: E402
+from gpu_util import say  # noqa: E402
+from rank_gradient_compression_amd.torch_api import PowerSGD  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("rank,beta", [(2, None), (4, 0.9), (16, None)])
+def test_graph_replays_match_eager_calls(rank, beta):
+    shapes = [(300, 650), (257, 1030), (64, 3, 3, 3), (11,), (2, 2)]
+    tensors = [(str(i), s) for i, s in enumerate(shapes)]
+    wl = W.ModelSetWorkload(tensors, "plain", seed=190 + rank)
+    a = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta)
+    b = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta)
+    for ps in (a, b):
+        for i in ps.compressed():
+            ps.set_q(i, wl.q0(i, rank))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        a.compress(mhat=True)
+    for t in range(1, 5):
+        for ps in (a, b):
+            for i in range(len(shapes)):
+                ps.view(ps.grads, i).copy_(torch.from_numpy(np.ascontiguousarray(wl.grad(i, t))).to(DEV))
+        torch.cuda.synchronize()
+        say(f"[graph r={rank} beta={beta}] replay {t}")
+        graph.replay()
+        b.compress(mhat=True)
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device=DEV).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del junk
+        for name in ("p", "q", "err", "mhat") + (("mom",) if beta is not None else ()):
+            assert torch.equal(getattr(a, name), getattr(b, name)), f"replay {t}: {name} differs"
