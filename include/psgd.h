@@ -34,7 +34,10 @@
  *   aggregation of P carries them.
  * - Every device-side call is asynchronous on the given stream and performs
  *   no host synchronisation; device faults surface at the caller's next
- *   synchronisation.  Calls return a status and never throw; on failure,
+ *   synchronisation.  psgd_compress, psgd_decompress, psgd_refresh and
+ *   psgd_init_q only enqueue kernels (no allocation, memset or copy), so they
+ *   can be captured in a HIP graph when timing is off and the hook, if any,
+ *   only enqueues work on the stream.  Calls return a status and never throw; on failure,
  *   psgd_last_error() gives a thread-local message.
  * - Thread safety: a plan is immutable after creation and may be shared by
  *   threads and streams, provided concurrent calls use distinct workspaces.
