@@ -79,6 +79,32 @@ __device__ __forceinline__ float4 ldq(const float* rowp, int col, bool ok, int c
   }
 }
 
+// Streaming (non-temporal) variants for data used once per step: the M read
+// and the M_hat write of the residual pass.
+typedef float v4f_nt __attribute__((ext_vector_type(4)));
+
+template <bool VEC4>
+__device__ __forceinline__ float4 ldq_nt(const float* rowp, int col, bool ok, int col_safe, int n) {
+  if constexpr (VEC4) {
+    const v4f_nt v = __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(rowp + (ok ? col : col_safe)));
+    return ok ? make_float4(v[0], v[1], v[2], v[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    return ld4(rowp, ok ? col : n, n, false);
+  }
+}
+
+template <bool VEC4>
+__device__ __forceinline__ void stq_nt(float* rowp, int col, int n, float4 v) {
+  if constexpr (VEC4) {
+    if (col < n) {
+      const v4f_nt t = {v.x, v.y, v.z, v.w};
+      __builtin_nontemporal_store(t, reinterpret_cast<v4f_nt*>(rowp + col));
+    }
+  } else {
+    st4(rowp, col, n, false, v);
+  }
+}
+
 // Four bfloat16 gradients widened to fp32 (same masking as ldq).
 template <bool VEC4>
 __device__ __forceinline__ float4 ldq_bf16(const uint16_t* rowp, int col, bool ok, int col_safe, int n) {
@@ -629,7 +655,7 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
           const float4 x = cur.xm[rt];
           stq<VEC4>(rowp, col, n, make_float4(x.x - mh.x, x.y - mh.y, x.z - mh.z, x.w - mh.w));
         }
-        if constexpr (WRITE_MHAT) stq<VEC4>(Mhat + d.off + (int64_t)rr * n, col, n, mh);
+        if constexpr (WRITE_MHAT) stq_nt<VEC4>(Mhat + d.off + (int64_t)rr * n, col, n, mh);
         if constexpr (SGD) {
           float4 mm = cur.xb[rt], xp = cur.xx[rt];
           mm.x = fmaf(sg.mu, mm.x, mh.x);
