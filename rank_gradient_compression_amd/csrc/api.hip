@@ -122,8 +122,8 @@ static GridRange mat_range(const psgd_plan* p, size_t k, int32_t MatDesc::*first
 // offsets (p_fixed < 0) or at p_fixed, column-split partials summed.
 static hipError_t stage_mq(const psgd_plan* p, const LaunchCtx& c, const GridRange& g, const GridRange& gp, int mode,
                            const void* G, float* E, float* U, const float* Q, float* P, int64_t p_fixed) {
-  if (!c.mfma) return launch_ef_p(c, g, mode, G, E, U, p->beta, Q, P, p_fixed);
-  hipError_t e = launch_mfma_p(c, g, mode, G, E, U, p->beta, Q, P, p_fixed);
+  hipError_t e = c.mfma ? launch_mfma_p(c, g, mode, G, E, U, p->beta, Q, P, p_fixed)
+                        : launch_ef_p(c, g, mode, G, E, U, p->beta, Q, P, p_fixed);
   if (e != hipSuccess) return e;
   return launch_psum(c, gp, P, p_fixed);
 }
@@ -392,7 +392,7 @@ extern "C" psgd_status_t psgd_refresh(psgd_plan_t p, int32_t tensor, const float
   const GridRange rows = mat_range(p, k, &MatDesc::wg_rows0, c.wg_rows);
   const GridRange mtp = mat_range(p, k, &MatDesc::wg_mtp0, c.wg_mtp);
   const GridRange red = mat_range(p, k, &MatDesc::wg_red0, c.wg_red);
-  const GridRange pred = c.mfma ? mat_range(p, k, &MatDesc::wg_pred0, c.wg_pred) : GridRange{0, 0};
+  const GridRange pred = mat_range(p, k, &MatDesc::wg_pred0, c.wg_pred);
   const int op = c.nmat + (int)k, oq = 2 * c.nmat + (int)k;
   const int nb_p = (d.m + kGramRows - 1) / kGramRows, nb_q = (d.n + kGramRows - 1) / kGramRows;
   float* M = const_cast<float*>(m);

@@ -774,26 +774,41 @@ __global__ __launch_bounds__(256) void k_gram_partial(const OrthDesc* __restrict
     for (int b = 0; b < BF; ++b) g[(ta * BF + a) * RP + tb * BF + b] = acc[a][b];
 }
 
-// Fixed-order block sum: A (at t_off) = sum_b A_b.  Four running sums over
-// interleaved blocks keep several loads in flight; they are combined in a
-// fixed order, so the result is deterministic.
+// Fixed-order block sum: A (at t_off) = sum_b A_b.  A workgroup covers 256
+// entries of one factor's A with kGramRedGroups groups of 256 threads: group
+// g sums the blocks b = g, g + kGramRedGroups, ... in four running sums (so
+// that several loads are in flight), and the group totals are added in
+// group order through LDS.  The order is fixed: deterministic.
+constexpr int kGramRedGroups = 4;
+
 template <int RP>
-__global__ __launch_bounds__(256) void k_gram_reduce(const OrthDesc* __restrict__ descs, int first,
-                                                     double* __restrict__ gram) {
+__global__ __launch_bounds__(256 * kGramRedGroups) void k_gram_reduce(const OrthDesc* __restrict__ descs, int first,
+                                                                      double* __restrict__ gram) {
   constexpr int WPD = RP * RP / 256;  // workgroups per descriptor
+  constexpr int NG = kGramRedGroups;
+  constexpr int64_t BS = (int64_t)RP * RP;  // doubles per block partial
+  __shared__ double tot[NG][256];
   const OrthDesc o = descs[first + blockIdx.x / WPD];
-  const int e = (blockIdx.x % WPD) * 256 + threadIdx.x;
+  const int grp = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int e = (blockIdx.x % WPD) * 256 + t;
   const double* g = gram + o.gram_off + e;
   double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-  int b = 0;
-  for (; b + 4 <= o.ngb; b += 4) {
-    s0 += g[(int64_t)b * RP * RP];
-    s1 += g[(int64_t)(b + 1) * RP * RP];
-    s2 += g[(int64_t)(b + 2) * RP * RP];
-    s3 += g[(int64_t)(b + 3) * RP * RP];
+  int b = grp;
+  for (; b + 3 * NG < o.ngb; b += 4 * NG) {
+    s0 += g[b * BS];
+    s1 += g[(b + NG) * BS];
+    s2 += g[(b + 2 * NG) * BS];
+    s3 += g[(b + 3 * NG) * BS];
   }
-  for (; b < o.ngb; ++b) s0 += g[(int64_t)b * RP * RP];
-  gram[o.t_off + e] = (s0 + s1) + (s2 + s3);
+  for (; b < o.ngb; b += NG) s0 += g[b * BS];
+  tot[grp][t] = (s0 + s1) + (s2 + s3);
+  __syncthreads();
+  if (grp == 0) {
+    double a = tot[0][t];
+#pragma unroll
+    for (int u = 1; u < NG; ++u) a += tot[u][t];
+    gram[o.t_off + e] = a;
+  }
 }
 
 __device__ __forceinline__ double readlane_f64(double v, int l) {
@@ -1000,8 +1015,8 @@ static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const i
                      c.gram);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gram_reduce<RP>), dim3(count * (RP * RP / 256)), dim3(256), 0, c.stream, c.orth, first,
-                     c.gram);
+  hipLaunchKernelGGL((k_gram_reduce<RP>), dim3(count * (RP * RP / 256)), dim3(256 * kGramRedGroups), 0, c.stream,
+                     c.orth, first, c.gram);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(64), 0, c.stream, c.orth, first, c.rank, c.gram,

@@ -158,9 +158,11 @@ constexpr int pow2_at_least(int x) {
 // Pass 1: EF-add (+ momentum) and P = M Q
 // ---------------------------------------------------------------------------
 
-// One wavefront: rows [row0, row0 + kWaveRows) of matrix d, all columns.  Each
-// lane keeps its VEC x R slice of Q in registers for the current column step
-// and reuses it across the wavefront's rows.
+// One wavefront: rows [row0, row0 + kWaveRows) of matrix d, columns
+// [c0, c1) (all of them, or one column split).  Each lane keeps its VEC x R
+// slice of Q in registers for the current column step and reuses it across
+// the wavefront's rows.  The row sums of P go to pdst (column k of m floats
+// from there): P itself, or this split's partial.
 // Row `rr` of P_hat Q^T at the lane's VEC columns: the reconstruction of the
 // residual pass, in one fixed summation order.  The leading product is kept a
 // separately rounded multiply (no contraction into a later subtraction), so
@@ -186,9 +188,9 @@ __device__ __forceinline__ Vec<VEC> recon_row(const float (&ph)[R], const Vec<VE
 // 6: u = beta u + G, M = u + E.  Modes 1..6 store M over E.  Pold may be P
 // itself: each wavefront reads its rows of Pold before writing them in P.
 template <int R, int VEC, int MODE, bool GBF16>
-__device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, const void* __restrict__ G,
-                                          float* __restrict__ E, float* __restrict__ U, float beta,
-                                          const float* __restrict__ Q, float* P, int64_t p_fixed, const float* Pold) {
+__device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, int c1, int lane,
+                                          const void* __restrict__ G, float* __restrict__ E, float* __restrict__ U,
+                                          float beta, const float* __restrict__ Q, float* pdst, const float* Pold) {
   constexpr bool MOM = MODE == 2 || MODE == 4 || MODE == 6;
   constexpr bool LOAD_E = MODE <= 2 || MODE >= 5;
   constexpr bool DEFERRED = MODE >= 5;
@@ -209,7 +211,7 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
 
   const float* q = Q + d.q_off;
   const int64_t base = d.off + (int64_t)row0 * n;
-  for (int j = lane * VEC; j < n; j += 64 * VEC) {
+  for (int j = c0 + lane * VEC; j < c1; j += 64 * VEC) {
     Vec<VEC> qv[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) qv[k] = ldv<VEC>(q + (int64_t)k * n + j);
@@ -265,29 +267,45 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int lane, 
   const int vi = lane >> SHIFT;
   if ((lane & ((1 << SHIFT) - 1)) == 0 && vi < kWaveRows * R) {
     const int rr = vi / R, k = vi % R;
-    if (rr < nrows) P[(p_fixed >= 0 ? p_fixed : d.p_off) + (int64_t)k * m + row0 + rr] = tot;
+    if (rr < nrows) pdst[(int64_t)k * m + row0 + rr] = tot;
   }
 }
 
+// Row tile and column range of a pass-1 / pass-3 workgroup: the matrix's
+// workgroups run over (row tile, column split), splits fastest.
+struct RowTile {
+  int row0, c0, c1, split;
+};
+
+__device__ __forceinline__ RowTile row_tile(const MatDesc& d, int wg, int wave) {
+  const int local = wg - d.wg_rows0;
+  const int tile = local / d.s1, split = local - tile * d.s1;
+  const int c0 = split * d.s1_cols;
+  return RowTile{tile * kRowsPerWG + wave * kWaveRows, c0, min(d.n, c0 + d.s1_cols), split};
+}
+
+// P (or, for a column-split matrix, the split's partial in ppart, summed
+// afterwards in fixed order) at the plan's offsets or at p_fixed.
 template <int R, int MODE, bool GBF16>
 __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__ mats,
                                                      const int32_t* __restrict__ map, int wg_base,
                                                      const void* __restrict__ G, float* __restrict__ E,
                                                      float* __restrict__ U, float beta,
                                                      const float* __restrict__ Q, float* P, int64_t p_fixed,
-                                                     const float* Pold) {
+                                                     const float* Pold, float* __restrict__ ppart) {
   const int wg = blockIdx.x + wg_base;
   const MatDesc d = mats[map[wg]];
   // wave index made provably uniform: row addressing and P_hat loads go scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
-  if (row0 >= d.m) return;
+  const RowTile t = row_tile(d, wg, wave);
+  if (t.row0 >= d.m) return;
+  float* pdst = d.s1 > 1 ? ppart + d.ppart_off + (int64_t)t.split * R * d.m : P + (p_fixed >= 0 ? p_fixed : d.p_off);
   if (d.vec == 4)
-    ef_p_wave<R, 4, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed, Pold);
+    ef_p_wave<R, 4, MODE, GBF16>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
   else if (d.vec == 2)
-    ef_p_wave<R, 2, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed, Pold);
+    ef_p_wave<R, 2, MODE, GBF16>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
   else
-    ef_p_wave<R, 1, MODE, GBF16>(d, row0, lane, G, E, U, beta, Q, P, p_fixed, Pold);
+    ef_p_wave<R, 1, MODE, GBF16>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
 }
 
 // ---------------------------------------------------------------------------
@@ -368,27 +386,45 @@ __global__ __launch_bounds__(kWGThreads) void k_mtp(const MatDesc* __restrict__ 
 }
 
 // Fixed-order sum of the row-block partials: Q[k*n + j] = sum_b part_b[k*n + j].
-__global__ __launch_bounds__(kRedCols) void k_qreduce(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
-                                                      int wg_base, int R, const float* __restrict__ part,
-                                                      float* __restrict__ Q) {
+// A workgroup of kRedWaves wavefronts.  Lane l of a wavefront owns output
+// element l of a 64-element slice (256-byte loads per block); the matrix's
+// red_split S wavefronts share a slice, wavefront s summing the blocks
+// b = s, s + S, ... in two running sums, and the S totals are added in
+// wavefront order through LDS.  The order is fixed: deterministic.
+__global__ __launch_bounds__(64 * kRedWaves) void k_qreduce(const MatDesc* __restrict__ mats,
+                                                            const int32_t* __restrict__ map, int wg_base, int R,
+                                                            const float* __restrict__ part, float* __restrict__ Q) {
+  __shared__ float tot[kRedWaves][64];
   const int wg = blockIdx.x + wg_base;
   const MatDesc d = mats[map[wg]];
+  const int S = d.red_split;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int grp = wave / S, s = wave - grp * S;
   const int64_t len = (int64_t)R * d.n;
-  const int64_t idx = (int64_t)(wg - d.wg_red0) * kRedCols + threadIdx.x;
-  if (idx >= len) return;
-  const float* src = part + d.part_off + idx;
-  // four running sums over interleaved blocks (several loads in flight),
-  // combined in a fixed order: deterministic
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-  int b = 0;
-  for (; b + 4 <= d.nrb; b += 4) {
-    s0 += src[(int64_t)b * len];
-    s1 += src[(int64_t)(b + 1) * len];
-    s2 += src[(int64_t)(b + 2) * len];
-    s3 += src[(int64_t)(b + 3) * len];
+  const int64_t idx = ((int64_t)(wg - d.wg_red0) * (kRedWaves / S) + grp) * 64 + lane;
+  float acc = 0.f;
+  if (idx < len) {
+    const float* src = part + d.part_off + idx;
+    float s0 = 0.f, s1 = 0.f;
+    int b = s;
+    for (; b + S < d.nrb; b += 2 * S) {
+      s0 += src[(int64_t)b * len];
+      s1 += src[(int64_t)(b + S) * len];
+    }
+    if (b < d.nrb) s0 += src[(int64_t)b * len];
+    acc = s0 + s1;
   }
-  for (; b < d.nrb; ++b) s0 += src[(int64_t)b * len];
-  Q[d.q_off + idx] = (s0 + s1) + (s2 + s3);
+  if (S == 1) {  // uniform over the workgroup
+    if (idx < len) Q[d.q_off + idx] = acc;
+    return;
+  }
+  tot[wave][lane] = acc;
+  __syncthreads();
+  if (s == 0 && idx < len) {
+    float t = tot[wave][lane];
+    for (int u = 1; u < S; ++u) t += tot[wave + u][lane];
+    Q[d.q_off + idx] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -399,7 +435,7 @@ __global__ __launch_bounds__(kRedCols) void k_qreduce(const MatDesc* __restrict_
 // post-compression heavy-ball step with the decompressed update M_hat,
 // m <- mu m + M_hat, x <- x - lr m (X = parameters, Mb = momentum buffer).
 template <int R, int VEC, bool RESID, bool WRITE_MHAT, bool SGD>
-__device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane, float* __restrict__ E,
+__device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int c0, int c1, int lane, float* __restrict__ E,
                                            const float* __restrict__ Q, const float* __restrict__ Ph,
                                            float* __restrict__ Mhat, const SgdArgs& sg) {
   const int m = d.m, n = d.n;
@@ -411,7 +447,7 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int lane,
     for (int k = 0; k < R; ++k) ph[rr][k] = Ph[d.p_off + (int64_t)k * m + row0 + min(rr, nrows - 1)];
   const float* q = Q + d.q_off;
   const int64_t base = d.off + (int64_t)row0 * n;
-  for (int j = lane * VEC; j < n; j += 64 * VEC) {
+  for (int j = c0 + lane * VEC; j < c1; j += 64 * VEC) {
     Vec<VEC> qv[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) qv[k] = ldv<VEC>(q + (int64_t)k * n + j);
@@ -463,14 +499,14 @@ __global__ __launch_bounds__(kWGThreads) void k_recon(const MatDesc* __restrict_
   const MatDesc d = mats[map[wg]];
   // wave index made provably uniform: row addressing and P_hat loads go scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int row0 = (wg - d.wg_rows0) * kRowsPerWG + wave * kWaveRows;
-  if (row0 >= d.m) return;
+  const RowTile t = row_tile(d, wg, wave);
+  if (t.row0 >= d.m) return;
   if (d.vec == 4)
-    recon_wave<R, 4, RESID, WRITE_MHAT, SGD>(d, row0, lane, E, Q, Ph, Mhat, sg);
+    recon_wave<R, 4, RESID, WRITE_MHAT, SGD>(d, t.row0, t.c0, t.c1, lane, E, Q, Ph, Mhat, sg);
   else if (d.vec == 2)
-    recon_wave<R, 2, RESID, WRITE_MHAT, SGD>(d, row0, lane, E, Q, Ph, Mhat, sg);
+    recon_wave<R, 2, RESID, WRITE_MHAT, SGD>(d, t.row0, t.c0, t.c1, lane, E, Q, Ph, Mhat, sg);
   else
-    recon_wave<R, 1, RESID, WRITE_MHAT, SGD>(d, row0, lane, E, Q, Ph, Mhat, sg);
+    recon_wave<R, 1, RESID, WRITE_MHAT, SGD>(d, t.row0, t.c0, t.c1, lane, E, Q, Ph, Mhat, sg);
 }
 
 // ---------------------------------------------------------------------------
@@ -564,7 +600,7 @@ static hipError_t launch_ef_p_rg(const LaunchCtx& c, const GridRange& g, int mod
   const dim3 gr(g.count), b(kWGThreads);
 #define PSGD_EFP(MD)                                                                                            \
   hipLaunchKernelGGL((k_ef_p<R, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, \
-                     p_fixed, c.p_prev)
+                     p_fixed, c.p_prev, c.ppart)
   switch (mode) {
     case 1: PSGD_EFP(1); break;
     case 2: PSGD_EFP(2); break;
@@ -583,7 +619,7 @@ static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode
   if (g.count == 0) return hipSuccess;
   if (mode == 0) {  // P = M Q with M read from E: no gradient involved
     hipLaunchKernelGGL((k_ef_p<R, 0, false>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map,
-                       g.base, G, E, U, beta, Q, P, p_fixed, nullptr);
+                       g.base, G, E, U, beta, Q, P, p_fixed, nullptr, c.ppart);
     return hipGetLastError();
   }
   return c.g_bf16 ? launch_ef_p_rg<R, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)
@@ -647,8 +683,8 @@ hipError_t launch_mtp(const LaunchCtx& c, const GridRange& g, const float* M, co
 
 hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q) {
   if (g.count == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_qreduce, dim3(g.count), dim3(kRedCols), 0, c.stream, c.mats, c.red_map, g.base, c.rank, c.part,
-                     Q);
+  hipLaunchKernelGGL(k_qreduce, dim3(g.count), dim3(64 * kRedWaves), 0, c.stream, c.mats, c.red_map, g.base, c.rank,
+                     c.part, Q);
   return hipGetLastError();
 }
 

@@ -200,12 +200,14 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   const bool mfma = rank > kValuMaxRank;
   const int64_t rp = align_up(r, 16);  // rank padding of the matrix-core and Gram kernels
   const int32_t rb = choose_rb_rows(p->mats, r, mfma);
-  // MFMA passes 1 and 3 split the columns until the grid covers the chip.
+  // Passes 1 and 3 split the columns until the grid covers the chip (a set
+  // of few, short matrices otherwise leaves compute units idle).
+  const int32_t tile_rows = mfma ? kMfmaRows : kRowsPerWG;
   int32_t s1 = 1;
-  if (mfma) {
+  {
     int64_t base = 0;
-    for (const MatDesc& d : p->mats) base += (d.m + kMfmaRows - 1) / kMfmaRows;
-    while (base * s1 < 1024 && s1 < 64) s1 *= 2;
+    for (const MatDesc& d : p->mats) base += (d.m + tile_rows - 1) / tile_rows;
+    while (base * s1 < kRowTilesTarget && s1 < 64) s1 *= 2;
   }
   int64_t part = 0, ppart = 0, gram = 0, rscr = 0;
   int32_t wg_rows = 0, wg_mtp = 0, wg_red = 0, wg_pred = 0, wg_gram = 0;
@@ -217,25 +219,25 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     d.ncb = (d.n + cols_per_wg - 1) / cols_per_wg;
     d.part_off = part;
     if (d.nrb > 1) part += align_up((int64_t)d.nrb * r * d.n, kAlignElems);
+    // Q reduce: `red_split` wavefronts share one 64-element slice of Q, so
+    // that each sums at most 8 row blocks (up to 16 wavefronts per slice).
+    d.red_split = 1;
+    while (d.red_split < kRedWaves && (d.nrb + d.red_split - 1) / d.red_split > 8) d.red_split *= 2;
     d.wg_rows0 = wg_rows;
-    int32_t nrow_wg;
-    if (mfma) {
-      int32_t sm = std::max<int32_t>(1, std::min<int32_t>(s1, d.n / 256));
-      d.s1_cols = (int32_t)align_up((d.n + sm - 1) / sm, 64);
-      d.s1 = (d.n + d.s1_cols - 1) / d.s1_cols;
-      nrow_wg = ((d.m + kMfmaRows - 1) / kMfmaRows) * d.s1;
-      d.ppart_off = ppart;
-      d.wg_pred0 = wg_pred;
-      if (d.s1 > 1) {
-        ppart += align_up((int64_t)d.s1 * r * d.m, kAlignElems);
-        const int32_t np = (int32_t)((r * d.m + kRedCols - 1) / kRedCols);
-        for (int32_t t = 0; t < np; ++t) p->pred_map.push_back((int32_t)k);
-        wg_pred += np;
-      }
-    } else {
-      d.s1 = 1;
-      d.s1_cols = d.n;
-      nrow_wg = (d.m + kRowsPerWG - 1) / kRowsPerWG;
+    // column splits of passes 1 and 3: a split is a multiple of one
+    // wavefront's columns (64 for the matrix cores, 64 vectors otherwise)
+    const int32_t unit = mfma ? 64 : 64 * d.vec;
+    const int32_t sm = std::max<int32_t>(1, std::min<int32_t>(s1, d.n / (mfma ? 256 : unit)));
+    d.s1_cols = (int32_t)align_up((d.n + sm - 1) / sm, unit);
+    d.s1 = (d.n + d.s1_cols - 1) / d.s1_cols;
+    const int32_t nrow_wg = ((d.m + tile_rows - 1) / tile_rows) * d.s1;
+    d.ppart_off = ppart;
+    d.wg_pred0 = wg_pred;
+    if (d.s1 > 1) {
+      ppart += align_up((int64_t)d.s1 * r * d.m, kAlignElems);
+      const int32_t np = (int32_t)((r * d.m + kRedCols - 1) / kRedCols);
+      for (int32_t t = 0; t < np; ++t) p->pred_map.push_back((int32_t)k);
+      wg_pred += np;
     }
     for (int32_t t = 0; t < nrow_wg; ++t) p->rows_map.push_back((int32_t)k);
     wg_rows += nrow_wg;
@@ -254,7 +256,8 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     wg_mtp += d.nrb * d.ncb;
     d.wg_red0 = wg_red;
     if (d.nrb > 1) {
-      const int32_t nred = (int32_t)((r * d.n + kRedCols - 1) / kRedCols);
+      const int32_t per_wg = 64 * (kRedWaves / d.red_split);
+      const int32_t nred = (int32_t)((r * d.n + per_wg - 1) / per_wg);
       for (int32_t t = 0; t < nred; ++t) p->red_map.push_back((int32_t)k);
       wg_red += nred;
     }

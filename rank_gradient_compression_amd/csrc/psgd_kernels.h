@@ -33,7 +33,7 @@ struct LaunchCtx {
   const int32_t* gram_map;
   const int32_t* gramq_map;
   float* part;    // partial-Q scratch
-  float* ppart;   // partial-P scratch (MFMA pass 1 column splits)
+  float* ppart;   // partial-P scratch (column splits of pass 1)
   double* gram;   // orthonormalisation scratch
   float* rscr;    // refresh scratch
 };

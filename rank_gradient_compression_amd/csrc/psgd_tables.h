@@ -40,7 +40,7 @@ struct MatDesc {
   int64_t q_off;     // Q: rank columns of n floats from here
   int64_t part_off;  // partial-Q scratch (floats, from the scratch base)
   int64_t gram_off;  // Gram partials (doubles, from the Gram scratch base)
-  int64_t ppart_off; // partial-P scratch of the MFMA pass 1 (floats)
+  int64_t ppart_off; // partial-P scratch of a column-split pass 1 (floats)
   int64_t t_off;     // triangular factor T (doubles, from the Gram scratch base)
   int32_t m, n;
   int32_t vec;       // 4, 2 or 1: widest vector access both n and off allow
@@ -50,13 +50,14 @@ struct MatDesc {
   int32_t wg_rows0;  // first workgroup of this matrix in the row-tile grid
   int32_t wg_mtp0;   // first workgroup of this matrix in the M^T P_hat grid
   int32_t wg_red0;   // first workgroup of this matrix in the Q-reduce grid
-  int32_t s1;        // MFMA passes 1 and 3: column splits
-  int32_t s1_cols;   // MFMA passes 1 and 3: columns per split (multiple of 64)
+  int32_t s1;        // passes 1 and 3: column splits
+  int32_t s1_cols;   // passes 1 and 3: columns per split (whole wavefront widths)
   int32_t wg_pred0;  // first workgroup in the P-partial reduce grid (s1 > 1)
   int32_t wg_gram0;  // first workgroup in the Gram-partial / apply grid
   int32_t ngb;       // Gram-partial blocks (kGramRows rows each)
   int32_t tensor;    // index of the tensor in the plan
-  int32_t pad_[3];
+  int32_t red_split; // wavefronts summing one 64-element slice of Q partials
+  int32_t pad_[2];
 };
 static_assert(sizeof(MatDesc) == 128, "MatDesc layout");
 
@@ -83,7 +84,12 @@ struct OrthDesc {
 };
 
 constexpr int kPassChunk = 4096;  // elements per pass-through workgroup
-constexpr int kRedCols = 256;     // Q elements per reduce workgroup
+constexpr int kRedCols = 256;     // P elements per column-split reduce workgroup
+constexpr int kRedWaves = 16;     // wavefronts of one Q-reduce workgroup
+
+// Row-tile workgroups passes 1 and 3 aim for (the columns are split until the
+// grid has this many).
+constexpr int kRowTilesTarget = 1024;
 
 // Header at the start of the workspace.
 struct WsHeader {
@@ -98,13 +104,13 @@ struct WsHeader {
   int64_t mtp_map_off;   // int32 per M^T P_hat workgroup
   int64_t red_map_off;   // int32 per Q-reduce workgroup
   int64_t pass_map_off;  // int32 pass-through tensor per pass-through workgroup
-  int64_t pred_map_off;  // int32 per P-partial reduce workgroup (MFMA path)
-  int64_t gram_map_off;  // int32 per Gram-partial / apply workgroup (MFMA path)
+  int64_t pred_map_off;  // int32 per P-partial reduce workgroup
+  int64_t gram_map_off;  // int32 per Gram-partial / apply workgroup
   int64_t gramq_map_off; // int32 per Gram workgroup over the Q factors (refresh)
   int64_t orth_off;      // OrthDesc[3 * nmat]: P of compress, refresh P, refresh Q
   int64_t tables_bytes;  // bytes of the table part (uploaded by workspace_init)
   int64_t part_base;     // bytes: partial-Q scratch (float)
-  int64_t ppart_base;    // bytes: partial-P scratch (float, MFMA path)
+  int64_t ppart_base;    // bytes: partial-P scratch (float)
   int64_t gram_base;     // bytes: orthonormalisation scratch (double)
   int64_t refresh_base;  // bytes: refresh scratch (float)
   int64_t total_bytes;
