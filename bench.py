@@ -33,6 +33,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_FP32_PEAK_TFLOPS = 157.3
 KERNEL_OF_STAGE = {"ef_p": "k_ef_p", "mtp": "k_mtp", "residual": "k_recon"}
 KERNEL_OF_STAGE_MFMA = {"ef_p": "k_mfma_p", "mtp": "k_mfma_qt", "residual": "k_mfma_recon"}
+# Byte pattern of each pass (arrays read, arrays written), measured with the
+# library's streaming probe: the practical bandwidth of that pattern.
+PATTERNS = {"r2w1": (2, 1), "r1": (1, 0), "r1w1": (1, 1), "r1w2": (1, 2), "r3w2": (3, 2), "w1": (0, 1)}
 
 
 def log(*a):
@@ -116,6 +119,26 @@ def roofline_of(stages, mfma, profile=None):
             "alg_bytes_per_launch": d["bytes_alg"], "avg_launch_ms": round(d["ms_avg"], 4)}
 
 
+def stage_patterns(momentum=False, mhat=True, deferred=False):
+    res = "w1" if deferred else ("r1w2" if mhat else "r1w1")
+    return {"ef_p": "r3w2" if momentum else "r2w1", "mtp": "r1", "residual": res}
+
+
+def attach_ceilings(stages, ceilings, patterns):
+    """Each streaming stage against the probe's bandwidth for its byte
+    pattern; returns the step time if every pass ran at that bandwidth."""
+    total = 0.0
+    for name, pat in patterns.items():
+        st = stages.get(name)
+        if not st or "bytes_alg" not in st:
+            continue
+        st["pattern"] = pat
+        st["ceiling_gbs"] = ceilings[pat]
+        st["frac_of_ceiling"] = st["gbs"] / ceilings[pat]
+        total += st["bytes_alg"] / (ceilings[pat] * 1e9) * 1e3  # one launch per step
+    return total
+
+
 def round_stages(stages):
     return {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in stages.items()}
 
@@ -172,6 +195,24 @@ class Runner:
         torch.cuda.empty_cache()
         return 8 * n / (ms * 1e-3) / 1e9
 
+    def pattern_ceilings(self, n=1 << 29):
+        """GB/s of bytes moved by the library's streaming probe for each pass
+        pattern in PATTERNS, over n-float arrays (2 GiB each)."""
+        torch, B = self.torch, self.B
+        arrs = [torch.empty(n, dtype=torch.float32, device="cuda").normal_() for _ in range(5)]
+        sink = torch.zeros(B.PSGD_PROBE_SINK_FLOATS, dtype=torch.float32, device="cuda")
+        out = {}
+        for name, (nin, nout) in PATTERNS.items():
+            ins = [a.data_ptr() for a in arrs[:nin]]
+            outs = [a.data_ptr() for a in arrs[3:3 + nout]]
+            ms, _ = self.time(f"probe {name}", lambda: B.psgd_stream_probe(ins, outs, n, sink.data_ptr(),
+                                                                          self.stream.cuda_stream), 5, 2,
+                              per_step=False)
+            out[name] = round(4.0 * n * (nin + nout) / (ms * 1e-3) / 1e9, 1)
+        del arrs, sink
+        torch.cuda.empty_cache()
+        return out
+
 
 def base_result(args, value, ms_step, per, workload, extra):
     cfg = {"workload": workload}
@@ -213,6 +254,7 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
     torch.cuda.synchronize()
     log(f"bench: {dense} synthetic gradient elements ready in {time.time() - t0:.1f} s")
     copy_gbs = R.copy_ceiling()
+    ceilings = R.pattern_ceilings()
     deferred = args.residual == "deferred"
     if deferred:
         ps.compress(mhat=True, defer_residual=True)  # leaves M in err: the steady state below
@@ -233,9 +275,12 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
                       {"rank": rank, "matrices": len(shapes), "elements": dense, "residual": args.residual,
                        "alg_bytes_per_step": bpe * dense,
                        "step_hbm_frac": round(bpe * dense / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                       "copy_ceiling_gbs": round(copy_gbs, 1)})
+                       "copy_ceiling_gbs": round(copy_gbs, 1), "pattern_ceilings_gbs": ceilings})
     if not args.no_stage_timing:
         st = stage_table(B, ps.plan, step_bytes(mfma, deferred=deferred), step_flops(rank, deferred=deferred), dense)
+        at_ceil = attach_ceilings(st, ceilings, stage_patterns(deferred=deferred))
+        res["config"]["step_ms_at_pattern_ceilings"] = round(at_ceil, 3)
+        res["config"]["frac_of_pattern_ceilings"] = round(at_ceil / ms, 4)
         prof = f"hbm_bytes_llama7b_r4_{'deferred' if deferred else 'fused'}.md" if rank == 4 else None
         res["roofline"] = roofline_of(st, mfma, prof)
         res["stages"] = round_stages(st)

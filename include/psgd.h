@@ -339,6 +339,22 @@ psgd_status_t psgd_timing_read(psgd_plan_t plan, double* ms, int64_t* launches);
  * the byte-counter calibration kernel. */
 psgd_status_t psgd_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);
 
+/* Streaming-bandwidth probe: the byte pattern of one pass of the step
+ * without its arithmetic, to measure the practical bandwidth of that pattern
+ * on the device.  Reads nin arrays in[0..nin) and writes nout arrays
+ * out[0..nout) of n floats each, out_j[i] = in_0[i] + ... + in_{nin-1}[i]
+ * (0 with no input); 0 <= nin <= 3, 0 <= nout <= 2, nin + nout >= 1, n a
+ * multiple of 4, every array 16-byte aligned device memory.  With nout = 0
+ * the sums are reduced into sink, device memory of PSGD_PROBE_SINK_FLOATS
+ * floats (one per workgroup; contents meaningless), so that only the reads
+ * reach memory.  `in` and `out` are host arrays of device pointers.  The
+ * pattern of each pass: EF-add + P 2 in / 1 out (3 / 2 with momentum),
+ * M^T P_hat 1 / 0, residual 1 / 1 (1 / 2 with M_hat), decompression 0 / 1.
+ * Asynchronous on `stream`; PSGD_ERR_INVALID_ARG on bad counts or pointers. */
+#define PSGD_PROBE_SINK_FLOATS 16384
+psgd_status_t psgd_stream_probe(const float* const* in, int32_t nin, float* const* out, int32_t nout, size_t n,
+                                float* sink, hipStream_t stream);
+
 /* Thread-local message describing the last failure on this thread. */
 const char* psgd_last_error(void);
 

@@ -10,6 +10,7 @@ from .binding import (PSGD_FLAG_GRADS_BF16, PSGD_FLAG_MOMENTUM, PSGD_KIND_COMPRE
                       PSGD_STEP_NO_ERROR_FEEDBACK, PSGD_STEP_PAYLOAD_BF16, PSGD_STEP_RESIDUAL_DEFERRED,
                       PsgdError, psgd_compress, psgd_decompress, psgd_init_q, psgd_last_error, psgd_plan_create,
                       psgd_plan_destroy, psgd_plan_get_info, psgd_plan_tensor, psgd_refresh, psgd_stream_copy,
+                      psgd_stream_probe,
                       psgd_timing_enable, psgd_timing_read, psgd_version, psgd_workspace_init, step_opts)
 
 __all__ = [n for n in dir() if n.startswith("psgd_") or n.startswith("PSGD_")] + ["PsgdError", "binding"]

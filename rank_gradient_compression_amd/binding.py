@@ -49,7 +49,8 @@ STAGE_NAMES = ["ef_p", "gs", "mtp", "qreduce", "residual", "passthru", "refresh"
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_destroy", "psgd_plan_get_info", "psgd_plan_tensor",
     "psgd_workspace_init", "psgd_compress", "psgd_decompress", "psgd_refresh", "psgd_init_q",
-    "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy", "psgd_last_error", "psgd_version",
+    "psgd_timing_enable", "psgd_timing_read", "psgd_stream_probe", "psgd_stream_copy", "psgd_last_error",
+    "psgd_version",
 ]
 
 
@@ -131,10 +132,12 @@ lib.psgd_init_q.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, ctypes.c_size_t, _vp
 lib.psgd_timing_enable.argtypes = [_vp, ctypes.c_int32]
 lib.psgd_timing_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
 lib.psgd_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+lib.psgd_stream_probe.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, ctypes.c_size_t, _vp, _vp]
 lib.psgd_last_error.restype = ctypes.c_char_p
 lib.psgd_version.restype = ctypes.c_char_p
 for _f in ["psgd_plan_create", "psgd_plan_get_info", "psgd_plan_tensor", "psgd_workspace_init", "psgd_compress",
-           "psgd_decompress", "psgd_refresh", "psgd_init_q", "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy"]:
+           "psgd_decompress", "psgd_refresh", "psgd_init_q", "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy",
+           "psgd_stream_probe"]:
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -231,3 +234,14 @@ def psgd_timing_read(plan: int):
 
 def psgd_stream_copy(dst: int, src: int, n: int, stream: int = 0) -> None:
     _check("psgd_stream_copy", lib.psgd_stream_copy(dst, src, n, stream))
+
+
+PSGD_PROBE_SINK_FLOATS = 16384
+
+
+def psgd_stream_probe(ins, outs, n: int, sink: int = 0, stream: int = 0) -> None:
+    """ins / outs: device pointers (ints) of the arrays read / written."""
+    a_in = (ctypes.c_void_p * max(1, len(ins)))(*ins)
+    a_out = (ctypes.c_void_p * max(1, len(outs)))(*outs)
+    _check("psgd_stream_probe", lib.psgd_stream_probe(a_in if ins else None, len(ins), a_out if outs else None,
+                                                      len(outs), n, sink or None, stream))

@@ -473,6 +473,38 @@ extern "C" psgd_status_t psgd_timing_read(psgd_plan_t p, double* ms, int64_t* la
   return st;
 }
 
+extern "C" psgd_status_t psgd_stream_probe(const float* const* in, int32_t nin, float* const* out, int32_t nout,
+                                          size_t n, float* sink, hipStream_t stream) {
+  clear_error();
+  static_assert(PSGD_PROBE_SINK_FLOATS == kProbeMaxBlocks, "probe sink size");
+  if (nin < 0 || nin > 3 || nout < 0 || nout > 2 || nin + nout == 0 || (nin > 0 && !in) || (nout > 0 && !out) ||
+      (nout == 0 && !sink) || (n & 3u)) {
+    set_error("psgd_stream_probe: need 0..3 inputs, 0..2 outputs (at least one array), a sink without outputs "
+              "and n a multiple of 4 (nin=%d nout=%d n=%zu)", nin, nout, n);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  ProbeArgs a{};
+  for (int k = 0; k < nin; ++k) {
+    if (!in[k] || !aligned16(in[k])) {
+      set_error("psgd_stream_probe: input %d is NULL or not 16-byte aligned", k);
+      return PSGD_ERR_INVALID_ARG;
+    }
+    a.in[k] = reinterpret_cast<const float4*>(in[k]);
+  }
+  for (int j = 0; j < nout; ++j) {
+    if (!out[j] || !aligned16(out[j])) {
+      set_error("psgd_stream_probe: output %d is NULL or not 16-byte aligned", j);
+      return PSGD_ERR_INVALID_ARG;
+    }
+    a.out[j] = reinterpret_cast<float4*>(out[j]);
+  }
+  a.sink = sink;
+  a.n4 = (int64_t)(n / 4);
+  const hipError_t e = launch_stream_probe(a, nin, nout, stream);
+  if (e != hipSuccess) return hip_fail(e, "psgd_stream_probe");
+  return PSGD_OK;
+}
+
 extern "C" psgd_status_t psgd_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream) {
   clear_error();
   if (!dst || !src || (n & 3u) || ((uintptr_t)dst & 15u) || ((uintptr_t)src & 15u)) {

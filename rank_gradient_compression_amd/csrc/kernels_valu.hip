@@ -564,6 +564,54 @@ __global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, c
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
 }
 
+// Streaming-bandwidth probe: the byte pattern of a pass (NIN arrays read,
+// NOUT written) without its arithmetic, out_j[i] = sum_k in_k[i] (zero with
+// no input).  With no output the sums are reduced per workgroup into
+// sink[blockIdx.x], so the loads are not dead.  Each thread moves kProbeUnroll
+// 16-byte vectors per array per grid step, all loads issued before the sums.
+template <int NIN, int NOUT>
+__global__ __launch_bounds__(256) void k_stream_probe(ProbeArgs a) {
+  constexpr int U = kProbeUnroll;
+  __shared__ float wsum[4];
+  const int64_t stride = (int64_t)gridDim.x * 256 * U;
+  float part = 0.f;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x; i0 < a.n4; i0 += stride) {
+    float4 x[NIN > 0 ? NIN : 1][U];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + (int64_t)u * 256;
+        x[k][u] = i < a.n4 ? a.in[k][i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < NIN; ++k) {
+        v.x += x[k][u].x;
+        v.y += x[k][u].y;
+        v.z += x[k][u].z;
+        v.w += x[k][u].w;
+      }
+      const int64_t i = i0 + (int64_t)u * 256;
+      if constexpr (NOUT == 0) {
+        part += (v.x + v.y) + (v.z + v.w);
+      } else if (i < a.n4) {
+#pragma unroll
+        for (int j = 0; j < NOUT; ++j) a.out[j][i] = v;
+      }
+    }
+  }
+  if constexpr (NOUT == 0) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) a.sink[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  }
+}
+
 // Payload quantiser: every value rounded to the nearest bfloat16 (ties to
 // even), kept in fp32 storage.  Adding 0x7fff plus the lowest kept bit to the
 // fp32 pattern and clearing the low half rounds the magnitude to 8
@@ -725,6 +773,21 @@ hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_
   if (blocks > 256 * 64) blocks = 256 * 64;
   hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float4*>(dst),
                      reinterpret_cast<const float4*>(src), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_probe(const ProbeArgs& a, int nin, int nout, hipStream_t stream) {
+  if (a.n4 == 0) return hipSuccess;
+  int64_t blocks = (a.n4 + 256 * kProbeUnroll - 1) / (256 * kProbeUnroll);
+  if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
+  const dim3 g((unsigned)blocks), b(256);
+#define PSGD_PROBE(I, O) \
+  if (nin == I && nout == O) hipLaunchKernelGGL((k_stream_probe<I, O>), g, b, 0, stream, a)
+  PSGD_PROBE(0, 1); PSGD_PROBE(0, 2);
+  PSGD_PROBE(1, 0); PSGD_PROBE(1, 1); PSGD_PROBE(1, 2);
+  PSGD_PROBE(2, 0); PSGD_PROBE(2, 1); PSGD_PROBE(2, 2);
+  PSGD_PROBE(3, 0); PSGD_PROBE(3, 1); PSGD_PROBE(3, 2);
+#undef PSGD_PROBE
   return hipGetLastError();
 }
 

@@ -97,4 +97,17 @@ hipError_t launch_round_bf16(float* buf, int64_t n, hipStream_t stream);
 
 hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);
 
+// Streaming-bandwidth probe (psgd_stream_probe): up to 3 inputs, 2 outputs,
+// n4 16-byte vectors each; sink holds one float per workgroup when there is
+// no output.
+constexpr int kProbeUnroll = 4;
+constexpr int kProbeMaxBlocks = 16384;
+struct ProbeArgs {
+  const float4* in[3];
+  float4* out[2];
+  float* sink;
+  int64_t n4;
+};
+hipError_t launch_stream_probe(const ProbeArgs& a, int nin, int nout, hipStream_t stream);
+
 }  // namespace psgd

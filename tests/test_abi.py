@@ -260,6 +260,22 @@ def test_stream_copy_argument_errors():
         R.psgd_stream_copy(FAKE, FAKE, 3)
 
 
+@pytest.mark.parametrize("nin,nout,n,sink", [(0, 0, 16, True), (4, 1, 16, True), (1, 3, 16, True),
+                                             (1, 0, 16, False), (1, 1, 6, True)])
+def test_stream_probe_argument_errors(nin, nout, n, sink):
+    with pytest.raises(B.PsgdError) as e:
+        R.psgd_stream_probe([FAKE] * nin, [FAKE * 2] * nout, n, FAKE * 3 if sink else 0)
+    assert e.value.status == B.PSGD_ERR_INVALID_ARG
+
+
+def test_stream_probe_misaligned_array():
+    with pytest.raises(B.PsgdError) as e:
+        R.psgd_stream_probe([FAKE, FAKE + 4], [FAKE * 2], 16)
+    assert e.value.status == B.PSGD_ERR_INVALID_ARG
+    with pytest.raises(B.PsgdError):
+        R.psgd_stream_probe([FAKE], [FAKE * 2 + 8], 16)
+
+
 def test_timing_read_without_records():
     p = R.psgd_plan_create([64], [48], 2)
     ms, n = R.psgd_timing_read(p)

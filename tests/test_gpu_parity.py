@@ -297,6 +297,26 @@ def test_stream_copy():
     assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("nin,nout", [(0, 1), (1, 0), (1, 1), (2, 1), (1, 2), (3, 2), (3, 0)])
+def test_stream_probe(nin, nout):
+    """The bandwidth probe moves the bytes it claims: every output is the
+    sum of the inputs, and without outputs the per-workgroup sums add up to
+    the total (a ragged length exercises the bounds)."""
+    n = (1 << 20) + 4 * 37
+    ins = [torch.randn(n, device=DEV) for _ in range(nin)]
+    outs = [torch.full((n,), 7.0, device=DEV) for _ in range(nout)]
+    sink = torch.zeros(B.PSGD_PROBE_SINK_FLOATS, device=DEV)
+    B.psgd_stream_probe([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, sink.data_ptr(),
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    want = sum(t.double() for t in ins) if ins else torch.zeros(n, dtype=torch.float64, device=DEV)
+    for o in outs:
+        assert torch.allclose(o.double(), want, rtol=0, atol=1e-5)
+    if nout == 0:
+        got = sink.double().sum().item()
+        assert abs(got - want.sum().item()) <= 1e-3 * max(1.0, want.abs().sum().item() / n ** 0.5)
+
+
 def test_empty_and_vector_only_plans_run():
     ps = PowerSGD([(5,), (7,)], 2, device=DEV)
     ps.view(ps.grads, 0).fill_(1.0)
