@@ -86,6 +86,7 @@ static LaunchCtx make_ctx(const psgd_plan* p, void* ws, hipStream_t s) {
   c.nmat = h.nmat;
   c.npass = h.npass;
   c.wg_rows = h.wg_rows;
+  c.wg_rec = h.wg_rec;
   c.wg_mtp = h.wg_mtp;
   c.wg_red = h.wg_red;
   c.wg_pass = h.wg_pass;
@@ -96,6 +97,7 @@ static LaunchCtx make_ctx(const psgd_plan* p, void* ws, hipStream_t s) {
   c.pass = reinterpret_cast<const PassDesc*>(b + h.pass_off);
   c.orth = reinterpret_cast<const OrthDesc*>(b + h.orth_off);
   c.rows_map = reinterpret_cast<const int32_t*>(b + h.rows_map_off);
+  c.rec_map = reinterpret_cast<const int32_t*>(b + h.rec_map_off);
   c.mtp_map = reinterpret_cast<const int32_t*>(b + h.mtp_map_off);
   c.red_map = reinterpret_cast<const int32_t*>(b + h.red_map_off);
   c.pass_map = reinterpret_cast<const int32_t*>(b + h.pass_map_off);

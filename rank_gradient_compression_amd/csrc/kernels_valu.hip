@@ -272,16 +272,16 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, in
 }
 
 // Row tile and column range of a pass-1 / pass-3 workgroup: the matrix's
-// workgroups run over (row tile, column split), splits fastest.
+// workgroups (`local` counts from its first one) run over (row tile, column
+// split), splits fastest; `splits` of `cols` columns each.
 struct RowTile {
   int row0, c0, c1, split;
 };
 
-__device__ __forceinline__ RowTile row_tile(const MatDesc& d, int wg, int wave) {
-  const int local = wg - d.wg_rows0;
-  const int tile = local / d.s1, split = local - tile * d.s1;
-  const int c0 = split * d.s1_cols;
-  return RowTile{tile * kRowsPerWG + wave * kWaveRows, c0, min(d.n, c0 + d.s1_cols), split};
+__device__ __forceinline__ RowTile row_tile(const MatDesc& d, int local, int splits, int cols, int wave) {
+  const int tile = local / splits, split = local - tile * splits;
+  const int c0 = split * cols;
+  return RowTile{tile * kRowsPerWG + wave * kWaveRows, c0, min(d.n, c0 + cols), split};
 }
 
 // P (or, for a column-split matrix, the split's partial in ppart, summed
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__
   const MatDesc d = mats[map[wg]];
   // wave index made provably uniform: row addressing and P_hat loads go scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const RowTile t = row_tile(d, wg, wave);
+  const RowTile t = row_tile(d, wg - d.wg_rows0, d.s1, d.s1_cols, wave);
   if (t.row0 >= d.m) return;
   float* pdst = d.s1 > 1 ? ppart + d.ppart_off + (int64_t)t.split * R * d.m : P + (p_fixed >= 0 ? p_fixed : d.p_off);
   if (d.vec == 4)
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kWGThreads) void k_recon(const MatDesc* __restrict_
   const MatDesc d = mats[map[wg]];
   // wave index made provably uniform: row addressing and P_hat loads go scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const RowTile t = row_tile(d, wg, wave);
+  const RowTile t = row_tile(d, wg - d.wg_rec0, d.s3, d.s3_cols, wave);
   if (t.row0 >= d.m) return;
   if (d.vec == 4)
     recon_wave<R, 4, RESID, WRITE_MHAT, SGD>(d, t.row0, t.c0, t.c1, lane, E, Q, Ph, Mhat, sg);
@@ -686,11 +686,11 @@ static hipError_t launch_mtp_r(const LaunchCtx& c, const GridRange& g, const flo
 template <int R>
 static hipError_t launch_recon_r(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
                                  bool residual, const SgdArgs& sg) {
-  if (c.wg_rows == 0) return hipSuccess;
-  const dim3 g(c.wg_rows), b(kWGThreads);
+  if (c.wg_rec == 0) return hipSuccess;
+  const dim3 g(c.wg_rec), b(kWGThreads);
   const bool mh = Mhat != nullptr, sgd = sg.x != nullptr;
 #define PSGD_RECON(RS, MH, SG)                                                                                  \
-  hipLaunchKernelGGL((k_recon<R, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rows_map, E, Q, Ph, Mhat, sg)
+  hipLaunchKernelGGL((k_recon<R, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rec_map, E, Q, Ph, Mhat, sg)
   if (residual) {
     if (mh && sgd) PSGD_RECON(true, true, true);
     else if (mh) PSGD_RECON(true, true, false);

@@ -200,17 +200,31 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   const bool mfma = rank > kValuMaxRank;
   const int64_t rp = align_up(r, 16);  // rank padding of the matrix-core and Gram kernels
   const int32_t rb = choose_rb_rows(p->mats, r, mfma);
-  // Passes 1 and 3 split the columns until the grid covers the chip (a set
-  // of few, short matrices otherwise leaves compute units idle).
+  // Column splits of passes 1 and 3.  Matrix cores: split until the grid
+  // covers the chip (a set of few, short matrices otherwise leaves compute
+  // units idle); passes 1 and 3 share the split.  Vector ALU: pass 1 in
+  // kEfpSplitCols-column pieces, halved while the grid is short of
+  // kRowTilesTarget workgroups; pass 3 in kRecSplitCols-column pieces.
   const int32_t tile_rows = mfma ? kMfmaRows : kRowsPerWG;
-  int32_t s1 = 1;
+  int32_t s1 = 1, w1 = kEfpSplitCols;
   {
     int64_t base = 0;
     for (const MatDesc& d : p->mats) base += (d.m + tile_rows - 1) / tile_rows;
-    while (base * s1 < kRowTilesTarget && s1 < 64) s1 *= 2;
+    if (mfma) {
+      while (base * s1 < kRowTilesTarget && s1 < 64) s1 *= 2;
+    } else {
+      for (;; w1 /= 2) {
+        int64_t wgs = 0;
+        for (const MatDesc& d : p->mats) {
+          const int64_t cols = align_up(std::min<int64_t>(d.n, w1), 64 * d.vec);
+          wgs += ((d.m + tile_rows - 1) / tile_rows) * ((d.n + cols - 1) / cols);
+        }
+        if (wgs >= kRowTilesTarget || w1 <= 256) break;
+      }
+    }
   }
   int64_t part = 0, ppart = 0, gram = 0, rscr = 0;
-  int32_t wg_rows = 0, wg_mtp = 0, wg_red = 0, wg_pred = 0, wg_gram = 0;
+  int32_t wg_rows = 0, wg_rec = 0, wg_mtp = 0, wg_red = 0, wg_pred = 0, wg_gram = 0;
   for (size_t k = 0; k < p->mats.size(); ++k) {
     MatDesc& d = p->mats[k];
     d.rb_rows = rb;
@@ -224,13 +238,22 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     d.red_split = 1;
     while (d.red_split < kRedWaves && (d.nrb + d.red_split - 1) / d.red_split > 8) d.red_split *= 2;
     d.wg_rows0 = wg_rows;
-    // column splits of passes 1 and 3: a split is a multiple of one
-    // wavefront's columns (64 for the matrix cores, 64 vectors otherwise)
+    d.wg_rec0 = wg_rec;
+    // column splits: a split is a whole number of wavefront widths (64
+    // columns on the matrix cores, 64 vectors otherwise)
     const int32_t unit = mfma ? 64 : 64 * d.vec;
-    const int32_t sm = std::max<int32_t>(1, std::min<int32_t>(s1, d.n / (mfma ? 256 : unit)));
-    d.s1_cols = (int32_t)align_up((d.n + sm - 1) / sm, unit);
+    if (mfma) {
+      const int32_t sm = std::max<int32_t>(1, std::min<int32_t>(s1, d.n / 256));
+      d.s1_cols = (int32_t)align_up((d.n + sm - 1) / sm, unit);
+      d.s3_cols = d.s1_cols;
+    } else {
+      d.s1_cols = (int32_t)align_up(std::min<int32_t>(d.n, w1), unit);
+      d.s3_cols = (int32_t)align_up(std::min<int32_t>(d.n, kRecSplitCols), unit);
+    }
     d.s1 = (d.n + d.s1_cols - 1) / d.s1_cols;
-    const int32_t nrow_wg = ((d.m + tile_rows - 1) / tile_rows) * d.s1;
+    d.s3 = (d.n + d.s3_cols - 1) / d.s3_cols;
+    const int32_t row_tiles = (d.m + tile_rows - 1) / tile_rows;
+    const int32_t nrow_wg = row_tiles * d.s1, nrec_wg = row_tiles * d.s3;
     d.ppart_off = ppart;
     d.wg_pred0 = wg_pred;
     if (d.s1 > 1) {
@@ -241,6 +264,8 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     }
     for (int32_t t = 0; t < nrow_wg; ++t) p->rows_map.push_back((int32_t)k);
     wg_rows += nrow_wg;
+    for (int32_t t = 0; t < nrec_wg; ++t) p->rec_map.push_back((int32_t)k);
+    wg_rec += nrec_wg;
     // Gram grid (orthonormalisation of P) and the Gram scratch, sized for P
     // (m rows) and for the refresh's Q (n rows)
     d.ngb = (d.m + kGramRows - 1) / kGramRows;
@@ -309,6 +334,7 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   h.rank = rank;
   h.flags = (int32_t)flags;
   h.wg_rows = wg_rows;
+  h.wg_rec = wg_rec;
   h.wg_mtp = wg_mtp;
   h.wg_red = wg_red;
   h.wg_pass = wg_pass;
@@ -324,6 +350,8 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   b = align_up(b + (int64_t)sizeof(PassDesc) * h.npass, 256);
   h.rows_map_off = b;
   b = align_up(b + 4 * (int64_t)p->rows_map.size(), 256);
+  h.rec_map_off = b;
+  b = align_up(b + 4 * (int64_t)p->rec_map.size(), 256);
   h.mtp_map_off = b;
   b = align_up(b + 4 * (int64_t)p->mtp_map.size(), 256);
   h.red_map_off = b;
@@ -355,6 +383,8 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   if (h.npass) memcpy(p->tables.data() + h.pass_off, p->pass.data(), sizeof(PassDesc) * h.npass);
   if (!p->rows_map.empty())
     memcpy(p->tables.data() + h.rows_map_off, p->rows_map.data(), 4 * p->rows_map.size());
+  if (!p->rec_map.empty())
+    memcpy(p->tables.data() + h.rec_map_off, p->rec_map.data(), 4 * p->rec_map.size());
   if (!p->mtp_map.empty())
     memcpy(p->tables.data() + h.mtp_map_off, p->mtp_map.data(), 4 * p->mtp_map.size());
   if (!p->red_map.empty())

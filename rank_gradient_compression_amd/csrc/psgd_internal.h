@@ -34,7 +34,7 @@ struct psgd_plan {
   std::vector<psgd::MatDesc> mats;
   std::vector<int32_t> mat_tensor;  // tensor index of each compressed matrix
   std::vector<psgd::PassDesc> pass;
-  std::vector<int32_t> rows_map, mtp_map, red_map, pass_map, pred_map, gram_map, gramq_map;
+  std::vector<int32_t> rows_map, rec_map, mtp_map, red_map, pass_map, pred_map, gram_map, gramq_map;
   std::vector<psgd::OrthDesc> orth;  // 3 * nmat
   psgd::WsHeader hdr{};
   std::vector<uint8_t> tables;  // hdr + all tables, as uploaded

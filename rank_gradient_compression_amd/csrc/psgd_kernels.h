@@ -21,11 +21,12 @@ struct LaunchCtx {
   bool g_bf16;  // gradients stored as bfloat16
   const float* p_prev;  // deferred residual: the previous step's P_hat (plan offsets)
   int nmat, npass;
-  int wg_rows, wg_mtp, wg_red, wg_pass, wg_pred, wg_gram, wg_gramq;
+  int wg_rows, wg_rec, wg_mtp, wg_red, wg_pass, wg_pred, wg_gram, wg_gramq;
   const MatDesc* mats;
   const PassDesc* pass;
   const OrthDesc* orth;
-  const int32_t* rows_map;
+  const int32_t* rows_map;  // pass-1 row tiles (and the matrix-core pass 3)
+  const int32_t* rec_map;   // vector-ALU residual / decompression pass
   const int32_t* mtp_map;
   const int32_t* red_map;
   const int32_t* pass_map;

@@ -47,19 +47,22 @@ struct MatDesc {
   int32_t nrb;       // row blocks of the M^T P_hat pass
   int32_t rb_rows;   // rows per row block of the M^T P_hat pass
   int32_t ncb;       // column tiles of the M^T P_hat pass
-  int32_t wg_rows0;  // first workgroup of this matrix in the row-tile grid
+  int32_t wg_rows0;  // first workgroup of this matrix in the pass-1 row-tile grid
   int32_t wg_mtp0;   // first workgroup of this matrix in the M^T P_hat grid
   int32_t wg_red0;   // first workgroup of this matrix in the Q-reduce grid
-  int32_t s1;        // passes 1 and 3: column splits
-  int32_t s1_cols;   // passes 1 and 3: columns per split (whole wavefront widths)
+  int32_t s1;        // pass 1 (and the matrix-core pass 3): column splits
+  int32_t s1_cols;   // pass 1: columns per split (whole wavefront widths)
   int32_t wg_pred0;  // first workgroup in the P-partial reduce grid (s1 > 1)
   int32_t wg_gram0;  // first workgroup in the Gram-partial / apply grid
   int32_t ngb;       // Gram-partial blocks (kGramRows rows each)
   int32_t tensor;    // index of the tensor in the plan
   int32_t red_split; // wavefronts summing one 64-element slice of Q partials
-  int32_t pad_[2];
+  int32_t s3;        // residual / decompression pass: column splits
+  int32_t s3_cols;   // residual / decompression pass: columns per split
+  int32_t wg_rec0;   // first workgroup of this matrix in the residual-pass grid
+  int32_t pad_[3];
 };
-static_assert(sizeof(MatDesc) == 128, "MatDesc layout");
+static_assert(sizeof(MatDesc) == 144, "MatDesc layout");
 
 // One pass-through tensor: `len` elements at flat offset `off`, packed at
 // `p_off` (absolute, in the P buffer).
@@ -91,16 +94,26 @@ constexpr int kRedWaves = 16;     // wavefronts of one Q-reduce workgroup
 // grid has this many).
 constexpr int kRowTilesTarget = 1024;
 
+// Column splits of the vector-ALU passes.  A wavefront streams 8 rows of its
+// split, so the split width sets how much of each array it touches: pass 1
+// (two arrays read, one written, plus the P row sums at the end) is split
+// into kEfpSplitCols-column pieces (narrower while the grid is short of
+// kRowTilesTarget workgroups, down to one wavefront width), the residual pass
+// (one read, two written, nothing to reduce) into kRecSplitCols-column pieces.
+constexpr int kEfpSplitCols = 1024;
+constexpr int kRecSplitCols = 256;
+
 // Header at the start of the workspace.
 struct WsHeader {
   uint64_t magic;
   int32_t nmat, npass;
   int32_t rank, flags;
   int32_t wg_rows, wg_mtp, wg_red, wg_pass;
-  int32_t wg_pred, wg_gram, wg_gramq, rank_pad, mfma, pad_;
+  int32_t wg_pred, wg_gram, wg_gramq, rank_pad, mfma, wg_rec;
   int64_t mat_off;       // bytes from workspace start: MatDesc[nmat]
   int64_t pass_off;      // PassDesc[npass]
-  int64_t rows_map_off;  // int32 matrix index per row-tile workgroup
+  int64_t rows_map_off;  // int32 matrix index per row-tile workgroup (pass 1)
+  int64_t rec_map_off;   // int32 matrix index per residual-pass workgroup
   int64_t mtp_map_off;   // int32 per M^T P_hat workgroup
   int64_t red_map_off;   // int32 per Q-reduce workgroup
   int64_t pass_map_off;  // int32 pass-through tensor per pass-through workgroup
