@@ -60,8 +60,10 @@ __device__ __forceinline__ void stv(float* p, const Vec<VEC>& a) {
 
 // Non-temporal (streaming) variants: the nt bit on the access tells the
 // caches the line will not be reused soon.  Measured on the grouped 7B-shaped
-// set: streaming loads of G and of M in the residual pass and a streaming
-// store of M_hat shave about 2% off a step; a streaming store of E or M costs.
+// set: streaming loads of G and of M in the residual pass and streaming
+// stores of M_hat and E there shave a few percent off a step (E is read
+// again only by the next step); a streaming store of M in pass 1 costs (the
+// next pass reads it).
 typedef float v4f_nt __attribute__((ext_vector_type(4)));
 typedef float v2f_nt __attribute__((ext_vector_type(2)));
 typedef uint32_t v2u_nt __attribute__((ext_vector_type(2)));
@@ -470,7 +472,7 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int c0, i
           Vec<VEC> e;
 #pragma unroll
           for (int c = 0; c < VEC; ++c) e.v[c] = x[rr].v[c] - mh.v[c];
-          stv<VEC>(E + idx, e);
+          stv_nt<VEC>(E + idx, e);
         }
         // M_hat is consumed by the optimizer after the step, not by this
         // pipeline: streaming store.
