@@ -578,7 +578,7 @@ __global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mat
 // ---------------------------------------------------------------------------
 // Pass 3: M_hat = P_hat Q^T (transposed on the matrix core); residual and/or
 // decompression.  One wavefront: 64 rows (four 16-row tiles) and every fourth
-// 16-column tile of the workgroup's column split.
+// pair of 16-column tiles of the workgroup's column split.
 // ---------------------------------------------------------------------------
 
 template <int RP, bool READ_M, bool WRITE_E, bool WRITE_MHAT, bool SGD, bool VEC4>
@@ -587,10 +587,10 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
                                                 float* __restrict__ Mhat, const SgdArgs& sg) {
   constexpr int KS = RP / 4;  // k-steps of 4 rank columns
   const int m = d.m, n = d.n;
-  const int local = wg - d.wg_rows0;
-  const int rb = local / d.s1, split = local - rb * d.s1;
-  const int c_begin = split * d.s1_cols;
-  const int c_end = min(n, c_begin + d.s1_cols);
+  const int local = wg - d.wg_rec0;
+  const int rb = local / d.s3, split = local - rb * d.s3;
+  const int c_begin = split * d.s3_cols;
+  const int c_end = min(n, c_begin + d.s3_cols);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
   const int i0 = rb * kMfmaRows;
@@ -635,11 +635,16 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
     }
   };
 
+  // A wavefront takes pairs of adjacent 16-column tiles (tiles 2w, 2w + 1,
+  // 2w + 8, 2w + 9, ...), so each 128-byte line of E and M_hat is written
+  // whole by one wavefront in two consecutive stores, never half by each of
+  // two wavefronts.
   Step cur, nxt;
-  int j0 = c_begin + 16 * wave;
+  int j0 = c_begin + 32 * wave;
   if (j0 < c_end) load(j0, cur);
-  for (; j0 < c_end; j0 += 64) {
-    if (j0 + 64 < c_end) load(j0 + 64, nxt);
+  while (j0 < c_end) {
+    const int jn = (((j0 - c_begin) >> 4) & 1) ? j0 + 112 : j0 + 16;
+    if (jn < c_end) load(jn, nxt);
     const int col = j0 + 4 * ls;
     const bool col_ok = col < c_end;
 #pragma unroll
@@ -679,6 +684,7 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
       }
     }
     cur = nxt;
+    j0 = jn;
   }
 }
 
@@ -981,11 +987,11 @@ hipError_t launch_mfma_qt(const LaunchCtx& c, const GridRange& g, const float* M
 template <int RP>
 static hipError_t mfma_recon_rp(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
                                 bool residual, const SgdArgs& sg) {
-  if (c.wg_rows == 0) return hipSuccess;
-  const dim3 g(c.wg_rows), b(256);
+  if (c.wg_rec == 0) return hipSuccess;
+  const dim3 g(c.wg_rec), b(256);
   const bool mh = Mhat != nullptr, sgd = sg.x != nullptr;
-#define PSGD_MRECON(RS, MH, SG)                                                                              \
-  hipLaunchKernelGGL((k_mfma_recon<RP, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rows_map, 0, c.rank, E, Q, Ph, \
+#define PSGD_MRECON(RS, MH, SG)                                                                             \
+  hipLaunchKernelGGL((k_mfma_recon<RP, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rec_map, 0, c.rank, E, Q, Ph, \
                      Mhat, sg)
   if (residual) {
     if (mh && sgd) PSGD_MRECON(true, true, true);

@@ -200,28 +200,20 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   const bool mfma = rank > kValuMaxRank;
   const int64_t rp = align_up(r, 16);  // rank padding of the matrix-core and Gram kernels
   const int32_t rb = choose_rb_rows(p->mats, r, mfma);
-  // Column splits of passes 1 and 3.  Matrix cores: split until the grid
-  // covers the chip (a set of few, short matrices otherwise leaves compute
-  // units idle); passes 1 and 3 share the split.  Vector ALU: pass 1 in
-  // kEfpSplitCols-column pieces, halved while the grid is short of
-  // kRowTilesTarget workgroups; pass 3 in kRecSplitCols-column pieces.
+  // Column splits of passes 1 and 3.  A wavefront streams a few rows of its
+  // split, so the split width sets how much of each array a workgroup
+  // touches at once: pass 1 in kEfpSplitCols-column pieces (halved, down to
+  // 256 columns, while the grid is short of kRowTilesTarget workgroups, as
+  // for a set of few, short matrices), pass 3 in kRecSplitCols-column pieces.
   const int32_t tile_rows = mfma ? kMfmaRows : kRowsPerWG;
-  int32_t s1 = 1, w1 = kEfpSplitCols;
-  {
-    int64_t base = 0;
-    for (const MatDesc& d : p->mats) base += (d.m + tile_rows - 1) / tile_rows;
-    if (mfma) {
-      while (base * s1 < kRowTilesTarget && s1 < 64) s1 *= 2;
-    } else {
-      for (;; w1 /= 2) {
-        int64_t wgs = 0;
-        for (const MatDesc& d : p->mats) {
-          const int64_t cols = align_up(std::min<int64_t>(d.n, w1), 64 * d.vec);
-          wgs += ((d.m + tile_rows - 1) / tile_rows) * ((d.n + cols - 1) / cols);
-        }
-        if (wgs >= kRowTilesTarget || w1 <= 256) break;
-      }
+  int32_t w1 = kEfpSplitCols;
+  for (;; w1 /= 2) {
+    int64_t wgs = 0;
+    for (const MatDesc& d : p->mats) {
+      const int64_t cols = align_up(std::min<int64_t>(d.n, w1), mfma ? 64 : 64 * d.vec);
+      wgs += ((d.m + tile_rows - 1) / tile_rows) * ((d.n + cols - 1) / cols);
     }
+    if (wgs >= kRowTilesTarget || w1 <= 256) break;
   }
   int64_t part = 0, ppart = 0, gram = 0, rscr = 0;
   int32_t wg_rows = 0, wg_rec = 0, wg_mtp = 0, wg_red = 0, wg_pred = 0, wg_gram = 0;
@@ -242,14 +234,8 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     // column splits: a split is a whole number of wavefront widths (64
     // columns on the matrix cores, 64 vectors otherwise)
     const int32_t unit = mfma ? 64 : 64 * d.vec;
-    if (mfma) {
-      const int32_t sm = std::max<int32_t>(1, std::min<int32_t>(s1, d.n / 256));
-      d.s1_cols = (int32_t)align_up((d.n + sm - 1) / sm, unit);
-      d.s3_cols = d.s1_cols;
-    } else {
-      d.s1_cols = (int32_t)align_up(std::min<int32_t>(d.n, w1), unit);
-      d.s3_cols = (int32_t)align_up(std::min<int32_t>(d.n, kRecSplitCols), unit);
-    }
+    d.s1_cols = (int32_t)align_up(std::min<int32_t>(d.n, w1), unit);
+    d.s3_cols = (int32_t)align_up(std::min<int32_t>(d.n, kRecSplitCols), unit);
     d.s1 = (d.n + d.s1_cols - 1) / d.s1_cols;
     d.s3 = (d.n + d.s3_cols - 1) / d.s3_cols;
     const int32_t row_tiles = (d.m + tile_rows - 1) / tile_rows;

@@ -25,8 +25,8 @@ struct LaunchCtx {
   const MatDesc* mats;
   const PassDesc* pass;
   const OrthDesc* orth;
-  const int32_t* rows_map;  // pass-1 row tiles (and the matrix-core pass 3)
-  const int32_t* rec_map;   // vector-ALU residual / decompression pass
+  const int32_t* rows_map;  // pass-1 row tiles
+  const int32_t* rec_map;   // residual / decompression pass row tiles
   const int32_t* mtp_map;
   const int32_t* red_map;
   const int32_t* pass_map;

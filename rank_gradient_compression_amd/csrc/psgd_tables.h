@@ -50,7 +50,7 @@ struct MatDesc {
   int32_t wg_rows0;  // first workgroup of this matrix in the pass-1 row-tile grid
   int32_t wg_mtp0;   // first workgroup of this matrix in the M^T P_hat grid
   int32_t wg_red0;   // first workgroup of this matrix in the Q-reduce grid
-  int32_t s1;        // pass 1 (and the matrix-core pass 3): column splits
+  int32_t s1;        // pass 1: column splits
   int32_t s1_cols;   // pass 1: columns per split (whole wavefront widths)
   int32_t wg_pred0;  // first workgroup in the P-partial reduce grid (s1 > 1)
   int32_t wg_gram0;  // first workgroup in the Gram-partial / apply grid
@@ -94,12 +94,13 @@ constexpr int kRedWaves = 16;     // wavefronts of one Q-reduce workgroup
 // grid has this many).
 constexpr int kRowTilesTarget = 1024;
 
-// Column splits of the vector-ALU passes.  A wavefront streams 8 rows of its
-// split, so the split width sets how much of each array it touches: pass 1
-// (two arrays read, one written, plus the P row sums at the end) is split
-// into kEfpSplitCols-column pieces (narrower while the grid is short of
-// kRowTilesTarget workgroups, down to one wavefront width), the residual pass
-// (one read, two written, nothing to reduce) into kRecSplitCols-column pieces.
+// Column splits of passes 1 and 3.  A workgroup streams a few rows of its
+// split, so the split width sets how much of each array it touches at once:
+// pass 1 (two arrays read, one written, plus the P row sums at the end) is
+// split into kEfpSplitCols-column pieces (narrower, down to 256 columns,
+// while the grid is short of kRowTilesTarget workgroups), the residual pass
+// (one read, two written, nothing to reduce) into kRecSplitCols-column
+// pieces, each with its own grid.
 constexpr int kEfpSplitCols = 1024;
 constexpr int kRecSplitCols = 256;
 
