@@ -197,6 +197,12 @@ typedef struct psgd_plan_info {
  *
  * Classification ([N152] Method; the size rule is this library's reading of
  * "small tensors"): a matrix is compressed iff r*(rows+cols) < rows*cols.
+ *
+ * Errors: PSGD_ERR_INVALID_ARG for a NULL list or out, a size < 1 (or a
+ * vector's), a size above INT32_MAX, bad offsets or a NaN beta;
+ * PSGD_ERR_UNSUPPORTED for a rank above PSGD_MAX_RANK, unknown flags, or a
+ * compressed matrix with 2^30 columns or more (rows are addressed with
+ * 32-bit byte offsets).
  */
 psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows, const int64_t* cols,
                                const int64_t* offsets, int32_t rank, uint32_t flags, float beta,

@@ -101,7 +101,7 @@ __device__ __forceinline__ Vec<VEC> ldv_nt(const float* p) {
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 template <int VEC, bool BF16>
-__device__ __forceinline__ Vec<VEC> ldg(const void* G, int64_t idx) {
+__device__ __forceinline__ Vec<VEC> ldg(const void* G, unsigned idx) {
   if constexpr (!BF16) {
     return ldv_nt<VEC>(static_cast<const float*>(G) + idx);
   } else {
@@ -122,6 +122,19 @@ __device__ __forceinline__ Vec<VEC> ldg(const void* G, int64_t idx) {
     }
     return r;
   }
+}
+
+// Element j of a row whose base pointer is wavefront-uniform, addressed by a
+// 32-bit byte offset (the scalar-base + vector-offset form of the memory
+// instructions; rows are shorter than 2^30 elements).
+__device__ __forceinline__ const float* at_row(const float* rowp, unsigned j) {
+  return reinterpret_cast<const float*>(reinterpret_cast<const char*>(rowp) + (j << 2));
+}
+__device__ __forceinline__ float* at_row(float* rowp, unsigned j) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(rowp) + (j << 2));
+}
+__device__ __forceinline__ const void* at_row_g(const void* rowp, unsigned j, bool bf16) {
+  return static_cast<const char*>(rowp) + (bf16 ? (j << 1) : (j << 2));
 }
 
 // Sum of NV per-lane values over the 64 lanes of a wavefront, transposed: on
@@ -211,28 +224,43 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, in
       for (int k = 0; k < R; ++k) ph[rr][k] = Pold[d.p_off + (int64_t)k * m + row0 + min(rr, nrows - 1)];
   }
 
-  const float* q = Q + d.q_off;
-  const int64_t base = d.off + (int64_t)row0 * n;
-  for (int j = c0 + lane * VEC; j < c1; j += 64 * VEC) {
+  // Row and Q-column base pointers are wavefront-uniform (scalar
+  // registers) and the lane's column is a 32-bit unsigned offset from them,
+  // so every access takes the scalar-base + vector-offset form (no 64-bit
+  // address per lane and row).  Rows past the matrix repeat its last row for
+  // the loads; their stores are skipped.
+  const float* qcol[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) qcol[k] = Q + d.q_off + (int64_t)k * n;
+  float* erow[kWaveRows];
+  const void* grow[kWaveRows];
+  float* urow[kWaveRows];
+#pragma unroll
+  for (int rr = 0; rr < kWaveRows; ++rr) {
+    const int64_t ro = d.off + (int64_t)(row0 + min(rr, nrows - 1)) * n;
+    erow[rr] = E + ro;
+    grow[rr] = GBF16 ? static_cast<const void*>(static_cast<const uint16_t*>(G) + ro)
+                     : static_cast<const void*>(static_cast<const float*>(G) + ro);
+    urow[rr] = U + ro;
+  }
+  for (unsigned j = (unsigned)(c0 + lane * VEC); j < (unsigned)c1; j += 64 * VEC) {
     Vec<VEC> qv[R];
 #pragma unroll
-    for (int k = 0; k < R; ++k) qv[k] = ldv<VEC>(q + (int64_t)k * n + j);
+    for (int k = 0; k < R; ++k) qv[k] = ldv<VEC>(at_row(qcol[k], j));
     Vec<VEC> g[kWaveRows], e[kWaveRows];
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
-      const int64_t idx = base + (int64_t)min(rr, nrows - 1) * n + j;
-      if constexpr (MODE != 0) g[rr] = ldg<VEC, GBF16>(G, idx);
-      if constexpr (LOAD_E) e[rr] = ldv<VEC>(E + idx);
+      if constexpr (MODE != 0) g[rr] = ldg<VEC, GBF16>(at_row_g(grow[rr], j, GBF16), 0u);
+      if constexpr (LOAD_E) e[rr] = ldv<VEC>(at_row(erow[rr], j));
     }
     Vec<VEC> u[kWaveRows];
     if constexpr (MOM) {
 #pragma unroll
-      for (int rr = 0; rr < kWaveRows; ++rr) u[rr] = ldv<VEC>(U + base + (int64_t)min(rr, nrows - 1) * n + j);
+      for (int rr = 0; rr < kWaveRows; ++rr) u[rr] = ldv<VEC>(at_row(urow[rr], j));
     }
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
       if (rr < nrows) {
-        const int64_t idx = base + (int64_t)rr * n + j;
         Vec<VEC> mv;
         if constexpr (DEFERRED) {
           const Vec<VEC> mh = recon_row<R, VEC>(ph[rr], qv);
@@ -244,14 +272,14 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, in
         } else if constexpr (MOM) {
 #pragma unroll
           for (int c = 0; c < VEC; ++c) u[rr].v[c] = fmaf(beta, u[rr].v[c], g[rr].v[c]);
-          stv<VEC>(U + idx, u[rr]);
+          stv<VEC>(at_row(urow[rr], j), u[rr]);
 #pragma unroll
           for (int c = 0; c < VEC; ++c) mv.v[c] = LOAD_E ? u[rr].v[c] + e[rr].v[c] : u[rr].v[c];
         } else {
 #pragma unroll
           for (int c = 0; c < VEC; ++c) mv.v[c] = LOAD_E ? g[rr].v[c] + e[rr].v[c] : g[rr].v[c];
         }
-        if constexpr (MODE != 0) stv<VEC>(E + idx, mv);
+        if constexpr (MODE != 0) stv<VEC>(at_row(erow[rr], j), mv);
 #pragma unroll
         for (int k = 0; k < R; ++k)
 #pragma unroll

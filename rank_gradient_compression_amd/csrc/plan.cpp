@@ -121,6 +121,13 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
       p->kind[i] = PSGD_KIND_VECTOR;
     else
       p->kind[i] = (r * (m + n) < m * n) ? PSGD_KIND_COMPRESSED : PSGD_KIND_PASSTHRU;
+    // the streaming kernels address a row with 32-bit byte offsets
+    if (p->kind[i] == PSGD_KIND_COMPRESSED && n >= kMaxCols) {
+      set_error("psgd_plan_create: tensor %d has %lld columns; a compressed matrix has fewer than %lld", i,
+                (long long)n, (long long)kMaxCols);
+      delete p;
+      return PSGD_ERR_UNSUPPORTED;
+    }
   }
 
   // Flat layout.

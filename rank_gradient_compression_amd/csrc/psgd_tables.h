@@ -24,6 +24,10 @@ constexpr int kMtpWaves = 4;
 // kernels.
 constexpr int kValuMaxRank = 8;
 
+// Columns a compressed matrix may have (exclusive): the streaming kernels
+// address a row from a wavefront-uniform base with a 32-bit byte offset.
+constexpr int64_t kMaxCols = int64_t(1) << 30;
+
 // Alignment (elements) of every region the plan lays out.
 constexpr int64_t kAlignElems = 64;
 

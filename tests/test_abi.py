@@ -127,6 +127,7 @@ def test_caller_offsets_accepted_and_checked():
     ([0], [4], 1, 0, B.PSGD_ERR_INVALID_ARG),
     ([4], [-1], 1, 0, B.PSGD_ERR_INVALID_ARG),
     ([4], [4], 1, 6, B.PSGD_ERR_UNSUPPORTED),
+    ([2], [1 << 30], 1, 0, B.PSGD_ERR_UNSUPPORTED),
 ])
 def test_plan_create_errors(rows, cols, rank, flags, status):
     with pytest.raises(B.PsgdError) as e:
