@@ -577,14 +577,25 @@ __global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mat
 
 // ---------------------------------------------------------------------------
 // Pass 3: M_hat = P_hat Q^T (transposed on the matrix core); residual and/or
-// decompression.  One wavefront: 64 rows (four 16-row tiles) and every fourth
-// pair of 16-column tiles of the workgroup's column split.
+// decompression.  A workgroup owns kRecRows rows x one kRecCols-column split.
+// Phase 1: the 16 x 16 tiles of M_hat^T = Q P_hat^T on the matrix core (a
+// wavefront takes four adjacent column tiles of both row tiles), each written
+// to LDS in its result layout (lane = one row, four consecutive columns).
+// Phase 2: each wavefront streams kWaveRows rows of the tile with
+// row-contiguous accesses -- 64 lanes x 16 bytes, one 1 KB row segment per
+// instruction -- reading M, writing E and M_hat (and the SGD state), as the
+// vector-ALU residual pass does.  A tile is summed over the rank in the same
+// matrix-core step order as the deferred-residual form of pass 1.
 // ---------------------------------------------------------------------------
 
-template <int RP, bool READ_M, bool WRITE_E, bool WRITE_MHAT, bool SGD, bool VEC4>
+constexpr int kRecRows = kRowsPerWG;  // rows of a workgroup tile (two 16-row tiles)
+constexpr int kRecLd = kRecSplitCols + 4;  // LDS row stride (floats)
+static_assert(kRecRows == 32 && kRecSplitCols == 256, "tile shape of the matrix-core residual pass");
+
+template <int RP, bool RESID, bool WRITE_MHAT, bool SGD, bool VEC4>
 __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r, float* __restrict__ E,
                                                 const float* __restrict__ Q, const float* __restrict__ Ph,
-                                                float* __restrict__ Mhat, const SgdArgs& sg) {
+                                                float* __restrict__ Mhat, const SgdArgs& sg, float* tile) {
   constexpr int KS = RP / 4;  // k-steps of 4 rank columns
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_rec0;
@@ -593,98 +604,90 @@ __device__ __forceinline__ void mfma_recon_body(const MatDesc& d, int wg, int r,
   const int c_end = min(n, c_begin + d.s3_cols);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
-  const int i0 = rb * kMfmaRows;
+  const int i0 = rb * kRecRows;
   const float* ph = Ph + d.p_off;
   const float* q = Q + d.q_off;
 
-  // B operand: P_hat^T, lane (li, ls) holds P_hat[i0 + 16 rt + li][4 kk + ls]
-  float bfr[4][KS];
+  // Phase 1.  B operand: P_hat^T, lane (li, ls) holds P_hat[i0 + 16 rt + li][4 kk + ls];
+  // A operand: Q, lane (li, ls) holds Q[column j0 + li][4 kk + ls].
+  float bfr[2][KS];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int rr = i0 + 16 * rt + li, t = 4 * kk + ls;
       bfr[rt][kk] = (rr < m && t < r) ? ph[(int64_t)t * m + rr] : 0.f;
     }
-
-  // Operands of one 16-column step: A = Q (lane (li, ls) holds
-  // Q[j0 + li][4 kk + ls]) and the matching row segments of M and of the SGD
-  // state.  The next step's loads are issued before the current step's matrix
-  // products and stores, so every wavefront keeps two steps of loads in flight.
-  struct Step {
-    float afr[KS];
-    float4 xm[4], xx[4], xb[4];
-  };
-  auto load = [&](int j0, Step& st) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int t = 4 * kk + ls, c = j0 + li;
-      st.afr[kk] = (t < r && c < c_end) ? q[(int64_t)t * n + c] : 0.f;
+  for (int u = 0; u < 4; ++u) {
+    const int ct = 4 * wave + u;
+    const int j0 = c_begin + 16 * ct;
+    if (j0 < c_end) {  // wavefront-uniform
+      float afr[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int t = 4 * kk + ls, c = j0 + li;
+        afr[kk] = (t < r && c < c_end) ? q[(int64_t)t * n + c] : 0.f;
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) acc = mfma16x16x4(afr[kk], bfr[rt][kk], acc);
+        *reinterpret_cast<float4*>(&tile[(16 * rt + li) * kRecLd + 16 * ct + 4 * ls]) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
     }
-    const int col = j0 + 4 * ls;
-    const bool col_ok = col < c_end;
+  }
+  __syncthreads();
+
+  // Phase 2: rows i0 + kWaveRows * wave + rr, columns c_begin + 4 lane .. + 3.
+  const int row_base = i0 + kWaveRows * wave;
+  const int nrows = min(kWaveRows, m - row_base);
+  if (nrows <= 0) return;
+  const int cl = 4 * lane, col = c_begin + cl;
+  const bool col_ok = col < c_end;
+  float4 x[kWaveRows], xx[kWaveRows], xb[kWaveRows];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int rr = i0 + 16 * rt + li;
-      const int64_t ro = d.off + (int64_t)min(rr, m - 1) * n;
-      if constexpr (READ_M) st.xm[rt] = ldq<VEC4>(E + ro, col, rr < m && col_ok, c_begin, n);
+  for (int rr = 0; rr < kWaveRows; ++rr) {
+    const int64_t ro = d.off + (int64_t)(row_base + min(rr, nrows - 1)) * n;
+    if constexpr (RESID) x[rr] = ldq_nt<VEC4>(E + ro, col, col_ok, c_begin, n);
+    if constexpr (SGD) {
+      xx[rr] = ldq<VEC4>(sg.x + ro, col, col_ok, c_begin, n);
+      xb[rr] = ldq<VEC4>(sg.m + ro, col, col_ok, c_begin, n);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < kWaveRows; ++rr) {
+    if (rr < nrows && col_ok) {
+      const int64_t ro = d.off + (int64_t)(row_base + rr) * n;
+      const float4 mh = *reinterpret_cast<const float4*>(&tile[(kWaveRows * wave + rr) * kRecLd + cl]);
+      if constexpr (RESID) {
+        const float4 xm = x[rr];
+        stq_nt<VEC4>(E + ro, col, n, make_float4(xm.x - mh.x, xm.y - mh.y, xm.z - mh.z, xm.w - mh.w));
+      }
+      if constexpr (WRITE_MHAT) stq_nt<VEC4>(Mhat + ro, col, n, mh);
       if constexpr (SGD) {
-        st.xx[rt] = ldq<VEC4>(sg.x + ro, col, rr < m && col_ok, c_begin, n);
-        st.xb[rt] = ldq<VEC4>(sg.m + ro, col, rr < m && col_ok, c_begin, n);
+        float4 mm = xb[rr], xp = xx[rr];
+        mm.x = fmaf(sg.mu, mm.x, mh.x);
+        mm.y = fmaf(sg.mu, mm.y, mh.y);
+        mm.z = fmaf(sg.mu, mm.z, mh.z);
+        mm.w = fmaf(sg.mu, mm.w, mh.w);
+        if (sg.nesterov) {
+          xp.x = fmaf(-sg.lr, fmaf(sg.mu, mm.x, mh.x), xp.x);
+          xp.y = fmaf(-sg.lr, fmaf(sg.mu, mm.y, mh.y), xp.y);
+          xp.z = fmaf(-sg.lr, fmaf(sg.mu, mm.z, mh.z), xp.z);
+          xp.w = fmaf(-sg.lr, fmaf(sg.mu, mm.w, mh.w), xp.w);
+        } else {
+          xp.x = fmaf(-sg.lr, mm.x, xp.x);
+          xp.y = fmaf(-sg.lr, mm.y, xp.y);
+          xp.z = fmaf(-sg.lr, mm.z, xp.z);
+          xp.w = fmaf(-sg.lr, mm.w, xp.w);
+        }
+        stq<VEC4>(sg.m + ro, col, n, mm);
+        stq<VEC4>(sg.x + ro, col, n, xp);
       }
     }
-  };
-
-  // A wavefront takes pairs of adjacent 16-column tiles (tiles 2w, 2w + 1,
-  // 2w + 8, 2w + 9, ...), so each 128-byte line of E and M_hat is written
-  // whole by one wavefront in two consecutive stores, never half by each of
-  // two wavefronts.
-  Step cur, nxt;
-  int j0 = c_begin + 32 * wave;
-  if (j0 < c_end) load(j0, cur);
-  while (j0 < c_end) {
-    const int jn = (((j0 - c_begin) >> 4) & 1) ? j0 + 112 : j0 + 16;
-    if (jn < c_end) load(jn, nxt);
-    const int col = j0 + 4 * ls;
-    const bool col_ok = col < c_end;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) acc = mfma16x16x4(cur.afr[kk], bfr[rt][kk], acc);
-      const int rr = i0 + 16 * rt + li;
-      if (rr < m && col_ok) {
-        float* rowp = E + d.off + (int64_t)rr * n;
-        const float4 mh = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        if constexpr (READ_M && WRITE_E) {
-          const float4 x = cur.xm[rt];
-          stq<VEC4>(rowp, col, n, make_float4(x.x - mh.x, x.y - mh.y, x.z - mh.z, x.w - mh.w));
-        }
-        if constexpr (WRITE_MHAT) stq_nt<VEC4>(Mhat + d.off + (int64_t)rr * n, col, n, mh);
-        if constexpr (SGD) {
-          float4 mm = cur.xb[rt], xp = cur.xx[rt];
-          mm.x = fmaf(sg.mu, mm.x, mh.x);
-          mm.y = fmaf(sg.mu, mm.y, mh.y);
-          mm.z = fmaf(sg.mu, mm.z, mh.z);
-          mm.w = fmaf(sg.mu, mm.w, mh.w);
-          if (sg.nesterov) {
-            xp.x = fmaf(-sg.lr, fmaf(sg.mu, mm.x, mh.x), xp.x);
-            xp.y = fmaf(-sg.lr, fmaf(sg.mu, mm.y, mh.y), xp.y);
-            xp.z = fmaf(-sg.lr, fmaf(sg.mu, mm.z, mh.z), xp.z);
-            xp.w = fmaf(-sg.lr, fmaf(sg.mu, mm.w, mh.w), xp.w);
-          } else {
-            xp.x = fmaf(-sg.lr, mm.x, xp.x);
-            xp.y = fmaf(-sg.lr, mm.y, xp.y);
-            xp.z = fmaf(-sg.lr, mm.z, xp.z);
-            xp.w = fmaf(-sg.lr, mm.w, xp.w);
-          }
-          stq<VEC4>(sg.m + d.off + (int64_t)rr * n, col, n, mm);
-          stq<VEC4>(sg.x + d.off + (int64_t)rr * n, col, n, xp);
-        }
-      }
-    }
-    cur = nxt;
-    j0 = jn;
   }
 }
 
@@ -693,13 +696,14 @@ __global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ 
                                                     int wg_base, int r, float* __restrict__ E,
                                                     const float* __restrict__ Q, const float* __restrict__ Ph,
                                                     float* __restrict__ Mhat, SgdArgs sg) {
+  __shared__ float tile[kRecRows * kRecLd];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
   if (d.vec == 4)
-    mfma_recon_body<RP, RESID, RESID, WRITE_MHAT, SGD, true>(d, wg, r, E, Q, Ph, Mhat, sg);
+    mfma_recon_body<RP, RESID, WRITE_MHAT, SGD, true>(d, wg, r, E, Q, Ph, Mhat, sg, tile);
   else
-    mfma_recon_body<RP, RESID, RESID, WRITE_MHAT, SGD, false>(d, wg, r, E, Q, Ph, Mhat, sg);
+    mfma_recon_body<RP, RESID, WRITE_MHAT, SGD, false>(d, wg, r, E, Q, Ph, Mhat, sg, tile);
 }
 
 // ---------------------------------------------------------------------------

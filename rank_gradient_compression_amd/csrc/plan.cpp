@@ -245,8 +245,10 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     d.s3_cols = (int32_t)align_up(std::min<int32_t>(d.n, kRecSplitCols), unit);
     d.s1 = (d.n + d.s1_cols - 1) / d.s1_cols;
     d.s3 = (d.n + d.s3_cols - 1) / d.s3_cols;
-    const int32_t row_tiles = (d.m + tile_rows - 1) / tile_rows;
-    const int32_t nrow_wg = row_tiles * d.s1, nrec_wg = row_tiles * d.s3;
+    // pass 1 tiles are kMfmaRows / kRowsPerWG rows; pass 3 tiles kRowsPerWG
+    // rows on both paths
+    const int32_t nrow_wg = ((d.m + tile_rows - 1) / tile_rows) * d.s1;
+    const int32_t nrec_wg = ((d.m + kRowsPerWG - 1) / kRowsPerWG) * d.s3;
     d.ppart_off = ppart;
     d.wg_pred0 = wg_pred;
     if (d.s1 > 1) {
