@@ -457,26 +457,32 @@ __global__ __launch_bounds__(kRedCols) void k_psum(const MatDesc* __restrict__ m
 
 // ---------------------------------------------------------------------------
 // Pass 2: Q = M^T P_hat over one row block (partials when the matrix has
-// several row blocks)
+// several row blocks).
 //
-// A workgroup owns 64 columns of one row block; its four wavefronts take
-// interleaved 64-row chunks of the block and are combined in LDS at the end
-// (in wavefront order).  The summation index of matrix-core step kk of a
-// chunk is bound, for lane (li, ls), to row
-//   rho(kk, ls) = ib + 16 (kk / 4) + 4 ls + kk % 4,
-// so that lane holds columns 4 li .. 4 li + 3 of those rows (one 16-byte load
-// per row; each load instruction covers four rows of 256 bytes) and its B
-// operands P_hat[rho][16 T + li] for kk = 4 qq .. 4 qq + 3 are four
-// consecutive rows of one P_hat column: one 16-byte load, and the four lanes
-// ls together read 64 contiguous bytes of that column.  No LDS staging and
-// no barrier inside the row loop.
+// A workgroup owns kMfmaCols columns of one row block and walks it in
+// kQtChunk-row chunks.  Each wavefront loads kQtChunk / 4 rows of a chunk
+// with row-contiguous accesses (64 lanes x 16 bytes, one 1 KB row segment
+// per instruction) into an LDS tile, and the chunk's P_hat rows go to LDS
+// once for the workgroup; each wavefront then accumulates its 64 columns
+// (four 16-column tiles, every rank tile) on the matrix core from LDS.  The
+// next chunk's loads are issued before the current chunk's matrix products.
+// The summation index of matrix-core step v of a 16-row block is bound, for
+// lane (li, ls), to row 4 ls + v, so that lane's B operands P_hat[4 ls ..
+// 4 ls + 3][rank] are one 16-byte LDS read.  Each wavefront owns its columns:
+// nothing is summed across wavefronts.
 // ---------------------------------------------------------------------------
+
+constexpr int kQtChunk = 32;              // rows per LDS chunk
+constexpr int kQtLd = kMfmaCols + 4;      // LDS row stride of the M chunk (floats)
+constexpr int kQtPld = kQtChunk + 4;      // LDS stride of one rank's P_hat rows (floats)
+static_assert(kMfmaCols == 256, "a wavefront row load covers the workgroup's columns");
 
 template <int RP, bool VEC4>
 __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, const float* __restrict__ M,
                                              const float* __restrict__ Ph, int64_t ph_fixed, float* __restrict__ Q,
-                                             float* __restrict__ part, float* red) {
-  constexpr int RS = 65;  // LDS row stride of the [rank][64 columns] reduction tile
+                                             float* __restrict__ part, float* Ms, float* Ps) {
+  constexpr int RPW = kQtChunk / 4;                        // rows a wavefront loads per chunk
+  constexpr int PPT = (RP * kQtChunk + 255) / 256;         // P_hat values a thread loads per chunk
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_mtp0;
   const int rb = local / d.ncb, cb = local - rb * d.ncb;
@@ -484,79 +490,83 @@ __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, co
   const int i1 = min(m, i0 + d.rb_rows);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
-  const int cbase = cb * 64;
-  const int col = cbase + 4 * li;
-  const bool col_ok = col < n;
+  const int cbase = cb * kMfmaCols;
+  const int scol = cbase + 4 * lane;  // the lane's four columns in the row loads
+  const bool scol_ok = scol < n;
   const float* ph = Ph + (ph_fixed >= 0 ? ph_fixed : d.p_off);
-  const bool ph4 = (m & 3) == 0;  // P_hat columns start 16-byte aligned
 
   v4f acc[4][RP / 16];
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int T = 0; T < RP / 16; ++T) acc[v][T] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int T = 0; T < RP / 16; ++T) acc[ct][T] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int ib = i0 + 64 * wave; ib < i1; ib += 256) {
-    float4 x[16];
+  float4 xn[RPW];
+  float pn[PPT];
+  auto load_chunk = [&](int ib) {
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const int rr = ib + 16 * (kk >> 2) + 4 * ls + (kk & 3);
-      const bool ok = rr < i1 && col_ok;
-      x[kk] = ldq<VEC4>(M + d.off + (int64_t)(rr < i1 ? rr : i0) * n, col, ok, 0, n);
+    for (int u = 0; u < RPW; ++u) {
+      const int row = ib + RPW * wave + u;
+      xn[u] = row < i1 ? ldq<VEC4>(M + d.off + (int64_t)row * n, scol, scol_ok, cbase, n)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float4 pb[RP / 16][4];
 #pragma unroll
-    for (int T = 0; T < RP / 16; ++T)
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int t = 16 * T + li, r0 = ib + 16 * qq + 4 * ls;
-        const float* pp = ph + (int64_t)(t < r ? t : 0) * m + r0;
-        if (t < r && ph4 && r0 + 3 < i1) {
-          pb[T][qq] = *reinterpret_cast<const float4*>(pp);
-        } else {
-          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (t < r) {
-            if (r0 < i1) v.x = pp[0];
-            if (r0 + 1 < i1) v.y = pp[1];
-            if (r0 + 2 < i1) v.z = pp[2];
-            if (r0 + 3 < i1) v.w = pp[3];
-          }
-          pb[T][qq] = v;
-        }
-      }
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float xv[4] = {x[kk].x, x[kk].y, x[kk].z, x[kk].w};
-#pragma unroll
-      for (int T = 0; T < RP / 16; ++T) {
-        const float4 pq = pb[T][kk >> 2];
-        const float b = (kk & 3) == 0 ? pq.x : (kk & 3) == 1 ? pq.y : (kk & 3) == 2 ? pq.z : pq.w;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v][T] = mfma16x16x4(xv[v], b, acc[v][T]);
-      }
+    for (int u = 0; u < PPT; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      const int t = e / kQtChunk, rr = e % kQtChunk;
+      pn[u] = (e < RP * kQtChunk && t < r && ib + rr < i1) ? ph[(int64_t)t * m + ib + rr] : 0.f;
     }
-  }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) *reinterpret_cast<float4*>(&Ms[(RPW * wave + u) * kQtLd + 4 * lane]) = xn[u];
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      if (e < RP * kQtChunk) Ps[(e / kQtChunk) * kQtPld + e % kQtChunk] = pn[u];
+    }
+  };
 
-  // Wavefront partials summed in LDS in wavefront order.  acc[v][T][e] of
-  // lane (li, ls) is Q[cbase + 4 (4 ls + e) + v][16 T + li].
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+  if (i0 < i1) load_chunk(i0);
+  for (int ib = i0; ib < i1; ib += kQtChunk) {
+    store_chunk();
+    __syncthreads();
+    if (ib + kQtChunk < i1) load_chunk(ib + kQtChunk);
+#pragma unroll
+    for (int kb = 0; kb < kQtChunk / 16; ++kb) {
+      float4 pb[RP / 16];
 #pragma unroll
       for (int T = 0; T < RP / 16; ++T)
+        pb[T] = *reinterpret_cast<const float4*>(&Ps[(16 * T + li) * kQtPld + 16 * kb + 4 * ls]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < 4; ++v) {
+        const float* mrow = &Ms[(16 * kb + 4 * ls + v) * kQtLd + 64 * wave + li];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float* slot = &red[(16 * T + li) * RS + 4 * (4 * ls + e) + v];
-            *slot = w == 0 ? acc[v][T][e] : *slot + acc[v][T][e];
+        for (int ct = 0; ct < 4; ++ct) {
+          const float a = mrow[16 * ct];
+#pragma unroll
+          for (int T = 0; T < RP / 16; ++T) {
+            const float b = v == 0 ? pb[T].x : v == 1 ? pb[T].y : v == 2 ? pb[T].z : pb[T].w;
+            acc[ct][T] = mfma16x16x4(a, b, acc[ct][T]);
           }
+        }
+      }
     }
     __syncthreads();
   }
+
+  // acc[ct][T][e] of lane (li, ls) is Q[cbase + 64 wave + 16 ct + 4 ls + e][16 T + li].
   float* out = d.nrb > 1 ? part + d.part_off + (int64_t)rb * r * n : Q + d.q_off;
-  for (int idx = threadIdx.x; idx < RP * 64; idx += 256) {
-    const int t = idx >> 6, c = idx & 63;
-    if (t < r && cbase + c < n) out[(int64_t)t * n + cbase + c] = red[t * RS + c];
+  const bool out4 = (n & 3) == 0;
+#pragma unroll
+  for (int T = 0; T < RP / 16; ++T) {
+    const int t = 16 * T + li;
+    if (t < r) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        st4(out + (int64_t)t * n, cbase + 64 * wave + 16 * ct + 4 * ls, n, out4,
+            make_float4(acc[ct][T][0], acc[ct][T][1], acc[ct][T][2], acc[ct][T][3]));
+    }
   }
 }
 
@@ -565,14 +575,15 @@ __global__ __launch_bounds__(256) void k_mfma_qt(const MatDesc* __restrict__ mat
                                                  int wg_base, int r, const float* __restrict__ M,
                                                  const float* __restrict__ Ph, int64_t ph_fixed,
                                                  float* __restrict__ Q, float* __restrict__ part) {
-  __shared__ float red[RP * 65];
+  __shared__ float Ms[kQtChunk * kQtLd];
+  __shared__ float Ps[RP * kQtPld];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
   if (d.vec == 4)
-    mfma_qt_body<RP, true>(d, wg, r, M, Ph, ph_fixed, Q, part, red);
+    mfma_qt_body<RP, true>(d, wg, r, M, Ph, ph_fixed, Q, part, Ms, Ps);
   else
-    mfma_qt_body<RP, false>(d, wg, r, M, Ph, ph_fixed, Q, part, red);
+    mfma_qt_body<RP, false>(d, wg, r, M, Ph, ph_fixed, Q, part, Ms, Ps);
 }
 
 // ---------------------------------------------------------------------------

@@ -36,12 +36,16 @@ static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // Rows per row block of the M^T P_hat pass.  The row-block partial sums cost
 // 2*rank/rb_rows of that pass's matrix traffic, so a block has at least
-// 8*rank rows (at most 1/4 extra on the pass); above that, blocks are as long
-// as possible while the grid still has enough workgroups to cover the chip.
+// 8*rank rows (at most 1/4 extra on the pass; 16*rank up to 512 rows on the
+// matrix cores); above that, blocks are as long as possible while the grid
+// still has enough workgroups to cover the chip.
 static int32_t choose_rb_rows(const std::vector<MatDesc>& mats, int64_t rank, bool mfma) {
   const int64_t target_wgs = 2048;
   int32_t rb_min = 64;
-  while (rb_min < 8 * rank) rb_min *= 2;
+  // matrix cores: a workgroup is 256 columns wide, so a block needs more rows
+  // to keep the partials small (at most 1/8 of the pass from rank 16 on)
+  const int64_t want = mfma ? std::min<int64_t>(16 * rank, 512) : 8 * rank;
+  while (rb_min < want) rb_min *= 2;
   int32_t rb = 2048;
   for (; rb > rb_min; rb /= 2) {
     int64_t wgs = 0;
