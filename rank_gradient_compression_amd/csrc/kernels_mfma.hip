@@ -311,23 +311,27 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
   }
 }
 
-// Plain M Q (read only: the subspace refresh and the extra power
-// iterations).  A workgroup owns a 64-row tile and one column split; each
-// wavefront takes two 16-row MFMA tiles (a row half) and every second
-// 64-column chunk of the split, and the two wavefronts of a row half are
-// summed in LDS at the end in fixed order.  In a chunk, lane (li, ls) loads
-// 16 bytes -- columns c0 + 16 qq + 4 ls .. + 3 -- of its row in each tile
-// (the A operands of four k-steps), and the matching B operands
-// Q[c0 + 16 qq + 4 ls + v][16 T + li], v = 0..3, are one 16-byte load from
-// the column-major Q, shared by both tiles.  No LDS staging and no barrier in
-// the column loop (measured 19% faster than the staged form for this
-// read-only pass; slower for the EF-add modes, which keep the staged form).
+// Plain P = M Q (MODE 0, the refresh): a workgroup owns the 64-row tile of
+// its column split and walks the split in kMqChunk-column chunks.  Each
+// wavefront loads 16 rows of a chunk with row-contiguous accesses (32 lanes x
+// 16 bytes per row, two rows per instruction) into an LDS tile, the chunk's
+// Q columns go to LDS once for the workgroup, and each wavefront accumulates
+// its own 16 rows (every rank tile) on the matrix core from LDS.  The next
+// chunk's loads are issued before the current chunk's matrix products.  The
+// summation index of matrix-core step v of a 16-column block is bound, for
+// lane (li, ls), to column 4 ls + v, so that the lane's A and B operands are
+// one 16-byte LDS read each per block.
+constexpr int kMqChunk = 128;            // columns per LDS chunk
+constexpr int kMqLd = kMqChunk + 4;      // LDS row stride of the M chunk (floats)
+
 template <int RP, bool VEC4>
 __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, const float* __restrict__ M,
                                              const float* __restrict__ Q, float* P, int64_t p_fixed,
-                                             float* __restrict__ ppart, float* red) {
-  constexpr int RS = kMfmaRows + 1;  // LDS row stride of the [rank][64 rows] reduction tile
-  constexpr int NT = 2;              // 16-row tiles per wavefront
+                                             float* __restrict__ ppart, float* smem) {
+  constexpr int QLD = kMqChunk + 4;                         // LDS stride of one rank's Q chunk
+  constexpr int QPT = (RP * kMqChunk / 4 + 255) / 256;      // Q float4s a thread loads per chunk
+  float* Ms = smem;                                         // [64 rows][kMqLd]
+  float* Qs = smem + kMfmaRows * kMqLd;                     // [RP ranks][QLD]
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_rows0;
   const int rb = local / d.s1, split = local - rb * d.s1;
@@ -335,76 +339,78 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   const int c_end = min(n, c_begin + d.s1_cols);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
-  const int half = wave & 1, phase = wave >> 1;
-  const int tbase = rb * kMfmaRows + 32 * half;
-  bool row_ok[NT];
-  int64_t roff[NT];
-#pragma unroll
-  for (int tl = 0; tl < NT; ++tl) {
-    const int row = tbase + 16 * tl + li;
-    row_ok[tl] = row < m;
-    roff[tl] = d.off + (int64_t)min(row, m - 1) * n;
-  }
+  const int i0 = rb * kMfmaRows;
   const float* q = Q + d.q_off;
+  // row loads: lane (hr = lane / 32, cl = lane % 32) covers columns 4 cl .. 4 cl + 3 of rows 2 u + hr
+  const int hr = lane >> 5, cl4 = 4 * (lane & 31);
 
-  v4f acc[NT][RP / 16];
+  v4f acc[RP / 16];
 #pragma unroll
-  for (int tl = 0; tl < NT; ++tl)
-#pragma unroll
-    for (int T = 0; T < RP / 16; ++T) acc[tl][T] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int T = 0; T < RP / 16; ++T) acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = c_begin + 64 * phase; c0 < c_end; c0 += 128) {
-    float4 x[NT][4], qb[4][RP / 16];
+  float4 xn[8], qn[QPT];
+  auto load_chunk = [&](int c0) {
+    const int col = c0 + cl4;
+    const bool col_ok = col < c_end;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int col = c0 + 16 * qq + 4 * ls;
-      const bool col_ok = col < c_end;
-#pragma unroll
-      for (int tl = 0; tl < NT; ++tl) x[tl][qq] = ldq<VEC4>(M + roff[tl], col, col_ok, c_begin, n);
-#pragma unroll
-      for (int T = 0; T < RP / 16; ++T) {
-        const int t = 16 * T + li;
-        qb[qq][T] = ldq<VEC4>(q + (int64_t)(t < r ? t : 0) * n, col, col_ok && t < r, c_begin, n);
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int row = i0 + 16 * wave + 2 * u + hr;
+      xn[u] = row < m ? ldq<VEC4>(M + d.off + (int64_t)row * n, col, col_ok, c_begin, n)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
+    for (int u = 0; u < QPT; ++u) {
+      const int e = threadIdx.x + 256 * u;  // float4 index within [RP][kMqChunk / 4]
+      const int t = e / (kMqChunk / 4), c = c0 + 4 * (e % (kMqChunk / 4));
+      qn[u] = (e < RP * kMqChunk / 4 && t < r) ? ldq<VEC4>(q + (int64_t)t * n, c, c < c_end, c_begin, n)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_chunk = [&]() {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+    for (int u = 0; u < 8; ++u)
+      *reinterpret_cast<float4*>(&Ms[(16 * wave + 2 * u + hr) * kMqLd + cl4]) = xn[u];
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      if (e < RP * kMqChunk / 4)
+        *reinterpret_cast<float4*>(&Qs[(e / (kMqChunk / 4)) * QLD + 4 * (e % (kMqChunk / 4))]) = qn[u];
+    }
+  };
+
+  load_chunk(c_begin);
+  for (int c0 = c_begin; c0 < c_end; c0 += kMqChunk) {
+    store_chunk();
+    __syncthreads();
+    if (c0 + kMqChunk < c_end) load_chunk(c0 + kMqChunk);
+#pragma unroll
+    for (int kb = 0; kb < kMqChunk / 16; ++kb) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&Ms[(16 * wave + li) * kMqLd + 16 * kb + 4 * ls]);
+      float4 b4[RP / 16];
+#pragma unroll
+      for (int T = 0; T < RP / 16; ++T)
+        b4[T] = *reinterpret_cast<const float4*>(&Qs[(16 * T + li) * QLD + 16 * kb + 4 * ls]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float a = v == 0 ? a4.x : v == 1 ? a4.y : v == 2 ? a4.z : a4.w;
 #pragma unroll
         for (int T = 0; T < RP / 16; ++T) {
-          const float4 bq = qb[qq][T];
-          const float b = v == 0 ? bq.x : v == 1 ? bq.y : v == 2 ? bq.z : bq.w;
-#pragma unroll
-          for (int tl = 0; tl < NT; ++tl) {
-            const float4 xq = x[tl][qq];
-            const float a = row_ok[tl] ? (v == 0 ? xq.x : v == 1 ? xq.y : v == 2 ? xq.z : xq.w) : 0.f;
-            acc[tl][T] = mfma16x16x4(a, b, acc[tl][T]);
-          }
+          const float b = v == 0 ? b4[T].x : v == 1 ? b4[T].y : v == 2 ? b4[T].z : b4[T].w;
+          acc[T] = mfma16x16x4(a, b, acc[T]);
         }
-  }
-
-  // The two column phases of each row half summed in LDS in phase order;
-  // acc[tl][T][e] of lane (li, ls) is P[tbase + 16 tl + 4 ls + e][16 T + li].
-  for (int ph = 0; ph < 2; ++ph) {
-    if (phase == ph) {
-#pragma unroll
-      for (int tl = 0; tl < NT; ++tl)
-#pragma unroll
-        for (int T = 0; T < RP / 16; ++T)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float* slot = &red[(16 * T + li) * RS + 32 * half + 16 * tl + 4 * ls + e];
-            *slot = ph == 0 ? acc[tl][T][e] : *slot + acc[tl][T][e];
-          }
+      }
     }
     __syncthreads();
   }
+
+  // acc[T][e] of lane (li, ls) is P[i0 + 16 wave + 4 ls + e][16 T + li].
   float* dst = d.s1 > 1 ? ppart + d.ppart_off + (int64_t)split * r * m : P + (p_fixed >= 0 ? p_fixed : d.p_off);
-  const int rbase = rb * kMfmaRows;
-  for (int idx = threadIdx.x; idx < RP * kMfmaRows; idx += 256) {
-    const int t = idx / kMfmaRows, rl = idx % kMfmaRows;
-    if (t < r && rbase + rl < m) dst[(int64_t)t * m + rbase + rl] = red[t * RS + rl];
+  const bool out4 = (m & 3) == 0;
+#pragma unroll
+  for (int T = 0; T < RP / 16; ++T) {
+    const int t = 16 * T + li;
+    if (t < r) st4(dst + (int64_t)t * m, i0 + 16 * wave + 4 * ls, m, out4,
+                   make_float4(acc[T][0], acc[T][1], acc[T][2], acc[T][3]));
   }
 }
 
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
                                                 float* __restrict__ ppart, const float* Pold) {
   constexpr int QS = RP + 4;
   static_assert(16 * (kMfmaRows + 1) <= 64 * QS, "output staging does not fit");
-  constexpr int SMEM = MODE == 0 ? RP * (kMfmaRows + 1) : 64 * QS;
+  constexpr int SMEM = MODE == 0 ? kMfmaRows * kMqLd + RP * (kMqChunk + 4) : 64 * QS;
   __shared__ float smem[SMEM];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
