@@ -147,10 +147,11 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 // in, so E is formed bit for bit as the residual pass would have stored it.
 // ---------------------------------------------------------------------------
 
-// EF-add modes: the workgroup's four wavefronts take 16 rows each of the
-// 64-row tile and walk the column split in 64-column steps; each Q chunk is
-// staged once in LDS and shared by the four wavefronts (the EF-add modes run
-// best this way: the Q chunk is read from L2 once per 64 rows).
+// Register form (the deferred-residual modes 5 and 6; modes 0..4 take the
+// staged form further down): the workgroup's four wavefronts take 16 rows
+// each of the 64-row tile and walk the column split in 64-column steps; each
+// Q chunk is staged once in LDS and shared by the four wavefronts, and each
+// lane's 16-byte loads of G and E feed the matrix core directly.
 
 template <int RP, int MODE, bool VEC4, bool GBF16>
 __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
@@ -311,23 +312,32 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
   }
 }
 
-// Plain P = M Q (MODE 0, the refresh): a workgroup owns the 64-row tile of
-// its column split and walks the split in kMqChunk-column chunks.  Each
-// wavefront loads 16 rows of a chunk with row-contiguous accesses (32 lanes x
-// 16 bytes per row, two rows per instruction) into an LDS tile, the chunk's
-// Q columns go to LDS once for the workgroup, and each wavefront accumulates
+// P = M Q with the EF-add of MODE 1..4 (or M as is, MODE 0: the refresh),
+// staged: a workgroup owns the 64-row tile of its column split and walks the
+// split in kMqChunk-column chunks.  Each wavefront loads 16 rows of a chunk
+// with row-contiguous accesses (32 lanes x 16 bytes per row, two rows per
+// instruction) -- G, E and u as the mode needs --, forms M (and u) and stores
+// it back over E the same way, and writes M into an LDS tile; the chunk's Q
+// columns go to LDS once for the workgroup.  Each wavefront then accumulates
 // its own 16 rows (every rank tile) on the matrix core from LDS.  The next
 // chunk's loads are issued before the current chunk's matrix products.  The
 // summation index of matrix-core step v of a 16-column block is bound, for
 // lane (li, ls), to column 4 ls + v, so that the lane's A and B operands are
-// one 16-byte LDS read each per block.
+// one 16-byte LDS read each per block; the blocks are taken in ascending
+// column order, the same sequence of matrix-core steps as the deferred-
+// residual form below, so P is the same bit for bit.
 constexpr int kMqChunk = 128;            // columns per LDS chunk
 constexpr int kMqLd = kMqChunk + 4;      // LDS row stride of the M chunk (floats)
 
-template <int RP, bool VEC4>
-__device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, const float* __restrict__ M,
+template <int RP, int MODE, bool VEC4, bool GBF16>
+__device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
+                                             float* __restrict__ E, float* __restrict__ U, float beta,
                                              const float* __restrict__ Q, float* P, int64_t p_fixed,
                                              float* __restrict__ ppart, float* smem) {
+  static_assert(MODE >= 0 && MODE <= 4, "staged pass 1 modes");
+  constexpr bool LOAD_G = MODE != 0;
+  constexpr bool LOAD_E = MODE <= 2;
+  constexpr bool MOM = MODE == 2 || MODE == 4;
   constexpr int QLD = kMqChunk + 4;                         // LDS stride of one rank's Q chunk
   constexpr int QPT = (RP * kMqChunk / 4 + 255) / 256;      // Q float4s a thread loads per chunk
   float* Ms = smem;                                         // [64 rows][kMqLd]
@@ -341,22 +351,32 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   const int li = lane & 15, ls = lane >> 4;
   const int i0 = rb * kMfmaRows;
   const float* q = Q + d.q_off;
-  // row loads: lane (hr = lane / 32, cl = lane % 32) covers columns 4 cl .. 4 cl + 3 of rows 2 u + hr
+  // row accesses: lane (hr = lane / 32, lane % 32) covers columns 4 (lane % 32) .. + 3 of rows 2 u + hr
   const int hr = lane >> 5, cl4 = 4 * (lane & 31);
 
   v4f acc[RP / 16];
 #pragma unroll
   for (int T = 0; T < RP / 16; ++T) acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  float4 xn[8], qn[QPT];
+  float4 xg[8], xe[LOAD_E ? 8 : 1], xu[MOM ? 8 : 1], qn[QPT];
+  auto row_of = [&](int u) { return i0 + 16 * wave + 2 * u + hr; };
   auto load_chunk = [&](int c0) {
     const int col = c0 + cl4;
     const bool col_ok = col < c_end;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int row = i0 + 16 * wave + 2 * u + hr;
-      xn[u] = row < m ? ldq<VEC4>(M + d.off + (int64_t)row * n, col, col_ok, c_begin, n)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int row = row_of(u);
+      const bool ok = row < m && col_ok;
+      const int64_t ro = d.off + (int64_t)min(row, m - 1) * n;
+      if constexpr (!LOAD_G) {
+        xg[u] = ldq<VEC4>(E + ro, col, ok, c_begin, n);
+      } else if constexpr (GBF16) {
+        xg[u] = ldq_bf16<VEC4>(static_cast<const uint16_t*>(G) + ro, col, ok, c_begin, n);
+      } else {
+        xg[u] = ldq<VEC4>(static_cast<const float*>(G) + ro, col, ok, c_begin, n);
+      }
+      if constexpr (LOAD_E) xe[u] = ldq<VEC4>(E + ro, col, ok, c_begin, n);
+      if constexpr (MOM) xu[u] = ldq<VEC4>(U + ro, col, ok, c_begin, n);
     }
 #pragma unroll
     for (int u = 0; u < QPT; ++u) {
@@ -366,10 +386,34 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
                                                : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  auto store_chunk = [&]() {
+  // EF-add of the loaded chunk, M (and u) stored back, M into the LDS tile.
+  auto store_chunk = [&](int c0) {
+    const int col = c0 + cl4;
+    const bool col_ok = col < c_end;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      *reinterpret_cast<float4*>(&Ms[(16 * wave + 2 * u + hr) * kMqLd + cl4]) = xn[u];
+    for (int u = 0; u < 8; ++u) {
+      const int row = row_of(u);
+      float4 s;
+      if constexpr (MODE == 0) {
+        s = xg[u];
+      } else {
+        const float4 g = xg[u];
+        const float4 e = LOAD_E ? xe[LOAD_E ? u : 0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (MOM) {
+          float4 uu = xu[MOM ? u : 0];
+          uu.x = fmaf(beta, uu.x, g.x);
+          uu.y = fmaf(beta, uu.y, g.y);
+          uu.z = fmaf(beta, uu.z, g.z);
+          uu.w = fmaf(beta, uu.w, g.w);
+          if (row < m && col_ok) stq<VEC4>(U + d.off + (int64_t)row * n, col, n, uu);
+          s = make_float4(uu.x + e.x, uu.y + e.y, uu.z + e.z, uu.w + e.w);
+        } else {
+          s = make_float4(g.x + e.x, g.y + e.y, g.z + e.z, g.w + e.w);
+        }
+        if (row < m && col_ok) stq<VEC4>(E + d.off + (int64_t)row * n, col, n, s);
+      }
+      *reinterpret_cast<float4*>(&Ms[(16 * wave + 2 * u + hr) * kMqLd + cl4]) = s;
+    }
 #pragma unroll
     for (int u = 0; u < QPT; ++u) {
       const int e = threadIdx.x + 256 * u;
@@ -380,7 +424,7 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
 
   load_chunk(c_begin);
   for (int c0 = c_begin; c0 < c_end; c0 += kMqChunk) {
-    store_chunk();
+    store_chunk(c0);
     __syncthreads();
     if (c0 + kMqChunk < c_end) load_chunk(c0 + kMqChunk);
 #pragma unroll
@@ -420,18 +464,19 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
                                                 float* __restrict__ E, float* __restrict__ U, float beta,
                                                 const float* __restrict__ Q, float* P, int64_t p_fixed,
                                                 float* __restrict__ ppart, const float* Pold) {
+  constexpr bool STAGED = MODE <= 4;  // the deferred-residual modes keep the register form
   constexpr int QS = RP + 4;
   static_assert(16 * (kMfmaRows + 1) <= 64 * QS, "output staging does not fit");
-  constexpr int SMEM = MODE == 0 ? kMfmaRows * kMqLd + RP * (kMqChunk + 4) : 64 * QS;
+  constexpr int SMEM = STAGED ? kMfmaRows * kMqLd + RP * (kMqChunk + 4) : 64 * QS;
   __shared__ float smem[SMEM];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
-  if constexpr (MODE == 0) {
+  if constexpr (STAGED) {
     if (d.vec == 4)
-      mfma_mq_body<RP, true>(d, wg, r, E, Q, P, p_fixed, ppart, smem);
+      mfma_mq_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem);
     else
-      mfma_mq_body<RP, false>(d, wg, r, E, Q, P, p_fixed, ppart, smem);
+      mfma_mq_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem);
   } else {
     if (d.vec == 4)
       mfma_p_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
