@@ -803,47 +803,46 @@ __device__ __forceinline__ int orth_idx(const OrthDesc* descs, const int32_t* ma
 
 constexpr int kGramChunk = kGramRows;  // rows staged in LDS at a time
 
+// A_b = P_b^T P_b for one block of kGramRows rows on the fp64 matrix core
+// (v_mfma_f64_16x16x4f64; each fp32 product is exact in fp64).  The block is
+// staged in LDS; the (RP/16)^2 16 x 16 tiles of A_b are dealt round-robin to
+// the four wavefronts, each summing its tiles over the block's rows in
+// order, four rows per matrix-core step.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
 template <int RP>
 __global__ __launch_bounds__(256) void k_gram_partial(const OrthDesc* __restrict__ descs, const int32_t* __restrict__ map,
                                                       int first, int r, const float* __restrict__ base,
                                                       double* __restrict__ gram) {
   constexpr int LS = RP + 1;
-  constexpr int BF = RP / 16;  // each of the 16 x 16 threads owns a BF x BF block of A
+  constexpr int NT = RP / 16;
   __shared__ float Pl[kGramChunk * LS];
   int local;
   const OrthDesc o = descs[orth_idx(descs, map, first, local)];
   const float* p = base + o.off;
-  const int ta = threadIdx.x >> 4, tb = threadIdx.x & 15;
-  double acc[BF][BF];
-#pragma unroll
-  for (int a = 0; a < BF; ++a)
-#pragma unroll
-    for (int b = 0; b < BF; ++b) acc[a][b] = 0.0;
-  for (int r0 = local * kGramRows; r0 < min(o.rows, (local + 1) * kGramRows); r0 += kGramChunk) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < kGramChunk * RP; e += 256) {
-      const int i = e % kGramChunk, t = e / kGramChunk;
-      Pl[i * LS + t] = (t < r && r0 + i < o.rows) ? p[(int64_t)t * o.rows + r0 + i] : 0.f;
-    }
-    __syncthreads();
-    for (int i = 0; i < kGramChunk; ++i) {
-      double xa[BF], xb[BF];
-#pragma unroll
-      for (int a = 0; a < BF; ++a) {
-        xa[a] = (double)Pl[i * LS + ta * BF + a];
-        xb[a] = (double)Pl[i * LS + tb * BF + a];
-      }
-#pragma unroll
-      for (int a = 0; a < BF; ++a)
-#pragma unroll
-        for (int b = 0; b < BF; ++b) acc[a][b] = fma(xa[a], xb[b], acc[a][b]);
-    }
+  const int r0 = local * kGramRows;
+  for (int e = threadIdx.x; e < kGramChunk * RP; e += 256) {
+    const int i = e % kGramChunk, t = e / kGramChunk;
+    Pl[i * LS + t] = (t < r && r0 + i < o.rows) ? p[(int64_t)t * o.rows + r0 + i] : 0.f;
   }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, ls = lane >> 4;
   double* g = gram + o.gram_off + (int64_t)local * RP * RP;
+  for (int u = wave; u < NT * NT; u += 4) {
+    const int ta = u / NT, tb = u % NT;
+    v4d acc = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+    for (int kk = 0; kk < kGramChunk / 4; ++kk) {
+      const int i = 4 * kk + ls;
+      const double a = (double)Pl[i * LS + 16 * ta + li];
+      const double b = (double)Pl[i * LS + 16 * tb + li];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+    }
+    // fp64 result layout: acc[e] of lane (li, ls) is A_b[16 ta + 4 e + ls][16 tb + li]
 #pragma unroll
-  for (int a = 0; a < BF; ++a)
-#pragma unroll
-    for (int b = 0; b < BF; ++b) g[(ta * BF + a) * RP + tb * BF + b] = acc[a][b];
+    for (int e = 0; e < 4; ++e) g[(16 * ta + 4 * e + ls) * RP + 16 * tb + li] = acc[e];
+  }
 }
 
 // Fixed-order block sum: A (at t_off) = sum_b A_b.  A workgroup covers 256
