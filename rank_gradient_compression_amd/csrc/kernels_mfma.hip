@@ -1,4 +1,5 @@
-// Matrix-core kernels of the PowerSGD step for ranks 9..64 (gfx950, wave64).
+// Matrix-core kernels of the PowerSGD step for ranks 9..64 and the
+// orthonormalisation for every rank (gfx950, wave64).
 //
 // The anthology note on PowerSGD (note 152, "Limitations") points out that
 // transformer language models may need ranks of 32 and more.  At such ranks
@@ -11,19 +12,28 @@
 //   A[i][k] is supplied by lane i + 16k, B[k][j] by lane j + 16k,
 //   D[i][j] is returned in lane j + 16*(i/4), element i%4.
 // The summation index k can be bound to any four columns (or rows) of M as
-// long as A and B agree, which lets each lane feed the matrix core straight
-// from its own 16-byte load of a row of M.
+// long as A and B agree, so that a lane's operands for four steps are one
+// 16-byte read.
 //
-//   pass 1  P = M Q (with the EF-add and optional momentum), per 64-row tile
-//           and column split; Q chunks are staged in LDS and shared by the
-//           four wavefronts; split partials are summed in fixed order.
-//   pass 2  Q = M^T P_hat per row block; P_hat rows staged in LDS.
-//   pass 3  M_hat = P_hat Q^T computed transposed (M_hat^T = Q P_hat^T), so
-//           that each lane holds four consecutive columns of one row and
-//           the residual E = M - M_hat streams with 16-byte accesses.
-// The orthonormalisation of P for these ranks is Gram-Schmidt carried out on
-// the fp64 Gram matrix of P, spread over many workgroups (partial Gram
-// blocks, a one-wavefront triangular solve per matrix, and P_hat = P T).
+// Global memory is read and written row-contiguously (a wavefront moves 512
+// bytes to 1 KB of one or two rows per instruction) and the tiles reach the
+// matrix core through LDS; reading the operands from global memory in the
+// matrix core's own layout (16 rows x 64 bytes per instruction) streamed
+// markedly slower.
+//
+//   pass 1  P = M Q (with the EF-add and optional momentum): a workgroup
+//           walks its 64-row tile of one column split in 128-column chunks
+//           (M formed, stored back and staged in LDS with the chunk of Q);
+//           split partials are summed in fixed order.  The deferred-residual
+//           modes keep a register form.
+//   pass 2  Q = M^T P_hat: a workgroup walks 256 columns of a row block in
+//           32-row chunks staged in LDS with the chunk's P_hat rows.
+//   pass 3  M_hat = P_hat Q^T computed transposed (M_hat^T = Q P_hat^T) into
+//           an LDS tile of 32 rows x 256 columns, then streamed out with E.
+// The orthonormalisation (every rank) is Gram-Schmidt carried out on the
+// fp64 Gram matrix of P: Gram blocks on the fp64 matrix core, a fixed-order
+// reduction, a one-wavefront Cholesky per matrix, and P_hat = P R^-1 by
+// substitution.
 
 #include <hip/hip_runtime.h>
 
