@@ -394,7 +394,7 @@ def run_refresh(args, torch, B, W, PowerSGD, R):
     ps = PowerSGD([(m, n)], r, device="cuda")
     mbuf = torch.zeros_like(ps.grads)
     ps.view(mbuf, 0).copy_(A)
-    q0 = torch.from_numpy(W.gaussian_q0(n, r, 5)).cuda()
+    q0 = torch.from_numpy(W.gaussian_q0(n, r, 5)).float().cuda()
 
     def call():
         ps.set_q(0, q0)
@@ -414,6 +414,15 @@ def run_refresh(args, torch, B, W, PowerSGD, R):
         st = stage_table(B, ps.plan, {"ef_p": 4.0, "mtp": 4.0}, {"ef_p": 2.0 * r, "mtp": 2.0 * r}, m * n)
         res["roofline"] = roofline_of(st, r > 8, f"hbm_bytes_refresh_8192x8192_r{r}.md")
         res["stages"] = round_stages(st)
+    # The same call captured once in a HIP graph and replayed (its 96
+    # launches issued together).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    ms_g, _ = R.time(f"refresh 8192^2 r={r} x{iters}, graph replay", graph.replay, args.steps, args.warmup,
+                     per_step=False)
+    res["config"]["graph_replay"] = {"ms_per_step": round(ms_g, 4),
+                                     "tflops": round(flops / (ms_g * 1e-3) / 1e12, 2)}
     print(json.dumps(res), flush=True)
 
 

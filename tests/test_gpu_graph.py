@@ -1,5 +1,5 @@
-"""psgd_compress captured in a HIP graph (no hook, timing off: the call then
-only enqueues kernels) and replayed: every replay, with eager work and
+"""psgd_compress and psgd_refresh captured in a HIP graph (no hook, timing
+off: the calls then only enqueue kernels) and replayed: every replay, with eager work and
 synchronisations in between, must give bit for bit what the same sequence of
 eager calls gives on an identical twin (the kernels are deterministic)."""
 import numpy as np
@@ -45,3 +45,35 @@ def test_graph_replays_match_eager_calls(rank, beta):
         del junk
         for name in ("p", "q", "err", "mhat") + (("mom",) if beta is not None else ()):
             assert torch.equal(getattr(a, name), getattr(b, name)), f"replay {t}: {name} differs"
+
+
+@pytest.mark.parametrize("rank", [4, 32])
+def test_refresh_graph_replays_match_eager_calls(rank):
+    """psgd_refresh (setting the start Q, then the rounds) captured once and
+    replayed on changing matrices: bit for bit the eager calls' Q."""
+    m, n = 700, 520
+    a = PowerSGD([(m, n)], rank, device=DEV)
+    b = PowerSGD([(m, n)], rank, device=DEV)
+    q0 = torch.from_numpy(W.gaussian_q0(n, rank, 77)).float().to(DEV)
+    ma = torch.zeros(a.grads.numel(), device=DEV)
+    mb = torch.zeros_like(ma)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        a.set_q(0, q0)
+        a.refresh(0, ma, 3)
+    g = torch.Generator(device=DEV).manual_seed(rank)
+    for t in range(1, 4):
+        x = torch.randn(m, n, device=DEV, generator=g)
+        a.view(ma, 0).copy_(x)
+        b.view(mb, 0).copy_(x)
+        torch.cuda.synchronize()
+        say(f"[graph refresh r={rank}] replay {t}")
+        graph.replay()
+        b.set_q(0, q0)
+        b.refresh(0, mb, 3)
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        del junk
+        assert torch.equal(a.q_of(0), b.q_of(0)), f"replay {t}: Q differs"
