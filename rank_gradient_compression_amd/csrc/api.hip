@@ -289,14 +289,21 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
   const GridRange all_rows{0, c.wg_rows}, all_pred{0, c.wg_pred}, all_mtp{0, c.wg_mtp}, all_red{0, c.wg_red};
   const int mode = !ef ? (momentum ? 4 : 3) : defer_in ? (momentum ? 6 : 5) : (momentum ? 2 : 1);
 
-  PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_pack(c, grads, U, p->beta, pbuf), "pass-through pack");
+  // The pass-through values are packed into the P buffer: by the first
+  // pass's extra workgroups on the vector path, by a launch of their own on
+  // the matrix-core path.
+  LaunchCtx c1 = c;
+  if (c.mfma)
+    PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_pack(c, grads, U, p->beta, pbuf), "pass-through pack");
+  else
+    c1.pack_dst = pbuf;
   if (refresh_iters <= 0) {
-    PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, all_rows, all_pred, mode, grads, err, U, q, pbuf, -1),
+    PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c1, all_rows, all_pred, mode, grads, err, U, q, pbuf, -1),
                 "EF-add + P = M Q");
   } else {
     // PowerSGD+ step: M = X + E first, then the subspace refresh of every
     // warm-start Q on M, then P = M Q with the refreshed Q.
-    PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c, all_rows, all_pred, mode, grads, err, U, q, c.rscr, -1),
+    PSGD_LAUNCH(PSGD_STAGE_EF_P, stage_mq(p, c1, all_rows, all_pred, mode, grads, err, U, q, c.rscr, -1),
                 "EF-add");
     for (int it = 0; it < refresh_iters; ++it) {
       PSGD_LAUNCH(PSGD_STAGE_REFRESH, stage_mq(p, c, all_rows, all_pred, 0, nullptr, err, nullptr, q, c.rscr, -1),
@@ -335,11 +342,16 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
       return PSGD_ERR_HOOK;
     }
   }
+  // Aggregated pass-through values back out (with M_hat or the SGD step):
+  // extra workgroups of the residual pass on the vector path.
+  const bool unpack = mhat || sg.x;
+  LaunchCtx c3 = c;
+  if (unpack && !c.mfma) c3.unpack_src = pbuf;
   if (!defer_out)
-    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, err, q, pbuf, mhat, true, sg), "residual E = M - P_hat Q^T");
-  else if (mhat || sg.x)  // err keeps M; only the decompressed update is written
-    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, nullptr, q, pbuf, mhat, false, sg), "decompress P_hat Q^T");
-  if (mhat || sg.x)
+    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c3, err, q, pbuf, mhat, true, sg), "residual E = M - P_hat Q^T");
+  else if (unpack)  // err keeps M; only the decompressed update is written
+    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c3, nullptr, q, pbuf, mhat, false, sg), "decompress P_hat Q^T");
+  if (unpack && c.mfma)
     PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat, sg), "pass-through unpack");
   return PSGD_OK;
 }
@@ -361,10 +373,11 @@ extern "C" psgd_status_t psgd_decompress(psgd_plan_t p, const float* pbuf, const
   }
   if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_decompress")) return s;
   if (p->ntensors == 0) return PSGD_OK;
-  const LaunchCtx c = make_ctx(p, ws, stream);
+  LaunchCtx c = make_ctx(p, ws, stream);
   const SgdArgs none{nullptr, nullptr, 0.f, 0.f};
+  if (!c.mfma) c.unpack_src = pbuf;  // pass-through values by extra workgroups of the same launch
   PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, nullptr, q, pbuf, out, false, none), "decompress P_hat Q^T");
-  PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out, none), "pass-through unpack");
+  if (c.mfma) PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out, none), "pass-through unpack");
   return PSGD_OK;
 }
 

@@ -170,6 +170,55 @@ constexpr int pow2_at_least(int x) {
 }
 
 // ---------------------------------------------------------------------------
+// Pass-through tensors
+// ---------------------------------------------------------------------------
+
+// One pass-through workgroup (kPassChunk elements of one tensor): the value
+// (u = beta u + G first with momentum) copied into the P buffer after the
+// factors, where the P aggregation carries it.
+template <bool MOM, bool GBF16>
+__device__ __forceinline__ void pass_pack_wg(const PassDesc* __restrict__ pass, const int32_t* __restrict__ map,
+                                             int wg, const void* __restrict__ G, float* __restrict__ U, float beta,
+                                             float* __restrict__ Pbuf) {
+  const PassDesc pd = pass[map[wg]];
+  const int64_t c0 = (int64_t)(wg - pd.wg0) * kPassChunk;
+  const int64_t c1 = c0 + kPassChunk < pd.len ? c0 + kPassChunk : pd.len;
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
+    float x;
+    if constexpr (GBF16)
+      x = bf16_to_f32(static_cast<const uint16_t*>(G)[pd.off + i]);
+    else
+      x = static_cast<const float*>(G)[pd.off + i];
+    if constexpr (MOM) {
+      x = fmaf(beta, U[pd.off + i], x);
+      U[pd.off + i] = x;
+    }
+    Pbuf[pd.p_off + i] = x;
+  }
+}
+
+// Aggregated pass-through values back to flat buffers: into `out` (if
+// non-null) and/or as the update of the fused SGD step.
+template <bool SGD>
+__device__ __forceinline__ void pass_unpack_wg(const PassDesc* __restrict__ pass, const int32_t* __restrict__ map,
+                                               int wg, const float* __restrict__ Pbuf, float* __restrict__ out,
+                                               const SgdArgs& sg) {
+  const PassDesc pd = pass[map[wg]];
+  const int64_t c0 = (int64_t)(wg - pd.wg0) * kPassChunk;
+  const int64_t c1 = c0 + kPassChunk < pd.len ? c0 + kPassChunk : pd.len;
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
+    const float v = Pbuf[pd.p_off + i];
+    if (out) out[pd.off + i] = v;
+    if constexpr (SGD) {
+      const float mm = fmaf(sg.mu, sg.m[pd.off + i], v);
+      sg.m[pd.off + i] = mm;
+      const float dir = sg.nesterov ? fmaf(sg.mu, mm, v) : mm;
+      sg.x[pd.off + i] = fmaf(-sg.lr, dir, sg.x[pd.off + i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pass 1: EF-add (+ momentum) and P = M Q
 // ---------------------------------------------------------------------------
 
@@ -316,13 +365,24 @@ __device__ __forceinline__ RowTile row_tile(const MatDesc& d, int local, int spl
 
 // P (or, for a column-split matrix, the split's partial in ppart, summed
 // afterwards in fixed order) at the plan's offsets or at p_fixed.
+// Workgroups from nrow_wg on pack the pass-through tensors (the launch's
+// extra workgroups, when pack_dst is given).
 template <int R, int MODE, bool GBF16>
 __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__ mats,
                                                      const int32_t* __restrict__ map, int wg_base,
                                                      const void* __restrict__ G, float* __restrict__ E,
                                                      float* __restrict__ U, float beta,
                                                      const float* __restrict__ Q, float* P, int64_t p_fixed,
-                                                     const float* Pold, float* __restrict__ ppart) {
+                                                     const float* Pold, float* __restrict__ ppart, int nrow_wg,
+                                                     const PassDesc* __restrict__ pass,
+                                                     const int32_t* __restrict__ pass_map, float* pack_dst) {
+  if constexpr (MODE != 0) {
+    if ((int)blockIdx.x >= nrow_wg) {
+      constexpr bool MOM = MODE == 2 || MODE == 4 || MODE == 6;
+      pass_pack_wg<MOM, GBF16>(pass, pass_map, blockIdx.x - nrow_wg, G, U, beta, pack_dst);
+      return;
+    }
+  }
   const int wg = blockIdx.x + wg_base;
   const MatDesc d = mats[map[wg]];
   // wave index made provably uniform: row addressing and P_hat loads go scalar
@@ -520,11 +580,19 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int c0, i
   }
 }
 
+// Workgroups from nrec_wg on unpack the pass-through tensors (the launch's
+// extra workgroups, when unpack_src is given).
 template <int R, bool RESID, bool WRITE_MHAT, bool SGD>
 __global__ __launch_bounds__(kWGThreads) void k_recon(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
                                                       float* __restrict__ E, const float* __restrict__ Q,
                                                       const float* __restrict__ Ph, float* __restrict__ Mhat,
-                                                      SgdArgs sg) {
+                                                      SgdArgs sg, int nrec_wg, const PassDesc* __restrict__ pass,
+                                                      const int32_t* __restrict__ pass_map,
+                                                      const float* __restrict__ unpack_src) {
+  if ((int)blockIdx.x >= nrec_wg) {
+    pass_unpack_wg<SGD>(pass, pass_map, blockIdx.x - nrec_wg, unpack_src, Mhat, sg);
+    return;
+  }
   const int wg = blockIdx.x;
   const MatDesc d = mats[map[wg]];
   // wave index made provably uniform: row addressing and P_hat loads go scalar
@@ -547,44 +615,14 @@ template <bool MOM, bool GBF16>
 __global__ __launch_bounds__(256) void k_pass_pack(const PassDesc* __restrict__ pass, const int32_t* __restrict__ map,
                                                    const void* __restrict__ G, float* __restrict__ U, float beta,
                                                    float* __restrict__ Pbuf) {
-  const int wg = blockIdx.x;
-  const PassDesc pd = pass[map[wg]];
-  const int64_t c0 = (int64_t)(wg - pd.wg0) * kPassChunk;
-  const int64_t c1 = c0 + kPassChunk < pd.len ? c0 + kPassChunk : pd.len;
-  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
-    float x;
-    if constexpr (GBF16)
-      x = bf16_to_f32(static_cast<const uint16_t*>(G)[pd.off + i]);
-    else
-      x = static_cast<const float*>(G)[pd.off + i];
-    if constexpr (MOM) {
-      x = fmaf(beta, U[pd.off + i], x);
-      U[pd.off + i] = x;
-    }
-    Pbuf[pd.p_off + i] = x;
-  }
+  pass_pack_wg<MOM, GBF16>(pass, map, blockIdx.x, G, U, beta, Pbuf);
 }
 
-// Aggregated pass-through values back to flat buffers: into `out` (if
-// non-null) and/or as the update of the fused SGD step.
 template <bool SGD>
 __global__ __launch_bounds__(256) void k_pass_unpack(const PassDesc* __restrict__ pass, const int32_t* __restrict__ map,
                                                      const float* __restrict__ Pbuf, float* __restrict__ out,
                                                      SgdArgs sg) {
-  const int wg = blockIdx.x;
-  const PassDesc pd = pass[map[wg]];
-  const int64_t c0 = (int64_t)(wg - pd.wg0) * kPassChunk;
-  const int64_t c1 = c0 + kPassChunk < pd.len ? c0 + kPassChunk : pd.len;
-  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
-    const float v = Pbuf[pd.p_off + i];
-    if (out) out[pd.off + i] = v;
-    if constexpr (SGD) {
-      const float mm = fmaf(sg.mu, sg.m[pd.off + i], v);
-      sg.m[pd.off + i] = mm;
-      const float dir = sg.nesterov ? fmaf(sg.mu, mm, v) : mm;
-      sg.x[pd.off + i] = fmaf(-sg.lr, dir, sg.x[pd.off + i]);
-    }
-  }
+  pass_unpack_wg<SGD>(pass, map, blockIdx.x, Pbuf, out, sg);
 }
 
 // Plain 16-byte copy: the bandwidth ceiling and counter calibration.
@@ -675,10 +713,12 @@ __global__ __launch_bounds__(256) void k_round_bf16(float* __restrict__ buf, int
 template <int R, bool GBF16>
 static hipError_t launch_ef_p_rg(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                                  float beta, const float* Q, float* P, int64_t p_fixed) {
-  const dim3 gr(g.count), b(kWGThreads);
+  const int extra = c.pack_dst ? c.wg_pass : 0;
+  if (g.count + extra == 0) return hipSuccess;
+  const dim3 gr(g.count + extra), b(kWGThreads);
 #define PSGD_EFP(MD)                                                                                            \
   hipLaunchKernelGGL((k_ef_p<R, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, \
-                     p_fixed, c.p_prev, c.ppart)
+                     p_fixed, c.p_prev, c.ppart, g.count, c.pass, c.pass_map, c.pack_dst)
   switch (mode) {
     case 1: PSGD_EFP(1); break;
     case 2: PSGD_EFP(2); break;
@@ -694,10 +734,10 @@ static hipError_t launch_ef_p_rg(const LaunchCtx& c, const GridRange& g, int mod
 template <int R>
 static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                                 float beta, const float* Q, float* P, int64_t p_fixed) {
-  if (g.count == 0) return hipSuccess;
-  if (mode == 0) {  // P = M Q with M read from E: no gradient involved
+  if (mode == 0) {  // P = M Q with M read from E: no gradient involved, no packing
+    if (g.count == 0) return hipSuccess;
     hipLaunchKernelGGL((k_ef_p<R, 0, false>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map,
-                       g.base, G, E, U, beta, Q, P, p_fixed, nullptr, c.ppart);
+                       g.base, G, E, U, beta, Q, P, p_fixed, nullptr, c.ppart, g.count, c.pass, c.pass_map, nullptr);
     return hipGetLastError();
   }
   return c.g_bf16 ? launch_ef_p_rg<R, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)
@@ -716,11 +756,13 @@ static hipError_t launch_mtp_r(const LaunchCtx& c, const GridRange& g, const flo
 template <int R>
 static hipError_t launch_recon_r(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
                                  bool residual, const SgdArgs& sg) {
-  if (c.wg_rec == 0) return hipSuccess;
-  const dim3 g(c.wg_rec), b(kWGThreads);
+  const int extra = c.unpack_src ? c.wg_pass : 0;
+  if (c.wg_rec + extra == 0) return hipSuccess;
+  const dim3 g(c.wg_rec + extra), b(kWGThreads);
   const bool mh = Mhat != nullptr, sgd = sg.x != nullptr;
 #define PSGD_RECON(RS, MH, SG)                                                                                  \
-  hipLaunchKernelGGL((k_recon<R, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rec_map, E, Q, Ph, Mhat, sg)
+  hipLaunchKernelGGL((k_recon<R, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rec_map, E, Q, Ph, Mhat, sg, c.wg_rec, \
+                     c.pass, c.pass_map, c.unpack_src)
   if (residual) {
     if (mh && sgd) PSGD_RECON(true, true, true);
     else if (mh) PSGD_RECON(true, true, false);

@@ -35,6 +35,11 @@ struct LaunchCtx {
   const int32_t* gramq_map;
   float* part;    // partial-Q scratch
   float* ppart;   // partial-P scratch (column splits of pass 1)
+  // Vector-ALU path: the pass-through packing runs as extra workgroups of
+  // the pass-1 launch (into pack_dst, when non-null) and the unpacking as
+  // extra workgroups of the residual-pass launch (from unpack_src).
+  float* pack_dst;
+  const float* unpack_src;
   double* gram;   // orthonormalisation scratch
   float* rscr;    // refresh scratch
 };
