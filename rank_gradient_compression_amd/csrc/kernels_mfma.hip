@@ -189,18 +189,15 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
   // Raw loads of one 64-column step (G, E and u as the mode needs).  At rank
   // 16 the next step's loads are issued before the current step's EF-add, Q
   // staging and matrix products, so two steps of loads are in flight per
-  // wavefront (measured: 6% faster there; neutral or slower at higher ranks
-  // and for the plain M Q of the refresh, where it is left out).
-  constexpr bool PREFETCH = MODE != 0 && RP <= 16;
-  constexpr bool LOAD_G = MODE != 0;
-  constexpr bool DEFERRED = MODE >= 5;
-  constexpr bool LOAD_E = MODE <= 2 || DEFERRED;
-  constexpr bool MOM = MODE == 2 || MODE == 4 || MODE == 6;
+  // wavefront (measured: 6% faster there; neutral or slower at higher ranks).
+  static_assert(MODE == 5 || MODE == 6, "the register form serves the deferred-residual modes");
+  constexpr bool PREFETCH = RP <= 16;
+  constexpr bool MOM = MODE == 6;
   constexpr int KS = RP / 4;
   // Deferred residual: B operand P_hat_old^T of this wavefront's 16 rows,
   // lane (li, ls) holding Pold[row][4 kk + ls] (read before any P is written).
-  float bfr[DEFERRED ? KS : 1];
-  if constexpr (DEFERRED) {
+  float bfr[KS];
+  {
     const float* po = Pold + d.p_off;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -216,13 +213,13 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
     for (int qq = 0; qq < 4; ++qq) {
       const int col = c0 + 16 * qq + 4 * ls;
       const bool col_ok = col < c_end;
-      if constexpr (LOAD_G) {
+      {
         if constexpr (GBF16)
           st.g[qq] = ldq_bf16<VEC4>(static_cast<const uint16_t*>(G) + roff, col, col_ok, c_begin, n);
         else
           st.g[qq] = ldq<VEC4>(static_cast<const float*>(G) + roff, col, col_ok, c_begin, n);
       }
-      if constexpr (LOAD_E) st.e[qq] = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
+      st.e[qq] = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
       if constexpr (MOM) st.u[qq] = ldq<VEC4>(U + roff, col, col_ok, c_begin, n);
     }
   };
@@ -245,8 +242,8 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
       }
       lds_barrier();
     };
-    float4 mh[DEFERRED ? 4 : 1];
-    if constexpr (DEFERRED) {
+    float4 mh[4];
+    {
       // Q first: the reconstruction of the previous step needs it before the
       // EF-add; A = Q[c0 + 16 qq + li][4 kk + ls] from the staged tile.
       stage_q();
@@ -263,13 +260,10 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
     for (int qq = 0; qq < 4; ++qq) {
       const int col = c0 + 16 * qq + 4 * ls;
       const bool col_ok = col < c_end;
-      if constexpr (MODE == 0) {
-        x[qq] = cur.e[qq];
-      } else {
+      {
         const float4 g = cur.g[qq];
-        float4 e = LOAD_E ? cur.e[qq] : make_float4(0.f, 0.f, 0.f, 0.f);
-        if constexpr (DEFERRED)
-          e = make_float4(e.x - mh[qq].x, e.y - mh[qq].y, e.z - mh[qq].z, e.w - mh[qq].w);
+        float4 e = cur.e[qq];
+        e = make_float4(e.x - mh[qq].x, e.y - mh[qq].y, e.z - mh[qq].z, e.w - mh[qq].w);
         float4 s;
         if constexpr (MOM) {
           float4 u = cur.u[qq];
@@ -286,7 +280,6 @@ __device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, con
         x[qq] = s;
       }
     }
-    if constexpr (!DEFERRED) stage_q();
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const float xv[4] = {x[qq].x, x[qq].y, x[qq].z, x[qq].w};
