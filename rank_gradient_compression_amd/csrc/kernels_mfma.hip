@@ -24,8 +24,9 @@
 //   pass 1  P = M Q (with the EF-add and optional momentum): a workgroup
 //           walks its 64-row tile of one column split in 128-column chunks
 //           (M formed, stored back and staged in LDS with the chunk of Q);
-//           split partials are summed in fixed order.  The deferred-residual
-//           modes keep a register form.
+//           split partials are summed in fixed order.  With a deferred
+//           residual each wavefront first forms its 16 rows of the previous
+//           step's reconstruction in LDS from the staged Q chunk.
 //   pass 2  Q = M^T P_hat: a workgroup walks 256 columns of a row block in
 //           32-row chunks staged in LDS with the chunk's P_hat rows.
 //   pass 3  M_hat = P_hat Q^T computed transposed (M_hat^T = Q P_hat^T) into
@@ -157,164 +158,6 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 // in, so E is formed bit for bit as the residual pass would have stored it.
 // ---------------------------------------------------------------------------
 
-// Register form (the deferred-residual modes 5 and 6; modes 0..4 take the
-// staged form further down): the workgroup's four wavefronts take 16 rows
-// each of the 64-row tile and walk the column split in 64-column steps; each
-// Q chunk is staged once in LDS and shared by the four wavefronts, and each
-// lane's 16-byte loads of G and E feed the matrix core directly.
-
-template <int RP, int MODE, bool VEC4, bool GBF16>
-__device__ __forceinline__ void mfma_p_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
-                                            float* __restrict__ E, float* __restrict__ U, float beta,
-                                            const float* __restrict__ Q, float* P, int64_t p_fixed,
-                                            float* __restrict__ ppart, float* Qs, const float* Pold) {
-  constexpr int QS = RP + 4;  // LDS row stride: conflict-free B-operand reads
-  const int m = d.m, n = d.n;
-  const int local = wg - d.wg_rows0;
-  const int rb = local / d.s1, split = local - rb * d.s1;
-  const int c_begin = split * d.s1_cols;
-  const int c_end = min(n, c_begin + d.s1_cols);
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int li = lane & 15, ls = lane >> 4;
-  const int i0 = rb * kMfmaRows + wave * 16;
-  const int row = i0 + li;
-  const bool row_ok = row < m;
-  const int64_t roff = d.off + (int64_t)min(row, m - 1) * n;
-  const float* q = Q + d.q_off;
-
-  v4f acc[RP / 16];
-#pragma unroll
-  for (int T = 0; T < RP / 16; ++T) acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // Raw loads of one 64-column step (G, E and u as the mode needs).  At rank
-  // 16 the next step's loads are issued before the current step's EF-add, Q
-  // staging and matrix products, so two steps of loads are in flight per
-  // wavefront (measured: 6% faster there; neutral or slower at higher ranks).
-  static_assert(MODE == 5 || MODE == 6, "the register form serves the deferred-residual modes");
-  constexpr bool PREFETCH = RP <= 16;
-  constexpr bool MOM = MODE == 6;
-  constexpr int KS = RP / 4;
-  // Deferred residual: B operand P_hat_old^T of this wavefront's 16 rows,
-  // lane (li, ls) holding Pold[row][4 kk + ls] (read before any P is written).
-  float bfr[KS];
-  {
-    const float* po = Pold + d.p_off;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int t = 4 * kk + ls;
-      bfr[kk] = (row_ok && t < r) ? po[(int64_t)t * m + row] : 0.f;
-    }
-  }
-  struct Step {
-    float4 g[4], e[4], u[4];
-  };
-  auto load = [&](int c0, Step& st) {
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int col = c0 + 16 * qq + 4 * ls;
-      const bool col_ok = col < c_end;
-      {
-        if constexpr (GBF16)
-          st.g[qq] = ldq_bf16<VEC4>(static_cast<const uint16_t*>(G) + roff, col, col_ok, c_begin, n);
-        else
-          st.g[qq] = ldq<VEC4>(static_cast<const float*>(G) + roff, col, col_ok, c_begin, n);
-      }
-      st.e[qq] = ldq<VEC4>(E + roff, col, col_ok, c_begin, n);
-      if constexpr (MOM) st.u[qq] = ldq<VEC4>(U + roff, col, col_ok, c_begin, n);
-    }
-  };
-
-  Step cur, nxt;
-  if (PREFETCH && c_begin < c_end) load(c_begin, cur);
-  for (int c0 = c_begin; c0 < c_end; c0 += 64) {
-    if constexpr (PREFETCH) {
-      if (c0 + 64 < c_end) load(c0 + 64, nxt);
-    } else {
-      load(c0, cur);
-    }
-    auto stage_q = [&]() {
-      lds_barrier();  // previous step's reads of Qs are done
-      for (int e = threadIdx.x; e < 64 * RP; e += 256) {
-        const int c = e & 63, t = e >> 6;
-        float v = 0.f;
-        if (t < r && c0 + c < c_end) v = q[(int64_t)t * n + c0 + c];
-        Qs[c * QS + t] = v;
-      }
-      lds_barrier();
-    };
-    float4 mh[4];
-    {
-      // Q first: the reconstruction of the previous step needs it before the
-      // EF-add; A = Q[c0 + 16 qq + li][4 kk + ls] from the staged tile.
-      stage_q();
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        v4f a4 = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) a4 = mfma16x16x4(Qs[(16 * qq + li) * QS + 4 * kk + ls], bfr[kk], a4);
-        mh[qq] = make_float4(a4[0], a4[1], a4[2], a4[3]);
-      }
-    }
-    float4 x[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int col = c0 + 16 * qq + 4 * ls;
-      const bool col_ok = col < c_end;
-      {
-        const float4 g = cur.g[qq];
-        float4 e = cur.e[qq];
-        e = make_float4(e.x - mh[qq].x, e.y - mh[qq].y, e.z - mh[qq].z, e.w - mh[qq].w);
-        float4 s;
-        if constexpr (MOM) {
-          float4 u = cur.u[qq];
-          u.x = fmaf(beta, u.x, g.x);
-          u.y = fmaf(beta, u.y, g.y);
-          u.z = fmaf(beta, u.z, g.z);
-          u.w = fmaf(beta, u.w, g.w);
-          if (row_ok && col_ok) stq<VEC4>(U + roff, col, n, u);
-          s = make_float4(u.x + e.x, u.y + e.y, u.z + e.z, u.w + e.w);
-        } else {
-          s = make_float4(g.x + e.x, g.y + e.y, g.z + e.z, g.w + e.w);
-        }
-        if (row_ok && col_ok) stq<VEC4>(E + roff, col, n, s);
-        x[qq] = s;
-      }
-    }
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const float xv[4] = {x[qq].x, x[qq].y, x[qq].z, x[qq].w};
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float a = row_ok ? xv[v] : 0.f;
-        const float* qrow = &Qs[(16 * qq + 4 * ls + v) * QS + li];
-#pragma unroll
-        for (int T = 0; T < RP / 16; ++T) acc[T] = mfma16x16x4(a, qrow[16 * T], acc[T]);
-      }
-    }
-    if constexpr (PREFETCH) cur = nxt;
-  }
-
-  // Results leave through LDS so that each store instruction writes
-  // consecutive rows of one P column (D holds 16 columns x 4 rows per lane
-  // group, which would otherwise scatter 4-byte stores).
-  float* dst = d.s1 > 1 ? ppart + d.ppart_off + (int64_t)split * r * m : P + (p_fixed >= 0 ? p_fixed : d.p_off);
-  constexpr int OS = kMfmaRows + 1;
-  float* Os = Qs;  // 16 x OS floats fit in the Q staging buffer
-  const int rbase = rb * kMfmaRows;
-#pragma unroll
-  for (int T = 0; T < RP / 16; ++T) {
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Os[li * OS + wave * 16 + 4 * ls + e] = acc[T][e];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * kMfmaRows; idx += 256) {
-      const int tl = idx / kMfmaRows, rl = idx % kMfmaRows;
-      const int t = 16 * T + tl, rr = rbase + rl;
-      if (t < r && rr < m) dst[(int64_t)t * m + rr] = Os[tl * OS + rl];
-    }
-  }
-}
-
 // P = M Q with the EF-add of MODE 1..4 (or M as is, MODE 0: the refresh),
 // staged: a workgroup owns the 64-row tile of its column split and walks the
 // split in kMqChunk-column chunks.  Each wavefront loads 16 rows of a chunk
@@ -336,11 +179,13 @@ template <int RP, int MODE, bool VEC4, bool GBF16>
 __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
                                              float* __restrict__ E, float* __restrict__ U, float beta,
                                              const float* __restrict__ Q, float* P, int64_t p_fixed,
-                                             float* __restrict__ ppart, float* smem) {
-  static_assert(MODE >= 0 && MODE <= 4, "staged pass 1 modes");
+                                             float* __restrict__ ppart, float* smem, const float* Pold) {
+  static_assert(MODE >= 0 && MODE <= 6, "pass 1 modes");
   constexpr bool LOAD_G = MODE != 0;
-  constexpr bool LOAD_E = MODE <= 2;
-  constexpr bool MOM = MODE == 2 || MODE == 4;
+  constexpr bool DEFERRED = MODE >= 5;
+  constexpr bool LOAD_E = MODE <= 2 || DEFERRED;
+  constexpr bool MOM = MODE == 2 || MODE == 4 || MODE == 6;
+  constexpr int KS = RP / 4;
   constexpr int QLD = kMqChunk + 4;                         // LDS stride of one rank's Q chunk
   constexpr int QPT = (RP * kMqChunk / 4 + 255) / 256;      // Q float4s a thread loads per chunk
   float* Ms = smem;                                         // [64 rows][kMqLd]
@@ -360,6 +205,19 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   v4f acc[RP / 16];
 #pragma unroll
   for (int T = 0; T < RP / 16; ++T) acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Deferred residual: B operand P_hat_old^T of the wavefront's 16 rows, lane
+  // (li, ls) holding Pold[row][4 kk + ls] (read before any P is written).
+  float bfr[DEFERRED ? KS : 1];
+  if constexpr (DEFERRED) {
+    const int row = i0 + 16 * wave + li;
+    const float* po = Pold + d.p_off;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int t = 4 * kk + ls;
+      bfr[kk] = (row < m && t < r) ? po[(int64_t)t * m + row] : 0.f;
+    }
+  }
 
   float4 xg[8], xe[LOAD_E ? 8 : 1], xu[MOM ? 8 : 1], qn[QPT];
   auto row_of = [&](int u) { return i0 + 16 * wave + 2 * u + hr; };
@@ -389,19 +247,48 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
                                                : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  // EF-add of the loaded chunk, M (and u) stored back, M into the LDS tile.
-  auto store_chunk = [&](int c0) {
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      if (e < RP * kMqChunk / 4)
+        *reinterpret_cast<float4*>(&Qs[(e / (kMqChunk / 4)) * QLD + 4 * (e % (kMqChunk / 4))]) = qn[u];
+    }
+  };
+  // Deferred residual: the previous step's reconstruction of the wavefront's
+  // 16 rows x kMqChunk columns, M_hat^T = Q P_hat_old^T tile by tile (A = Q
+  // from LDS, the same operands and rank order as the residual pass), into
+  // the wavefront's own rows of Ms in the result layout (row li, columns
+  // 4 ls .. 4 ls + 3).
+  auto recon_tile = [&]() {
+#pragma unroll
+    for (int ct = 0; ct < kMqChunk / 16; ++ct) {
+      v4f a4 = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) a4 = mfma16x16x4(Qs[(4 * kk + ls) * QLD + 16 * ct + li], bfr[kk], a4);
+      *reinterpret_cast<float4*>(&Ms[(16 * wave + li) * kMqLd + 16 * ct + 4 * ls]) =
+          make_float4(a4[0], a4[1], a4[2], a4[3]);
+    }
+  };
+  // EF-add of the loaded chunk (E = E_in - M_hat_old first with a deferred
+  // residual), M (and u) stored back, M into the wavefront's rows of Ms.
+  auto ef_chunk = [&](int c0) {
     const int col = c0 + cl4;
     const bool col_ok = col < c_end;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int row = row_of(u);
+      float* mrow = &Ms[(16 * wave + 2 * u + hr) * kMqLd + cl4];
       float4 s;
       if constexpr (MODE == 0) {
         s = xg[u];
       } else {
         const float4 g = xg[u];
-        const float4 e = LOAD_E ? xe[LOAD_E ? u : 0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 e = LOAD_E ? xe[LOAD_E ? u : 0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (DEFERRED) {
+          const float4 mh = *reinterpret_cast<const float4*>(mrow);
+          e = make_float4(e.x - mh.x, e.y - mh.y, e.z - mh.z, e.w - mh.w);
+        }
         if constexpr (MOM) {
           float4 uu = xu[MOM ? u : 0];
           uu.x = fmaf(beta, uu.x, g.x);
@@ -415,20 +302,23 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
         }
         if (row < m && col_ok) stq<VEC4>(E + d.off + (int64_t)row * n, col, n, s);
       }
-      *reinterpret_cast<float4*>(&Ms[(16 * wave + 2 * u + hr) * kMqLd + cl4]) = s;
-    }
-#pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-      const int e = threadIdx.x + 256 * u;
-      if (e < RP * kMqChunk / 4)
-        *reinterpret_cast<float4*>(&Qs[(e / (kMqChunk / 4)) * QLD + 4 * (e % (kMqChunk / 4))]) = qn[u];
+      *reinterpret_cast<float4*>(mrow) = s;
     }
   };
 
+  // A wavefront reads only its own rows of Ms, so the barrier per chunk
+  // guards the shared Q chunk (and the overwrite of both tiles).
   load_chunk(c_begin);
   for (int c0 = c_begin; c0 < c_end; c0 += kMqChunk) {
-    store_chunk(c0);
-    __syncthreads();
+    stage_q();
+    if constexpr (DEFERRED) {
+      __syncthreads();
+      recon_tile();
+      ef_chunk(c0);
+    } else {
+      ef_chunk(c0);
+      __syncthreads();
+    }
     if (c0 + kMqChunk < c_end) load_chunk(c0 + kMqChunk);
 #pragma unroll
     for (int kb = 0; kb < kMqChunk / 16; ++kb) {
@@ -467,25 +357,14 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
                                                 float* __restrict__ E, float* __restrict__ U, float beta,
                                                 const float* __restrict__ Q, float* P, int64_t p_fixed,
                                                 float* __restrict__ ppart, const float* Pold) {
-  constexpr bool STAGED = MODE <= 4;  // the deferred-residual modes keep the register form
-  constexpr int QS = RP + 4;
-  static_assert(16 * (kMfmaRows + 1) <= 64 * QS, "output staging does not fit");
-  constexpr int SMEM = STAGED ? kMfmaRows * kMqLd + RP * (kMqChunk + 4) : 64 * QS;
-  __shared__ float smem[SMEM];
+  __shared__ float smem[kMfmaRows * kMqLd + RP * (kMqChunk + 4)];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
-  if constexpr (STAGED) {
-    if (d.vec == 4)
-      mfma_mq_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem);
-    else
-      mfma_mq_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem);
-  } else {
-    if (d.vec == 4)
-      mfma_p_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
-    else
-      mfma_p_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
-  }
+  if (d.vec == 4)
+    mfma_mq_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
+  else
+    mfma_mq_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
 }
 
 // Fixed-order sum of the column-split partials of pass 1.
