@@ -122,14 +122,20 @@ __device__ __forceinline__ float4 ldq_bf16(const uint16_t* rowp, int col, bool o
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (VEC4) {
     const uint2 t = *reinterpret_cast<const uint2*>(rowp + (ok ? col : col_safe));
-    if (ok)
-      r = make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u), __uint_as_float(t.y << 16),
-                      __uint_as_float(t.y & 0xffff0000u));
-  } else if (ok) {
-    if (col < n) r.x = __uint_as_float((uint32_t)rowp[col] << 16);
-    if (col + 1 < n) r.y = __uint_as_float((uint32_t)rowp[col + 1] << 16);
-    if (col + 2 < n) r.z = __uint_as_float((uint32_t)rowp[col + 2] << 16);
-    if (col + 3 < n) r.w = __uint_as_float((uint32_t)rowp[col + 3] << 16);
+    const float4 v = make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u),
+                                 __uint_as_float(t.y << 16), __uint_as_float(t.y & 0xffff0000u));
+    r = ok ? v : r;
+  } else {
+    // clamped addresses (col_safe < n), values zeroed past the row end
+    const int c = ok ? col : col_safe;
+    const uint32_t a0 = rowp[min(c, n - 1)], a1 = rowp[min(c + 1, n - 1)];
+    const uint32_t a2 = rowp[min(c + 2, n - 1)], a3 = rowp[min(c + 3, n - 1)];
+    if (ok) {
+      r.x = col < n ? __uint_as_float(a0 << 16) : 0.f;
+      r.y = col + 1 < n ? __uint_as_float(a1 << 16) : 0.f;
+      r.z = col + 2 < n ? __uint_as_float(a2 << 16) : 0.f;
+      r.w = col + 3 < n ? __uint_as_float(a3 << 16) : 0.f;
+    }
   }
   return r;
 }
@@ -703,9 +709,19 @@ __global__ __launch_bounds__(256) void k_gram_partial(const OrthDesc* __restrict
   const OrthDesc o = descs[orth_idx(descs, map, first, local)];
   const float* p = base + o.off;
   const int r0 = local * kGramRows;
-  for (int e = threadIdx.x; e < kGramChunk * RP; e += 256) {
-    const int i = e % kGramChunk, t = e / kGramChunk;
-    Pl[i * LS + t] = (t < r && r0 + i < o.rows) ? p[(int64_t)t * o.rows + r0 + i] : 0.f;
+  // Every load at a clamped, valid address and the value zeroed when out of
+  // range: no branches, so all of a thread's loads are in flight together.
+  constexpr int NL = kGramChunk * RP / 256;
+  float v[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int e = threadIdx.x + 256 * u, i = e % kGramChunk, t = e / kGramChunk;
+    v[u] = p[(int64_t)min(t, r - 1) * o.rows + min(r0 + i, o.rows - 1)];
+  }
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int e = threadIdx.x + 256 * u, i = e % kGramChunk, t = e / kGramChunk;
+    Pl[i * LS + t] = (t < r && r0 + i < o.rows) ? v[u] : 0.f;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -729,8 +745,8 @@ __global__ __launch_bounds__(256) void k_gram_partial(const OrthDesc* __restrict
 
 // Fixed-order block sum: A (at t_off) = sum_b A_b.  A workgroup covers 256
 // entries of one factor's A with kGramRedGroups groups of 256 threads: group
-// g sums the blocks b = g, g + kGramRedGroups, ... in four running sums (so
-// that several loads are in flight), and the group totals are added in
+// g sums the blocks b = g, g + kGramRedGroups, ... in eight running sums (so
+// that eight loads are in flight), and the group totals are added in
 // group order through LDS.  The order is fixed: deterministic.
 constexpr int kGramRedGroups = 4;
 
@@ -745,16 +761,14 @@ __global__ __launch_bounds__(256 * kGramRedGroups) void k_gram_reduce(const Orth
   const int grp = threadIdx.x >> 8, t = threadIdx.x & 255;
   const int e = (blockIdx.x % WPD) * 256 + t;
   const double* g = gram + o.gram_off + e;
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  double s[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   int b = grp;
-  for (; b + 3 * NG < o.ngb; b += 4 * NG) {
-    s0 += g[b * BS];
-    s1 += g[(b + NG) * BS];
-    s2 += g[(b + 2 * NG) * BS];
-    s3 += g[(b + 3 * NG) * BS];
+  for (; b + 7 * NG < o.ngb; b += 8 * NG) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s[u] += g[(b + u * NG) * BS];
   }
-  for (; b < o.ngb; b += NG) s0 += g[b * BS];
-  tot[grp][t] = (s0 + s1) + (s2 + s3);
+  for (; b < o.ngb; b += NG) s[0] += g[b * BS];
+  tot[grp][t] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
   __syncthreads();
   if (grp == 0) {
     double a = tot[0][t];
@@ -771,16 +785,31 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+// 1 / sqrt(d) for a positive normal d: the hardware estimate refined by two
+// Newton steps y <- y + y (1 - d y^2) / 2, each of which roughly doubles the
+// number of correct bits, to within a few units in the last place of fp64.
+__device__ __forceinline__ double rsqrt_nr(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const double e = fma(-d * y, y, 1.0);
+    y = fma(0.5 * y, e, y);
+  }
+  return y;
+}
+
 // One wavefront per factor: right-looking Cholesky of A with the dependence
 // rule.  Lane j keeps column j of the (symmetric) Schur complement S in fp64
 // registers.  At step k the pivot S_kk comes from lane k's registers
 // (readlane), every lane publishes S_kj through LDS and reads the row S_k.
 // back as broadcasts, and updates S_ij -= S_ki (S_kj / S_kk) for i > k; only
-// the one reciprocal 1 / S_kk is on the step-to-step path.  Row k of R is
-// S_k. / sqrt(S_kk), zero for a dependent column: sqrt(S_kk) <= 1e-4 of the
+// the reciprocal square root of S_kk is on the step-to-step path.  Row k of R
+// is S_k. / sqrt(S_kk), zero for a dependent column: sqrt(S_kk) <= 1e-4 of the
 // norm before projection sqrt(A_kk), tested squared.  A single wavefront
-// needs no barrier: its LDS accesses complete in program order.  The upper
-// triangle of the factor's A slot is overwritten with R (A is read first).
+// needs no barrier: its LDS accesses complete in program order.  The lower
+// triangle of the factor's A slot (diagonal included) is overwritten with R
+// transposed, slot[j RP + k] = R_kj (A is read first), so that row k of the
+// slot lists column k of R, the coefficients of the k-th substitution step.
 template <int RP>
 __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
                                                    double* __restrict__ gram, float zero_rel) {
@@ -803,10 +832,9 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
       const double d = readlane_f64(sc[k], k);
       const double dg = readlane_f64(dgj, k);
       const bool zero = !(dg > 0.0) || !(d > 0.0) || d <= zr2 * dg;
-      const double inv2 = zero ? 0.0 : 1.0 / d;
-      const double c = sc[k] * inv2;  // S_kj / S_kk
-      const double nv = zero ? 0.0 : sqrt(d);
-      if (own && j >= k && j < r) a[k * RP + j] = j == k ? nv : sc[k] * (nv * inv2);
+      const double y = zero ? 0.0 : rsqrt_nr(d);  // 1 / sqrt(S_kk)
+      const double c = sc[k] * (y * y);            // S_kj / S_kk
+      if (own && j >= k && j < r) a[j * RP + k] = j == k ? d * y : sc[k] * y;
 #pragma unroll
       for (int i = k + 1; i < RP; ++i) sc[i] = fma(-rowbuf[i], c, sc[i]);
     }
@@ -818,29 +846,39 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
 // x is kept in fp64 registers and rounded to fp32 when stored (in place: p_k
 // is read before x_k overwrites it).  The sum runs in four interleaved
 // partial sums and the diagonal is applied as a reciprocal, so a row is not
-// one long chain of dependent operations.
+// one long chain of dependent operations.  The solve's transposed slot is
+// copied to LDS as it is (row k: the coefficients of step k), and the row's
+// p values are all loaded before the first step (clamped addresses, no
+// branches), so that their latencies overlap.
 template <int RP>
 __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restrict__ descs,
                                                        const int32_t* __restrict__ map, int first, int r,
                                                        float* __restrict__ base, const double* __restrict__ gram) {
-  __shared__ double Rt[RP * RP];  // R transposed: column k of R is contiguous
+  constexpr int NS = RP * RP / kGramRows;
+  static_assert(NS * kGramRows == RP * RP, "whole slot per thread");
+  __shared__ double Rt[RP * RP];  // Rt[k RP + j] = R_jk
   __shared__ double rinv[RP];
   int local;
   const OrthDesc o = descs[orth_idx(descs, map, first, local)];
-  const double* rg = gram + o.t_off;
-  for (int e = threadIdx.x; e < RP * RP; e += kGramRows) Rt[(e % RP) * RP + e / RP] = rg[e];
-  for (int k = threadIdx.x; k < RP; k += kGramRows) {
-    const double d = rg[k * RP + k];
-    rinv[k] = d > 0.0 ? 1.0 / d : 0.0;
-  }
-  __syncthreads();
+  const double* rt = gram + o.t_off;
   const int i = local * kGramRows + threadIdx.x;
-  if (i >= o.rows) return;
-  float* p = base + o.off + i;
+  float* p = base + o.off + min(i, o.rows - 1);
   const int64_t ld = o.rows;
+  float pv[RP];
+#pragma unroll
+  for (int k = 0; k < RP; ++k) pv[k] = p[(int64_t)min(k, r - 1) * ld];
+  double sv[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) sv[u] = rt[threadIdx.x + u * kGramRows];
+  const double dk = rt[min((int)threadIdx.x, RP - 1) * (RP + 1)];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) Rt[threadIdx.x + u * kGramRows] = sv[u];
+  if (threadIdx.x < RP) rinv[threadIdx.x] = dk > 0.0 ? 1.0 / dk : 0.0;
+  __syncthreads();
+  if (i >= o.rows) return;
   double x[RP];
 #pragma unroll
-  for (int k = 0; k < RP; ++k) x[k] = k < r ? (double)p[k * ld] : 0.0;
+  for (int k = 0; k < RP; ++k) x[k] = (double)pv[k];
 #pragma unroll
   for (int k = 0; k < RP; ++k) {
     if (k < r) {
