@@ -806,14 +806,14 @@ __device__ __forceinline__ double rsqrt_nr(double d) {
 // the reciprocal square root of S_kk is on the step-to-step path.  Row k of R
 // is S_k. / sqrt(S_kk), zero for a dependent column: sqrt(S_kk) <= 1e-4 of the
 // norm before projection sqrt(A_kk), tested squared.  A single wavefront
-// needs no barrier: its LDS accesses complete in program order.  The lower
-// triangle of the factor's A slot (diagonal included) is overwritten with R
-// transposed, slot[j RP + k] = R_kj (A is read first), so that row k of the
-// slot lists column k of R, the coefficients of the k-th substitution step.
+// needs no barrier: its LDS accesses complete in program order.  The upper
+// triangle of the factor's A slot (diagonal included) is overwritten with R,
+// row by row (A is read first).
 template <int RP>
 __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
                                                    double* __restrict__ gram, float zero_rel) {
   __shared__ double rowbuf[RP];
+  __shared__ double Rl[RP * RP];  // the factor, until it is written out
   const OrthDesc o = descs[first + blockIdx.x];
   const int j = threadIdx.x;
   const bool own = j < RP;
@@ -824,43 +824,58 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
   const double dgj = own ? a[j * RP + j] : 0.0;  // A_jj: squared norm before projection
   const double zr2 = (double)zero_rel * (double)zero_rel;
   // Fully unrolled so that sc[] stays in registers; steps k >= r are skipped
-  // by a uniform branch.
+  // by a uniform branch.  No global store inside the steps: a pending store
+  // would be waited for at every step.
 #pragma unroll
   for (int k = 0; k < RP; ++k) {
     if (k < r) {
       if (own) rowbuf[j] = sc[k];
+      // the whole row S_k. read back before the pivot arithmetic, so that the
+      // LDS latency overlaps it
+      double rk[RP];
+#pragma unroll
+      for (int i = k + 1; i < RP; ++i) rk[i] = rowbuf[i];
       const double d = readlane_f64(sc[k], k);
       const double dg = readlane_f64(dgj, k);
       const bool zero = !(dg > 0.0) || !(d > 0.0) || d <= zr2 * dg;
       const double y = zero ? 0.0 : rsqrt_nr(d);  // 1 / sqrt(S_kk)
       const double c = sc[k] * (y * y);            // S_kj / S_kk
-      if (own && j >= k && j < r) a[j * RP + k] = j == k ? d * y : sc[k] * y;
+      if (own && j >= k && j < r) Rl[k * RP + j] = j == k ? d * y : sc[k] * y;
 #pragma unroll
-      for (int i = k + 1; i < RP; ++i) sc[i] = fma(-rowbuf[i], c, sc[i]);
+      for (int i = k + 1; i < RP; ++i) sc[i] = fma(-rk[i], c, sc[i]);
     }
+  }
+  // write-out: slot[kr RP + jc] = R_{kr jc} for kr <= jc < r
+#pragma unroll
+  for (int u = 0; u < RP * RP / 64; ++u) {
+    const int e = j + 64 * u, kr = e / RP, jc = e % RP;
+    if (kr <= jc && jc < r) a[e] = Rl[e];
   }
 }
 
-// P_hat = P R^-1, one row per thread: x R = p by forward substitution,
-// x_k = (p_k - sum_{j<k} x_j R_jk) / R_kk, x_k = 0 for a dependent column;
-// x is kept in fp64 registers and rounded to fp32 when stored (in place: p_k
-// is read before x_k overwrites it).  The sum runs in four interleaved
-// partial sums and the diagonal is applied as a reciprocal, so a row is not
-// one long chain of dependent operations.  The solve's transposed slot is
-// copied to LDS as it is (row k: the coefficients of step k), and the row's
-// p values are all loaded before the first step (clamped addresses, no
-// branches), so that their latencies overlap.
+// P_hat = P R^-1, one row per thread: x R = p by forward substitution in
+// right-looking order.  Step k takes x_k = b_k / R_kk (b starts as p; x_k = 0
+// for a dependent column) and removes its share from the later right-hand
+// sides, b_i -= x_k R_ki for i > k, with row k of R: only x_k and the next
+// b_{k+1} are on the step-to-step path, and row k's coefficients, the same
+// for every thread, are LDS broadcasts that do not depend on x.  The steps
+// run in groups of four without branches so that the reads of later steps
+// can be issued early (steps k >= r inside the last group are harmless:
+// 1 / R_kk is set to 0 there, and their b_i are never stored).  x is kept in
+// fp64 registers and rounded to fp32 when stored in place.  The row's p
+// values are all loaded up front (clamped addresses, no branches).
 template <int RP>
 __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restrict__ descs,
                                                        const int32_t* __restrict__ map, int first, int r,
                                                        float* __restrict__ base, const double* __restrict__ gram) {
   constexpr int NS = RP * RP / kGramRows;
   static_assert(NS * kGramRows == RP * RP, "whole slot per thread");
-  __shared__ double Rt[RP * RP];  // Rt[k RP + j] = R_jk
+  static_assert(RP % 4 == 0, "groups of four steps");
+  __shared__ double Rr[RP * RP];  // Rr[k RP + i] = R_ki
   __shared__ double rinv[RP];
   int local;
   const OrthDesc o = descs[orth_idx(descs, map, first, local)];
-  const double* rt = gram + o.t_off;
+  const double* rs = gram + o.t_off;
   const int i = local * kGramRows + threadIdx.x;
   float* p = base + o.off + min(i, o.rows - 1);
   const int64_t ld = o.rows;
@@ -869,32 +884,37 @@ __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restric
   for (int k = 0; k < RP; ++k) pv[k] = p[(int64_t)min(k, r - 1) * ld];
   double sv[NS];
 #pragma unroll
-  for (int u = 0; u < NS; ++u) sv[u] = rt[threadIdx.x + u * kGramRows];
-  const double dk = rt[min((int)threadIdx.x, RP - 1) * (RP + 1)];
+  for (int u = 0; u < NS; ++u) sv[u] = rs[threadIdx.x + u * kGramRows];
+  const double dk = rs[min((int)threadIdx.x, RP - 1) * (RP + 1)];
 #pragma unroll
-  for (int u = 0; u < NS; ++u) Rt[threadIdx.x + u * kGramRows] = sv[u];
-  if (threadIdx.x < RP) rinv[threadIdx.x] = dk > 0.0 ? 1.0 / dk : 0.0;
+  for (int u = 0; u < NS; ++u) Rr[threadIdx.x + u * kGramRows] = sv[u];
+  if (threadIdx.x < RP) rinv[threadIdx.x] = ((int)threadIdx.x < r && dk > 0.0) ? 1.0 / dk : 0.0;
   __syncthreads();
   if (i >= o.rows) return;
-  double x[RP];
+  double b[RP];
 #pragma unroll
-  for (int k = 0; k < RP; ++k) x[k] = (double)pv[k];
+  for (int k = 0; k < RP; ++k) b[k] = (double)pv[k];
+  // row k + 1 of R is read while step k runs (software pipelining by hand)
+  double rc[RP], rn[RP];
+#pragma unroll
+  for (int q = 1; q < RP; ++q) rc[q] = Rr[q];
 #pragma unroll
   for (int k = 0; k < RP; ++k) {
-    if (k < r) {
-      double s0 = x[k], s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    if ((k & 3) == 0 && k >= r) break;
+    if (k + 1 < RP) {
 #pragma unroll
-      for (int jj = 0; jj < k; ++jj) {
-        const double t = -x[jj] * Rt[k * RP + jj];
-        if ((jj & 3) == 0) s0 += t;
-        else if ((jj & 3) == 1) s1 += t;
-        else if ((jj & 3) == 2) s2 += t;
-        else s3 += t;
-      }
-      x[k] = ((s0 + s1) + (s2 + s3)) * rinv[k];
-      p[k * ld] = (float)x[k];
+      for (int q = k + 2; q < RP; ++q) rn[q] = Rr[(k + 1) * RP + q];
     }
+    const double xk = b[k] * rinv[k];
+    b[k] = xk;
+#pragma unroll
+    for (int q = k + 1; q < RP; ++q) b[q] = fma(-xk, rc[q], b[q]);
+#pragma unroll
+    for (int q = k + 2; q < RP; ++q) rc[q] = rn[q];
   }
+#pragma unroll
+  for (int k = 0; k < RP; ++k)
+    if (k < r) p[k * ld] = (float)b[k];
 }
 
 // ---------------------------------------------------------------------------
