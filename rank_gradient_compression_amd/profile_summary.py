@@ -31,8 +31,8 @@ COPY_BYTES = 4 * (1 << 30)
 
 def source_file(kernel: str) -> str:
     """The source file that defines a library kernel (by its name)."""
-    k = kernel.replace("psgd::", "")
-    if k.startswith(("k_mfma", "k_psum", "k_gram", "k_apply")) or "k_mfma" in k or "k_gram" in k:
+    k = kernel.replace("psgd::", "").replace("void ", "").strip()
+    if k.startswith(("k_mfma", "k_psum", "k_gram", "k_apply")):
         return "kernels_mfma.hip"
     if "k_init_q" in k:
         return "kernels_rng.hip"
