@@ -22,8 +22,9 @@
 // markedly slower.
 //
 //   pass 1  P = M Q (with the EF-add and optional momentum): a workgroup
-//           walks its 64-row tile of one column split in 128-column chunks
-//           (M formed, stored back and staged in LDS with the chunk of Q);
+//           walks its 64-row tile of one column split in 128- or 64-column
+//           chunks (M formed, stored back and staged in LDS with the chunk
+//           of Q);
 //           split partials are summed in fixed order.  With a deferred
 //           residual each wavefront first forms its 16 rows of the previous
 //           step's reconstruction in LDS from the staged Q chunk.
@@ -164,24 +165,27 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 // in, so E is formed bit for bit as the residual pass would have stored it.
 // ---------------------------------------------------------------------------
 
-// P = M Q with the EF-add of MODE 1..4 (or M as is, MODE 0: the refresh),
+// P = M Q with the EF-add of MODE 1..6 (or M as is, MODE 0: the refresh),
 // staged: a workgroup owns the 64-row tile of its column split and walks the
-// split in kMqChunk-column chunks.  Each wavefront loads 16 rows of a chunk
-// with row-contiguous accesses (32 lanes x 16 bytes per row, two rows per
-// instruction) -- G, E and u as the mode needs --, forms M (and u) and stores
-// it back over E the same way, and writes M into an LDS tile; the chunk's Q
-// columns go to LDS once for the workgroup.  Each wavefront then accumulates
-// its own 16 rows (every rank tile) on the matrix core from LDS.  The next
-// chunk's loads are issued before the current chunk's matrix products.  The
-// summation index of matrix-core step v of a 16-column block is bound, for
-// lane (li, ls), to column 4 ls + v, so that the lane's A and B operands are
-// one 16-byte LDS read each per block; the blocks are taken in ascending
-// column order, the same sequence of matrix-core steps as the deferred-
-// residual form below, so P is the same bit for bit.
-constexpr int kMqChunk = 128;            // columns per LDS chunk
-constexpr int kMqLd = kMqChunk + 4;      // LDS row stride of the M chunk (floats)
+// split in CH-column chunks.  Each wavefront loads 16 rows of a chunk with
+// row-contiguous accesses (CH / 4 lanes x 16 bytes per row, 256 / CH rows
+// per instruction) -- G, E and u as the mode needs --, forms M (and u) and
+// stores it back over E the same way, and writes M into an LDS tile; the
+// chunk's Q columns go to LDS once for the workgroup.  Each wavefront then
+// accumulates its own 16 rows (every rank tile) on the matrix core from LDS.
+// The next chunk's loads are issued before the current chunk's matrix
+// products.  The summation index of matrix-core step v of a 16-column block
+// is bound, for lane (li, ls), to column 4 ls + v, so that the lane's A and B
+// operands are one 16-byte LDS read each per block; the blocks are taken in
+// ascending column order whatever the chunk width, so P does not depend on
+// it bit for bit.
+//
+// Columns per LDS chunk: 128 by default; 64 where the workgroups are
+// limited by LDS and registers (the plain M Q of the refresh, ranks above
+// 32), halving both so that more workgroups stay resident per compute unit.
+constexpr int mq_chunk(int rp, int mode) { return (mode == 0 || rp > 32) ? 64 : 128; }
 
-template <int RP, int MODE, bool VEC4, bool GBF16>
+template <int RP, int MODE, bool VEC4, bool GBF16, int CH>
 __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
                                              float* __restrict__ E, float* __restrict__ U, float beta,
                                              const float* __restrict__ Q, float* P, int64_t p_fixed,
@@ -192,10 +196,15 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   constexpr bool LOAD_E = MODE <= 2 || DEFERRED;
   constexpr bool MOM = MODE == 2 || MODE == 4 || MODE == 6;
   constexpr int KS = RP / 4;
-  constexpr int QLD = kMqChunk + 4;                         // LDS stride of one rank's Q chunk
-  constexpr int QPT = (RP * kMqChunk / 4 + 255) / 256;      // Q float4s a thread loads per chunk
-  float* Ms = smem;                                         // [64 rows][kMqLd]
-  float* Qs = smem + kMfmaRows * kMqLd;                     // [RP ranks][QLD]
+  static_assert(CH == 64 || CH == 128, "chunk width");
+  constexpr int LDM = CH + 4;    // LDS row stride of the M chunk (floats)
+  constexpr int LPR = CH / 4;    // lanes per row of a chunk
+  constexpr int RPI = 64 / LPR;  // rows per wavefront load
+  constexpr int NU = 16 / RPI;   // wavefront loads per chunk (16 rows)
+  constexpr int QLD = CH + 4;                         // LDS stride of one rank's Q chunk
+  constexpr int QPT = (RP * CH / 4 + 255) / 256;      // Q float4s a thread loads per chunk
+  float* Ms = smem;                                         // [64 rows][LDM]
+  float* Qs = smem + kMfmaRows * LDM;                     // [RP ranks][QLD]
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_rows0;
   const int rb = local / d.s1, split = local - rb * d.s1;
@@ -205,8 +214,9 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   const int li = lane & 15, ls = lane >> 4;
   const int i0 = rb * kMfmaRows;
   const float* q = Q + d.q_off;
-  // row accesses: lane (hr = lane / 32, lane % 32) covers columns 4 (lane % 32) .. + 3 of rows 2 u + hr
-  const int hr = lane >> 5, cl4 = 4 * (lane & 31);
+  // row accesses: lane (hr = lane / LPR, lane % LPR) covers columns
+  // 4 (lane % LPR) .. + 3 of rows RPI u + hr
+  const int hr = lane / LPR, cl4 = 4 * (lane % LPR);
 
   v4f acc[RP / 16];
 #pragma unroll
@@ -225,13 +235,13 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
     }
   }
 
-  float4 xg[8], xe[LOAD_E ? 8 : 1], xu[MOM ? 8 : 1], qn[QPT];
-  auto row_of = [&](int u) { return i0 + 16 * wave + 2 * u + hr; };
+  float4 xg[NU], xe[LOAD_E ? NU : 1], xu[MOM ? NU : 1], qn[QPT];
+  auto row_of = [&](int u) { return i0 + 16 * wave + RPI * u + hr; };
   auto load_chunk = [&](int c0) {
     const int col = c0 + cl4;
     const bool col_ok = col < c_end;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int row = row_of(u);
       const bool ok = row < m && col_ok;
       const int64_t ro = d.off + (int64_t)min(row, m - 1) * n;
@@ -247,9 +257,9 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
     }
 #pragma unroll
     for (int u = 0; u < QPT; ++u) {
-      const int e = threadIdx.x + 256 * u;  // float4 index within [RP][kMqChunk / 4]
-      const int t = e / (kMqChunk / 4), c = c0 + 4 * (e % (kMqChunk / 4));
-      qn[u] = (e < RP * kMqChunk / 4 && t < r) ? ldq<VEC4>(q + (int64_t)t * n, c, c < c_end, c_begin, n)
+      const int e = threadIdx.x + 256 * u;  // float4 index within [RP][CH / 4]
+      const int t = e / (CH / 4), c = c0 + 4 * (e % (CH / 4));
+      qn[u] = (e < RP * CH / 4 && t < r) ? ldq<VEC4>(q + (int64_t)t * n, c, c < c_end, c_begin, n)
                                                : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
@@ -257,22 +267,22 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
 #pragma unroll
     for (int u = 0; u < QPT; ++u) {
       const int e = threadIdx.x + 256 * u;
-      if (e < RP * kMqChunk / 4)
-        *reinterpret_cast<float4*>(&Qs[(e / (kMqChunk / 4)) * QLD + 4 * (e % (kMqChunk / 4))]) = qn[u];
+      if (e < RP * CH / 4)
+        *reinterpret_cast<float4*>(&Qs[(e / (CH / 4)) * QLD + 4 * (e % (CH / 4))]) = qn[u];
     }
   };
   // Deferred residual: the previous step's reconstruction of the wavefront's
-  // 16 rows x kMqChunk columns, M_hat^T = Q P_hat_old^T tile by tile (A = Q
+  // 16 rows x CH columns, M_hat^T = Q P_hat_old^T tile by tile (A = Q
   // from LDS, the same operands and rank order as the residual pass), into
   // the wavefront's own rows of Ms in the result layout (row li, columns
   // 4 ls .. 4 ls + 3).
   auto recon_tile = [&]() {
 #pragma unroll
-    for (int ct = 0; ct < kMqChunk / 16; ++ct) {
+    for (int ct = 0; ct < CH / 16; ++ct) {
       v4f a4 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) a4 = mfma16x16x4(Qs[(4 * kk + ls) * QLD + 16 * ct + li], bfr[kk], a4);
-      *reinterpret_cast<float4*>(&Ms[(16 * wave + li) * kMqLd + 16 * ct + 4 * ls]) =
+      *reinterpret_cast<float4*>(&Ms[(16 * wave + li) * LDM + 16 * ct + 4 * ls]) =
           make_float4(a4[0], a4[1], a4[2], a4[3]);
     }
   };
@@ -282,9 +292,9 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
     const int col = c0 + cl4;
     const bool col_ok = col < c_end;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int row = row_of(u);
-      float* mrow = &Ms[(16 * wave + 2 * u + hr) * kMqLd + cl4];
+      float* mrow = &Ms[(16 * wave + RPI * u + hr) * LDM + cl4];
       float4 s;
       if constexpr (MODE == 0) {
         s = xg[u];
@@ -315,7 +325,7 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   // A wavefront reads only its own rows of Ms, so the barrier per chunk
   // guards the shared Q chunk (and the overwrite of both tiles).
   load_chunk(c_begin);
-  for (int c0 = c_begin; c0 < c_end; c0 += kMqChunk) {
+  for (int c0 = c_begin; c0 < c_end; c0 += CH) {
     stage_q();
     if constexpr (DEFERRED) {
       __syncthreads();
@@ -325,10 +335,10 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
       ef_chunk(c0);
       __syncthreads();
     }
-    if (c0 + kMqChunk < c_end) load_chunk(c0 + kMqChunk);
+    if (c0 + CH < c_end) load_chunk(c0 + CH);
 #pragma unroll
-    for (int kb = 0; kb < kMqChunk / 16; ++kb) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&Ms[(16 * wave + li) * kMqLd + 16 * kb + 4 * ls]);
+    for (int kb = 0; kb < CH / 16; ++kb) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&Ms[(16 * wave + li) * LDM + 16 * kb + 4 * ls]);
       float4 b4[RP / 16];
 #pragma unroll
       for (int T = 0; T < RP / 16; ++T)
@@ -363,14 +373,15 @@ __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats
                                                 float* __restrict__ E, float* __restrict__ U, float beta,
                                                 const float* __restrict__ Q, float* P, int64_t p_fixed,
                                                 float* __restrict__ ppart, const float* Pold) {
-  __shared__ float smem[kMfmaRows * kMqLd + RP * (kMqChunk + 4)];
+  constexpr int CH = mq_chunk(RP, MODE);
+  __shared__ float smem[(kMfmaRows + RP) * (CH + 4)];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
   if (d.vec == 4)
-    mfma_mq_body<RP, MODE, true, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
+    mfma_mq_body<RP, MODE, true, GBF16, CH>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
   else
-    mfma_mq_body<RP, MODE, false, GBF16>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
+    mfma_mq_body<RP, MODE, false, GBF16, CH>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
 }
 
 // Fixed-order sum of the column-split partials of pass 1.
