@@ -28,7 +28,7 @@
 //           split partials are summed in fixed order.  With a deferred
 //           residual each wavefront first forms its 16 rows of the previous
 //           step's reconstruction in LDS from the staged Q chunk.
-//   pass 2  Q = M^T P_hat: a workgroup walks 256 columns of a row block in
+//   pass 2  Q = M^T P_hat: a workgroup walks 128 columns of a row block in
 //           32-row chunks staged in LDS with the chunk's P_hat rows.
 //   pass 3  M_hat = P_hat Q^T computed transposed (M_hat^T = Q P_hat^T) into
 //           an LDS tile of 32 rows x 256 columns, then streamed out with E.
@@ -409,12 +409,15 @@ __global__ __launch_bounds__(kRedCols) void k_psum(const MatDesc* __restrict__ m
 // Pass 2: Q = M^T P_hat over one row block (partials when the matrix has
 // several row blocks).
 //
-// A workgroup owns kMfmaCols columns of one row block and walks it in
+// A workgroup owns kMfmaCols (128) columns of one row block and walks it in
 // kQtChunk-row chunks.  Each wavefront loads kQtChunk / 4 rows of a chunk
-// with row-contiguous accesses (64 lanes x 16 bytes, one 1 KB row segment
-// per instruction) into an LDS tile, and the chunk's P_hat rows go to LDS
-// once for the workgroup; each wavefront then accumulates its 64 columns
-// (four 16-column tiles, every rank tile) on the matrix core from LDS.  The
+// with row-contiguous accesses (32 lanes x 16 bytes per row, two 512-byte
+// row segments per instruction) into an LDS tile, and the chunk's P_hat rows
+// go to LDS once for the workgroup; each wavefront then accumulates its 32
+// columns (two 16-column tiles, every rank tile) on the matrix core from LDS.
+// A 128-column tile rather than 256 doubles the workgroups of a row block and
+// halves their LDS and load registers (about 3% on the refresh and on single
+// large matrices).  The
 // next chunk's loads are issued before the current chunk's matrix products.
 // The summation index of matrix-core step v of a 16-row block is bound, for
 // lane (li, ls), to row 4 ls + v, so that lane's B operands P_hat[4 ls ..
@@ -425,13 +428,18 @@ __global__ __launch_bounds__(kRedCols) void k_psum(const MatDesc* __restrict__ m
 constexpr int kQtChunk = 32;              // rows per LDS chunk
 constexpr int kQtLd = kMfmaCols + 4;      // LDS row stride of the M chunk (floats)
 constexpr int kQtPld = kQtChunk + 4;      // LDS stride of one rank's P_hat rows (floats)
-static_assert(kMfmaCols == 256, "a wavefront row load covers the workgroup's columns");
+constexpr int kQtLpr = kMfmaCols / 4;      // lanes per row of a wavefront load
+constexpr int kQtRpi = 64 / kQtLpr;        // rows per wavefront load
+constexpr int kQtWc = kMfmaCols / 4;       // columns a wavefront owns
+constexpr int kQtNct = kQtWc / 16;         // its 16-column tiles
+static_assert(kMfmaCols == 128 || kMfmaCols == 256, "a wavefront load covers whole rows of the tile");
 
 template <int RP, bool VEC4>
 __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, const float* __restrict__ M,
                                              const float* __restrict__ Ph, int64_t ph_fixed, float* __restrict__ Q,
                                              float* __restrict__ part, float* Ms, float* Ps) {
   constexpr int RPW = kQtChunk / 4;                        // rows a wavefront loads per chunk
+  constexpr int NL = RPW / kQtRpi;                         // its load instructions per chunk
   constexpr int PPT = (RP * kQtChunk + 255) / 256;         // P_hat values a thread loads per chunk
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_mtp0;
@@ -441,22 +449,23 @@ __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, co
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
   const int cbase = cb * kMfmaCols;
-  const int scol = cbase + 4 * lane;  // the lane's four columns in the row loads
+  const int hr = lane / kQtLpr;                      // the lane's row within a load
+  const int scol = cbase + 4 * (lane % kQtLpr);  // the lane's four columns in the row loads
   const bool scol_ok = scol < n;
   const float* ph = Ph + (ph_fixed >= 0 ? ph_fixed : d.p_off);
 
-  v4f acc[4][RP / 16];
+  v4f acc[kQtNct][RP / 16];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < kQtNct; ++ct)
 #pragma unroll
     for (int T = 0; T < RP / 16; ++T) acc[ct][T] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  float4 xn[RPW];
+  float4 xn[NL];
   float pn[PPT];
   auto load_chunk = [&](int ib) {
 #pragma unroll
-    for (int u = 0; u < RPW; ++u) {
-      const int row = ib + RPW * wave + u;
+    for (int u = 0; u < NL; ++u) {
+      const int row = ib + RPW * wave + kQtRpi * u + hr;
       xn[u] = row < i1 ? ldq<VEC4>(M + d.off + (int64_t)row * n, scol, scol_ok, cbase, n)
                        : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -469,7 +478,8 @@ __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, co
   };
   auto store_chunk = [&]() {
 #pragma unroll
-    for (int u = 0; u < RPW; ++u) *reinterpret_cast<float4*>(&Ms[(RPW * wave + u) * kQtLd + 4 * lane]) = xn[u];
+    for (int u = 0; u < NL; ++u)
+      *reinterpret_cast<float4*>(&Ms[(RPW * wave + kQtRpi * u + hr) * kQtLd + 4 * (lane % kQtLpr)]) = xn[u];
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int e = threadIdx.x + 256 * u;
@@ -490,9 +500,9 @@ __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, co
         pb[T] = *reinterpret_cast<const float4*>(&Ps[(16 * T + li) * kQtPld + 16 * kb + 4 * ls]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float* mrow = &Ms[(16 * kb + 4 * ls + v) * kQtLd + 64 * wave + li];
+        const float* mrow = &Ms[(16 * kb + 4 * ls + v) * kQtLd + kQtWc * wave + li];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int ct = 0; ct < kQtNct; ++ct) {
           const float a = mrow[16 * ct];
 #pragma unroll
           for (int T = 0; T < RP / 16; ++T) {
@@ -505,7 +515,7 @@ __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, co
     __syncthreads();
   }
 
-  // acc[ct][T][e] of lane (li, ls) is Q[cbase + 64 wave + 16 ct + 4 ls + e][16 T + li].
+  // acc[ct][T][e] of lane (li, ls) is Q[cbase + kQtWc wave + 16 ct + 4 ls + e][16 T + li].
   float* out = d.nrb > 1 ? part + d.part_off + (int64_t)rb * r * n : Q + d.q_off;
   const bool out4 = (n & 3) == 0;
 #pragma unroll
@@ -513,8 +523,8 @@ __device__ __forceinline__ void mfma_qt_body(const MatDesc& d, int wg, int r, co
     const int t = 16 * T + li;
     if (t < r) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        st4(out + (int64_t)t * n, cbase + 64 * wave + 16 * ct + 4 * ls, n, out4,
+      for (int ct = 0; ct < kQtNct; ++ct)
+        st4(out + (int64_t)t * n, cbase + kQtWc * wave + 16 * ct + 4 * ls, n, out4,
             make_float4(acc[ct][T][0], acc[ct][T][1], acc[ct][T][2], acc[ct][T][3]));
     }
   }

@@ -34,7 +34,7 @@ constexpr int64_t kAlignElems = 64;
 // Tiles of the MFMA kernels (ranks above kValuMaxRank, padded to a multiple
 // of 16).
 constexpr int kMfmaRows = 64;      // rows of one MFMA pass-1 / pass-3 workgroup tile
-constexpr int kMfmaCols = 256;     // columns of one MFMA pass-2 workgroup tile
+constexpr int kMfmaCols = 128;     // columns of one MFMA pass-2 workgroup tile
 constexpr int kGramRows = 128;     // rows of one Gram-partial / apply workgroup
 
 // One compressed matrix.
