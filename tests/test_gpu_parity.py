@@ -142,6 +142,32 @@ def test_exact_recovery_low_rank():
     assert oracle.orthonormality_error(Ph) <= ORTH_TOL
 
 
+@pytest.mark.parametrize("m,n,k,r", [(1000, 700, 5, 20), (777, 1290, 16, 33), (1500, 600, 30, 50)])
+def test_rank_deficient_matrix_core(m, n, k, r):
+    # An exactly rank-k matrix at rank r > k on the matrix-core path (padded
+    # ranks 32 / 48 / 64, ragged row and column tails): columns k .. r-1 of
+    # P = M Q are dependent, so the Gram-Schmidt rule zeroes them exactly;
+    # the first k match the oracle's Gram-Schmidt of the same P, and M is
+    # recovered with E ~ 0.
+    g = np.random.default_rng(100 + r)
+    M = (g.standard_normal((m, k)) @ g.standard_normal((k, n))).astype(np.float32)
+    q0 = g.standard_normal((n, r)).astype(np.float32)
+    say(f"[rank-deficient] {m}x{n}, true rank {k}, r = {r}")
+    ps = PowerSGD([(m, n)], r, device=DEV)
+    ps.set_q(0, q0)
+    ps.view(ps.grads, 0).copy_(torch.from_numpy(M).to(DEV))
+    ps.compress(mhat=True)
+    torch.cuda.synchronize()
+    Ph = cpu(ps.p_hat(0))
+    assert not Ph[:, k:].any(), "dependent columns must be zero"
+    assert oracle.orthonormality_error(Ph[:, :k]) <= ORTH_TOL
+    Ph_ref = oracle.gram_schmidt(M.astype(np.float64) @ q0.astype(np.float64))
+    assert not Ph_ref[:, k:].any()
+    assert rel(Ph, Ph_ref) <= REL_TOL
+    assert rel(cpu(ps.view(ps.mhat, 0)), M) <= 1e-5
+    assert np.linalg.norm(cpu(ps.view(ps.err, 0))) <= 1e-5 * np.linalg.norm(M)
+
+
 def test_decompress_equals_fused_and_is_deterministic():
     wl = W.ModelSetWorkload(W.resnet18_cifar_set(), "resnet18", seed=2)
     shapes = [s for _, s in wl.tensors]
