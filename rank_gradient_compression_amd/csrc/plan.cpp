@@ -42,8 +42,10 @@ static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 static int32_t choose_rb_rows(const std::vector<MatDesc>& mats, int64_t rank, bool mfma) {
   const int64_t target_wgs = 2048;
   int32_t rb_min = 64;
-  // matrix cores: a workgroup is 256 columns wide, so a block needs more rows
-  // to keep the partials small (at most 1/8 of the pass from rank 16 on)
+  // matrix cores: a block of rb rows writes r partial values per column for
+  // the rb it reads, so blocks take at least 16 r rows, capped at 512: the
+  // partials stay within 1/16 of the pass's reads up to rank 32 and 1/8 at
+  // rank 64
   const int64_t want = mfma ? std::min<int64_t>(16 * rank, 512) : 8 * rank;
   while (rb_min < want) rb_min *= 2;
   int32_t rb = 2048;
