@@ -50,11 +50,6 @@ __device__ __forceinline__ v4f mfma16x16x4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Workgroup barrier for LDS hand-offs only: waits for this wavefront's LDS
-// accesses (lgkmcnt) but, unlike __syncthreads(), not for its outstanding
-// global loads, so loads issued before the barrier stay in flight across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Four consecutive floats of a row from column `col` (zero past the row end).
 __device__ __forceinline__ float4 ld4(const float* p, int col, int n, bool vec4) {
   if (vec4) return col < n ? *reinterpret_cast<const float4*>(p + col) : make_float4(0.f, 0.f, 0.f, 0.f);
