@@ -333,10 +333,17 @@ psgd_status_t psgd_init_q(psgd_plan_t plan, float* q, uint64_t seed, void* works
  * Per-stage timing with HIP events recorded on the call's stream.  While
  * enabled, every compress / decompress / refresh call records one event pair
  * per stage it runs (psgd_refresh records its products under EF_P, MTP and
- * QREDUCE and its orthonormalisations under GS).  psgd_timing_read waits for the recorded events, adds
- * the elapsed milliseconds per stage into ms[PSGD_NSTAGES] (and the number of
- * launches per stage into launches[], nullable), and clears the record.
+ * QREDUCE and its orthonormalisations under GS).  psgd_timing_read waits for
+ * the recorded events, adds the elapsed milliseconds per stage into
+ * ms[PSGD_NSTAGES] (and the number of launches per stage into launches[],
+ * nullable), clears the record and keeps its events for reuse.  Enabling
+ * creates PSGD_TIMING_EVENTS events up front (once per plan), so that the
+ * calls being timed do not create events themselves until that many are
+ * pending unread; beyond it, events are created as needed.  Errors:
+ * PSGD_ERR_INVALID_ARG (null plan), PSGD_ERR_HIP (event creation failed at
+ * enable; timing then stays off).
  */
+#define PSGD_TIMING_EVENTS 4096
 psgd_status_t psgd_timing_enable(psgd_plan_t plan, int32_t enable);
 psgd_status_t psgd_timing_read(psgd_plan_t plan, double* ms, int64_t* launches);
 

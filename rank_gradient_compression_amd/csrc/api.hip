@@ -28,6 +28,7 @@ struct TimingRecord {
 
 struct TimingState {
   bool enabled = false;
+  bool reserved = false;  // the up-front event pool has been created
   std::vector<TimingRecord> records;
   std::vector<hipEvent_t> pool;
 };
@@ -457,7 +458,23 @@ extern "C" psgd_status_t psgd_timing_enable(psgd_plan_t p, int32_t enable) {
   }
   std::lock_guard<std::mutex> lk(p->timing_mu);
   if (!p->timing) p->timing = new TimingState();
-  p->timing->enabled = enable != 0;
+  TimingState* t = p->timing;
+  if (enable && !t->reserved) {
+    // the pool up front: creating events inside the timed calls would put
+    // host work between their launches
+    t->pool.reserve(PSGD_TIMING_EVENTS);
+    while (t->pool.size() < (size_t)PSGD_TIMING_EVENTS) {
+      hipEvent_t e = nullptr;
+      const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
+      if (err != hipSuccess) {
+        t->enabled = false;
+        return hip_fail(err, "psgd_timing_enable");
+      }
+      t->pool.push_back(e);
+    }
+    t->reserved = true;
+  }
+  t->enabled = enable != 0;
   return PSGD_OK;
 }
 
