@@ -78,13 +78,13 @@ def test_deferred_residual_ranks(rank):
     _run(SHAPES, rank, 4, seed=150 + rank)
 
 
-@pytest.mark.parametrize("rank", [4, 32])
+@pytest.mark.parametrize("rank", [4, 32, 64])
 def test_deferred_residual_momentum_bf16_odd_offsets(rank):
     shapes = [(300, 512), (200, 650), (13,)]
     offsets = [1, 300 * 512 + 3, 300 * 512 + 3 + 200 * 650 + 2]
     _run(shapes, rank, 4, beta=0.9, grads_dtype=torch.bfloat16, seed=160 + rank, offsets=offsets)
 
 
-@pytest.mark.parametrize("rank", [4, 16])
+@pytest.mark.parametrize("rank", [4, 16, 48])
 def test_deferred_residual_with_fused_sgd(rank):
     _run([(300, 650), (400, 512), (11,)], rank, 3, seed=170 + rank, sgd=True)
