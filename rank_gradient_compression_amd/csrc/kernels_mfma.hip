@@ -196,10 +196,10 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   constexpr int LPR = CH / 4;    // lanes per row of a chunk
   constexpr int RPI = 64 / LPR;  // rows per wavefront load
   constexpr int NU = 16 / RPI;   // wavefront loads per chunk (16 rows)
-  constexpr int QLD = CH + 4;                         // LDS stride of one rank's Q chunk
-  constexpr int QPT = (RP * CH / 4 + 255) / 256;      // Q float4s a thread loads per chunk
-  float* Ms = smem;                                         // [64 rows][LDM]
-  float* Qs = smem + kMfmaRows * LDM;                     // [RP ranks][QLD]
+  constexpr int QLD = CH + 4;                     // LDS stride of one rank's Q chunk
+  constexpr int QPT = (RP * CH / 4 + 255) / 256;  // Q float4s a thread loads per chunk
+  float* Ms = smem;                               // [64 rows][LDM]
+  float* Qs = smem + kMfmaRows * LDM;             // [RP ranks][QLD]
   const int m = d.m, n = d.n;
   const int local = wg - d.wg_rows0;
   const int rb = local / d.s1, split = local - rb * d.s1;
