@@ -22,7 +22,7 @@ M_ROWS, N_COLS = 32768, 65600  # 2,149,580,800 elements
 CHUNK = 2048
 
 
-@pytest.mark.parametrize("rank", [4, 16])
+@pytest.mark.parametrize("rank", [4, 16, 64])
 def test_matrix_beyond_2_31_elements(rank):
     m, n = M_ROWS, N_COLS
     assert m * n > 2 ** 31
