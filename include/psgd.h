@@ -290,6 +290,33 @@ psgd_status_t psgd_compress(psgd_plan_t plan, const void* grads, float* err, flo
                             void* user, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * psgd_compress_noalloc -- psgd_compress without a workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same step, same kernels,
+ * same arguments and results as psgd_compress, but the scratch lives in a
+ * static device array of the library, PSGD_NOALLOC_SCRATCH_BYTES per GPU,
+ * which every GPU the library runs on holds until the process ends.  The
+ * call allocates and frees nothing: the first call on a device looks up that
+ * device's copy of the array; the plan's tables are uploaded into it (an
+ * asynchronous host-to-device copy on `stream`) when the previous call on the
+ * device used another plan or another stream.  The caller still owns grads,
+ * err, mom, q, p and mhat.
+ *
+ * Every call on one GPU shares that GPU's array and finds the previous
+ * call's contents there: calls that overlap on one GPU (concurrent streams
+ * or threads) race, and so do calls on two streams that the caller has not
+ * ordered.  Use psgd_compress with distinct workspaces for concurrent steps.
+ *
+ * Errors: as psgd_compress; PSGD_ERR_WORKSPACE when the plan needs more than
+ * PSGD_NOALLOC_SCRATCH_BYTES of scratch (info.workspace_bytes; checked
+ * before any device call); PSGD_ERR_HIP if the device's copy cannot be found.
+ */
+#define PSGD_NOALLOC_SCRATCH_BYTES (64ll << 20)
+psgd_status_t psgd_compress_noalloc(psgd_plan_t plan, const void* grads, float* err, float* mom, float* q, float* p,
+                                    float* mhat, const psgd_step_opts_t* opts, psgd_reduce_fn hook, void* user,
+                                    hipStream_t stream);
+
+/*
  * psgd_decompress -- reconstruct G ~ P_hat Q^T ([GLOSS], factorisation
  * paragraph) for every compressed tensor and copy the pass-through values
  * from the P buffer, into the flat buffer `out` (may alias the gradients).

@@ -24,6 +24,7 @@ PSGD_ERR_HOOK = 5
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP", 5: "HOOK"}
 
 PSGD_MAX_RANK = 64
+PSGD_NOALLOC_SCRATCH_BYTES = 64 << 20
 PSGD_KIND_VECTOR = 0
 PSGD_KIND_PASSTHRU = 1
 PSGD_KIND_COMPRESSED = 2
@@ -48,7 +49,7 @@ STAGE_NAMES = ["ef_p", "gs", "mtp", "qreduce", "residual", "passthru", "refresh"
 # Every symbol include/psgd.h declares.
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_destroy", "psgd_plan_get_info", "psgd_plan_tensor",
-    "psgd_workspace_init", "psgd_compress", "psgd_decompress", "psgd_refresh", "psgd_init_q",
+    "psgd_workspace_init", "psgd_compress", "psgd_compress_noalloc", "psgd_decompress", "psgd_refresh", "psgd_init_q",
     "psgd_timing_enable", "psgd_timing_read", "psgd_stream_probe", "psgd_stream_copy", "psgd_last_error",
     "psgd_version",
 ]
@@ -126,6 +127,8 @@ lib.psgd_plan_tensor.argtypes = [_vp, ctypes.c_int32, _i32p, _i64p, _i64p, _i64p
 lib.psgd_workspace_init.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_compress.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(psgd_step_opts_t), psgd_reduce_fn,
                               _vp, _vp, ctypes.c_size_t, _vp]
+lib.psgd_compress_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(psgd_step_opts_t),
+                                      psgd_reduce_fn, _vp, _vp]
 lib.psgd_decompress.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_refresh.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
 lib.psgd_init_q.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, ctypes.c_size_t, _vp]
@@ -136,6 +139,7 @@ lib.psgd_stream_probe.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, ctyp
 lib.psgd_last_error.restype = ctypes.c_char_p
 lib.psgd_version.restype = ctypes.c_char_p
 for _f in ["psgd_plan_create", "psgd_plan_get_info", "psgd_plan_tensor", "psgd_workspace_init", "psgd_compress",
+           "psgd_compress_noalloc",
            "psgd_decompress", "psgd_refresh", "psgd_init_q", "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy",
            "psgd_stream_probe"]:
     getattr(lib, _f).restype = ctypes.c_int
@@ -205,6 +209,14 @@ def psgd_compress(plan: int, grads: int, err: int, mom: int, q: int, p: int, mha
     o = ctypes.byref(opts) if opts is not None else None
     _check("psgd_compress", lib.psgd_compress(plan, grads, err or None, mom or None, q or None, p, mhat or None, o,
                                               h, None, workspace, workspace_bytes, stream))
+
+
+def psgd_compress_noalloc(plan: int, grads: int, err: int, mom: int, q: int, p: int, mhat: int,
+                          opts: Optional[psgd_step_opts_t], hook, stream: int = 0) -> None:
+    h = hook if hook is not None else psgd_reduce_fn()
+    o = ctypes.byref(opts) if opts is not None else None
+    _check("psgd_compress_noalloc", lib.psgd_compress_noalloc(plan, grads, err or None, mom or None, q or None, p,
+                                                              mhat or None, o, h, None, stream))
 
 
 def psgd_decompress(plan: int, p: int, q: int, out: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:

@@ -213,76 +213,86 @@ extern "C" psgd_status_t psgd_workspace_init(psgd_plan_t p, void* ws, size_t byt
   return PSGD_OK;
 }
 
-extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* err, float* mom, float* q, float* pbuf,
-                                       float* mhat, const psgd_step_opts_t* opts, psgd_reduce_fn hook, void* user,
-                                       void* ws, size_t ws_bytes, hipStream_t stream) {
-  clear_error();
+// Argument checks of psgd_compress and psgd_compress_noalloc (host only; no
+// device call).  On success *o holds the step options.
+static psgd_status_t validate_compress(const char* fn, const psgd_plan* p, const void* grads, const float* err,
+                                       const float* mom, const float* q, const float* pbuf, const float* mhat,
+                                       const psgd_step_opts_t* opts, psgd_step_opts_t* o) {
   if (!p) {
-    set_error("psgd_compress: plan is NULL");
+    set_error("%s: plan is NULL", fn);
     return PSGD_ERR_INVALID_ARG;
   }
   const bool momentum = (p->flags & PSGD_FLAG_MOMENTUM) != 0;
   const bool any = p->ntensors > 0;
   if (any && (!grads || !pbuf || (!p->mats.empty() && (!err || !q)))) {
-    set_error("psgd_compress: a required buffer is NULL");
+    set_error("%s: a required buffer is NULL", fn);
     return PSGD_ERR_INVALID_ARG;
   }
   if (momentum && any && !mom) {
-    set_error("psgd_compress: the plan compresses momentum but mom is NULL");
+    set_error("%s: the plan compresses momentum but mom is NULL", fn);
     return PSGD_ERR_INVALID_ARG;
   }
   if (!momentum && mom) {
-    set_error("psgd_compress: mom given but the plan has no momentum flag");
+    set_error("%s: mom given but the plan has no momentum flag", fn);
     return PSGD_ERR_INVALID_ARG;
   }
   if (!aligned16(grads) || !aligned16(err) || !aligned16(mom) || !aligned16(q) || !aligned16(pbuf) ||
       !aligned16(mhat)) {
-    set_error("psgd_compress: buffers must be 16-byte aligned");
+    set_error("%s: buffers must be 16-byte aligned", fn);
     return PSGD_ERR_INVALID_ARG;
   }
   if (mhat && (mhat == err || mhat == mom)) {
-    set_error("psgd_compress: mhat may alias grads only");
+    set_error("%s: mhat may alias grads only", fn);
     return PSGD_ERR_INVALID_ARG;
   }
   if (mhat && (p->flags & PSGD_FLAG_GRADS_BF16) && (const void*)mhat == grads) {
-    set_error("psgd_compress: mhat (fp32) cannot alias bfloat16 gradients");
+    set_error("%s: mhat (fp32) cannot alias bfloat16 gradients", fn);
     return PSGD_ERR_INVALID_ARG;
   }
-  psgd_step_opts_t o{};
-  if (opts) o = *opts;
-  if (o.power_iters < 0 || o.refresh_iters < 0) {
-    set_error("psgd_compress: negative iteration count");
+  *o = psgd_step_opts_t{};
+  if (opts) *o = *opts;
+  if (o->power_iters < 0 || o->refresh_iters < 0) {
+    set_error("%s: negative iteration count", fn);
     return PSGD_ERR_INVALID_ARG;
   }
   constexpr uint32_t kKnownStepFlags =
       PSGD_STEP_NO_ERROR_FEEDBACK | PSGD_STEP_NESTEROV | PSGD_STEP_DEFER_RESIDUAL | PSGD_STEP_RESIDUAL_DEFERRED |
       PSGD_STEP_PAYLOAD_BF16;
-  if (o.flags & ~kKnownStepFlags) {
-    set_error("psgd_compress: unknown step flag bits 0x%x", o.flags & ~kKnownStepFlags);
+  if (o->flags & ~kKnownStepFlags) {
+    set_error("%s: unknown step flag bits 0x%x", fn, o->flags & ~kKnownStepFlags);
     return PSGD_ERR_INVALID_ARG;
   }
+  if ((o->flags & (PSGD_STEP_DEFER_RESIDUAL | PSGD_STEP_RESIDUAL_DEFERRED)) &&
+      (o->flags & PSGD_STEP_NO_ERROR_FEEDBACK)) {
+    set_error("%s: a deferred residual needs error feedback", fn);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if ((o->params != nullptr) != (o->sgd_buf != nullptr) || !aligned16(o->params) || !aligned16(o->sgd_buf)) {
+    set_error("%s: params and sgd_buf must be given together, 16-byte aligned", fn);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (o->params && (o->params == err || o->params == mom || o->params == mhat || o->sgd_buf == err ||
+                    o->sgd_buf == mom || o->sgd_buf == mhat || o->params == o->sgd_buf)) {
+    set_error("%s: params / sgd_buf must not alias the other buffers", fn);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  return PSGD_OK;
+}
+
+// The step itself, on validated arguments and an initialised workspace `ws`
+// (the caller's, or the library's static scratch).
+static psgd_status_t run_compress(psgd_plan* p, const void* grads, float* err, float* mom, float* q, float* pbuf,
+                                  float* mhat, const psgd_step_opts_t& o, psgd_reduce_fn hook, void* user, void* ws,
+                                  hipStream_t stream) {
+  const bool momentum = (p->flags & PSGD_FLAG_MOMENTUM) != 0;
   const bool defer_out = (o.flags & PSGD_STEP_DEFER_RESIDUAL) != 0;
   const bool defer_in = (o.flags & PSGD_STEP_RESIDUAL_DEFERRED) != 0;
-  if ((defer_out || defer_in) && (o.flags & PSGD_STEP_NO_ERROR_FEEDBACK)) {
-    set_error("psgd_compress: a deferred residual needs error feedback");
-    return PSGD_ERR_INVALID_ARG;
-  }
-  if ((o.params != nullptr) != (o.sgd_buf != nullptr) || !aligned16(o.params) || !aligned16(o.sgd_buf)) {
-    set_error("psgd_compress: params and sgd_buf must be given together, 16-byte aligned");
-    return PSGD_ERR_INVALID_ARG;
-  }
-  if (o.params && (o.params == err || o.params == mom || o.params == mhat || o.sgd_buf == err ||
-                   o.sgd_buf == mom || o.sgd_buf == mhat || o.params == o.sgd_buf)) {
-    set_error("psgd_compress: params / sgd_buf must not alias the other buffers");
-    return PSGD_ERR_INVALID_ARG;
-  }
   const int refresh_iters = o.refresh_iters;
   const int power_iters = o.power_iters > 1 ? o.power_iters : 1;
   const bool ef = (o.flags & PSGD_STEP_NO_ERROR_FEEDBACK) == 0;
   const bool payload_bf16 = (o.flags & PSGD_STEP_PAYLOAD_BF16) != 0;
   const SgdArgs sg{o.params, o.sgd_buf, o.sgd_lr, o.sgd_momentum, (o.flags & PSGD_STEP_NESTEROV) ? 1 : 0};
-  if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_compress")) return s;
-  if (!any) return PSGD_OK;
+  if (p->ntensors == 0) return PSGD_OK;
 
   LaunchCtx c = make_ctx(p, ws, stream);
   c.p_prev = pbuf;
@@ -355,6 +365,92 @@ extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* 
   if (unpack && c.mfma)
     PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat, sg), "pass-through unpack");
   return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_compress(psgd_plan_t p, const void* grads, float* err, float* mom, float* q, float* pbuf,
+                                       float* mhat, const psgd_step_opts_t* opts, psgd_reduce_fn hook, void* user,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  psgd_step_opts_t o;
+  if (psgd_status_t s = validate_compress("psgd_compress", p, grads, err, mom, q, pbuf, mhat, opts, &o)) return s;
+  if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_compress")) return s;
+  return run_compress(p, grads, err, mom, q, pbuf, mhat, o, hook, user, ws, stream);
+}
+
+// ------------------------------------------------- allocation-free compress
+//
+// psgd_compress_noalloc runs the same step with the library's own device
+// scratch in place of a caller workspace: one static array per GPU, made when
+// the library's code object is loaded on that GPU and kept until the process
+// ends.  Its device address is looked up once per device with
+// hipGetSymbolAddress; in host code the array's name is only a host-side
+// stand-in and is never passed to a kernel or a copy.
+
+static __device__ __align__(256) unsigned char scratch[PSGD_NOALLOC_SCRATCH_BYTES];
+
+namespace psgd {
+
+constexpr int kNoallocMaxDevices = 64;
+
+struct NoallocDevice {
+  bool ready = false;            // `ptr` looked up on this device
+  void* ptr = nullptr;           // device address of `scratch` on this device
+  uint64_t plan_id = 0;          // plan whose tables the scratch holds (0: none)
+  hipStream_t stream = nullptr;  // stream those tables were uploaded on
+};
+
+static std::mutex g_noalloc_mu;
+static NoallocDevice g_noalloc[kNoallocMaxDevices];
+
+}  // namespace psgd
+
+extern "C" psgd_status_t psgd_compress_noalloc(psgd_plan_t p, const void* grads, float* err, float* mom, float* q,
+                                               float* pbuf, float* mhat, const psgd_step_opts_t* opts,
+                                               psgd_reduce_fn hook, void* user, hipStream_t stream) {
+  clear_error();
+  psgd_step_opts_t o;
+  if (psgd_status_t s = validate_compress("psgd_compress_noalloc", p, grads, err, mom, q, pbuf, mhat, opts, &o))
+    return s;
+  if ((uint64_t)p->hdr.total_bytes > (uint64_t)PSGD_NOALLOC_SCRATCH_BYTES) {
+    set_error("psgd_compress_noalloc: the plan needs %lld bytes of scratch, more than the library's static %lld "
+              "(use psgd_compress with a workspace)",
+              (long long)p->hdr.total_bytes, (long long)PSGD_NOALLOC_SCRATCH_BYTES);
+    return PSGD_ERR_WORKSPACE;
+  }
+  if (p->ntensors == 0) return PSGD_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "psgd_compress_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kNoallocMaxDevices) {
+    set_error("psgd_compress_noalloc: device %d beyond the %d devices supported", dev, kNoallocMaxDevices);
+    return PSGD_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    NoallocDevice& st = g_noalloc[dev];
+    if (!st.ready) {
+      // first call on this device (which is current): the device's own copy
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "psgd_compress_noalloc: hipGetSymbolAddress(scratch)");
+      st.ptr = ptr;
+      st.ready = true;
+    }
+    ws = st.ptr;
+    // The scratch keeps the last call's contents: the plan's tables are
+    // uploaded again whenever another plan (or another stream) used it last.
+    if (st.plan_id != p->id || st.stream != stream) {
+      st.plan_id = 0;
+      if (!p->tables.empty()) {
+        e = hipMemcpyAsync(ws, p->tables.data(), p->tables.size(), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "psgd_compress_noalloc: table upload");
+      }
+      st.plan_id = p->id;
+      st.stream = stream;
+    }
+  }
+  return run_compress(p, grads, err, mom, q, pbuf, mhat, o, hook, user, ws, stream);
 }
 
 extern "C" psgd_status_t psgd_decompress(psgd_plan_t p, const float* pbuf, const float* q, float* out, void* ws,

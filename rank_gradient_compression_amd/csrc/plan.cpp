@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <new>
 #include <numeric>
 
@@ -31,6 +32,8 @@ void set_error(const char* fmt, ...) {
 }
 
 void clear_error() { g_err[0] = 0; }
+
+static std::atomic<uint64_t> g_next_plan_id{1};
 
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -106,6 +109,7 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     set_error("psgd_plan_create: out of host memory");
     return PSGD_ERR_INVALID_ARG;
   }
+  p->id = g_next_plan_id.fetch_add(1);
   p->ntensors = ntensors;
   p->rank = rank;
   p->flags = flags;

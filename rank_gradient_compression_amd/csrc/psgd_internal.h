@@ -21,6 +21,7 @@ void clear_error();
 }  // namespace psgd
 
 struct psgd_plan {
+  uint64_t id = 0;  // unique per plan created in this process (never 0)
   int32_t ntensors = 0;
   int32_t rank = 0;
   uint32_t flags = 0;

@@ -106,7 +106,9 @@ class PowerSGD:
                  refresh_iters: int = 0, power_iters: int = 0, error_feedback: bool = True,
                  params: Optional[torch.Tensor] = None, sgd_buf: Optional[torch.Tensor] = None, sgd_lr: float = 0.0,
                  sgd_momentum: float = 0.0, nesterov: bool = False, defer_residual: bool = False,
-                 residual_deferred: bool = False, payload_bf16: bool = False) -> None:
+                 residual_deferred: bool = False, payload_bf16: bool = False, noalloc: bool = False) -> None:
+        """One psgd_compress call on the owned buffers; noalloc=True takes
+        psgd_compress_noalloc (the library's static scratch, no workspace)."""
         out = mhat_buf if mhat_buf is not None else (self.mhat if mhat else None)
         opts = None
         flags = (0 if error_feedback else B.PSGD_STEP_NO_ERROR_FEEDBACK) | (B.PSGD_STEP_NESTEROV if nesterov else 0)
@@ -116,6 +118,12 @@ class PowerSGD:
         if refresh_iters or power_iters or flags or params is not None:
             opts = B.step_opts(power_iters, refresh_iters, flags, sgd_lr, sgd_momentum, params.data_ptr() if params is not None else 0,
                                sgd_buf.data_ptr() if sgd_buf is not None else 0)
+        if noalloc:
+            B.psgd_compress_noalloc(self.plan, self.grads.data_ptr(), self.err.data_ptr(),
+                                    self.mom.data_ptr() if self.mom is not None else 0, self.q.data_ptr(),
+                                    self.p.data_ptr(), out.data_ptr() if out is not None else 0, opts, hook,
+                                    self._stream())
+            return
         B.psgd_compress(self.plan, self.grads.data_ptr(), self.err.data_ptr(),
                         self.mom.data_ptr() if self.mom is not None else 0, self.q.data_ptr(), self.p.data_ptr(),
                         out.data_ptr() if out is not None else 0, opts, hook, self.workspace.data_ptr(),

@@ -317,3 +317,29 @@ def test_c_client_is_built_against_the_library():
     out = subprocess.run(["ldd", exe], capture_output=True, text=True).stdout
     assert "libpsgd.so" in out and "libamdhip64" in out
     assert "torch" not in out and "python" not in out
+
+
+def test_compress_noalloc_rejects_before_any_device_call():
+    """psgd_compress_noalloc validates like psgd_compress and rejects a plan
+    whose scratch exceeds the static array, all before touching a device."""
+    rows, cols = views(W.llama7b_set())
+    p = R.psgd_plan_create(rows, cols, 4)
+    try:
+        assert R.psgd_plan_get_info(p)["workspace_bytes"] > B.PSGD_NOALLOC_SCRATCH_BYTES
+        with pytest.raises(B.PsgdError) as e:
+            R.psgd_compress_noalloc(p, FAKE, FAKE, 0, FAKE, FAKE, 0, None, None, 0)
+        assert e.value.status == B.PSGD_ERR_WORKSPACE and "static" in str(e.value)
+    finally:
+        R.psgd_plan_destroy(p)
+    p = R.psgd_plan_create([64, 9], [48, 1], 2)
+    try:
+        assert R.psgd_plan_get_info(p)["workspace_bytes"] <= B.PSGD_NOALLOC_SCRATCH_BYTES
+        for kw in (dict(grads=0), dict(q=FAKE + 4), dict(mom=FAKE)):
+            a = dict(grads=FAKE, err=FAKE, mom=0, q=FAKE, pbuf=FAKE)
+            a.update(kw)
+            with pytest.raises(B.PsgdError) as e:
+                R.psgd_compress_noalloc(p, a["grads"], a["err"], a["mom"], a["q"], a["pbuf"], 0, None, None, 0)
+            assert e.value.status == B.PSGD_ERR_INVALID_ARG
+            assert "psgd_compress_noalloc" in str(e.value)
+    finally:
+        R.psgd_plan_destroy(p)
