@@ -53,7 +53,7 @@ design notes of the repository):
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 from typing import Callable, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -278,6 +278,7 @@ class SetResult:
     Q: List[Optional[np.ndarray]]
     M_hat: List[np.ndarray]             # reconstructed tensors (pass-through: the value sent)
     M: List[Optional[np.ndarray]]       # compressor inputs X + E of compressed tensors
+    P: List[Optional[np.ndarray]] = field(default_factory=list)  # P = M Q before orthogonalisation
 
 
 def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: float = 0.0,
@@ -293,6 +294,7 @@ def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: flo
     Qs: List[Optional[np.ndarray]] = []
     Mh: List[np.ndarray] = []
     Ms: List[Optional[np.ndarray]] = []
+    Pr: List[Optional[np.ndarray]] = []
     for i, kind in enumerate(plan.kinds):
         G = np.asarray(grads[i], dtype=np.float64).reshape(plan.views[i] if kind != KIND_VECTOR else -1)
         if state.u is not None:
@@ -305,6 +307,7 @@ def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: flo
             Qs.append(None)
             Mh.append(X.copy())
             Ms.append(None)
+            Pr.append(None)
             continue
         M = X + state.E[i] if error_feedback else X.copy()
         Qw = state.Q[i]
@@ -317,7 +320,8 @@ def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: flo
         Qs.append(res.Q)
         Mh.append(res.M_hat)
         Ms.append(M)
-    return SetResult(P_hat=Ph, Q=Qs, M_hat=Mh, M=Ms)
+        Pr.append(res.P)
+    return SetResult(P_hat=Ph, Q=Qs, M_hat=Mh, M=Ms, P=Pr)
 
 
 # --------------------------------------------------------------------------
@@ -326,16 +330,19 @@ def step_set(plan: Plan, grads: Sequence[np.ndarray], state: SetState, beta: flo
 # --------------------------------------------------------------------------
 
 
-def compress_workers(Ms: Sequence[np.ndarray], Q_warm: np.ndarray) -> Tuple[np.ndarray, np.ndarray, List[np.ndarray]]:
+def compress_workers(Ms: Sequence[np.ndarray], Q_warm: np.ndarray,
+                     power_iters: int = 1) -> Tuple[np.ndarray, np.ndarray, List[np.ndarray]]:
     """Each worker forms P_i = M_i Q; the all-reduce gives mean P; every worker
     orthogonalises the same mean into P_hat, forms Q_i = M_i^T P_hat; the
-    all-reduce gives mean Q.  Residuals use the aggregated reconstruction
-    (reading R4).  Returns (P_hat, Q, [E_i])."""
-    Qw = np.asarray(Q_warm, np.float64)
+    all-reduce gives mean Q.  power_iters > 1 repeats this from the mean Q
+    (reading R8).  Residuals use the aggregated reconstruction (reading R4).
+    Returns (P_hat, Q, [E_i])."""
+    Q = np.asarray(Q_warm, np.float64)
     Ms = [np.asarray(M, np.float64) for M in Ms]
-    P = sum(M @ Qw for M in Ms) / len(Ms)
-    P_hat = gram_schmidt(P)
-    Q = sum(M.T @ P_hat for M in Ms) / len(Ms)
+    for _ in range(max(1, power_iters)):
+        P = sum(M @ Q for M in Ms) / len(Ms)
+        P_hat = gram_schmidt(P)
+        Q = sum(M.T @ P_hat for M in Ms) / len(Ms)
     M_hat = P_hat @ Q.T
     return P_hat, Q, [M - M_hat for M in Ms]
 

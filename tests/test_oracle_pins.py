@@ -201,12 +201,13 @@ def test_linearity_of_p_and_q_stages():
     assert np.abs(Qs(a * M1 + b * M2) - (a * Qs(M1) + b * Qs(M2))).max() <= 1e-13
 
 
-def test_mean_hook_over_workers_equals_compressing_the_mean():
+@pytest.mark.parametrize("power_iters", [1, 3])
+def test_mean_hook_over_workers_equals_compressing_the_mean(power_iters):
     g = np.random.default_rng(13)
     Ms = [rand(g, 80, 60) for _ in range(4)]
     Q = rand(g, 60, 2)
-    Ph, Qn, Es = oracle.compress_workers(Ms, Q)
-    ref = oracle.compress_matrix(sum(Ms) / 4, Q)
+    Ph, Qn, Es = oracle.compress_workers(Ms, Q, power_iters=power_iters)
+    ref = oracle.compress_matrix(sum(Ms) / 4, Q, power_iters=power_iters)
     assert np.abs(Ph - ref.P_hat).max() <= 1e-13
     assert np.abs(Qn - ref.Q).max() <= 1e-13
     # each worker keeps its own residual against the shared reconstruction
@@ -228,6 +229,21 @@ def test_mean_hooks_in_step_set_match_workers():
     assert np.abs(r.P_hat - Ph2).max() <= 1e-13
     assert np.abs(r.Q - Q2).max() <= 1e-13
     assert np.abs(r.E - Es[0]).max() <= 1e-13
+
+
+def test_worker_power_iterations_with_one_worker_are_the_step():
+    """One worker: the mean is the identity, so compress_workers with k
+    iterations is compress_matrix with k iterations, and k = 2 is two single
+    iterations chained (the second starting from the first's Q)."""
+    g = np.random.default_rng(15)
+    M, Q = rand(g, 50, 40), rand(g, 40, 3)
+    Ph, Qn, Es = oracle.compress_workers([M], Q, power_iters=2)
+    ref = oracle.compress_matrix(M, Q, power_iters=2)
+    assert np.array_equal(Ph, ref.P_hat) and np.array_equal(Qn, ref.Q)
+    first = oracle.compress_matrix(M, Q)
+    second = oracle.compress_matrix(M, first.Q)
+    assert np.abs(Ph - second.P_hat).max() <= 1e-13
+    assert np.abs(Es[0] - second.E).max() <= 1e-13
 
 
 # ----------------------------------------------------------- error feedback
@@ -679,3 +695,67 @@ def test_quantised_payload_rounds_both_factors_before_the_hooks():
     # bfloat16 keeps about 3 significant digits: close to, but not equal to, fp64
     d = np.linalg.norm(res.M_hat - plain.M_hat) / np.linalg.norm(plain.M_hat)
     assert 1e-5 < d < 2e-2
+
+
+# ---------------------------------------------------------------- decompression
+#
+# The receiver rebuilds the gradient from the two transmitted factors as their
+# product P_hat Q^T (glossary entry "PowerSGD", factorisation paragraph).
+
+def _scalar_decompress(Ph, Q):
+    m, r, n = len(Ph), len(Ph[0]), len(Q)
+    return [[sum(Ph[i][k] * Q[j][k] for k in range(r)) for j in range(n)] for i in range(m)]
+
+
+@pytest.mark.parametrize("m,n,r", [(1, 1, 1), (2, 5, 1), (6, 4, 3), (5, 6, 2), (4, 4, 4)])
+def test_decompress_brute_force(m, n, r):
+    g = np.random.default_rng(300 + 10 * m + n + r)
+    Ph, Q = rand(g, m, r), rand(g, n, r)
+    want = np.array(_scalar_decompress(Ph.tolist(), Q.tolist()))
+    got = oracle.decompress(Ph, Q)
+    assert got.shape == (m, n)
+    assert np.abs(got - want).max() <= 1e-14
+
+
+@pytest.mark.parametrize("m,n,k,r", [(60, 40, 1, 1), (60, 40, 2, 5), (128, 64, 3, 4), (33, 27, 4, 4)])
+def test_decompress_exact_recovery_from_any_basis_of_the_column_space(m, n, k, r):
+    """M = A B^T of rank k <= r, P_hat any orthonormal m x r basis whose span
+    holds the columns of A, Q = M^T P_hat: the product is P_hat P_hat^T M = M
+    (a projection onto a space that holds M's columns)."""
+    g = np.random.default_rng(310 + k + r)
+    A, Bm = rand(g, m, k), rand(g, n, k)
+    M = A @ Bm.T
+    # the first k columns span A; the rest are random directions
+    Ph = qr_positive(np.hstack([A, rand(g, m, r - k)]))
+    Q = M.T @ Ph
+    assert np.linalg.norm(oracle.decompress(Ph, Q) - M) <= 1e-12 * np.linalg.norm(M)
+
+
+def test_decompress_equals_step_reconstruction_and_residual():
+    """decompress(P_hat, Q) of a step's outputs is the step's M_hat, and
+    M - decompress = E (error feedback keeps exactly what was not sent)."""
+    g = np.random.default_rng(320)
+    M, Q0 = rand(g, 90, 70), rand(g, 70, 3)
+    res = oracle.compress_matrix(M, Q0)
+    D = oracle.decompress(res.P_hat, res.Q)
+    assert np.array_equal(D, res.M_hat)
+    assert np.abs(M - D - res.E).max() <= 4 * np.spacing(np.abs(M).max())
+
+
+def test_decompress_planted_mistakes_are_caught():
+    """Plausible wrong forms of the product each fail a pin above."""
+    g = np.random.default_rng(330)
+    m, n, r = 6, 5, 2
+    Ph, Q = rand(g, m, r), rand(g, n, r)
+    want = np.array(_scalar_decompress(Ph.tolist(), Q.tolist()))
+    wrong = [
+        lambda P, Qf: P[:, :1] @ Qf[:, :1].T,           # drops the last rank term
+        lambda P, Qf: -(P @ Qf.T),                       # flipped sign
+        lambda P, Qf: P @ np.flip(Qf, axis=1).T,         # columns paired wrongly
+        lambda P, Qf: (P @ Qf.T)[::-1],                  # rows permuted
+    ]
+    for f in wrong:
+        assert np.abs(f(Ph, Q) - want).max() > 1e-3
+    # a transposed operand does not even give an m x n matrix
+    with pytest.raises(ValueError):
+        np.asarray(Ph.T @ Q)
