@@ -150,6 +150,16 @@ typedef struct psgd_plan* psgd_plan_t;
  *                  PSGD_STEP_NESTEROV: x <- x - sgd_lr * (D + sgd_momentum * m)),
  *                  on the flat parameter buffer `params` and the flat buffer `sgd_buf`
  *                  (both in/out, plan layout, required together).
+ *   zero_cols      nullable, 4-byte aligned: ncompressed int32 in device
+ *                  memory or in pinned host memory (hipHostMalloc), written
+ *                  by the device.  Once the call has completed on the stream,
+ *                  entry k holds how many columns of compressed matrix k's
+ *                  P_hat (plan order) the Gram-Schmidt dependence rule set to
+ *                  zero in this call (the last iteration's, with power_iters
+ *                  > 1).  A warm start keeps such a column zero on later steps
+ *                  (its Q column is M^T 0), so a non-zero count reports a drop
+ *                  of the transmitted rank ([N152] Method: Gram-Schmidt of the
+ *                  P factor; Concepts, "Warm-start subspace iteration").
  */
 typedef struct psgd_step_opts {
   int32_t power_iters;
@@ -159,6 +169,7 @@ typedef struct psgd_step_opts {
   float sgd_momentum;
   float* params;
   float* sgd_buf;
+  int32_t* zero_cols;
 } psgd_step_opts_t;
 
 /* Sizes derived from a plan.  Element counts are fp32 elements. */
@@ -275,7 +286,9 @@ typedef int (*psgd_reduce_fn)(float* buf, size_t count, hipStream_t stream, void
  *          PowerSGD+ refresh, the no-error-feedback ablation, fused
  *          post-compression momentum SGD.
  *   hook   nullable aggregation hook, called on (p, p_buffer_elems) after P is
- *          formed and on (q, q_elems) after Q is formed.
+ *          formed and on (q, q_elems) after Q is formed.  With power_iters
+ *          > 1 the later iterations call it on (p, p_elems): the pass-through
+ *          values are aggregated once, with the first P.
  *   workspace, workspace_bytes   initialised workspace (psgd_workspace_init).
  *
  * Errors: PSGD_ERR_INVALID_ARG for null or not 16-byte aligned buffers, a

@@ -77,13 +77,14 @@ class psgd_step_opts_t(ctypes.Structure):
     _fields_ = [
         ("power_iters", ctypes.c_int32), ("refresh_iters", ctypes.c_int32), ("flags", ctypes.c_uint32),
         ("sgd_lr", ctypes.c_float), ("sgd_momentum", ctypes.c_float), ("params", ctypes.c_void_p),
-        ("sgd_buf", ctypes.c_void_p),
+        ("sgd_buf", ctypes.c_void_p), ("zero_cols", ctypes.c_void_p),
     ]
 
 
 def step_opts(power_iters: int = 0, refresh_iters: int = 0, flags: int = 0, sgd_lr: float = 0.0,
-              sgd_momentum: float = 0.0, params: int = 0, sgd_buf: int = 0) -> psgd_step_opts_t:
-    return psgd_step_opts_t(power_iters, refresh_iters, flags, sgd_lr, sgd_momentum, params or None, sgd_buf or None)
+              sgd_momentum: float = 0.0, params: int = 0, sgd_buf: int = 0, zero_cols: int = 0) -> psgd_step_opts_t:
+    return psgd_step_opts_t(power_iters, refresh_iters, flags, sgd_lr, sgd_momentum, params or None, sgd_buf or None,
+                            zero_cols or None)
 
 
 psgd_reduce_fn = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p)

@@ -84,9 +84,11 @@ static LaunchCtx make_ctx(const psgd_plan* p, void* ws, hipStream_t s) {
   c.rank_pad = h.rank_pad;
   c.mfma = h.mfma != 0;
   c.g_bf16 = (p->flags & PSGD_FLAG_GRADS_BF16) != 0;
+  c.stream_hint = (int64_t)p->dense * 4 > kStreamHintBytes;
   c.nmat = h.nmat;
   c.npass = h.npass;
   c.wg_rows = h.wg_rows;
+  c.wg_rows_v4 = h.wg_rows_v4;
   c.wg_rec = h.wg_rec;
   c.wg_mtp = h.wg_mtp;
   c.wg_red = h.wg_red;
@@ -106,7 +108,7 @@ static LaunchCtx make_ctx(const psgd_plan* p, void* ws, hipStream_t s) {
   c.gram_map = reinterpret_cast<const int32_t*>(b + h.gram_map_off);
   c.gramq_map = reinterpret_cast<const int32_t*>(b + h.gramq_map_off);
   c.part = reinterpret_cast<float*>(b + h.part_base);
-  c.ppart = reinterpret_cast<float*>(b + h.ppart_base);
+  c.ppart = b + h.ppart_base;
   c.gram = reinterpret_cast<double*>(b + h.gram_base);
   c.rscr = reinterpret_cast<float*>(b + h.refresh_base);
   return c;
@@ -133,8 +135,8 @@ static hipError_t stage_mq(const psgd_plan* p, const LaunchCtx& c, const GridRan
 
 // Orthonormalise the P factors of all matrices (P in `base` at the plan's
 // offsets).
-static hipError_t stage_orth_all_p(const LaunchCtx& c, float* base) {
-  return launch_gram_orth(c, 0, c.nmat, c.gram_map, c.wg_gram, base);
+static hipError_t stage_orth_all_p(const LaunchCtx& c, float* base, int32_t* zcount = nullptr) {
+  return launch_gram_orth(c, 0, c.nmat, c.gram_map, c.wg_gram, base, zcount);
 }
 
 // Orthonormalise the Q factors of all matrices (the refresh).
@@ -271,6 +273,10 @@ static psgd_status_t validate_compress(const char* fn, const psgd_plan* p, const
     set_error("%s: params and sgd_buf must be given together, 16-byte aligned", fn);
     return PSGD_ERR_INVALID_ARG;
   }
+  if (((uintptr_t)o->zero_cols & 3u) != 0) {
+    set_error("%s: zero_cols must be 4-byte aligned", fn);
+    return PSGD_ERR_INVALID_ARG;
+  }
   if (o->params && (o->params == err || o->params == mom || o->params == mhat || o->sgd_buf == err ||
                     o->sgd_buf == mom || o->sgd_buf == mhat || o->params == o->sgd_buf)) {
     set_error("%s: params / sgd_buf must not alias the other buffers", fn);
@@ -334,11 +340,14 @@ static psgd_status_t run_compress(psgd_plan* p, const void* grads, float* err, f
                   "P = M Q");
     if (payload_bf16)  // the factors only; pass-through values stay fp32
       PSGD_LAUNCH(PSGD_STAGE_EF_P, launch_round_bf16(pbuf, (int64_t)p->p_elems, stream), "round P to bfloat16");
-    if (hook && hook(pbuf, p->p_elems + p->pt_elems, stream, user) != 0) {
+    // The pass-through values ride with the first P only: later iterations
+    // aggregate the factors alone, so those values are averaged exactly once.
+    const size_t p_count = it == 0 ? p->p_elems + p->pt_elems : p->p_elems;
+    if (hook && p_count > 0 && hook(pbuf, p_count, stream, user) != 0) {
       set_error("psgd_compress: aggregation hook failed on P");
       return PSGD_ERR_HOOK;
     }
-    PSGD_LAUNCH(PSGD_STAGE_GS, stage_orth_all_p(c, pbuf), "orthogonalise P");
+    PSGD_LAUNCH(PSGD_STAGE_GS, stage_orth_all_p(c, pbuf, o.zero_cols), "orthogonalise P");
     {
       StageTimer _t(p, PSGD_STAGE_MTP, stream);
       const hipError_t e =
@@ -501,7 +510,7 @@ extern "C" psgd_status_t psgd_refresh(psgd_plan_t p, int32_t tensor, const float
   const size_t k = (size_t)(std::find(p->mat_tensor.begin(), p->mat_tensor.end(), tensor) - p->mat_tensor.begin());
   const LaunchCtx c = make_ctx(p, ws, stream);
   const MatDesc& d = p->mats[k];
-  const GridRange rows = mat_range(p, k, &MatDesc::wg_rows0, c.wg_rows);
+  const GridRange rows{d.wg_rows0, p->nrow_wg[k]};
   const GridRange mtp = mat_range(p, k, &MatDesc::wg_mtp0, c.wg_mtp);
   const GridRange red = mat_range(p, k, &MatDesc::wg_red0, c.wg_red);
   const GridRange pred = mat_range(p, k, &MatDesc::wg_pred0, c.wg_pred);

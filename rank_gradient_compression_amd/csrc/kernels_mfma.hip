@@ -76,11 +76,17 @@ __device__ __forceinline__ void st4(float* p, int col, int n, bool vec4, float4 
 // clamped, always valid column and zero the value when out of range: no
 // branches, so every load of a step can be in flight at once.  Other rows
 // take the guarded scalar path.
+// Zero a loaded value past the row end, component by component (a
+// conditional on the whole struct is lowered to a select between two stack
+// addresses, i.e. private scratch memory).
+__device__ __forceinline__ float4 keep_if(bool ok, float4 v) {
+  return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
+}
+
 template <bool VEC4>
 __device__ __forceinline__ float4 ldq(const float* rowp, int col, bool ok, int col_safe, int n) {
   if constexpr (VEC4) {
-    const float4 v = *reinterpret_cast<const float4*>(rowp + (ok ? col : col_safe));
-    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    return keep_if(ok, *reinterpret_cast<const float4*>(rowp + (ok ? col : col_safe)));
   } else {
     return ld4(rowp, ok ? col : n, n, false);
   }
@@ -94,7 +100,7 @@ template <bool VEC4>
 __device__ __forceinline__ float4 ldq_nt(const float* rowp, int col, bool ok, int col_safe, int n) {
   if constexpr (VEC4) {
     const v4f_nt v = __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(rowp + (ok ? col : col_safe)));
-    return ok ? make_float4(v[0], v[1], v[2], v[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    return keep_if(ok, make_float4(v[0], v[1], v[2], v[3]));
   } else {
     return ld4(rowp, ok ? col : n, n, false);
   }
@@ -118,9 +124,8 @@ __device__ __forceinline__ float4 ldq_bf16(const uint16_t* rowp, int col, bool o
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (VEC4) {
     const uint2 t = *reinterpret_cast<const uint2*>(rowp + (ok ? col : col_safe));
-    const float4 v = make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u),
-                                 __uint_as_float(t.y << 16), __uint_as_float(t.y & 0xffff0000u));
-    r = ok ? v : r;
+    r = keep_if(ok, make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u),
+                                __uint_as_float(t.y << 16), __uint_as_float(t.y & 0xffff0000u)));
   } else {
     // clamped addresses (col_safe < n), values zeroed past the row end
     const int c = ok ? col : col_safe;
@@ -171,9 +176,18 @@ __device__ __forceinline__ int wg_of(const int32_t* map, int wg_base, int& idx) 
 // The next chunk's loads are issued before the current chunk's matrix
 // products.  The summation index of matrix-core step v of a 16-column block
 // is bound, for lane (li, ls), to column 4 ls + v, so that the lane's A and B
-// operands are one 16-byte LDS read each per block; the blocks are taken in
-// ascending column order whatever the chunk width, so P does not depend on
-// it bit for bit.
+// operands are one 16-byte LDS read each per block.
+//
+// Accumulation: the matrix core sums one chunk's products in fp32, and each
+// chunk's sums are then added into fp64 running sums (and the column-split
+// partials are kept and summed in fp64).  A long fp32 accumulation loses
+// digits to rounding at the size of the running sum, while P = M Q can be
+// much smaller than that after cancellation: with a warm start, column k of
+// Q lines up with the k-th right singular direction of M, so |P_k| ~ s_k^2
+// against running sums of order s_1 s_k (s_k the singular values).  On
+// spectra that fall off like k^-1.5 that cancellation costs fp32 most of its
+// digits at ranks of 32 and more; summing short fp32 runs in fp64 keeps P
+// accurate to about the fp32 rounding of its own entries.
 //
 // Columns per LDS chunk: 128 by default; 64 where the workgroups are
 // limited by LDS and registers (the plain M Q of the refresh, ranks above
@@ -184,7 +198,7 @@ template <int RP, int MODE, bool VEC4, bool GBF16, int CH>
 __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, const void* __restrict__ G,
                                              float* __restrict__ E, float* __restrict__ U, float beta,
                                              const float* __restrict__ Q, float* P, int64_t p_fixed,
-                                             float* __restrict__ ppart, float* smem, const float* Pold) {
+                                             double* __restrict__ ppart, float* smem, const float* Pold) {
   static_assert(MODE >= 0 && MODE <= 6, "pass 1 modes");
   constexpr bool LOAD_G = MODE != 0;
   constexpr bool DEFERRED = MODE >= 5;
@@ -213,9 +227,14 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   // 4 (lane % LPR) .. + 3 of rows RPI u + hr
   const int hr = lane / LPR, cl4 = 4 * (lane % LPR);
 
-  v4f acc[RP / 16];
+  v4f acc[RP / 16];        // this chunk's products (fp32, matrix core)
+  double accd[RP / 16][4];  // running sums over the chunks (fp64)
 #pragma unroll
-  for (int T = 0; T < RP / 16; ++T) acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int T = 0; T < RP / 16; ++T) {
+    acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) accd[T][e] = 0.0;
+  }
 
   // Deferred residual: B operand P_hat_old^T of the wavefront's 16 rows, lane
   // (li, ls) holding Pold[row][4 kk + ls] (read before any P is written).
@@ -318,14 +337,22 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
   };
 
   // A wavefront reads only its own rows of Ms, so the barrier per chunk
-  // guards the shared Q chunk (and the overwrite of both tiles).
+  // guards the shared Q chunk (and the overwrite of both tiles).  In the
+  // deferred modes a wavefront's own rows of Ms pass between its lanes three
+  // times (reconstruction written, read back and overwritten with M by other
+  // lanes, then read as A operands) with no workgroup barrier in between:
+  // the LDS instructions of one wavefront complete in program order, and a
+  // wave barrier between the phases keeps the compiler from moving an LDS
+  // access of one phase past the other (it costs no instruction).
   load_chunk(c_begin);
   for (int c0 = c_begin; c0 < c_end; c0 += CH) {
     stage_q();
     if constexpr (DEFERRED) {
       __syncthreads();
       recon_tile();
+      __builtin_amdgcn_wave_barrier();
       ef_chunk(c0);
+      __builtin_amdgcn_wave_barrier();
     } else {
       ef_chunk(c0);
       __syncthreads();
@@ -349,39 +376,63 @@ __device__ __forceinline__ void mfma_mq_body(const MatDesc& d, int wg, int r, co
       }
     }
     __syncthreads();
+#pragma unroll
+    for (int T = 0; T < RP / 16; ++T) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) accd[T][e] += (double)acc[T][e];
+      acc[T] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
   }
 
-  // acc[T][e] of lane (li, ls) is P[i0 + 16 wave + 4 ls + e][16 T + li].
-  float* dst = d.s1 > 1 ? ppart + d.ppart_off + (int64_t)split * r * m : P + (p_fixed >= 0 ? p_fixed : d.p_off);
-  const bool out4 = (m & 3) == 0;
+  // accd[T][e] of lane (li, ls) is P[i0 + 16 wave + 4 ls + e][16 T + li]:
+  // this split's fp64 partial, or P itself rounded to fp32.
+  const int row = i0 + 16 * wave + 4 * ls;
+  if (d.s1 > 1) {
+    double* dst = ppart + d.ppart_off + (int64_t)split * r * m;
 #pragma unroll
-  for (int T = 0; T < RP / 16; ++T) {
-    const int t = 16 * T + li;
-    if (t < r) st4(dst + (int64_t)t * m, i0 + 16 * wave + 4 * ls, m, out4,
-                   make_float4(acc[T][0], acc[T][1], acc[T][2], acc[T][3]));
+    for (int T = 0; T < RP / 16; ++T) {
+      const int t = 16 * T + li;
+      if (t < r) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (row + e < m) dst[(int64_t)t * m + row + e] = accd[T][e];
+      }
+    }
+  } else {
+    float* dst = P + (p_fixed >= 0 ? p_fixed : d.p_off);
+    const bool out4 = (m & 3) == 0;
+#pragma unroll
+    for (int T = 0; T < RP / 16; ++T) {
+      const int t = 16 * T + li;
+      if (t < r)
+        st4(dst + (int64_t)t * m, row, m, out4,
+            make_float4((float)accd[T][0], (float)accd[T][1], (float)accd[T][2], (float)accd[T][3]));
+    }
   }
 }
 
-template <int RP, int MODE, bool GBF16>
+// VEC4: every matrix of this launch has rows that allow 16-byte accesses (the
+// plan puts them first in the grid), or none has.
+template <int RP, int MODE, bool GBF16, bool VEC4>
 __global__ __launch_bounds__(256) void k_mfma_p(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
                                                 int wg_base, int r, const void* __restrict__ G,
                                                 float* __restrict__ E, float* __restrict__ U, float beta,
                                                 const float* __restrict__ Q, float* P, int64_t p_fixed,
-                                                float* __restrict__ ppart, const float* Pold) {
+                                                double* __restrict__ ppart, const float* Pold) {
   constexpr int CH = mq_chunk(RP, MODE);
   __shared__ float smem[(kMfmaRows + RP) * (CH + 4)];
   int mi;
   const int wg = wg_of(map, wg_base, mi);
   const MatDesc d = mats[mi];
-  if (d.vec == 4)
-    mfma_mq_body<RP, MODE, true, GBF16, CH>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
-  else
-    mfma_mq_body<RP, MODE, false, GBF16, CH>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
+  mfma_mq_body<RP, MODE, VEC4, GBF16, CH>(d, wg, r, G, E, U, beta, Q, P, p_fixed, ppart, smem, Pold);
 }
 
-// Fixed-order sum of the column-split partials of pass 1.
+// Fixed-order sum of the column-split partials of pass 1 (fp32 partials of
+// the vector path, fp64 ones of the matrix cores, summed in their own
+// precision and rounded to fp32 once).
+template <typename T>
 __global__ __launch_bounds__(kRedCols) void k_psum(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
-                                                   int wg_base, int r, const float* __restrict__ ppart,
+                                                   int wg_base, int r, const T* __restrict__ ppart,
                                                    float* __restrict__ P, int64_t p_fixed) {
   int mi;
   const int wg = wg_of(map, wg_base, mi);
@@ -389,15 +440,15 @@ __global__ __launch_bounds__(kRedCols) void k_psum(const MatDesc* __restrict__ m
   const int64_t len = (int64_t)r * d.m;
   const int64_t idx = (int64_t)(wg - d.wg_pred0) * kRedCols + threadIdx.x;
   if (idx >= len) return;
-  const float* src = ppart + d.ppart_off + idx;
-  float s0 = 0.f, s1 = 0.f;
+  const T* src = ppart + d.ppart_off + idx;
+  T s0 = 0, s1 = 0;
   int b = 0;
   for (; b + 2 <= d.s1; b += 2) {
     s0 += src[(int64_t)b * len];
     s1 += src[(int64_t)(b + 1) * len];
   }
   if (b < d.s1) s0 += src[(int64_t)b * len];
-  P[(p_fixed >= 0 ? p_fixed : d.p_off) + idx] = s0 + s1;
+  P[(p_fixed >= 0 ? p_fixed : d.p_off) + idx] = (float)(s0 + s1);
 }
 
 // ---------------------------------------------------------------------------
@@ -825,9 +876,12 @@ __device__ __forceinline__ double rsqrt_nr(double d) {
 // needs no barrier: its LDS accesses complete in program order.  The upper
 // triangle of the factor's A slot (diagonal included) is overwritten with R,
 // row by row (A is read first).
+// With zcount non-null, zcount[blockIdx.x] receives the number of columns
+// the dependence rule set to zero.
 template <int RP>
 __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ descs, int first, int r,
-                                                   double* __restrict__ gram, float zero_rel) {
+                                                   double* __restrict__ gram, float zero_rel,
+                                                   int32_t* __restrict__ zcount) {
   __shared__ double rowbuf[RP];
   __shared__ double Rl[RP * RP];  // the factor, until it is written out
   const OrthDesc o = descs[first + blockIdx.x];
@@ -839,6 +893,7 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
   for (int i = 0; i < RP; ++i) sc[i] = own ? a[i * RP + j] : 0.0;
   const double dgj = own ? a[j * RP + j] : 0.0;  // A_jj: squared norm before projection
   const double zr2 = (double)zero_rel * (double)zero_rel;
+  int nzero = 0;  // wavefront-uniform
   // Fully unrolled so that sc[] stays in registers; steps k >= r are skipped
   // by a uniform branch.  No global store inside the steps: a pending store
   // would be waited for at every step.
@@ -854,6 +909,7 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
       const double d = readlane_f64(sc[k], k);
       const double dg = readlane_f64(dgj, k);
       const bool zero = !(dg > 0.0) || !(d > 0.0) || d <= zr2 * dg;
+      nzero += zero ? 1 : 0;
       const double y = zero ? 0.0 : rsqrt_nr(d);  // 1 / sqrt(S_kk)
       const double c = sc[k] * (y * y);            // S_kj / S_kk
       if (own && j >= k && j < r) Rl[k * RP + j] = j == k ? d * y : sc[k] * y;
@@ -867,6 +923,7 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
     const int e = j + 64 * u, kr = e / RP, jc = e % RP;
     if (kr <= jc && jc < r) a[e] = Rl[e];
   }
+  if (zcount && j == 0) zcount[blockIdx.x] = nzero;
 }
 
 // P_hat = P R^-1, one row per thread: x R = p by forward substitution in
@@ -946,35 +1003,43 @@ __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restric
     default: return hipErrorInvalidValue;             \
   }
 
+// One launch per access-width part of the grid range g (the plan puts the
+// 16-byte-row matrices first, in [0, wg_rows_v4)).
+template <int RP, int MODE, bool GBF16>
+static hipError_t mfma_p_launch(const LaunchCtx& c, const GridRange& g, const void* G, float* E, float* U, float beta,
+                                const float* Q, float* P, int64_t p_fixed) {
+  const int split = min(max(c.wg_rows_v4, g.base), g.base + g.count);
+  const float* pold = MODE >= 5 ? c.p_prev : nullptr;
+  double* pp = static_cast<double*>(c.ppart);
+  if (split > g.base)
+    hipLaunchKernelGGL((k_mfma_p<RP, MODE, GBF16, true>), dim3(split - g.base), dim3(256), 0, c.stream, c.mats,
+                       c.rows_map, g.base, c.rank, G, E, U, beta, Q, P, p_fixed, pp, pold);
+  if (g.base + g.count > split)
+    hipLaunchKernelGGL((k_mfma_p<RP, MODE, GBF16, false>), dim3(g.base + g.count - split), dim3(256), 0, c.stream,
+                       c.mats, c.rows_map, split, c.rank, G, E, U, beta, Q, P, p_fixed, pp, pold);
+  return hipGetLastError();
+}
+
 template <int RP, bool GBF16>
 static hipError_t mfma_p_rpg(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                              float beta, const float* Q, float* P, int64_t p_fixed) {
-  const dim3 gr(g.count), b(256);
-#define PSGD_MP(MD)                                                                                          \
-  hipLaunchKernelGGL((k_mfma_p<RP, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, c.rank, G, E, U, \
-                     beta, Q, P, p_fixed, c.ppart, c.p_prev)
   switch (mode) {
-    case 1: PSGD_MP(1); break;
-    case 2: PSGD_MP(2); break;
-    case 3: PSGD_MP(3); break;
-    case 4: PSGD_MP(4); break;
-    case 5: PSGD_MP(5); break;
-    case 6: PSGD_MP(6); break;
+    case 1: return mfma_p_launch<RP, 1, GBF16>(c, g, G, E, U, beta, Q, P, p_fixed);
+    case 2: return mfma_p_launch<RP, 2, GBF16>(c, g, G, E, U, beta, Q, P, p_fixed);
+    case 3: return mfma_p_launch<RP, 3, GBF16>(c, g, G, E, U, beta, Q, P, p_fixed);
+    case 4: return mfma_p_launch<RP, 4, GBF16>(c, g, G, E, U, beta, Q, P, p_fixed);
+    case 5: return mfma_p_launch<RP, 5, GBF16>(c, g, G, E, U, beta, Q, P, p_fixed);
+    case 6: return mfma_p_launch<RP, 6, GBF16>(c, g, G, E, U, beta, Q, P, p_fixed);
     default: return hipErrorInvalidValue;
   }
-#undef PSGD_MP
-  return hipGetLastError();
 }
 
 template <int RP>
 static hipError_t mfma_p_rp(const LaunchCtx& c, const GridRange& g, int mode, const void* G, float* E, float* U,
                             float beta, const float* Q, float* P, int64_t p_fixed) {
   if (g.count == 0) return hipSuccess;
-  if (mode == 0) {  // M read from E: no gradient involved
-    hipLaunchKernelGGL((k_mfma_p<RP, 0, false>), dim3(g.count), dim3(256), 0, c.stream, c.mats, c.rows_map, g.base,
-                       c.rank, G, E, U, beta, Q, P, p_fixed, c.ppart, nullptr);
-    return hipGetLastError();
-  }
+  if (mode == 0)  // M read from E: no gradient involved
+    return mfma_p_launch<RP, 0, false>(c, g, G, E, U, beta, Q, P, p_fixed);
   return c.g_bf16 ? mfma_p_rpg<RP, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)
                   : mfma_p_rpg<RP, false>(c, g, mode, G, E, U, beta, Q, P, p_fixed);
 }
@@ -986,8 +1051,12 @@ hipError_t launch_mfma_p(const LaunchCtx& c, const GridRange& g, int mode, const
 
 hipError_t launch_psum(const LaunchCtx& c, const GridRange& g, float* P, int64_t p_fixed) {
   if (g.count == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_psum, dim3(g.count), dim3(kRedCols), 0, c.stream, c.mats, c.pred_map, g.base, c.rank, c.ppart,
-                     P, p_fixed);
+  if (c.mfma)
+    hipLaunchKernelGGL(k_psum<double>, dim3(g.count), dim3(kRedCols), 0, c.stream, c.mats, c.pred_map, g.base, c.rank,
+                       static_cast<const double*>(c.ppart), P, p_fixed);
+  else
+    hipLaunchKernelGGL(k_psum<float>, dim3(g.count), dim3(kRedCols), 0, c.stream, c.mats, c.pred_map, g.base, c.rank,
+                       static_cast<const float*>(c.ppart), P, p_fixed);
   return hipGetLastError();
 }
 
@@ -1036,7 +1105,7 @@ hipError_t launch_mfma_recon(const LaunchCtx& c, float* E, const float* Q, const
 
 template <int RP>
 static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const int32_t* map, int nblocks,
-                               float* base) {
+                               float* base, int32_t* zcount) {
   if (nblocks == 0 || count == 0) return hipSuccess;
   hipLaunchKernelGGL((k_gram_partial<RP>), dim3(nblocks), dim3(256), 0, c.stream, c.orth, map, first, c.rank, base,
                      c.gram);
@@ -1047,7 +1116,7 @@ static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const i
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(64), 0, c.stream, c.orth, first, c.rank, c.gram,
-                     kZeroColumnRel);
+                     kZeroColumnRel, zcount);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_apply_t<RP>), dim3(nblocks), dim3(kGramRows), 0, c.stream, c.orth, map, first, c.rank, base,
@@ -1056,8 +1125,8 @@ static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const i
 }
 
 hipError_t launch_gram_orth(const LaunchCtx& c, int first, int count, const int32_t* map, int nblocks,
-                            float* base) {
-  PSGD_RP_SWITCH(c.rank_pad, gram_orth_rp<RPV>(c, first, count, map, nblocks, base));
+                            float* base, int32_t* zcount) {
+  PSGD_RP_SWITCH(c.rank_pad, gram_orth_rp<RPV>(c, first, count, map, nblocks, base, zcount));
 }
 
 }  // namespace psgd

@@ -337,16 +337,22 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, in
     }
   }
 
-  constexpr int NV = pow2_at_least(kWaveRows * R);
-  float vals[NV];
+  // The kWaveRows x R row sums, at most 32 values per transposed butterfly
+  // (a 64-value one does not stay in registers: it spilled to scratch).
+  constexpr int NALL = kWaveRows * R;
+  constexpr int NV = pow2_at_least(NALL < 32 ? NALL : 32);
+  constexpr int SHIFT = NV >= 32 ? 1 : NV >= 16 ? 2 : NV >= 8 ? 3 : NV >= 4 ? 4 : NV >= 2 ? 5 : 6;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) vals[i] = i < kWaveRows * R ? acc[i / R][i % R] : 0.f;
-  const float tot = wave_transpose_sum<NV>(vals, lane);
-  constexpr int SHIFT = NV >= 64 ? 0 : NV >= 32 ? 1 : NV >= 16 ? 2 : NV >= 8 ? 3 : NV >= 4 ? 4 : NV >= 2 ? 5 : 6;
-  const int vi = lane >> SHIFT;
-  if ((lane & ((1 << SHIFT) - 1)) == 0 && vi < kWaveRows * R) {
-    const int rr = vi / R, k = vi % R;
-    if (rr < nrows) pdst[(int64_t)k * m + row0 + rr] = tot;
+  for (int base = 0; base < NALL; base += NV) {
+    float vals[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vals[i] = base + i < NALL ? acc[(base + i) / R][(base + i) % R] : 0.f;
+    const float tot = wave_transpose_sum<NV>(vals, lane);
+    const int vi = base + (lane >> SHIFT);
+    if ((lane & ((1 << SHIFT) - 1)) == 0 && vi < NALL) {
+      const int rr = vi / R, k = vi % R;
+      if (rr < nrows) pdst[(int64_t)k * m + row0 + rr] = tot;
+    }
   }
 }
 
@@ -404,8 +410,18 @@ __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__
 
 // One wavefront: 64*VEC consecutive columns of one row block.  P_hat values
 // of a row are wavefront-uniform (scalar loads); each lane accumulates VEC x R
-// dot products over the block's rows.
-template <int R, int VEC>
+// dot products over the block's rows.  NT: M is read with the non-temporal
+// hint, for sets far larger than the caches (7B-shaped set 4.49 -> 4.19 ms,
+// the step 33.4 -> 32.4-32.9 ms); a set that fits the 256 MB last-level cache
+// keeps plain loads, so that M is still cached for the residual pass that
+// reads it next.
+template <int R, int VEC, bool NT>
+__device__ __forceinline__ Vec<VEC> ld_m(const float* p) {
+  if constexpr (NT) return ldv_nt<VEC>(p);
+  else return ldv<VEC>(p);
+}
+
+template <int R, int VEC, bool NT>
 __device__ __forceinline__ void mtp_wave(const MatDesc& d, int rb, int j, const float* __restrict__ M,
                                          const float* __restrict__ Ph, int64_t ph_fixed, float* __restrict__ Q,
                                          float* __restrict__ part) {
@@ -425,7 +441,7 @@ __device__ __forceinline__ void mtp_wave(const MatDesc& d, int rb, int j, const 
   for (; i + U <= i1; i += U) {
     Vec<VEC> x[U];
 #pragma unroll
-    for (int t = 0; t < U; ++t) x[t] = ldv<VEC>(mp + (int64_t)(i + t) * n);
+    for (int t = 0; t < U; ++t) x[t] = ld_m<R, VEC, NT>(mp + (int64_t)(i + t) * n);
 #pragma unroll
     for (int t = 0; t < U; ++t)
 #pragma unroll
@@ -436,7 +452,7 @@ __device__ __forceinline__ void mtp_wave(const MatDesc& d, int rb, int j, const 
       }
   }
   for (; i < i1; ++i) {
-    const Vec<VEC> x = ldv<VEC>(mp + (int64_t)i * n);
+    const Vec<VEC> x = ld_m<R, VEC, NT>(mp + (int64_t)i * n);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const float w = ph[(int64_t)k * m + i];
@@ -454,7 +470,7 @@ __device__ __forceinline__ void mtp_wave(const MatDesc& d, int rb, int j, const 
   }
 }
 
-template <int R>
+template <int R, bool NT>
 __global__ __launch_bounds__(kWGThreads) void k_mtp(const MatDesc* __restrict__ mats, const int32_t* __restrict__ map,
                                                     int wg_base, const float* __restrict__ M,
                                                     const float* __restrict__ Ph, int64_t ph_fixed,
@@ -468,11 +484,11 @@ __global__ __launch_bounds__(kWGThreads) void k_mtp(const MatDesc* __restrict__ 
   const int j = (cb * kMtpWaves + wave) * 64 * d.vec + lane * d.vec;
   if (j >= d.n) return;
   if (d.vec == 4)
-    mtp_wave<R, 4>(d, rb, j, M, Ph, ph_fixed, Q, part);
+    mtp_wave<R, 4, NT>(d, rb, j, M, Ph, ph_fixed, Q, part);
   else if (d.vec == 2)
-    mtp_wave<R, 2>(d, rb, j, M, Ph, ph_fixed, Q, part);
+    mtp_wave<R, 2, NT>(d, rb, j, M, Ph, ph_fixed, Q, part);
   else
-    mtp_wave<R, 1>(d, rb, j, M, Ph, ph_fixed, Q, part);
+    mtp_wave<R, 1, NT>(d, rb, j, M, Ph, ph_fixed, Q, part);
 }
 
 // Fixed-order sum of the row-block partials: Q[k*n + j] = sum_b part_b[k*n + j].
@@ -625,49 +641,67 @@ __global__ __launch_bounds__(256) void k_pass_unpack(const PassDesc* __restrict_
   pass_unpack_wg<SGD>(pass, map, blockIdx.x, Pbuf, out, sg);
 }
 
-// Plain 16-byte copy: the bandwidth ceiling and counter calibration.
+// Streaming helpers of the copy and probe kernels: 16-byte non-temporal
+// accesses (the data streams through once), loads at a clamped, always valid
+// index so that they need no branch and all of a thread's loads can be in
+// flight together.
+__device__ __forceinline__ v4f_nt ld_stream(const float4* p, int64_t i, int64_t n4) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(p + (i < n4 ? i : n4 - 1)));
+}
+
+__device__ __forceinline__ void st_stream(float4* p, int64_t i, v4f_nt v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<v4f_nt*>(p + i));
+}
+
+// Plain 16-byte copy: the bandwidth ceiling and counter calibration.  Each
+// thread moves kStreamUnroll vectors per grid step, all loads issued before
+// the stores.
 __global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, const float4* __restrict__ src,
                                                      int64_t n4) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+  constexpr int U = kStreamUnroll;
+  const int64_t stride = (int64_t)gridDim.x * 256 * U;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x; i0 < n4; i0 += stride) {
+    v4f_nt x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = ld_stream(src, i0 + (int64_t)u * 256, n4);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * 256;
+      if (i < n4) st_stream(dst, i, x[u]);
+    }
+  }
 }
 
 // Streaming-bandwidth probe: the byte pattern of a pass (NIN arrays read,
 // NOUT written) without its arithmetic, out_j[i] = sum_k in_k[i] (zero with
 // no input).  With no output the sums are reduced per workgroup into
-// sink[blockIdx.x], so the loads are not dead.  Each thread moves kProbeUnroll
-// 16-byte vectors per array per grid step, all loads issued before the sums.
+// sink[blockIdx.x], so the loads are not dead.  Each thread moves
+// kStreamUnroll 16-byte vectors per array per grid step, every load of the
+// step issued before the sums, with the access hints of the passes
+// (non-temporal loads and stores).
 template <int NIN, int NOUT>
 __global__ __launch_bounds__(256) void k_stream_probe(ProbeArgs a) {
-  constexpr int U = kProbeUnroll;
+  constexpr int U = kStreamUnroll;
   __shared__ float wsum[4];
   const int64_t stride = (int64_t)gridDim.x * 256 * U;
   float part = 0.f;
   for (int64_t i0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x; i0 < a.n4; i0 += stride) {
-    float4 x[NIN > 0 ? NIN : 1][U];
+    v4f_nt x[NIN > 0 ? NIN : 1][U];
 #pragma unroll
     for (int k = 0; k < NIN; ++k)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = i0 + (int64_t)u * 256;
-        x[k][u] = i < a.n4 ? a.in[k][i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int u = 0; u < U; ++u) x[k][u] = ld_stream(a.in[k], i0 + (int64_t)u * 256, a.n4);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      v4f_nt v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < NIN; ++k) {
-        v.x += x[k][u].x;
-        v.y += x[k][u].y;
-        v.z += x[k][u].z;
-        v.w += x[k][u].w;
-      }
+      for (int k = 0; k < NIN; ++k) v += x[k][u];
       const int64_t i = i0 + (int64_t)u * 256;
       if constexpr (NOUT == 0) {
-        part += (v.x + v.y) + (v.z + v.w);
+        if (i < a.n4) part += (v[0] + v[1]) + (v[2] + v[3]);
       } else if (i < a.n4) {
 #pragma unroll
-        for (int j = 0; j < NOUT; ++j) a.out[j][i] = v;
+        for (int j = 0; j < NOUT; ++j) st_stream(a.out[j], i, v);
       }
     }
   }
@@ -718,7 +752,7 @@ static hipError_t launch_ef_p_rg(const LaunchCtx& c, const GridRange& g, int mod
   const dim3 gr(g.count + extra), b(kWGThreads);
 #define PSGD_EFP(MD)                                                                                            \
   hipLaunchKernelGGL((k_ef_p<R, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, \
-                     p_fixed, c.p_prev, c.ppart, g.count, c.pass, c.pass_map, c.pack_dst)
+                     p_fixed, c.p_prev, static_cast<float*>(c.ppart), g.count, c.pass, c.pass_map, c.pack_dst)
   switch (mode) {
     case 1: PSGD_EFP(1); break;
     case 2: PSGD_EFP(2); break;
@@ -737,7 +771,7 @@ static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode
   if (mode == 0) {  // P = M Q with M read from E: no gradient involved, no packing
     if (g.count == 0) return hipSuccess;
     hipLaunchKernelGGL((k_ef_p<R, 0, false>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map,
-                       g.base, G, E, U, beta, Q, P, p_fixed, nullptr, c.ppart, g.count, c.pass, c.pass_map, nullptr);
+                       g.base, G, E, U, beta, Q, P, p_fixed, nullptr, static_cast<float*>(c.ppart), g.count, c.pass, c.pass_map, nullptr);
     return hipGetLastError();
   }
   return c.g_bf16 ? launch_ef_p_rg<R, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)
@@ -748,8 +782,12 @@ template <int R>
 static hipError_t launch_mtp_r(const LaunchCtx& c, const GridRange& g, const float* M, const float* Ph,
                                int64_t ph_fixed, float* Q) {
   if (g.count == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_mtp<R>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.mtp_map, g.base, M, Ph,
-                     ph_fixed, Q, c.part);
+  if (c.stream_hint)
+    hipLaunchKernelGGL((k_mtp<R, true>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.mtp_map, g.base, M,
+                       Ph, ph_fixed, Q, c.part);
+  else
+    hipLaunchKernelGGL((k_mtp<R, false>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.mtp_map, g.base, M,
+                       Ph, ph_fixed, Q, c.part);
   return hipGetLastError();
 }
 
@@ -841,8 +879,8 @@ hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out,
 hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream) {
   const int64_t n4 = (int64_t)(n / 4);
   if (n4 == 0) return hipSuccess;
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
+  int64_t blocks = (n4 + 256 * kStreamUnroll - 1) / (256 * kStreamUnroll);
+  if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
   hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float4*>(dst),
                      reinterpret_cast<const float4*>(src), n4);
   return hipGetLastError();
@@ -850,7 +888,7 @@ hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_
 
 hipError_t launch_stream_probe(const ProbeArgs& a, int nin, int nout, hipStream_t stream) {
   if (a.n4 == 0) return hipSuccess;
-  int64_t blocks = (a.n4 + 256 * kProbeUnroll - 1) / (256 * kProbeUnroll);
+  int64_t blocks = (a.n4 + 256 * kStreamUnroll - 1) / (256 * kStreamUnroll);
   if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
   const dim3 g((unsigned)blocks), b(256);
 #define PSGD_PROBE(I, O) \

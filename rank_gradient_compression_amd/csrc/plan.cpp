@@ -246,7 +246,6 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     // that each sums at most 8 row blocks (up to 16 wavefronts per slice).
     d.red_split = 1;
     while (d.red_split < kRedWaves && (d.nrb + d.red_split - 1) / d.red_split > 8) d.red_split *= 2;
-    d.wg_rows0 = wg_rows;
     d.wg_rec0 = wg_rec;
     // column splits: a split is a whole number of wavefront widths (64
     // columns on the matrix cores, 64 vectors otherwise)
@@ -267,8 +266,7 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
       for (int32_t t = 0; t < np; ++t) p->pred_map.push_back((int32_t)k);
       wg_pred += np;
     }
-    for (int32_t t = 0; t < nrow_wg; ++t) p->rows_map.push_back((int32_t)k);
-    wg_rows += nrow_wg;
+    p->nrow_wg.push_back(nrow_wg);
     for (int32_t t = 0; t < nrec_wg; ++t) p->rec_map.push_back((int32_t)k);
     wg_rec += nrec_wg;
     // Gram grid (orthonormalisation of P) and the Gram scratch, sized for P
@@ -293,6 +291,21 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     }
     // refresh scratch: P of this matrix (rank columns of m rows)
     rscr = std::max<int64_t>(rscr, align_up((int64_t)d.m * rp, kAlignElems));
+  }
+  // Pass-1 grid.  On the matrix cores the matrices whose rows allow 16-byte
+  // accesses take the first workgroups and the others the rest, so that each
+  // part runs in an instantiation of the kernel compiled for its access width
+  // only (the narrow-access path alone would raise the wide one's register
+  // count); the vector path keeps the matrix order.
+  for (int part = 0; part < (mfma ? 2 : 1); ++part) {
+    for (size_t k = 0; k < p->mats.size(); ++k) {
+      MatDesc& d = p->mats[k];
+      if (mfma && (part == 0) != (d.vec == 4)) continue;
+      d.wg_rows0 = wg_rows;
+      for (int32_t t = 0; t < p->nrow_wg[k]; ++t) p->rows_map.push_back((int32_t)k);
+      wg_rows += p->nrow_wg[k];
+    }
+    if (part == 0) p->hdr.wg_rows_v4 = mfma ? wg_rows : 0;
   }
   // orthonormalisation descriptors: P of compress, P and Q of the refresh
   const size_t nm = p->mats.size();
@@ -375,7 +388,7 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   h.part_base = b;
   b = align_up(b + 4 * part, 256);
   h.ppart_base = b;
-  b = align_up(b + 4 * ppart, 256);
+  b = align_up(b + (mfma ? 8 : 4) * ppart, 256);  // fp64 partials on the matrix cores
   h.gram_base = b;
   b = align_up(b + 8 * gram, 256);
   h.refresh_base = b;

@@ -8,6 +8,11 @@
 
 namespace psgd {
 
+// A set whose compressed matrices hold more bytes than this streams through
+// the caches whatever the access hints; smaller ones can stay in the 256 MB
+// last-level cache from one pass to the next.
+constexpr int64_t kStreamHintBytes = int64_t(1) << 30;
+
 // Relative threshold under which a Gram-Schmidt column counts as dependent
 // and is set to zero.
 constexpr float kZeroColumnRel = 1e-4f;
@@ -19,9 +24,11 @@ struct LaunchCtx {
   int rank, rank_pad;
   bool mfma;
   bool g_bf16;  // gradients stored as bfloat16
+  bool stream_hint;  // the compressed matrices exceed kStreamHintBytes: read M non-temporally where it pays
   const float* p_prev;  // deferred residual: the previous step's P_hat (plan offsets)
   int nmat, npass;
   int wg_rows, wg_rec, wg_mtp, wg_red, wg_pass, wg_pred, wg_gram, wg_gramq;
+  int wg_rows_v4;  // matrix cores: the pass-1 grid's 16-byte-row part is [0, wg_rows_v4)
   const MatDesc* mats;
   const PassDesc* pass;
   const OrthDesc* orth;
@@ -34,7 +41,8 @@ struct LaunchCtx {
   const int32_t* gram_map;
   const int32_t* gramq_map;
   float* part;    // partial-Q scratch
-  float* ppart;   // partial-P scratch (column splits of pass 1)
+  void* ppart;    // partial-P scratch (column splits of pass 1): fp32 on the
+                  // vector path, fp64 on the matrix cores
   // Vector-ALU path: the pass-through packing runs as extra workgroups of
   // the pass-1 launch (into pack_dst, when non-null) and the unpacking as
   // extra workgroups of the residual-pass launch (from unpack_src).
@@ -86,9 +94,10 @@ hipError_t launch_mfma_recon(const LaunchCtx& c, float* E, const float* Q, const
                              bool residual, const SgdArgs& sg);
 // With a map: descriptors first + [0, count) over a grouped Gram grid of
 // nblocks workgroups (map gives the matrix of each workgroup).  Without: the
-// single descriptor `first` with nblocks Gram blocks.
+// single descriptor `first` with nblocks Gram blocks.  zcount (nullable)
+// receives, per descriptor, the number of columns set to zero.
 hipError_t launch_gram_orth(const LaunchCtx& c, int first, int count, const int32_t* map, int nblocks,
-                            float* base);
+                            float* base, int32_t* zcount = nullptr);
 
 // ---- shared
 hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q);
@@ -105,8 +114,9 @@ hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_
 
 // Streaming-bandwidth probe (psgd_stream_probe): up to 3 inputs, 2 outputs,
 // n4 16-byte vectors each; sink holds one float per workgroup when there is
-// no output.
-constexpr int kProbeUnroll = 4;
+// no output.  The copy and the probe move kStreamUnroll vectors per array and
+// thread per grid step, on at most kProbeMaxBlocks workgroups.
+constexpr int kStreamUnroll = 8;
 constexpr int kProbeMaxBlocks = 16384;
 struct ProbeArgs {
   const float4* in[3];

@@ -44,7 +44,8 @@ struct MatDesc {
   int64_t q_off;     // Q: rank columns of n floats from here
   int64_t part_off;  // partial-Q scratch (floats, from the scratch base)
   int64_t gram_off;  // Gram partials (doubles, from the Gram scratch base)
-  int64_t ppart_off; // partial-P scratch of a column-split pass 1 (floats)
+  int64_t ppart_off; // partial-P scratch of a column-split pass 1 (elements: fp32
+                     // on the vector path, fp64 on the matrix cores)
   int64_t t_off;     // triangular factor T (doubles, from the Gram scratch base)
   int32_t m, n;
   int32_t vec;       // 4, 2 or 1: widest vector access both n and off allow
@@ -115,6 +116,8 @@ struct WsHeader {
   int32_t rank, flags;
   int32_t wg_rows, wg_mtp, wg_red, wg_pass;
   int32_t wg_pred, wg_gram, wg_gramq, rank_pad, mfma, wg_rec;
+  int32_t wg_rows_v4;    // matrix cores: pass-1 workgroups of the 16-byte-row matrices (first)
+  int32_t pad_;
   int64_t mat_off;       // bytes from workspace start: MatDesc[nmat]
   int64_t pass_off;      // PassDesc[npass]
   int64_t rows_map_off;  // int32 matrix index per row-tile workgroup (pass 1)
@@ -128,7 +131,7 @@ struct WsHeader {
   int64_t orth_off;      // OrthDesc[3 * nmat]: P of compress, refresh P, refresh Q
   int64_t tables_bytes;  // bytes of the table part (uploaded by workspace_init)
   int64_t part_base;     // bytes: partial-Q scratch (float)
-  int64_t ppart_base;    // bytes: partial-P scratch (float)
+  int64_t ppart_base;    // bytes: partial-P scratch (float; double on the matrix cores)
   int64_t gram_base;     // bytes: orthonormalisation scratch (double)
   int64_t refresh_base;  // bytes: refresh scratch (float)
   int64_t total_bytes;

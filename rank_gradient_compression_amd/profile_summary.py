@@ -2,8 +2,14 @@
 
     python -m rank_gradient_compression_amd.profile_summary trace STATS_CSV "COMMAND" "TITLE"
     python -m rank_gradient_compression_amd.profile_summary bytes FETCH_CSV WRITE_CSV "CMD_FETCH" "CMD_WRITE" "TITLE"
+    python -m rank_gradient_compression_amd.profile_summary dispatches KERNEL TRACE_CSV "CMD_TRACE"
+        COUNTER_CSV "CMD_COUNTERS" [COUNTER_CSV "CMD_COUNTERS" ...] "TITLE"
 
-`trace` reads a `--kernel-trace --stats` kernel_stats.csv; `bytes` reads the
+`dispatches` lists every dispatch of one kernel in launch order: its duration
+from a `--kernel-trace` kernel_trace.csv and its counters from one or more
+`--pmc` counter_collection.csv files of the same program (the n-th dispatch
+of the kernel in each file).  `trace` reads a `--kernel-trace --stats`
+kernel_stats.csv; `bytes` reads the
 counter_collection.csv of one `--pmc FETCH_SIZE` run and one `--pmc
 WRITE_SIZE` run of the same program.  The byte counters are calibrated with
 the library's 16-byte copy kernel over 4 GiB (`psgd_stream_copy`, which the
@@ -116,12 +122,45 @@ def hbm_bytes(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, title: str
     return "\n".join(out) + "\n"
 
 
+def dispatches(kernel: str, trace_csv: str, cmd_trace: str, counter_runs, title: str) -> str:
+    """Every dispatch of `kernel` in launch order: duration from a kernel
+    trace, counters from one or more counter-collection runs (matched by the
+    dispatch's position among the kernel's dispatches in each file)."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in rows]
+    cols, per = [], []
+    for path, _ in counter_runs:
+        by = collections.OrderedDict()
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"]:
+                by.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        seq = [by[k] for k in sorted(by)]
+        names = sorted({n for c in seq for n in c})
+        cols += names
+        per.append((names, seq))
+    out = [f"# {title}\n", "Commands:\n", "```\n" + "\n".join([cmd_trace] + [c for _, c in counter_runs]) + "\n```\n",
+           "| dispatch | duration (ms, trace run) | " + " | ".join(cols) + " |", "|---" * (2 + len(cols)) + "|"]
+    n = max([len(durs)] + [len(seq) for _, seq in per])
+    for i in range(n):
+        cells = [str(i), f"{durs[i]:.3f}" if i < len(durs) else ""]
+        for names, seq in per:
+            cells += [f"{seq[i][c]:.4g}" if i < len(seq) and c in seq[i] else "" for c in names]
+        out.append("| " + " | ".join(cells) + " |")
+    out.append("\nSummarised by `python -m rank_gradient_compression_amd.profile_summary dispatches`.")
+    return "\n".join(out) + "\n"
+
+
 def main(argv) -> int:
     if len(argv) >= 5 and argv[1] == "trace":
         sys.stdout.write(trace(argv[2], argv[3], argv[4]))
         return 0
     if len(argv) >= 7 and argv[1] == "bytes":
         sys.stdout.write(hbm_bytes(*argv[2:7]))
+        return 0
+    if len(argv) >= 8 and argv[1] == "dispatches" and len(argv) % 2 == 0:
+        runs = [(argv[i], argv[i + 1]) for i in range(5, len(argv) - 1, 2)]
+        sys.stdout.write(dispatches(argv[2], argv[3], argv[4], runs, argv[-1]))
         return 0
     sys.stderr.write(__doc__)
     return 2

@@ -106,7 +106,8 @@ class PowerSGD:
                  refresh_iters: int = 0, power_iters: int = 0, error_feedback: bool = True,
                  params: Optional[torch.Tensor] = None, sgd_buf: Optional[torch.Tensor] = None, sgd_lr: float = 0.0,
                  sgd_momentum: float = 0.0, nesterov: bool = False, defer_residual: bool = False,
-                 residual_deferred: bool = False, payload_bf16: bool = False, noalloc: bool = False) -> None:
+                 residual_deferred: bool = False, payload_bf16: bool = False, noalloc: bool = False,
+                 zero_cols: Optional[torch.Tensor] = None) -> None:
         """One psgd_compress call on the owned buffers; noalloc=True takes
         psgd_compress_noalloc (the library's static scratch, no workspace)."""
         out = mhat_buf if mhat_buf is not None else (self.mhat if mhat else None)
@@ -115,9 +116,12 @@ class PowerSGD:
         flags |= (B.PSGD_STEP_DEFER_RESIDUAL if defer_residual else 0)
         flags |= (B.PSGD_STEP_RESIDUAL_DEFERRED if residual_deferred else 0)
         flags |= (B.PSGD_STEP_PAYLOAD_BF16 if payload_bf16 else 0)
-        if refresh_iters or power_iters or flags or params is not None:
+        if refresh_iters or power_iters or flags or params is not None or zero_cols is not None:
+            if zero_cols is not None:
+                assert zero_cols.dtype == torch.int32 and zero_cols.numel() >= self.info["ncompressed"]
             opts = B.step_opts(power_iters, refresh_iters, flags, sgd_lr, sgd_momentum, params.data_ptr() if params is not None else 0,
-                               sgd_buf.data_ptr() if sgd_buf is not None else 0)
+                               sgd_buf.data_ptr() if sgd_buf is not None else 0,
+                               zero_cols.data_ptr() if zero_cols is not None else 0)
         if noalloc:
             B.psgd_compress_noalloc(self.plan, self.grads.data_ptr(), self.err.data_ptr(),
                                     self.mom.data_ptr() if self.mom is not None else 0, self.q.data_ptr(),
