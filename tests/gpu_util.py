@@ -1,5 +1,30 @@
 """Helpers shared by the GPU tests: run the HIP path and the fp64 oracle on the
-same seeded inputs and compare per matrix."""
+same seeded inputs and compare per matrix.
+
+Two kinds of comparison (the survey's reading o11):
+  gate   teacher-forced: the oracle takes the GPU's own state before the step
+         (E_{t-1}, Q_{t-1}, u_{t-1}) with the same G_t; every matrix within
+         REL_TOL.
+  drift  free-running: an oracle that has followed its own trajectory from the
+         same start.  Besides each step's own error it carries the rounding
+         of the fp32 buffers the ABI fixes (P, Q, E), amplified by the
+         conditioning of P: rounding P's columns to fp32 moves P_hat by about
+         u kappa in its last columns (u = 2^-24, kappa the 2-norm condition
+         number of P with unit columns), and a warm-started trajectory keeps
+         that difference.  With exact products and only fp32 storage it
+         measured 0.009-0.05 u kappa on the k^-1.5 spectrum at ranks 16-64 over
+         four steps, so over the first DRIFT_STEPS steps the drift tolerance
+         of a matrix is max(REL_TOL, DRIFT_FACTOR u kappa), kappa the largest
+         seen on that matrix so far.  Later the drift is only reported: error
+         feedback on a fixed signal moves the transmitted subspace whenever
+         the error memory's untransmitted directions overtake it, and near
+         those steps the subspace is barely determined, so two correct
+         trajectories that start one rounding apart separate (with exact
+         products and fp32 storage, a ResNet18-shaped matrix at rank 2 drifted
+         from 6e-7 at step 10 to 1e-3 at step 50 and O(1) by step 90).  Over a
+         whole trajectory the GPU's own run is held to error feedback's
+         telescoping sum instead (telescoping_error).
+"""
 from __future__ import annotations
 
 import sys
@@ -10,6 +35,10 @@ import oracle
 
 REL_TOL = 1e-4     # relative Frobenius error on P_hat, Q, E (and M_hat)
 ORTH_TOL = 1e-5    # ||P_hat^T P_hat - I||_F over the non-zero columns
+U32 = 2.0 ** -24   # unit roundoff of fp32
+DRIFT_FACTOR = 0.25
+DRIFT_STEPS = 10   # free-running comparisons asserted up to this step, reported after it
+TELESCOPE_TOL = 1e-6
 
 
 def say(*a):
@@ -30,13 +59,79 @@ def cpu(t) -> np.ndarray:
     return t.detach().to("cpu").double().numpy()
 
 
+def col_cond(P) -> float:
+    """2-norm condition number of P with its columns scaled to unit norm
+    (Gram-Schmidt is invariant under that scaling); inf with a zero column."""
+    P = np.asarray(P, np.float64)
+    nrm = np.linalg.norm(P, axis=0)
+    if not np.all(nrm > 0):
+        return float("inf")
+    s = np.linalg.svd(P / nrm, compute_uv=False)
+    return float(s[0] / s[-1]) if s[-1] > 0 else float("inf")
+
+
+class DriftTolerance:
+    """Per-tensor free-running tolerance max(REL_TOL, DRIFT_FACTOR u kappa_max)."""
+
+    def __init__(self):
+        self.kappa = {}
+
+    def update(self, ores):
+        for i, P in enumerate(ores.P):
+            if P is not None:
+                self.kappa[i] = max(self.kappa.get(i, 1.0), col_cond(P))
+
+    def tols(self):
+        return {i: max(REL_TOL, DRIFT_FACTOR * U32 * k) for i, k in self.kappa.items()}
+
+
+class Telescope:
+    """Error feedback loses nothing, it only delays ("Error feedback",
+    anthology note on PowerSGD, Concepts): over a trajectory with E_0 = 0,
+    sum_t M_hat_t + E_T = sum_t X_t, X_t the compressor input (G_t, or the
+    momentum u_t).  Each step adds the rounding of M = X + E and of
+    E = M - M_hat, so on the GPU's flat fp32 buffers (accumulated in fp64)
+    the relative error stays at the level of fp32 rounding."""
+
+    def __init__(self, ps):
+        import torch
+
+        self.ps = ps
+        self.sx = torch.zeros(ps.err.numel(), dtype=torch.float64, device=ps.err.device)
+        self.sm = torch.zeros_like(self.sx)
+
+    def add(self):
+        x = self.ps.mom if self.ps.mom is not None else self.ps.grads
+        self.sx += x[: self.sx.numel()].double()
+        self.sm += self.ps.mhat.double()
+
+    def error(self) -> float:
+        d = (self.sm + self.ps.err.double() - self.sx).norm().item()
+        return d / max(self.sx.norm().item(), 1e-300)
+
+
+def snapshot_state(ps, oplan, momentum=False):
+    """The GPU's per-tensor state before a step, as an oracle SetState (for a
+    teacher-forced oracle step)."""
+    comp = [oplan.kinds[i] == oracle.KIND_COMPRESSED for i in range(len(oplan.shapes))]
+    E = [cpu(ps.view(ps.err, i)) if c else None for i, c in enumerate(comp)]
+    Q = [cpu(ps.q_of(i)) if c else None for i, c in enumerate(comp)]
+    u = None
+    if momentum:
+        u = [cpu(ps.view(ps.mom, i)).reshape(oplan.views[i] if oplan.kinds[i] != oracle.KIND_VECTOR else -1)
+             for i in range(len(oplan.shapes))]
+    return oracle.SetState(E=E, Q=Q, u=u)
+
+
 def compare_set(ps, oplan, ores, ostate, idx=None, mhat=True, tol=REL_TOL, tag="", check_e=True):
-    """Compare the GPU buffers of `ps` against one oracle step result."""
+    """Compare the GPU buffers of `ps` against one oracle step result.  `tol`
+    is one tolerance or a dict per tensor index (REL_TOL where missing)."""
     import rank_gradient_compression_amd.binding as B
 
     idx = range(len(oplan.shapes)) if idx is None else idx
     worst = {}
     for i in idx:
+        ti = tol.get(i, REL_TOL) if isinstance(tol, dict) else tol
         if oplan.kinds[i] == oracle.KIND_COMPRESSED:
             Ph = cpu(ps.p_hat(i))
             errs = {"P_hat": rel(Ph, ores.P_hat[i]), "Q": rel(cpu(ps.q_of(i)), ores.Q[i])}
@@ -47,7 +142,7 @@ def compare_set(ps, oplan, ores, ostate, idx=None, mhat=True, tol=REL_TOL, tag="
             orth = oracle.orthonormality_error(Ph)
             assert orth <= ORTH_TOL, f"{tag} tensor {i}: orthonormality {orth:.3e}"
             for k, v in errs.items():
-                assert v <= tol, f"{tag} tensor {i} {ps.shapes[i]}: {k} rel err {v:.3e}"
+                assert v <= ti, f"{tag} tensor {i} {ps.shapes[i]}: {k} rel err {v:.3e} (tolerance {ti:.2e})"
                 worst[k] = max(worst.get(k, 0.0), v)
         else:
             if mhat:

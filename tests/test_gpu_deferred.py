@@ -1,9 +1,12 @@
 """Deferred residual (PSGD_STEP_DEFER_RESIDUAL / PSGD_STEP_RESIDUAL_DEFERRED)
-against the fp64 oracle's ordinary step: P_hat, Q and M_hat every step, the
-M left in the error buffer against the oracle's compressor input, and the
-explicit E once a call ends without deferring.  Also bit-for-bit equality with
-the explicit-residual path on the GPU, since both form the same E with the
-same operations."""
+against the fp64 oracle's ordinary step and the explicit-residual path.
+
+Every step: bit-for-bit equality with the explicit-residual path on the GPU
+(both form the same E with the same operations); the teacher-forced oracle
+step (from the explicit path's E_{t-1} and Q_{t-1}) on P_hat, Q and M_hat at
+1e-4, with the M left in the error buffer against the oracle's compressor
+input, and the explicit E once a call ends without deferring; and the
+free-running oracle at the drift tolerance."""
 import numpy as np
 import pytest
 
@@ -13,7 +16,7 @@ if not torch.cuda.is_available():
 
 import oracle  # noqa: E402
 import workloads as W  # noqa: E402
-from gpu_util import REL_TOL, compare_set, cpu, rel, say  # noqa: E402
+from gpu_util import REL_TOL, DriftTolerance, compare_set, cpu, rel, say, snapshot_state  # noqa: E402
 from rank_gradient_compression_amd.torch_api import PowerSGD  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -24,11 +27,11 @@ SHAPES = [(300, 650), (257, 4099), (97, 1030), (33, 27), (5,), (640, 512), (2, 2
 
 def _run(shapes, rank, steps, beta=None, grads_dtype=torch.float32, seed=0, offsets=None, sgd=False):
     tensors = [(str(i), s) for i, s in enumerate(shapes)]
-    # The k^-1.5 spectrum at ranks above 8 on the 97-row matrix makes P
-    # ill-conditioned enough that fp32 and fp64 differ near the tolerance on
-    # both paths alike; the matrix-core ranks use well-conditioned Gaussian
-    # gradients, as in the other matrix-core parity tests.
-    wl = W.ModelSetWorkload(tensors, "lstm3" if beta is None and rank <= 8 else "plain", seed=seed)
+    # The LSTM-shaped spectrum (sigma_k ~ k^-1.5 plus 5% noise) at every
+    # rank: at ranks of 32 and more, P = M Q of a warm start cancels down to
+    # sigma_k^2 against running sums of order sigma_1 sigma_k, the case the
+    # matrix-core pass 1 sums in fp64.  Momentum runs on Gaussian gradients.
+    wl = W.ModelSetWorkload(tensors, "lstm3" if beta is None else "plain", seed=seed)
     ps = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta, offsets=offsets, grads_dtype=grads_dtype)
     ref = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta, offsets=offsets, grads_dtype=grads_dtype)
     oplan = oracle.Plan(shapes, rank)
@@ -42,6 +45,7 @@ def _run(shapes, rank, steps, beta=None, grads_dtype=torch.float32, seed=0, offs
         x = torch.randn(ps.grads.numel(), device=DEV)
         sgd_kw = dict(params=x.clone(), sgd_buf=torch.zeros_like(x), sgd_lr=0.05, sgd_momentum=0.9)
         sgd_ref = dict(params=x.clone(), sgd_buf=torch.zeros_like(x), sgd_lr=0.05, sgd_momentum=0.9)
+    drift = DriftTolerance()
     for t in range(1, steps + 1):
         grads = [wl.grad(i, t) for i in range(len(shapes))]
         host = [torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to(grads_dtype) for g in grads]
@@ -49,6 +53,7 @@ def _run(shapes, rank, steps, beta=None, grads_dtype=torch.float32, seed=0, offs
         for i, h in enumerate(host):
             ps.view(ps.grads, i).copy_(h.to(DEV))
             ref.view(ref.grads, i).copy_(h.to(DEV))
+        forced = snapshot_state(ref, oplan, momentum=beta is not None)
         last = t == steps
         say(f"[deferred r={rank} beta={beta}] step {t}{' (explicit E at the end)' if last else ''}")
         ps.compress(mhat=True, defer_residual=not last, residual_deferred=t > 1, **sgd_kw)
@@ -64,13 +69,17 @@ def _run(shapes, rank, steps, beta=None, grads_dtype=torch.float32, seed=0, offs
         if beta is not None:
             assert torch.equal(ps.mom, ref.mom)
         res = oracle.step_set(oplan, grads, ost, beta=beta or 0.0)
-        if last:
-            compare_set(ps, oplan, res, ost, tag=f"deferred r={rank} step {t}")
-        else:
-            compare_set(ps, oplan, res, ost, tag=f"deferred r={rank} step {t}", check_e=False)
-            for i in ps.compressed():
-                e = rel(cpu(ps.view(ps.err, i)), res.M[i])
-                assert e <= REL_TOL, f"step {t} tensor {i}: M left in err, rel err {e:.3e}"
+        drift.update(res)
+        gres = oracle.step_set(oplan, grads, forced, beta=beta or 0.0)
+        for name, r, st, tol in (("teacher-forced", gres, forced, REL_TOL), ("free-running", res, ost, drift.tols())):
+            tag = f"deferred r={rank} step {t} ({name})"
+            w = compare_set(ps, oplan, r, st, tag=tag, check_e=last, tol=tol)
+            if not last:
+                for i in ps.compressed():
+                    e = rel(cpu(ps.view(ps.err, i)), r.M[i])
+                    ti = tol.get(i, REL_TOL) if isinstance(tol, dict) else tol
+                    assert e <= ti, f"{tag} tensor {i}: M left in err, rel err {e:.3e}"
+            say(f"[{tag}] " + " ".join(f"{k}={v:.2e}" for k, v in w.items()))
 
 
 @pytest.mark.parametrize("rank", [1, 2, 4, 7, 8, 16, 32, 64])

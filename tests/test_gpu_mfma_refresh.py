@@ -1,6 +1,5 @@
 """Parity of the matrix-core path (ranks 9..64) and of the PowerSGD+ subspace
 refresh with the fp64 oracle."""
-import functools
 
 import numpy as np
 import pytest
@@ -28,6 +27,20 @@ def test_ragged_shapes_matrix_core_ranks(rank):
     run_set_parity(tensors, rank, 2, wl.grad, lambda i: wl.q0(i, rank), tag=f"mfma ragged r={rank}")
 
 
+@pytest.mark.parametrize("rank", [16, 32, 64])
+def test_ill_conditioned_spectrum_matrix_core(rank):
+    """The LSTM-shaped gradients (sigma_k ~ k^-1.5, 5% noise, fresh per step)
+    on the matrix-core ranks, four free-running steps: the rows of 97, 300 and
+    2600 and the 650-column width of the LSTM set, plus a 16-byte-row
+    matrix, every matrix checked at 1e-4 each step.  Warm-started P = M Q
+    cancels down to sigma_k^2 here (the anthology note on PowerSGD,
+    Limitations: transformer models may need ranks of 32 and more)."""
+    shapes = [(97, 1030), (300, 650), (2600, 650), (640, 1024), (650,)]
+    tensors = [(str(i), s) for i, s in enumerate(shapes)]
+    wl = W.ModelSetWorkload(tensors, "lstm3", seed=60 + rank)
+    run_set_parity(tensors, rank, 4, wl.grad, lambda i: wl.q0(i, rank), tag=f"k^-1.5 r={rank}")
+
+
 def test_matrix_core_momentum_and_offsets():
     shapes = [(300, 512), (200, 650)]
     offsets = [1, 300 * 512 + 5]
@@ -36,17 +49,6 @@ def test_matrix_core_momentum_and_offsets():
     run_set_parity(tensors, 16, 3, wl.grad, lambda i: wl.q0(i, 16), beta=0.9, offsets=offsets,
                    tag="mfma momentum offsets")
 
-
-@functools.lru_cache(maxsize=1)
-def sweep_matrix():
-    return W.decaying_spectrum_matrix(11008, 4096, seed=5)
-
-
-@pytest.mark.parametrize("rank", [16, 32, 64])
-def test_rank_sweep_11008x4096_matrix_core(rank):
-    A, V, s = sweep_matrix()
-    q0 = W.gaussian_q0(4096, rank, 5)
-    run_set_parity([("A", (11008, 4096))], rank, 2, lambda i, t: A, lambda i: q0, tag=f"11008x4096 r={rank}")
 
 
 def _refresh_case(m, n, rank, iters, seed):
