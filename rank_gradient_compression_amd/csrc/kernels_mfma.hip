@@ -76,17 +76,17 @@ __device__ __forceinline__ void st4(float* p, int col, int n, bool vec4, float4 
 // clamped, always valid column and zero the value when out of range: no
 // branches, so every load of a step can be in flight at once.  Other rows
 // take the guarded scalar path.
-// Zero a loaded value past the row end, component by component (a
-// conditional on the whole struct is lowered to a select between two stack
-// addresses, i.e. private scratch memory).
-__device__ __forceinline__ float4 keep_if(bool ok, float4 v) {
-  return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
-}
-
+// Values past the row end are zeroed with a select between the loaded value
+// and a zero rvalue, which the compiler can defer to the value's use (so the
+// loads stay in flight together); a select between two struct lvalues
+// (r = ok ? v : r) is lowered to a select of stack addresses, i.e. private
+// scratch, and masking each component right after the load makes the
+// compiler wait for that load there (k_mfma_qt<64> 72 -> 88 us).
 template <bool VEC4>
 __device__ __forceinline__ float4 ldq(const float* rowp, int col, bool ok, int col_safe, int n) {
   if constexpr (VEC4) {
-    return keep_if(ok, *reinterpret_cast<const float4*>(rowp + (ok ? col : col_safe)));
+    const float4 v = *reinterpret_cast<const float4*>(rowp + (ok ? col : col_safe));
+    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
   } else {
     return ld4(rowp, ok ? col : n, n, false);
   }
@@ -100,7 +100,7 @@ template <bool VEC4>
 __device__ __forceinline__ float4 ldq_nt(const float* rowp, int col, bool ok, int col_safe, int n) {
   if constexpr (VEC4) {
     const v4f_nt v = __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(rowp + (ok ? col : col_safe)));
-    return keep_if(ok, make_float4(v[0], v[1], v[2], v[3]));
+    return ok ? make_float4(v[0], v[1], v[2], v[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
   } else {
     return ld4(rowp, ok ? col : n, n, false);
   }
@@ -124,8 +124,9 @@ __device__ __forceinline__ float4 ldq_bf16(const uint16_t* rowp, int col, bool o
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (VEC4) {
     const uint2 t = *reinterpret_cast<const uint2*>(rowp + (ok ? col : col_safe));
-    r = keep_if(ok, make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u),
-                                __uint_as_float(t.y << 16), __uint_as_float(t.y & 0xffff0000u)));
+    const float4 v = make_float4(__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u),
+                                 __uint_as_float(t.y << 16), __uint_as_float(t.y & 0xffff0000u));
+    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
   } else {
     // clamped addresses (col_safe < n), values zeroed past the row end
     const int c = ok ? col : col_safe;

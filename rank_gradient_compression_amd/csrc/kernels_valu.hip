@@ -149,11 +149,16 @@ __device__ __forceinline__ float wave_transpose_sum(float (&v)[NV], int lane) {
   for (int s = 0; s < LOG; ++s) {
     const int bit = 5 - s;
     const int half = NV >> (s + 1);
-    const bool up = (lane >> bit) & 1;
+    // lane-dependent exchange written as bit operations on the two values:
+    // a select between v[i] and v[i + half] is turned by the compiler into a
+    // load through a lane-dependent index, which keeps v an indexable array
+    // (compare-and-select chains over all of it, or private scratch)
+    const uint32_t up = 0u - ((uint32_t)(lane >> bit) & 1u);
 #pragma unroll
     for (int i = 0; i < half; ++i) {
-      const float send = up ? v[i] : v[i + half];
-      const float keep = up ? v[i + half] : v[i];
+      const uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[i + half]);
+      const float send = __uint_as_float((a & up) | (b & ~up));
+      const float keep = __uint_as_float((b & up) | (a & ~up));
       v[i] = keep + __shfl_xor(send, 1 << bit);
     }
   }
@@ -243,6 +248,30 @@ __device__ __forceinline__ Vec<VEC> recon_row(const float (&ph)[R], const Vec<VE
     mh.v[c] = s;
   }
   return mh;
+}
+
+// The kWaveRows x R row sums of a pass-1 wavefront into pdst (column k of m
+// floats), at most 32 values per transposed butterfly (a 64-value one does
+// not stay in registers: it spilled to scratch).  BASE, the first value of
+// this piece, is a template parameter so that every index into acc is a
+// compile-time constant (a run-time index into a register array is lowered
+// to a compare-and-select over all of its elements).
+template <int R, int BASE>
+__device__ __forceinline__ void row_sums(const float (&acc)[kWaveRows][R], int lane, int nrows, int m, int row0,
+                                         float* pdst) {
+  constexpr int NALL = kWaveRows * R;
+  constexpr int NV = pow2_at_least(NALL < 32 ? NALL : 32);
+  constexpr int SHIFT = NV >= 32 ? 1 : NV >= 16 ? 2 : NV >= 8 ? 3 : NV >= 4 ? 4 : NV >= 2 ? 5 : 6;
+  float vals[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) vals[i] = BASE + i < NALL ? acc[(BASE + i) / R][(BASE + i) % R] : 0.f;
+  const float tot = wave_transpose_sum<NV>(vals, lane);
+  const int vi = BASE + (lane >> SHIFT);
+  if ((lane & ((1 << SHIFT) - 1)) == 0 && vi < NALL) {
+    const int rr = vi / R, k = vi % R;
+    if (rr < nrows) pdst[(int64_t)k * m + row0 + rr] = tot;
+  }
+  if constexpr (BASE + NV < NALL) row_sums<R, BASE + NV>(acc, lane, nrows, m, row0, pdst);
 }
 
 // MODE 0: M read from E (plain M Q); 1: M = G + E; 2: u = beta u + G,
@@ -337,23 +366,7 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, in
     }
   }
 
-  // The kWaveRows x R row sums, at most 32 values per transposed butterfly
-  // (a 64-value one does not stay in registers: it spilled to scratch).
-  constexpr int NALL = kWaveRows * R;
-  constexpr int NV = pow2_at_least(NALL < 32 ? NALL : 32);
-  constexpr int SHIFT = NV >= 32 ? 1 : NV >= 16 ? 2 : NV >= 8 ? 3 : NV >= 4 ? 4 : NV >= 2 ? 5 : 6;
-#pragma unroll
-  for (int base = 0; base < NALL; base += NV) {
-    float vals[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) vals[i] = base + i < NALL ? acc[(base + i) / R][(base + i) % R] : 0.f;
-    const float tot = wave_transpose_sum<NV>(vals, lane);
-    const int vi = base + (lane >> SHIFT);
-    if ((lane & ((1 << SHIFT) - 1)) == 0 && vi < NALL) {
-      const int rr = vi / R, k = vi % R;
-      if (rr < nrows) pdst[(int64_t)k * m + row0 + rr] = tot;
-    }
-  }
+  row_sums<R, 0>(acc, lane, nrows, m, row0, pdst);
 }
 
 // Row tile and column range of a pass-1 / pass-3 workgroup: the matrix's
