@@ -9,12 +9,19 @@ the library's HIP kernels.  The gradients are synthetic (seeded rank-16 signal
 plus Gaussian noise, unit Frobenius norm per matrix) and resident in HBM
 before timing starts.
 
-Other workloads (--workload): `sweep` (11008x4096 at ranks 1..64),
-`refresh` (PowerSGD+ refresh, 8 iterations at rank 32 on 8192x8192),
-`resnet18` (rank 2), `lstm3` (rank 4).  Each prints its own JSON line.
+The default run also times the other seeded workloads and nests them in the
+same JSON line under "configs", each with its own roofline (dominant kernel
+named) and the fp64 oracle timed on the host cores beside it: the single
+256x128 matrix at rank 2, the ResNet18-shaped set at rank 2, the LSTM-shaped
+set at rank 4, the 11008x4096 decaying-spectrum matrix at ranks 1..64 and the
+PowerSGD+ refresh (8 rounds at rank 32 on 8192x8192).  --no-configs skips
+them.
 
-Prints ONE JSON line per workload (per rank for the sweep).  `value` is
-gradient GB compressed per second (4 bytes x elements / step time).
+Other workloads (--workload): `single`, `sweep`, `refresh`, `resnet18`,
+`lstm3`, each printed as a JSON line of its own.
+
+`value` is gradient GB compressed per second (4 bytes x elements / step
+time).
 """
 from __future__ import annotations
 
@@ -47,12 +54,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b", choices=["llama7b", "sweep", "refresh", "resnet18", "lstm3"])
+    ap.add_argument("--workload", default="llama7b",
+                    choices=["llama7b", "single", "sweep", "refresh", "resnet18", "lstm3"])
+    ap.add_argument("--no-configs", action="store_true",
+                    help="7B workload: skip the other workloads nested under 'configs'")
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the plain-compress and momentum figures")
     ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--mhat-buffers", type=int, default=0,
+                    help="7B workload: also time the fused step with this many further M_hat buffers, each "
+                         "allocated on its own (the residual pass's speed depends on where M_hat lands)")
     ap.add_argument("--residual", default="explicit", choices=["explicit", "deferred"],
                     help="7B workload: time the step that writes E (default) or the steady-state step with the "
                          "residual deferred into the next step's first pass")
@@ -284,6 +297,8 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
         prof = f"hbm_bytes_llama7b_r4_{'deferred' if deferred else 'fused'}.md" if rank == 4 else None
         res["roofline"] = roofline_of(st, mfma, prof)
         res["stages"] = round_stages(st)
+    if args.mhat_buffers > 0 and not deferred:
+        res["config"]["mhat_buffers"] = mhat_buffer_sweep(torch, B, ps, args.mhat_buffers)
     if not args.no_variants and not deferred:
         ms_c, _ = R.time("compress only", lambda: ps.compress(mhat=False), max(3, args.steps // 2), 1,
                          per_step=False)
@@ -344,7 +359,32 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
         psb.close()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(tensors, rank)
-    print(json.dumps(res), flush=True)
+    return res
+
+
+def mhat_buffer_sweep(torch, B, ps, count, calls=3):
+    """The fused step with `count` further M_hat buffers, each allocated on
+    its own, `calls` calls per buffer, twice round-robin: per-call residual
+    stage time.  The residual pass runs in one of two speeds per buffer
+    (about 12.3 or 13.8 ms on the 7B set), repeatably."""
+    bufs = [torch.empty_like(ps.err) for _ in range(count)]
+    out = [{"buffer": k, "va_offset_from_err": bufs[k].data_ptr() - ps.err.data_ptr(), "residual_ms": []}
+           for k in range(count)]
+    torch.cuda.synchronize()
+    B.psgd_timing_read(ps.plan)
+    B.psgd_timing_enable(ps.plan, True)
+    for _ in range(2):
+        for k, m in enumerate(bufs):
+            for _ in range(calls):
+                ps.compress(mhat_buf=m)
+                ms, _ = B.psgd_timing_read(ps.plan)
+                out[k]["residual_ms"].append(round(ms[B.PSGD_STAGE_RESIDUAL], 3))
+    B.psgd_timing_enable(ps.plan, False)
+    for o in out:
+        log(f"bench: M_hat buffer {o['buffer']}: residual pass {o['residual_ms']} ms")
+    del bufs
+    torch.cuda.empty_cache()
+    return out
 
 
 def device_decaying(torch, W, m, n, seed, K=512):
@@ -360,11 +400,13 @@ def device_decaying(torch, W, m, n, seed, K=512):
     return ((U * s) @ V.T).float()
 
 
-def run_sweep(args, torch, B, W, PowerSGD, R):
+def run_sweep(args, torch, B, W, PowerSGD, R, nested=False):
     m, n = 11008, 4096
-    ranks = [args.rank] if args.rank else [1, 2, 4, 7, 16, 32, 64]
+    ranks = [args.rank] if (args.rank and not nested) else [1, 2, 4, 7, 16, 32, 64]
     A = device_decaying(torch, W, m, n, 5)
-    R.copy_ceiling()  # also the byte-counter calibration of a profiled run
+    if not nested:
+        R.copy_ceiling()  # also the byte-counter calibration of a profiled run
+    out = []
     for r in ranks:
         ps = PowerSGD([(m, n)], r, device="cuda")
         ps.view(ps.grads, 0).copy_(A)
@@ -381,16 +423,22 @@ def run_sweep(args, torch, B, W, PowerSGD, R):
             st = stage_table(B, ps.plan, step_bytes(mfma), step_flops(r), m * n)
             res["roofline"] = roofline_of(st, mfma, f"hbm_bytes_sweep_11008x4096_r{r}.md")
             res["stages"] = round_stages(st)
-        print(json.dumps(res), flush=True)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_sweep(W, m, n, r)
+        out.append(res)
         ps.close()
+    del A
+    torch.cuda.empty_cache()
+    return out
 
 
-def run_refresh(args, torch, B, W, PowerSGD, R):
+def run_refresh(args, torch, B, W, PowerSGD, R, nested=False):
     m = n = 8192
-    r = args.rank or 32
+    r = 32 if nested else (args.rank or 32)
     iters = 8
     A = device_decaying(torch, W, m, n, 5)
-    R.copy_ceiling()  # also the byte-counter calibration of a profiled run
+    if not nested:
+        R.copy_ceiling()  # also the byte-counter calibration of a profiled run
     ps = PowerSGD([(m, n)], r, device="cuda")
     mbuf = torch.zeros_like(ps.grads)
     ps.view(mbuf, 0).copy_(A)
@@ -423,14 +471,48 @@ def run_refresh(args, torch, B, W, PowerSGD, R):
                      per_step=False)
     res["config"]["graph_replay"] = {"ms_per_step": round(ms_g, 4),
                                      "tflops": round(flops / (ms_g * 1e-3) / 1e12, 2)}
-    print(json.dumps(res), flush=True)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_refresh(W, m, n, r, iters)
+    ps.close()
+    del A, mbuf, graph
+    torch.cuda.empty_cache()
+    return res
 
 
-def run_small_set(args, torch, B, W, PowerSGD, R, name):
+def run_single(args, torch, B, W, PowerSGD, R):
+    """The single 256x128 matrix at rank 2 (G = U diag(1/k) V^T + noise)."""
+    wl = W.SmallMatrixWorkload()
+    ps = PowerSGD([(wl.m, wl.n)], wl.rank, device="cuda")
+    ps.view(ps.grads, 0).copy_(torch.from_numpy(wl.grads[0]).cuda())
+    ps.set_q(0, wl.Q0)
+    dense = wl.m * wl.n
+    ms, per = R.time(f"single {wl.m}x{wl.n} r={wl.rank}", lambda: ps.compress(mhat=True), args.steps, args.warmup,
+                     plan=None if args.no_stage_timing else ps.plan)
+    res = base_result(args, 4.0 * dense / (ms * 1e-3) / 1e9, ms, per,
+                      f"one {wl.m}x{wl.n} fp32 matrix, rank {wl.rank}, compress with fused decompression "
+                      "(launch-latency bound: a few tens of kilobytes per step)",
+                      {"rank": wl.rank, "elements": dense})
+    if not args.no_stage_timing:
+        st = stage_table(B, ps.plan, step_bytes(False), step_flops(wl.rank), dense)
+        res["roofline"] = roofline_of(st, False)
+        res["stages"] = round_stages(st)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ps.compress(mhat=True)
+    ms_g, _ = R.time(f"single r={wl.rank}, graph replay", graph.replay, args.steps, args.warmup, per_step=False)
+    res["config"]["graph_replay"] = {"ms_per_step": round(ms_g, 4),
+                                     "grad_gbs": round(4.0 * dense / (ms_g * 1e-3) / 1e9, 3)}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_trajectory(W, "single", wl.rank)
+    ps.close()
+    return res
+
+
+def run_small_set(args, torch, B, W, PowerSGD, R, name, nested=False):
     if name == "resnet18":
-        tensors, kind, seed, rank = W.resnet18_cifar_set(), "resnet18", 2, args.rank or 2
+        tensors, kind, seed, rank = W.resnet18_cifar_set(), "resnet18", 2, (None if nested else args.rank) or 2
     else:
-        tensors, kind, seed, rank = W.lstm3_wikitext_set(), "lstm3", 3, args.rank or 4
+        tensors, kind, seed, rank = W.lstm3_wikitext_set(), "lstm3", 3, (None if nested else args.rank) or 4
     wl = W.ModelSetWorkload(tensors, kind, seed)
     shapes = [s for _, s in tensors]
     ps = PowerSGD(shapes, rank, device="cuda")
@@ -457,7 +539,26 @@ def run_small_set(args, torch, B, W, PowerSGD, R, name):
     ms_g, _ = R.time(f"{name} r={rank}, graph replay", graph.replay, args.steps, args.warmup, per_step=False)
     res["config"]["graph_replay"] = {"ms_per_step": round(ms_g, 4),
                                      "grad_gbs": round(4.0 * dense / (ms_g * 1e-3) / 1e9, 2)}
-    print(json.dumps(res), flush=True)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_trajectory(W, name, rank)
+    ps.close()
+    return res
+
+
+def nested_configs(args, torch, B, W, PowerSGD, R):
+    """The other seeded workloads, each as a result object of its own."""
+    out = {}
+    log("bench: nested workloads")
+    out["single_256x128_r2"] = run_single(args, torch, B, W, PowerSGD, R)
+    out["resnet18_r2"] = run_small_set(args, torch, B, W, PowerSGD, R, "resnet18", nested=True)
+    out["lstm3_r4"] = run_small_set(args, torch, B, W, PowerSGD, R, "lstm3", nested=True)
+    for res in run_sweep(args, torch, B, W, PowerSGD, R, nested=True):
+        out[f"sweep_11008x4096_r{res['config']['rank']}"] = res
+    out["refresh_8192x8192_r32"] = run_refresh(args, torch, B, W, PowerSGD, R, nested=True)
+    for v in out.values():  # nested objects carry what differs from the headline line
+        for k in ("metric", "n_gpus", "higher_is_better", "scaling", "data", "dtype"):
+            v.pop(k, None)
+    return out
 
 
 def cpu_model():
@@ -523,6 +624,118 @@ def cpu_baseline(tensors, rank, budget_s=10.0, cap_s=30.0):
             "host_cores": cores, "cpu_model": cpu_model(), "detail": detail}
 
 
+def blas_threads(default):
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [default])
+    except Exception:  # pragma: no cover
+        return default
+
+
+def cpu_baseline_trajectory(W, name, rank, budget_s=6.0):
+    """The fp64 oracle's steps of a seeded set (the whole set, one step after
+    another from the seeded start, as the GPU runs it) on the host cores,
+    stopped after the step that passes `budget_s` of oracle time (at least 3
+    steps, at most the workload's length); the inputs are drawn outside the
+    timed calls."""
+    import numpy as np
+
+    import oracle
+
+    if name == "single":
+        wl = W.SmallMatrixWorkload()
+        shapes, total = [(wl.m, wl.n)], wl.steps
+        grad = lambda i, t: wl.grads[t - 1]  # noqa: E731
+        q0 = [wl.Q0]
+    else:
+        tensors, kind, seed, total = ((W.resnet18_cifar_set(), "resnet18", 2, 100) if name == "resnet18"
+                                      else (W.lstm3_wikitext_set(), "lstm3", 3, 100))
+        wl = W.ModelSetWorkload(tensors, kind, seed)
+        shapes = [s for _, s in tensors]
+        grad = wl.grad
+        q0 = None
+    plan = oracle.Plan(shapes, rank)
+    if q0 is None:
+        q0 = [wl.q0(i, rank) if plan.kinds[i] == oracle.KIND_COMPRESSED else None for i in range(len(shapes))]
+    spent, steps, reps = 0.0, 0, 0
+    # a trajectory shorter than the budget is run again from its start
+    while spent < min(budget_s, 0.5) or reps == 0:
+        st = oracle.init_state(plan, q0)
+        reps += 1
+        for t in range(1, total + 1):
+            grads = [grad(i, t) for i in range(len(shapes))]
+            t0 = time.perf_counter()
+            oracle.step_set(plan, grads, st)
+            spent += time.perf_counter() - t0
+            steps += 1
+            if steps >= 3 and spent >= budget_s:
+                break
+    dense = plan.dense_elems()
+    cores = len(os.sched_getaffinity(0))
+    what = (f"its whole {total}-step trajectory, {reps} times" if reps > 1 or steps == total
+            else f"the first {steps} of its {total} steps")
+    return {"value": round(4.0 * dense * steps / spent / 1e9, 5), "unit": "GB/s", "cores": int(blas_threads(cores)),
+            "kind": "oracle",
+            "sample": f"fp64 oracle steps of the {name} set at rank {rank} from its seeded start: {what} "
+                      f"({steps} steps, {spent:.2f} s of oracle time, inputs drawn outside the timed calls)",
+            "host_cores": cores}
+
+
+_DECAYING = {}
+
+
+def decaying_host(W, m, n):
+    """The seeded decaying-spectrum matrix in fp64 on the host (cached)."""
+    import numpy as np
+
+    if (m, n) not in _DECAYING:
+        _DECAYING[(m, n)] = W.decaying_spectrum_matrix(m, n, seed=5)[0].astype(np.float64)
+    return _DECAYING[(m, n)]
+
+
+def cpu_baseline_sweep(W, m, n, r, runs=2):
+    """The oracle's step on the decaying-spectrum matrix at rank r (median of
+    `runs`, from the seeded start)."""
+    import numpy as np
+
+    import oracle
+
+    A = decaying_host(W, m, n)
+    q0 = W.gaussian_q0(n, r, 5).astype(np.float64)
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.compress_matrix(A, q0)
+        ts.append(time.perf_counter() - t0)
+    t = statistics.median(ts)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(4.0 * m * n / t / 1e9, 5), "unit": "GB/s", "cores": int(blas_threads(cores)),
+            "kind": "oracle",
+            "sample": f"one fp64 oracle step of the {m}x{n} matrix at rank {r} (first step, E = 0), median of {runs}: "
+                      f"{t:.3f} s",
+            "host_cores": cores}
+
+
+def cpu_baseline_refresh(W, m, n, r, iters):
+    """One cold refresh by the oracle: `iters` rounds from the seeded Q0."""
+    import numpy as np
+
+    import oracle
+
+    A = decaying_host(W, m, n)
+    q0 = W.gaussian_q0(n, r, 5).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.refresh(A, q0, iters)
+    t = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(4.0 * m * n / t / 1e9, 5), "unit": "GB/s", "cores": int(blas_threads(cores)),
+            "kind": "oracle",
+            "sample": f"one cold fp64 oracle refresh of the {m}x{n} matrix at rank {r}, {iters} rounds from the seeded "
+                      f"Q0: {t:.2f} s",
+            "host_cores": cores}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -538,13 +751,23 @@ def main():
     torch.cuda.set_device(0)
     R = Runner(torch, B)
     if args.workload == "llama7b":
-        run_llama7b(args, torch, B, W, PowerSGD, R)
+        # the smaller workloads first, on a device that has not yet held the
+        # 7B set's 108 GB of buffers
+        configs = None if args.no_configs else nested_configs(args, torch, B, W, PowerSGD, R)
+        torch.cuda.empty_cache()
+        res = run_llama7b(args, torch, B, W, PowerSGD, R)
+        if configs is not None:
+            res["configs"] = configs
+        print(json.dumps(res), flush=True)
+    elif args.workload == "single":
+        print(json.dumps(run_single(args, torch, B, W, PowerSGD, R)), flush=True)
     elif args.workload == "sweep":
-        run_sweep(args, torch, B, W, PowerSGD, R)
+        for res in run_sweep(args, torch, B, W, PowerSGD, R):
+            print(json.dumps(res), flush=True)
     elif args.workload == "refresh":
-        run_refresh(args, torch, B, W, PowerSGD, R)
+        print(json.dumps(run_refresh(args, torch, B, W, PowerSGD, R)), flush=True)
     else:
-        run_small_set(args, torch, B, W, PowerSGD, R, args.workload)
+        print(json.dumps(run_small_set(args, torch, B, W, PowerSGD, R, args.workload)), flush=True)
 
 
 if __name__ == "__main__":
