@@ -654,79 +654,6 @@ __global__ __launch_bounds__(256) void k_pass_unpack(const PassDesc* __restrict_
   pass_unpack_wg<SGD>(pass, map, blockIdx.x, Pbuf, out, sg);
 }
 
-// Streaming helpers of the copy and probe kernels: 16-byte non-temporal
-// accesses (the data streams through once), loads at a clamped, always valid
-// index so that they need no branch and all of a thread's loads can be in
-// flight together.
-__device__ __forceinline__ v4f_nt ld_stream(const float4* p, int64_t i, int64_t n4) {
-  return __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(p + (i < n4 ? i : n4 - 1)));
-}
-
-__device__ __forceinline__ void st_stream(float4* p, int64_t i, v4f_nt v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<v4f_nt*>(p + i));
-}
-
-// Plain 16-byte copy: the bandwidth ceiling and counter calibration.  Each
-// thread moves kStreamUnroll vectors per grid step, all loads issued before
-// the stores.
-__global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, const float4* __restrict__ src,
-                                                     int64_t n4) {
-  constexpr int U = kStreamUnroll;
-  const int64_t stride = (int64_t)gridDim.x * 256 * U;
-  for (int64_t i0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x; i0 < n4; i0 += stride) {
-    v4f_nt x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = ld_stream(src, i0 + (int64_t)u * 256, n4);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = i0 + (int64_t)u * 256;
-      if (i < n4) st_stream(dst, i, x[u]);
-    }
-  }
-}
-
-// Streaming-bandwidth probe: the byte pattern of a pass (NIN arrays read,
-// NOUT written) without its arithmetic, out_j[i] = sum_k in_k[i] (zero with
-// no input).  With no output the sums are reduced per workgroup into
-// sink[blockIdx.x], so the loads are not dead.  Each thread moves
-// kStreamUnroll 16-byte vectors per array per grid step, every load of the
-// step issued before the sums, with the access hints of the passes
-// (non-temporal loads and stores).
-template <int NIN, int NOUT>
-__global__ __launch_bounds__(256) void k_stream_probe(ProbeArgs a) {
-  constexpr int U = kStreamUnroll;
-  __shared__ float wsum[4];
-  const int64_t stride = (int64_t)gridDim.x * 256 * U;
-  float part = 0.f;
-  for (int64_t i0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x; i0 < a.n4; i0 += stride) {
-    v4f_nt x[NIN > 0 ? NIN : 1][U];
-#pragma unroll
-    for (int k = 0; k < NIN; ++k)
-#pragma unroll
-      for (int u = 0; u < U; ++u) x[k][u] = ld_stream(a.in[k], i0 + (int64_t)u * 256, a.n4);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v4f_nt v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < NIN; ++k) v += x[k][u];
-      const int64_t i = i0 + (int64_t)u * 256;
-      if constexpr (NOUT == 0) {
-        if (i < a.n4) part += (v[0] + v[1]) + (v[2] + v[3]);
-      } else if (i < a.n4) {
-#pragma unroll
-        for (int j = 0; j < NOUT; ++j) st_stream(a.out[j], i, v);
-      }
-    }
-  }
-  if constexpr (NOUT == 0) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = part;
-    __syncthreads();
-    if (threadIdx.x == 0) a.sink[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  }
-}
-
 // Payload quantiser: every value rounded to the nearest bfloat16 (ties to
 // even), kept in fp32 storage.  Adding 0x7fff plus the lowest kept bit to the
 // fp32 pattern and clearing the low half rounds the magnitude to 8
@@ -886,31 +813,6 @@ hipError_t launch_pass_unpack(const LaunchCtx& c, const float* Pbuf, float* out,
   else
     hipLaunchKernelGGL((k_pass_unpack<false>), dim3(c.wg_pass), dim3(256), 0, c.stream, c.pass, c.pass_map, Pbuf, out,
                        sg);
-  return hipGetLastError();
-}
-
-hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream) {
-  const int64_t n4 = (int64_t)(n / 4);
-  if (n4 == 0) return hipSuccess;
-  int64_t blocks = (n4 + 256 * kStreamUnroll - 1) / (256 * kStreamUnroll);
-  if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
-  hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float4*>(dst),
-                     reinterpret_cast<const float4*>(src), n4);
-  return hipGetLastError();
-}
-
-hipError_t launch_stream_probe(const ProbeArgs& a, int nin, int nout, hipStream_t stream) {
-  if (a.n4 == 0) return hipSuccess;
-  int64_t blocks = (a.n4 + 256 * kStreamUnroll - 1) / (256 * kStreamUnroll);
-  if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
-  const dim3 g((unsigned)blocks), b(256);
-#define PSGD_PROBE(I, O) \
-  if (nin == I && nout == O) hipLaunchKernelGGL((k_stream_probe<I, O>), g, b, 0, stream, a)
-  PSGD_PROBE(0, 1); PSGD_PROBE(0, 2);
-  PSGD_PROBE(1, 0); PSGD_PROBE(1, 1); PSGD_PROBE(1, 2);
-  PSGD_PROBE(2, 0); PSGD_PROBE(2, 1); PSGD_PROBE(2, 2);
-  PSGD_PROBE(3, 0); PSGD_PROBE(3, 1); PSGD_PROBE(3, 2);
-#undef PSGD_PROBE
   return hipGetLastError();
 }
 

@@ -42,6 +42,8 @@ def source_file(kernel: str) -> str:
         return "kernels_mfma.hip"
     if "k_init_q" in k:
         return "kernels_rng.hip"
+    if k.startswith("k_stream"):
+        return "kernels_probe.hip"
     return "kernels_valu.hip"
 
 
