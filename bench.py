@@ -40,9 +40,15 @@ HBM_PEAK_GBS = 8000.0
 MFMA_FP32_PEAK_TFLOPS = 157.3
 KERNEL_OF_STAGE = {"ef_p": "k_ef_p", "mtp": "k_mtp", "residual": "k_recon"}
 KERNEL_OF_STAGE_MFMA = {"ef_p": "k_mfma_p", "mtp": "k_mfma_qt", "residual": "k_mfma_recon"}
-# Byte pattern of each pass (arrays read, arrays written), measured with the
-# library's streaming probe: the practical bandwidth of that pattern.
-PATTERNS = {"r2w1": (2, 1), "r1": (1, 0), "r1w1": (1, 1), "r1w2": (1, 2), "r3w2": (3, 2), "w1": (0, 1)}
+# Byte pattern of each pass (arrays read, arrays written, and for each output
+# the input it overwrites or None), measured with the library's streaming
+# probe: the practical bandwidth of that pattern.  The passes write in place:
+# EF-add stores M over E (and u over u with momentum), the residual stores E
+# over M; the "_sep" forms write separate arrays, for comparison.
+PATTERNS = {"r2w1": (2, 1, (1,)), "r2w1_sep": (2, 1, (None,)), "r1": (1, 0, ()),
+            "r1w1": (1, 1, (0,)), "r1w2": (1, 2, (0, None)), "r1w2_sep": (1, 2, (None, None)),
+            "r3w2": (3, 2, (1, 2)), "r3w2_sep": (3, 2, (None, None)), "w1": (0, 1, (None,))}
+PROBE_PLACEMENTS = 3  # array sets the probe is run on; each pattern's best counts
 
 
 def log(*a):
@@ -208,21 +214,26 @@ class Runner:
         torch.cuda.empty_cache()
         return 8 * n / (ms * 1e-3) / 1e9
 
-    def pattern_ceilings(self, n=1 << 29):
+    def pattern_ceilings(self, n=1 << 29, placements=PROBE_PLACEMENTS):
         """GB/s of bytes moved by the library's streaming probe for each pass
-        pattern in PATTERNS, over n-float arrays (2 GiB each)."""
+        pattern in PATTERNS, over n-float arrays (2 GiB each): the best of
+        `placements` sets of arrays, all allocated before the first is
+        measured so that each set lands in other physical memory (the
+        passes' own speed moves with where their buffers land)."""
         torch, B = self.torch, self.B
-        arrs = [torch.empty(n, dtype=torch.float32, device="cuda").normal_() for _ in range(5)]
+        sets = [[torch.empty(n, dtype=torch.float32, device="cuda").normal_() for _ in range(5)]
+                for _ in range(placements)]
         sink = torch.zeros(B.PSGD_PROBE_SINK_FLOATS, dtype=torch.float32, device="cuda")
         out = {}
-        for name, (nin, nout) in PATTERNS.items():
-            ins = [a.data_ptr() for a in arrs[:nin]]
-            outs = [a.data_ptr() for a in arrs[3:3 + nout]]
-            ms, _ = self.time(f"probe {name}", lambda: B.psgd_stream_probe(ins, outs, n, sink.data_ptr(),
-                                                                          self.stream.cuda_stream), 5, 2,
-                              per_step=False)
-            out[name] = round(4.0 * n * (nin + nout) / (ms * 1e-3) / 1e9, 1)
-        del arrs, sink
+        for t, arrs in enumerate(sets):
+            for name, (nin, nout, alias) in PATTERNS.items():
+                ins = [a.data_ptr() for a in arrs[:nin]]
+                outs = [ins[alias[j]] if alias[j] is not None else arrs[3 + j].data_ptr() for j in range(nout)]
+                ms, _ = self.time(f"probe {name} (arrays {t})",
+                                  lambda: B.psgd_stream_probe(ins, outs, n, sink.data_ptr(), self.stream.cuda_stream),
+                                  5, 2, per_step=False)
+                out[name] = max(out.get(name, 0.0), round(4.0 * n * (nin + nout) / (ms * 1e-3) / 1e9, 1))
+        del sets, sink
         torch.cuda.empty_cache()
         return out
 
@@ -288,7 +299,8 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
                       {"rank": rank, "matrices": len(shapes), "elements": dense, "residual": args.residual,
                        "alg_bytes_per_step": bpe * dense,
                        "step_hbm_frac": round(bpe * dense / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                       "copy_ceiling_gbs": round(copy_gbs, 1), "pattern_ceilings_gbs": ceilings})
+                       "copy_ceiling_gbs": round(copy_gbs, 1), "pattern_ceilings_gbs": ceilings,
+                       "pattern_ceiling_placements": PROBE_PLACEMENTS})
     if not args.no_stage_timing:
         st = stage_table(B, ps.plan, step_bytes(mfma, deferred=deferred), step_flops(rank, deferred=deferred), dense)
         at_ceil = attach_ceilings(st, ceilings, stage_patterns(deferred=deferred))

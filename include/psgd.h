@@ -224,10 +224,14 @@ psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows, const int6
  * uploads, and the timing events). */
 void psgd_plan_destroy(psgd_plan_t plan);
 
-/* Sizes of the plan's buffers; host only. */
+/* Sizes of the plan's buffers; host only.  payload_elems is what one step
+ * transmits: r (m + n) floats per compressed m x n matrix, the factors P_hat
+ * and Q of [GLOSS] factorisation paragraph ([N152] Method: those two are
+ * what the workers exchange), plus every pass-through tensor whole. */
 psgd_status_t psgd_plan_get_info(psgd_plan_t plan, psgd_plan_info_t* info);
 
-/* Where tensor `tensor` lives: kind (PSGD_KIND_*), flat element offset,
+/* Where tensor `tensor` lives: kind (PSGD_KIND_*: [N152] Method sends
+ * vectors and matrices that rank r would not shrink uncompressed), flat element offset,
  * P offset (P_hat start for compressed tensors; start of its values in the
  * pass-through region for others) and Q offset (-1 if not compressed).  Host
  * only.  Any output pointer may be NULL. */
@@ -398,11 +402,15 @@ psgd_status_t psgd_stream_copy(float* dst, const float* src, size_t n, hipStream
  * out[0..nout) of n floats each, out_j[i] = in_0[i] + ... + in_{nin-1}[i]
  * (0 with no input); 0 <= nin <= 3, 0 <= nout <= 2, nin + nout >= 1, n a
  * multiple of 4, every array 16-byte aligned device memory.  With nout = 0
- * the sums are reduced into sink, device memory of PSGD_PROBE_SINK_FLOATS
- * floats (one per workgroup; contents meaningless), so that only the reads
- * reach memory.  `in` and `out` are host arrays of device pointers.  The
- * pattern of each pass: EF-add + P 2 in / 1 out (3 / 2 with momentum),
- * M^T P_hat 1 / 0, residual 1 / 1 (1 / 2 with M_hat), decompression 0 / 1.
+ * the sums are added atomically into sink, device memory of
+ * PSGD_PROBE_SINK_FLOATS floats (several workgroups share a float; if the
+ * sink was zeroed first, its total is the sum of all inputs), so that only
+ * the reads reach memory.  `in` and `out` are host arrays of device pointers; an
+ * output may be one of the inputs (the in-place form, each element read
+ * before it is written by the same thread).  The pattern of each pass:
+ * EF-add + P 2 in / 1 out (3 / 2 with momentum), M^T P_hat 1 / 0, residual
+ * 1 / 1 (1 / 2 with M_hat), decompression 0 / 1; the passes write M over E,
+ * u over u and E over M.
  * Asynchronous on `stream`; PSGD_ERR_INVALID_ARG on bad counts or pointers. */
 #define PSGD_PROBE_SINK_FLOATS 16384
 psgd_status_t psgd_stream_probe(const float* const* in, int32_t nin, float* const* out, int32_t nout, size_t n,

@@ -613,7 +613,7 @@ extern "C" psgd_status_t psgd_timing_read(psgd_plan_t p, double* ms, int64_t* la
 extern "C" psgd_status_t psgd_stream_probe(const float* const* in, int32_t nin, float* const* out, int32_t nout,
                                           size_t n, float* sink, hipStream_t stream) {
   clear_error();
-  static_assert(PSGD_PROBE_SINK_FLOATS == kProbeMaxBlocks, "probe sink size");
+  static_assert(PSGD_PROBE_SINK_FLOATS == kProbeSinkFloats, "probe sink size");
   if (nin < 0 || nin > 3 || nout < 0 || nout > 2 || nin + nout == 0 || (nin > 0 && !in) || (nout > 0 && !out) ||
       (nout == 0 && !sink) || (n & 3u)) {
     set_error("psgd_stream_probe: need 0..3 inputs, 0..2 outputs (at least one array), a sink without outputs "

@@ -24,7 +24,8 @@ __device__ __forceinline__ void st_stream(float4* p, int64_t i, v4f_nt v) {
 
 // Plain 16-byte copy: the bandwidth ceiling and counter calibration.  Each
 // thread moves kStreamUnroll vectors per grid step, all loads issued before
-// the stores.
+// the stores, on at most kCopyMaxBlocks workgroups (the grid-stride form
+// copies 4 GiB at 5.7 TB/s, one run per workgroup at 5.2).
 __global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, const float4* __restrict__ src,
                                                      int64_t n4) {
   constexpr int U = kStreamUnroll;
@@ -45,12 +46,15 @@ __global__ __launch_bounds__(256) void k_stream_copy(float4* __restrict__ dst, c
 // NOUT written) without its arithmetic, out_j[i] = sum_k in_k[i] (zero with
 // no input).  The arrays are viewed as rows of kProbeRowVec 16-byte vectors
 // (a 4096-column fp32 matrix) and walked with the geometry of the streaming
-// passes: a workgroup owns kRowsPerWG rows x one kRecSplitCols-column split
-// (splits fastest), each wavefront kWaveRows rows of it, one 16-byte access
-// per lane and row (a 1 KB row segment per instruction), every load of the
-// wavefront issued before its sums and stores, with the passes' access hints
-// (non-temporal loads and stores).  With no output the sums are reduced per
-// workgroup into sink[blockIdx.x], so the loads are not dead.
+// passes: a workgroup owns one tile of kRowsPerWG rows x one
+// kRecSplitCols-column split (splits fastest, one tile per workgroup and no
+// grid-stride loop: a capped grid that loops made the resident workgroups
+// touch tiles far apart and cost 5-10% on patterns that read and write),
+// each wavefront kWaveRows rows of it, one 16-byte access per lane and row
+// (a 1 KB row segment per instruction), every load of the wavefront issued
+// before its sums and stores, with non-temporal loads and stores.  With no
+// output the sums are reduced per wavefront and added into
+// sink[blockIdx.x % kProbeSinkFloats], so the loads are not dead.
 constexpr int64_t kProbeRowVec = 1024;
 constexpr int kProbeSplitVec = kRecSplitCols / 4;  // 16-byte vectors per row segment (one per lane)
 static_assert(kProbeSplitVec == 64, "one vector per lane and row");
@@ -58,44 +62,33 @@ static_assert(kProbeSplitVec == 64, "one vector per lane and row");
 template <int NIN, int NOUT>
 __global__ __launch_bounds__(kWGThreads) void k_stream_probe(ProbeArgs a) {
   constexpr int SPLITS = (int)(kProbeRowVec / kProbeSplitVec);
-  __shared__ float wsum[kWavesPerWG];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t rows = (a.n4 + kProbeRowVec - 1) / kProbeRowVec;
-  const int64_t tiles = (rows + kRowsPerWG - 1) / kRowsPerWG * SPLITS;
+  const int64_t t = blockIdx.x;
+  const int64_t row0 = (t / SPLITS) * kRowsPerWG + (int64_t)wave * kWaveRows;
+  const int64_t col = (t % SPLITS) * kProbeSplitVec + lane;
+  v4f_nt x[NIN > 0 ? NIN : 1][kWaveRows];
+#pragma unroll
+  for (int k = 0; k < NIN; ++k)
+#pragma unroll
+    for (int rr = 0; rr < kWaveRows; ++rr) x[k][rr] = ld_stream(a.in[k], (row0 + rr) * kProbeRowVec + col, a.n4);
   float part = 0.f;
-  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-    const int64_t row0 = (t / SPLITS) * kRowsPerWG + (int64_t)wave * kWaveRows;
-    const int64_t col = (t % SPLITS) * kProbeSplitVec + lane;
-    v4f_nt x[NIN > 0 ? NIN : 1][kWaveRows];
 #pragma unroll
-    for (int k = 0; k < NIN; ++k)
+  for (int rr = 0; rr < kWaveRows; ++rr) {
+    const int64_t i = (row0 + rr) * kProbeRowVec + col;
+    v4f_nt v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rr = 0; rr < kWaveRows; ++rr) x[k][rr] = ld_stream(a.in[k], (row0 + rr) * kProbeRowVec + col, a.n4);
+    for (int k = 0; k < NIN; ++k) v += x[k][rr];
+    if constexpr (NOUT == 0) {
+      if (i < a.n4) part += (v[0] + v[1]) + (v[2] + v[3]);
+    } else if (i < a.n4) {
 #pragma unroll
-    for (int rr = 0; rr < kWaveRows; ++rr) {
-      const int64_t i = (row0 + rr) * kProbeRowVec + col;
-      v4f_nt v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < NIN; ++k) v += x[k][rr];
-      if constexpr (NOUT == 0) {
-        if (i < a.n4) part += (v[0] + v[1]) + (v[2] + v[3]);
-      } else if (i < a.n4) {
-#pragma unroll
-        for (int j = 0; j < NOUT; ++j) st_stream(a.out[j], i, v);
-      }
+      for (int j = 0; j < NOUT; ++j) st_stream(a.out[j], i, v);
     }
   }
   if constexpr (NOUT == 0) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-    if (lane == 0) wsum[wave] = part;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float tot = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWavesPerWG; ++w) tot += wsum[w];
-      a.sink[blockIdx.x] = tot;
-    }
+    if (lane == 0) atomicAdd(&a.sink[blockIdx.x % kProbeSinkFloats], part);
   }
 }
 
@@ -103,7 +96,7 @@ hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_
   const int64_t n4 = (int64_t)(n / 4);
   if (n4 == 0) return hipSuccess;
   int64_t blocks = (n4 + 256 * kStreamUnroll - 1) / (256 * kStreamUnroll);
-  if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
+  if (blocks > kCopyMaxBlocks) blocks = kCopyMaxBlocks;
   hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float4*>(dst),
                      reinterpret_cast<const float4*>(src), n4);
   return hipGetLastError();
@@ -112,8 +105,8 @@ hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_
 hipError_t launch_stream_probe(const ProbeArgs& a, int nin, int nout, hipStream_t stream) {
   if (a.n4 == 0) return hipSuccess;
   const int64_t rows = (a.n4 + kProbeRowVec - 1) / kProbeRowVec;
-  int64_t blocks = (rows + kRowsPerWG - 1) / kRowsPerWG * (kProbeRowVec / kProbeSplitVec);
-  if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
+  const int64_t blocks = (rows + kRowsPerWG - 1) / kRowsPerWG * (kProbeRowVec / kProbeSplitVec);
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const dim3 g((unsigned)blocks), b(kWGThreads);
 #define PSGD_PROBE(I, O) \
   if (nin == I && nout == O) hipLaunchKernelGGL((k_stream_probe<I, O>), g, b, 0, stream, a)

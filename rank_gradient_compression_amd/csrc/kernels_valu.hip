@@ -62,8 +62,9 @@ __device__ __forceinline__ void stv(float* p, const Vec<VEC>& a) {
 // caches the line will not be reused soon.  Measured on the grouped 7B-shaped
 // set: streaming loads of G and of M in the residual pass and streaming
 // stores of M_hat and E there shave a few percent off a step (E is read
-// again only by the next step); a streaming store of M in pass 1 costs (the
-// next pass reads it).
+// again only by the next step).  In pass 1, streaming loads of E and a
+// streaming store of M pay together with 256-column splits (14.8 -> 13.4 ms
+// with both) and cost with 1024-column ones.
 typedef float v4f_nt __attribute__((ext_vector_type(4)));
 typedef float v2f_nt __attribute__((ext_vector_type(2)));
 typedef uint32_t v2u_nt __attribute__((ext_vector_type(2)));
@@ -94,6 +95,21 @@ __device__ __forceinline__ Vec<VEC> ldv_nt(const float* p) {
     r.v[0] = __builtin_nontemporal_load(p);
   }
   return r;
+}
+
+// Loads and stores of the arrays a pass streams through (E, M, u), with the
+// non-temporal hint when NT: for sets far larger than the caches, where no
+// pass finds the previous one's lines anyway.
+template <int VEC, bool NT>
+__device__ __forceinline__ Vec<VEC> ldv_s(const float* p) {
+  if constexpr (NT) return ldv_nt<VEC>(p);
+  else return ldv<VEC>(p);
+}
+
+template <int VEC, bool NT>
+__device__ __forceinline__ void stv_s(float* p, const Vec<VEC>& a) {
+  if constexpr (NT) stv_nt<VEC>(p, a);
+  else stv<VEC>(p, a);
 }
 
 // Gradient loads: fp32, or bfloat16 widened exactly to fp32 (the upper 16
@@ -280,7 +296,7 @@ __device__ __forceinline__ void row_sums(const float (&acc)[kWaveRows][R], int l
 // Q, so E = M_prev - P_hat Q^T is formed here on the fly; 5: M = G + E,
 // 6: u = beta u + G, M = u + E.  Modes 1..6 store M over E.  Pold may be P
 // itself: each wavefront reads its rows of Pold before writing them in P.
-template <int R, int VEC, int MODE, bool GBF16>
+template <int R, int VEC, int MODE, bool GBF16, bool NT>
 __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, int c1, int lane,
                                           const void* __restrict__ G, float* __restrict__ E, float* __restrict__ U,
                                           float beta, const float* __restrict__ Q, float* pdst, const float* Pold) {
@@ -329,12 +345,12 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, in
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
       if constexpr (MODE != 0) g[rr] = ldg<VEC, GBF16>(at_row_g(grow[rr], j, GBF16), 0u);
-      if constexpr (LOAD_E) e[rr] = ldv<VEC>(at_row(erow[rr], j));
+      if constexpr (LOAD_E) e[rr] = ldv_s<VEC, NT>(at_row(erow[rr], j));
     }
     Vec<VEC> u[kWaveRows];
     if constexpr (MOM) {
 #pragma unroll
-      for (int rr = 0; rr < kWaveRows; ++rr) u[rr] = ldv<VEC>(at_row(urow[rr], j));
+      for (int rr = 0; rr < kWaveRows; ++rr) u[rr] = ldv_s<VEC, NT>(at_row(urow[rr], j));
     }
 #pragma unroll
     for (int rr = 0; rr < kWaveRows; ++rr) {
@@ -350,14 +366,14 @@ __device__ __forceinline__ void ef_p_wave(const MatDesc& d, int row0, int c0, in
         } else if constexpr (MOM) {
 #pragma unroll
           for (int c = 0; c < VEC; ++c) u[rr].v[c] = fmaf(beta, u[rr].v[c], g[rr].v[c]);
-          stv<VEC>(at_row(urow[rr], j), u[rr]);
+          stv_s<VEC, NT>(at_row(urow[rr], j), u[rr]);
 #pragma unroll
           for (int c = 0; c < VEC; ++c) mv.v[c] = LOAD_E ? u[rr].v[c] + e[rr].v[c] : u[rr].v[c];
         } else {
 #pragma unroll
           for (int c = 0; c < VEC; ++c) mv.v[c] = LOAD_E ? g[rr].v[c] + e[rr].v[c] : g[rr].v[c];
         }
-        if constexpr (MODE != 0) stv<VEC>(at_row(erow[rr], j), mv);
+        if constexpr (MODE != 0) stv_s<VEC, NT>(at_row(erow[rr], j), mv);
 #pragma unroll
         for (int k = 0; k < R; ++k)
 #pragma unroll
@@ -386,7 +402,8 @@ __device__ __forceinline__ RowTile row_tile(const MatDesc& d, int local, int spl
 // afterwards in fixed order) at the plan's offsets or at p_fixed.
 // Workgroups from nrow_wg on pack the pass-through tensors (the launch's
 // extra workgroups, when pack_dst is given).
-template <int R, int MODE, bool GBF16>
+// NT: streaming hints on E, M and u (sets far larger than the caches).
+template <int R, int MODE, bool GBF16, bool NT>
 __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__ mats,
                                                      const int32_t* __restrict__ map, int wg_base,
                                                      const void* __restrict__ G, float* __restrict__ E,
@@ -410,11 +427,11 @@ __global__ __launch_bounds__(kWGThreads) void k_ef_p(const MatDesc* __restrict__
   if (t.row0 >= d.m) return;
   float* pdst = d.s1 > 1 ? ppart + d.ppart_off + (int64_t)t.split * R * d.m : P + (p_fixed >= 0 ? p_fixed : d.p_off);
   if (d.vec == 4)
-    ef_p_wave<R, 4, MODE, GBF16>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
+    ef_p_wave<R, 4, MODE, GBF16, NT>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
   else if (d.vec == 2)
-    ef_p_wave<R, 2, MODE, GBF16>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
+    ef_p_wave<R, 2, MODE, GBF16, NT>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
   else
-    ef_p_wave<R, 1, MODE, GBF16>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
+    ef_p_wave<R, 1, MODE, GBF16, NT>(d, t.row0, t.c0, t.c1, lane, G, E, U, beta, Q, pdst, Pold);
 }
 
 // ---------------------------------------------------------------------------
@@ -690,8 +707,16 @@ static hipError_t launch_ef_p_rg(const LaunchCtx& c, const GridRange& g, int mod
   const int extra = c.pack_dst ? c.wg_pass : 0;
   if (g.count + extra == 0) return hipSuccess;
   const dim3 gr(g.count + extra), b(kWGThreads);
-#define PSGD_EFP(MD)                                                                                            \
-  hipLaunchKernelGGL((k_ef_p<R, MD, GBF16>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, \
+#define PSGD_EFP(MD)              \
+  do {                            \
+    if (c.stream_hint) {          \
+      PSGD_EFP_NT(MD, true);      \
+    } else {                      \
+      PSGD_EFP_NT(MD, false);     \
+    }                             \
+  } while (0)
+#define PSGD_EFP_NT(MD, NT_)                                                                                      \
+  hipLaunchKernelGGL((k_ef_p<R, MD, GBF16, NT_>), gr, b, 0, c.stream, c.mats, c.rows_map, g.base, G, E, U, beta, Q, P, \
                      p_fixed, c.p_prev, static_cast<float*>(c.ppart), g.count, c.pass, c.pass_map, c.pack_dst)
   switch (mode) {
     case 1: PSGD_EFP(1); break;
@@ -702,6 +727,7 @@ static hipError_t launch_ef_p_rg(const LaunchCtx& c, const GridRange& g, int mod
     default: PSGD_EFP(6); break;
   }
 #undef PSGD_EFP
+#undef PSGD_EFP_NT
   return hipGetLastError();
 }
 
@@ -710,8 +736,14 @@ static hipError_t launch_ef_p_r(const LaunchCtx& c, const GridRange& g, int mode
                                 float beta, const float* Q, float* P, int64_t p_fixed) {
   if (mode == 0) {  // P = M Q with M read from E: no gradient involved, no packing
     if (g.count == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_ef_p<R, 0, false>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats, c.rows_map,
-                       g.base, G, E, U, beta, Q, P, p_fixed, nullptr, static_cast<float*>(c.ppart), g.count, c.pass, c.pass_map, nullptr);
+    if (c.stream_hint)
+      hipLaunchKernelGGL((k_ef_p<R, 0, false, true>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats,
+                         c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed, nullptr, static_cast<float*>(c.ppart),
+                         g.count, c.pass, c.pass_map, nullptr);
+    else
+      hipLaunchKernelGGL((k_ef_p<R, 0, false, false>), dim3(g.count), dim3(kWGThreads), 0, c.stream, c.mats,
+                         c.rows_map, g.base, G, E, U, beta, Q, P, p_fixed, nullptr, static_cast<float*>(c.ppart),
+                         g.count, c.pass, c.pass_map, nullptr);
     return hipGetLastError();
   }
   return c.g_bf16 ? launch_ef_p_rg<R, true>(c, g, mode, G, E, U, beta, Q, P, p_fixed)

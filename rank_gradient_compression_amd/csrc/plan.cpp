@@ -219,11 +219,12 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
   const int32_t rb = choose_rb_rows(p->mats, r, mfma);
   // Column splits of passes 1 and 3.  A wavefront streams a few rows of its
   // split, so the split width sets how much of each array a workgroup
-  // touches at once: pass 1 in kEfpSplitCols-column pieces (halved, down to
-  // 256 columns, while the grid is short of kRowTilesTarget workgroups, as
-  // for a set of few, short matrices), pass 3 in kRecSplitCols-column pieces.
+  // touches at once: pass 1 in kEfpSplitCols-column pieces on the vector
+  // path, kEfpSplitColsMfma on the matrix cores (halved, down to 256
+  // columns, while the grid is short of kRowTilesTarget workgroups, as for a
+  // set of few, short matrices), pass 3 in kRecSplitCols-column pieces.
   const int32_t tile_rows = mfma ? kMfmaRows : kRowsPerWG;
-  int32_t w1 = kEfpSplitCols;
+  int32_t w1 = mfma ? kEfpSplitColsMfma : kEfpSplitCols;
   for (;; w1 /= 2) {
     int64_t wgs = 0;
     for (const MatDesc& d : p->mats) {

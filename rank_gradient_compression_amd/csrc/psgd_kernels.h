@@ -113,11 +113,12 @@ hipError_t launch_round_bf16(float* buf, int64_t n, hipStream_t stream);
 hipError_t launch_stream_copy(float* dst, const float* src, size_t n, hipStream_t stream);
 
 // Streaming-bandwidth probe (psgd_stream_probe): up to 3 inputs, 2 outputs,
-// n4 16-byte vectors each; sink holds one float per workgroup when there is
-// no output.  The copy and the probe move kStreamUnroll vectors per array and
-// thread per grid step, on at most kProbeMaxBlocks workgroups.
+// n4 16-byte vectors each; without outputs each wavefront adds its sum into
+// one of the sink's kProbeSinkFloats floats.  The copy moves kStreamUnroll
+// vectors per thread and grid step on at most kCopyMaxBlocks workgroups.
 constexpr int kStreamUnroll = 8;
-constexpr int kProbeMaxBlocks = 16384;
+constexpr int kProbeSinkFloats = 16384;
+constexpr int kCopyMaxBlocks = 16384;
 struct ProbeArgs {
   const float4* in[3];
   float4* out[2];

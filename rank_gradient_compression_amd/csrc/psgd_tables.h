@@ -100,13 +100,18 @@ constexpr int kRedWaves = 16;     // wavefronts of one Q-reduce workgroup
 constexpr int kRowTilesTarget = 1024;
 
 // Column splits of passes 1 and 3.  A workgroup streams a few rows of its
-// split, so the split width sets how much of each array it touches at once:
-// pass 1 (two arrays read, one written, plus the P row sums at the end) is
-// split into kEfpSplitCols-column pieces (narrower, down to 256 columns,
-// while the grid is short of kRowTilesTarget workgroups), the residual pass
-// (one read, two written, nothing to reduce) into kRecSplitCols-column
-// pieces, each with its own grid.
-constexpr int kEfpSplitCols = 1024;
+// split, so the split width sets how much of each array it touches at once.
+// On the vector path pass 1 (two arrays read, one written, plus the P row
+// sums at the end) and the residual pass (one read, two written) both take
+// one 256-column piece per wavefront row: a workgroup is one 32-row x
+// 256-column tile, and the grid's dispatch order walks the arrays as one
+// contiguous front (1024-column pass-1 splits were 10% slower on the 7B-shaped
+// set once its loads and stores stream).  The matrix-core pass 1 keeps
+// kEfpSplitColsMfma-column splits (narrower, down to 256 columns, while the
+// grid is short of kRowTilesTarget workgroups): its column-split partials of
+// P are r fp64 values per row and split.
+constexpr int kEfpSplitCols = 256;
+constexpr int kEfpSplitColsMfma = 1024;
 constexpr int kRecSplitCols = 256;
 
 // Header at the start of the workspace.

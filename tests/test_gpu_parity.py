@@ -367,6 +367,36 @@ def test_stream_probe(nin, nout):
         assert abs(got - want.sum().item()) <= 1e-3 * max(1.0, want.abs().sum().item() / n ** 0.5)
 
 
+def test_stream_probe_sink_shared_by_workgroups():
+    """More workgroups than sink floats: the wavefront sums still add up to
+    the total."""
+    n = (1 << 27) + 4 * 37
+    x = torch.randn(n, device=DEV)
+    sink = torch.zeros(B.PSGD_PROBE_SINK_FLOATS, device=DEV)
+    B.psgd_stream_probe([x.data_ptr()], [], n, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    want = x.double().sum().item()
+    assert abs(sink.double().sum().item() - want) <= 1e-3 * max(1.0, x.abs().double().sum().item() / n ** 0.5)
+    del x
+
+
+@pytest.mark.parametrize("nin,nout,alias", [(1, 1, (0,)), (2, 1, (1,)), (1, 2, (0, None)), (3, 2, (1, 2))])
+def test_stream_probe_in_place(nin, nout, alias):
+    """The in-place forms of the passes' patterns: an output that is one of
+    the inputs ends as the sum of the inputs' values before the call."""
+    n = (1 << 20) + 4 * 37
+    ins = [torch.randn(n, device=DEV) for _ in range(nin)]
+    want = sum(t.double() for t in ins)
+    extra = [torch.full((n,), 7.0, device=DEV) for _ in range(nout)]
+    outs = [ins[alias[j]] if alias[j] is not None else extra[j] for j in range(nout)]
+    sink = torch.zeros(B.PSGD_PROBE_SINK_FLOATS, device=DEV)
+    B.psgd_stream_probe([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, sink.data_ptr(),
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.allclose(o.double(), want, rtol=0, atol=1e-5)
+
+
 def test_empty_and_vector_only_plans_run():
     ps = PowerSGD([(5,), (7,)], 2, device=DEV)
     ps.view(ps.grads, 0).fill_(1.0)
