@@ -739,7 +739,8 @@ __global__ __launch_bounds__(256) void k_mfma_recon(const MatDesc* __restrict__ 
 // the cancellation in R_kk^2 = A_kk - sum_j R_jk^2 is harmless at fp32 output
 // precision and the threshold is decided reliably.  Four launches, all
 // grouped over the matrices:
-//   k_gram_partial  A_b = P_b^T P_b over blocks of kGramRows rows
+//   k_gram_partial  A_b = P_b^T P_b over blocks of kGramRows rows (the
+//                   upper block triangle; A is symmetric)
 //   k_gram_reduce   A = sum_b A_b in block order
 //   k_gram_solve    R by right-looking Cholesky with the dependence rule
 //   k_apply_t       P_hat rows by forward substitution, x R = p, in fp64
@@ -761,9 +762,10 @@ constexpr int kGramChunk = kGramRows;  // rows staged in LDS at a time
 
 // A_b = P_b^T P_b for one block of kGramRows rows on the fp64 matrix core
 // (v_mfma_f64_16x16x4f64; each fp32 product is exact in fp64).  The block is
-// staged in LDS; the (RP/16)^2 16 x 16 tiles of A_b are dealt round-robin to
-// the four wavefronts, each summing its tiles over the block's rows in
-// order, four rows per matrix-core step.
+// staged in LDS; the 16 x 16 tiles (ta, tb) of A_b with ta <= tb (A is
+// symmetric: the Cholesky reads the lower block triangle from the upper) are
+// dealt round-robin to the four wavefronts, each summing its tiles over the
+// block's rows in order, four rows per matrix-core step.
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 template <int RP>
@@ -795,8 +797,17 @@ __global__ __launch_bounds__(256) void k_gram_partial(const OrthDesc* __restrict
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, ls = lane >> 4;
   double* g = gram + o.gram_off + (int64_t)local * RP * RP;
-  for (int u = wave; u < NT * NT; u += 4) {
-    const int ta = u / NT, tb = u % NT;
+  constexpr int NUT = NT * (NT + 1) / 2;  // upper tiles, row by row
+  for (int u = wave; u < NUT; u += 4) {
+    int ta = 0, rem = u;  // tile row ta holds NT - ta tiles
+#pragma unroll
+    for (int a = 0; a < NT - 1; ++a) {
+      if (ta == a && rem >= NT - a) {
+        rem -= NT - a;
+        ta = a + 1;
+      }
+    }
+    const int tb = ta + rem;
     v4d acc = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
     for (int kk = 0; kk < kGramChunk / 4; ++kk) {
@@ -889,10 +900,18 @@ __global__ __launch_bounds__(64) void k_gram_solve(const OrthDesc* __restrict__ 
   const int j = threadIdx.x;
   const bool own = j < RP;
   double* a = gram + o.t_off;
+  // A's lower block triangle is read from the upper one (only its 16 x 16
+  // tiles with ta <= tb are accumulated); every load at a valid address, the
+  // value selected afterwards
+  const int jc = min(j, RP - 1);
   double sc[RP];
 #pragma unroll
-  for (int i = 0; i < RP; ++i) sc[i] = own ? a[i * RP + j] : 0.0;
-  const double dgj = own ? a[j * RP + j] : 0.0;  // A_jj: squared norm before projection
+  for (int i = 0; i < RP; ++i) {
+    const double v = a[(i >> 4) <= (jc >> 4) ? i * RP + jc : jc * RP + i];
+    sc[i] = own ? v : 0.0;
+  }
+  const double dv = a[jc * RP + jc];
+  const double dgj = own ? dv : 0.0;  // A_jj: squared norm before projection
   const double zr2 = (double)zero_rel * (double)zero_rel;
   int nzero = 0;  // wavefront-uniform
   // Fully unrolled so that sc[] stays in registers; steps k >= r are skipped

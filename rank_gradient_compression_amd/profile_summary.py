@@ -4,6 +4,15 @@
     python -m rank_gradient_compression_amd.profile_summary bytes FETCH_CSV WRITE_CSV "CMD_FETCH" "CMD_WRITE" "TITLE"
     python -m rank_gradient_compression_amd.profile_summary dispatches KERNEL TRACE_CSV "CMD_TRACE"
         COUNTER_CSV "CMD_COUNTERS" [COUNTER_CSV "CMD_COUNTERS" ...] "TITLE"
+    python -m rank_gradient_compression_amd.profile_summary counters COUNTER_CSV "CMD" [COUNTER_CSV "CMD" ...]
+        "TITLE"
+
+`counters` averages every counter of one or more `--pmc` runs per dispatch of
+each library kernel, and derives the matrix-core busy fraction (of SIMD
+cycles while the kernel runs), the matrix-core fp32 / fp64 flops (512 per
+MOPS count), LDS
+bank-conflict cycles per LDS instruction and the share of wave time spent
+waiting to issue, where the counters they need are present.
 
 `dispatches` lists every dispatch of one kernel in launch order: its duration
 from a `--kernel-trace` kernel_trace.csv and its counters from one or more
@@ -153,6 +162,59 @@ def dispatches(kernel: str, trace_csv: str, cmd_trace: str, counter_runs, title:
     return "\n".join(out) + "\n"
 
 
+N_CU = 256  # compute units of the device the counters are read on (MI355X)
+N_XCD = 8   # its accelerator dies: GRBM_GUI_ACTIVE is summed over them
+
+
+def counters(runs, title: str) -> str:
+    """Mean per dispatch of every counter of the given `--pmc` runs, per
+    library kernel, with derived figures (see the module docstring)."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    order = []
+    for path, _ in runs:
+        per = collections.defaultdict(dict)
+        for r in csv.DictReader(open(path)):
+            if "psgd" not in r["Kernel_Name"]:
+                continue
+            per[(short(r["Kernel_Name"]), int(r["Dispatch_Id"]))][r["Counter_Name"]] = float(r["Counter_Value"])
+        for (k, _), cs in per.items():
+            if k not in order:
+                order.append(k)
+            for c, v in cs.items():
+                vals[k][c].append(v)
+    names = sorted({c for k in vals for c in vals[k]})
+    out = [f"# {title}\n", "Commands (one counter set per run):\n",
+           "```\n" + "\n".join(c for _, c in runs) + "\n```\n",
+           "Mean per dispatch.  Derived: matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / "
+           f"{N_XCD} dies x {N_CU} CUs x 4 SIMDs) (the busy count is 32 cycles per 16x16x4 fp32 instruction, "
+           "summed over the SIMDs; GRBM_GUI_ACTIVE is summed over the dies); fp32 / fp64 matrix-core GFLOP = "
+           "512 x SQ_INSTS_VALU_MFMA_MOPS_F32 / F64; "
+           "LDS conflict cycles per LDS instruction = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS; issue wait = "
+           "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (both in quad-cycles).\n"]
+    derived = [("MFMA busy", lambda m: m["SQ_VALU_MFMA_BUSY_CYCLES"] / (m["GRBM_GUI_ACTIVE"] / N_XCD * N_CU * 4),
+                "{:.1%}"),
+               ("MFMA f32 GFLOP", lambda m: 512 * m["SQ_INSTS_VALU_MFMA_MOPS_F32"] / 1e9, "{:.3f}"),
+               ("MFMA f64 GFLOP", lambda m: 512 * m["SQ_INSTS_VALU_MFMA_MOPS_F64"] / 1e9, "{:.3f}"),
+               ("LDS conflict cyc / LDS inst", lambda m: m["SQ_LDS_BANK_CONFLICT"] / m["SQ_INSTS_LDS"], "{:.3f}"),
+               ("issue wait", lambda m: m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"], "{:.1%}")]
+    rows = []
+    for k in order:
+        m = {c: statistics.mean(v) for c, v in vals[k].items()}
+        cells = [f"`{k}`", str(max(len(v) for v in vals[k].values()))]
+        dcells = []
+        for _, f, fmt in derived:
+            try:
+                dcells.append(fmt.format(f(m)))
+            except (KeyError, ZeroDivisionError):
+                dcells.append("")
+        cells += dcells + [f"{m[c]:.4g}" if c in m else "" for c in names]
+        rows.append("| " + " | ".join(cells) + " |")
+    head = ["kernel", "dispatches"] + [d[0] for d in derived] + names
+    out += ["| " + " | ".join(head) + " |", "|---" * len(head) + "|"] + rows
+    out.append("\nSummarised by `python -m rank_gradient_compression_amd.profile_summary counters`.")
+    return "\n".join(out) + "\n"
+
+
 def main(argv) -> int:
     if len(argv) >= 5 and argv[1] == "trace":
         sys.stdout.write(trace(argv[2], argv[3], argv[4]))
@@ -163,6 +225,10 @@ def main(argv) -> int:
     if len(argv) >= 8 and argv[1] == "dispatches" and len(argv) % 2 == 0:
         runs = [(argv[i], argv[i + 1]) for i in range(5, len(argv) - 1, 2)]
         sys.stdout.write(dispatches(argv[2], argv[3], argv[4], runs, argv[-1]))
+        return 0
+    if len(argv) >= 5 and argv[1] == "counters" and len(argv) % 2 == 1:
+        runs = [(argv[i], argv[i + 1]) for i in range(2, len(argv) - 1, 2)]
+        sys.stdout.write(counters(runs, argv[-1]))
         return 0
     sys.stderr.write(__doc__)
     return 2
