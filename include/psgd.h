@@ -374,6 +374,42 @@ psgd_status_t psgd_init_q(psgd_plan_t plan, float* q, uint64_t seed, void* works
                           hipStream_t stream);
 
 /*
+ * Diagnostics (outside the step; each reads the buffers it is given and
+ * writes fp64 results in the order of the plan's compressed tensors, like
+ * zero_cols; sums in a fixed order, so repeated calls agree bit for bit).
+ *
+ * psgd_step_stats -- after a compress with the fused decompression:
+ * out[2k] = ||E_k||_F^2 and out[2k + 1] = ||M_hat_k + E_k||_F^2 = ||M_k||_F^2
+ * (to the rounding of the residual) for compressed matrix k, so that
+ * sqrt(out[2k] / out[2k + 1]) is the share of the compressor's input that
+ * error feedback carries to later steps ([GLOSS] error-feedback paragraph:
+ * e_t = G_t - compress(G_t)).  err and mhat: the flat buffers of that call
+ * (with a deferred residual err holds M, not E: call it on an explicit-
+ * residual step).  out: 2 * ncompressed doubles, device or pinned host
+ * memory, 8-byte aligned.  Reads both buffers once.  Asynchronous on
+ * `stream`; PSGD_ERR_INVALID_ARG on NULL or misaligned pointers.
+ *
+ * psgd_subspace_overlap -- out[k] = mean cosine of the principal angles
+ * between the spans of compressed matrix k's factors in two Q buffers, e.g.
+ * a copy of Q taken before a step and Q after it ([GLOSS] temporal-coherence
+ * paragraph: consecutive steps' subspaces overlap with cosine similarity
+ * often above 0.9).  Both factors are copied into `scratch` (caller-owned
+ * device memory of 2 * q_elems floats, not overlapping q_a or q_b) and
+ * orthonormalised there as the refresh orthonormalises Q (Gram-Schmidt with
+ * the dependence rule: a dependent column becomes zero); the cosines are the
+ * singular values of A_hat^T B_hat (cyclic Jacobi on its Gram matrix, fp64)
+ * and the mean is over the r columns, a zero column counting as 0.  q_a and
+ * q_b are not modified.  out: ncompressed doubles, device or pinned host
+ * memory, 8-byte aligned.  Copies with hipMemcpyAsync (not for graph
+ * capture).  Asynchronous on `stream`; PSGD_ERR_INVALID_ARG on NULL,
+ * misaligned or overlapping pointers.
+ */
+psgd_status_t psgd_step_stats(psgd_plan_t plan, const float* err, const float* mhat, double* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+psgd_status_t psgd_subspace_overlap(psgd_plan_t plan, const float* q_a, const float* q_b, float* scratch,
+                                    double* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Per-stage timing with HIP events recorded on the call's stream.  While
  * enabled, every compress / decompress / refresh call records one event pair
  * per stage it runs (psgd_refresh records its products under EF_P, MTP and

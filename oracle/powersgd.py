@@ -374,3 +374,26 @@ def principal_angle_sines(A: np.ndarray, B: np.ndarray) -> np.ndarray:
     R = X - Y @ (Y.T @ X)
     s = np.linalg.svd(R, compute_uv=False)
     return np.sort(np.clip(s, 0.0, 1.0))[::-1]
+
+
+def compression_error(E: np.ndarray, M: np.ndarray) -> float:
+    """||E||_F / ||M||_F: the share of the compressor's input that error
+    feedback keeps for later steps ([GLOSS] error-feedback paragraph: e_t =
+    G_t - compress(G_t)); 0 for a zero M."""
+    nm = float(np.linalg.norm(np.asarray(M, np.float64)))
+    return float(np.linalg.norm(np.asarray(E, np.float64))) / nm if nm > 0 else 0.0
+
+
+def subspace_overlap(Qa: np.ndarray, Qb: np.ndarray) -> float:
+    """Mean cosine of the principal angles between span(Qa) and span(Qb)
+    ([GLOSS] temporal-coherence paragraph: the subspaces of consecutive steps
+    overlap with cosine similarity often above 0.9).  Both n x r factors are
+    orthonormalised with this module's Gram-Schmidt (dependent columns become
+    zero); the cosines are the singular values of Qa_hat^T Qb_hat and the
+    mean is taken over the r columns, so a zero column counts as a cosine of
+    0."""
+    A = gram_schmidt(Qa)
+    B = gram_schmidt(Qb)
+    r = np.asarray(Qa).shape[1]
+    return float(np.sum(np.linalg.svd(A.T @ B, compute_uv=False)) / r)
+

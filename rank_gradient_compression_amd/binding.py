@@ -50,6 +50,7 @@ STAGE_NAMES = ["ef_p", "gs", "mtp", "qreduce", "residual", "passthru", "refresh"
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_destroy", "psgd_plan_get_info", "psgd_plan_tensor",
     "psgd_workspace_init", "psgd_compress", "psgd_compress_noalloc", "psgd_decompress", "psgd_refresh", "psgd_init_q",
+    "psgd_step_stats", "psgd_subspace_overlap",
     "psgd_timing_enable", "psgd_timing_read", "psgd_stream_probe", "psgd_stream_copy", "psgd_last_error",
     "psgd_version",
 ]
@@ -133,6 +134,8 @@ lib.psgd_compress_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.
 lib.psgd_decompress.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_refresh.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
 lib.psgd_init_q.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, ctypes.c_size_t, _vp]
+lib.psgd_step_stats.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+lib.psgd_subspace_overlap.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_timing_enable.argtypes = [_vp, ctypes.c_int32]
 lib.psgd_timing_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
 lib.psgd_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
@@ -142,7 +145,7 @@ lib.psgd_version.restype = ctypes.c_char_p
 for _f in ["psgd_plan_create", "psgd_plan_get_info", "psgd_plan_tensor", "psgd_workspace_init", "psgd_compress",
            "psgd_compress_noalloc",
            "psgd_decompress", "psgd_refresh", "psgd_init_q", "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy",
-           "psgd_stream_probe"]:
+           "psgd_stream_probe", "psgd_step_stats", "psgd_subspace_overlap"]:
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -232,6 +235,18 @@ def psgd_refresh(plan: int, tensor: int, m: int, q: int, iters: int, workspace: 
 def psgd_init_q(plan: int, q: int, seed: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:
     _check("psgd_init_q", lib.psgd_init_q(plan, q or None, seed & ((1 << 64) - 1), workspace, workspace_bytes,
                                           stream))
+
+
+def psgd_step_stats(plan: int, err: int, mhat: int, out: int, workspace: int, workspace_bytes: int,
+                    stream: int = 0) -> None:
+    _check("psgd_step_stats", lib.psgd_step_stats(plan, err or None, mhat or None, out or None, workspace,
+                                                  workspace_bytes, stream))
+
+
+def psgd_subspace_overlap(plan: int, q_a: int, q_b: int, scratch: int, out: int, workspace: int,
+                          workspace_bytes: int, stream: int = 0) -> None:
+    _check("psgd_subspace_overlap", lib.psgd_subspace_overlap(plan, q_a or None, q_b or None, scratch or None,
+                                                              out or None, workspace, workspace_bytes, stream))
 
 
 def psgd_timing_enable(plan: int, enable: bool) -> None:

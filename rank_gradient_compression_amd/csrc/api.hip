@@ -534,6 +534,59 @@ extern "C" psgd_status_t psgd_refresh(psgd_plan_t p, int32_t tensor, const float
   return PSGD_OK;
 }
 
+extern "C" psgd_status_t psgd_step_stats(psgd_plan_t p, const float* err, const float* mhat, double* out, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_step_stats: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (p->mats.empty()) return PSGD_OK;
+  if (!err || !mhat || !out || ((uintptr_t)out & 7u)) {
+    set_error("psgd_step_stats: err, mhat and out must be non-null (out 8-byte aligned)");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_step_stats")) return s;
+  const LaunchCtx c = make_ctx(p, ws, stream);
+  const hipError_t e = launch_sumsq(c, err, mhat, out);
+  if (e != hipSuccess) return hip_fail(e, "psgd_step_stats");
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_subspace_overlap(psgd_plan_t p, const float* q_a, const float* q_b, float* scratch,
+                                               double* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_subspace_overlap: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (p->mats.empty()) return PSGD_OK;
+  if (!q_a || !q_b || !scratch || !out || ((uintptr_t)out & 7u)) {
+    set_error("psgd_subspace_overlap: q_a, q_b, scratch and out must be non-null (out 8-byte aligned)");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  const size_t qn = p->q_elems;
+  if ((scratch < q_a + qn && q_a < scratch + 2 * qn) || (scratch < q_b + qn && q_b < scratch + 2 * qn)) {
+    set_error("psgd_subspace_overlap: scratch must not overlap q_a or q_b");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (psgd_status_t s = check_ws(p, ws, ws_bytes, "psgd_subspace_overlap")) return s;
+  const LaunchCtx c = make_ctx(p, ws, stream);
+  float* a = scratch;
+  float* b = scratch + qn;
+  hipError_t e = hipMemcpyAsync(a, q_a, qn * sizeof(float), hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(b, q_b, qn * sizeof(float), hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "psgd_subspace_overlap: copy");
+  // both copies orthonormalised as the refresh does its Q (Gram-Schmidt with
+  // the dependence rule), then the cosines of their principal angles
+  const int first = 2 * c.nmat;
+  if ((e = launch_gram_orth(c, first, c.nmat, c.gramq_map, c.wg_gramq, a)) != hipSuccess ||
+      (e = launch_gram_orth(c, first, c.nmat, c.gramq_map, c.wg_gramq, b)) != hipSuccess)
+    return hip_fail(e, "psgd_subspace_overlap: orthonormalise");
+  if ((e = launch_overlap(c, first, a, b, out)) != hipSuccess) return hip_fail(e, "psgd_subspace_overlap");
+  return PSGD_OK;
+}
+
 extern "C" psgd_status_t psgd_init_q(psgd_plan_t p, float* q, uint64_t seed, void* ws, size_t ws_bytes,
                                      hipStream_t stream) {
   clear_error();

@@ -1144,6 +1144,18 @@ static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const i
   return hipGetLastError();
 }
 
+template <int RP>
+static hipError_t gram_reduce_rp(const LaunchCtx& c, int first, int count) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gram_reduce<RP>), dim3(count * (RP * RP / 256)), dim3(256 * kGramRedGroups), 0, c.stream,
+                     c.orth, first, c.gram);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_reduce(const LaunchCtx& c, int first, int count) {
+  PSGD_RP_SWITCH(c.rank_pad, gram_reduce_rp<RPV>(c, first, count));
+}
+
 hipError_t launch_gram_orth(const LaunchCtx& c, int first, int count, const int32_t* map, int nblocks,
                             float* base, int32_t* zcount) {
   PSGD_RP_SWITCH(c.rank_pad, gram_orth_rp<RPV>(c, first, count, map, nblocks, base, zcount));

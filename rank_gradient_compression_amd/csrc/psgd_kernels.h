@@ -99,6 +99,20 @@ hipError_t launch_mfma_recon(const LaunchCtx& c, float* E, const float* Q, const
 hipError_t launch_gram_orth(const LaunchCtx& c, int first, int count, const int32_t* map, int nblocks,
                             float* base, int32_t* zcount = nullptr);
 
+// Block partials (RP x RP doubles each, at the descriptors' Gram offsets)
+// summed into the T slots: descriptors first + [0, count).
+hipError_t launch_gram_reduce(const LaunchCtx& c, int first, int count);
+
+// ---- diagnostics (outside the step)
+// out[2k], out[2k + 1] = ||E_k||^2, ||M_hat_k + E_k||^2 for matrix k (fp64),
+// from kStatsWGs partial sums per matrix in its Gram scratch.
+constexpr int kStatsWGs = 64;
+hipError_t launch_sumsq(const LaunchCtx& c, const float* E, const float* Mh, double* out);
+// out[k] = mean cosine of the principal angles between the spans of two
+// orthonormalised factors laid out as the Q buffer (descriptors first + k).
+constexpr int kJacobiSweeps = 12;
+hipError_t launch_overlap(const LaunchCtx& c, int first, const float* a, const float* b, double* out);
+
 // ---- shared
 hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q);
 hipError_t launch_pass_pack(const LaunchCtx& c, const void* G, float* U, float beta, float* Pbuf);

@@ -53,6 +53,8 @@ def source_file(kernel: str) -> str:
         return "kernels_rng.hip"
     if k.startswith("k_stream"):
         return "kernels_probe.hip"
+    if k.startswith(("k_sumsq", "k_cross", "k_overlap")):
+        return "kernels_diag.hip"
     return "kernels_valu.hip"
 
 

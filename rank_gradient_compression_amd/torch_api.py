@@ -148,6 +148,30 @@ class PowerSGD:
         B.psgd_refresh(self.plan, i, m_buf.data_ptr(), self.q.data_ptr(), iters, self.workspace.data_ptr(),
                        self.ws_bytes, self._stream())
 
+    def step_stats(self) -> torch.Tensor:
+        """(ncompressed, 2) fp64 on the device: ||E||^2 and ||M||^2 per
+        compressed matrix after a compress with mhat=True (psgd_step_stats)."""
+        out = torch.empty((max(1, self.info["ncompressed"]), 2), dtype=torch.float64, device=self.device)
+        B.psgd_step_stats(self.plan, self.err.data_ptr(), self.mhat.data_ptr(), out.data_ptr(),
+                          self.workspace.data_ptr(), self.ws_bytes, self._stream())
+        return out[: self.info["ncompressed"]]
+
+    def compression_errors(self) -> torch.Tensor:
+        """||E|| / ||M|| per compressed matrix (0 where M is zero)."""
+        st = self.step_stats()
+        return torch.where(st[:, 1] > 0, (st[:, 0] / st[:, 1].clamp_min(1e-300)).sqrt(), torch.zeros_like(st[:, 0]))
+
+    def subspace_overlap(self, q_other: torch.Tensor, q: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """(ncompressed,) fp64 on the device: mean cosine of the principal
+        angles between each matrix's factor in q_other and in q (default:
+        the current Q), psgd_subspace_overlap."""
+        q = self.q if q is None else q
+        scratch = torch.empty(2 * max(1, self.info["q_elems"]), dtype=torch.float32, device=self.device)
+        out = torch.empty(max(1, self.info["ncompressed"]), dtype=torch.float64, device=self.device)
+        B.psgd_subspace_overlap(self.plan, q_other.data_ptr(), q.data_ptr(), scratch.data_ptr(), out.data_ptr(),
+                                self.workspace.data_ptr(), self.ws_bytes, self._stream())
+        return out[: self.info["ncompressed"]]
+
     def close(self) -> None:
         if self.plan:
             B.psgd_plan_destroy(self.plan)

@@ -254,6 +254,32 @@ def test_decompress_and_refresh_argument_errors():
         R.psgd_plan_destroy(p)
 
 
+def test_diagnostics_argument_errors():
+    p = R.psgd_plan_create([64, 5], [48, 1], 2)
+    qn = R.psgd_plan_get_info(p)["q_elems"]
+    try:
+        for args in [(0, FAKE, FAKE), (FAKE, 0, FAKE), (FAKE, FAKE * 2, 0), (FAKE, FAKE * 2, FAKE * 3 + 4)]:
+            with pytest.raises(B.PsgdError) as e:
+                R.psgd_step_stats(p, *args, FAKE * 4, 1 << 40, 0)
+            assert e.value.status == B.PSGD_ERR_INVALID_ARG, args
+        with pytest.raises(B.PsgdError) as e:
+            R.psgd_step_stats(p, FAKE, FAKE * 2, FAKE * 3, 0, 1 << 40, 0)
+        assert e.value.status == B.PSGD_ERR_WORKSPACE
+        far = FAKE * 16
+        for qa, qb, scr, out in [(0, FAKE, far, FAKE * 3), (FAKE, FAKE * 2, 0, FAKE * 3),
+                                 (FAKE, FAKE * 2, far, 0), (FAKE, FAKE * 2, far, FAKE * 3 + 4),
+                                 (FAKE, FAKE * 2, FAKE + 4 * (qn - 1), FAKE * 3),      # scratch over q_a
+                                 (FAKE, far + 4 * qn, far, FAKE * 3)]:                 # q_b inside scratch
+            with pytest.raises(B.PsgdError) as e:
+                R.psgd_subspace_overlap(p, qa, qb, scr, out, FAKE * 4, 1 << 40, 0)
+            assert e.value.status == B.PSGD_ERR_INVALID_ARG, (qa, qb, scr, out)
+        with pytest.raises(B.PsgdError) as e:
+            R.psgd_subspace_overlap(p, FAKE, FAKE * 2, far, FAKE * 3, FAKE * 4, 16, 0)
+        assert e.value.status == B.PSGD_ERR_WORKSPACE
+    finally:
+        R.psgd_plan_destroy(p)
+
+
 def test_stream_copy_argument_errors():
     with pytest.raises(B.PsgdError):
         R.psgd_stream_copy(FAKE, FAKE + 4, 16)

@@ -759,3 +759,58 @@ def test_decompress_planted_mistakes_are_caught():
     # a transposed operand does not even give an m x n matrix
     with pytest.raises(ValueError):
         np.asarray(Ph.T @ Q)
+
+
+# ---------------------------------------------------------------- diagnostics
+
+def test_compression_error_closed_form_at_the_svd_subspace():
+    # Warm start on the exact top-r right singular vectors: P_hat spans the
+    # top-r left singular vectors, so E = M - U_r U_r^T M and
+    # ||E||^2 = sum_{k > r} sigma_k^2 (Eckart-Young).
+    g = np.random.default_rng(41)
+    m, n, r = 60, 40, 3
+    U = W.orthonormal(g, m, n)
+    V = W.orthonormal(g, n, n)
+    s = np.linspace(5.0, 0.1, n)
+    M = (U * s) @ V.T
+    res = oracle.compress_matrix(M, V[:, :r] @ np.diag([2.0, 0.5, 1.0]))
+    want = math.sqrt(np.sum(s[r:] ** 2) / np.sum(s ** 2))
+    assert abs(oracle.compression_error(res.E, M) - want) <= 1e-12
+    # exact rank r: nothing is left for later steps
+    Mr = (U[:, :r] * s[:r]) @ V[:, :r].T
+    res = oracle.compress_matrix(Mr, rand(g, n, r))
+    assert oracle.compression_error(res.E, Mr) <= 1e-12
+    assert oracle.compression_error(np.zeros((3, 4)), np.zeros((3, 4))) == 0.0
+    assert abs(oracle.compression_error(2.0 * res.E + 1.0, 2.0 * Mr + 2.0)
+               - np.linalg.norm(2.0 * res.E + 1.0) / np.linalg.norm(2.0 * Mr + 2.0)) <= 1e-15
+
+
+def test_subspace_overlap_special_cases():
+    g = np.random.default_rng(42)
+    n, r = 30, 4
+    A = rand(g, n, r)
+    # the same span, other basis: every cosine is 1
+    assert abs(oracle.subspace_overlap(A, A @ rand(g, r, r)) - 1.0) <= 1e-12
+    I = np.eye(n)
+    # orthogonal spans: 0; one shared direction of r: 1 / r
+    assert abs(oracle.subspace_overlap(I[:, :r], I[:, r:2 * r])) <= 1e-15
+    assert abs(oracle.subspace_overlap(I[:, :r], np.c_[I[:, :1], I[:, r:2 * r - 1]]) - 1.0 / r) <= 1e-15
+    # one direction turned by theta: (r - 1 + cos theta) / r
+    th = 0.3
+    B = I[:, :r].copy()
+    B[:, r - 1] = math.cos(th) * I[:, r - 1] + math.sin(th) * I[:, r]
+    assert abs(oracle.subspace_overlap(I[:, :r], B) - (r - 1 + math.cos(th)) / r) <= 1e-14
+    # a dependent column counts as a cosine of 0
+    C = I[:, :r].copy()
+    C[:, 2] = C[:, 0] + C[:, 1]
+    assert abs(oracle.subspace_overlap(I[:, :r], C) - (r - 1) / r) <= 1e-14
+
+
+def test_subspace_overlap_equals_scipy_principal_angles():
+    scipy_linalg = pytest.importorskip("scipy.linalg")
+    g = np.random.default_rng(43)
+    for n, r in ((50, 3), (200, 16), (90, 32)):
+        A = rand(g, n, r)
+        B = A + 0.3 * rand(g, n, r)
+        want = float(np.mean(np.cos(scipy_linalg.subspace_angles(A, B))))
+        assert abs(oracle.subspace_overlap(A, B) - want) <= 1e-12
