@@ -214,9 +214,10 @@ class Runner:
         torch.cuda.empty_cache()
         return 8 * n / (ms * 1e-3) / 1e9
 
-    def pattern_ceilings(self, n=1 << 29, placements=PROBE_PLACEMENTS):
+    def pattern_ceilings(self, n=1 << 30, placements=PROBE_PLACEMENTS):
         """GB/s of bytes moved by the library's streaming probe for each pass
-        pattern in PATTERNS, over n-float arrays (2 GiB each): the best of
+        pattern in PATTERNS, over n-float arrays (4 GiB each, so that a launch
+        lasts milliseconds and its ramp-up and drain weigh about 1%): the best of
         `placements` sets of arrays, all allocated before the first is
         measured so that each set lands in other physical memory (the
         passes' own speed moves with where their buffers land)."""
