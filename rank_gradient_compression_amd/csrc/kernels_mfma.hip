@@ -1010,6 +1010,225 @@ __global__ __launch_bounds__(kGramRows) void k_apply_t(const OrthDesc* __restric
     if (k < r) p[k * ld] = (float)b[k];
 }
 
+// Blocked form of the same Cholesky for RP >= 32: 16-row block rows, each
+// factored by one wavefront over all of its remaining columns, then a
+// rank-16 update of the trailing tiles on the fp64 matrix core by all four
+// wavefronts.  Within block row B (rows 16 B .. 16 B + 15), lane j of
+// wavefront 0 keeps column 16 B + j of the Schur complement S restricted to
+// the block row's 16 rows, and step k runs as in the one-wavefront form
+// (pivot, dependence rule, row k of R, update of the later rows of the
+// block row), so a step updates at most 15 entries per lane instead of up
+// to RP - 1.  The contribution of the block row's 16 rows of R to the later
+// rows, S_CD -= R_BC^T R_BD over the upper trailing tiles (C <= D), is then
+// one 16 x 16 x 16 product per tile (the negated R_BC^T as A operand).  The
+// arithmetic is that of the right-looking factorisation; only the order in
+// which each later entry of S receives the 16 terms of one block row
+// differs (summed on the matrix core, then subtracted).  S holds A's upper
+// 16 x 16 tiles (the diagonal ones whole), which is all the updates and the
+// block rows read.  A is read whole before the first step, so the rows of R
+// are written over it block row by block row.  Block rows from r on are
+// skipped; inside the last one, steps k >= r find zero pivots (A is zero
+// there) and leave their rows of R zero.
+template <int RP>
+__global__ __launch_bounds__(256) void k_gram_solve_blk(const OrthDesc* __restrict__ descs, int first, int r,
+                                                        double* __restrict__ gram, float zero_rel,
+                                                        int32_t* __restrict__ zcount) {
+  static_assert(RP % 16 == 0 && RP >= 32 && RP <= 64, "16-row block rows, one lane per column");
+  constexpr int NB = RP / 16;
+  __shared__ double S[RP * RP];
+  __shared__ double Rb[16 * RP];  // the block row's rows of R (zero until a step writes one)
+  __shared__ double dgl[RP];      // A_kk: squared norms before projection
+  __shared__ double rowbuf[64];
+  const OrthDesc o = descs[first + blockIdx.x];
+  double* a = gram + o.t_off;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, ls = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < RP * RP / 256; ++u) {
+    const int e = tid + 256 * u, i = e / RP, j = e % RP;
+    const double v = a[e];  // every entry of the slot is a valid address
+    S[e] = (i >> 4) <= (j >> 4) ? v : 0.0;
+    if (i == j) dgl[i] = v;
+  }
+  __syncthreads();
+  const double zr2 = (double)zero_rel * (double)zero_rel;
+  int nzero = 0;  // counted by wavefront 0 (uniform there)
+  for (int B = 0; B < NB && 16 * B < r; ++B) {
+    if (wave == 0) {
+      const int ncol = RP - 16 * B;
+      const bool own = lane < ncol;
+      const int col = 16 * B + min(lane, ncol - 1);
+      const double dgv = dgl[16 * B + min(lane, 15)];  // lane k < 16: A_kk of the block row's step k
+      double sc[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sc[i] = S[(16 * B + i) * RP + col];
+        if (lane < RP) Rb[i * RP + lane] = 0.0;
+      }
+      // Steps past r need no guard (a uniform branch per step would cost
+      // register copies at every join): A's rows and columns from r on are
+      // zero (P's padding), so there the pivot and A_kk are zero, the
+      // dependence rule applies, and the step changes nothing.  The pivot
+      // arithmetic runs without a branch and the rule selects its result.
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int kk = 16 * B + k;
+        // row k of the block row's Schur complement (S_ki = S_ik for the
+        // later rows i) through LDS, read back before the pivot arithmetic
+        rowbuf[lane] = sc[k];  // lanes past the last column repeat it; only entries < 16 are read
+        double rk[16];
+#pragma unroll
+        for (int i = k + 1; i < 16; ++i) rk[i] = rowbuf[i];
+        const double d = readlane_f64(sc[k], k);
+        const double dg = readlane_f64(dgv, k);
+        const bool zero = !(dg > 0.0) || !(d > 0.0) || d <= zr2 * dg;
+        nzero += (zero && kk < r) ? 1 : 0;
+        const double yn = rsqrt_nr(d);
+        const double y = zero ? 0.0 : yn;
+        const double c = sc[k] * (y * y);
+        if (own && lane >= k) Rb[k * RP + col] = lane == k ? d * y : sc[k] * y;
+#pragma unroll
+        for (int i = k + 1; i < 16; ++i) sc[i] = fma(-rk[i], c, sc[i]);
+      }
+    }
+    __syncthreads();
+    // the block row's rows of R into the slot (kr <= jc < r) ...
+#pragma unroll
+    for (int u = 0; u < RP / 16; ++u) {
+      const int e = tid + 256 * u, kr = 16 * B + e / RP, jc = e % RP;
+      if (kr <= jc && jc < r) a[kr * RP + jc] = Rb[e];
+    }
+    // ... and their contribution to the later rows
+    const int nt = NB - 1 - B;
+    for (int u = wave; u < nt * (nt + 1) / 2; u += 4) {
+      int C = B + 1, rem = u;  // tile row C holds NB - C tiles
+      while (rem >= NB - C) {
+        rem -= NB - C;
+        ++C;
+      }
+      const int D = C + rem;
+      // acc[e] of lane (li, ls) is S[16 C + 4 e + ls][16 D + li]
+      v4d acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = S[(16 * C + 4 * e + ls) * RP + 16 * D + li];
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const int row = 4 * kq + ls;
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-Rb[row * RP + 16 * C + li], Rb[row * RP + 16 * D + li], acc, 0,
+                                                   0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[(16 * C + 4 * e + ls) * RP + 16 * D + li] = acc[e];
+    }
+    __syncthreads();
+  }
+  if (zcount && tid == 0) zcount[blockIdx.x] = nzero;
+}
+
+// x from lane G of each group of four lanes (a quad permutation on the
+// data-parallel-primitive path; both halves of the double).
+template <int G>
+__device__ __forceinline__ double quad_bcast(double v) {
+  constexpr int ctrl = G * 0x55;  // quad_perm [G, G, G, G]
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), ctrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), ctrl, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+__device__ __forceinline__ double quad_bcast_k(double v, int g) {
+  switch (g) {
+    case 0: return quad_bcast<0>(v);
+    case 1: return quad_bcast<1>(v);
+    case 2: return quad_bcast<2>(v);
+    default: return quad_bcast<3>(v);
+  }
+}
+
+// P_hat = P R^-1 with four lanes per row: the forward substitution x R = p
+// of the one-lane form (step k: x_k = b_k / R_kk, zero for a dependent
+// column, then b_q -= x_k R_kq for q > k, in the order k = 0, 1, ...), with
+// the columns dealt to the lanes of a quad cyclically (lane g keeps b_q for
+// q = 4 j + g).  The owner of column k forms x_k and hands it to the other
+// three lanes with a quad permutation; each lane then updates only its own
+// columns, reading R_kq from an LDS copy laid out by lane (Rg[g][k][j] =
+// R_{k, 4 j + g}).  Every b_q receives the same operations in the same
+// order as in the one-lane form: the result is the same, bit for bit, with
+// a quarter of the per-lane work and four times the lanes.
+template <int RP>
+__global__ __launch_bounds__(4 * kGramRows) void k_apply_q4(const OrthDesc* __restrict__ descs,
+                                                            const int32_t* __restrict__ map, int first, int r,
+                                                            float* __restrict__ base, const double* __restrict__ gram) {
+  constexpr int NJ = RP / 4;
+  constexpr int NT = 4 * kGramRows;
+  // one table per lane of the quad, each 16 bytes past a multiple of 256:
+  // the four lanes' 16-byte reads of a step fall in different banks
+  constexpr int TS = RP * NJ + 2;
+  __shared__ double Rg[4 * TS];
+  __shared__ double rinv[RP];
+  int local;
+  const OrthDesc o = descs[orth_idx(descs, map, first, local)];
+  const double* rs = gram + o.t_off;
+  const int tid = threadIdx.x, g = tid & 3;
+  const int i = local * kGramRows + (tid >> 2);
+  float* p = base + o.off + min(i, o.rows - 1);
+  const int64_t ld = o.rows;
+  float pv[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) pv[j] = p[(int64_t)min(4 * j + g, r - 1) * ld];
+  // R staged by lane: entries with q <= k or q >= r are zero (never used)
+#pragma unroll
+  for (int u = 0; u < (RP * RP + NT - 1) / NT; ++u) {
+    const int e = tid + NT * u;
+    if (e < RP * RP) {
+      const int k = e / RP, q = e % RP;
+      const double v = rs[e];
+      Rg[(q & 3) * TS + k * NJ + (q >> 2)] = (q > k && q < r) ? v : 0.0;
+      if (q == k) rinv[k] = (k < r && v > 0.0) ? 1.0 / v : 0.0;
+    }
+  }
+  __syncthreads();
+  if (i >= o.rows) return;
+  double b[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) b[j] = (double)pv[j];
+  const double* rg = Rg + g * TS;
+  // Steps in groups of four (one column per lane of the quad), a group
+  // skipped by a uniform branch once 4 G >= r; inside the last group, steps
+  // k >= r have 1 / R_kk = 0 and zero rows of R, so they change nothing that
+  // is stored.  A break instead of the branch keeps the loop rolled, with b
+  // indexed at run time.  Step k + 1's coefficients are read during step k.
+  double rc[NJ], rn[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) rc[j] = rg[j];
+#pragma unroll
+  for (int G = 0; G < NJ; ++G) {
+    if (4 * G < r) {
+#pragma unroll
+      for (int gk = 0; gk < 4; ++gk) {
+        const int k = 4 * G + gk;
+        if (k + 1 < RP) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            if (j >= ((k + 1) >> 2)) rn[j] = rg[(k + 1) * NJ + j];
+        }
+        const double xk = quad_bcast_k(b[G] * rinv[k], gk);
+        const double own = fma(-xk, rc[G], b[G]);  // zero coefficient for q <= k
+        b[G] = g == gk ? xk : (g > gk ? own : b[G]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)  // constant trip count: unrolled before the outer loops
+          if (j > G) b[j] = fma(-xk, rc[j], b[j]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          if (j >= ((k + 1) >> 2)) rc[j] = rn[j];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (4 * j + g < r) p[(int64_t)(4 * j + g) * ld] = (float)b[j];
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -1135,12 +1354,20 @@ static hipError_t gram_orth_rp(const LaunchCtx& c, int first, int count, const i
                      c.orth, first, c.gram);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(64), 0, c.stream, c.orth, first, c.rank, c.gram,
-                     kZeroColumnRel, zcount);
+  if constexpr (RP >= 32)
+    hipLaunchKernelGGL((k_gram_solve_blk<RP>), dim3(count), dim3(256), 0, c.stream, c.orth, first, c.rank, c.gram,
+                       kZeroColumnRel, zcount);
+  else
+    hipLaunchKernelGGL((k_gram_solve<RP>), dim3(count), dim3(64), 0, c.stream, c.orth, first, c.rank, c.gram,
+                       kZeroColumnRel, zcount);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_apply_t<RP>), dim3(nblocks), dim3(kGramRows), 0, c.stream, c.orth, map, first, c.rank, base,
-                     c.gram);
+  if constexpr (RP >= 32)
+    hipLaunchKernelGGL((k_apply_q4<RP>), dim3(nblocks), dim3(4 * kGramRows), 0, c.stream, c.orth, map, first, c.rank,
+                       base, c.gram);
+  else
+    hipLaunchKernelGGL((k_apply_t<RP>), dim3(nblocks), dim3(kGramRows), 0, c.stream, c.orth, map, first, c.rank, base,
+                       c.gram);
   return hipGetLastError();
 }
 
