@@ -38,6 +38,8 @@ sys.path.insert(0, ROOT)
 METRIC = "gradient GB compressed/s (EF+P+Q+E) and % HBM peak, 1×MI355X, r=2/4"
 HBM_PEAK_GBS = 8000.0
 MFMA_FP32_PEAK_TFLOPS = 157.3
+# the streaming passes: the stages whose launches move the matrix and carry its bytes
+STREAM_STAGES = ("ef_p", "mtp", "residual")
 KERNEL_OF_STAGE = {"ef_p": "k_ef_p", "mtp": "k_mtp", "residual": "k_recon"}
 KERNEL_OF_STAGE_MFMA = {"ef_p": "k_mfma_p", "mtp": "k_mfma_qt", "residual": "k_mfma_recon"}
 # Byte pattern of each pass (arrays read, arrays written, and for each output
@@ -99,15 +101,21 @@ def measured_traffic(kernel, profile):
     return v["read_bytes"] + v["write_bytes"]
 
 
-def stage_table(B, plan, bytes_per_el, flops_per_el, elems):
+def stage_table(B, R, bytes_per_el, flops_per_el, elems):
     """Per-stage average launch time from the library's HIP events and the
-    algorithmic bytes / flops of one launch."""
-    ms, n = B.psgd_timing_read(plan)
+    algorithmic bytes / flops of one launch: every stage from the breakdown
+    steps of the last Runner.time call, except the stage timed inside the
+    headline steps (`"timed": "headline"`), whose figures are taken there."""
+    ms, n = (list(v) for v in R.breakdown)
+    focus = R.focus
+    if focus is not None:
+        ms[focus[0]], n[focus[0]] = focus[1], focus[2]
     out = {}
     for i, name in enumerate(B.STAGE_NAMES):
         if not n[i]:
             continue
-        s = {"ms_avg": ms[i] / n[i], "launches": n[i]}
+        s = {"ms_avg": ms[i] / n[i], "launches": n[i],
+             "timed": "headline" if focus is not None and i == focus[0] else "breakdown"}
         if name in bytes_per_el:
             s["bytes_alg"] = bytes_per_el[name] * elems
             s["flops_alg"] = flops_per_el[name] * elems
@@ -124,7 +132,10 @@ def roofline_of(stages, mfma, profile=None):
     cand = [s for s in stages if "bytes_alg" in stages[s]]
     if not cand:
         return None
-    dom = max(cand, key=lambda s: stages[s]["ms_avg"] * stages[s]["launches"])
+    # the stage timed inside the headline steps (chosen there as the one that
+    # took the most time), else the largest
+    head = [s for s in cand if stages[s].get("timed") == "headline"]
+    dom = head[0] if head else max(cand, key=lambda s: stages[s]["ms_avg"] * stages[s]["launches"])
     d = stages[dom]
     ridge = MFMA_FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     kernel = (KERNEL_OF_STAGE_MFMA if mfma else KERNEL_OF_STAGE)[dom]
@@ -167,17 +178,34 @@ class Runner:
         self.torch, self.B = torch, B
         self.stream = torch.cuda.current_stream()
 
-    def time(self, label, call, steps, warmup, plan=None, per_step=True):
-        """K timed steps between one pair of events (the headline figure),
-        with the library's per-stage events on when `plan` is given; then,
-        separately, K steps with an event after each one for the spread."""
+    def time(self, label, call, steps, warmup, plan=None, per_step=True, focus=None):
+        """K timed steps between one pair of events (the headline figure).
+        With `plan`: first K steps with the library's events on every stage
+        (the stage breakdown, kept in self.breakdown), then the headline K
+        steps with events around the stage that took the most time (among
+        the stage names in `focus`, default all) only, kept in self.focus, so
+        that the timed calls carry one event pair per launch of one kernel
+        instead of one per stage.  Then, separately, K steps with an event
+        after each one for the spread."""
         torch, B = self.torch, self.B
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
+        self.breakdown = self.focus = None
         if plan is not None:
             B.psgd_timing_read(plan)  # drop warm-up records
+            B.psgd_timing_stages(plan, 0xFFFFFFFF)
             B.psgd_timing_enable(plan, True)
+            for _ in range(steps):
+                call()
+            B.psgd_timing_enable(plan, False)
+            self.breakdown = B.psgd_timing_read(plan)
+            ms_b, n_b = self.breakdown
+            cand = [i for i, nm in enumerate(B.STAGE_NAMES) if n_b[i] and (focus is None or nm in focus)]
+            dom = max(cand, key=lambda i: ms_b[i]) if cand else None
+            if dom is not None:
+                B.psgd_timing_stages(plan, 1 << dom)
+                B.psgd_timing_enable(plan, True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
@@ -189,6 +217,10 @@ class Runner:
         wall = time.perf_counter() - t_wall
         if plan is not None:
             B.psgd_timing_enable(plan, False)
+            B.psgd_timing_stages(plan, 0xFFFFFFFF)
+            ms_f, n_f = B.psgd_timing_read(plan)
+            if dom is not None:
+                self.focus = (dom, ms_f[dom], n_f[dom])
         total_ms = e0.elapsed_time(e1)
         per = [total_ms / steps]
         if per_step:
@@ -290,7 +322,7 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
         def step():
             ps.compress(mhat=True)
     ms, per = R.time("compress + fused decompress" + (" (deferred residual)" if deferred else ""), step, args.steps,
-                     args.warmup, plan=None if args.no_stage_timing else ps.plan)
+                     args.warmup, plan=None if args.no_stage_timing else ps.plan, focus=STREAM_STAGES)
     mfma = rank > 8
     bpe = 20.0 if deferred else 28.0
     res = base_result(args, 4.0 * dense / (ms * 1e-3) / 1e9, ms, per,
@@ -303,7 +335,7 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
                        "copy_ceiling_gbs": round(copy_gbs, 1), "pattern_ceilings_gbs": ceilings,
                        "pattern_ceiling_placements": PROBE_PLACEMENTS})
     if not args.no_stage_timing:
-        st = stage_table(B, ps.plan, step_bytes(mfma, deferred=deferred), step_flops(rank, deferred=deferred), dense)
+        st = stage_table(B, R, step_bytes(mfma, deferred=deferred), step_flops(rank, deferred=deferred), dense)
         at_ceil = attach_ceilings(st, ceilings, stage_patterns(deferred=deferred))
         res["config"]["step_ms_at_pattern_ceilings"] = round(at_ceil, 3)
         res["config"]["frac_of_pattern_ceilings"] = round(at_ceil / ms, 4)
@@ -425,7 +457,7 @@ def run_sweep(args, torch, B, W, PowerSGD, R, nested=False):
         ps.view(ps.grads, 0).copy_(A)
         ps.set_q(0, torch.from_numpy(W.gaussian_q0(n, r, 5)))
         ms, per = R.time(f"11008x4096 r={r}", lambda: ps.compress(mhat=True), args.steps, args.warmup,
-                         plan=None if args.no_stage_timing else ps.plan)
+                         plan=None if args.no_stage_timing else ps.plan, focus=STREAM_STAGES)
         mfma = r > 8
         res = base_result(args, 4.0 * m * n / (ms * 1e-3) / 1e9, ms, per,
                           f"one 11008x4096 fp32 matrix (sigma_k = exp(-k/20)), rank {r}, compress with fused "
@@ -433,7 +465,7 @@ def run_sweep(args, torch, B, W, PowerSGD, R, nested=False):
                                             "step_hbm_frac": round(28.0 * m * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                                                    4)})
         if not args.no_stage_timing:
-            st = stage_table(B, ps.plan, step_bytes(mfma), step_flops(r), m * n)
+            st = stage_table(B, R, step_bytes(mfma), step_flops(r), m * n)
             res["roofline"] = roofline_of(st, mfma, f"hbm_bytes_sweep_11008x4096_r{r}.md")
             res["stages"] = round_stages(st)
         if not args.no_cpu_baseline:
@@ -462,7 +494,7 @@ def run_refresh(args, torch, B, W, PowerSGD, R, nested=False):
         ps.refresh(0, mbuf, iters)
 
     ms, per = R.time(f"refresh 8192^2 r={r} x{iters}", call, args.steps, args.warmup,
-                     plan=None if args.no_stage_timing else ps.plan)
+                     plan=None if args.no_stage_timing else ps.plan, focus=STREAM_STAGES)
     flops = iters * 4.0 * m * n * r
     res = base_result(args, 4.0 * m * n / (ms * 1e-3) / 1e9, ms, per,
                       f"PowerSGD+ subspace refresh: {iters} rounds of orthonormalised block power iteration at rank "
@@ -472,7 +504,7 @@ def run_refresh(args, torch, B, W, PowerSGD, R, nested=False):
                        "alg_bytes": iters * 8.0 * m * n,
                        "hbm_frac": round(iters * 8.0 * m * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
     if not args.no_stage_timing:
-        st = stage_table(B, ps.plan, {"ef_p": 4.0, "mtp": 4.0}, {"ef_p": 2.0 * r, "mtp": 2.0 * r}, m * n)
+        st = stage_table(B, R, {"ef_p": 4.0, "mtp": 4.0}, {"ef_p": 2.0 * r, "mtp": 2.0 * r}, m * n)
         res["roofline"] = roofline_of(st, r > 8, f"hbm_bytes_refresh_8192x8192_r{r}.md")
         res["stages"] = round_stages(st)
     # The same call captured once in a HIP graph and replayed (its 96
@@ -500,13 +532,13 @@ def run_single(args, torch, B, W, PowerSGD, R):
     ps.set_q(0, wl.Q0)
     dense = wl.m * wl.n
     ms, per = R.time(f"single {wl.m}x{wl.n} r={wl.rank}", lambda: ps.compress(mhat=True), args.steps, args.warmup,
-                     plan=None if args.no_stage_timing else ps.plan)
+                     plan=None if args.no_stage_timing else ps.plan, focus=STREAM_STAGES)
     res = base_result(args, 4.0 * dense / (ms * 1e-3) / 1e9, ms, per,
                       f"one {wl.m}x{wl.n} fp32 matrix, rank {wl.rank}, compress with fused decompression "
                       "(launch-latency bound: a few tens of kilobytes per step)",
                       {"rank": wl.rank, "elements": dense})
     if not args.no_stage_timing:
-        st = stage_table(B, ps.plan, step_bytes(False), step_flops(wl.rank), dense)
+        st = stage_table(B, R, step_bytes(False), step_flops(wl.rank), dense)
         res["roofline"] = roofline_of(st, False)
         res["stages"] = round_stages(st)
     graph = torch.cuda.CUDAGraph()
@@ -535,13 +567,13 @@ def run_small_set(args, torch, B, W, PowerSGD, R, name, nested=False):
             ps.set_q(i, wl.q0(i, rank))
     dense = ps.info["dense_elems"]
     ms, per = R.time(f"{name} r={rank}", lambda: ps.compress(mhat=True), args.steps, args.warmup,
-                     plan=None if args.no_stage_timing else ps.plan)
+                     plan=None if args.no_stage_timing else ps.plan, focus=STREAM_STAGES)
     res = base_result(args, 4.0 * dense / (ms * 1e-3) / 1e9, ms, per,
                       f"{name}-shaped gradient set, rank {rank}, compress with fused decompression (working set "
                       "fits the 256 MB last-level cache)", {"rank": rank, "elements": dense,
                                                            "tensors": len(shapes)})
     if not args.no_stage_timing:
-        st = stage_table(B, ps.plan, step_bytes(False), step_flops(rank), dense)
+        st = stage_table(B, R, step_bytes(False), step_flops(rank), dense)
         res["roofline"] = roofline_of(st, rank > 8)
         res["stages"] = round_stages(st)
     # The same step captured once in a HIP graph and replayed: these sets are

@@ -425,6 +425,12 @@ psgd_status_t psgd_subspace_overlap(psgd_plan_t plan, const float* q_a, const fl
  */
 #define PSGD_TIMING_EVENTS 4096
 psgd_status_t psgd_timing_enable(psgd_plan_t plan, int32_t enable);
+/* Restricts the event pairs that enabled timing records to the stages whose
+ * bit (1u << PSGD_STAGE_*) is set in mask; a new plan records every stage
+ * (mask ~0u).  Fewer events per call keep host work out of launch-bound
+ * calls that are being timed.  Takes effect from the next call; records
+ * already taken are kept.  Errors: PSGD_ERR_INVALID_ARG (null plan). */
+psgd_status_t psgd_timing_stages(psgd_plan_t plan, uint32_t mask);
 psgd_status_t psgd_timing_read(psgd_plan_t plan, double* ms, int64_t* launches);
 
 /* A plain device copy dst[i] = src[i], i < n, with 16-byte accesses (n a

@@ -11,6 +11,7 @@ from .binding import (PSGD_FLAG_GRADS_BF16, PSGD_FLAG_MOMENTUM, PSGD_KIND_COMPRE
                       PsgdError, psgd_compress, psgd_compress_noalloc, psgd_decompress, psgd_init_q, psgd_last_error, psgd_plan_create,
                       psgd_plan_destroy, psgd_plan_get_info, psgd_plan_tensor, psgd_refresh, psgd_stream_copy,
                       psgd_step_stats, psgd_stream_probe, psgd_subspace_overlap,
-                      psgd_timing_enable, psgd_timing_read, psgd_version, psgd_workspace_init, step_opts)
+                      psgd_timing_enable, psgd_timing_read, psgd_timing_stages, psgd_version, psgd_workspace_init,
+                      step_opts)
 
 __all__ = [n for n in dir() if n.startswith("psgd_") or n.startswith("PSGD_")] + ["PsgdError", "binding"]

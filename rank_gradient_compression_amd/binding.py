@@ -51,7 +51,7 @@ EXPORTED = [
     "psgd_plan_create", "psgd_plan_destroy", "psgd_plan_get_info", "psgd_plan_tensor",
     "psgd_workspace_init", "psgd_compress", "psgd_compress_noalloc", "psgd_decompress", "psgd_refresh", "psgd_init_q",
     "psgd_step_stats", "psgd_subspace_overlap",
-    "psgd_timing_enable", "psgd_timing_read", "psgd_stream_probe", "psgd_stream_copy", "psgd_last_error",
+    "psgd_timing_enable", "psgd_timing_stages", "psgd_timing_read", "psgd_stream_probe", "psgd_stream_copy", "psgd_last_error",
     "psgd_version",
 ]
 
@@ -137,6 +137,7 @@ lib.psgd_init_q.argtypes = [_vp, _vp, ctypes.c_uint64, _vp, ctypes.c_size_t, _vp
 lib.psgd_step_stats.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_subspace_overlap.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_timing_enable.argtypes = [_vp, ctypes.c_int32]
+lib.psgd_timing_stages.argtypes = [_vp, ctypes.c_uint32]
 lib.psgd_timing_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), _i64p]
 lib.psgd_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
 lib.psgd_stream_probe.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, ctypes.c_size_t, _vp, _vp]
@@ -144,7 +145,8 @@ lib.psgd_last_error.restype = ctypes.c_char_p
 lib.psgd_version.restype = ctypes.c_char_p
 for _f in ["psgd_plan_create", "psgd_plan_get_info", "psgd_plan_tensor", "psgd_workspace_init", "psgd_compress",
            "psgd_compress_noalloc",
-           "psgd_decompress", "psgd_refresh", "psgd_init_q", "psgd_timing_enable", "psgd_timing_read", "psgd_stream_copy",
+           "psgd_decompress", "psgd_refresh", "psgd_init_q", "psgd_timing_enable", "psgd_timing_stages", "psgd_timing_read",
+           "psgd_stream_copy",
            "psgd_stream_probe", "psgd_step_stats", "psgd_subspace_overlap"]:
     getattr(lib, _f).restype = ctypes.c_int
 
@@ -251,6 +253,10 @@ def psgd_subspace_overlap(plan: int, q_a: int, q_b: int, scratch: int, out: int,
 
 def psgd_timing_enable(plan: int, enable: bool) -> None:
     _check("psgd_timing_enable", lib.psgd_timing_enable(plan, 1 if enable else 0))
+
+
+def psgd_timing_stages(plan: int, mask: int) -> None:
+    _check("psgd_timing_stages", lib.psgd_timing_stages(plan, mask & 0xFFFFFFFF))
 
 
 def psgd_timing_read(plan: int):

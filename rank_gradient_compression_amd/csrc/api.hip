@@ -29,6 +29,7 @@ struct TimingRecord {
 struct TimingState {
   bool enabled = false;
   bool reserved = false;  // the up-front event pool has been created
+  uint32_t mask = ~0u;    // stages that record events (bit s = stage s)
   std::vector<TimingRecord> records;
   std::vector<hipEvent_t> pool;
 };
@@ -50,7 +51,7 @@ static hipEvent_t take_event(TimingState* t) {
 class StageTimer {
  public:
   StageTimer(psgd_plan* p, int stage, hipStream_t s) : p_(p), stage_(stage), s_(s) {
-    if (!p_->timing || !p_->timing->enabled) return;
+    if (!p_->timing || !p_->timing->enabled || !((p_->timing->mask >> stage_) & 1u)) return;
     std::lock_guard<std::mutex> lk(p_->timing_mu);
     start_ = take_event(p_->timing);
     stop_ = take_event(p_->timing);
@@ -633,6 +634,18 @@ extern "C" psgd_status_t psgd_timing_enable(psgd_plan_t p, int32_t enable) {
     t->reserved = true;
   }
   t->enabled = enable != 0;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status_t psgd_timing_stages(psgd_plan_t p, uint32_t mask) {
+  clear_error();
+  if (!p) {
+    set_error("psgd_timing_stages: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lk(p->timing_mu);
+  if (!p->timing) p->timing = new TimingState();
+  p->timing->mask = mask;
   return PSGD_OK;
 }
 

@@ -307,7 +307,13 @@ def test_timing_read_without_records():
     p = R.psgd_plan_create([64], [48], 2)
     ms, n = R.psgd_timing_read(p)
     assert ms == [0.0] * B.PSGD_NSTAGES and n == [0] * B.PSGD_NSTAGES
+    R.psgd_timing_stages(p, 1 << B.PSGD_STAGE_RESIDUAL)  # host state only
+    ms, n = R.psgd_timing_read(p)
+    assert n == [0] * B.PSGD_NSTAGES
     R.psgd_plan_destroy(p)
+    with pytest.raises(B.PsgdError) as e:
+        R.psgd_timing_stages(0, 1)
+    assert e.value.status == B.PSGD_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("q,ws,wsb,status", [
