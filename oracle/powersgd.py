@@ -50,6 +50,14 @@ design notes of the repository):
       their fp32 values (round to nearest, ties to even); everything after a
       hook uses the values as received, so the residual, and with it the
       error memory, carries the quantisation error too.
+  R12 compound compression to 8 bits: each column of each transmitted factor
+      (P, then Q, before its aggregation, as in R11) is sent as an OCP FP8
+      E4M3 code per value times one power of two per column, 2^k with k the
+      smallest integer for which the column's largest magnitude (of its fp32
+      values) is at most 448 * 2^k, the format's largest finite value; each
+      value becomes 2^k * e4m3(x / 2^k), rounded to nearest with ties to
+      even, so it stays exact in fp32 and no value overflows.  An all-zero
+      column stays zero.  Pass-through values are not rounded.
 """
 from __future__ import annotations
 
@@ -179,6 +187,51 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+FP8_E4M3_MAX = 448.0  # (1 + 6/8) * 2^8: the largest finite E4M3 value
+
+
+def round_fp8_e4m3(y: np.ndarray) -> np.ndarray:
+    """The nearest OCP FP8 E4M3 value (ties to even) to each y, |y| <= 448,
+    in fp64.  E4M3 has 3 fraction bits and exponents -6..8: in the binade
+    [2^e, 2^(e+1)) its values are 2^(e-3) apart, and below 2^-6 (the
+    subnormals, m/8 * 2^-6) 2^-9 apart; np.rint rounds halves to even."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    if (a > FP8_E4M3_MAX).any():
+        raise ValueError("round_fp8_e4m3: magnitude above 448")
+    out = np.zeros_like(a)
+    nz = a != 0.0
+    e = np.floor(np.log2(a[nz]))
+    e = np.where(a[nz] < 2.0 ** e, e - 1, e)  # guard log2 rounding at powers of two
+    e = np.where(a[nz] >= 2.0 ** (e + 1), e + 1, e)
+    step = 2.0 ** (np.maximum(e, -6.0) - 3.0)
+    out[nz] = np.rint(a[nz] / step) * step
+    return np.copysign(out, y)
+
+
+def fp8_column_exponent(amax: float) -> int:
+    """Reading R12: the smallest integer k with amax <= 448 * 2^k (0 for a
+    zero column).  With amax = f 2^E, f in [0.5, 1) (frexp) and
+    448 = 0.875 * 2^9: k = E - 9 when f <= 0.875, else E - 8."""
+    if amax == 0.0:
+        return 0
+    f, E = np.frexp(float(amax))
+    return int(E) - 9 if f <= 0.875 else int(E) - 8
+
+
+def round_fp8_columns(F: np.ndarray) -> np.ndarray:
+    """Payload quantiser of reading R12 on a factor (rows x r): the values as
+    the kernels hold them (fp32), each column scaled by its power of two,
+    rounded to E4M3 and scaled back; returned in fp64."""
+    f = np.asarray(F, dtype=np.float64).astype(np.float32).astype(np.float64)
+    f = f.reshape(f.shape[0], -1)
+    out = np.zeros_like(f)
+    for c in range(f.shape[1]):
+        k = fp8_column_exponent(np.abs(f[:, c]).max() if f.shape[0] else 0.0)
+        out[:, c] = np.ldexp(round_fp8_e4m3(np.ldexp(f[:, c], -k)), k)
+    return out.reshape(np.shape(F))
+
+
 def compress_matrix(M: np.ndarray, Q_warm: np.ndarray, hook_p: Hook = None,
                     hook_q: Hook = None, power_iters: int = 1,
                     quantize: Optional[Callable[[np.ndarray], np.ndarray]] = None) -> MatrixResult:
@@ -187,8 +240,8 @@ def compress_matrix(M: np.ndarray, Q_warm: np.ndarray, hook_p: Hook = None,
     Q = M^T P_hat, aggregate Q.  Then the reconstruction P_hat Q^T and the
     error-feedback residual M - P_hat Q^T ([GLOSS] error-feedback paragraph;
     [N152] Concepts, "Error feedback").  power_iters > 1 repeats the
-    iteration from the new Q (reading R8).  `quantize` (reading R11) is
-    applied to P and to Q as they are formed, before their hooks."""
+    iteration from the new Q (reading R8).  `quantize` (reading R11 or R12)
+    is applied to P and to Q as they are formed, before their hooks."""
     M = np.asarray(M, dtype=np.float64)
     Q = np.asarray(Q_warm, dtype=np.float64)
     for _ in range(max(1, power_iters)):

@@ -697,6 +697,121 @@ def test_quantised_payload_rounds_both_factors_before_the_hooks():
     assert 1e-5 < d < 2e-2
 
 
+# ------------------------------------------------ fp8 (E4M3) payload (R12)
+
+def _e4m3_grid():
+    """Every finite non-negative OCP FP8 E4M3 value, from the format's
+    definition: subnormals m/8 * 2^-6 (m = 0..7), normals (1 + m/8) * 2^e for
+    e = -6..8, except e = 8, m = 7 (the NaN code); the codes in order."""
+    vals = [m / 8.0 * 2.0 ** -6 for m in range(8)]
+    vals += [(1.0 + m / 8.0) * 2.0 ** e for e in range(-6, 9) for m in range(8) if not (e == 8 and m == 7)]
+    return np.array(vals)
+
+
+def test_e4m3_grid_definition():
+    grid = _e4m3_grid()
+    assert grid.size == 127 and grid[-1] == oracle.FP8_E4M3_MAX == 448.0
+    assert np.all(np.diff(grid) > 0)
+
+
+def test_round_fp8_e4m3_matches_torch_conversion():
+    # Library routine: torch's float32 -> float8_e4m3fn conversion (round to
+    # nearest even) on the CPU, over normals, subnormals, ties and carries.
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(41)
+    grid = _e4m3_grid()
+    mids = 0.5 * (grid[1:] + grid[:-1])
+    x = np.concatenate([
+        g.uniform(-448.0, 448.0, 20000),
+        g.standard_normal(20000) * 2.0 ** g.integers(-14, 8, 20000),
+        grid, -grid, mids, -mids,                                # grid values and every midpoint (ties)
+        np.array([2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -12, 1e-30, 0.0, 447.9, 2.0 ** -6 * (1 - 2 ** -5)]),
+    ])
+    x = x[np.abs(x) <= 448.0].astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.round_fp8_e4m3(x)
+    assert np.array_equal(got, want)
+
+
+def test_round_fp8_e4m3_is_the_nearest_grid_value_brute_force():
+    # Brute force over the format's 127 magnitudes: the nearest value, and on
+    # a tie the one with the even code (an even index into the ordered grid).
+    grid = _e4m3_grid()
+    g = np.random.default_rng(42)
+    mids = 0.5 * (grid[1:] + grid[:-1])
+    x = np.concatenate([g.uniform(0, 448.0, 3000), g.uniform(0, 2.0 ** -5, 1000), mids, grid])
+    for v in x:
+        d = np.abs(grid - v)
+        best = np.flatnonzero(d == d.min())
+        idx = best[0] if best.size == 1 else [b for b in best if b % 2 == 0][0]
+        assert oracle.round_fp8_e4m3(np.array([v]))[0] == grid[idx]
+        assert oracle.round_fp8_e4m3(np.array([-v]))[0] == -grid[idx]
+
+
+def test_fp8_column_exponent_is_the_smallest_sufficient_power():
+    g = np.random.default_rng(43)
+    amax = np.concatenate([np.abs(g.standard_normal(3000)) * 10.0 ** g.integers(-20, 20, 3000),
+                           448.0 * 2.0 ** np.arange(-30, 30), np.nextafter(448.0 * 2.0 ** np.arange(-30, 30), np.inf),
+                           np.nextafter(448.0 * 2.0 ** np.arange(-30, 30), 0)])
+    for a in amax:
+        k = oracle.fp8_column_exponent(a)
+        assert a <= 448.0 * 2.0 ** k and not a <= 448.0 * 2.0 ** (k - 1), a
+    assert oracle.fp8_column_exponent(0.0) == 0
+
+
+def test_round_fp8_columns_scales_each_column_on_its_own():
+    g = np.random.default_rng(44)
+    F = g.standard_normal((300, 5)) * np.array([1e-3, 1.0, 40.0, 1e4, 0.0])
+    F[:, 4] = 0.0
+    out = oracle.round_fp8_columns(F)
+    assert np.all(out[:, 4] == 0.0)
+    for c in range(4):
+        f32 = F[:, c].astype(np.float32).astype(np.float64)
+        k = oracle.fp8_column_exponent(np.abs(f32).max())
+        y = out[:, c] / 2.0 ** k
+        assert 224.0 < np.abs(y).max() <= 448.0
+        assert np.array_equal(oracle.round_fp8_e4m3(y), y)       # on the E4M3 grid
+        # the nearest value: within half a step of the binade the scaled value lies in
+        a = np.abs(f32 / 2.0 ** k)
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6)
+        assert np.all(np.abs(y - f32 / 2.0 ** k) <= 0.5 * 2.0 ** (e - 3) * (1 + 1e-12))
+    # scaling one column by a power of two scales only its result, exactly
+    G = F.copy()
+    G[:, 2] *= 2.0 ** 7
+    out2 = oracle.round_fp8_columns(G)
+    assert np.array_equal(out2[:, 2], out[:, 2] * 2.0 ** 7)
+    assert np.array_equal(np.delete(out2, 2, axis=1), np.delete(out, 2, axis=1))
+    # planted mistake: one scale for the whole factor loses the small columns
+    k_all = oracle.fp8_column_exponent(np.abs(F).max())
+    one_scale = np.ldexp(oracle.round_fp8_e4m3(np.ldexp(F.astype(np.float32).astype(np.float64), -k_all)), k_all)
+    assert not np.array_equal(one_scale, out)
+
+
+def test_fp8_payload_rounds_both_factors_before_the_hooks():
+    g = np.random.default_rng(45)
+    M = rand(g, 40, 30)
+    Q0 = rand(g, 30, 3)
+    seen = {}
+
+    def keep(name):
+        def h(X):
+            seen[name] = X.copy()
+            return X
+        return h
+
+    res = oracle.compress_matrix(M, Q0, keep("P"), keep("Q"), quantize=oracle.round_fp8_columns)
+    for name in ("P", "Q"):
+        assert np.array_equal(oracle.round_fp8_columns(seen[name]), seen[name])
+    np.testing.assert_array_equal(seen["P"], oracle.round_fp8_columns(M @ Q0))
+    np.testing.assert_allclose(res.M_hat + res.E, M, rtol=0, atol=1e-14)
+    plain = oracle.compress_matrix(M, Q0)
+    # E4M3 keeps 4 significant bits: a few percent from fp64, more than bfloat16
+    d = np.linalg.norm(res.M_hat - plain.M_hat) / np.linalg.norm(plain.M_hat)
+    db = np.linalg.norm(oracle.compress_matrix(M, Q0, quantize=oracle.round_bf16).M_hat - plain.M_hat) \
+        / np.linalg.norm(plain.M_hat)
+    assert db < d < 0.2
+
+
 # ---------------------------------------------------------------- decompression
 #
 # The receiver rebuilds the gradient from the two transmitted factors as their
