@@ -355,6 +355,20 @@ def run_llama7b(args, torch, B, W, PowerSGD, R):
         ms_dd, _ = R.time("decompress", lambda: ps.decompress(), max(3, args.steps // 2), 1, per_step=False)
         res["config"]["decompress"] = {"ms_per_step": round(ms_dd, 4),
                                        "hbm_frac": round(4.0 * dense / (ms_dd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # Quantised payloads (compound compression): the factors rounded
+        # before their hooks to bfloat16, or to E4M3 codes with one power-of-two
+        # exponent per column; the same passes plus the quantiser launches.
+        # Bytes on the wire per step: factor values at 4, 2 or 1 B (+ one
+        # exponent byte per factor column for E4M3).
+        fac = sum(rank * (m + n) for m, n in shapes)
+        wire = {"fp32": 4.0 * fac, "bf16": 2.0 * fac, "fp8_e4m3": 1.0 * fac + 2 * rank * len(shapes)}
+        pay = {"fp32": {"wire_bytes_per_step": wire["fp32"]}}
+        for name, kw in (("bf16", {"payload_bf16": True}), ("fp8_e4m3", {"payload_fp8": True})):
+            ms_p, _ = R.time(f"{name} payload, compress + fused decompress",
+                             lambda kw=kw: ps.compress(mhat=True, **kw), max(3, args.steps // 2), 1, per_step=False)
+            pay[name] = {"ms_per_step": round(ms_p, 4), "grad_gbs": round(4.0 * dense / (ms_p * 1e-3) / 1e9, 2),
+                         "wire_bytes_per_step": wire[name]}
+        res["config"]["quantised_payload"] = pay
         # Deferred residual: E = M - P_hat Q^T is formed inside the next
         # step's EF-add pass instead of being stored (20 / 16 B per element).
         ps.compress(mhat=True, defer_residual=True)

@@ -123,6 +123,20 @@ typedef struct psgd_plan* psgd_plan_t;
  * pass-through values in the P buffer are not rounded.
  */
 #define PSGD_STEP_PAYLOAD_BF16 16u
+/*
+ * Compound compression to 8 bits (same passage): every column of P and of Q
+ * (per compressed matrix, r columns each) is rounded, before its hook, to
+ * OCP FP8 E4M3 values (3 fraction bits, largest finite value 448; nearest,
+ * ties to even) times one power of two per column, 2^k with k the smallest
+ * integer for which the column's largest magnitude is at most 448 * 2^k; the
+ * values stay in the fp32 buffers, each exactly an 8-bit code times its
+ * column's 2^k, so a hook can send one byte per value plus one exponent per
+ * column without further loss.  An all-zero column stays zero.  As with
+ * bfloat16, everything after a hook uses the factors as received and the
+ * pass-through values are not rounded.  Exclusive with
+ * PSGD_STEP_PAYLOAD_BF16 (PSGD_ERR_INVALID_ARG if both are set).
+ */
+#define PSGD_STEP_PAYLOAD_FP8 32u
 
 /*
  * Options of one psgd_compress call; a NULL pointer means all defaults.
@@ -140,7 +154,7 @@ typedef struct psgd_plan* psgd_plan_t;
  *                  the period (for example every 50th step).
  *   flags          any of PSGD_STEP_NO_ERROR_FEEDBACK, PSGD_STEP_NESTEROV,
  *                  PSGD_STEP_DEFER_RESIDUAL, PSGD_STEP_RESIDUAL_DEFERRED,
- *                  PSGD_STEP_PAYLOAD_BF16, or 0.
+ *                  PSGD_STEP_PAYLOAD_BF16 or PSGD_STEP_PAYLOAD_FP8, or 0.
  *   params, sgd_buf, sgd_lr, sgd_momentum
  *                  fused post-compression momentum SGD ([N152] Concepts,
  *                  "Post-compression momentum"): when params is non-NULL, the

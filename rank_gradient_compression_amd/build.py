@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsgd.so")
 
 SOURCES = ["plan.cpp", "api.hip", "kernels_valu.hip", "kernels_mfma.hip", "kernels_rng.hip", "kernels_probe.hip",
-           "kernels_diag.hip"]
+           "kernels_diag.hip", "kernels_payload.hip"]
 
 # Packed fp32 instructions are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -16,6 +16,7 @@
 
 #include "psgd_internal.h"
 #include "psgd_kernels.h"
+#include "psgd_payload.h"
 
 namespace psgd {
 
@@ -260,9 +261,13 @@ static psgd_status_t validate_compress(const char* fn, const psgd_plan* p, const
   }
   constexpr uint32_t kKnownStepFlags =
       PSGD_STEP_NO_ERROR_FEEDBACK | PSGD_STEP_NESTEROV | PSGD_STEP_DEFER_RESIDUAL | PSGD_STEP_RESIDUAL_DEFERRED |
-      PSGD_STEP_PAYLOAD_BF16;
+      PSGD_STEP_PAYLOAD_BF16 | PSGD_STEP_PAYLOAD_FP8;
   if (o->flags & ~kKnownStepFlags) {
     set_error("%s: unknown step flag bits 0x%x", fn, o->flags & ~kKnownStepFlags);
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if ((o->flags & PSGD_STEP_PAYLOAD_BF16) && (o->flags & PSGD_STEP_PAYLOAD_FP8)) {
+    set_error("%s: PSGD_STEP_PAYLOAD_BF16 and PSGD_STEP_PAYLOAD_FP8 are exclusive", fn);
     return PSGD_ERR_INVALID_ARG;
   }
   if ((o->flags & (PSGD_STEP_DEFER_RESIDUAL | PSGD_STEP_RESIDUAL_DEFERRED)) &&
@@ -298,6 +303,7 @@ static psgd_status_t run_compress(psgd_plan* p, const void* grads, float* err, f
   const int power_iters = o.power_iters > 1 ? o.power_iters : 1;
   const bool ef = (o.flags & PSGD_STEP_NO_ERROR_FEEDBACK) == 0;
   const bool payload_bf16 = (o.flags & PSGD_STEP_PAYLOAD_BF16) != 0;
+  const bool payload_fp8 = (o.flags & PSGD_STEP_PAYLOAD_FP8) != 0;
   const SgdArgs sg{o.params, o.sgd_buf, o.sgd_lr, o.sgd_momentum, (o.flags & PSGD_STEP_NESTEROV) ? 1 : 0};
   if (p->ntensors == 0) return PSGD_OK;
 
@@ -341,6 +347,8 @@ static psgd_status_t run_compress(psgd_plan* p, const void* grads, float* err, f
                   "P = M Q");
     if (payload_bf16)  // the factors only; pass-through values stay fp32
       PSGD_LAUNCH(PSGD_STAGE_EF_P, launch_round_bf16(pbuf, (int64_t)p->p_elems, stream), "round P to bfloat16");
+    else if (payload_fp8)  // per column of each matrix's P
+      PSGD_LAUNCH(PSGD_STAGE_EF_P, launch_round_fp8_cols(c, 0, pbuf), "round P to fp8");
     // The pass-through values ride with the first P only: later iterations
     // aggregate the factors alone, so those values are averaged exactly once.
     const size_t p_count = it == 0 ? p->p_elems + p->pt_elems : p->p_elems;
@@ -358,6 +366,8 @@ static psgd_status_t run_compress(psgd_plan* p, const void* grads, float* err, f
     PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_qreduce(c, all_red, q), "Q partial reduction");
     if (payload_bf16)
       PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_round_bf16(q, (int64_t)p->q_elems, stream), "round Q to bfloat16");
+    else if (payload_fp8)
+      PSGD_LAUNCH(PSGD_STAGE_QREDUCE, launch_round_fp8_cols(c, 2 * c.nmat, q), "round Q to fp8");
     if (hook && hook(q, p->q_elems, stream, user) != 0) {
       set_error("psgd_compress: aggregation hook failed on Q");
       return PSGD_ERR_HOOK;

@@ -55,6 +55,8 @@ def source_file(kernel: str) -> str:
         return "kernels_probe.hip"
     if k.startswith(("k_sumsq", "k_cross", "k_overlap")):
         return "kernels_diag.hip"
+    if k.startswith("k_round_fp8"):
+        return "kernels_payload.hip"
     return "kernels_valu.hip"
 
 

@@ -106,8 +106,8 @@ class PowerSGD:
                  refresh_iters: int = 0, power_iters: int = 0, error_feedback: bool = True,
                  params: Optional[torch.Tensor] = None, sgd_buf: Optional[torch.Tensor] = None, sgd_lr: float = 0.0,
                  sgd_momentum: float = 0.0, nesterov: bool = False, defer_residual: bool = False,
-                 residual_deferred: bool = False, payload_bf16: bool = False, noalloc: bool = False,
-                 zero_cols: Optional[torch.Tensor] = None) -> None:
+                 residual_deferred: bool = False, payload_bf16: bool = False, payload_fp8: bool = False,
+                 noalloc: bool = False, zero_cols: Optional[torch.Tensor] = None) -> None:
         """One psgd_compress call on the owned buffers; noalloc=True takes
         psgd_compress_noalloc (the library's static scratch, no workspace)."""
         out = mhat_buf if mhat_buf is not None else (self.mhat if mhat else None)
@@ -116,6 +116,7 @@ class PowerSGD:
         flags |= (B.PSGD_STEP_DEFER_RESIDUAL if defer_residual else 0)
         flags |= (B.PSGD_STEP_RESIDUAL_DEFERRED if residual_deferred else 0)
         flags |= (B.PSGD_STEP_PAYLOAD_BF16 if payload_bf16 else 0)
+        flags |= (B.PSGD_STEP_PAYLOAD_FP8 if payload_fp8 else 0)
         if refresh_iters or power_iters or flags or params is not None or zero_cols is not None:
             if zero_cols is not None:
                 assert zero_cols.dtype == torch.int32 and zero_cols.numel() >= self.info["ncompressed"]

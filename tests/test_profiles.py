@@ -43,7 +43,8 @@ def test_kernels_attributed_to_their_defining_file():
 
 def test_source_file_map_covers_every_kernel():
     # every __global__ kernel of the library maps to the file that defines it
-    for source in ("kernels_valu.hip", "kernels_mfma.hip", "kernels_rng.hip"):
+    for source in ("kernels_valu.hip", "kernels_mfma.hip", "kernels_rng.hip", "kernels_probe.hip", "kernels_diag.hip",
+                   "kernels_payload.hip"):
         code = open(os.path.join(CSRC, source)).read()
         for name in set(re.findall(r"__global__[^;{(]*?\b(k_[A-Za-z0-9_]+)\s*\(", code)):
             assert PS.source_file(f"void {name}<4>") == source, (name, source)
