@@ -317,7 +317,7 @@ static psgd_status_t run_compress(psgd_plan* p, const void* grads, float* err, f
   // pass's extra workgroups on the vector path, by a launch of their own on
   // the matrix-core path.
   LaunchCtx c1 = c;
-  if (c.mfma)
+  if (c.mfma && c.wg_pass > 0)  // (no stage, and no timing events, without pass-through tensors)
     PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_pack(c, grads, U, p->beta, pbuf), "pass-through pack");
   else
     c1.pack_dst = pbuf;
@@ -382,7 +382,7 @@ static psgd_status_t run_compress(psgd_plan* p, const void* grads, float* err, f
     PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c3, err, q, pbuf, mhat, true, sg), "residual E = M - P_hat Q^T");
   else if (unpack)  // err keeps M; only the decompressed update is written
     PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c3, nullptr, q, pbuf, mhat, false, sg), "decompress P_hat Q^T");
-  if (unpack && c.mfma)
+  if (unpack && c.mfma && c.wg_pass > 0)
     PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat, sg), "pass-through unpack");
   return PSGD_OK;
 }
@@ -494,7 +494,8 @@ extern "C" psgd_status_t psgd_decompress(psgd_plan_t p, const float* pbuf, const
   const SgdArgs none{nullptr, nullptr, 0.f, 0.f};
   if (!c.mfma) c.unpack_src = pbuf;  // pass-through values by extra workgroups of the same launch
   PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, nullptr, q, pbuf, out, false, none), "decompress P_hat Q^T");
-  if (c.mfma) PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out, none), "pass-through unpack");
+  if (c.mfma && c.wg_pass > 0)
+    PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out, none), "pass-through unpack");
   return PSGD_OK;
 }
 
