@@ -17,28 +17,30 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("rank,beta", [(2, None), (4, 0.9), (16, None)])
-def test_graph_replays_match_eager_calls(rank, beta):
+@pytest.mark.parametrize("rank,beta,payload", [(2, None, None), (4, 0.9, None), (16, None, None),
+                                                (4, None, "bf16"), (4, None, "fp8"), (32, None, "fp8")])
+def test_graph_replays_match_eager_calls(rank, beta, payload):
     shapes = [(300, 650), (257, 1030), (64, 3, 3, 3), (11,), (2, 2)]
     tensors = [(str(i), s) for i, s in enumerate(shapes)]
     wl = W.ModelSetWorkload(tensors, "plain", seed=190 + rank)
     a = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta)
     b = PowerSGD(shapes, rank, device=DEV, momentum_beta=beta)
+    kw = {"payload_bf16": payload == "bf16", "payload_fp8": payload == "fp8"}
     for ps in (a, b):
         for i in ps.compressed():
             ps.set_q(i, wl.q0(i, rank))
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        a.compress(mhat=True)
+        a.compress(mhat=True, **kw)
     for t in range(1, 5):
         for ps in (a, b):
             for i in range(len(shapes)):
                 ps.view(ps.grads, i).copy_(torch.from_numpy(np.ascontiguousarray(wl.grad(i, t))).to(DEV))
         torch.cuda.synchronize()
-        say(f"[graph r={rank} beta={beta}] replay {t}")
+        say(f"[graph r={rank} beta={beta} payload={payload}] replay {t}")
         graph.replay()
-        b.compress(mhat=True)
+        b.compress(mhat=True, **kw)
         torch.cuda.synchronize()
         junk = torch.randn(1 << 20, device=DEV).sum()  # unrelated eager work between replays
         torch.cuda.synchronize()
