@@ -16,6 +16,7 @@
 
 #include "psgd_internal.h"
 #include "psgd_kernels.h"
+#include "psgd_flat.h"
 #include "psgd_payload.h"
 
 namespace psgd {
@@ -154,9 +155,11 @@ static hipError_t stage_mtp(const LaunchCtx& c, const GridRange& g, const GridRa
   return launch_qreduce(c, gr, Q);
 }
 
-static hipError_t stage_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
-                              bool residual, const SgdArgs& sg) {
-  return c.mfma ? launch_mfma_recon(c, E, Q, Ph, Mhat, residual, sg) : launch_recon(c, E, Q, Ph, Mhat, residual, sg);
+// (flat_lds: the plan's dynamic LDS for flat-tiled matrices on the vector path)
+static hipError_t stage_recon(const psgd_plan* p, const LaunchCtx& c, float* E, const float* Q, const float* Ph,
+                              float* Mhat, bool residual, const SgdArgs& sg) {
+  return c.mfma ? launch_mfma_recon(c, E, Q, Ph, Mhat, residual, sg)
+                : launch_recon_lds(c, E, Q, Ph, Mhat, residual, sg, p->flat_lds);
 }
 
 static psgd_status_t check_ws(const psgd_plan* p, const void* ws, size_t bytes, const char* fn) {
@@ -379,9 +382,9 @@ static psgd_status_t run_compress(psgd_plan* p, const void* grads, float* err, f
   LaunchCtx c3 = c;
   if (unpack && !c.mfma) c3.unpack_src = pbuf;
   if (!defer_out)
-    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c3, err, q, pbuf, mhat, true, sg), "residual E = M - P_hat Q^T");
+    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(p, c3, err, q, pbuf, mhat, true, sg), "residual E = M - P_hat Q^T");
   else if (unpack)  // err keeps M; only the decompressed update is written
-    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c3, nullptr, q, pbuf, mhat, false, sg), "decompress P_hat Q^T");
+    PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(p, c3, nullptr, q, pbuf, mhat, false, sg), "decompress P_hat Q^T");
   if (unpack && c.mfma && c.wg_pass > 0)
     PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, mhat, sg), "pass-through unpack");
   return PSGD_OK;
@@ -493,7 +496,7 @@ extern "C" psgd_status_t psgd_decompress(psgd_plan_t p, const float* pbuf, const
   LaunchCtx c = make_ctx(p, ws, stream);
   const SgdArgs none{nullptr, nullptr, 0.f, 0.f};
   if (!c.mfma) c.unpack_src = pbuf;  // pass-through values by extra workgroups of the same launch
-  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(c, nullptr, q, pbuf, out, false, none), "decompress P_hat Q^T");
+  PSGD_LAUNCH(PSGD_STAGE_RESIDUAL, stage_recon(p, c, nullptr, q, pbuf, out, false, none), "decompress P_hat Q^T");
   if (c.mfma && c.wg_pass > 0)
     PSGD_LAUNCH(PSGD_STAGE_PASSTHRU, launch_pass_unpack(c, pbuf, out, none), "pass-through unpack");
   return PSGD_OK;

@@ -18,6 +18,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "psgd_flat.h"
 #include "psgd_kernels.h"
 #include "psgd_tables.h"
 
@@ -626,6 +627,114 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int c0, i
   }
 }
 
+// Flat tiling (a matrix with d.s3 == 0, see psgd_flat.h): the workgroup's
+// kFlatChunk elements, 8 float4 per thread (each wavefront load or store one
+// aligned 1 KB stretch).  Q is staged in LDS transposed (row j: the RQ
+// values Q[j][k], zero past the rank) and so are the P_hat rows the chunk
+// touches; each value is formed with recon_row, the arithmetic of the row
+// tiles and of the deferred residual.  The last float4 of a matrix whose
+// size is not a multiple of 4 is handled element by element.
+extern __shared__ float4 psgd_flat_lds[];
+
+template <int R, bool RESID, bool WRITE_MHAT, bool SGD>
+__device__ __forceinline__ void recon_flat(const MatDesc& d, int chunk, float* __restrict__ E,
+                                           const float* __restrict__ Q, const float* __restrict__ Ph,
+                                           float* __restrict__ Mhat, const SgdArgs& sg) {
+  constexpr int RQ = flat_rq(R);
+  constexpr int NV = kFlatChunk / 4 / kWGThreads;  // float4 per thread
+  const int m = d.m, n = d.n;
+  const uint32_t total = (uint32_t)m * (uint32_t)n;
+  const uint32_t f0 = (uint32_t)chunk * kFlatChunk;
+  const uint32_t f1 = min(total, f0 + (uint32_t)kFlatChunk);
+  const int row_a = (int)(f0 / (uint32_t)n), row_b = (int)((f1 - 1) / (uint32_t)n);
+  float* qs = reinterpret_cast<float*>(psgd_flat_lds);  // [n][RQ]
+  float* ps = qs + n * RQ;                              // [row_b - row_a + 1][RQ]
+  for (int e = threadIdx.x; e < RQ * n; e += kWGThreads) {
+    const int k = e / n, j = e - k * n;
+    qs[j * RQ + k] = k < R ? Q[d.q_off + (int64_t)k * n + j] : 0.f;
+  }
+  const int nr = row_b - row_a + 1;
+  for (int e = threadIdx.x; e < RQ * nr; e += kWGThreads) {
+    const int k = e / nr, rr = e - k * nr;
+    ps[rr * RQ + k] = k < R ? Ph[d.p_off + (int64_t)k * m + row_a + rr] : 0.f;
+  }
+  __syncthreads();
+  const int64_t base = d.off;
+  Vec<4> x[NV], xp[NV], xm[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const uint32_t f = f0 + 4u * (threadIdx.x + kWGThreads * u);
+    if (f + 4 <= f1) {
+      if constexpr (RESID) x[u] = ldv_nt<4>(E + base + f);
+      if constexpr (SGD) {
+        xp[u] = ldv<4>(sg.x + base + f);
+        xm[u] = ldv<4>(sg.m + base + f);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const uint32_t f = f0 + 4u * (threadIdx.x + kWGThreads * u);
+    if (f >= f1) continue;
+    const int cnt = (int)min(4u, f1 - f);
+    int i = (int)(f / (uint32_t)n);
+    int j = (int)(f - (uint32_t)i * (uint32_t)n);
+    Vec<4> mh;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (j >= n) {
+        j -= n;
+        ++i;
+      }
+      // (past the matrix's end, in its last float4, i may reach row_b + 1:
+      // clamped to a staged row, the value is discarded)
+      const int prow = min(i, row_b) - row_a;
+      float ph[R];
+      Vec<1> qv[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        ph[k] = ps[prow * RQ + k];
+        qv[k].v[0] = qs[j * RQ + k];
+      }
+      mh.v[c] = recon_row<R, 1>(ph, qv).v[0];
+      ++j;
+    }
+    const int64_t idx = base + f;
+    if (cnt == 4) {
+      if constexpr (RESID) {
+        Vec<4> e;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) e.v[c] = x[u].v[c] - mh.v[c];
+        stv_nt<4>(E + idx, e);
+      }
+      if constexpr (WRITE_MHAT) stv_nt<4>(Mhat + idx, mh);
+      if constexpr (SGD) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          xm[u].v[c] = fmaf(sg.mu, xm[u].v[c], mh.v[c]);
+          const float dir = sg.nesterov ? fmaf(sg.mu, xm[u].v[c], mh.v[c]) : xm[u].v[c];
+          xp[u].v[c] = fmaf(-sg.lr, dir, xp[u].v[c]);
+        }
+        stv<4>(sg.m + idx, xm[u]);
+        stv<4>(sg.x + idx, xp[u]);
+      }
+    } else {  // the matrix's last, partial float4 (constant indices into mh)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c >= cnt) break;
+        if constexpr (RESID) E[idx + c] = E[idx + c] - mh.v[c];
+        if constexpr (WRITE_MHAT) Mhat[idx + c] = mh.v[c];
+        if constexpr (SGD) {
+          float mm = fmaf(sg.mu, sg.m[idx + c], mh.v[c]);
+          const float dir = sg.nesterov ? fmaf(sg.mu, mm, mh.v[c]) : mm;
+          sg.x[idx + c] = fmaf(-sg.lr, dir, sg.x[idx + c]);
+          sg.m[idx + c] = mm;
+        }
+      }
+    }
+  }
+}
+
 // Workgroups from nrec_wg on unpack the pass-through tensors (the launch's
 // extra workgroups, when unpack_src is given).
 template <int R, bool RESID, bool WRITE_MHAT, bool SGD>
@@ -641,6 +750,10 @@ __global__ __launch_bounds__(kWGThreads) void k_recon(const MatDesc* __restrict_
   }
   const int wg = blockIdx.x;
   const MatDesc d = mats[map[wg]];
+  if (d.s3 == 0) {  // flat tiling (uniform over the workgroup)
+    recon_flat<R, RESID, WRITE_MHAT, SGD>(d, wg - d.wg_rec0, E, Q, Ph, Mhat, sg);
+    return;
+  }
   // wave index made provably uniform: row addressing and P_hat loads go scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const RowTile t = row_tile(d, wg - d.wg_rec0, d.s3, d.s3_cols, wave);
@@ -765,13 +878,13 @@ static hipError_t launch_mtp_r(const LaunchCtx& c, const GridRange& g, const flo
 
 template <int R>
 static hipError_t launch_recon_r(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
-                                 bool residual, const SgdArgs& sg) {
+                                 bool residual, const SgdArgs& sg, size_t lds) {
   const int extra = c.unpack_src ? c.wg_pass : 0;
   if (c.wg_rec + extra == 0) return hipSuccess;
   const dim3 g(c.wg_rec + extra), b(kWGThreads);
   const bool mh = Mhat != nullptr, sgd = sg.x != nullptr;
 #define PSGD_RECON(RS, MH, SG)                                                                                  \
-  hipLaunchKernelGGL((k_recon<R, RS, MH, SG>), g, b, 0, c.stream, c.mats, c.rec_map, E, Q, Ph, Mhat, sg, c.wg_rec, \
+  hipLaunchKernelGGL((k_recon<R, RS, MH, SG>), g, b, lds, c.stream, c.mats, c.rec_map, E, Q, Ph, Mhat, sg, c.wg_rec, \
                      c.pass, c.pass_map, c.unpack_src)
   if (residual) {
     if (mh && sgd) PSGD_RECON(true, true, true);
@@ -820,7 +933,12 @@ hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q) {
 
 hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat, bool residual,
                         const SgdArgs& sg) {
-  PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual, sg));
+  PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual, sg, 0));
+}
+
+hipError_t launch_recon_lds(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
+                            bool residual, const SgdArgs& sg, size_t lds_bytes) {
+  PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual, sg, lds_bytes));
 }
 
 hipError_t launch_pass_pack(const LaunchCtx& c, const void* G, float* U, float beta, float* Pbuf) {

@@ -18,6 +18,7 @@
 #include <new>
 #include <numeric>
 
+#include "psgd_flat.h"
 #include "psgd_internal.h"
 
 namespace psgd {
@@ -258,7 +259,19 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     // pass 1 tiles are kMfmaRows / kRowsPerWG rows; pass 3 tiles kRowsPerWG
     // rows on both paths
     const int32_t nrow_wg = ((d.m + tile_rows - 1) / tile_rows) * d.s1;
-    const int32_t nrec_wg = ((d.m + kRowsPerWG - 1) / kRowsPerWG) * d.s3;
+    int32_t nrec_wg = ((d.m + kRowsPerWG - 1) / kRowsPerWG) * d.s3;
+    // Rows that do not start on 128-byte lines: the vector-path residual
+    // pass tiles the matrix flat (s3 = 0, kFlatChunk elements per
+    // workgroup), with Q and the chunk's P_hat rows staged in LDS.
+    const int64_t rq = flat_rq((int)r);
+    if (!mfma && d.n % 32 != 0 && d.off % 32 == 0 && d.n >= kFlatMinCols && d.n * rq <= kFlatQMax &&
+        (int64_t)d.m * d.n < (int64_t(1) << 31)) {
+      d.s3 = 0;
+      d.s3_cols = kFlatChunk;
+      nrec_wg = (int32_t)(((int64_t)d.m * d.n + kFlatChunk - 1) / kFlatChunk);
+      const int64_t rows = kFlatChunk / d.n + 2;  // rows one chunk can touch
+      p->flat_lds = std::max<size_t>(p->flat_lds, (size_t)((d.n + rows) * rq * sizeof(float)));
+    }
     d.ppart_off = ppart;
     d.wg_pred0 = wg_pred;
     if (d.s1 > 1) {

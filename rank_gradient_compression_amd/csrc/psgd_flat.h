@@ -1,0 +1,32 @@
+// Flat tiling of the vector-path residual / decompression pass (host and
+// device declarations).
+//
+// A matrix whose rows do not start on 128-byte lines (row length not a
+// multiple of 32 floats) makes every row-contiguous 1 KB store of a
+// wavefront cover two partly written lines; the passes that write two
+// arrays then stream far below their bandwidth (33278 x 650 at rank 4:
+// 68 us against 41 us for 33278 x 640).  Such matrices are tiled flat
+// instead: workgroup w of the matrix covers the elements [w * kFlatChunk,
+// (w + 1) * kFlatChunk) of its row-major storage, whose start is line
+// aligned, and each element's row and column are computed from its index.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "psgd_kernels.h"
+
+namespace psgd {
+
+constexpr int kFlatChunk = 8192;  // elements per workgroup (256 threads x 8 float4)
+constexpr int kFlatQMax = 8192;   // largest n * flat_rq(r) staged in LDS (floats)
+constexpr int kFlatMinCols = 64;  // shorter rows keep the row tiles
+// Q and P_hat rows staged in LDS with the rank padded to 4 or 8 floats.
+constexpr int flat_rq(int r) { return r <= 4 ? 4 : 8; }
+
+// The residual / decompression pass as launch_recon, with lds_bytes of
+// dynamic LDS for the flat-tiled matrices (0 when the plan has none).
+hipError_t launch_recon_lds(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,
+                            bool residual, const SgdArgs& sg, size_t lds_bytes);
+
+}  // namespace psgd

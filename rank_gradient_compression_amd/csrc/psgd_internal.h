@@ -44,6 +44,7 @@ struct psgd_plan {
   size_t flat_elems = 0, p_elems = 0, pt_elems = 0, q_elems = 0;
   size_t payload = 0, dense = 0;
   int32_t max_m = 0, max_n = 0;
+  size_t flat_lds = 0;  // dynamic LDS of the residual pass (flat-tiled matrices), bytes
 
   std::mutex timing_mu;
   psgd::TimingState* timing = nullptr;

@@ -62,8 +62,10 @@ struct MatDesc {
   int32_t ngb;       // Gram-partial blocks (kGramRows rows each)
   int32_t tensor;    // index of the tensor in the plan
   int32_t red_split; // wavefronts summing one 64-element slice of Q partials
-  int32_t s3;        // residual / decompression pass: column splits
+  int32_t s3;        // residual / decompression pass: column splits; 0: the
+                     // vector path tiles the matrix flat (psgd_flat.h)
   int32_t s3_cols;   // residual / decompression pass: columns per split
+                     // (with s3 == 0: elements per workgroup)
   int32_t wg_rec0;   // first workgroup of this matrix in the residual-pass grid
   int32_t pad_[3];
 };
