@@ -32,14 +32,27 @@ __device__ __forceinline__ float round_e4m3_scaled(float x, int k) {
 // One workgroup per (descriptor first + blockIdx.x, column blockIdx.y): the
 // column's largest magnitude, its exponent k, then every value rounded in
 // place.  448 = 0.875 * 2^9, so with max = f 2^E (f in [0.5, 1)) the
-// smallest sufficient k is E - 9 when f <= 0.875 and E - 8 otherwise.
+// smallest sufficient k is E - 9 when f <= 0.875 and E - 8 otherwise.  Each
+// thread keeps kFp8Unroll loads in flight (at clamped addresses, masked
+// afterwards): one load at a time left a 32000-row column waiting out one
+// memory latency per 256 rows.
+constexpr int kFp8Unroll = 8;
+
 __global__ __launch_bounds__(256) void k_round_fp8_cols(const OrthDesc* __restrict__ orth, int first,
                                                         float* __restrict__ base) {
   const OrthDesc d = orth[first + blockIdx.x];
   float* __restrict__ col = base + d.off + (int64_t)blockIdx.y * d.rows;
   const int rows = d.rows;
+  constexpr int STEP = 256 * kFp8Unroll;
   float a = 0.f;
-  for (int i = threadIdx.x; i < rows; i += 256) a = fmaxf(a, fabsf(col[i]));
+  for (int i0 = 0; i0 < rows; i0 += STEP) {
+    float v[kFp8Unroll];
+#pragma unroll
+    for (int u = 0; u < kFp8Unroll; ++u) v[u] = col[min(i0 + 256 * u + (int)threadIdx.x, rows - 1)];
+#pragma unroll
+    for (int u = 0; u < kFp8Unroll; ++u)
+      if (i0 + 256 * u + (int)threadIdx.x < rows) a = fmaxf(a, fabsf(v[u]));
+  }
   for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
   __shared__ float wmax[4];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
@@ -49,7 +62,16 @@ __global__ __launch_bounds__(256) void k_round_fp8_cols(const OrthDesc* __restri
   int E;
   const float f = frexpf(amax, &E);
   const int k = f <= 0.875f ? E - 9 : E - 8;
-  for (int i = threadIdx.x; i < rows; i += 256) col[i] = round_e4m3_scaled(col[i], k);
+  for (int i0 = 0; i0 < rows; i0 += STEP) {
+    float v[kFp8Unroll];
+#pragma unroll
+    for (int u = 0; u < kFp8Unroll; ++u) v[u] = col[min(i0 + 256 * u + (int)threadIdx.x, rows - 1)];
+#pragma unroll
+    for (int u = 0; u < kFp8Unroll; ++u) {
+      const int i = i0 + 256 * u + (int)threadIdx.x;
+      if (i < rows) col[i] = round_e4m3_scaled(v[u], k);
+    }
+  }
 }
 
 hipError_t launch_round_fp8_cols(const LaunchCtx& c, int first, float* base) {
