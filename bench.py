@@ -63,7 +63,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "single", "sweep", "refresh", "resnet18", "lstm3"])
+                    choices=["llama7b", "single", "sweep", "refresh", "resnet18", "lstm3", "matrix"])
+    ap.add_argument("--shape", default="33278x650",
+                    help="matrix workload: comma-separated MxN shapes, each timed on its own (Gaussian gradients)")
     ap.add_argument("--no-configs", action="store_true",
                     help="7B workload: skip the other workloads nested under 'configs'")
     ap.add_argument("--rank", type=int, default=None)
@@ -491,6 +493,36 @@ def run_sweep(args, torch, B, W, PowerSGD, R, nested=False):
     return out
 
 
+def run_matrix(args, torch, B, W, PowerSGD, R):
+    """One m x n fp32 matrix per shape of --shape (seeded Gaussian gradients,
+    Gaussian Q0), compress with fused decompression at --rank (default 4),
+    each shape in its own plan: a probe of how a pass depends on the shape
+    (row alignment, row length)."""
+    r = args.rank or 4
+    out = []
+    for spec in args.shape.split(","):
+        m, n = (int(x) for x in spec.lower().split("x"))
+        ps = PowerSGD([(m, n)], r, device="cuda")
+        ps.grads.normal_(generator=torch.Generator(device="cuda").manual_seed(m * 100003 + n))
+        ps.set_q(0, torch.from_numpy(W.gaussian_q0(n, r, 5)))
+        mfma = r > 8
+        ms, per = R.time(f"{m}x{n} r={r}", lambda: ps.compress(mhat=True), args.steps, args.warmup,
+                         plan=None if args.no_stage_timing else ps.plan, focus=STREAM_STAGES)
+        res = base_result(args, 4.0 * m * n / (ms * 1e-3) / 1e9, ms, per,
+                          f"one {m}x{n} fp32 matrix (Gaussian gradients), rank {r}, compress with fused decompression",
+                          {"rank": r, "elements": m * n, "path": "mfma" if mfma else "valu",
+                           "row_bytes_mod_128": (4 * n) % 128,
+                           "step_hbm_frac": round(28.0 * m * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        if not args.no_stage_timing:
+            st = stage_table(B, R, step_bytes(mfma), step_flops(r), m * n)
+            res["roofline"] = roofline_of(st, mfma)
+            res["stages"] = round_stages(st)
+        out.append(res)
+        ps.close()
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_refresh(args, torch, B, W, PowerSGD, R, nested=False):
     m = n = 8192
     r = 32 if nested else (args.rank or 32)
@@ -825,6 +857,9 @@ def main():
             print(json.dumps(res), flush=True)
     elif args.workload == "refresh":
         print(json.dumps(run_refresh(args, torch, B, W, PowerSGD, R)), flush=True)
+    elif args.workload == "matrix":
+        for res in run_matrix(args, torch, B, W, PowerSGD, R):
+            print(json.dumps(res), flush=True)
     else:
         print(json.dumps(run_small_set(args, torch, B, W, PowerSGD, R, args.workload)), flush=True)
 
