@@ -628,7 +628,7 @@ __device__ __forceinline__ void recon_wave(const MatDesc& d, int row0, int c0, i
 }
 
 // Flat tiling (a matrix with d.s3 == 0, see psgd_flat.h): the workgroup's
-// kFlatChunk elements, 8 float4 per thread (each wavefront load or store one
+// d.s3_cols elements (1 to kFlatSub pieces of kFlatChunk), 8 float4 per thread and piece (each wavefront load or store one
 // aligned 1 KB stretch).  Q is staged in LDS transposed (row j: the RQ
 // values Q[j][k], zero past the rank) and so are the P_hat rows the chunk
 // touches; each value is formed with recon_row, the arithmetic of the row
@@ -644,9 +644,11 @@ __device__ __forceinline__ void recon_flat(const MatDesc& d, int chunk, float* _
   constexpr int NV = kFlatChunk / 4 / kWGThreads;  // float4 per thread
   const int m = d.m, n = d.n;
   const uint32_t total = (uint32_t)m * (uint32_t)n;
-  const uint32_t f0 = (uint32_t)chunk * kFlatChunk;
-  const uint32_t f1 = min(total, f0 + (uint32_t)kFlatChunk);
-  const int row_a = (int)(f0 / (uint32_t)n), row_b = (int)((f1 - 1) / (uint32_t)n);
+  const uint32_t GW = (uint32_t)d.s3_cols;  // elements per workgroup (a multiple of kFlatChunk)
+  const int nsub = (int)(GW / kFlatChunk);
+  const uint32_t g0 = (uint32_t)chunk * GW;
+  const uint32_t g1 = min(total, g0 + GW);
+  const int row_a = (int)(g0 / (uint32_t)n), row_b = (int)((g1 - 1) / (uint32_t)n);
   float* qs = reinterpret_cast<float*>(psgd_flat_lds);  // [n][RQ]
   float* ps = qs + n * RQ;                              // [row_b - row_a + 1][RQ]
   for (int e = threadIdx.x; e < RQ * n; e += kWGThreads) {
@@ -660,6 +662,12 @@ __device__ __forceinline__ void recon_flat(const MatDesc& d, int chunk, float* _
   }
   __syncthreads();
   const int64_t base = d.off;
+  // nsub pieces of kFlatChunk elements, one after the other, on the
+  // staged Q and P_hat rows
+  for (int sc = 0; sc < nsub; ++sc) {
+  const uint32_t f0 = g0 + (uint32_t)sc * kFlatChunk;
+  if (f0 >= g1) break;
+  const uint32_t f1 = min(g1, f0 + (uint32_t)kFlatChunk);
   Vec<4> x[NV], xp[NV], xm[NV];
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
@@ -733,6 +741,7 @@ __device__ __forceinline__ void recon_flat(const MatDesc& d, int chunk, float* _
       }
     }
   }
+  }  // sub-chunks
 }
 
 // Workgroups from nrec_wg on unpack the pass-through tensors (the launch's

@@ -261,15 +261,22 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
     const int32_t nrow_wg = ((d.m + tile_rows - 1) / tile_rows) * d.s1;
     int32_t nrec_wg = ((d.m + kRowsPerWG - 1) / kRowsPerWG) * d.s3;
     // Rows that do not start on 128-byte lines: the vector-path residual
-    // pass tiles the matrix flat (s3 = 0, kFlatChunk elements per
-    // workgroup), with Q and the chunk's P_hat rows staged in LDS.
+    // pass tiles the matrix flat (s3 = 0, s3_cols elements per workgroup,
+    // in pieces of kFlatChunk), with Q and the P_hat rows of the
+    // workgroup's elements staged in LDS.
     const int64_t rq = flat_rq((int)r);
     if (!mfma && d.n % 32 != 0 && d.off % 32 == 0 && d.n >= kFlatMinCols && d.n * rq <= kFlatQMax &&
         (int64_t)d.m * d.n < (int64_t(1) << 31)) {
+      // one staging of Q (n x rq floats) serves S pieces: one piece while Q
+      // is at most a quarter of a piece's elements, up to kFlatSub (10000 x
+      // 2046: pass 55.7 -> 51 us with four pieces; with four, the LSTM set's
+      // short matrices had too few workgroups)
+      const int64_t nsub = std::min<int64_t>(kFlatSub, std::max<int64_t>(1, d.n * rq / (kFlatChunk / 4)));
+      const int64_t per_wg = (int64_t)kFlatChunk * nsub;
       d.s3 = 0;
-      d.s3_cols = kFlatChunk;
-      nrec_wg = (int32_t)(((int64_t)d.m * d.n + kFlatChunk - 1) / kFlatChunk);
-      const int64_t rows = kFlatChunk / d.n + 2;  // rows one chunk can touch
+      d.s3_cols = (int32_t)per_wg;
+      nrec_wg = (int32_t)(((int64_t)d.m * d.n + per_wg - 1) / per_wg);
+      const int64_t rows = per_wg / d.n + 2;  // rows one workgroup can touch
       p->flat_lds = std::max<size_t>(p->flat_lds, (size_t)((d.n + rows) * rq * sizeof(float)));
     }
     d.ppart_off = ppart;

@@ -6,8 +6,9 @@
 // wavefront cover two partly written lines; the passes that write two
 // arrays then stream far below their bandwidth (33278 x 650 at rank 4:
 // 68 us against 41 us for 33278 x 640).  Such matrices are tiled flat
-// instead: workgroup w of the matrix covers the elements [w * kFlatChunk,
-// (w + 1) * kFlatChunk) of its row-major storage, whose start is line
+// instead: workgroup w of the matrix covers the elements [w * G,
+// (w + 1) * G) of its row-major storage, G = S * kFlatChunk with S pieces
+// (1 to kFlatSub: more where staging Q costs more per piece), whose start is line
 // aligned, and each element's row and column are computed from its index.
 #pragma once
 
@@ -18,7 +19,8 @@
 
 namespace psgd {
 
-constexpr int kFlatChunk = 8192;  // elements per workgroup (256 threads x 8 float4)
+constexpr int kFlatChunk = 8192;  // elements per piece (256 threads x 8 float4)
+constexpr int kFlatSub = 4;       // most pieces per workgroup, on one staging of Q and P_hat rows
 constexpr int kFlatQMax = 8192;   // largest n * flat_rq(r) staged in LDS (floats)
 constexpr int kFlatMinCols = 64;  // shorter rows keep the row tiles
 // Q and P_hat rows staged in LDS with the rank padded to 4 or 8 floats.
