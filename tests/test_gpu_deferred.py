@@ -97,3 +97,18 @@ def test_deferred_residual_momentum_bf16_odd_offsets(rank):
 @pytest.mark.parametrize("rank", [4, 16, 48])
 def test_deferred_residual_with_fused_sgd(rank):
     _run([(300, 650), (400, 512), (11,)], rank, 3, seed=170 + rank, sgd=True)
+
+
+@pytest.mark.parametrize("rank,shapes", [
+    (1, [(3, 70), (9, 130), (5,)]),
+    (4, [(9, 70), (1001, 2047), (7,)]),
+    (7, [(500, 1023), (66, 650), (3,)]),
+])
+def test_flat_residual_tiling_edges(rank, shapes):
+    """Rows that are not 128-byte aligned take the flat-tiled residual pass:
+    matrices smaller than one 8192-element piece whose size is not a multiple
+    of 4 (the last float4 element by element), three pieces per workgroup
+    (1001 x 2047 at rank 4, 500 x 1023 at rank 7), the 8-float rank padding at
+    rank 7, with the fused SGD step; bit for bit against the deferred
+    residual, and within the gate of the oracle."""
+    _run(shapes, rank, 3, seed=190 + rank, sgd=True)
