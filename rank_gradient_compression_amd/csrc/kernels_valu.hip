@@ -940,9 +940,10 @@ hipError_t launch_qreduce(const LaunchCtx& c, const GridRange& g, float* Q) {
   return hipGetLastError();
 }
 
+// Without the plan's figure: the most any flat-tiled matrix can need.
 hipError_t launch_recon(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat, bool residual,
                         const SgdArgs& sg) {
-  PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual, sg, 0));
+  PSGD_RANK_SWITCH(c.rank, launch_recon_r<RR>(c, E, Q, Ph, Mhat, residual, sg, (size_t)kFlatReconLdsMax));
 }
 
 hipError_t launch_recon_lds(const LaunchCtx& c, float* E, const float* Q, const float* Ph, float* Mhat,

@@ -278,6 +278,7 @@ extern "C" psgd_status_t psgd_plan_create(int32_t ntensors, const int64_t* rows,
       nrec_wg = (int32_t)(((int64_t)d.m * d.n + per_wg - 1) / per_wg);
       const int64_t rows = per_wg / d.n + 2;  // rows one workgroup can touch
       p->flat_lds = std::max<size_t>(p->flat_lds, (size_t)((d.n + rows) * rq * sizeof(float)));
+      static_assert(kFlatReconLdsMax <= 65536, "flat residual LDS bound");
     }
     d.ppart_off = ppart;
     d.wg_pred0 = wg_pred;

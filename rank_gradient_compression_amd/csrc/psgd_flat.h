@@ -25,6 +25,10 @@ constexpr int kFlatQMax = 8192;   // largest n * flat_rq(r) staged in LDS (float
 constexpr int kFlatMinCols = 64;  // shorter rows keep the row tiles
 // Q and P_hat rows staged in LDS with the rank padded to 4 or 8 floats.
 constexpr int flat_rq(int r) { return r <= 4 ? 4 : 8; }
+// The most dynamic LDS a flat-tiled residual pass needs: Q (n * rq <=
+// kFlatQMax floats) and the P_hat rows one workgroup can touch (at most
+// kFlatSub * kFlatChunk / kFlatMinCols + 2 rows of 8 floats).
+constexpr int kFlatReconLdsMax = (kFlatQMax + (kFlatSub * kFlatChunk / kFlatMinCols + 2) * 8) * 4;
 
 // The residual / decompression pass as launch_recon, with lds_bytes of
 // dynamic LDS for the flat-tiled matrices (0 when the plan has none).
